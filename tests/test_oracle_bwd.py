@@ -1,0 +1,133 @@
+"""Pins of the oracle's backward by float64 central finite differences of the
+oracle's own exact forward on tiny shapes (the selection is checked to stay
+fixed under every perturbation), plus closed-form properties."""
+import numpy as np
+import pytest
+
+import oracle
+from combine_router_top_expert_amd import synth
+
+H = 2.0 ** -12  # exact in fp32 for the bf16-valued inputs used here
+
+
+def _bf16(a):
+    return synth.bf16_bits_to_f32(synth.f64_to_bf16_bits(np.asarray(a, np.float64)))
+
+
+def _setup(seed, T=6, d=16, E=4, k=2, I=12, local=None):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.normal(size=(T, d)))
+    wr = _bf16(rng.normal(size=(E, d)) / np.sqrt(d))
+    bias = _bf16(rng.normal(size=E) * 0.3)
+    E_l = E if local is None else len(local)
+    wg = _bf16(rng.normal(size=(E_l, I, d)) / np.sqrt(d))
+    wu = _bf16(rng.normal(size=(E_l, I, d)) / np.sqrt(d))
+    wd = _bf16(rng.normal(size=(E_l, d, I)) / np.sqrt(I))
+    dout = _bf16(rng.normal(size=(T, d)))
+    e2l = np.full(E, -1, np.int32)
+    for i, e in enumerate(range(E) if local is None else local):
+        e2l[e] = i
+    return dict(x=x, wr=wr, bias=bias, wg=wg, wu=wu, wd=wd, dout=dout, e2l=e2l, k=k)
+
+
+def _loss(p):
+    idx, g = oracle.route(p["x"], p["wr"], p["bias"], p["k"], "exact")
+    _, out = oracle.fwd_tokens(p["x"], idx, g, p["e2l"], p["wg"], p["wu"], p["wd"], "exact")
+    return float((out * p["dout"].astype(np.float64)).sum()), idx
+
+
+def _fd(p, name, pos):
+    base_idx = _loss(p)[1]
+    vals = []
+    for sgn in (1, -1):
+        q = dict(p)
+        q[name] = p[name].copy()
+        q[name][pos] += np.float32(sgn * H)
+        L, idx = _loss(q)
+        assert np.array_equal(idx, base_idx), "selection changed under perturbation"
+        vals.append(L)
+    return (vals[0] - vals[1]) / (2 * H)
+
+
+def _analytic(p):
+    idx, g = oracle.route(p["x"], p["wr"], p["bias"], p["k"], "exact")
+    d_gate, dz, dx = oracle.bwd_tokens(p["x"], p["dout"], idx, g, p["e2l"], p["wr"], p["wg"],
+                                       p["wu"], p["wd"])
+    dwr = oracle.router_wgrad(p["x"], idx, dz, p["wr"].shape[0])
+    E_l = p["wg"].shape[0]
+    dW = []
+    for le in range(E_l):
+        rows = [(t, j) for t in range(idx.shape[0]) for j in range(idx.shape[1])
+                if p["e2l"][idx[t, j]] == le]
+        if rows:
+            tt = [t for t, _ in rows]
+            gg = [g[t, j] for t, j in rows]
+            dW.append(oracle.expert_wgrad(p["x"][tt], np.array(gg), p["dout"][tt], p["wg"][le],
+                                          p["wu"][le], p["wd"][le]))
+        else:
+            dW.append(tuple(np.zeros_like(w[le], dtype=np.float64)
+                            for w in (p["wg"], p["wu"], p["wd"])))
+    return dict(dx=dx, dwr=dwr, dW=dW, d_gate=d_gate, idx=idx, g=g)
+
+
+@pytest.mark.parametrize("seed,local", [(0, None), (1, None), (2, [3, 1])])
+def test_backward_matches_finite_differences(seed, local):
+    p = _setup(seed, local=local)
+    A = _analytic(p)
+    rng = np.random.default_rng(seed + 50)
+    T, d = p["x"].shape
+    for _ in range(12):
+        t, c = rng.integers(T), rng.integers(d)
+        np.testing.assert_allclose(A["dx"][t, c], _fd(p, "x", (t, c)), rtol=1e-5, atol=1e-8)
+    for _ in range(8):
+        e, c = rng.integers(p["wr"].shape[0]), rng.integers(d)
+        np.testing.assert_allclose(A["dwr"][e, c], _fd(p, "wr", (e, c)), rtol=1e-5, atol=1e-8)
+    I = p["wg"].shape[1]
+    for le in range(p["wg"].shape[0]):
+        for _ in range(4):
+            i, c = rng.integers(I), rng.integers(d)
+            np.testing.assert_allclose(A["dW"][le][0][i, c], _fd(p, "wg", (le, i, c)), rtol=1e-5,
+                                       atol=1e-8)
+            np.testing.assert_allclose(A["dW"][le][1][i, c], _fd(p, "wu", (le, i, c)), rtol=1e-5,
+                                       atol=1e-8)
+            np.testing.assert_allclose(A["dW"][le][2][c, i], _fd(p, "wd", (le, c, i)), rtol=1e-5,
+                                       atol=1e-8)
+
+
+def test_gate_gradient_is_derivative_wrt_gate():
+    p = _setup(3)
+    A = _analytic(p)
+    idx, g = A["idx"], A["g"]
+    for t in range(idx.shape[0]):
+        for j in range(idx.shape[1]):
+            vals = []
+            for sgn in (1, -1):
+                gg = g.copy()
+                gg[t, j] += sgn * H
+                _, out = oracle.fwd_tokens(p["x"], idx, gg, p["e2l"], p["wg"], p["wu"], p["wd"],
+                                           "exact")
+                vals.append((out * p["dout"]).sum())
+            np.testing.assert_allclose(A["d_gate"][t, j], (vals[0] - vals[1]) / (2 * H),
+                                       rtol=1e-7, atol=1e-10)
+
+
+def test_router_bwd_closed_form_properties():
+    rng = np.random.default_rng(9)
+    k, d, E = 4, 8, 6
+    idx = np.array([4, 0, 2, 5], np.int32)
+    g = rng.dirichlet(np.ones(k))
+    dg = rng.normal(size=k)
+    wr = rng.normal(size=(E, d)).astype(np.float32)
+    dz, dxr = oracle.router_bwd_token(idx, g, dg, wr)
+    assert abs(dz.sum()) < 1e-15           # softmax gradient sums to zero
+    dz2, _ = oracle.router_bwd_token(idx, g, dg + 3.0, wr)   # invariant to a shift of dg
+    np.testing.assert_allclose(dz, dz2, atol=1e-14)
+    # FD through the softmax of the chosen logits
+    z = rng.normal(size=k)
+    gz = np.exp(z - z.max()); gz /= gz.sum()
+    dz3, _ = oracle.router_bwd_token(idx, gz, dg, wr)
+    for j in range(k):
+        zp, zm = z.copy(), z.copy()
+        zp[j] += 1e-6; zm[j] -= 1e-6
+        f = lambda zz: (np.exp(zz - zz.max()) / np.exp(zz - zz.max()).sum() * dg).sum()
+        np.testing.assert_allclose(dz3[j], (f(zp) - f(zm)) / 2e-6, rtol=1e-6, atol=1e-10)

@@ -1,0 +1,142 @@
+"""Pins of the oracle's expert FFN and forward combine: the dense SwiGLU FFN
+written with numpy matmuls (a textbook composition), special cases of the
+layer (one expert, identical experts, remote slots) and storage rounding."""
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+from combine_router_top_expert_amd import synth
+
+
+def _dense_swiglu(x, wg, wu, wd):
+    x = x.astype(np.float64)
+    a = wg.astype(np.float64) @ x
+    b = wu.astype(np.float64) @ x
+    return wd.astype(np.float64) @ (a * expit(a) * b)
+
+
+def _weights(rng, E, d, I):
+    wg = (rng.normal(size=(E, I, d)) / np.sqrt(d)).astype(np.float32)
+    wu = (rng.normal(size=(E, I, d)) / np.sqrt(d)).astype(np.float32)
+    wd = (rng.normal(size=(E, d, I)) / np.sqrt(I)).astype(np.float32)
+    return wg, wu, wd
+
+
+def test_ffn_row_exact_is_dense_swiglu():
+    rng = np.random.default_rng(0)
+    d, I = 48, 80                       # non-square: a transposed operand fails
+    wg, wu, wd = _weights(rng, 1, d, I)
+    for _ in range(5):
+        x = rng.normal(size=d).astype(np.float32)
+        a, b, h, y = oracle.ffn_row(x, wg[0], wu[0], wd[0], "exact")
+        np.testing.assert_allclose(y, _dense_swiglu(x, wg[0], wu[0], wd[0]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(a, wg[0].astype(np.float64) @ x, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(h, a * expit(a) * b, rtol=1e-12, atol=1e-14)
+
+
+def test_one_expert_k1_layer_is_dense_ffn():
+    rng = np.random.default_rng(1)
+    T, d, I = 20, 32, 64
+    wg, wu, wd = _weights(rng, 1, d, I)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    wr = rng.normal(size=(1, d)).astype(np.float32)
+    idx, g = oracle.route(x, wr, None, 1, "exact")
+    assert np.all(idx == 0) and np.all(g == 1.0)
+    y, out = oracle.fwd_tokens(x, idx, g, np.zeros(1, np.int32), wg, wu, wd, "exact")
+    for t in range(T):
+        np.testing.assert_allclose(out[t], _dense_swiglu(x[t], wg[0], wu[0], wd[0]), rtol=1e-12,
+                                   atol=1e-12)
+
+
+def test_identical_experts_give_dense_ffn_for_any_routing():
+    rng = np.random.default_rng(2)
+    T, d, I, E, k = 30, 32, 40, 6, 3
+    wg1, wu1, wd1 = _weights(rng, 1, d, I)
+    wg, wu, wd = (np.repeat(w, E, axis=0) for w in (wg1, wu1, wd1))
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    wr = rng.normal(size=(E, d)).astype(np.float32)
+    idx, g = oracle.route(x, wr, None, k, "exact")
+    _, out = oracle.fwd_tokens(x, idx, g, np.arange(E, dtype=np.int32), wg, wu, wd, "exact")
+    for t in range(T):
+        np.testing.assert_allclose(out[t], _dense_swiglu(x[t], wg1[0], wu1[0], wd1[0]), rtol=1e-11,
+                                   atol=1e-12)
+
+
+def test_remote_slots_are_zero_and_excluded():
+    rng = np.random.default_rng(3)
+    T, d, I, E, k = 10, 16, 32, 4, 2
+    wg, wu, wd = _weights(rng, 2, d, I)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    idx = np.array([[0, 1], [2, 3], [1, 2], [3, 0]] * 2 + [[0, 2], [1, 3]], np.int32)
+    g = np.full((T, k), 0.5)
+    e2l = np.array([-1, 0, -1, 1], np.int32)   # experts 1 and 3 are local
+    y, out = oracle.fwd_tokens(x, idx, g, e2l, wg, wu, wd, "exact")
+    for t in range(T):
+        ref = np.zeros(d)
+        for j in range(k):
+            le = e2l[idx[t, j]]
+            if le < 0:
+                assert np.all(y[t, j] == 0)
+            else:
+                np.testing.assert_allclose(y[t, j], _dense_swiglu(x[t], wg[le], wu[le], wd[le]),
+                                           rtol=1e-12, atol=1e-13)
+                ref += 0.5 * y[t, j]
+        np.testing.assert_allclose(out[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def _is_bf16(v):
+    f = np.asarray(v, np.float32)
+    return np.all(f.astype(np.float64) == v) and np.all((f.view(np.uint32) & 0xFFFF) == 0)
+
+
+@pytest.mark.parametrize("prec", ["f32", "bf16"])
+def test_stored_rounding(prec):
+    rng = np.random.default_rng(4)
+    T, d, I, E, k = 16, 64, 96, 4, 2
+    wg, wu, wd = _weights(rng, E, d, I)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    wr = rng.normal(size=(E, d)).astype(np.float32)
+    idx, g = oracle.route(x, wr, None, k, prec)
+    y, out = oracle.fwd_tokens(x, idx, g, np.arange(E, dtype=np.int32), wg, wu, wd, prec)
+    _, oute = oracle.fwd_tokens(x, idx, g, np.arange(E, dtype=np.int32), wg, wu, wd, "exact")
+    if prec == "bf16":
+        assert _is_bf16(y) and _is_bf16(out)
+    else:
+        assert np.all(y.astype(np.float32).astype(np.float64) == y)
+    err = np.abs(out - oute).max() / np.abs(oute).max()
+    assert err < (1e-2 if prec == "bf16" else 1e-6)
+
+
+def test_bf16_rounding_is_nearest_even():
+    assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0                 # tie -> even
+    assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie -> even (up)
+    assert oracle.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    # agrees with the bit-level fp32 -> bf16 rounding of the input generator on fp32 values
+    rng = np.random.default_rng(5)
+    v = rng.normal(size=2000).astype(np.float32)
+    bits = synth.f64_to_bf16_bits(v.astype(np.float64))
+    ref = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    assert all(oracle.round_bf16(float(a)) == b for a, b in zip(v, ref))
+
+
+def test_mxfp8_row_quantisation_points():
+    rng = np.random.default_rng(6)
+    d, I = 64, 96
+    wg, wu, wd = _weights(rng, 1, d, I)
+    # the layer stores MX weights: pass their dequantised values
+    deq = [oracle.mx_dequantize(*oracle.mx_quantize(w[0].astype(np.float64))).astype(np.float32)
+           for w in (wg, wu, wd)]
+    x = rng.normal(size=d).astype(np.float32)
+    _, _, h, y = oracle.ffn_row(x, *deq, "mxfp8")
+    xq = oracle.mx_dequantize(*oracle.mx_quantize(x[None].astype(np.float64)))[0]
+    a = deq[0].astype(np.float64) @ xq
+    b = deq[1].astype(np.float64) @ xq
+    h32 = (a * expit(a) * b).astype(np.float32).astype(np.float64)
+    hq = oracle.mx_dequantize(*oracle.mx_quantize(h32[None]))[0]
+    np.testing.assert_array_equal(h, hq)
+    yref = np.array([oracle.round_bf16(v) for v in deq[2].astype(np.float64) @ hq])
+    np.testing.assert_allclose(y, yref, rtol=2 ** -7, atol=0)
+    # and within MX error of the unquantised FFN
+    yex = _dense_swiglu(x, wg[0], wu[0], wd[0])
+    assert np.abs(y - yex).max() / np.abs(yex).max() < 0.1

@@ -1,0 +1,205 @@
+"""Python binding of the gfx950 MoE layer library (``libmok.so``).
+
+Argument marshalling only: every function below has the name of a C entry
+point declared in ``include/mok.h``, turns torch tensors into device pointers
+(PyTorch provides device memory and streams) and raises ``MokError`` on a
+negative status.  Every step of the layer runs in the library's HIP kernels;
+there is no fallback: importing the binding works without a GPU, but calling
+into it needs the built library (``build.build()``) and a gfx950 device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmok.so")
+
+MOK_F32, MOK_BF16, MOK_MXFP8 = 0, 1, 2
+PREC = {"f32": MOK_F32, "bf16": MOK_BF16, "mxfp8": MOK_MXFP8}
+MAX_SOURCES = 64
+
+STATUS = {
+    0: "MOK_OK", -1: "MOK_EINVAL", -2: "MOK_ESHAPE", -3: "MOK_EDEVICE", -4: "MOK_ECAPACITY",
+    -5: "MOK_ETIMEOUT", -6: "MOK_EROUTE",
+}
+
+# every symbol include/mok.h declares
+EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
+           "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_version")
+
+
+class MokError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class mok_config(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("T_src", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E_local", ctypes.c_int32), ("prec", ctypes.c_int32), ("R_cap", ctypes.c_int32),
+                ("minibatch_rows", ctypes.c_int32), ("ring_bytes", ctypes.c_int64),
+                ("comm_wgs", ctypes.c_int32), ("gemm_wgs", ctypes.c_int32)]
+
+
+class mok_expert_weights(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class mok_fwd_state(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("row_src", ctypes.c_void_p), ("dest_row", ctypes.c_void_p),
+                ("h", ctypes.c_void_p), ("ab", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmok.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m combine_router_top_expert_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        cfgp = ctypes.POINTER(mok_config)
+        L.mok_workspace_bytes.argtypes = [cfgp]
+        L.mok_workspace_bytes.restype = ctypes.c_size_t
+        L.mok_route.argtypes = [cfgp, I32, P, P, P, P, P, P]
+        L.mok_layout.argtypes = [cfgp, P, P, P, P, P, P, P, P, P]
+        L.mok_dispatch.argtypes = [cfgp, P, P, P, P, P, P, P]
+        L.mok_expert_ffn.argtypes = [cfgp, P, P, P, ctypes.POINTER(mok_expert_weights), P, P, P, P,
+                                     P, P]
+        L.mok_combine.argtypes = [cfgp, P, P, P, P, I32, I32, P, P, P]
+        L.mok_layer_fwd.argtypes = [cfgp, I32, I32, P, P, P, P,
+                                    ctypes.POINTER(mok_expert_weights),
+                                    ctypes.POINTER(mok_fwd_state), P, P, P, P, P]
+        L.mok_layer_bwd.argtypes = [cfgp, I32, I32, P, P, P, P, ctypes.POINTER(mok_expert_weights),
+                                    ctypes.POINTER(mok_fwd_state), P, P, P, P, P, P, P, P, P, P, P]
+        L.mok_mx_quantize.argtypes = [I64, I64, P, P, P, P]
+        L.mok_version.argtypes = []
+        L.mok_version.restype = ctypes.c_char_p
+        for name in EXPORTS[1:-1]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _table(tensors: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * MAX_SOURCES)()
+    for i, t in enumerate(tensors):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise MokError(fn, rc)
+
+
+def make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows=256, ring_bytes=0,
+                comm_wgs=0, gemm_wgs=0) -> mok_config:
+    return mok_config(S, T_src, d, E, k, I, E_local, PREC.get(prec, prec), R_cap, minibatch_rows,
+                      ring_bytes, comm_wgs, gemm_wgs)
+
+
+def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> mok_expert_weights:
+    return mok_expert_weights(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
+                              _ptr(s_down))
+
+
+def make_state(topk_idx, topk_gate, counts, offsets, row_src, dest_row, h, ab) -> mok_fwd_state:
+    return mok_fwd_state(_ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(offsets),
+                         _ptr(row_src), _ptr(dest_row), _ptr(h), _ptr(ab))
+
+
+# ------------------------------------------------------------------ entry points
+def mok_version() -> str:
+    return lib().mok_version().decode()
+
+
+def mok_workspace_bytes(cfg: mok_config) -> int:
+    return int(lib().mok_workspace_bytes(ctypes.byref(cfg)))
+
+
+def mok_route(cfg, T, x, w_router, bias, topk_idx, topk_gate, stream=None):
+    _check("mok_route", lib().mok_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                        _ptr(topk_idx), _ptr(topk_gate), _stream(stream)))
+
+
+def mok_layout(cfg, topk_idx_all, expert_to_local, counts, offsets, row_src, dest_row, ws,
+               dev_status, stream=None):
+    _check("mok_layout", lib().mok_layout(ctypes.byref(cfg), _ptr(topk_idx_all),
+                                          _ptr(expert_to_local), _ptr(counts), _ptr(offsets),
+                                          _ptr(row_src), _ptr(dest_row), _ptr(ws), _ptr(dev_status),
+                                          _stream(stream)))
+
+
+def mok_dispatch(cfg, src_x, row_src, offsets, x_perm, x_scale, dev_status, stream=None):
+    _check("mok_dispatch", lib().mok_dispatch(ctypes.byref(cfg), _table(src_x), _ptr(row_src),
+                                              _ptr(offsets), _ptr(x_perm), _ptr(x_scale),
+                                              _ptr(dev_status), _stream(stream)))
+
+
+def mok_expert_ffn(cfg, x_perm, x_scale, offsets, weights: mok_expert_weights, h, h_scale, ab, y,
+                   dev_status, stream=None):
+    _check("mok_expert_ffn", lib().mok_expert_ffn(ctypes.byref(cfg), _ptr(x_perm), _ptr(x_scale),
+                                                  _ptr(offsets), ctypes.byref(weights), _ptr(h),
+                                                  _ptr(h_scale), _ptr(ab), _ptr(y), _ptr(dev_status),
+                                                  _stream(stream)))
+
+
+def mok_combine(cfg, y, dest_row, topk_gate, staging, own_lo, own_n, out, dev_status,
+                stream=None):
+    _check("mok_combine", lib().mok_combine(ctypes.byref(cfg), _ptr(y), _ptr(dest_row),
+                                            _ptr(topk_gate), _table(staging), own_lo, own_n,
+                                            _table(out) if out is not None else None,
+                                            _ptr(dev_status), _stream(stream)))
+
+
+def mok_layer_fwd(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_local,
+                  weights: mok_expert_weights, state: mok_fwd_state, staging, out, ws, dev_status,
+                  stream=None):
+    _check("mok_layer_fwd", lib().mok_layer_fwd(
+        ctypes.byref(cfg), own_lo, own_n, _table(src_x), _ptr(w_router), _ptr(bias),
+        _ptr(expert_to_local), ctypes.byref(weights), ctypes.byref(state), _table(staging),
+        _table(out) if out is not None else None, _ptr(ws), _ptr(dev_status), _stream(stream)))
+
+
+def mok_layer_bwd(cfg, own_lo, own_n, d_out, src_x, w_router, expert_to_local,
+                  weights: mok_expert_weights, state: mok_fwd_state, staging, d_gate, dx_stage,
+                  d_x, dw_gate, dw_up, dw_down, dw_router, ws, dev_status, stream=None):
+    _check("mok_layer_bwd", lib().mok_layer_bwd(
+        ctypes.byref(cfg), own_lo, own_n, _table(d_out), _table(src_x), _ptr(w_router),
+        _ptr(expert_to_local), ctypes.byref(weights), ctypes.byref(state), _table(staging),
+        _ptr(d_gate), _table(dx_stage), _table(d_x) if d_x is not None else None, _ptr(dw_gate),
+        _ptr(dw_up), _ptr(dw_down), _ptr(dw_router), _ptr(ws), _ptr(dev_status), _stream(stream)))
+
+
+def mok_mx_quantize(rows, K, src, codes, scales, stream=None):
+    _check("mok_mx_quantize", lib().mok_mx_quantize(rows, K, _ptr(src), _ptr(codes), _ptr(scales),
+                                                    _stream(stream)))

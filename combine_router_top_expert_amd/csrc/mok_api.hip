@@ -1,0 +1,285 @@
+// C ABI of the library (declared in include/mok.h): argument validation,
+// workspace carving and launch sequencing.  No allocation, no host sync.
+#include <string.h>
+
+#include "mok_internal.h"
+
+using namespace mok;
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t act_bytes(int prec) { return prec == MOK_F32 ? 4 : 2; }
+
+bool valid_cfg(const mok_config* c) {
+  if (!c) return false;
+  if (c->S < 1 || c->S > MOK_MAX_SOURCES || c->T_src < 0) return false;
+  if (c->d <= 0 || c->d % 64 != 0) return false;
+  if (c->I <= 0 || c->I % 64 != 0) return false;
+  if (c->E < 1 || c->E > 512) return false;
+  if (c->k < 1 || c->k > 16 || c->k > c->E) return false;
+  if (c->E_local < 1 || c->E_local > 256 || c->E_local > c->E) return false;
+  if (c->prec != MOK_F32 && c->prec != MOK_BF16 && c->prec != MOK_MXFP8) return false;
+  if (c->R_cap < 0) return false;
+  int64_t N = (int64_t)c->S * c->T_src * c->k;
+  if (N > 0x7FFFFFFF) return false;  // items are indexed by int32
+  if (c->ring_bytes < 0) return false;
+  return true;
+}
+
+struct Ws {
+  size_t layout, xperm, xscale, hscale, dy, dab, dz, dwr, total;
+};
+
+Ws ws_layout(const mok_config* c) {
+  Ws w;
+  const int64_t N = (int64_t)c->S * c->T_src * c->k;
+  const size_t R = (size_t)c->R_cap;
+  size_t off = 0;
+  w.layout = off;
+  off += align256(layout_ws_bytes(N, c->E_local));
+  const size_t base = off;
+  // forward pieces
+  size_t f = base;
+  w.xperm = f;
+  f += align256(c->prec == MOK_MXFP8 ? R * c->d : R * c->d * act_bytes(c->prec));
+  w.xscale = f;
+  f += align256(c->prec == MOK_MXFP8 ? R * (c->d / 32) : 0);
+  w.hscale = f;
+  f += align256(c->prec == MOK_MXFP8 ? R * (c->I / 32) : 0);
+  // backward pieces (same region)
+  size_t b = base;
+  w.dy = b;
+  b += align256(R * c->d * act_bytes(c->prec));
+  w.dab = b;
+  b += align256(R * 2 * c->I * act_bytes(c->prec));
+  w.dz = b;
+  b += align256((size_t)N * sizeof(float));
+  w.dwr = b;
+  b += align256((size_t)kRouterChunks * c->E * c->d * sizeof(float));
+  w.total = f > b ? f : b;
+  return w;
+}
+
+template <class Tab>
+bool fill_table(Tab* tab, const void* const* ptrs, int S) {
+  if (!ptrs) return false;
+  memset(tab, 0, sizeof(*tab));
+  for (int s = 0; s < S; ++s) tab->p[s] = (decltype(tab->p[0]))ptrs[s];
+  return true;
+}
+
+bool own_range_ok(const mok_config* c, int own_lo, int own_n) {
+  return own_lo >= 0 && own_n >= 0 && own_lo + own_n <= c->S;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mok_version(void) { return "mok 0.1 gfx950"; }
+
+size_t mok_workspace_bytes(const mok_config* cfg) {
+  if (!valid_cfg(cfg)) return 0;
+  return ws_layout(cfg).total;
+}
+
+mok_status mok_route(const mok_config* cfg, int32_t T, const void* x, const void* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_gate, void* stream) {
+  if (!valid_cfg(cfg) || T < 0) return MOK_EINVAL;
+  if (T > 0 && (!x || !w_router || !topk_idx || !topk_gate)) return MOK_EINVAL;
+  return launch_route(cfg->prec, T, cfg->d, cfg->E, cfg->k, x, w_router, bias, topk_idx,
+                      topk_gate, (hipStream_t)stream);
+}
+
+mok_status mok_layout(const mok_config* cfg, const int32_t* topk_idx_all,
+                      const int32_t* expert_to_local, int32_t* counts, int32_t* offsets,
+                      int32_t* row_src, int32_t* dest_row, void* ws, int32_t* dev_status,
+                      void* stream) {
+  if (!valid_cfg(cfg)) return MOK_EINVAL;
+  const int64_t N = (int64_t)cfg->S * cfg->T_src * cfg->k;
+  if (!expert_to_local || !counts || !offsets || !ws) return MOK_EINVAL;
+  if (N > 0 && (!topk_idx_all || !dest_row)) return MOK_EINVAL;
+  if (cfg->R_cap > 0 && !row_src) return MOK_EINVAL;
+  return launch_layout(N, cfg->E, cfg->E_local, cfg->R_cap, topk_idx_all, expert_to_local, counts,
+                       offsets, row_src, dest_row, (char*)ws + ws_layout(cfg).layout, dev_status,
+                       (hipStream_t)stream);
+}
+
+mok_status mok_dispatch(const mok_config* cfg, const void* const* src_x, const int32_t* row_src,
+                        const int32_t* offsets, void* x_perm, uint8_t* x_scale,
+                        int32_t* dev_status, void* stream) {
+  (void)dev_status;
+  if (!valid_cfg(cfg)) return MOK_EINVAL;
+  if (cfg->R_cap == 0) return MOK_OK;
+  SrcTable src;
+  if (!fill_table(&src, src_x, cfg->S) || !row_src || !offsets || !x_perm) return MOK_EINVAL;
+  if (cfg->prec == MOK_MXFP8 && !x_scale) return MOK_EINVAL;
+  return launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
+                       row_src, offsets, x_perm, x_scale, (hipStream_t)stream);
+}
+
+mok_status mok_expert_ffn(const mok_config* cfg, const void* x_perm, const uint8_t* x_scale,
+                          const int32_t* offsets, const mok_expert_weights* w, void* h,
+                          uint8_t* h_scale, void* ab, void* y, int32_t* dev_status,
+                          void* stream) {
+  (void)dev_status;
+  if (!valid_cfg(cfg) || !w || !offsets) return MOK_EINVAL;
+  if (cfg->R_cap == 0) return MOK_OK;
+  if (!x_perm || !w->w_gate || !w->w_up || !w->w_down || !h || !y) return MOK_EINVAL;
+  if (cfg->prec == MOK_MXFP8) {
+    if (!x_scale || !h_scale || !w->s_gate || !w->s_up || !w->s_down) return MOK_EINVAL;
+    return launch_ffn_mx(cfg->d, cfg->I, cfg->E_local, cfg->R_cap, (const uint8_t*)x_perm,
+                         x_scale, offsets, nullptr, w, (uint8_t*)h, h_scale, ab, y, nullptr,
+                         cfg->T_src, cfg->k, (hipStream_t)stream);
+  }
+  return launch_ffn(cfg->prec, cfg->d, cfg->I, cfg->E_local, cfg->R_cap, x_perm, offsets, nullptr,
+                    w->w_gate, w->w_up, w->w_down, h, ab, y, nullptr, cfg->T_src, cfg->k,
+                    (hipStream_t)stream);
+}
+
+mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest_row,
+                       const float* topk_gate, void* const* staging, int32_t own_lo,
+                       int32_t own_n, void* const* out, int32_t* dev_status, void* stream) {
+  (void)dev_status;
+  if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
+  const int64_t N = (int64_t)cfg->S * cfg->T_src * cfg->k;
+  if (N == 0) return MOK_OK;
+  DstTable stg, o;
+  if (!fill_table(&stg, (const void* const*)staging, cfg->S) || !dest_row) return MOK_EINVAL;
+  const int prec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  if (y) {
+    mok_status rc = launch_push(prec, y, dest_row, N, stg, cfg->T_src, cfg->d, cfg->k, cfg->R_cap, st);
+    if (rc != MOK_OK) return rc;
+  }
+  if (own_n == 0) return MOK_OK;
+  if (!fill_table(&o, (const void* const*)out, cfg->S) || !topk_gate) return MOK_EINVAL;
+  for (int s = own_lo; s < own_lo + own_n; ++s)
+    if (!o.p[s] || !stg.p[s]) return MOK_EINVAL;
+  return launch_combine(prec, dest_row, topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k, own_lo,
+                        own_n, cfg->R_cap, st);
+}
+
+mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                         const void* const* src_x, const void* w_router, const float* bias,
+                         const int32_t* expert_to_local, const mok_expert_weights* w,
+                         const mok_fwd_state* st, void* const* staging, void* const* out,
+                         void* ws, int32_t* dev_status, void* stream) {
+  if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
+  if (!src_x || !w_router || !expert_to_local || !w || !st || !staging || !ws) return MOK_EINVAL;
+  if (!st->topk_idx || !st->topk_gate || !st->counts || !st->offsets || !st->dest_row)
+    return MOK_EINVAL;
+  if (cfg->R_cap > 0 && (!st->row_src || !st->h)) return MOK_EINVAL;
+  if (own_n > 0 && !out) return MOK_EINVAL;
+  if (cfg->ring_bytes > 0) return MOK_EINVAL;  // fused ring path: not available in this build
+  hipStream_t sm = (hipStream_t)stream;
+  const int64_t per_src = (int64_t)cfg->T_src * cfg->k;
+  const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
+  for (int s = own_lo; s < own_lo + own_n; ++s) {
+    if (!src_x[s]) return MOK_EINVAL;
+    mok_status rc = launch_route(rprec, cfg->T_src, cfg->d, cfg->E, cfg->k, src_x[s], w_router,
+                                 bias, st->topk_idx + s * per_src, st->topk_gate + s * per_src, sm);
+    if (rc != MOK_OK) return rc;
+  }
+  mok_status rc = mok_layout(cfg, st->topk_idx, expert_to_local, st->counts, st->offsets,
+                             st->row_src, st->dest_row, ws, dev_status, stream);
+  if (rc != MOK_OK) return rc;
+  const Ws wl = ws_layout(cfg);
+  char* wsb = (char*)ws;
+  DstTable stg;
+  fill_table(&stg, (const void* const*)staging, cfg->S);
+  if (cfg->R_cap > 0) {
+    SrcTable src;
+    fill_table(&src, src_x, cfg->S);
+    if (cfg->prec == MOK_MXFP8) {
+      rc = launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
+                         st->row_src, st->offsets, wsb + wl.xperm, (uint8_t*)(wsb + wl.xscale), sm);
+      if (rc != MOK_OK) return rc;
+      rc = launch_ffn_mx(cfg->d, cfg->I, cfg->E_local, cfg->R_cap, (const uint8_t*)(wsb + wl.xperm),
+                         (const uint8_t*)(wsb + wl.xscale), st->offsets, st->row_src, w,
+                         (uint8_t*)st->h, (uint8_t*)(wsb + wl.hscale), st->ab, nullptr, &stg,
+                         cfg->T_src, cfg->k, sm);
+    } else {
+      rc = launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
+                         st->row_src, st->offsets, wsb + wl.xperm, nullptr, sm);
+      if (rc != MOK_OK) return rc;
+      rc = launch_ffn(cfg->prec, cfg->d, cfg->I, cfg->E_local, cfg->R_cap, wsb + wl.xperm,
+                      st->offsets, st->row_src, w->w_gate, w->w_up, w->w_down, st->h, st->ab,
+                      nullptr, &stg, cfg->T_src, cfg->k, sm);
+    }
+    if (rc != MOK_OK) return rc;
+  }
+  if (own_n == 0) return MOK_OK;
+  return mok_combine(cfg, nullptr, st->dest_row, st->topk_gate, staging, own_lo, own_n, out,
+                     dev_status, stream);
+}
+
+mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                         const void* const* d_out, const void* const* src_x,
+                         const void* w_router, const int32_t* expert_to_local,
+                         const mok_expert_weights* w, const mok_fwd_state* st,
+                         void* const* staging, float* d_gate, void* const* dx_stage,
+                         void* const* d_x, float* dw_gate, float* dw_up, float* dw_down,
+                         float* dw_router, void* ws, int32_t* dev_status, void* stream) {
+  (void)dev_status;
+  (void)expert_to_local;
+  if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
+  if (cfg->prec == MOK_MXFP8) return MOK_EINVAL;
+  if (!d_out || !src_x || !w_router || !w || !st || !staging || !d_gate || !dx_stage || !ws)
+    return MOK_EINVAL;
+  if (!dw_gate || !dw_up || !dw_down || !st->ab || !st->h) return MOK_EINVAL;
+  if (own_n > 0 && !d_x) return MOK_EINVAL;
+  BwdPlan p;
+  memset(&p, 0, sizeof(p));
+  p.prec = cfg->prec;
+  p.S = cfg->S;
+  p.T_src = cfg->T_src;
+  p.d = cfg->d;
+  p.E = cfg->E;
+  p.k = cfg->k;
+  p.I = cfg->I;
+  p.E_local = cfg->E_local;
+  p.R_cap = cfg->R_cap;
+  p.own_lo = own_lo;
+  p.own_n = own_n;
+  fill_table(&p.d_out, d_out, cfg->S);
+  fill_table(&p.src_x, src_x, cfg->S);
+  fill_table(&p.staging, (const void* const*)staging, cfg->S);
+  fill_table(&p.dx_stage, (const void* const*)dx_stage, cfg->S);
+  if (own_n > 0) fill_table(&p.d_x, (const void* const*)d_x, cfg->S);
+  p.w_router = w_router;
+  p.wg = w->w_gate;
+  p.wu = w->w_up;
+  p.wd = w->w_down;
+  p.topk_idx = st->topk_idx;
+  p.topk_gate = st->topk_gate;
+  p.offsets = st->offsets;
+  p.row_src = st->row_src;
+  p.dest_row = st->dest_row;
+  p.h = st->h;
+  p.ab = st->ab;
+  p.d_gate = d_gate;
+  p.dw_gate = dw_gate;
+  p.dw_up = dw_up;
+  p.dw_down = dw_down;
+  p.dw_router = dw_router;
+  const Ws wl = ws_layout(cfg);
+  char* wsb = (char*)ws;
+  p.dy = wsb + wl.dy;
+  p.dab = wsb + wl.dab;
+  p.dz = (float*)(wsb + wl.dz);
+  p.dwr_part = (float*)(wsb + wl.dwr);
+  return launch_bwd(p, (hipStream_t)stream);
+}
+
+mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_EINVAL;
+  if (rows == 0) return MOK_OK;
+  if (!src || !codes || !scales) return MOK_EINVAL;
+  return launch_mx_quantize(rows, K, src, codes, scales, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,362 @@
+// Backward pass of the MoE layer.
+//
+// kucoin article, section 01: the backward pass runs two more rounds of
+// communication in the reverse direction; section 02: pull reverse-combine
+// and push reverse-dispatch.  Steps (float32 accumulation everywhere, every
+// reduction in a fixed order, no floating-point atomics):
+//   1. reverse-combine pull: for every routed row r <- item n = (s, t, j):
+//        dy[r] = g_n * dout_s[t]                                  (bf16 rows)
+//        d_gate[n] = dout_s[t] . y_n   (y_n = the row the forward pushed)
+//   2. dgrad through W_down with the SwiGLU derivative in the epilogue:
+//        dh = dy W_down[e];  s = sigmoid(a);
+//        da = dh b s (1 + a (1 - s)),  db = dh a s   -> dab[r] = da | db
+//   3. dgrad to the tokens:  dx = dab [W_gate[e]; W_up[e]], pushed to the
+//      item's reverse-dispatch staging row dx_stage_s[t*k + j];
+//   4. weight gradients per expert, contraction over the expert's rows in
+//      ascending row order (one workgroup owns each output tile):
+//        [dW_gate; dW_up][e] = dab^T X_e,   dW_down[e] = dy^T h_e
+//      with X_e the expert's token rows gathered again through row_src;
+//   5. per own token: dz_j = g_j (dg_j - sum_i g_i dg_i) over the chosen
+//      experts (router through the renormalised softmax; selection is
+//      piecewise constant), d_x = sum_j dx_stage_j + sum_j dz_j w_router[e_j];
+//   6. dW_router[e] = sum_t dz_{t,e} x_t: partial sums over fixed token
+//      chunks, then a fixed-order sum of the chunks.
+#include "mok_gemm.h"
+#include "mok_internal.h"
+
+namespace mok {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------ 1. pull
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rc_pull_kernel(BwdPlan p) {
+  __shared__ float red[kThreads / 64];
+  int R = p.offsets[p.E_local];
+  if (R > p.R_cap) R = p.R_cap;
+  const int r = blockIdx.x;
+  if (r >= R) return;
+  const int n = p.row_src[r];
+  const int tok = n / p.k, j = n % p.k;
+  const int s = tok / p.T_src, t = tok % p.T_src;
+  const float g = p.topk_gate[n];
+  const T* dout = reinterpret_cast<const T*>(p.d_out.p[s]) + (size_t)t * p.d;
+  const T* y = reinterpret_cast<const T*>(p.staging.p[s]) + ((size_t)t * p.k + j) * p.d;
+  T* dy = reinterpret_cast<T*>(p.dy) + (size_t)r * p.d;
+  constexpr int U = 16 / sizeof(T);
+  float part = 0.0f;
+  for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
+    uint4 dv = ld16(dout + u * U), yv = ld16(y + u * U);
+    const T* de = reinterpret_cast<const T*>(&dv);
+    const T* ye = reinterpret_cast<const T*>(&yv);
+    uint4 ov;
+    T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const float dvf = to_f32<T>(de[i]);
+      part = __builtin_fmaf(dvf, to_f32<T>(ye[i]), part);
+      oe[i] = from_f32<T>(g * dvf);
+    }
+    st16(dy + u * U, ov);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.0f;
+    for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
+    p.d_gate[n] = tot;
+  }
+}
+
+// ------------------------------------------------------------------ 2. dh + SwiGLU'
+template <typename T>
+__global__ __launch_bounds__(kGemmThreads) void dh_kernel(BwdPlan p, int ntn) {
+  __shared__ __attribute__((aligned(16))) T smem[TileSmem<T>::BYTES / sizeof(T)];
+  __shared__ int s_prefix[257];
+  const int mtile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  GroupTile g;
+  if (!find_group_tile(p.offsets, p.E_local, p.R_cap, mtile, s_prefix, &g)) return;
+  const T* dy = reinterpret_cast<const T*>(p.dy);
+  const int n0 = nt * kBN;
+  const T* wd = reinterpret_cast<const T*>(p.wd) + (size_t)g.e * p.d * p.I + n0;
+  KLoader<T, kBM> la;
+  la.init([&](int row) -> const T* {
+    const int r = g.r0 + row;
+    return r < g.r1 ? dy + (size_t)r * p.d : nullptr;
+  });
+  MNLoader<T, kBN> lb;
+  lb.init(p.I - n0);
+  auto kptr = [&](int kk) -> const T* { return wd + (size_t)kk * p.I; };
+  Acc acc;
+  gemm_mainloop<T>(p.d / MfmaT<T>::BK, la, lb,
+                   [&](int kt, uint4(&r)[KLoader<T, kBM>::NU]) { la.load(kt, r); },
+                   [&](int kt, uint4(&r)[MNLoader<T, kBN>::NU]) { lb.load(kt, kptr, r); }, smem,
+                   acc);
+  const T* ab = reinterpret_cast<const T*>(p.ab);
+  T* dab = reinterpret_cast<T*>(p.dab);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = g.r0 + acc_row(mi, v);
+      if (r >= g.r1) continue;
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj) {
+        const int i = n0 + acc_col(nj);
+        if (i >= p.I) continue;
+        const float dh = acc.c[mi][nj][v];
+        const float av = to_f32<T>(ab[(size_t)r * 2 * p.I + i]);
+        const float bv = to_f32<T>(ab[(size_t)r * 2 * p.I + p.I + i]);
+        const float sg = 1.0f / (1.0f + __expf(-av));
+        dab[(size_t)r * 2 * p.I + i] = from_f32<T>(dh * bv * sg * (1.0f + av * (1.0f - sg)));
+        dab[(size_t)r * 2 * p.I + p.I + i] = from_f32<T>(dh * av * sg);
+      }
+    }
+}
+
+// ------------------------------------------------------------------ 3. dx + push
+template <typename T>
+__global__ __launch_bounds__(kGemmThreads) void dx_kernel(BwdPlan p, int ntn) {
+  __shared__ __attribute__((aligned(16))) T smem[TileSmem<T>::BYTES / sizeof(T)];
+  __shared__ int s_prefix[257];
+  const int mtile = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  GroupTile g;
+  if (!find_group_tile(p.offsets, p.E_local, p.R_cap, mtile, s_prefix, &g)) return;
+  const T* dab = reinterpret_cast<const T*>(p.dab);
+  const int n0 = nt * kBN;
+  const T* wg = reinterpret_cast<const T*>(p.wg) + (size_t)g.e * p.I * p.d + n0;
+  const T* wu = reinterpret_cast<const T*>(p.wu) + (size_t)g.e * p.I * p.d + n0;
+  KLoader<T, kBM> la;
+  la.init([&](int row) -> const T* {
+    const int r = g.r0 + row;
+    return r < g.r1 ? dab + (size_t)r * 2 * p.I : nullptr;
+  });
+  MNLoader<T, kBN> lb;
+  lb.init(p.d - n0);
+  auto kptr = [&](int kk) -> const T* {
+    return kk < p.I ? wg + (size_t)kk * p.d : wu + (size_t)(kk - p.I) * p.d;
+  };
+  Acc acc;
+  gemm_mainloop<T>(2 * p.I / MfmaT<T>::BK, la, lb,
+                   [&](int kt, uint4(&r)[KLoader<T, kBM>::NU]) { la.load(kt, r); },
+                   [&](int kt, uint4(&r)[MNLoader<T, kBN>::NU]) { lb.load(kt, kptr, r); }, smem,
+                   acc);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = g.r0 + acc_row(mi, v);
+      if (r >= g.r1) continue;
+      const int n = p.row_src[r];
+      const int tok = n / p.k, j = n % p.k;
+      const int s = tok / p.T_src, t = tok % p.T_src;
+      T* dst = reinterpret_cast<T*>(p.dx_stage.p[s]) + ((size_t)t * p.k + j) * p.d;
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj) {
+        const int c = n0 + acc_col(nj);
+        if (c < p.d) dst[c] = from_f32<T>(acc.c[mi][nj][v]);
+      }
+    }
+}
+
+// ------------------------------------------------------------------ 4. wgrad
+// mode 0: [dW_gate; dW_up][e] (M = 2I, N = d) = dab^T X_e
+// mode 1: dW_down[e]          (M = d,  N = I) = dy^T h_e
+template <typename T, int MODE>
+__global__ __launch_bounds__(kGemmThreads) void wgrad_kernel(BwdPlan p, int mtn, int ntn) {
+  __shared__ __attribute__((aligned(16))) T smem[TileSmem<T>::BYTES / sizeof(T)];
+  const int per = mtn * ntn;
+  const int e = blockIdx.x / per;
+  const int mt = (blockIdx.x % per) / ntn, nt = blockIdx.x % ntn;
+  int off = p.offsets[e], end = p.offsets[e + 1];
+  if (off > p.R_cap) off = p.R_cap;
+  if (end > p.R_cap) end = p.R_cap;
+  const int cnt = end > off ? end - off : 0;
+  const int M = MODE == 0 ? 2 * p.I : p.d;
+  const int N = MODE == 0 ? p.d : p.I;
+  const int m0 = mt * kBM, n0 = nt * kBN;
+  MNLoader<T, kBM> la;
+  MNLoader<T, kBN> lb;
+  la.init(M - m0);
+  lb.init(N - n0);
+  const T* Abase = reinterpret_cast<const T*>(MODE == 0 ? p.dab : p.dy);
+  const int lda = MODE == 0 ? 2 * p.I : p.d;
+  auto aptr = [&](int kk) -> const T* {
+    return kk < cnt ? Abase + (size_t)(off + kk) * lda + m0 : nullptr;
+  };
+  auto bptr = [&](int kk) -> const T* {
+    if (kk >= cnt) return nullptr;
+    if (MODE == 0) {
+      const int n = p.row_src[off + kk];
+      const int tok = n / p.k;
+      const int s = tok / p.T_src, t = tok % p.T_src;
+      return reinterpret_cast<const T*>(p.src_x.p[s]) + (size_t)t * p.d + n0;
+    } else {
+      return reinterpret_cast<const T*>(p.h) + (size_t)(off + kk) * p.I + n0;
+    }
+  };
+  const int BK = MfmaT<T>::BK;
+  Acc acc;
+  gemm_mainloop<T>((cnt + BK - 1) / BK, la, lb,
+                   [&](int kt, uint4(&r)[MNLoader<T, kBM>::NU]) { la.load(kt, aptr, r); },
+                   [&](int kt, uint4(&r)[MNLoader<T, kBN>::NU]) { lb.load(kt, bptr, r); }, smem,
+                   acc);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + acc_row(mi, v);
+      if (m >= M) continue;
+      float* dst;
+      if (MODE == 0)
+        dst = m < p.I ? p.dw_gate + ((size_t)e * p.I + m) * p.d
+                      : p.dw_up + ((size_t)e * p.I + (m - p.I)) * p.d;
+      else
+        dst = p.dw_down + ((size_t)e * p.d + m) * p.I;
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj) {
+        const int c = n0 + acc_col(nj);
+        if (c < N) dst[c] = acc.c[mi][nj][v];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ 5. d_x
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
+  const int64_t gt = blockIdx.x;  // own token index
+  const int s = p.own_lo + (int)(gt / p.T_src);
+  const int t = (int)(gt % p.T_src);
+  const int64_t n0 = ((int64_t)s * p.T_src + t) * p.k;
+  float dz[16];
+  int ex[16];
+  bool loc[16];
+  float m = 0.0f;
+  for (int j = 0; j < p.k; ++j) {
+    loc[j] = p.dest_row[n0 + j] >= 0 && p.dest_row[n0 + j] < p.R_cap;
+    const float dg = loc[j] ? p.d_gate[n0 + j] : 0.0f;
+    dz[j] = dg;
+    m = __builtin_fmaf(p.topk_gate[n0 + j], dg, m);
+    ex[j] = p.topk_idx[n0 + j];
+  }
+  for (int j = 0; j < p.k; ++j) dz[j] = p.topk_gate[n0 + j] * (dz[j] - m);
+  if (threadIdx.x < p.k) p.dz[gt * p.k + threadIdx.x] = dz[threadIdx.x];
+  const T* stg = reinterpret_cast<const T*>(p.dx_stage.p[s]) + (size_t)t * p.k * p.d;
+  const T* wr = reinterpret_cast<const T*>(p.w_router);
+  T* o = reinterpret_cast<T*>(p.d_x.p[s]) + (size_t)t * p.d;
+  constexpr int U = 16 / sizeof(T);
+  for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
+    float acc[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < p.k; ++j) {
+      if (!loc[j]) continue;
+      uint4 v = ld16(stg + (size_t)j * p.d + u * U);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int i = 0; i < U; ++i) acc[i] += to_f32<T>(e[i]);
+    }
+    for (int j = 0; j < p.k; ++j) {
+      uint4 v = ld16(wr + (size_t)ex[j] * p.d + u * U);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz[j], to_f32<T>(e[i]), acc[i]);
+    }
+    uint4 ov;
+    T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+    for (int i = 0; i < U; ++i) oe[i] = from_f32<T>(acc[i]);
+    st16(o + u * U, ov);
+  }
+}
+
+// ------------------------------------------------------------------ 6. dW_router
+// grid: (column blocks of 256, expert groups of 16, kRouterChunks token chunks)
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dwr_part_kernel(BwdPlan p, int64_t n_own, int64_t per) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const int e0 = blockIdx.y * 16;
+  const int64_t ta = (int64_t)blockIdx.z * per;
+  const int64_t tb = ta + per < n_own ? ta + per : n_own;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  const bool col = c < p.d;
+  for (int64_t gt = ta; gt < tb; ++gt) {
+    const int s = p.own_lo + (int)(gt / p.T_src);
+    const int t = (int)(gt % p.T_src);
+    const int64_t n0 = ((int64_t)s * p.T_src + t) * p.k;
+    const float xv = col ? to_f32<T>(reinterpret_cast<const T*>(p.src_x.p[s])[(size_t)t * p.d + c]) : 0.0f;
+    for (int j = 0; j < p.k; ++j) {
+      const int e = p.topk_idx[n0 + j] - e0;
+      const float z = p.dz[gt * p.k + j];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (e == i) acc[i] = __builtin_fmaf(z, xv, acc[i]);
+    }
+  }
+  if (!col) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (e0 + i < p.E)
+      p.dwr_part[((size_t)blockIdx.z * p.E + e0 + i) * p.d + c] = acc[i];
+}
+
+__global__ __launch_bounds__(kThreads) void dwr_reduce_kernel(BwdPlan p, int nchunk) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t tot = (int64_t)p.E * p.d;
+  if (i >= tot) return;
+  float acc = 0.0f;
+  for (int c = 0; c < nchunk; ++c) acc += p.dwr_part[(size_t)c * tot + i];
+  p.dw_router[i] = acc;
+}
+
+template <typename T>
+mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
+  if (p.R_cap > 0) {
+    const int mt = grouped_mtiles_bound(p.R_cap, p.E_local);
+    hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
+    int ntn = (p.I + kBN - 1) / kBN;
+    hipLaunchKernelGGL(dh_kernel<T>, dim3(mt * ntn), dim3(kGemmThreads), 0, stream, p, ntn);
+    ntn = (p.d + kBN - 1) / kBN;
+    hipLaunchKernelGGL(dx_kernel<T>, dim3(mt * ntn), dim3(kGemmThreads), 0, stream, p, ntn);
+  }
+  {
+    int mtn = (2 * p.I + kBM - 1) / kBM, ntn = (p.d + kBN - 1) / kBN;
+    hipLaunchKernelGGL((wgrad_kernel<T, 0>), dim3(p.E_local * mtn * ntn), dim3(kGemmThreads), 0,
+                       stream, p, mtn, ntn);
+    mtn = (p.d + kBM - 1) / kBM;
+    ntn = (p.I + kBN - 1) / kBN;
+    hipLaunchKernelGGL((wgrad_kernel<T, 1>), dim3(p.E_local * mtn * ntn), dim3(kGemmThreads), 0,
+                       stream, p, mtn, ntn);
+  }
+  const int64_t n_own = (int64_t)p.own_n * p.T_src;
+  if (n_own > 0) {
+    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)n_own), dim3(kThreads), 0, stream, p);
+    if (p.dw_router) {
+      const int64_t per = (n_own + kRouterChunks - 1) / kRouterChunks;
+      dim3 g((p.d + kThreads - 1) / kThreads, (p.E + 15) / 16, kRouterChunks);
+      hipLaunchKernelGGL(dwr_part_kernel<T>, g, dim3(kThreads), 0, stream, p, n_own, per);
+      const int64_t tot = (int64_t)p.E * p.d;
+      hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
+                         dim3(kThreads), 0, stream, p, kRouterChunks);
+    }
+  } else if (p.dw_router) {
+    const int64_t tot = (int64_t)p.E * p.d;
+    hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, p, 0);
+  }
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+}  // namespace
+
+mok_status launch_bwd(const BwdPlan& p, hipStream_t stream) {
+  return p.prec == MOK_F32 ? run_bwd<float>(p, stream) : run_bwd<bf16_t>(p, stream);
+}
+
+}  // namespace mok

@@ -1,0 +1,335 @@
+// Data movement kernels: pull dispatch (gather, optionally MX-quantising),
+// push combine, final weighted combine, and the E4M3/E8M0 row quantiser.
+//
+// All of them stream rows with 16-byte vector loads and stores; consecutive
+// lanes touch consecutive 16-byte units of one row, so every wave moves whole
+// 1 KiB spans of HBM.  They are bound by HBM bandwidth.
+#include "mok_internal.h"
+
+namespace mok {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- E4M3 / E8M0
+// floor(log2(v)) of a positive finite fp32 value (subnormals included).
+__device__ __forceinline__ int ilog2f(float v) {
+  uint32_t b = __float_as_uint(v);
+  int ex = (int)((b >> 23) & 0xFF);
+  if (ex != 0) return ex - 127;
+  uint32_t m = b & 0x7FFFFFu;
+  return (31 - __clz((int)m)) - 149;
+}
+
+// Shared exponent of an MX block from its max magnitude (OCP MX v1.0: largest
+// power of two <= amax, divided by 2^8, 8 = largest E4M3 exponent).
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = ilog2f(amax) - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Nearest E4M3 (OCP "fn") code of v, ties to even, saturating at +-448.
+// Normal range: round the fp32 bits to 3 mantissa bits and rebias the
+// exponent (127 -> 7); below 2^-6 the code is the integer v * 2^9.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  uint32_t b = __float_as_uint(v);
+  uint32_t s = (b >> 24) & 0x80u;
+  float a = __uint_as_float(b & 0x7FFFFFFFu);
+  if (a >= 448.0f) return s | 0x7Eu;
+  uint32_t ab = b & 0x7FFFFFFFu;
+  if (ab < 0x3C800000u) {  // a < 2^-6
+    return s | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20;
+  return s | (r - 960u);
+}
+
+// ---------------------------------------------------------------- dispatch
+struct GatherArgs {
+  SrcTable src;          // S pointers [T_src, d]
+  const int32_t* row_src;
+  const int32_t* offsets;
+  void* dst;             // [R_cap, d] (activation dtype or E4M3 codes)
+  uint8_t* dst_scale;    // [R_cap, d/32] for MX
+  int T_src, d, k, E_local, R_cap;
+  int rows_per_block;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
+  int R = a.offsets[a.E_local];
+  if (R > a.R_cap) R = a.R_cap;
+  constexpr int U = 16 / sizeof(T);
+  const int units = a.d / U;
+  const int r0 = blockIdx.x * a.rows_per_block;
+  for (int rr = 0; rr < a.rows_per_block; ++rr) {
+    const int r = r0 + rr;
+    if (r >= R) return;
+    const int n = a.row_src[r];
+    const int tok = n / a.k;
+    const int s = tok / a.T_src, t = tok % a.T_src;
+    const T* src = reinterpret_cast<const T*>(a.src.p[s]) + (size_t)t * a.d;
+    T* dst = reinterpret_cast<T*>(a.dst) + (size_t)r * a.d;
+    for (int u = threadIdx.x; u < units; u += kThreads) st16(dst + u * U, ld16(src + u * U));
+  }
+}
+
+// MX gather: a 32-element block is 4 consecutive 16-byte units (4 lanes).
+__global__ __launch_bounds__(kThreads) void gather_mx_kernel(GatherArgs a) {
+  int R = a.offsets[a.E_local];
+  if (R > a.R_cap) R = a.R_cap;
+  const int units = a.d / 8;
+  const int r0 = blockIdx.x * a.rows_per_block;
+  for (int rr = 0; rr < a.rows_per_block; ++rr) {
+    const int r = r0 + rr;
+    if (r >= R) return;
+    const int n = a.row_src[r];
+    const int tok = n / a.k;
+    const int s = tok / a.T_src, t = tok % a.T_src;
+    const bf16_t* src = reinterpret_cast<const bf16_t*>(a.src.p[s]) + (size_t)t * a.d;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.dst) + (size_t)r * a.d;
+    uint8_t* dsc = a.dst_scale + (size_t)r * (a.d / 32);
+    for (int u0 = 0; u0 < units; u0 += kThreads) {
+      const int u = u0 + threadIdx.x;
+      const bool have = u < units;  // units % 4 == 0: a 4-lane group is all in or all out
+      float v[8];
+      float amax = 0.0f;
+      if (have) {
+        uint4 q = ld16(src + u * 8);
+        uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(w[i] << 16);
+          v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      if (have) {
+        const int sh = mx_shared_exp(amax);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[i], -sh)) << (8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + i], -sh)) << (8 * i);
+        *reinterpret_cast<uint2*>(dst + u * 8) = make_uint2(lo, hi);
+        if ((u & 3) == 0) dsc[u >> 2] = (uint8_t)(sh + 127);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- push combine
+// Item-indexed: every item n with a local row pushes y[dest_row[n]] to its
+// (source, token, slot) staging row.
+struct PushArgs {
+  const void* y;           // [R_cap, d] rows in expert order
+  const int32_t* dest_row; // [N]
+  DstTable staging;        // S pointers [T_src*k, d]
+  int64_t N;
+  int T_src, d, k, R_cap;
+  int items_per_block;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void push_kernel(PushArgs a) {
+  constexpr int U = 16 / sizeof(T);
+  const int units = a.d / U;
+  for (int q = 0; q < a.items_per_block; ++q) {
+    const int64_t n = (int64_t)blockIdx.x * a.items_per_block + q;
+    if (n >= a.N) return;
+    const int r = a.dest_row[n];
+    if (r < 0 || r >= a.R_cap) continue;
+    const int64_t tok = n / a.k;
+    const int j = (int)(n % a.k);
+    const int s = (int)(tok / a.T_src), t = (int)(tok % a.T_src);
+    const T* src = reinterpret_cast<const T*>(a.y) + (size_t)r * a.d;
+    T* dst = reinterpret_cast<T*>(a.staging.p[s]) + ((size_t)t * a.k + j) * a.d;
+    for (int u = threadIdx.x; u < units; u += kThreads) st16(dst + u * U, ld16(src + u * U));
+  }
+}
+
+// ---------------------------------------------------------------- final combine
+struct CombineArgs {
+  const int32_t* dest_row;  // [S*T_src*k]
+  const float* gate;        // [S*T_src*k]
+  DstTable staging;         // S pointers [T_src*k, d]
+  DstTable out;             // S pointers [T_src, d]
+  int T_src, d, k, own_lo, R_cap;
+  int64_t n_tok;            // own tokens
+  int tok_per_block;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  constexpr int U = 16 / sizeof(T);
+  const int units = a.d / U;
+  for (int q = 0; q < a.tok_per_block; ++q) {
+    const int64_t g = (int64_t)blockIdx.x * a.tok_per_block + q;
+    if (g >= a.n_tok) return;
+    const int s = a.own_lo + (int)(g / a.T_src);
+    const int t = (int)(g % a.T_src);
+    const int64_t n0 = ((int64_t)s * a.T_src + t) * a.k;
+    const T* stg = reinterpret_cast<const T*>(a.staging.p[s]) + (size_t)t * a.k * a.d;
+    T* o = reinterpret_cast<T*>(a.out.p[s]) + (size_t)t * a.d;
+    for (int u = threadIdx.x; u < units; u += kThreads) {
+      float acc[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < a.k; ++j) {
+        const int row = a.dest_row[n0 + j];
+        if (row < 0 || row >= a.R_cap) continue;
+        const float gj = a.gate[n0 + j];
+        uint4 v = ld16(stg + (size_t)j * a.d + u * U);
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(gj, to_f32<T>(e[i]), acc[i]);
+      }
+      uint4 outv;
+      T* ov = reinterpret_cast<T*>(&outv);
+#pragma unroll
+      for (int i = 0; i < U; ++i) ov[i] = from_f32<T>(acc[i]);
+      st16(o + u * U, outv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MX rows
+struct MxArgs {
+  const bf16_t* src;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t rows, K;
+};
+
+__global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
+  // one 16-byte unit (8 values) per thread; 4 threads per 32-value block
+  const int64_t units = a.rows * (a.K / 8);
+  for (int64_t u0 = (int64_t)blockIdx.x * kThreads; u0 < units; u0 += (int64_t)gridDim.x * kThreads) {
+    const int64_t u = u0 + threadIdx.x;
+    const bool have = u < units;  // units % 4 == 0 and u0 % 4 == 0
+    float v[8];
+    float amax = 0.0f;
+    if (have) {
+      uint4 q = ld16(a.src + u * 8);
+      uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    if (have) {
+      const int sh = mx_shared_exp(amax);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[i], -sh)) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + i], -sh)) << (8 * i);
+      *reinterpret_cast<uint2*>(a.codes + u * 8) = make_uint2(lo, hi);
+      if ((u & 3) == 0) a.scales[u >> 2] = (uint8_t)(sh + 127);
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+mok_status launch_gather(int prec, const SrcTable& src, int T_src, int d, int k, int E_local,
+                         int R_cap, const int32_t* row_src, const int32_t* offsets, void* dst,
+                         uint8_t* dst_scale, hipStream_t stream) {
+  if (R_cap == 0) return MOK_OK;
+  GatherArgs a;
+  a.src = src;
+  a.row_src = row_src;
+  a.offsets = offsets;
+  a.dst = dst;
+  a.dst_scale = dst_scale;
+  a.T_src = T_src;
+  a.d = d;
+  a.k = k;
+  a.E_local = E_local;
+  a.R_cap = R_cap;
+  a.rows_per_block = 4;
+  dim3 grid((R_cap + a.rows_per_block - 1) / a.rows_per_block);
+  if (prec == MOK_F32)
+    hipLaunchKernelGGL(gather_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+  else if (prec == MOK_BF16)
+    hipLaunchKernelGGL(gather_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gather_mx_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_push(int prec, const void* y, const int32_t* dest_row, int64_t N,
+                       const DstTable& staging, int T_src, int d, int k, int R_cap,
+                       hipStream_t stream) {
+  if (N == 0) return MOK_OK;
+  PushArgs a;
+  a.y = y;
+  a.dest_row = dest_row;
+  a.staging = staging;
+  a.N = N;
+  a.T_src = T_src;
+  a.d = d;
+  a.k = k;
+  a.R_cap = R_cap;
+  a.items_per_block = 4;
+  dim3 grid((unsigned)((N + a.items_per_block - 1) / a.items_per_block));
+  if (prec == MOK_F32)
+    hipLaunchKernelGGL(push_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(push_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
+                          const DstTable& staging, const DstTable& out, int T_src, int d, int k,
+                          int own_lo, int own_n, int R_cap, hipStream_t stream) {
+  CombineArgs a;
+  a.dest_row = dest_row;
+  a.gate = gate;
+  a.staging = staging;
+  a.out = out;
+  a.T_src = T_src;
+  a.d = d;
+  a.k = k;
+  a.own_lo = own_lo;
+  a.R_cap = R_cap;
+  a.n_tok = (int64_t)own_n * T_src;
+  a.tok_per_block = 2;
+  if (a.n_tok == 0) return MOK_OK;
+  dim3 grid((unsigned)((a.n_tok + a.tok_per_block - 1) / a.tok_per_block));
+  if (prec == MOK_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
+  MxArgs a;
+  a.src = reinterpret_cast<const bf16_t*>(src);
+  a.codes = codes;
+  a.scales = scales;
+  a.rows = rows;
+  a.K = K;
+  int64_t units = rows * (K / 8);
+  if (units == 0) return MOK_OK;
+  int64_t blocks = (units + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(mx_quantize_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+}  // namespace mok

@@ -1,0 +1,124 @@
+"""Device buffers of one MoE layer instance, allocated with torch.
+
+``MoELayer`` owns the caller-side memory the C ABI expects (configuration,
+weights, forward state, staging rows, outputs, gradients, workspace, device
+status word) and calls ``mok_layer_fwd`` / ``mok_layer_bwd``.  It does no
+arithmetic of its own.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import (MAX_SOURCES, make_config, make_state, make_weights, mok_layer_bwd, mok_layer_fwd,
+               mok_mx_quantize, mok_workspace_bytes, STATUS)
+
+
+def _dt(prec: str):
+    return torch.float32 if prec == "f32" else torch.bfloat16
+
+
+def to_device(a: np.ndarray, prec: str, device) -> torch.Tensor:
+    """Storage array from the input generator (fp32 values or bf16 bits) -> device tensor."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class MoELayer:
+    def __init__(self, S, T_src, d, E, k, I, E_local, prec, R_cap, own_lo, own_n, device="cuda",
+                 ring_bytes=0, minibatch_rows=256, comm_wgs=0, gemm_wgs=0, with_bwd=True):
+        assert S <= MAX_SOURCES
+        self.S, self.T_src, self.d, self.E, self.k, self.I = S, T_src, d, E, k, I
+        self.E_local, self.prec, self.R_cap = E_local, prec, R_cap
+        self.own_lo, self.own_n = own_lo, own_n
+        self.device = torch.device(device)
+        self.cfg = make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows,
+                               ring_bytes, comm_wgs, gemm_wgs)
+        dev = self.device
+        act = _dt(prec)
+        N = S * T_src * k
+        self.topk_idx = torch.zeros(N, dtype=torch.int32, device=dev)
+        self.topk_gate = torch.zeros(N, dtype=torch.float32, device=dev)
+        self.counts = torch.zeros(E_local, dtype=torch.int32, device=dev)
+        self.offsets = torch.zeros(E_local + 1, dtype=torch.int32, device=dev)
+        self.row_src = torch.zeros(max(R_cap, 1), dtype=torch.int32, device=dev)
+        self.dest_row = torch.zeros(max(N, 1), dtype=torch.int32, device=dev)
+        if prec == "mxfp8":
+            self.h = torch.zeros(max(R_cap, 1) * I, dtype=torch.uint8, device=dev)
+        else:
+            self.h = torch.zeros(max(R_cap, 1), I, dtype=act, device=dev)
+        self.ab = torch.zeros(max(R_cap, 1), 2 * I, dtype=act, device=dev) if with_bwd or prec != "mxfp8" else None
+        out_dt = torch.float32 if prec == "f32" else torch.bfloat16
+        self.staging = [torch.zeros(T_src * k, d, dtype=out_dt, device=dev) for _ in range(S)]
+        self.out = [torch.zeros(T_src, d, dtype=out_dt, device=dev) if own_lo <= s < own_lo + own_n
+                    else None for s in range(S)]
+        self.ws = torch.zeros(max(mok_workspace_bytes(self.cfg), 256), dtype=torch.uint8,
+                              device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.state = make_state(self.topk_idx, self.topk_gate, self.counts, self.offsets,
+                                self.row_src, self.dest_row, self.h, self.ab)
+        self.with_bwd = with_bwd
+        if with_bwd and prec != "mxfp8":
+            self.d_gate = torch.zeros(N, dtype=torch.float32, device=dev)
+            self.dx_stage = [torch.zeros(T_src * k, d, dtype=act, device=dev) for _ in range(S)]
+            self.d_x = [torch.zeros(T_src, d, dtype=act, device=dev) if own_lo <= s < own_lo + own_n
+                        else None for s in range(S)]
+            self.dw_gate = torch.zeros(E_local, I, d, dtype=torch.float32, device=dev)
+            self.dw_up = torch.zeros(E_local, I, d, dtype=torch.float32, device=dev)
+            self.dw_down = torch.zeros(E_local, d, I, dtype=torch.float32, device=dev)
+            self.dw_router = torch.zeros(E, d, dtype=torch.float32, device=dev)
+
+    # ---------------------------------------------------------------- inputs
+    def set_inputs(self, xs: List[torch.Tensor], w_router, bias, e2l, w_gate, w_up, w_down,
+                   other_topk: Optional[List] = None):
+        """xs: S device tensors [T_src, d]; other_topk: per non-own source
+        (topk_idx [T_src, k] int32, topk_gate [T_src, k] fp32) numpy arrays."""
+        self.xs = xs
+        self.w_router = w_router
+        self.bias = bias
+        self.e2l = e2l
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        per = self.T_src * self.k
+        for s in range(self.S):
+            if self.own_lo <= s < self.own_lo + self.own_n:
+                continue
+            idx, g = other_topk[s]
+            self.topk_idx[s * per:(s + 1) * per] = torch.from_numpy(idx.reshape(-1)).to(self.device)
+            self.topk_gate[s * per:(s + 1) * per] = torch.from_numpy(g.reshape(-1)).to(self.device)
+        if self.prec == "mxfp8":
+            self._quantize_weights()
+        else:
+            self.weights = make_weights(w_gate, w_up, w_down)
+
+    def _quantize_weights(self):
+        """MX-quantise the expert weights once (off the timed path)."""
+        q = []
+        for w in (self.w_gate, self.w_up, self.w_down):
+            rows = w.numel() // w.shape[-1]
+            K = w.shape[-1]
+            codes = torch.empty(w.numel(), dtype=torch.uint8, device=self.device)
+            scales = torch.empty(w.numel() // 32, dtype=torch.uint8, device=self.device)
+            mok_mx_quantize(rows, K, w, codes, scales)
+            q.append((codes, scales))
+        self.wq = q
+        self.weights = make_weights(q[0][0], q[1][0], q[2][0], q[0][1], q[1][1], q[2][1])
+
+    # ---------------------------------------------------------------- passes
+    def forward(self, stream=None):
+        mok_layer_fwd(self.cfg, self.own_lo, self.own_n, self.xs, self.w_router, self.bias,
+                      self.e2l, self.weights, self.state, self.staging, self.out, self.ws,
+                      self.status, stream)
+
+    def backward(self, d_out: List[torch.Tensor], stream=None, router_grad=True):
+        mok_layer_bwd(self.cfg, self.own_lo, self.own_n, d_out, self.xs, self.w_router, self.e2l,
+                      self.weights, self.state, self.staging, self.d_gate, self.dx_stage, self.d_x,
+                      self.dw_gate, self.dw_up, self.dw_down,
+                      self.dw_router if router_grad else None, self.ws, self.status, stream)
+
+    def check_status(self):
+        st = int(self.status.item())
+        if st != 0:
+            raise RuntimeError(f"device status {STATUS.get(st, st)}")

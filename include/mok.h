@@ -1,0 +1,234 @@
+/*
+ * mok.h -- C ABI of the MI355X (gfx950) fused MoE layer: route -> expert-
+ * contiguous layout -> gather (pull dispatch) -> SwiGLU expert grouped GEMM ->
+ * gate-weighted combine, forward and backward, deterministic.
+ *
+ * The operations follow the Mixture-of-Kittens write-ups:
+ *   [K01] LeFeng.com article on kucoin.com, section 01 ("the communication tax
+ *         of MoE"): the router picks a few experts per token; the system counts
+ *         the tokens of each expert, decides where they go and groups each
+ *         expert's tokens together so that a grouped GEMM gets ordered input;
+ *         dispatch and combine in the forward pass, two more rounds in reverse
+ *         in the backward pass.
+ *   [K02] same article, section 02: pull dispatch (the receiver only needs to
+ *         know which source holds a token and where, and chooses its own
+ *         placement, ordered by local expert), push combine, pull
+ *         reverse-combine and push reverse-dispatch; a fixed-size ring token
+ *         buffer whose slots are reused as soon as compute and combine are
+ *         done; a minibatch size; SMs split between communication and compute
+ *         sides that hand off through on-GPU counters; MXFP8 quantisation fused
+ *         into the dispatch, grouped-GEMM and SwiGLU data paths.
+ *   [K03] same article, section 03: the measured layer consists of scheduling,
+ *         routing, the expert FFN, the combine and the final weighted combine.
+ *   [M-P] miku-ai.ru article, section "Производительность и масштабируемость":
+ *         identical inputs give bit-identical results.
+ *
+ * Conventions for every entry point
+ *   - Memory: the caller owns every buffer (device memory unless stated).
+ *     The library allocates and frees nothing, keeps no global mutable state
+ *     and never synchronises the host with the device.
+ *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and runs asynchronously.
+ *   - Errors: invalid arguments are rejected before anything is enqueued with
+ *     a negative mok_status.  Conditions that only the device can see (more
+ *     routed rows than R_cap, an expert id out of range, a bounded wait that
+ *     timed out) are latched into `*dev_status` (a device int32 the caller
+ *     zeroes; the first error code written wins) and the affected kernels skip
+ *     the offending work instead of writing out of bounds.
+ *   - Sizes that depend on routing (rows per expert, R) stay on the device;
+ *     the host passes capacities only.
+ *   - Layout: all matrices are row-major.  Expert weights are stored with the
+ *     contraction dimension innermost for the forward pass: W_gate, W_up are
+ *     [E_local, I, d], W_down is [E_local, d, I].
+ *   - Determinism: every reduction runs in a fixed order; no floating-point
+ *     atomics.  Two runs give bit-identical outputs.
+ *   - Source buffers: S simulated source ranks, each a separate device buffer
+ *     of T_src tokens, passed as a host array of S device pointers (up to
+ *     MOK_MAX_SOURCES).  Item n = (s * T_src + t) * k + j names slot j of
+ *     token t of source s.
+ */
+#ifndef MOK_H
+#define MOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOK_MAX_SOURCES 64
+#define MOK_MX_BLOCK 32
+
+typedef enum {
+  MOK_OK = 0,
+  MOK_EINVAL = -1,     /* null pointer, bad size, unsupported combination */
+  MOK_ESHAPE = -2,     /* shape constraint violated (e.g. d % 32 for MXFP8) */
+  MOK_EDEVICE = -3,    /* HIP runtime error at launch */
+  MOK_ECAPACITY = -4,  /* device-latched: routed rows exceed R_cap */
+  MOK_ETIMEOUT = -5,   /* device-latched: a bounded wait in the fused kernel ran out */
+  MOK_EROUTE = -6      /* device-latched: an expert id outside [0, E) in routing input */
+} mok_status;
+
+typedef enum {
+  MOK_F32 = 0,   /* fp32 tokens, weights, outputs; fp32 GEMMs */
+  MOK_BF16 = 1,  /* bf16 tokens, weights, outputs; bf16 MFMA with fp32 accumulation */
+  MOK_MXFP8 = 2  /* bf16 tokens/outputs in HBM; E4M3 elements + one E8M0 scale per 32
+                    along the contraction dim inside the expert GEMMs */
+} mok_prec;
+
+typedef struct mok_config {
+  int32_t S;              /* source token buffers (simulated source ranks), 1..MOK_MAX_SOURCES */
+  int32_t T_src;          /* tokens per source buffer */
+  int32_t d;              /* hidden size (multiple of 8; of 32 for MXFP8) */
+  int32_t E;              /* experts in the layer */
+  int32_t k;              /* experts chosen per token, 1..min(E, 8) */
+  int32_t I;              /* SwiGLU intermediate size per expert (multiple of 8; of 32 for MXFP8) */
+  int32_t E_local;        /* experts whose FFN runs on this GPU, 1..256 */
+  int32_t prec;           /* mok_prec */
+  int32_t R_cap;          /* row capacity of every routed-row buffer */
+  int32_t minibatch_rows; /* fused path: at most this many rows of one expert per minibatch */
+  int64_t ring_bytes;     /* fused path: bytes of the ring of token slots; 0 = staged path */
+  int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = auto) */
+  int32_t gemm_wgs;       /* fused path: grouped-GEMM workgroups (0 = auto) */
+} mok_config;
+
+/* Expert weights of the E_local local experts (see Layout above).  For
+ * MOK_MXFP8 the three matrices hold E4M3 codes (uint8, same shapes) and
+ * s_gate, s_up, s_down their E8M0 scales ([E_local, I, d/32] and
+ * [E_local, d, I/32]); otherwise the s_* pointers are NULL. */
+typedef struct mok_expert_weights {
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const uint8_t* s_gate;
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+} mok_expert_weights;
+
+/* State the forward pass leaves for the backward pass (all caller-owned). */
+typedef struct mok_fwd_state {
+  int32_t* topk_idx;   /* [S*T_src*k]: in for non-own sources, out for own sources */
+  float* topk_gate;    /* [S*T_src*k] fp32, same split */
+  int32_t* counts;     /* [E_local] routed rows per local expert */
+  int32_t* offsets;    /* [E_local+1] exclusive scan of counts; offsets[E_local] = R */
+  int32_t* row_src;    /* [R_cap] row -> item n */
+  int32_t* dest_row;   /* [S*T_src*k] item n -> row, -1 for remote experts */
+  void* h;             /* [R_cap, I] SwiGLU output in the activation dtype (bf16 / f32) */
+  void* ab;            /* [R_cap, 2I] pre-activation a | b in the activation dtype, or NULL */
+} mok_fwd_state;
+
+/* Bytes of device workspace the calls below need for `cfg` (256-byte aligned
+ * pointer expected).  Covers layout scratch, gathered rows, intermediates of
+ * the backward pass and, when cfg->ring_bytes > 0, the ring and its counters. */
+size_t mok_workspace_bytes(const mok_config* cfg);
+
+/* Router [K01 router; K03 routing].  For T tokens x [T, d] (fp32 for MOK_F32,
+ * else bf16) and router weights w_router [E, d] (same dtype), bias [E] fp32 or
+ * NULL:  z[t][e] = fp32 chain (z = 0; for i ascending z = fma(x_i, w_i, z))
+ * then z += bias[e];  topk_idx[t][0..k) = the k largest z, ties to the lower
+ * expert id, slot 0 largest;  topk_gate[t][j] = softmax over all E experts
+ * renormalised over the chosen k (= softmax of the chosen logits), fp32. */
+mok_status mok_route(const mok_config* cfg, int32_t T, const void* x, const void* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_gate, void* stream);
+
+/* Expert-contiguous layout [K01 count / place / group; K02 receiver-chosen
+ * placement ordered by local expert].  Input: routing of all S sources
+ * topk_idx_all [S*T_src*k] and expert_to_local [E] (local index, -1 remote).
+ * Output: counts [E_local], offsets [E_local+1], row_src [R_cap] (row -> n),
+ * dest_row [S*T_src*k] (n -> row or -1).  Rows of an expert are in ascending
+ * n (a stable counting sort).  R > R_cap latches MOK_ECAPACITY (rows past
+ * R_cap are not written); a bad expert id latches MOK_EROUTE.  ws: workspace. */
+mok_status mok_layout(const mok_config* cfg, const int32_t* topk_idx_all,
+                      const int32_t* expert_to_local, int32_t* counts, int32_t* offsets,
+                      int32_t* row_src, int32_t* dest_row, void* ws, int32_t* dev_status,
+                      void* stream);
+
+/* Pull dispatch [K02 pull dispatch]: x_perm[r] = src_x[s][t] for every routed
+ * row r < R (n = row_src[r]).  src_x: host array of S device pointers, each
+ * [T_src, d] in the activation dtype.  x_perm: [R_cap, d] activation dtype, or
+ * for MOK_MXFP8 [R_cap, d] E4M3 codes with x_scale [R_cap, d/32] E8M0 (the
+ * quantisation is fused into the gather [K02 MXFP8]); x_scale NULL otherwise. */
+mok_status mok_dispatch(const mok_config* cfg, const void* const* src_x, const int32_t* row_src,
+                        const int32_t* offsets, void* x_perm, uint8_t* x_scale,
+                        int32_t* dev_status, void* stream);
+
+/* Expert FFN as grouped GEMMs [K01 grouped GEMM; K02 SwiGLU]: for each local
+ * expert e and its rows [offsets[e], offsets[e+1]):
+ *   a = x W_gate[e]^T, b = x W_up[e]^T (fp32 accumulation); h = silu(a) * b;
+ *   y = h W_down[e]^T.
+ * h [R_cap, I] (activation dtype; for MOK_MXFP8 h_scale [R_cap, I/32] holds
+ * its scales and h its E4M3 codes, quantised from fp32 in the GEMM epilogue),
+ * ab [R_cap, 2I] a | b (activation dtype) or NULL, y [R_cap, d] (activation
+ * dtype; bf16 for MOK_MXFP8). */
+mok_status mok_expert_ffn(const mok_config* cfg, const void* x_perm, const uint8_t* x_scale,
+                          const int32_t* offsets, const mok_expert_weights* w, void* h,
+                          uint8_t* h_scale, void* ab, void* y, int32_t* dev_status, void* stream);
+
+/* Push combine + final weighted combine [K02 push combine; K03 final weighted
+ * combine].  Push: staging[s][t*k+j] = y[dest_row[n]] for every routed item
+ * (staging: host array of S device pointers, each [T_src*k, d] activation
+ * dtype; rows of remote items are not written).  Final combine for the own
+ * sources s in [own_lo, own_lo+own_n):  out[s][t] = sum over j ascending with
+ * dest_row[n] >= 0 of topk_gate[n] * staging[s][t*k+j], fp32, rounded once.
+ * out: host array of S device pointers ([T_src, d]); only own entries used.
+ * y may be NULL to skip the push (staging already filled). */
+mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest_row,
+                       const float* topk_gate, void* const* staging, int32_t own_lo,
+                       int32_t own_n, void* const* out, int32_t* dev_status, void* stream);
+
+/* Whole forward pass of the layer on this GPU's share.  Routes the own
+ * sources [own_lo, own_lo+own_n) (their topk written into st->topk_idx /
+ * st->topk_gate; the other sources' routing is read from there), builds the
+ * layout, gathers, runs the expert FFN, pushes every local row to `staging`
+ * and final-combines the own sources into `out`.  With cfg->ring_bytes == 0
+ * the steps run as separate kernels; with ring_bytes > 0 the gather, the FFN
+ * and the push run in one persistent kernel whose workgroups are split into
+ * dispatch/combine and grouped-GEMM roles handing minibatches over through a
+ * fixed ring of expert-contiguous slots and device-scope counters [K02].
+ * Results are bit-identical between the two paths, across ring sizes and
+ * minibatch sizes. */
+mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                         const void* const* src_x, const void* w_router, const float* bias,
+                         const int32_t* expert_to_local, const mok_expert_weights* w,
+                         const mok_fwd_state* st, void* const* staging, void* const* out,
+                         void* ws, int32_t* dev_status, void* stream);
+
+/* Backward pass [K01 two more rounds in reverse; K02 pull reverse-combine and
+ * push reverse-dispatch].  Inputs: d_out (host array of S device pointers
+ * [T_src, d], the upstream gradient; sources whose rows are routed here are
+ * read), src_x, w_router, expert_to_local, the weights, the forward state and
+ * `staging` as the forward pass left them.  Outputs:
+ *   d_gate [S*T_src*k] fp32: dL/dg for every local item (others untouched);
+ *   dx_stage (host array of S device pointers [T_src*k, d], activation
+ *     dtype): the pushed input gradient of every local row;
+ *   d_x (host array of S pointers [T_src, d]): for own sources, the sum over
+ *     local slots of dx_stage plus the router path sum_j dz_j w_router[e_j],
+ *     dz_j = g_j (dg_j - sum_i g_i dg_i);
+ *   dw_gate, dw_up [E_local, I, d], dw_down [E_local, d, I] fp32 (overwritten);
+ *   dw_router [E, d] fp32 over the own tokens (overwritten), or NULL.
+ * Only MOK_F32 and MOK_BF16 are supported (MOK_EINVAL otherwise). */
+mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                         const void* const* d_out, const void* const* src_x,
+                         const void* w_router, const int32_t* expert_to_local,
+                         const mok_expert_weights* w, const mok_fwd_state* st,
+                         void* const* staging, float* d_gate, void* const* dx_stage,
+                         void* const* d_x, float* dw_gate, float* dw_up, float* dw_down,
+                         float* dw_router, void* ws, int32_t* dev_status, void* stream);
+
+/* MX quantisation of rows of bf16 values (weight preparation off the timed
+ * path, and the same codec as the fused activation paths):  src [rows, K]
+ * bf16 (K % 32 == 0) -> codes [rows, K] E4M3, scales [rows, K/32] E8M0.
+ * Per block of 32: shared = clamp(floor(log2 max|v|) - 8, -127, 127) (-127 for
+ * an all-zero block), scale byte = shared + 127, code = E4M3 of v / 2^shared,
+ * nearest, ties to even, saturating at +-448 (OCP Microscaling v1.0). */
+mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
+                           uint8_t* scales, void* stream);
+
+/* Library version string (static storage). */
+const char* mok_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOK_H */

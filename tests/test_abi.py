@@ -1,0 +1,68 @@
+"""The C-ABI library loads, exports every symbol include/mok.h declares, and
+rejects invalid arguments on the host (no GPU work is enqueued here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_router_top_expert_amd as mok
+from combine_router_top_expert_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mok.LIB_PATH):
+        build.build()
+    return mok.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mok.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|mok_status)\s+(mok_\w+)\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == set(mok.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version(L):
+    assert mok.mok_version().startswith("mok ")
+
+
+def _cfg(**kw):
+    base = dict(S=2, T_src=100, d=256, E=8, k=2, I=128, E_local=8, prec="bf16", R_cap=400)
+    base.update(kw)
+    return mok.make_config(**base)
+
+
+def test_workspace_bytes_host_logic(L):
+    a = mok.mok_workspace_bytes(_cfg())
+    b = mok.mok_workspace_bytes(_cfg(R_cap=4000))
+    assert a > 0 and b > a
+    assert mok.mok_workspace_bytes(_cfg(d=100)) == 0       # d % 64 != 0
+    assert mok.mok_workspace_bytes(_cfg(k=9)) == 0         # k > E
+    assert mok.mok_workspace_bytes(_cfg(S=65)) == 0        # too many sources
+
+
+@pytest.mark.parametrize("bad", [dict(d=96), dict(I=100), dict(E=0), dict(k=0), dict(E_local=9),
+                                 dict(prec=7), dict(R_cap=-1), dict(S=0)])
+def test_invalid_config_rejected_before_any_launch(L, bad):
+    cfg = _cfg(**bad)
+    rc = L.mok_route(ctypes.byref(cfg), 10, 1, 1, None, 1, 1, None)
+    assert rc == -1
+    rc = L.mok_layout(ctypes.byref(cfg), 1, 1, 1, 1, 1, 1, 1, None, None)
+    assert rc == -1
+
+
+def test_null_pointers_rejected(L):
+    cfg = _cfg()
+    assert L.mok_route(ctypes.byref(cfg), 10, None, 1, None, 1, 1, None) == -1
+    assert L.mok_layout(ctypes.byref(cfg), None, 1, 1, 1, 1, 1, 1, None, None) == -1
+    assert L.mok_mx_quantize(4, 48, 1, 1, 1, None) == -1       # K % 32 != 0
+    assert L.mok_combine(ctypes.byref(cfg), None, 1, 1, None, 0, 3, None, None, None) == -1

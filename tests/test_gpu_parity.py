@@ -1,0 +1,363 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Bit-exact: routing indices, counts, offsets, row_src, dest_row, gathered
+rows, MX codes.  Floating point: max|err| / max|ref| <= 1e-2 (fp32, bf16) and
+2e-2 (MXFP8 against the MX-emulating oracle); gates within 2e-6."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cases import make_host_case, oracle_fwd_tokens, rel_err, sample_tokens
+from combine_router_top_expert_amd import (STATUS, make_config, make_weights, mok_combine,
+                                           mok_dispatch, mok_expert_ffn, mok_layout,
+                                           mok_mx_quantize, mok_route, mok_workspace_bytes, synth)
+from combine_router_top_expert_amd.layer import MoELayer, to_device
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 1e-2, "bf16": 1e-2, "mxfp8": 2e-2}
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _layer(c, R_cap=None, with_bwd=True, **kw):
+    w = c.w
+    L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap or c.R_cap(),
+                 own_lo=w.own[0], own_n=len(w.own), device=DEV, with_bwd=with_bwd, **kw)
+    xs = [to_device(a, w.prec, DEV) for a in c.x_store]
+    bias = None if c.bias is None else torch.from_numpy(c.bias).to(DEV)
+    L.set_inputs(xs, to_device(c.wr_store, w.prec, DEV), bias, torch.from_numpy(c.e2l).to(DEV),
+                 to_device(c.wg_store, w.prec, DEV), to_device(c.wu_store, w.prec, DEV),
+                 to_device(c.wd_store, w.prec, DEV), other_topk=c.other)
+    return L
+
+
+def _small(name, **kw):
+    return synth.WORKLOADS[name].replace(**kw)
+
+
+ROUTE_CASES = {
+    "c1": synth.WORKLOADS["C1"],
+    "e1k1": _small("C2", S=1, T_src=70, d=128, E=1, k=1, I=64, own=[0], local_experts=[0]),
+    "e3k2": _small("C2", S=1, T_src=129, d=64, E=3, k=2, I=64, own=[0], local_experts=[0, 1, 2]),
+    "c2shape": _small("C2", S=1, T_src=1000, own=[0]),
+    "c3shape": _small("C3", S=1, T_src=100, own=[0], local_experts=[0]),
+    "e512k16": _small("C2", S=1, T_src=33, d=256, E=512, k=16, I=64, own=[0], local_experts=[0]),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_CASES))
+def test_route_bit_exact(name):
+    w = ROUTE_CASES[name]
+    _log("route", name, w.T_src, w.d, w.E, w.k)
+    xs, xv = synth.gen_x(w, 0)
+    wr, wrv = synth.gen_router(w)
+    bias = synth.load_bias(w) if w.zipf_s else None
+    if name == "c3shape":
+        bias = synth.load_bias(synth.WORKLOADS["C3"])
+    ref_idx, ref_g = oracle.route(xv, wrv, bias, w.k, w.prec)
+    cfg = make_config(1, w.T_src, w.d, w.E, w.k, w.I, 1, w.prec, 1)
+    x = to_device(xs, w.prec, DEV)
+    wrd = to_device(wr, w.prec, DEV)
+    b = None if bias is None else torch.from_numpy(bias).to(DEV)
+    idx = torch.full((w.T_src, w.k), -1, dtype=torch.int32, device=DEV)
+    g = torch.zeros((w.T_src, w.k), dtype=torch.float32, device=DEV)
+    mok_route(cfg, w.T_src, x, wrd, b, idx, g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(g.cpu().numpy(), ref_g, atol=2e-6, rtol=0)
+
+
+LAYOUT_CASES = {
+    "c2": (synth.WORKLOADS["C2"], None),
+    "c3": (synth.WORKLOADS["C3"], None),
+    "tiny": (_small("C2", S=1, T_src=1, d=64, E=4, k=2, I=64, own=[0], local_experts=[2, 0]), None),
+    "ragged": (_small("C2", S=3, T_src=999, d=64, E=40, k=5, I=64, own=[0],
+                      local_experts=list(range(0, 40, 3))), None),
+    "e256": (_small("C2", S=2, T_src=3000, d=64, E=256, k=8, I=64, own=[0],
+                    local_experts=list(range(256))), None),
+}
+
+
+@pytest.mark.parametrize("name", list(LAYOUT_CASES))
+def test_layout_bit_exact(name):
+    w, _ = LAYOUT_CASES[name]
+    _log("layout", name, w.S, w.T_src, w.k, w.E, w.E_local)
+    topk = np.stack([synth.gen_other_routing(w.replace(own=[]), s)[0] for s in range(w.S)])
+    e2l = w.expert_to_local()
+    ref = oracle.layout(topk, e2l, w.E_local)
+    R_cap = max(ref["R"], 1)
+    cfg = make_config(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap)
+    ws = torch.zeros(mok_workspace_bytes(cfg), dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros(w.E_local, dtype=torch.int32, device=DEV)
+    offsets = torch.zeros(w.E_local + 1, dtype=torch.int32, device=DEV)
+    row_src = torch.full((R_cap,), -7, dtype=torch.int32, device=DEV)
+    dest_row = torch.full((topk.size,), -7, dtype=torch.int32, device=DEV)
+    mok_layout(cfg, torch.from_numpy(topk.reshape(-1)).to(DEV), torch.from_numpy(e2l).to(DEV),
+               counts, offsets, row_src, dest_row, ws, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(row_src.cpu().numpy()[:ref["R"]], ref["row_src"])
+    np.testing.assert_array_equal(dest_row.cpu().numpy(), ref["dest_row"])
+
+
+def test_layout_errors_latched():
+    w = _small("C2", S=1, T_src=50, d=64, E=4, k=2, I=64, own=[0], local_experts=[0, 1, 2, 3])
+    topk = synth.gen_other_routing(w.replace(own=[]), 0)[0]
+    e2l = w.expert_to_local()
+    for R_cap, bad, expect in ((99, False, "MOK_ECAPACITY"), (100, True, "MOK_EROUTE")):
+        _log("layout error", expect)
+        t = topk.copy()
+        if bad:
+            t[7, 1] = 9
+        cfg = make_config(1, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap)
+        ws = torch.zeros(mok_workspace_bytes(cfg), dtype=torch.uint8, device=DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        counts = torch.zeros(4, dtype=torch.int32, device=DEV)
+        offsets = torch.zeros(5, dtype=torch.int32, device=DEV)
+        row_src = torch.zeros(R_cap, dtype=torch.int32, device=DEV)
+        dest_row = torch.zeros(t.size, dtype=torch.int32, device=DEV)
+        mok_layout(cfg, torch.from_numpy(t.reshape(-1)).to(DEV), torch.from_numpy(e2l).to(DEV),
+                   counts, offsets, row_src, dest_row, ws, st)
+        torch.cuda.synchronize()
+        assert STATUS[int(st.item())] == expect
+        rs = row_src.cpu().numpy()
+        assert rs.min() >= 0 and rs.max() < t.size   # nothing written out of range
+
+
+def test_dispatch_tagged_rows_and_identity_combine():
+    """Rows tagged with their (source, token) come back exactly where row_src
+    says; combining the gathered rows with identity experts gives sum_j g_j x."""
+    w = _small("C2", S=3, T_src=301, d=256, E=16, k=4, I=64, own=[1],
+               local_experts=[1, 4, 7, 10, 13, 2])
+    _log("dispatch", w.S, w.T_src)
+    rng = np.random.default_rng(5)
+    xs_val = []
+    for s in range(w.S):
+        v = rng.normal(size=(w.T_src, w.d))
+        v[:, 0] = s
+        v[:, 1] = np.arange(w.T_src) // 128
+        v[:, 2] = np.arange(w.T_src) % 128
+        xs_val.append(synth.f64_to_bf16_bits(v))
+    topk = np.stack([synth.gen_other_routing(w.replace(own=[]), s)[0] for s in range(w.S)])
+    gate = np.stack([synth.gen_other_routing(w.replace(own=[]), s)[1] for s in range(w.S)])
+    e2l = w.expert_to_local()
+    ref = oracle.layout(topk, e2l, w.E_local)
+    R = ref["R"]
+    cfg = make_config(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, "bf16", R)
+    offsets = torch.from_numpy(ref["offsets"]).to(DEV)
+    row_src = torch.from_numpy(ref["row_src"]).to(DEV)
+    x = [to_device(a, "bf16", DEV) for a in xs_val]
+    xp = torch.zeros(R, w.d, dtype=torch.bfloat16, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mok_dispatch(cfg, x, row_src, offsets, xp, None, st)
+    torch.cuda.synchronize()
+    got = xp.view(torch.int16).cpu().numpy().view(np.uint16)
+    toks = ref["row_src"] // w.k
+    want = np.stack([xs_val[t // w.T_src][t % w.T_src] for t in toks])
+    np.testing.assert_array_equal(got, want)
+    # identity experts: y = gathered rows; push + final combine for the own source
+    staging = [torch.zeros(w.T_src * w.k, w.d, dtype=torch.bfloat16, device=DEV) for _ in range(w.S)]
+    out = [torch.zeros(w.T_src, w.d, dtype=torch.bfloat16, device=DEV) for _ in range(w.S)]
+    mok_combine(cfg, xp, torch.from_numpy(ref["dest_row"]).to(DEV),
+                torch.from_numpy(gate.reshape(-1)).to(DEV), staging, 1, 1, out, st)
+    torch.cuda.synchronize()
+    o = out[1].float().cpu().numpy()
+    xv = synth.bf16_bits_to_f32(xs_val[1]).astype(np.float64)
+    loc = (e2l[topk[1]] >= 0)
+    gsum = (gate[1].astype(np.float64) * loc).sum(1)
+    expect = xv * gsum[:, None]
+    assert np.all(np.abs(o - expect) <= 2.0 ** -8 * np.abs(expect) + 1e-30)
+
+
+def _ffn_case(prec):
+    w = _small("C2", S=2, T_src=150, d=256, E=6, k=2, I=320, own=[0, 1],
+               local_experts=list(range(6)), prec=prec)
+    if prec == "f32":
+        w = w.replace(prec="f32")
+    return w
+
+
+@pytest.mark.parametrize("prec", ["f32", "bf16"])
+def test_expert_ffn_rows(prec):
+    w = _ffn_case(prec)
+    _log("expert_ffn", prec)
+    c = make_host_case(w)
+    R = c.layout["R"]
+    cfg = make_config(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, prec, R)
+    # inputs: the gathered rows, built on the host from the oracle layout
+    toks = c.layout["row_src"] // w.k
+    xs_rows = np.stack([c.x_store[t // w.T_src][t % w.T_src] for t in toks])
+    xp = to_device(xs_rows, prec, DEV)
+    dt = torch.float32 if prec == "f32" else torch.bfloat16
+    h = torch.zeros(R, w.I, dtype=dt, device=DEV)
+    ab = torch.zeros(R, 2 * w.I, dtype=dt, device=DEV)
+    y = torch.zeros(R, w.d, dtype=dt, device=DEV)
+    wts = [to_device(a, prec, DEV) for a in (c.wg_store, c.wu_store, c.wd_store)]
+    W = make_weights(*wts)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mok_expert_ffn(cfg, xp, None, torch.from_numpy(c.layout["offsets"]).to(DEV), W, h, None, ab, y,
+                   st)
+    torch.cuda.synchronize()
+    yg = y.float().cpu().numpy()
+    hg = h.float().cpu().numpy()
+    abg = ab.float().cpu().numpy()
+    offs = c.layout["offsets"]
+    for r in range(R):
+        le = int(np.searchsorted(offs, r, side="right") - 1)
+        t = toks[r]
+        a, b, hr, yr = oracle.ffn_row(c.x_val[t // w.T_src][t % w.T_src], c.wg_val[le], c.wu_val[le],
+                                      c.wd_val[le], prec)
+        assert rel_err(yg[r], yr) <= TOL[prec], r
+        assert rel_err(hg[r], hr) <= TOL[prec], r
+        assert rel_err(abg[r, :w.I], a) <= TOL[prec] and rel_err(abg[r, w.I:], b) <= TOL[prec]
+
+
+FWD_CASES = {
+    "c1": synth.WORKLOADS["C1"],
+    "bf16_small": _small("C2", S=2, T_src=300, d=256, E=8, k=2, I=320, own=[0, 1],
+                         local_experts=list(range(8))),
+    "bf16_share": _small("C3", S=3, T_src=65, d=128, E=16, k=4, I=192, own=[1],
+                         local_experts=[1, 4, 7, 10, 13], zipf_s=0.0),
+    "c2_full": synth.WORKLOADS["C2"],
+}
+
+
+def _check_fwd(c, L, toks):
+    w = c.w
+    per = w.T_src * w.k
+    gi = L.topk_idx.cpu().numpy().reshape(w.S, w.T_src, w.k)
+    gg = L.topk_gate.cpu().numpy().reshape(w.S, w.T_src, w.k)
+    for s in w.own:
+        np.testing.assert_array_equal(gi[s], c.topk_all[s])
+        np.testing.assert_allclose(gg[s], c.gate_all[s], atol=2e-6, rtol=0)
+    lay = c.layout
+    np.testing.assert_array_equal(L.counts.cpu().numpy(), lay["counts"])
+    np.testing.assert_array_equal(L.offsets.cpu().numpy(), lay["offsets"])
+    np.testing.assert_array_equal(L.row_src.cpu().numpy()[:lay["R"]], lay["row_src"])
+    np.testing.assert_array_equal(L.dest_row.cpu().numpy()[:w.S * per], lay["dest_row"])
+    y_ref, out_ref = oracle_fwd_tokens(c, toks)
+    ys, outs, ysr = [], [], []
+    for i, (s, t) in enumerate(toks):
+        o = L.out[s][t].float().cpu().numpy()
+        outs.append(o)
+        for j in range(w.k):
+            if c.e2l[c.topk_all[s, t, j]] >= 0:
+                ys.append(L.staging[s][t * w.k + j].float().cpu().numpy())
+                ysr.append(y_ref[i, j])
+    e_out = rel_err(np.stack(outs), out_ref)
+    e_y = rel_err(np.stack(ys), np.stack(ysr)) if ys else 0.0
+    _log(f"  out rel err {e_out:.3e}  y rel err {e_y:.3e}")
+    assert e_out <= TOL[w.prec] and e_y <= TOL[w.prec]
+
+
+@pytest.mark.parametrize("name", list(FWD_CASES))
+def test_layer_fwd(name):
+    w = FWD_CASES[name]
+    _log("layer_fwd", name)
+    c = make_host_case(w)
+    L = _layer(c, with_bwd=False)
+    L.forward()
+    torch.cuda.synchronize()
+    L.check_status()
+    n = 24 if name == "c2_full" else min(w.T_src * len(w.own), 64)
+    toks = sample_tokens(w, n) if name == "c2_full" else sorted(
+        {(s, t) for s in w.own for t in range(w.T_src)})[:: max(1, (w.T_src * len(w.own)) // n)]
+    _check_fwd(c, L, toks)
+
+
+BWD_CASES = {
+    "bf16_all_local": _small("C2", S=2, T_src=100, d=128, E=8, k=2, I=128, own=[0, 1],
+                             local_experts=list(range(8))),
+    "f32": _small("C1", S=1, T_src=90, d=64, E=4, k=2, I=192, own=[0], local_experts=[0, 1, 2, 3]),
+    "bf16_share": _small("C3", S=3, T_src=65, d=128, E=16, k=4, I=192, own=[1],
+                         local_experts=[1, 4, 7, 10, 13], zipf_s=0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_layer_bwd(name):
+    w = BWD_CASES[name]
+    _log("layer_bwd", name)
+    c = make_host_case(w)
+    L = _layer(c)
+    dout_store = [synth.gen_dout(w, s) for s in range(w.S)]
+    d_out = [to_device(a, w.prec, DEV) for a, _ in dout_store]
+    L.forward()
+    L.backward(d_out)
+    torch.cuda.synchronize()
+    L.check_status()
+    lay = c.layout
+    tol = TOL[w.prec]
+    # per own token: d_gate, dx (incl. router path)
+    toks = [(s, t) for s in w.own for t in range(w.T_src)]
+    tok_x = np.stack([c.x_val[s][t] for s, t in toks])
+    tok_d = np.stack([dout_store[s][1][t] for s, t in toks])
+    idx = np.stack([c.topk_all[s, t] for s, t in toks])
+    g = np.stack([c.gate_all[s, t] for s, t in toks])
+    dg_ref, dz_ref, dx_ref = oracle.bwd_tokens(tok_x, tok_d, idx, g, c.e2l, c.wr_val, c.wg_val,
+                                               c.wu_val, c.wd_val)
+    dg = L.d_gate.cpu().numpy().reshape(w.S, w.T_src, w.k)
+    dg_got = np.stack([dg[s, t] for s, t in toks])
+    local = c.e2l[idx] >= 0
+    assert rel_err(dg_got[local], dg_ref[local]) <= tol
+    dx_got = np.stack([L.d_x[s][t].float().cpu().numpy() for s, t in toks])
+    e_dx = rel_err(dx_got, dx_ref)
+    # weight gradients per local expert (rows of all sources, in layout order)
+    e_w = 0.0
+    for le in range(w.E_local):
+        rows = lay["row_src"][lay["offsets"][le]:lay["offsets"][le + 1]]
+        if len(rows) == 0:
+            assert float(L.dw_gate[le].abs().max()) == 0.0
+            continue
+        tt = rows // w.k
+        jj = rows % w.k
+        rx = np.stack([c.x_val[t // w.T_src][t % w.T_src] for t in tt])
+        rg = np.array([c.gate_all[t // w.T_src, t % w.T_src, j] for t, j in zip(tt, jj)])
+        rd = np.stack([dout_store[t // w.T_src][1][t % w.T_src] for t in tt])
+        dwg, dwu, dwd = oracle.expert_wgrad(rx, rg, rd, c.wg_val[le], c.wu_val[le], c.wd_val[le])
+        e_w = max(e_w, rel_err(L.dw_gate[le].cpu().numpy(), dwg),
+                  rel_err(L.dw_up[le].cpu().numpy(), dwu), rel_err(L.dw_down[le].cpu().numpy(), dwd))
+    dwr_ref = oracle.router_wgrad(tok_x, idx, dz_ref, w.E)
+    e_r = rel_err(L.dw_router.cpu().numpy(), dwr_ref)
+    _log(f"  dx {e_dx:.3e} dW {e_w:.3e} dWr {e_r:.3e}")
+    assert e_dx <= tol and e_w <= tol and e_r <= tol
+
+
+def test_fwd_bwd_run_to_run_bit_identical():
+    w = BWD_CASES["bf16_all_local"].replace(T_src=400)
+    _log("determinism")
+    c = make_host_case(w)
+    L = _layer(c)
+    d_out = [to_device(synth.gen_dout(w, s)[0], w.prec, DEV) for s in range(w.S)]
+    snaps = []
+    for _ in range(2):
+        L.forward()
+        L.backward(d_out)
+        torch.cuda.synchronize()
+        snaps.append([t.clone() for t in (L.out[0], L.out[1], L.staging[0], L.h, L.ab, L.d_gate,
+                                          L.d_x[0], L.d_x[1], L.dw_gate, L.dw_up, L.dw_down,
+                                          L.dw_router)])
+    for a, b in zip(*snaps):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b.view(torch.uint8) if b.dtype != torch.uint8 else b)
+
+
+def test_mx_quantize_bit_exact():
+    w = synth.WORKLOADS["C2"].replace(E=2, local_experts=[0, 1], I=256, d=512)
+    _log("mx_quantize")
+    store, val = synth.gen_expert_weights(w, "gate")
+    rows, K = w.E_local * w.I, w.d
+    codes = torch.zeros(rows * K, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(rows * K // 32, dtype=torch.uint8, device=DEV)
+    mok_mx_quantize(rows, K, to_device(store, "bf16", DEV), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(val.reshape(rows, K).astype(np.float64))
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(rows, K), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, K // 32), rs)

@@ -1,0 +1,230 @@
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+One step = the whole layer, forward and backward, over one batch of synthetic
+input resident in HBM: route -> layout -> gather -> SwiGLU grouped GEMMs ->
+push + final weighted combine, then reverse-combine pull -> dgrad GEMMs with
+the SwiGLU derivative -> wgrad GEMMs -> reverse-dispatch push + router
+backward.  Workload (default): the mid-size layer, T = 16384 tokens in 8
+source buffers of 2048, d = 2048, E = 64 experts all local, top-6, SwiGLU
+I = 1408, bf16 with fp32 accumulation, balanced routing.
+
+Prints ONE JSON line on stdout: layer tokens/s (forward + backward), the
+forward-only rate, per-kernel average times (HIP events recorded by the
+library between its kernels on the layer's stream, during the timed steps),
+the roofline of the dominant kernel, and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec fwd & fwd+bwd on 1 MI355X; % MFMA peak, % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name, w, R):
+    """Algorithmic work of one launch: ('mfma', flops) or ('hbm', bytes)."""
+    d, I, k, T = w.d, w.I, w.k, w.S * w.T_src
+    eb = 2 if w.prec != "f32" else 4
+    gemm = {
+        "ffn1_gate_up_swiglu": 2.0 * R * d * 2 * I,
+        "ffn2_down": 2.0 * R * I * d,
+        "bwd_dh_swiglu": 2.0 * R * d * I,
+        "bwd_dx_push": 2.0 * R * 2 * I * d,
+        "bwd_wgrad_gate_up": 2.0 * R * 2 * I * d,
+        "bwd_wgrad_down": 2.0 * R * d * I,
+    }
+    if name in gemm:
+        return "mfma", gemm[name]
+    moves = {
+        "gather": 2.0 * R * d * eb,                       # read token row, write slot row
+        "combine": (T * k * d + T * d) * eb,              # read k pushed rows, write out
+        "bwd_reverse_combine_pull": 3.0 * R * d * eb,     # read dout + y rows, write dy
+        "bwd_dx_sum_router": (T * k * d + T * d) * eb,    # read k dx rows, write dX
+    }
+    if name in moves:
+        return "hbm", moves[name]
+    return None, None
+
+
+def cpu_baseline(w, host, n_tok):
+    """Time the CPU oracle (single thread) on n_tok tokens of the workload:
+    routing, forward, backward and their share of the weight gradients."""
+    import numpy as np
+
+    import oracle
+    own = w.own
+    toks = [(own[i % len(own)], (i * 7919) % w.T_src) for i in range(n_tok)]
+    tok_x = np.stack([host["x_val"][s][t] for s, t in toks])
+    tok_d = np.stack([host["dout_val"][s][t] for s, t in toks])
+    e2l = w.expert_to_local()
+    t0 = time.perf_counter()
+    idx, g = oracle.route(tok_x, host["wr_val"], host["bias"], w.k, w.prec)
+    oracle.fwd_tokens(tok_x, idx, g, e2l, host["wg_val"], host["wu_val"], host["wd_val"], w.prec)
+    _, dz, _ = oracle.bwd_tokens(tok_x, tok_d, idx, g, e2l, host["wr_val"], host["wg_val"],
+                                 host["wu_val"], host["wd_val"])
+    for le in range(w.E_local):
+        sel = [(i, j) for i in range(n_tok) for j in range(w.k) if e2l[idx[i, j]] == le]
+        if sel:
+            ii = [i for i, _ in sel]
+            oracle.expert_wgrad(tok_x[ii], np.array([g[i, j] for i, j in sel]), tok_d[ii],
+                                host["wg_val"][le], host["wu_val"][le], host["wd_val"][le])
+    oracle.router_wgrad(tok_x, idx, dz, w.E)
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tok} tokens of the workload, forward + backward (routing, FFN rows, "
+                      f"combine, backward rows, their weight-gradient rows, router gradient); "
+                      f"{dt:.1f} s single-threaded float64 C"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--cpu-tokens", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_router_top_expert_amd import Trace, synth
+    from combine_router_top_expert_amd.layer import MoELayer, to_device
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.workload]
+    if w.prec == "mxfp8":
+        raise SystemExit("the MXFP8 workload has no backward pass in this build")
+    t0 = time.time()
+    xs = [synth.gen_x(w, s) for s in range(w.S)]
+    wr = synth.gen_router(w)
+    bias = synth.load_bias(w)
+    wg = synth.gen_expert_weights(w, "gate")
+    wu = synth.gen_expert_weights(w, "up")
+    wd = synth.gen_expert_weights(w, "down")
+    dout = [synth.gen_dout(w, s) for s in range(w.S)]
+    other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    N = w.S * w.T_src * w.k
+    R_cap = N if w.E_local == w.E else N  # every item can be local in the worst case
+    L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
+                 len(w.own), device=dev)
+    L.set_inputs([to_device(a, w.prec, dev) for a, _ in xs], to_device(wr[0], w.prec, dev),
+                 None if bias is None else torch.from_numpy(bias).to(dev),
+                 torch.from_numpy(w.expert_to_local()).to(dev),
+                 to_device(wg[0], w.prec, dev), to_device(wu[0], w.prec, dev),
+                 to_device(wd[0], w.prec, dev), other_topk=other)
+    d_out = [to_device(a, w.prec, dev) for a, _ in dout]
+
+    for _ in range(args.warmup):
+        L.forward()
+        L.backward(d_out)
+    torch.cuda.synchronize()
+    L.check_status()
+    R = int(L.offsets[-1].item())
+
+    trace = Trace(capacity=64 * (args.steps + 1))
+    trace.attach(L.cfg)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        L.forward()
+        L.backward(d_out)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    Trace.detach(L.cfg)
+    L.check_status()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    T_tok = w.T_total if len(w.own) == w.S else len(w.own) * w.T_src
+
+    recs = trace.records()
+    per_kernel = {}
+    for name, ms in recs:
+        per_kernel.setdefault(name, []).append(ms)
+    fwd_names = {"route", "layout_count", "layout_scan", "layout_place", "gather",
+                 "ffn1_gate_up_swiglu", "ffn2_down", "combine"}
+    fwd_ms = sum(sum(v) for n, v in per_kernel.items() if n in fwd_names) / args.steps
+    bwd_ms = sum(sum(v) for n, v in per_kernel.items() if n not in fwd_names) / args.steps
+    kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps}
+               for n, v in per_kernel.items()}
+    # dominant kernel: largest time per step
+    dom = max(per_kernel, key=lambda n: sum(per_kernel[n]))
+    kind, work = kernel_work(dom, w, R)
+    avg_s = float(np.mean(per_kernel[dom])) * 1e-3
+    if kind == "mfma":
+        achieved = work / avg_s / 1e12
+        peak = PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "kernel": dom,
+                "algorithmic_flops_per_launch": work}
+    else:
+        achieved = work / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
+                "algorithmic_bytes_per_launch": work}
+    # per-kernel roofline fractions, for the record
+    for n, v in kernels.items():
+        kd, wk = kernel_work(n, w, R)
+        if kd == "mfma":
+            v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
+            v["frac_mfma_peak"] = v["tflops"] / PEAK_BF16_TFLOPS
+        elif kd == "hbm":
+            v["gbs"] = wk / (v["avg_ms"] * 1e-3) / 1e9
+            v["frac_hbm_peak"] = v["gbs"] / PEAK_HBM_GBS
+
+    result = {
+        "metric": METRIC,
+        "value": T_tok / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.prec == "bf16" else w.prec,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={T_tok} tokens ({w.S} sources x {w.T_src}), d={w.d}, "
+                               f"E={w.E} ({w.E_local} local), top-{w.k}, SwiGLU I={w.I}, {w.prec}, "
+                               f"{'Zipf %.1f skew' % w.zipf_s if w.zipf_s else 'balanced routing'}; "
+                               f"step = forward + backward",
+                   "routed_rows": R, "path": "staged"},
+        "fwd_tokens_per_s": T_tok / (fwd_ms * 1e-3),
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        host = {"x_val": [b for _, b in xs], "dout_val": [b for _, b in dout], "wr_val": wr[1],
+                "bias": bias, "wg_val": wg[1], "wu_val": wu[1], "wd_val": wd[1]}
+        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_tokens)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,7 +41,93 @@ class mok_config(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E_local", ctypes.c_int32), ("prec", ctypes.c_int32), ("R_cap", ctypes.c_int32),
                 ("minibatch_rows", ctypes.c_int32), ("ring_bytes", ctypes.c_int64),
-                ("comm_wgs", ctypes.c_int32), ("gemm_wgs", ctypes.c_int32)]
+                ("comm_wgs", ctypes.c_int32), ("gemm_wgs", ctypes.c_int32),
+                ("trace", ctypes.c_void_p)]
+
+
+class mok_trace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("names", ctypes.POINTER(ctypes.c_char_p)),
+                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32)]
+
+
+def _hip_runtime():
+    """The HIP runtime instance this process already uses (torch's copy when
+    torch is loaded), with the event functions' signatures declared."""
+    path = None
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+    except OSError:
+        pass
+    hip = ctypes.CDLL(path or "libamdhip64.so.7")
+    P = ctypes.c_void_p
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+    hip.hipEventSynchronize.argtypes = [P]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+    hip.hipEventDestroy.argtypes = [P]
+    for fn in (hip.hipEventCreate, hip.hipEventSynchronize, hip.hipEventElapsedTime,
+               hip.hipEventDestroy):
+        fn.restype = ctypes.c_int
+    return hip
+
+
+class Trace:
+    """Caller-owned kernel timing: `capacity` hipEvents (created through the HIP
+    runtime) handed to the library through mok_config.trace."""
+
+    def __init__(self, capacity: int):
+        self.hip = _hip_runtime()
+        self.capacity = capacity
+        self.events = (ctypes.c_void_p * capacity)()
+        for i in range(capacity):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.events[i] = ev
+        self.names = (ctypes.c_char_p * capacity)()
+        self.t = mok_trace(self.events, self.names, capacity, 0)
+
+    def attach(self, cfg: "mok_config"):
+        cfg.trace = ctypes.addressof(self.t)
+
+    @staticmethod
+    def detach(cfg: "mok_config"):
+        cfg.trace = None
+
+    def reset(self):
+        self.t.count = 0
+
+    def records(self):
+        """[(name, ms since the previous event)] for every recorded event after
+        the first of each call (the 'start' marks carry no duration)."""
+        if self.t.count == 0:
+            return []
+        rc = self.hip.hipEventSynchronize(self.events[self.t.count - 1])
+        if rc != 0:
+            raise RuntimeError(f"hipEventSynchronize failed: {rc}")
+        out = []
+        for i in range(1, self.t.count):
+            name = self.names[i].decode()
+            if name == "start":
+                continue
+            ms = ctypes.c_float()
+            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i - 1], self.events[i])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+            out.append((name, float(ms.value)))
+        return out
+
+    def __del__(self):
+        try:
+            for i in range(self.capacity):
+                self.hip.hipEventDestroy(self.events[i])
+        except Exception:
+            pass
 
 
 class mok_expert_weights(ctypes.Structure):
@@ -124,7 +210,7 @@ def _check(fn: str, rc: int):
 def make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows=256, ring_bytes=0,
                 comm_wgs=0, gemm_wgs=0) -> mok_config:
     return mok_config(S, T_src, d, E, k, I, E_local, PREC.get(prec, prec), R_cap, minibatch_rows,
-                      ring_bytes, comm_wgs, gemm_wgs)
+                      ring_bytes, comm_wgs, gemm_wgs, None)
 
 
 def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> mok_expert_weights:

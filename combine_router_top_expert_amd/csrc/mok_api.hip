@@ -89,8 +89,9 @@ mok_status mok_route(const mok_config* cfg, int32_t T, const void* x, const void
                      const float* bias, int32_t* topk_idx, float* topk_gate, void* stream) {
   if (!valid_cfg(cfg) || T < 0) return MOK_EINVAL;
   if (T > 0 && (!x || !w_router || !topk_idx || !topk_gate)) return MOK_EINVAL;
+  trace_mark(cfg->trace, "start", (hipStream_t)stream);
   return launch_route(cfg->prec, T, cfg->d, cfg->E, cfg->k, x, w_router, bias, topk_idx,
-                      topk_gate, (hipStream_t)stream);
+                      topk_gate, (hipStream_t)stream, cfg->trace);
 }
 
 mok_status mok_layout(const mok_config* cfg, const int32_t* topk_idx_all,
@@ -104,7 +105,7 @@ mok_status mok_layout(const mok_config* cfg, const int32_t* topk_idx_all,
   if (cfg->R_cap > 0 && !row_src) return MOK_EINVAL;
   return launch_layout(N, cfg->E, cfg->E_local, cfg->R_cap, topk_idx_all, expert_to_local, counts,
                        offsets, row_src, dest_row, (char*)ws + ws_layout(cfg).layout, dev_status,
-                       (hipStream_t)stream);
+                       (hipStream_t)stream, cfg->trace);
 }
 
 mok_status mok_dispatch(const mok_config* cfg, const void* const* src_x, const int32_t* row_src,
@@ -116,8 +117,9 @@ mok_status mok_dispatch(const mok_config* cfg, const void* const* src_x, const i
   SrcTable src;
   if (!fill_table(&src, src_x, cfg->S) || !row_src || !offsets || !x_perm) return MOK_EINVAL;
   if (cfg->prec == MOK_MXFP8 && !x_scale) return MOK_EINVAL;
+  trace_mark(cfg->trace, "start", (hipStream_t)stream);
   return launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
-                       row_src, offsets, x_perm, x_scale, (hipStream_t)stream);
+                       row_src, offsets, x_perm, x_scale, (hipStream_t)stream, cfg->trace);
 }
 
 mok_status mok_expert_ffn(const mok_config* cfg, const void* x_perm, const uint8_t* x_scale,
@@ -130,13 +132,15 @@ mok_status mok_expert_ffn(const mok_config* cfg, const void* x_perm, const uint8
   if (!x_perm || !w->w_gate || !w->w_up || !w->w_down || !h || !y) return MOK_EINVAL;
   if (cfg->prec == MOK_MXFP8) {
     if (!x_scale || !h_scale || !w->s_gate || !w->s_up || !w->s_down) return MOK_EINVAL;
+    trace_mark(cfg->trace, "start", (hipStream_t)stream);
     return launch_ffn_mx(cfg->d, cfg->I, cfg->E_local, cfg->R_cap, (const uint8_t*)x_perm,
                          x_scale, offsets, nullptr, w, (uint8_t*)h, h_scale, ab, y, nullptr,
-                         cfg->T_src, cfg->k, (hipStream_t)stream);
+                         cfg->T_src, cfg->k, (hipStream_t)stream, cfg->trace);
   }
+  trace_mark(cfg->trace, "start", (hipStream_t)stream);
   return launch_ffn(cfg->prec, cfg->d, cfg->I, cfg->E_local, cfg->R_cap, x_perm, offsets, nullptr,
                     w->w_gate, w->w_up, w->w_down, h, ab, y, nullptr, cfg->T_src, cfg->k,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, cfg->trace);
 }
 
 mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest_row,
@@ -151,7 +155,8 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
   const int prec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
   hipStream_t st = (hipStream_t)stream;
   if (y) {
-    mok_status rc = launch_push(prec, y, dest_row, N, stg, cfg->T_src, cfg->d, cfg->k, cfg->R_cap, st);
+    mok_status rc = launch_push(prec, y, dest_row, N, stg, cfg->T_src, cfg->d, cfg->k, cfg->R_cap,
+                                st, cfg->trace);
     if (rc != MOK_OK) return rc;
   }
   if (own_n == 0) return MOK_OK;
@@ -159,7 +164,7 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
   for (int s = own_lo; s < own_lo + own_n; ++s)
     if (!o.p[s] || !stg.p[s]) return MOK_EINVAL;
   return launch_combine(prec, dest_row, topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k, own_lo,
-                        own_n, cfg->R_cap, st);
+                        own_n, cfg->R_cap, st, cfg->trace);
 }
 
 mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
@@ -175,16 +180,22 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   if (own_n > 0 && !out) return MOK_EINVAL;
   if (cfg->ring_bytes > 0) return MOK_EINVAL;  // fused ring path: not available in this build
   hipStream_t sm = (hipStream_t)stream;
+  mok_trace* tr = cfg->trace;
+  trace_mark(tr, "start", sm);
   const int64_t per_src = (int64_t)cfg->T_src * cfg->k;
   const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
-  for (int s = own_lo; s < own_lo + own_n; ++s) {
+  for (int s = own_lo; s < own_lo + own_n; ++s)
     if (!src_x[s]) return MOK_EINVAL;
+  for (int s = own_lo; s < own_lo + own_n; ++s) {
     mok_status rc = launch_route(rprec, cfg->T_src, cfg->d, cfg->E, cfg->k, src_x[s], w_router,
-                                 bias, st->topk_idx + s * per_src, st->topk_gate + s * per_src, sm);
+                                 bias, st->topk_idx + s * per_src, st->topk_gate + s * per_src, sm,
+                                 tr);
     if (rc != MOK_OK) return rc;
   }
-  mok_status rc = mok_layout(cfg, st->topk_idx, expert_to_local, st->counts, st->offsets,
-                             st->row_src, st->dest_row, ws, dev_status, stream);
+  mok_status rc = launch_layout((int64_t)cfg->S * cfg->T_src * cfg->k, cfg->E, cfg->E_local,
+                                cfg->R_cap, st->topk_idx, expert_to_local, st->counts,
+                                st->offsets, st->row_src, st->dest_row,
+                                (char*)ws + ws_layout(cfg).layout, dev_status, sm, tr);
   if (rc != MOK_OK) return rc;
   const Ws wl = ws_layout(cfg);
   char* wsb = (char*)ws;
@@ -195,25 +206,30 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
     fill_table(&src, src_x, cfg->S);
     if (cfg->prec == MOK_MXFP8) {
       rc = launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
-                         st->row_src, st->offsets, wsb + wl.xperm, (uint8_t*)(wsb + wl.xscale), sm);
+                         st->row_src, st->offsets, wsb + wl.xperm, (uint8_t*)(wsb + wl.xscale), sm,
+                         tr);
       if (rc != MOK_OK) return rc;
       rc = launch_ffn_mx(cfg->d, cfg->I, cfg->E_local, cfg->R_cap, (const uint8_t*)(wsb + wl.xperm),
                          (const uint8_t*)(wsb + wl.xscale), st->offsets, st->row_src, w,
                          (uint8_t*)st->h, (uint8_t*)(wsb + wl.hscale), st->ab, nullptr, &stg,
-                         cfg->T_src, cfg->k, sm);
+                         cfg->T_src, cfg->k, sm, tr);
     } else {
       rc = launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
-                         st->row_src, st->offsets, wsb + wl.xperm, nullptr, sm);
+                         st->row_src, st->offsets, wsb + wl.xperm, nullptr, sm, tr);
       if (rc != MOK_OK) return rc;
       rc = launch_ffn(cfg->prec, cfg->d, cfg->I, cfg->E_local, cfg->R_cap, wsb + wl.xperm,
                       st->offsets, st->row_src, w->w_gate, w->w_up, w->w_down, st->h, st->ab,
-                      nullptr, &stg, cfg->T_src, cfg->k, sm);
+                      nullptr, &stg, cfg->T_src, cfg->k, sm, tr);
     }
     if (rc != MOK_OK) return rc;
   }
   if (own_n == 0) return MOK_OK;
-  return mok_combine(cfg, nullptr, st->dest_row, st->topk_gate, staging, own_lo, own_n, out,
-                     dev_status, stream);
+  DstTable o;
+  fill_table(&o, (const void* const*)out, cfg->S);
+  for (int s = own_lo; s < own_lo + own_n; ++s)
+    if (!o.p[s] || !stg.p[s]) return MOK_EINVAL;
+  return launch_combine(rprec, st->dest_row, st->topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k,
+                        own_lo, own_n, cfg->R_cap, sm, tr);
 }
 
 mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
@@ -271,6 +287,8 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.dab = wsb + wl.dab;
   p.dz = (float*)(wsb + wl.dz);
   p.dwr_part = (float*)(wsb + wl.dwr);
+  p.tr = cfg->trace;
+  trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);
 }
 

@@ -320,30 +320,38 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   if (p.R_cap > 0) {
     const int mt = grouped_mtiles_bound(p.R_cap, p.E_local);
     hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
     int ntn = (p.I + kBN - 1) / kBN;
     hipLaunchKernelGGL(dh_kernel<T>, dim3(mt * ntn), dim3(kGemmThreads), 0, stream, p, ntn);
+    trace_mark(p.tr, "bwd_dh_swiglu", stream);
     ntn = (p.d + kBN - 1) / kBN;
     hipLaunchKernelGGL(dx_kernel<T>, dim3(mt * ntn), dim3(kGemmThreads), 0, stream, p, ntn);
+    trace_mark(p.tr, "bwd_dx_push", stream);
   }
   {
     int mtn = (2 * p.I + kBM - 1) / kBM, ntn = (p.d + kBN - 1) / kBN;
     hipLaunchKernelGGL((wgrad_kernel<T, 0>), dim3(p.E_local * mtn * ntn), dim3(kGemmThreads), 0,
                        stream, p, mtn, ntn);
+    trace_mark(p.tr, "bwd_wgrad_gate_up", stream);
     mtn = (p.d + kBM - 1) / kBM;
     ntn = (p.I + kBN - 1) / kBN;
     hipLaunchKernelGGL((wgrad_kernel<T, 1>), dim3(p.E_local * mtn * ntn), dim3(kGemmThreads), 0,
                        stream, p, mtn, ntn);
+    trace_mark(p.tr, "bwd_wgrad_down", stream);
   }
   const int64_t n_own = (int64_t)p.own_n * p.T_src;
   if (n_own > 0) {
     hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)n_own), dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_dx_sum_router", stream);
     if (p.dw_router) {
       const int64_t per = (n_own + kRouterChunks - 1) / kRouterChunks;
       dim3 g((p.d + kThreads - 1) / kThreads, (p.E + 15) / 16, kRouterChunks);
       hipLaunchKernelGGL(dwr_part_kernel<T>, g, dim3(kThreads), 0, stream, p, n_own, per);
+      trace_mark(p.tr, "bwd_dw_router_part", stream);
       const int64_t tot = (int64_t)p.E * p.d;
       hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
                          dim3(kThreads), 0, stream, p, kRouterChunks);
+      trace_mark(p.tr, "bwd_dw_router_reduce", stream);
     }
   } else if (p.dw_router) {
     const int64_t tot = (int64_t)p.E * p.d;

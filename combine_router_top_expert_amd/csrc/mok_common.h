@@ -69,6 +69,14 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
 
+// Record one trace event after the kernel just launched (host side).
+inline void trace_mark(mok_trace* t, const char* name, hipStream_t s) {
+  if (!t || !t->events || t->count >= t->capacity) return;
+  (void)hipEventRecord((hipEvent_t)t->events[t->count], s);
+  if (t->names) t->names[t->count] = name;
+  t->count += 1;
+}
+
 }  // namespace mok
 
 #define MOK_HIP_CHECK(x)                         \

@@ -137,7 +137,8 @@ int grouped_mtiles_bound(int R_cap, int E_local) { return (R_cap + kBM - 1) / kB
 mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void* x,
                       const int32_t* offsets, const int32_t* row_src, const void* wg,
                       const void* wu, const void* wd, void* h, void* ab, void* y,
-                      const DstTable* staging, int T_src, int k, hipStream_t stream) {
+                      const DstTable* staging, int T_src, int k, hipStream_t stream,
+                      mok_trace* tr) {
   if (R_cap == 0) return MOK_OK;
   const int mt = grouped_mtiles_bound(R_cap, E_local);
   Ffn1Args a1;
@@ -169,13 +170,16 @@ mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void
   a2.T_src = T_src;
   a2.k = k;
   dim3 g2((unsigned)(mt * a2.ntn));
-  if (prec == MOK_F32) {
+  if (prec == MOK_F32)
     hipLaunchKernelGGL(ffn1_kernel<float>, g1, dim3(kGemmThreads), 0, stream, a1);
-    hipLaunchKernelGGL(ffn2_kernel<float>, g2, dim3(kGemmThreads), 0, stream, a2);
-  } else {
+  else
     hipLaunchKernelGGL(ffn1_kernel<bf16_t>, g1, dim3(kGemmThreads), 0, stream, a1);
+  trace_mark(tr, "ffn1_gate_up_swiglu", stream);
+  if (prec == MOK_F32)
+    hipLaunchKernelGGL(ffn2_kernel<float>, g2, dim3(kGemmThreads), 0, stream, a2);
+  else
     hipLaunchKernelGGL(ffn2_kernel<bf16_t>, g2, dim3(kGemmThreads), 0, stream, a2);
-  }
+  trace_mark(tr, "ffn2_down", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

@@ -10,22 +10,24 @@ int route_geometry(int E, int* EG, int* TG, int* TB, int* dc);
 size_t route_smem_bytes(int E);
 mok_status launch_route(int prec, int T, int d, int E, int k, const void* x, const void* w,
                         const float* bias, int32_t* topk_idx, float* topk_gate,
-                        hipStream_t stream);
+                        hipStream_t stream, mok_trace* tr = nullptr);
 
 size_t layout_ws_bytes(int64_t N, int E_local);
 mok_status launch_layout(int64_t N, int E, int E_local, int R_cap, const int32_t* topk,
                          const int32_t* e2l, int32_t* counts, int32_t* offsets, int32_t* row_src,
-                         int32_t* dest_row, void* ws, int32_t* status, hipStream_t stream);
+                         int32_t* dest_row, void* ws, int32_t* status, hipStream_t stream,
+                         mok_trace* tr = nullptr);
 
 mok_status launch_gather(int prec, const SrcTable& src, int T_src, int d, int k, int E_local,
                          int R_cap, const int32_t* row_src, const int32_t* offsets, void* dst,
-                         uint8_t* dst_scale, hipStream_t stream);
+                         uint8_t* dst_scale, hipStream_t stream, mok_trace* tr = nullptr);
 mok_status launch_push(int prec, const void* y, const int32_t* dest_row, int64_t N,
                        const DstTable& staging, int T_src, int d, int k, int R_cap,
-                       hipStream_t stream);
+                       hipStream_t stream, mok_trace* tr = nullptr);
 mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
                           const DstTable& staging, const DstTable& out, int T_src, int d, int k,
-                          int own_lo, int own_n, int R_cap, hipStream_t stream);
+                          int own_lo, int own_n, int R_cap, hipStream_t stream,
+                          mok_trace* tr = nullptr);
 mok_status launch_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream);
 
@@ -33,11 +35,13 @@ int grouped_mtiles_bound(int R_cap, int E_local);
 mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void* x,
                       const int32_t* offsets, const int32_t* row_src, const void* wg,
                       const void* wu, const void* wd, void* h, void* ab, void* y,
-                      const DstTable* staging, int T_src, int k, hipStream_t stream);
+                      const DstTable* staging, int T_src, int k, hipStream_t stream,
+                      mok_trace* tr = nullptr);
 mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq,
                          const uint8_t* xs, const int32_t* offsets, const int32_t* row_src,
                          const mok_expert_weights* w, uint8_t* hq, uint8_t* hs, void* ab, void* y,
-                         const DstTable* staging, int T_src, int k, hipStream_t stream);
+                         const DstTable* staging, int T_src, int k, hipStream_t stream,
+                         mok_trace* tr = nullptr);
 
 struct BwdPlan {
   int prec;
@@ -61,6 +65,7 @@ struct BwdPlan {
   void* dab;     // [R_cap, 2I]
   float* dz;     // [own tokens, k]
   float* dwr_part;  // [kRouterChunks, E, d]
+  mok_trace* tr;    // host-side trace, may be null
 };
 constexpr int kRouterChunks = 32;
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);

@@ -154,7 +154,8 @@ size_t layout_ws_bytes(int64_t N, int E_local) {
 
 mok_status launch_layout(int64_t N, int E, int E_local, int R_cap, const int32_t* topk,
                          const int32_t* e2l, int32_t* counts, int32_t* offsets, int32_t* row_src,
-                         int32_t* dest_row, void* ws, int32_t* status, hipStream_t stream) {
+                         int32_t* dest_row, void* ws, int32_t* status, hipStream_t stream,
+                         mok_trace* tr) {
   LayoutArgs a;
   a.topk = topk;
   a.e2l = e2l;
@@ -170,8 +171,11 @@ mok_status launch_layout(int64_t N, int E, int E_local, int R_cap, const int32_t
   a.R_cap = R_cap;
   a.nchunk = (int)((N + kChunk - 1) / kChunk);
   if (a.nchunk > 0) hipLaunchKernelGGL(layout_count, dim3(a.nchunk), dim3(64), 0, stream, a);
+  trace_mark(tr, "layout_count", stream);
   hipLaunchKernelGGL(layout_scan, dim3(1), dim3(256), 0, stream, a);
+  trace_mark(tr, "layout_scan", stream);
   if (a.nchunk > 0) hipLaunchKernelGGL(layout_place, dim3(a.nchunk), dim3(64), 0, stream, a);
+  trace_mark(tr, "layout_place", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

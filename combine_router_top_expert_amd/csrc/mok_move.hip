@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
 // ---------------------------------------------------------------- launchers
 mok_status launch_gather(int prec, const SrcTable& src, int T_src, int d, int k, int E_local,
                          int R_cap, const int32_t* row_src, const int32_t* offsets, void* dst,
-                         uint8_t* dst_scale, hipStream_t stream) {
+                         uint8_t* dst_scale, hipStream_t stream, mok_trace* tr) {
   if (R_cap == 0) return MOK_OK;
   GatherArgs a;
   a.src = src;
@@ -267,12 +267,13 @@ mok_status launch_gather(int prec, const SrcTable& src, int T_src, int d, int k,
     hipLaunchKernelGGL(gather_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(gather_mx_kernel, grid, dim3(kThreads), 0, stream, a);
+  trace_mark(tr, "gather", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
 mok_status launch_push(int prec, const void* y, const int32_t* dest_row, int64_t N,
                        const DstTable& staging, int T_src, int d, int k, int R_cap,
-                       hipStream_t stream) {
+                       hipStream_t stream, mok_trace* tr) {
   if (N == 0) return MOK_OK;
   PushArgs a;
   a.y = y;
@@ -289,12 +290,14 @@ mok_status launch_push(int prec, const void* y, const int32_t* dest_row, int64_t
     hipLaunchKernelGGL(push_kernel<float>, grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(push_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
+  trace_mark(tr, "push", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
 mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
                           const DstTable& staging, const DstTable& out, int T_src, int d, int k,
-                          int own_lo, int own_n, int R_cap, hipStream_t stream) {
+                          int own_lo, int own_n, int R_cap, hipStream_t stream,
+                          mok_trace* tr) {
   CombineArgs a;
   a.dest_row = dest_row;
   a.gate = gate;
@@ -313,6 +316,7 @@ mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
+  trace_mark(tr, "combine", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

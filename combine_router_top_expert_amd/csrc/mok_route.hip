@@ -218,7 +218,7 @@ int route_geometry(int E, int* EG, int* TG, int* TB, int* dc) {
 
 mok_status launch_route(int prec, int T, int d, int E, int k, const void* x, const void* w,
                         const float* bias, int32_t* topk_idx, float* topk_gate,
-                        hipStream_t stream) {
+                        hipStream_t stream, mok_trace* tr) {
   if (T == 0) return MOK_OK;
   RouteArgs a;
   a.x = x;
@@ -247,6 +247,7 @@ mok_status launch_route(int prec, int T, int d, int E, int k, const void* x, con
     else
       hipLaunchKernelGGL((route_kernel<bf16_t, 4>), grid, dim3(kRouteThreads), smem, stream, a);
   }
+  trace_mark(tr, "route", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

@@ -77,6 +77,18 @@ typedef enum {
                     along the contraction dim inside the expert GEMMs */
 } mok_prec;
 
+/* Optional per-kernel timing [tracing]: when mok_config.trace is non-NULL,
+ * every entry point records events[count] on its stream at its start and
+ * after each kernel it launches, stores the name of the kernel that ended at
+ * that event in names[count] (static strings) and increments count, while
+ * count < capacity.  events are caller-created hipEvent_t handles. */
+typedef struct mok_trace {
+  void** events;
+  const char** names;
+  int32_t capacity;
+  int32_t count;
+} mok_trace;
+
 typedef struct mok_config {
   int32_t S;              /* source token buffers (simulated source ranks), 1..MOK_MAX_SOURCES */
   int32_t T_src;          /* tokens per source buffer */
@@ -91,6 +103,7 @@ typedef struct mok_config {
   int64_t ring_bytes;     /* fused path: bytes of the ring of token slots; 0 = staged path */
   int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = auto) */
   int32_t gemm_wgs;       /* fused path: grouped-GEMM workgroups (0 = auto) */
+  mok_trace* trace;       /* optional kernel timing, NULL = off (host memory) */
 } mok_config;
 
 /* Expert weights of the E_local local experts (see Layout above).  For

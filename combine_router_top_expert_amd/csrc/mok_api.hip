@@ -29,7 +29,8 @@ bool valid_cfg(const mok_config* c) {
 }
 
 struct Ws {
-  size_t layout, xperm, xscale, hscale, dy, dab, dz, dwr, total;
+  size_t layout, xperm, xscale, hscale, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
+      r_row_src, r_dest_row, r_scratch, total;
 };
 
 Ws ws_layout(const mok_config* c) {
@@ -57,7 +58,19 @@ Ws ws_layout(const mok_config* c) {
   w.dz = b;
   b += align256((size_t)N * sizeof(float));
   w.dwr = b;
-  b += align256((size_t)kRouterChunks * c->E * c->d * sizeof(float));
+  b += align256(((size_t)N / 64 + c->E) * c->d * sizeof(float));
+  w.r_ident = b;
+  b += align256((size_t)c->E * sizeof(int32_t));
+  w.r_counts = b;
+  b += align256((size_t)c->E * sizeof(int32_t));
+  w.r_offsets = b;
+  b += align256((size_t)(c->E + 1) * sizeof(int32_t));
+  w.r_row_src = b;
+  b += align256((size_t)N * sizeof(int32_t));
+  w.r_dest_row = b;
+  b += align256((size_t)N * sizeof(int32_t));
+  w.r_scratch = b;
+  b += align256(c->E <= 256 ? layout_ws_bytes(N, c->E) : 0);
   w.total = f > b ? f : b;
   return w;
 }
@@ -90,8 +103,12 @@ mok_status mok_route(const mok_config* cfg, int32_t T, const void* x, const void
   if (!valid_cfg(cfg) || T < 0) return MOK_EINVAL;
   if (T > 0 && (!x || !w_router || !topk_idx || !topk_gate)) return MOK_EINVAL;
   trace_mark(cfg->trace, "start", (hipStream_t)stream);
-  return launch_route(cfg->prec, T, cfg->d, cfg->E, cfg->k, x, w_router, bias, topk_idx,
-                      topk_gate, (hipStream_t)stream, cfg->trace);
+  SrcTable src;
+  memset(&src, 0, sizeof(src));
+  src.p[0] = x;
+  const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
+  return launch_route(rprec, src, 0, T > 0 ? T : 1, T, cfg->d, cfg->E, cfg->k, w_router, bias,
+                      topk_idx, topk_gate, (hipStream_t)stream, cfg->trace);
 }
 
 mok_status mok_layout(const mok_config* cfg, const int32_t* topk_idx_all,
@@ -186,10 +203,12 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
   for (int s = own_lo; s < own_lo + own_n; ++s)
     if (!src_x[s]) return MOK_EINVAL;
-  for (int s = own_lo; s < own_lo + own_n; ++s) {
-    mok_status rc = launch_route(rprec, cfg->T_src, cfg->d, cfg->E, cfg->k, src_x[s], w_router,
-                                 bias, st->topk_idx + s * per_src, st->topk_gate + s * per_src, sm,
-                                 tr);
+  {
+    SrcTable src;
+    fill_table(&src, src_x, cfg->S);
+    mok_status rc = launch_route(rprec, src, own_lo, cfg->T_src, own_n * cfg->T_src, cfg->d,
+                                 cfg->E, cfg->k, w_router, bias, st->topk_idx + own_lo * per_src,
+                                 st->topk_gate + own_lo * per_src, sm, tr);
     if (rc != MOK_OK) return rc;
   }
   mok_status rc = launch_layout((int64_t)cfg->S * cfg->T_src * cfg->k, cfg->E, cfg->E_local,
@@ -247,6 +266,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
     return MOK_EINVAL;
   if (!dw_gate || !dw_up || !dw_down || !st->ab || !st->h) return MOK_EINVAL;
   if (own_n > 0 && !d_x) return MOK_EINVAL;
+  if (dw_router && cfg->E > 256) return MOK_EINVAL;  // router layout holds at most 256 experts
   BwdPlan p;
   memset(&p, 0, sizeof(p));
   p.prec = cfg->prec;
@@ -287,6 +307,12 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.dab = wsb + wl.dab;
   p.dz = (float*)(wsb + wl.dz);
   p.dwr_part = (float*)(wsb + wl.dwr);
+  p.r_ident = (int32_t*)(wsb + wl.r_ident);
+  p.r_counts = (int32_t*)(wsb + wl.r_counts);
+  p.r_offsets = (int32_t*)(wsb + wl.r_offsets);
+  p.r_row_src = (int32_t*)(wsb + wl.r_row_src);
+  p.r_dest_row = (int32_t*)(wsb + wl.r_dest_row);
+  p.r_scratch = wsb + wl.r_scratch;
   p.tr = cfg->trace;
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);

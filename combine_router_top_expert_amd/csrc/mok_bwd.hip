@@ -228,23 +228,31 @@ __global__ __launch_bounds__(kGemmThreads) void wgrad_kernel(BwdPlan p, int mtn,
 // ------------------------------------------------------------------ 5. d_x
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
+  __shared__ float s_dz[16];
+  __shared__ int s_e[16];
+  __shared__ int s_loc[16];
   const int64_t gt = blockIdx.x;  // own token index
   const int s = p.own_lo + (int)(gt / p.T_src);
   const int t = (int)(gt % p.T_src);
   const int64_t n0 = ((int64_t)s * p.T_src + t) * p.k;
-  float dz[16];
-  int ex[16];
-  bool loc[16];
-  float m = 0.0f;
-  for (int j = 0; j < p.k; ++j) {
-    loc[j] = p.dest_row[n0 + j] >= 0 && p.dest_row[n0 + j] < p.R_cap;
-    const float dg = loc[j] ? p.d_gate[n0 + j] : 0.0f;
-    dz[j] = dg;
-    m = __builtin_fmaf(p.topk_gate[n0 + j], dg, m);
-    ex[j] = p.topk_idx[n0 + j];
+  if (threadIdx.x == 0) {
+    float dg[16];
+    float m = 0.0f;
+    for (int j = 0; j < p.k; ++j) {
+      const int row = p.dest_row[n0 + j];
+      const bool loc = row >= 0 && row < p.R_cap;
+      dg[j] = loc ? p.d_gate[n0 + j] : 0.0f;
+      m = __builtin_fmaf(p.topk_gate[n0 + j], dg[j], m);
+      s_loc[j] = loc;
+      s_e[j] = p.topk_idx[n0 + j];
+    }
+    for (int j = 0; j < p.k; ++j) {
+      const float dz = p.topk_gate[n0 + j] * (dg[j] - m);
+      s_dz[j] = dz;
+      p.dz[gt * p.k + j] = dz;
+    }
   }
-  for (int j = 0; j < p.k; ++j) dz[j] = p.topk_gate[n0 + j] * (dz[j] - m);
-  if (threadIdx.x < p.k) p.dz[gt * p.k + threadIdx.x] = dz[threadIdx.x];
+  __syncthreads();
   const T* stg = reinterpret_cast<const T*>(p.dx_stage.p[s]) + (size_t)t * p.k * p.d;
   const T* wr = reinterpret_cast<const T*>(p.w_router);
   T* o = reinterpret_cast<T*>(p.d_x.p[s]) + (size_t)t * p.d;
@@ -254,17 +262,18 @@ __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
 #pragma unroll
     for (int i = 0; i < U; ++i) acc[i] = 0.0f;
     for (int j = 0; j < p.k; ++j) {
-      if (!loc[j]) continue;
+      if (!s_loc[j]) continue;
       uint4 v = ld16(stg + (size_t)j * p.d + u * U);
       const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
       for (int i = 0; i < U; ++i) acc[i] += to_f32<T>(e[i]);
     }
     for (int j = 0; j < p.k; ++j) {
-      uint4 v = ld16(wr + (size_t)ex[j] * p.d + u * U);
+      const float dz = s_dz[j];
+      uint4 v = ld16(wr + (size_t)s_e[j] * p.d + u * U);
       const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-      for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz[j], to_f32<T>(e[i]), acc[i]);
+      for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz, to_f32<T>(e[i]), acc[i]);
     }
     uint4 ov;
     T* oe = reinterpret_cast<T*>(&ov);
@@ -275,44 +284,103 @@ __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
 }
 
 // ------------------------------------------------------------------ 6. dW_router
-// grid: (column blocks of 256, expert groups of 16, kRouterChunks token chunks)
-template <typename T>
-__global__ __launch_bounds__(kThreads) void dwr_part_kernel(BwdPlan p, int64_t n_own, int64_t per) {
-  const int c = blockIdx.x * kThreads + threadIdx.x;
-  const int e0 = blockIdx.y * 16;
-  const int64_t ta = (int64_t)blockIdx.z * per;
-  const int64_t tb = ta + per < n_own ? ta + per : n_own;
-  float acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  const bool col = c < p.d;
-  for (int64_t gt = ta; gt < tb; ++gt) {
-    const int s = p.own_lo + (int)(gt / p.T_src);
-    const int t = (int)(gt % p.T_src);
-    const int64_t n0 = ((int64_t)s * p.T_src + t) * p.k;
-    const float xv = col ? to_f32<T>(reinterpret_cast<const T*>(p.src_x.p[s])[(size_t)t * p.d + c]) : 0.0f;
-    for (int j = 0; j < p.k; ++j) {
-      const int e = p.topk_idx[n0 + j] - e0;
-      const float z = p.dz[gt * p.k + j];
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (e == i) acc[i] = __builtin_fmaf(z, xv, acc[i]);
-    }
-  }
-  if (!col) return;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (e0 + i < p.E)
-      p.dwr_part[((size_t)blockIdx.z * p.E + e0 + i) * p.d + c] = acc[i];
+// The own tokens' items are grouped by expert (the same stable counting-sort
+// layout as the forward pass, over all E experts); the rows of every expert
+// are cut into chunks of kRChunk rows.  One workgroup sums one chunk in row
+// order (partial[chunk][d]); a second kernel sums each expert's chunks in
+// chunk order.
+constexpr int kRChunk = 64;
+
+__global__ void iota_kernel(int32_t* v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = i;
 }
 
-__global__ __launch_bounds__(kThreads) void dwr_reduce_kernel(BwdPlan p, int nchunk) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t tot = (int64_t)p.E * p.d;
-  if (i >= tot) return;
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dwr_part_kernel(BwdPlan p, int N_own) {
+  __shared__ int s_prefix[257];
+  __shared__ int s_tok[kRChunk];
+  __shared__ float s_dz[kRChunk];
+  // chunk -> (expert, rows): same prefix search as the grouped GEMM tiles
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int loc[4], run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      int c = 0;
+      if (e < p.E) {
+        const int lo = p.r_offsets[e], hi = p.r_offsets[e + 1];
+        c = (hi - lo + kRChunk - 1) / kRChunk;
+      }
+      loc[q] = c;
+      run += c;
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    int excl = incl - run;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s_prefix[lane * 4 + q] = excl;
+      excl += loc[q];
+    }
+    if (lane == 63) s_prefix[256] = incl;
+  }
+  __syncthreads();
+  const int chunk = blockIdx.x;
+  const int total = s_prefix[p.E];
+  if (chunk >= total) return;
+  int lo = 0, hi = p.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_prefix[mid] <= chunk) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = p.r_offsets[e] + (chunk - s_prefix[e]) * kRChunk;
+  const int r1 = min(r0 + kRChunk, p.r_offsets[e + 1]);
+  const int nr = r1 - r0;
+  if (threadIdx.x < nr) {
+    const int n = p.r_row_src[r0 + threadIdx.x];  // item index among the own items
+    s_tok[threadIdx.x] = n / p.k;
+    s_dz[threadIdx.x] = p.dz[n];
+  }
+  __syncthreads();
+  constexpr int U = 16 / sizeof(T);
+  float* out = p.dwr_part + (size_t)chunk * p.d;
+  for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
+    float acc[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) acc[i] = 0.0f;
+    for (int r = 0; r < nr; ++r) {
+      const int gt = s_tok[r];
+      const int s = p.own_lo + gt / p.T_src, t = gt % p.T_src;
+      uint4 v = ld16(reinterpret_cast<const T*>(p.src_x.p[s]) + (size_t)t * p.d + u * U);
+      const T* xe = reinterpret_cast<const T*>(&v);
+      const float z = s_dz[r];
+#pragma unroll
+      for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(z, to_f32<T>(xe[i]), acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) out[u * U + i] = acc[i];
+  }
+}
+
+// dW_router[e][c] = sum over e's chunks in order; grid (column blocks, E)
+__global__ __launch_bounds__(kThreads) void dwr_reduce_kernel(BwdPlan p) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c >= p.d) return;
+  int c0 = 0;
+  for (int q = 0; q < e; ++q)
+    c0 += (p.r_offsets[q + 1] - p.r_offsets[q] + kRChunk - 1) / kRChunk;
+  const int nc = (p.r_offsets[e + 1] - p.r_offsets[e] + kRChunk - 1) / kRChunk;
   float acc = 0.0f;
-  for (int c = 0; c < nchunk; ++c) acc += p.dwr_part[(size_t)c * tot + i];
-  p.dw_router[i] = acc;
+  for (int q = 0; q < nc; ++q) acc += p.dwr_part[(size_t)(c0 + q) * p.d + c];
+  p.dw_router[(size_t)e * p.d + c] = acc;
 }
 
 template <typename T>
@@ -343,20 +411,21 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   if (n_own > 0) {
     hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)n_own), dim3(kThreads), 0, stream, p);
     trace_mark(p.tr, "bwd_dx_sum_router", stream);
-    if (p.dw_router) {
-      const int64_t per = (n_own + kRouterChunks - 1) / kRouterChunks;
-      dim3 g((p.d + kThreads - 1) / kThreads, (p.E + 15) / 16, kRouterChunks);
-      hipLaunchKernelGGL(dwr_part_kernel<T>, g, dim3(kThreads), 0, stream, p, n_own, per);
-      trace_mark(p.tr, "bwd_dw_router_part", stream);
-      const int64_t tot = (int64_t)p.E * p.d;
-      hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
-                         dim3(kThreads), 0, stream, p, kRouterChunks);
-      trace_mark(p.tr, "bwd_dw_router_reduce", stream);
-    }
-  } else if (p.dw_router) {
-    const int64_t tot = (int64_t)p.E * p.d;
-    hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, p, 0);
+  }
+  if (p.dw_router) {
+    const int N_own = (int)(n_own * p.k);
+    hipLaunchKernelGGL(iota_kernel, dim3((p.E + 255) / 256), dim3(256), 0, stream, p.r_ident, p.E);
+    mok_status rc = launch_layout(N_own, p.E, p.E, N_own, p.topk_idx + (int64_t)p.own_lo * p.T_src * p.k,
+                                  p.r_ident, p.r_counts, p.r_offsets, p.r_row_src, p.r_dest_row,
+                                  p.r_scratch, nullptr, stream, nullptr);
+    if (rc != MOK_OK) return rc;
+    trace_mark(p.tr, "bwd_router_layout", stream);
+    const int nchunk = N_own / kRChunk + p.E;
+    hipLaunchKernelGGL(dwr_part_kernel<T>, dim3(nchunk), dim3(kThreads), 0, stream, p, N_own);
+    trace_mark(p.tr, "bwd_dw_router_part", stream);
+    dim3 g((p.d + kThreads - 1) / kThreads, p.E);
+    hipLaunchKernelGGL(dwr_reduce_kernel, g, dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_dw_router_reduce", stream);
   }
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }

@@ -6,11 +6,13 @@
 
 namespace mok {
 
-int route_geometry(int E, int* EG, int* TG, int* TB, int* dc);
-size_t route_smem_bytes(int E);
-mok_status launch_route(int prec, int T, int d, int E, int k, const void* x, const void* w,
-                        const float* bias, int32_t* topk_idx, float* topk_gate,
-                        hipStream_t stream, mok_trace* tr = nullptr);
+int route_geometry(int E, int T, int* EG, int* TG, int* TB, int* dc);
+size_t route_smem_bytes(int E, int T);
+// Routes T consecutive tokens starting at token 0 of source src_lo (sources
+// of T_src tokens each, contiguous in the table).
+mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, int T, int d,
+                        int E, int k, const void* w, const float* bias, int32_t* topk_idx,
+                        float* topk_gate, hipStream_t stream, mok_trace* tr = nullptr);
 
 size_t layout_ws_bytes(int64_t N, int E_local);
 mok_status launch_layout(int64_t N, int E, int E_local, int R_cap, const int32_t* topk,
@@ -64,10 +66,12 @@ struct BwdPlan {
   void* dy;      // [R_cap, d]
   void* dab;     // [R_cap, 2I]
   float* dz;     // [own tokens, k]
-  float* dwr_part;  // [kRouterChunks, E, d]
+  float* dwr_part;  // [N_own/64 + E, d] per-chunk partial router gradients
+  // router layout of the own items over all E experts (workspace)
+  int32_t *r_ident, *r_counts, *r_offsets, *r_row_src, *r_dest_row;
+  void* r_scratch;
   mok_trace* tr;    // host-side trace, may be null
 };
-constexpr int kRouterChunks = 32;
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
 
 }  // namespace mok

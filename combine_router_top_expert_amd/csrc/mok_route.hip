@@ -21,10 +21,11 @@ constexpr int kTE = 4;      // experts per thread
 constexpr int kMaxK = 16;
 
 struct RouteArgs {
-  const void* x;
+  SrcTable src;     // token buffers: token g of the launch is src.p[src_lo + g / T_src][g % T_src]
+  int src_lo, T_src;
   const void* w;
   const float* bias;
-  int32_t* topk_idx;
+  int32_t* topk_idx;  // [T, k] for the launch's tokens, in order
   float* topk_gate;
   int T, d, E, k;
   int EG, TG, TB;   // threads across experts, threads across tokens, tokens per block
@@ -76,7 +77,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int eg = tid % a.EG;
   const int tg = tid / a.EG;
   const bool computes = tg < a.TG;
-  const T* x = reinterpret_cast<const T*>(a.x);
   const T* w = reinterpret_cast<const T*>(a.w);
   const int Epad = a.EG * kTE;
 
@@ -92,7 +92,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       int t = u / UPR, q = u % UPR;
       float v[U];
       if (t0 + t < a.T) {
-        unpack<T>(ld16(x + (size_t)(t0 + t) * a.d + c0 + q * U), v);
+        const int g = t0 + t;
+        const T* x = reinterpret_cast<const T*>(a.src.p[a.src_lo + g / a.T_src]) +
+                     (size_t)(g % a.T_src) * a.d;
+        unpack<T>(ld16(x + c0 + q * U), v);
       } else {
 #pragma unroll
         for (int i = 0; i < U; ++i) v[i] = 0.0f;
@@ -205,23 +208,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
 // Block geometry for E experts: EG threads across experts (kTE each), TG across
 // tokens (TT each), TB tokens per block, dc-wide d chunks.  Returns TT.
-int route_geometry(int E, int* EG, int* TG, int* TB, int* dc) {
-  const int TT = E >= 128 ? 8 : 4;
+int route_geometry(int E, int T, int* EG, int* TG, int* TB, int* dc) {
   *EG = (E + kTE - 1) / kTE;
   int tg = kRouteThreads / *EG;
+  *dc = E > 256 ? 16 : 32;
+  // 4 tokens per thread, fewer when that leaves fewer than two workgroups per CU
+  int TT = 4;
+  while (TT > 1) {
+    int cap = 128 / TT;
+    int g = tg < cap ? tg : cap;
+    if ((T + g * TT - 1) / (g * TT) >= 512) break;
+    TT >>= 1;
+  }
   int cap = 128 / TT;
   *TG = tg < cap ? tg : cap;
   *TB = *TG * TT;
-  *dc = E > 256 ? 16 : 32;
   return TT;
 }
 
-mok_status launch_route(int prec, int T, int d, int E, int k, const void* x, const void* w,
-                        const float* bias, int32_t* topk_idx, float* topk_gate,
-                        hipStream_t stream, mok_trace* tr) {
+mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, int T, int d,
+                        int E, int k, const void* w, const float* bias, int32_t* topk_idx,
+                        float* topk_gate, hipStream_t stream, mok_trace* tr) {
   if (T == 0) return MOK_OK;
   RouteArgs a;
-  a.x = x;
+  a.src = src;
+  a.src_lo = src_lo;
+  a.T_src = T_src;
   a.w = w;
   a.bias = bias;
   a.topk_idx = topk_idx;
@@ -230,30 +242,32 @@ mok_status launch_route(int prec, int T, int d, int E, int k, const void* x, con
   a.d = d;
   a.E = E;
   a.k = k;
-  const int TT = route_geometry(E, &a.EG, &a.TG, &a.TB, &a.dc);
+  const int TT = route_geometry(E, T, &a.EG, &a.TG, &a.TB, &a.dc);
   a.xs_pitch = a.TB + 4;
   a.ws_pitch = a.EG * kTE + 4;
   a.zs_pitch = a.EG * kTE + 1;
-  size_t smem = route_smem_bytes(E);
+  size_t smem = route_smem_bytes(E, T);
   dim3 grid((T + a.TB - 1) / a.TB);
+  dim3 blk(kRouteThreads);
+#define MOK_ROUTE_LAUNCH(TY, TTV) \
+  hipLaunchKernelGGL((route_kernel<TY, TTV>), grid, blk, smem, stream, a)
   if (prec == MOK_F32) {
-    if (TT == 8)
-      hipLaunchKernelGGL((route_kernel<float, 8>), grid, dim3(kRouteThreads), smem, stream, a);
-    else
-      hipLaunchKernelGGL((route_kernel<float, 4>), grid, dim3(kRouteThreads), smem, stream, a);
+    if (TT == 4) MOK_ROUTE_LAUNCH(float, 4);
+    else if (TT == 2) MOK_ROUTE_LAUNCH(float, 2);
+    else MOK_ROUTE_LAUNCH(float, 1);
   } else {
-    if (TT == 8)
-      hipLaunchKernelGGL((route_kernel<bf16_t, 8>), grid, dim3(kRouteThreads), smem, stream, a);
-    else
-      hipLaunchKernelGGL((route_kernel<bf16_t, 4>), grid, dim3(kRouteThreads), smem, stream, a);
+    if (TT == 4) MOK_ROUTE_LAUNCH(bf16_t, 4);
+    else if (TT == 2) MOK_ROUTE_LAUNCH(bf16_t, 2);
+    else MOK_ROUTE_LAUNCH(bf16_t, 1);
   }
+#undef MOK_ROUTE_LAUNCH
   trace_mark(tr, "route", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
-size_t route_smem_bytes(int E) {
+size_t route_smem_bytes(int E, int T) {
   int EG, TG, TB, dc;
-  route_geometry(E, &EG, &TG, &TB, &dc);
+  route_geometry(E, T, &EG, &TG, &TB, &dc);
   size_t stage = (size_t)dc * (TB + 4) + (size_t)dc * (EG * kTE + 4);
   size_t logits = (size_t)TB * (EG * kTE + 1);
   return sizeof(float) * (stage > logits ? stage : logits);

@@ -30,7 +30,7 @@ bool valid_cfg(const mok_config* c) {
 
 struct Ws {
   size_t layout, xperm, xscale, hscale, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
-      r_row_src, r_dest_row, r_scratch, total;
+      r_row_src, r_dest_row, r_scratch, bx, total;
 };
 
 Ws ws_layout(const mok_config* c) {
@@ -71,6 +71,8 @@ Ws ws_layout(const mok_config* c) {
   b += align256((size_t)N * sizeof(int32_t));
   w.r_scratch = b;
   b += align256(c->E <= 256 ? layout_ws_bytes(N, c->E) : 0);
+  w.bx = b;
+  b += align256(R * c->d * act_bytes(c->prec));
   w.total = f > b ? f : b;
   return w;
 }
@@ -232,6 +234,11 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          (const uint8_t*)(wsb + wl.xscale), st->offsets, st->row_src, w,
                          (uint8_t*)st->h, (uint8_t*)(wsb + wl.hscale), st->ab, nullptr, &stg,
                          cfg->T_src, cfg->k, sm, tr);
+    } else if (cfg->prec == MOK_BF16) {
+      // the pull dispatch runs inside GEMM1: its A rows are read from the sources
+      rc = launch_ffn_bf16(cfg->d, cfg->I, cfg->E_local, cfg->R_cap, nullptr, &src, cfg->T_src,
+                           cfg->k, st->offsets, st->row_src, w->w_gate, w->w_up, w->w_down, st->h,
+                           st->ab, nullptr, &stg, sm, tr);
     } else {
       rc = launch_gather(cfg->prec, src, cfg->T_src, cfg->d, cfg->k, cfg->E_local, cfg->R_cap,
                          st->row_src, st->offsets, wsb + wl.xperm, nullptr, sm, tr);
@@ -313,6 +320,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.r_row_src = (int32_t*)(wsb + wl.r_row_src);
   p.r_dest_row = (int32_t*)(wsb + wl.r_dest_row);
   p.r_scratch = wsb + wl.r_scratch;
+  p.x_perm = wsb + wl.bx;
   p.tr = cfg->trace;
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);

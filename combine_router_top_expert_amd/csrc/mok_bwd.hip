@@ -385,6 +385,17 @@ __global__ __launch_bounds__(kThreads) void dwr_reduce_kernel(BwdPlan p) {
 
 template <typename T>
 mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
+  if (sizeof(T) == 2) {
+    if (p.R_cap > 0) {
+      hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
+      trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
+      mok_status rc = launch_gather(MOK_BF16, p.src_x, p.T_src, p.d, p.k, p.E_local, p.R_cap,
+                                    p.row_src, p.offsets, p.x_perm, nullptr, stream, p.tr);
+      if (rc != MOK_OK) return rc;
+    }
+    mok_status rc = launch_bwd_gemms_bf16(p, p.x_perm, stream);
+    if (rc != MOK_OK) return rc;
+  } else {
   if (p.R_cap > 0) {
     const int mt = grouped_mtiles_bound(p.R_cap, p.E_local);
     hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
@@ -406,6 +417,7 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
     hipLaunchKernelGGL((wgrad_kernel<T, 1>), dim3(p.E_local * mtn * ntn), dim3(kGemmThreads), 0,
                        stream, p, mtn, ntn);
     trace_mark(p.tr, "bwd_wgrad_down", stream);
+  }
   }
   const int64_t n_own = (int64_t)p.own_n * p.T_src;
   if (n_own > 0) {

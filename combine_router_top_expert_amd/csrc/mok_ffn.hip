@@ -140,6 +140,9 @@ mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void
                       const DstTable* staging, int T_src, int k, hipStream_t stream,
                       mok_trace* tr) {
   if (R_cap == 0) return MOK_OK;
+  if (prec == MOK_BF16)
+    return launch_ffn_bf16(d, I, E_local, R_cap, x, nullptr, T_src, k, offsets, row_src, wg, wu,
+                           wd, h, ab, y, staging, stream, tr);
   const int mt = grouped_mtiles_bound(R_cap, E_local);
   Ffn1Args a1;
   a1.x = x;

@@ -1,0 +1,459 @@
+// Pipelined bf16 tile engine for the expert grouped GEMMs (gfx950).
+//
+// One workgroup (4 waves, 2 x 2) computes a 256 x BN tile of
+// C[m][n] = sum_k A(m, k) B(n, k) in fp32; each wave owns 128 x BN/2 as
+// 32 x 32 blocks of v_mfma_f32_32x32x16_bf16.
+//
+// Operand tiles of BK k are staged through a ring of NS LDS stages.  Global memory is copied straight into LDS by
+// global_load_lds_dwordx4 (lane i of an instruction fills bytes 16i..16i+15
+// of a 1 KiB block), so no registers hold staged data and three stages are
+// in flight while the matrix cores consume the fourth.  Every lane picks the
+// global address of the 16 bytes its LDS slot must hold, which is how the
+// layouts below are swizzled:
+//   K-major operand (k contiguous in memory): LDS [rows][2 BK bytes] with
+//     the 16-byte chunks of a row XOR-swizzled by row, so the 16-lane phases
+//     of a ds_read_b128 fragment read hit 16 distinct bank groups.
+//   MN-major operand (m or n contiguous, k strided): LDS [BK k-rows][2 BN
+//     bytes]; chunk c of k-row r sits at c ^ (4 * (r & 3)).  Fragments are
+//     read with ds_read_b64_tr_b16: in each 16-lane group lane a points at
+//     (k0 + a/4, n0 + 4*(a%4)) and lane i receives k0..k0+3 of column n0 + i,
+//     i.e. the k-consecutive fragment the MFMA wants, without a transpose in
+//     registers.
+// Rows or k-rows outside the problem read a page of zeros, so contraction
+// tails contribute nothing and no address leaves its buffer.
+#pragma once
+
+#include "mok_common.h"
+
+namespace mok {
+namespace g2 {
+
+constexpr int kThreads = 256;
+constexpr int BM = 256;
+
+// Zeros read by lanes whose rows, k-rows or columns fall outside a problem.
+static __device__ const uint4 g_zero[64] = {};
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// One global_load_lds_dwordx4: lane i's 16 bytes from g land at LDS byte
+// lds_addr + 16 i.  Issued from inline assembly so that the compiler does not
+// treat it as a pending LDS write (it would otherwise wait for every load in
+// flight before each LDS read); the main loop orders it explicitly with
+// s_waitcnt vmcnt and barriers.  lds_addr must be wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* g, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ location, made wave-uniform.
+__device__ __forceinline__ unsigned lds_addr_of(const char* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const char*)p);
+}
+
+__device__ __forceinline__ unsigned wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// s_waitcnt on vmcnt only (expcnt, lgkmcnt at their maxima = no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// ---------------------------------------------------------------- operands
+// K-major operand tile: ROWS rows x BK k (k contiguous in memory).  LDS
+// [ROWS][2*BK bytes]; 16-byte chunk c of row r sits at c ^ ((r / RS) % CPR)
+// (CPR chunks per row, RS = 16 / CPR), which puts the 16 lanes of each
+// ds_read_b128 phase into 16 distinct bank groups.  rowptr(row) returns the
+// address of element k = 0 of the row, or nullptr for a padding row.
+template <int ROWS, int BK>
+struct KMajor {
+  static constexpr int CPR = BK / 8;            // chunks per row
+  static constexpr int RPI = 1024 / (2 * BK);   // rows per 1 KiB load
+  static constexpr int NI = ROWS / RPI / 4;     // loads per wave per stage
+  static constexpr int RS = 16 / CPR;
+  static constexpr int BYTES = ROWS * BK * 2;
+  const char* p[NI];
+  int adv[NI];
+  template <class RowPtr>
+  __device__ __forceinline__ void init(RowPtr rowptr) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int I = w * NI + j;
+      const int row = RPI * I + lane / CPR;
+      const int c = (lane % CPR) ^ ((row / RS) % CPR);
+      const bf16_t* rp = rowptr(row);
+      if (rp) {
+        p[j] = reinterpret_cast<const char*>(rp) + c * 16;
+        adv[j] = BK * 2;
+      } else {
+        p[j] = reinterpret_cast<const char*>(g_zero);
+        adv[j] = 0;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, unsigned lds_op) const {
+    const unsigned w = wave_id();
+#pragma unroll
+    for (int j = 0; j < NI; ++j) load_lds16(p[j] + (size_t)kt * adv[j], lds_op + (w * NI + j) * 1024);
+  }
+  // fragment of rows [r0, r0+32), k16 step s: lane l reads row r0 + l%32
+  __device__ __forceinline__ static bf16x8_t frag(const char* lds_op, int r0, int s) {
+    const int lane = threadIdx.x & 63;
+    const int row = r0 + (lane & 31);
+    const int c = (2 * s + (lane >> 5)) ^ ((row / RS) % CPR);
+    return *reinterpret_cast<const bf16x8_t*>(lds_op + row * (2 * BK) + c * 16);
+  }
+};
+
+// MN-major operand tile: BK k-rows x COLS (m or n contiguous in memory,
+// k strided).  LDS [BK][2*COLS bytes]; chunk c of k-row r sits at
+// c ^ (4 * (r & 3)).  Fragments are read with ds_read_b64_tr_b16: in each
+// 16-lane group lane a points at (k0 + a/4, n0 + 4*(a%4)) and lane i
+// receives k0..k0+3 of column n0 + i -- the k-consecutive fragment the MFMA
+// wants, without a transpose in registers.  kptr(k) gives the address of
+// element (k, 0) of the tile or nullptr outside the contraction; columns
+// >= ncols_left read zeros.
+template <int COLS, int BK>
+struct MNMajor {
+  static constexpr int RB = 2 * COLS;           // bytes per k-row
+  static constexpr int KPI = 1024 / RB;         // k-rows per 1 KiB load
+  static constexpr int CPK = COLS / 8;          // chunks per k-row
+  static constexpr int NI = BK / KPI / 4;       // loads per wave per stage
+  static constexpr int BYTES = BK * RB;
+  static_assert(CPK >= 16, "swizzle needs 16 chunks per k-row");
+  int ncols_left;
+  template <class KPtr>
+  __device__ __forceinline__ void issue(int kt, unsigned lds_op, KPtr kptr) const {
+    const int lane = threadIdx.x & 63;
+    const unsigned w = wave_id();
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int I = w * NI + j;
+      const int krow = KPI * I + lane / CPK;
+      const int c = (lane % CPK) ^ (4 * (krow & 3));
+      const bf16_t* kp = kptr(kt * BK + krow);
+      const void* src = (kp && c * 8 < ncols_left) ? (const void*)(kp + c * 8) : (const void*)g_zero;
+      load_lds16(src, lds_op + I * 1024);
+    }
+  }
+  __device__ __forceinline__ static bf16x8_t frag(const char* lds_op, int n0, int s) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, li = lane & 15;
+    const int n = n0 + 16 * (g & 1) + 4 * (li & 3);
+    const int kb = 16 * s + 8 * (g >> 1) + (li >> 2);
+    v4s lo, hi;
+    {
+      const int kr = kb;
+      const int c = (n >> 3) ^ (4 * (kr & 3));
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_op + kr * RB + c * 16 + (n & 7) * 2));
+    }
+    {
+      const int kr = kb + 4;
+      const int c = (n >> 3) ^ (4 * (kr & 3));
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_op + kr * RB + c * 16 + (n & 7) * 2));
+    }
+    bf16x8_t out;
+    short* o = reinterpret_cast<short*>(&out);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[q] = lo[q];
+      o[4 + q] = hi[q];
+    }
+    return out;
+  }
+};
+
+// ---------------------------------------------------------------- tile config
+// BM = 256 rows x BN columns per workgroup (4 waves, 2 x 2, each 128 x BN/2),
+// BK-wide k stages, NS stages in the LDS ring.
+template <int BN_, int BK_, int NS_>
+struct Cfg {
+  static constexpr int BN = BN_, BK = BK_, NS = NS_;
+  static constexpr int WNB = BN / 64;  // 32-column MFMA blocks per wave
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int SMEM = NS * STAGE;
+  static constexpr int LOADS = STAGE / 1024 / 4;  // per wave per stage
+  static_assert(NS >= 2 && NS <= 6 && (NS - 2) * LOADS < 64, "vmcnt range");
+};
+
+// The default configuration of the expert GEMMs.
+typedef Cfg<256, 64, 2> Default;
+
+template <class C>
+struct Acc {
+  f32x16_t c[4][C::WNB];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WNB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[i][j][v] = 0.0f;
+  }
+};
+
+// The MFMAs compute transposed 32 x 32 blocks (the B fragment goes in the
+// instruction's first operand), so lane l holds, for block (i, j), row
+// out_row(i) of the tile and the four consecutive columns
+// out_col(j, g) .. out_col(j, g) + 3 in accumulators 4g .. 4g+3: outputs
+// leave as 8- or 16-byte vectors, one row per lane.
+__device__ __forceinline__ int out_row(int i) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave >> 1) * 128 + i * 32 + (lane & 31);
+}
+template <class C>
+__device__ __forceinline__ int out_col(int j, int g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave & 1) * (C::BN / 2) + j * 32 + 8 * g + 4 * (lane >> 5);
+}
+
+// Four fp32 -> four bf16 packed in 8 bytes.
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+                    (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+}
+
+// Fragments of one k16 step for a wave: 4 row blocks of A, WNB column blocks of B.
+template <class C, bool A_MN, bool B_MN>
+struct Frags {
+  bf16x8_t a[4], b[C::WNB];
+  __device__ __forceinline__ void load(const char* As, const char* Bs, int s) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = A_MN ? MNMajor<BM, C::BK>::frag(As, wm * 128 + i * 32, s)
+                  : KMajor<BM, C::BK>::frag(As, wm * 128 + i * 32, s);
+#pragma unroll
+    for (int j = 0; j < C::WNB; ++j)
+      b[j] = B_MN ? MNMajor<C::BN, C::BK>::frag(Bs, wn * (C::BN / 2) + j * 32, s)
+                  : KMajor<C::BN, C::BK>::frag(Bs, wn * (C::BN / 2) + j * 32, s);
+  }
+};
+
+// One LDS stage of MFMAs, the LDS reads of k16 step s+1 in flight while the
+// MFMAs of step s run (two fragment register sets).
+template <class C, bool A_MN, bool B_MN>
+__device__ __forceinline__ void stage_mma(const char* As, const char* Bs, Acc<C>& acc) {
+  constexpr int S = C::BK / 16;
+  constexpr int NMFMA = 4 * C::WNB;                         // per k16 step
+  constexpr int NREAD = (A_MN ? 8 : 4) + (B_MN ? 2 : 1) * C::WNB;  // LDS reads per step
+  Frags<C, A_MN, B_MN> f[2];
+  f[0].load(As, Bs, 0);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (s + 1 < S) f[(s + 1) & 1].load(As, Bs, s + 1);
+    const Frags<C, A_MN, B_MN>& cur = f[s & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WNB; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc.c[i][j], 0, 0, 0);
+  }
+  __builtin_amdgcn_iglp_opt(0);
+}
+
+// Wait until at most `after` stages of N loads each are still in flight
+// (after = stages issued after the one about to be consumed, 0 .. MAXA).
+template <int N, int MAXA>
+__device__ __forceinline__ void wait_stages(int after) {
+  if constexpr (MAXA >= 4) {
+    if (after >= 4) { wait_vmcnt<4 * N>(); return; }
+  }
+  if constexpr (MAXA >= 3) {
+    if (after == 3) { wait_vmcnt<3 * N>(); return; }
+  }
+  if constexpr (MAXA >= 2) {
+    if (after == 2) { wait_vmcnt<2 * N>(); return; }
+  }
+  if constexpr (MAXA >= 1) {
+    if (after == 1) { wait_vmcnt<N>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Main loop over KT stages.  issueA(kt, lds) / issueB(kt, lds) issue this
+// wave's direct loads of one stage (lds = LDS byte address of the operand's
+// tile in the stage).
+template <class C, bool A_MN, bool B_MN, class IA, class IB>
+__device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* smem, Acc<C>& acc) {
+  acc.zero();
+  if (KT <= 0) return;
+  const unsigned lds0 = lds_addr_of(smem);
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s) {
+    if (s < KT) {
+      issueA(s, lds0 + s * C::STAGE);
+      issueB(s, lds0 + s * C::STAGE + C::A_BYTES);
+    }
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stages<C::LOADS, C::NS - 2>(min(KT - 1, kt + C::NS - 2) - kt);
+    // every wave's loads of stage kt have landed, and every wave is done with
+    // the stage the next issue overwrites
+    __builtin_amdgcn_s_barrier();
+    const int nk = kt + C::NS - 1;
+    if (nk < KT) {
+      const unsigned st = lds0 + (nk % C::NS) * C::STAGE;
+      issueA(nk, st);
+      issueB(nk, st + C::A_BYTES);
+    }
+    const char* cur = smem + (kt % C::NS) * C::STAGE;
+    stage_mma<C, A_MN, B_MN>(cur, cur + C::A_BYTES, acc);
+  }
+}
+
+// ---------------------------------------------------------------- epilogue staging
+// After the main loop every wave copies its 128 x BN/2 accumulator tile (as T =
+// float or bf16) into a private 32 KiB LDS region, then walks it row by row:
+// each lane takes one 16-byte chunk of a row, so the global stores (and the
+// loads of an epilogue's extra operands) of a wave instruction cover whole
+// rows instead of one 8-byte piece of 32 different rows.  Rows of a region
+// are XOR-swizzled by 16-byte chunk to keep both phases free of systematic
+// bank conflicts.  fp32 tiles of 256 bytes per row and more are staged in
+// several passes of ROWS rows.
+template <class C, typename T>
+struct WaveStage {
+  static constexpr int WCOLS = C::BN / 2;
+  static constexpr int PITCH = WCOLS * (int)sizeof(T);       // bytes per row
+  static constexpr int CPR = PITCH / 16;                      // chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);             // elements per chunk
+  static constexpr int ROWS = 32768 / PITCH < 128 ? 32768 / PITCH : 128;  // rows per pass
+  static constexpr int PASSES = 128 / ROWS;
+  static constexpr int SW = CPR < 32 ? CPR : 32;              // swizzle period
+  char* base;
+  __device__ __forceinline__ explicit WaveStage(char* smem) : base(smem + (threadIdx.x >> 6) * 32768) {}
+  __device__ __forceinline__ char* chunk_addr(int row, int c) const {
+    return base + row * PITCH + ((c ^ (row % SW)) * 16);
+  }
+  // copy accumulator rows [pass*ROWS, (pass+1)*ROWS) of the wave tile into the region
+  __device__ __forceinline__ void put(const Acc<C>& acc, int pass) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi * 32 < pass * ROWS || mi * 32 >= (pass + 1) * ROWS) continue;
+      const int row = mi * 32 + (lane & 31) - pass * ROWS;
+#pragma unroll
+      for (int nj = 0; nj < C::WNB; ++nj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nj * 32 + 8 * q + 4 * (lane >> 5);  // first of 4 columns
+          const f32x16_t& a = acc.c[mi][nj];
+          char* p = chunk_addr(row, col / EPC) + (col % EPC) * (int)sizeof(T);
+          if constexpr (sizeof(T) == 4)
+            *reinterpret_cast<float4*>(p) = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          else
+            *reinterpret_cast<uint2*>(p) = pack4_bf16(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }
+    }
+  }
+  __device__ __forceinline__ uint4 raw(int row, int c) const {
+    return *reinterpret_cast<const uint4*>(chunk_addr(row, c));
+  }
+  // the EPC values of chunk c of staged row `row` as floats
+  __device__ __forceinline__ void get(int row, int c, float* v) const {
+    const uint4 u = *reinterpret_cast<const uint4*>(chunk_addr(row, c));
+    if constexpr (sizeof(T) == 4) {
+      v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+      v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    } else {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+  }
+  // visit every chunk of the staged pass: fn(row_in_wave_tile, chunk) with
+  // CPR consecutive lanes per row
+  template <class Fn>
+  __device__ __forceinline__ void for_chunks(int pass, Fn fn) const {
+    const int lane = threadIdx.x & 63;
+    constexpr int RPI = 64 / CPR > 0 ? 64 / CPR : 1;  // rows per wave instruction
+    if constexpr (CPR <= 64) {
+#pragma unroll 4
+      for (int r0 = 0; r0 < ROWS; r0 += RPI) {
+        const int row = r0 + lane / CPR;
+        fn(pass * ROWS + row, row, lane % CPR);
+      }
+    }
+  }
+};
+
+// Wave-local ordering of LDS stores before LDS loads of the same wave.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// XCD-aware order: workgroup b is dispatched to XCD b % 8; give each XCD a
+// contiguous range of the `total` logical tiles so that neighbouring tiles
+// (which share operand panels) meet in the same L2.
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  const int per = total / 8;
+  if (b >= per * 8) return b;
+  return (b % 8) * per + b / 8;
+}
+
+// Grouped-M tiles (rows of expert e are [offsets[e], offsets[e+1]), BM-row
+// tiles): per-expert tile counts, exclusive-scanned by wave 0 into s_prefix.
+__device__ __forceinline__ int group_prefix(const int32_t* offsets, int E_local, int R_cap,
+                                            int* s_prefix) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int loc[4];
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      int c = 0;
+      if (e < E_local) {
+        int lo = min(offsets[e], R_cap), hi = min(offsets[e + 1], R_cap);
+        c = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+      }
+      loc[q] = c;
+      run += c;
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    int excl = incl - run;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s_prefix[lane * 4 + q] = excl;
+      excl += loc[q];
+    }
+    if (lane == 63) s_prefix[256] = incl;
+  }
+  __syncthreads();
+  return s_prefix[E_local < 256 ? E_local : 256];
+}
+
+struct GTile {
+  int e, r0, r1;
+};
+__device__ __forceinline__ GTile group_tile(const int32_t* offsets, int E_local, int R_cap,
+                                            const int* s_prefix, int mtile) {
+  int lo = 0, hi = E_local - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_prefix[mid] <= mtile) lo = mid; else hi = mid - 1;
+  }
+  GTile t;
+  t.e = lo;
+  const int end = min(offsets[lo + 1], R_cap);
+  t.r0 = offsets[lo] + (mtile - s_prefix[lo]) * BM;
+  t.r1 = min(t.r0 + BM, end);
+  return t;
+}
+
+}  // namespace g2
+}  // namespace mok

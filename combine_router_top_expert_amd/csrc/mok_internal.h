@@ -45,6 +45,14 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
                          const DstTable* staging, int T_src, int k, hipStream_t stream,
                          mok_trace* tr = nullptr);
 
+// bf16 forward GEMMs on the pipelined engine; x == null gathers the A rows
+// from the source table through row_src.
+mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
+                           const SrcTable* src, int T_src, int k, const int32_t* offsets,
+                           const int32_t* row_src, const void* wg, const void* wu, const void* wd,
+                           void* h, void* ab, void* y, const DstTable* staging,
+                           hipStream_t stream, mok_trace* tr = nullptr);
+
 struct BwdPlan {
   int prec;
   int S, T_src, d, E, k, I, E_local, R_cap;
@@ -70,8 +78,10 @@ struct BwdPlan {
   // router layout of the own items over all E experts (workspace)
   int32_t *r_ident, *r_counts, *r_offsets, *r_row_src, *r_dest_row;
   void* r_scratch;
+  void* x_perm;     // [R_cap, d] token rows gathered again for the wgrad GEMM
   mok_trace* tr;    // host-side trace, may be null
 };
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
+mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream);
 
 }  // namespace mok

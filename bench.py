@@ -8,6 +8,11 @@ backward.  Workload (default): the mid-size layer, T = 16384 tokens in 8
 source buffers of 2048, d = 2048, E = 64 experts all local, top-6, SwiGLU
 I = 1408, bf16 with fp32 accumulation, balanced routing.
 
+Other workloads (--workload): C3, one GPU's share of a 256-expert layer
+(own 4096 tokens, 8 local experts, Zipf 1.2 skew), forward + backward; C4,
+the mid-size layer in MXFP8, forward only (the MXFP8 layer has no backward
+pass); C5, the mid-size layer with Zipf 1.2 skew, forward + backward.
+
 Prints ONE JSON line on stdout: layer tokens/s (forward + backward), the
 forward-only rate, per-kernel average times (HIP events recorded by the
 library between its kernels on the layer's stream, during the timed steps),
@@ -37,20 +42,25 @@ def log(*a):
 
 def kernel_work(name, w, R):
     """Algorithmic work of one launch: ('mfma', flops) or ('hbm', bytes)."""
-    d, I, k, T = w.d, w.I, w.k, w.S * w.T_src
+    d, I, k = w.d, w.I, w.k
+    T = len(w.own) * w.T_src  # tokens combined / summed here (own sources)
     eb = 2 if w.prec != "f32" else 4
     gemm = {
         "ffn1_gate_up_swiglu": 2.0 * R * d * 2 * I,
         "ffn2_down": 2.0 * R * I * d,
+        "ffn1_gate_up_swiglu_mx": 2.0 * R * d * 2 * I,
+        "ffn2_down_mx": 2.0 * R * I * d,
         "bwd_dh_swiglu": 2.0 * R * d * I,
         "bwd_dx_push": 2.0 * R * 2 * I * d,
         "bwd_wgrad_gate_up": 2.0 * R * 2 * I * d,
         "bwd_wgrad_down": 2.0 * R * d * I,
     }
     if name in gemm:
-        return "mfma", gemm[name]
+        return ("mfma_fp8" if name.endswith("_mx") else "mfma"), gemm[name]
     moves = {
-        "gather": 2.0 * R * d * eb,                       # read token row, write slot row
+        # read token row, write slot row (MX: d E4M3 codes + d/32 scales)
+        "gather": R * d * 2.0 + (R * d * (1 + 1 / 32) if w.prec == "mxfp8" else R * d * eb),
+        "bwd_regather_x": 2.0 * R * d * eb,
         "combine": (T * k * d + T * d) * eb,              # read k pushed rows, write out
         "bwd_reverse_combine_pull": 3.0 * R * d * eb,     # read dout + y rows, write dy
         "bwd_dx_sum_router": (T * k * d + T * d) * eb,    # read k dx rows, write dX
@@ -62,32 +72,39 @@ def kernel_work(name, w, R):
 
 def cpu_baseline(w, host, n_tok):
     """Time the CPU oracle (single thread) on n_tok tokens of the workload:
-    routing, forward, backward and their share of the weight gradients."""
+    routing, forward, and -- where the workload has one -- backward with the
+    tokens' share of the weight gradients."""
     import numpy as np
 
     import oracle
     own = w.own
+    has_bwd = host["dout_val"] is not None
     toks = [(own[i % len(own)], (i * 7919) % w.T_src) for i in range(n_tok)]
     tok_x = np.stack([host["x_val"][s][t] for s, t in toks])
-    tok_d = np.stack([host["dout_val"][s][t] for s, t in toks])
     e2l = w.expert_to_local()
     t0 = time.perf_counter()
     idx, g = oracle.route(tok_x, host["wr_val"], host["bias"], w.k, w.prec)
+    # (MXFP8: the FFN rows take the weights as given; their cost does not
+    # depend on whether the values were rounded to MX first)
     oracle.fwd_tokens(tok_x, idx, g, e2l, host["wg_val"], host["wu_val"], host["wd_val"], w.prec)
-    _, dz, _ = oracle.bwd_tokens(tok_x, tok_d, idx, g, e2l, host["wr_val"], host["wg_val"],
-                                 host["wu_val"], host["wd_val"])
-    for le in range(w.E_local):
-        sel = [(i, j) for i in range(n_tok) for j in range(w.k) if e2l[idx[i, j]] == le]
-        if sel:
-            ii = [i for i, _ in sel]
-            oracle.expert_wgrad(tok_x[ii], np.array([g[i, j] for i, j in sel]), tok_d[ii],
-                                host["wg_val"][le], host["wu_val"][le], host["wd_val"][le])
-    oracle.router_wgrad(tok_x, idx, dz, w.E)
+    if has_bwd:
+        tok_d = np.stack([host["dout_val"][s][t] for s, t in toks])
+        _, dz, _ = oracle.bwd_tokens(tok_x, tok_d, idx, g, e2l, host["wr_val"], host["wg_val"],
+                                     host["wu_val"], host["wd_val"])
+        for le in range(w.E_local):
+            sel = [(i, j) for i in range(n_tok) for j in range(w.k) if e2l[idx[i, j]] == le]
+            if sel:
+                ii = [i for i, _ in sel]
+                oracle.expert_wgrad(tok_x[ii], np.array([g[i, j] for i, j in sel]), tok_d[ii],
+                                    host["wg_val"][le], host["wu_val"][le], host["wd_val"][le])
+        oracle.router_wgrad(tok_x, idx, dz, w.E)
     dt = time.perf_counter() - t0
+    what = ("forward + backward (routing, FFN rows, combine, backward rows, their "
+            "weight-gradient rows, router gradient)" if has_bwd else
+            "forward (routing, MX FFN rows, combine)")
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tok} tokens of the workload, forward + backward (routing, FFN rows, "
-                      f"combine, backward rows, their weight-gradient rows, router gradient); "
-                      f"{dt:.1f} s single-threaded float64 C"}
+            "sample": f"{n_tok} tokens of the workload, {what}; {dt:.1f} s single-threaded "
+                      f"float64 C"}
 
 
 def main():
@@ -114,8 +131,7 @@ def main():
         raise SystemExit("no GPU visible")
     dev = "cuda:0"
     w = synth.WORKLOADS[args.workload]
-    if w.prec == "mxfp8":
-        raise SystemExit("the MXFP8 workload has no backward pass in this build")
+    has_bwd = w.prec != "mxfp8"
     t0 = time.time()
     xs = [synth.gen_x(w, s) for s in range(w.S)]
     wr = synth.gen_router(w)
@@ -123,23 +139,29 @@ def main():
     wg = synth.gen_expert_weights(w, "gate")
     wu = synth.gen_expert_weights(w, "up")
     wd = synth.gen_expert_weights(w, "down")
-    dout = [synth.gen_dout(w, s) for s in range(w.S)]
+    dout = [synth.gen_dout(w, s) for s in range(w.S)] if has_bwd else None
     other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
     log(f"inputs generated in {time.time() - t0:.1f} s")
     N = w.S * w.T_src * w.k
-    R_cap = N if w.E_local == w.E else N  # every item can be local in the worst case
+    # row capacity: every item when all experts are local, else twice the
+    # balanced share (a layer latches MOK_ECAPACITY if routing exceeds it)
+    R_cap = N if w.E_local == w.E else min(N, 2 * N * w.E_local // w.E)
     L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
-                 len(w.own), device=dev)
+                 len(w.own), device=dev, with_bwd=has_bwd)
     L.set_inputs([to_device(a, w.prec, dev) for a, _ in xs], to_device(wr[0], w.prec, dev),
                  None if bias is None else torch.from_numpy(bias).to(dev),
                  torch.from_numpy(w.expert_to_local()).to(dev),
                  to_device(wg[0], w.prec, dev), to_device(wu[0], w.prec, dev),
                  to_device(wd[0], w.prec, dev), other_topk=other)
-    d_out = [to_device(a, w.prec, dev) for a, _ in dout]
+    d_out = [to_device(a, w.prec, dev) for a, _ in dout] if has_bwd else None
+
+    def step():
+        L.forward()
+        if has_bwd:
+            L.backward(d_out)
 
     for _ in range(args.warmup):
-        L.forward()
-        L.backward(d_out)
+        step()
     torch.cuda.synchronize()
     L.check_status()
     R = int(L.offsets[-1].item())
@@ -149,8 +171,7 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        L.forward()
-        L.backward(d_out)
+        step()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     Trace.detach(L.cfg)
@@ -163,7 +184,8 @@ def main():
     for name, ms in recs:
         per_kernel.setdefault(name, []).append(ms)
     fwd_names = {"route", "layout_count", "layout_scan", "layout_place", "gather",
-                 "ffn1_gate_up_swiglu", "ffn2_down", "combine"}
+                 "ffn1_gate_up_swiglu", "ffn2_down", "ffn1_gate_up_swiglu_mx", "ffn2_down_mx",
+                 "combine"}
     fwd_ms = sum(sum(v) for n, v in per_kernel.items() if n in fwd_names) / args.steps
     bwd_ms = sum(sum(v) for n, v in per_kernel.items() if n not in fwd_names) / args.steps
     kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps}
@@ -172,9 +194,9 @@ def main():
     dom = max(per_kernel, key=lambda n: sum(per_kernel[n]))
     kind, work = kernel_work(dom, w, R)
     avg_s = float(np.mean(per_kernel[dom])) * 1e-3
-    if kind == "mfma":
+    if kind in ("mfma", "mfma_fp8"):
         achieved = work / avg_s / 1e12
-        peak = PEAK_BF16_TFLOPS
+        peak = PEAK_FP8_TFLOPS if kind == "mfma_fp8" else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": None, "kernel": dom,
                 "algorithmic_flops_per_launch": work}
@@ -186,9 +208,10 @@ def main():
     # per-kernel roofline fractions, for the record
     for n, v in kernels.items():
         kd, wk = kernel_work(n, w, R)
-        if kd == "mfma":
+        if kd in ("mfma", "mfma_fp8"):
             v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
-            v["frac_mfma_peak"] = v["tflops"] / PEAK_BF16_TFLOPS
+            v["frac_mfma_peak"] = v["tflops"] / (PEAK_FP8_TFLOPS if kd == "mfma_fp8"
+                                                 else PEAK_BF16_TFLOPS)
         elif kd == "hbm":
             v["gbs"] = wk / (v["avg_ms"] * 1e-3) / 1e9
             v["frac_hbm_peak"] = v["gbs"] / PEAK_HBM_GBS
@@ -209,17 +232,17 @@ def main():
         "config": {"workload": f"{w.name}: T={T_tok} tokens ({w.S} sources x {w.T_src}), d={w.d}, "
                                f"E={w.E} ({w.E_local} local), top-{w.k}, SwiGLU I={w.I}, {w.prec}, "
                                f"{'Zipf %.1f skew' % w.zipf_s if w.zipf_s else 'balanced routing'}; "
-                               f"step = forward + backward",
+                               f"step = {'forward + backward' if has_bwd else 'forward'}",
                    "routed_rows": R, "path": "staged"},
         "fwd_tokens_per_s": T_tok / (fwd_ms * 1e-3),
         "fwd_ms": fwd_ms,
-        "bwd_ms": bwd_ms,
+        "bwd_ms": bwd_ms if has_bwd else None,
         "roofline": roof,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        host = {"x_val": [b for _, b in xs], "dout_val": [b for _, b in dout], "wr_val": wr[1],
-                "bias": bias, "wg_val": wg[1], "wu_val": wu[1], "wd_val": wd[1]}
+        host = {"x_val": [b for _, b in xs], "dout_val": [b for _, b in dout] if has_bwd else None,
+                "wr_val": wr[1], "bias": bias, "wg_val": wg[1], "wu_val": wu[1], "wd_val": wd[1]}
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_tokens)
     else:
         result["cpu_baseline"] = None

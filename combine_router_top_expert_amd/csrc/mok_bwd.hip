@@ -390,8 +390,9 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
       hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
       trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
       mok_status rc = launch_gather(MOK_BF16, p.src_x, p.T_src, p.d, p.k, p.E_local, p.R_cap,
-                                    p.row_src, p.offsets, p.x_perm, nullptr, stream, p.tr);
+                                    p.row_src, p.offsets, p.x_perm, nullptr, stream, nullptr);
       if (rc != MOK_OK) return rc;
+      trace_mark(p.tr, "bwd_regather_x", stream);
     }
     mok_status rc = launch_bwd_gemms_bf16(p, p.x_perm, stream);
     if (rc != MOK_OK) return rc;

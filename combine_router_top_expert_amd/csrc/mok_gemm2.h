@@ -49,6 +49,14 @@ __device__ __forceinline__ void load_lds16(const void* g, unsigned lds_addr) {
                : "memory", "m0");
 }
 
+// One global_load_lds_dword: lane i's 4 bytes from g land at lds_addr + 4 i.
+__device__ __forceinline__ void load_lds4(const void* g, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // LDS byte address of a __shared__ location, made wave-uniform.
 __device__ __forceinline__ unsigned lds_addr_of(const char* p) {
   return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const char*)p);
@@ -279,35 +287,40 @@ __device__ __forceinline__ void wait_stages(int after) {
   wait_vmcnt<0>();
 }
 
-// Main loop over KT stages.  issueA(kt, lds) / issueB(kt, lds) issue this
-// wave's direct loads of one stage (lds = LDS byte address of the operand's
-// tile in the stage).
-template <class C, bool A_MN, bool B_MN, class IA, class IB>
-__device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* smem, Acc<C>& acc) {
-  acc.zero();
+// Main loop over KT stages of C::STAGE bytes in an NS-deep LDS ring.
+// issue(kt, lds) issues this wave's C::LOADS direct loads of stage kt into the
+// stage at LDS byte address lds; compute(stage) consumes a landed stage.
+template <class C, class Issue, class Compute>
+__device__ __forceinline__ void pipeline(int KT, Issue issue, Compute compute, char* smem) {
   if (KT <= 0) return;
   const unsigned lds0 = lds_addr_of(smem);
 #pragma unroll
-  for (int s = 0; s < C::NS - 1; ++s) {
-    if (s < KT) {
-      issueA(s, lds0 + s * C::STAGE);
-      issueB(s, lds0 + s * C::STAGE + C::A_BYTES);
-    }
-  }
+  for (int s = 0; s < C::NS - 1; ++s)
+    if (s < KT) issue(s, lds0 + s * C::STAGE);
   for (int kt = 0; kt < KT; ++kt) {
     wait_stages<C::LOADS, C::NS - 2>(min(KT - 1, kt + C::NS - 2) - kt);
     // every wave's loads of stage kt have landed, and every wave is done with
     // the stage the next issue overwrites
     __builtin_amdgcn_s_barrier();
     const int nk = kt + C::NS - 1;
-    if (nk < KT) {
-      const unsigned st = lds0 + (nk % C::NS) * C::STAGE;
-      issueA(nk, st);
-      issueB(nk, st + C::A_BYTES);
-    }
-    const char* cur = smem + (kt % C::NS) * C::STAGE;
-    stage_mma<C, A_MN, B_MN>(cur, cur + C::A_BYTES, acc);
+    if (nk < KT) issue(nk, lds0 + (nk % C::NS) * C::STAGE);
+    compute(smem + (kt % C::NS) * C::STAGE);
   }
+}
+
+// bf16 main loop: issueA(kt, lds) / issueB(kt, lds) issue this wave's direct
+// loads of one stage (lds = LDS byte address of the operand's tile in the
+// stage).
+template <class C, bool A_MN, bool B_MN, class IA, class IB>
+__device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* smem, Acc<C>& acc) {
+  acc.zero();
+  pipeline<C>(
+      KT,
+      [&](int kt, unsigned st) {
+        issueA(kt, st);
+        issueB(kt, st + C::A_BYTES);
+      },
+      [&](const char* cur) { stage_mma<C, A_MN, B_MN>(cur, cur + C::A_BYTES, acc); }, smem);
 }
 
 // ---------------------------------------------------------------- epilogue staging

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from cases import make_host_case, oracle_fwd_tokens, rel_err, sample_tokens
+from cases import make_host_case, oracle_fwd_tokens, oracle_weights, rel_err, sample_tokens
 from combine_router_top_expert_amd import (STATUS, make_config, make_weights, mok_combine,
                                            mok_dispatch, mok_expert_ffn, mok_layout,
                                            mok_mx_quantize, mok_route, mok_workspace_bytes, synth)
@@ -219,6 +219,70 @@ def test_expert_ffn_rows(prec):
         assert rel_err(abg[r, :w.I], a) <= TOL[prec] and rel_err(abg[r, w.I:], b) <= TOL[prec]
 
 
+def _mx_h_close(hq, hs, ref_codes, ref_scales):
+    """GPU h (E4M3 codes + E8M0 scales) against the oracle's MX h.  h is
+    quantised from fp32 on the GPU and from fp64 in the oracle, so a value
+    lying within rounding noise of a code boundary may land one code step
+    away: require at most one step per element (two if its block scale
+    moved) and such elements to be rare."""
+    got = oracle.mx_dequantize(hq, hs)
+    ref = oracle.mx_dequantize(ref_codes, ref_scales)
+    # one E4M3 step at value v in a block of shared exponent X: <= |v| 2^-3
+    # (normal codes) or 2^(X-9) (subnormal codes)
+    sub = np.repeat(np.exp2(ref_scales.astype(np.float64) - 127 - 9), 32, axis=1)
+    one_step = np.maximum(np.abs(ref), np.abs(got)) * 2.0 ** -3 + sub
+    assert np.all(np.abs(got - ref) <= 2 * one_step)
+    frac = float(np.mean(hq != ref_codes))
+    _log(f"  h codes differing: {frac:.2e}")
+    assert frac <= 2e-3
+
+
+def test_expert_ffn_rows_mx():
+    w = _small("C4", S=2, T_src=150, d=256, E=6, k=2, I=384, own=[0, 1],
+               local_experts=list(range(6)))
+    _log("expert_ffn mxfp8")
+    c = make_host_case(w)
+    R = c.layout["R"]
+    cfg = make_config(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, "mxfp8", R)
+    toks = c.layout["row_src"] // w.k
+    xs_rows = np.stack([c.x_store[t // w.T_src][t % w.T_src] for t in toks])
+    xq = torch.zeros(R * w.d, dtype=torch.uint8, device=DEV)
+    xsc = torch.zeros(R * w.d // 32, dtype=torch.uint8, device=DEV)
+    mok_mx_quantize(R, w.d, to_device(xs_rows, "bf16", DEV), xq, xsc)
+    q = []
+    for a in (c.wg_store, c.wu_store, c.wd_store):
+        K = a.shape[-1]
+        cq = torch.zeros(a.size, dtype=torch.uint8, device=DEV)
+        cs = torch.zeros(a.size // 32, dtype=torch.uint8, device=DEV)
+        mok_mx_quantize(a.size // K, K, to_device(a, "bf16", DEV), cq, cs)
+        q.append((cq, cs))
+    W = make_weights(q[0][0], q[1][0], q[2][0], q[0][1], q[1][1], q[2][1])
+    hq = torch.zeros(R * w.I, dtype=torch.uint8, device=DEV)
+    hs = torch.zeros(R * w.I // 32, dtype=torch.uint8, device=DEV)
+    y = torch.zeros(R, w.d, dtype=torch.bfloat16, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mok_expert_ffn(cfg, xq, xsc, torch.from_numpy(c.layout["offsets"]).to(DEV), W, hq, hs, None,
+                   y, st)
+    torch.cuda.synchronize()
+    wg, wu, wd = oracle_weights(c)
+    yg = y.float().cpu().numpy()
+    offs = c.layout["offsets"]
+    h_ref = np.zeros((R, w.I))
+    y_ref = np.zeros((R, w.d))
+    for r in range(R):
+        le = int(np.searchsorted(offs, r, side="right") - 1)
+        t = toks[r]
+        _, _, h_ref[r], y_ref[r] = oracle.ffn_row(c.x_val[t // w.T_src][t % w.T_src], wg[le],
+                                                  wu[le], wd[le], "mxfp8")
+    e_y = rel_err(yg, y_ref)
+    _log(f"  y rel err {e_y:.3e}")
+    assert e_y <= TOL["mxfp8"]
+    # h: the oracle's MX h is exactly representable, so re-quantising it
+    # returns its codes and scales
+    rc, rs = oracle.mx_quantize(h_ref)
+    _mx_h_close(hq.cpu().numpy().reshape(R, w.I), hs.cpu().numpy().reshape(R, w.I // 32), rc, rs)
+
+
 FWD_CASES = {
     "c1": synth.WORKLOADS["C1"],
     "bf16_small": _small("C2", S=2, T_src=300, d=256, E=8, k=2, I=320, own=[0, 1],
@@ -226,6 +290,11 @@ FWD_CASES = {
     "bf16_share": _small("C3", S=3, T_src=65, d=128, E=16, k=4, I=192, own=[1],
                          local_experts=[1, 4, 7, 10, 13], zipf_s=0.0),
     "c2_full": synth.WORKLOADS["C2"],
+    "mx_small": _small("C4", S=2, T_src=300, d=256, E=8, k=2, I=256, own=[0, 1],
+                       local_experts=list(range(8))),
+    "mx_share": _small("C4", S=3, T_src=65, d=128, E=16, k=4, I=384, own=[1],
+                       local_experts=[1, 4, 7, 10, 13]),
+    "c4_full": synth.WORKLOADS["C4"],
 }
 
 
@@ -266,8 +335,9 @@ def test_layer_fwd(name):
     L.forward()
     torch.cuda.synchronize()
     L.check_status()
-    n = 24 if name == "c2_full" else min(w.T_src * len(w.own), 64)
-    toks = sample_tokens(w, n) if name == "c2_full" else sorted(
+    full = name.endswith("_full")
+    n = 24 if full else min(w.T_src * len(w.own), 64)
+    toks = sample_tokens(w, n) if full else sorted(
         {(s, t) for s in w.own for t in range(w.T_src)})[:: max(1, (w.T_src * len(w.own)) // n)]
     _check_fwd(c, L, toks)
 

@@ -42,7 +42,7 @@ class mok_config(ctypes.Structure):
                 ("E_local", ctypes.c_int32), ("prec", ctypes.c_int32), ("R_cap", ctypes.c_int32),
                 ("minibatch_rows", ctypes.c_int32), ("ring_bytes", ctypes.c_int64),
                 ("comm_wgs", ctypes.c_int32), ("gemm_wgs", ctypes.c_int32),
-                ("trace", ctypes.c_void_p)]
+                ("wait_limit_us", ctypes.c_int32), ("trace", ctypes.c_void_p)]
 
 
 class mok_trace(ctypes.Structure):
@@ -208,9 +208,9 @@ def _check(fn: str, rc: int):
 
 
 def make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows=256, ring_bytes=0,
-                comm_wgs=0, gemm_wgs=0) -> mok_config:
+                comm_wgs=0, gemm_wgs=0, wait_limit_us=0) -> mok_config:
     return mok_config(S, T_src, d, E, k, I, E_local, PREC.get(prec, prec), R_cap, minibatch_rows,
-                      ring_bytes, comm_wgs, gemm_wgs, None)
+                      ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, None)
 
 
 def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> mok_expert_weights:

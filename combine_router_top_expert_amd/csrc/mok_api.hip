@@ -25,11 +25,13 @@ bool valid_cfg(const mok_config* c) {
   int64_t N = (int64_t)c->S * c->T_src * c->k;
   if (N > 0x7FFFFFFF) return false;  // items are indexed by int32
   if (c->ring_bytes < 0) return false;
+  if (c->ring_bytes > 0 && c->minibatch_rows < 1) return false;
+  if (c->comm_wgs < 0 || c->gemm_wgs < 0 || c->wait_limit_us < 0) return false;
   return true;
 }
 
 struct Ws {
-  size_t layout, xperm, xscale, hscale, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
+  size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
       r_row_src, r_dest_row, r_scratch, bx, total;
 };
 
@@ -49,6 +51,13 @@ Ws ws_layout(const mok_config* c) {
   f += align256(c->prec == MOK_MXFP8 ? R * (c->d / 32) : 0);
   w.hscale = f;
   f += align256(c->prec == MOK_MXFP8 ? R * (c->I / 32) : 0);
+  w.ring = f;
+  w.ring_ctr = f;
+  if (c->ring_bytes > 0) {
+    f += align256((size_t)c->ring_bytes);
+    w.ring_ctr = f;
+    f += align256(ring_counter_bytes(c->R_cap, c->E_local, c->minibatch_rows));
+  }
   // backward pieces (same region)
   size_t b = base;
   w.dy = b;
@@ -197,7 +206,12 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
     return MOK_EINVAL;
   if (cfg->R_cap > 0 && (!st->row_src || !st->h)) return MOK_EINVAL;
   if (own_n > 0 && !out) return MOK_EINVAL;
-  if (cfg->ring_bytes > 0) return MOK_EINVAL;  // fused ring path: not available in this build
+  if (cfg->ring_bytes > 0 && cfg->R_cap > 0) {  // ring path: bf16 / MXFP8
+    if (!dev_status) return MOK_EINVAL;
+    const mok_status rc = ring_check(cfg->prec, cfg->d, cfg->I, cfg->minibatch_rows,
+                                     cfg->ring_bytes, cfg->comm_wgs, cfg->gemm_wgs, nullptr, nullptr);
+    if (rc != MOK_OK) return rc;
+  }
   hipStream_t sm = (hipStream_t)stream;
   mok_trace* tr = cfg->trace;
   trace_mark(tr, "start", sm);
@@ -222,7 +236,37 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   char* wsb = (char*)ws;
   DstTable stg;
   fill_table(&stg, (const void* const*)staging, cfg->S);
-  if (cfg->R_cap > 0) {
+  if (cfg->R_cap > 0 && cfg->ring_bytes > 0) {
+    // one persistent launch: dispatch workgroups fill ring slots, GEMM
+    // workgroups run GEMM1 + SwiGLU and GEMM2 and push to staging
+    RingPlan p;
+    memset(&p, 0, sizeof(p));
+    p.prec = cfg->prec;
+    fill_table(&p.src, src_x, cfg->S);
+    p.row_src = st->row_src;
+    p.offsets = st->offsets;
+    p.d = cfg->d;
+    p.I = cfg->I;
+    p.E_local = cfg->E_local;
+    p.R_cap = cfg->R_cap;
+    p.T_src = cfg->T_src;
+    p.k = cfg->k;
+    p.mb = cfg->minibatch_rows;
+    p.ring_bytes = cfg->ring_bytes;
+    p.comm_wgs = cfg->comm_wgs;
+    p.gemm_wgs = cfg->gemm_wgs;
+    p.wait_limit_us = cfg->wait_limit_us;
+    p.ring = wsb + wl.ring;
+    p.counters = (int32_t*)(wsb + wl.ring_ctr);
+    p.status = dev_status;
+    p.w = w;
+    p.h = st->h;
+    p.h_scale = (uint8_t*)(wsb + wl.hscale);
+    p.ab = cfg->prec == MOK_BF16 ? st->ab : nullptr;
+    p.staging = stg;
+    rc = launch_ring_fwd(p, sm, tr);
+    if (rc != MOK_OK) return rc;
+  } else if (cfg->R_cap > 0) {
     SrcTable src;
     fill_table(&src, src_x, cfg->S);
     if (cfg->prec == MOK_MXFP8) {

@@ -413,10 +413,11 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
   return (b % 8) * per + b / 8;
 }
 
-// Grouped-M tiles (rows of expert e are [offsets[e], offsets[e+1]), BM-row
-// tiles): per-expert tile counts, exclusive-scanned by wave 0 into s_prefix.
+// Grouped-M tiles (rows of expert e are [offsets[e], offsets[e+1]), tiles of
+// tile_rows rows): per-expert tile counts, exclusive-scanned by wave 0 into
+// s_prefix; returns the total.
 __device__ __forceinline__ int group_prefix(const int32_t* offsets, int E_local, int R_cap,
-                                            int* s_prefix) {
+                                            int* s_prefix, int tile_rows = BM) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int loc[4];
@@ -427,7 +428,7 @@ __device__ __forceinline__ int group_prefix(const int32_t* offsets, int E_local,
       int c = 0;
       if (e < E_local) {
         int lo = min(offsets[e], R_cap), hi = min(offsets[e + 1], R_cap);
-        c = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+        c = hi > lo ? (hi - lo + tile_rows - 1) / tile_rows : 0;
       }
       loc[q] = c;
       run += c;
@@ -454,7 +455,7 @@ struct GTile {
   int e, r0, r1;
 };
 __device__ __forceinline__ GTile group_tile(const int32_t* offsets, int E_local, int R_cap,
-                                            const int* s_prefix, int mtile) {
+                                            const int* s_prefix, int mtile, int tile_rows = BM) {
   int lo = 0, hi = E_local - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -463,8 +464,8 @@ __device__ __forceinline__ GTile group_tile(const int32_t* offsets, int E_local,
   GTile t;
   t.e = lo;
   const int end = min(offsets[lo + 1], R_cap);
-  t.r0 = offsets[lo] + (mtile - s_prefix[lo]) * BM;
-  t.r1 = min(t.r0 + BM, end);
+  t.r0 = offsets[lo] + (mtile - s_prefix[lo]) * tile_rows;
+  t.r1 = min(t.r0 + tile_rows, end);
   return t;
 }
 

@@ -53,6 +53,35 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
                            void* h, void* ab, void* y, const DstTable* staging,
                            hipStream_t stream, mok_trace* tr = nullptr);
 
+// Persistent ring kernel of the forward pass (gather + GEMM1 + SwiGLU +
+// GEMM2 + push in one launch; see mok_ring.hip).
+struct RingPlan {
+  int prec;
+  SrcTable src;
+  const int32_t* row_src;
+  const int32_t* offsets;
+  int d, I, E_local, R_cap, T_src, k;
+  int mb;                 // minibatch rows
+  int64_t ring_bytes;
+  int comm_wgs, gemm_wgs, wait_limit_us;
+  void* ring;             // ring_bytes of workspace
+  int32_t* counters;      // ring_counter_bytes() of workspace
+  int32_t* status;
+  const mok_expert_weights* w;
+  void* h;                // [R_cap, I] (MX: codes)
+  uint8_t* h_scale;       // MX: [R_cap, I/32]
+  void* ab;               // [R_cap, 2I] or null (bf16)
+  DstTable staging;
+};
+int64_t ring_slot_bytes(int prec, int d, int mb);
+int ring_max_minibatches(int R_cap, int E_local, int mb);
+size_t ring_counter_bytes(int R_cap, int E_local, int mb);
+// Argument check of the ring path (also run by launch_ring_fwd); the auto
+// split of workgroups is returned through comm_out / gemm_out.
+mok_status ring_check(int prec, int d, int I, int mb, int64_t ring_bytes, int comm_wgs,
+                      int gemm_wgs, int* comm_out, int* gemm_out);
+mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr = nullptr);
+
 struct BwdPlan {
   int prec;
   int S, T_src, d, E, k, I, E_local, R_cap;

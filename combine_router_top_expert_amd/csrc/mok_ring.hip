@@ -1,0 +1,434 @@
+// Persistent ring kernel of the layer's forward pass (kucoin article,
+// section 02: the GPU's SMs are split into a side that dispatches, combines
+// and keeps state and a side that runs the expert FFN; the two hand work over
+// through local counters, a fixed-size ring token buffer whose space is reused
+// once the experts are done with it, and a minibatch size).
+//
+// One launch of comm_wgs + gemm_wgs workgroups, all resident at once (one per
+// CU).  The first comm_wgs workgroups to start take the dispatch role, the
+// rest the grouped-GEMM role.
+//
+// Work units.  Every local expert's rows [offsets[e], offsets[e+1]) are cut
+// into minibatches of at most MB rows, numbered m = 0 .. M-1 in expert order.
+// Minibatch m lives in ring slot m % nslot (MB token rows; MXFP8: their E4M3
+// codes and E8M0 scales).
+//   fill (m, c)   dispatch side: pull rows [32c, 32c+32) of minibatch m from
+//                 their source buffers into the slot (quantising for MXFP8);
+//                 waits until GEMM1 is done with the slot's previous
+//                 minibatch m - nslot; then x_ready[m] += 1.
+//   G1 (m, tile)  GEMM side: one 256 x BN tile of GEMM1 + SwiGLU over the
+//                 slot; waits for x_ready[m] == fill chunks of m; writes h
+//                 (and a | b) at the rows' global positions; then
+//                 g1_done[m] += 1.
+//   G2 (m, tile)  GEMM side: one tile of GEMM2 over h, pushed to the staging
+//                 rows (push combine); waits for g1_done[m] == GEMM1 tiles.
+// Each side takes its units from an atomic ticket counter in a fixed order:
+// fills by (m, c); GEMM work in steps u = 0, 1, ... each holding the GEMM1
+// tiles of minibatch u followed by the GEMM2 tiles of minibatch u - kLag.
+// Every wait is on work with a smaller ticket (GEMM2 on GEMM1 of an earlier
+// step, a fill on GEMM1 of minibatch m - nslot < m, GEMM1 on the fills of its
+// own step), and tickets are taken in order by running workgroups, so the
+// smallest unfinished unit can always proceed.  Every wait is also bounded in
+// time: on expiry the kernel latches MOK_ETIMEOUT, raises an abort flag that
+// every other wait checks, and all workgroups return.
+//
+// Ordering: a producer's lanes wait for their stores, the workgroup meets at
+// a barrier, and one lane increments the counter with release semantics at
+// agent scope (writing back the XCD's L2).  A consumer's lane acquires the
+// counter at agent scope (invalidating stale L2 and L1 lines) before the
+// workgroup's barrier, and only then issues its loads.
+//
+// The arithmetic of each tile is the same device code as the one-launch-per-
+// GEMM path (mok_ffn_tiles.h), and every output element is produced by exactly
+// one tile, so the two paths give bit-identical results for any ring size and
+// minibatch size.
+#include <string.h>
+
+#include "mok_ffn_tiles.h"
+#include "mok_internal.h"
+#include "mok_mx.h"
+
+namespace mok {
+
+namespace {
+
+using namespace g2;
+
+constexpr int kFillRows = 32;  // rows per fill unit
+constexpr int kLag = 2;        // GEMM2 of minibatch u runs in step u + kLag
+constexpr int kCtr = 4;        // fill ticket, GEMM ticket, role ticket, abort flag
+
+struct RingArgs {
+  SrcTable src;
+  const int32_t* row_src;
+  const int32_t* offsets;
+  int d, I, E_local, R_cap, T_src, k;
+  int mb, nslot, cpm, nmt, ntn1, ntn2, M_max;
+  int comm_wgs;
+  char* ring;
+  int64_t slot_bytes;
+  int32_t* ctr;        // [kCtr + 2 * M_max]: tickets, abort, x_ready[], g1_done[]
+  int32_t* status;
+  uint64_t wait_ticks;  // bound of one wait in s_memrealtime ticks (100 MHz)
+  F1Args f1;
+  F1MxArgs f1m;
+  F2Args f2;
+};
+
+__global__ void ring_init_kernel(int32_t* ctr, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) ctr[i] = 0;
+}
+
+// Control flow of the role loops.  Every value that steers a loop containing
+// a barrier is wave-uniform in the compiler's eyes (read back through
+// readfirstlane), and the single-thread steps (take a ticket, wait on a
+// counter, publish) run on all 64 lanes of wave 0 under a wave-uniform
+// branch rather than under `threadIdx.x == 0`.  With a lane-divergent branch
+// at the end of one iteration and the start of the next, the compiler
+// restructures the loop into nested loops whose exit masks send lanes 1..63
+// around the back edge to the next barrier before lane 0 has taken the next
+// ticket; the workgroup then never leaves the loop.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ bool wave0() { return uniform((int)(threadIdx.x >> 6)) == 0; }
+
+// Wave 0 waits until *p >= target: relaxed polls of the counter, then one
+// acquire fence at agent scope.  False if the wait ran out (MOK_ETIMEOUT
+// latched, abort raised) or another wait already did.
+__device__ bool ring_wait(int32_t* p, int target, const RingArgs& a) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    if (uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= target) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return true;
+    }
+    if (uniform(__hip_atomic_load(a.ctr + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+      return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > a.wait_ticks) {
+      latch(a.status, MOK_ETIMEOUT);
+      __hip_atomic_store(a.ctr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Workgroup-wide wait: wave 0 waits, the result is broadcast through LDS.
+__device__ bool wg_wait(int32_t* p, int target, const RingArgs& a, int* s_flag) {
+  if (wave0()) *s_flag = ring_wait(p, target, a) ? 1 : 0;
+  __syncthreads();
+  return uniform(*s_flag) != 0;
+}
+
+// Publish this workgroup's stores: every lane waits for its own stores, the
+// workgroup meets, then wave 0 adds 1 (lane 0 adds 1, the others 0) after a
+// release fence at agent scope.
+__device__ void wg_publish(int32_t* p) {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), expcnt(7), lgkmcnt(0)
+  __syncthreads();
+  if (wave0()) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(p, (threadIdx.x & 63) == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Next ticket of a counter for the workgroup (lane 0 of wave 0 adds 1, the
+// other lanes 0; lane 0's pre-value is the ticket).
+__device__ int wg_ticket(int32_t* p, int* s_val) {
+  if (wave0()) {
+    const int old = __hip_atomic_fetch_add(p, (threadIdx.x & 63) == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    *s_val = __builtin_amdgcn_readlane(old, 0);
+  }
+  __syncthreads();
+  return uniform(*s_val);
+}
+
+// Minibatch m -> (expert, rows [r0, r1)).
+__device__ __forceinline__ GTile minibatch(const RingArgs& a, const int* s_mbp, int m) {
+  GTile t = group_tile(a.offsets, a.E_local, a.R_cap, s_mbp, m, a.mb);
+  t.e = uniform(t.e);
+  t.r0 = uniform(t.r0);
+  t.r1 = uniform(t.r1);
+  return t;
+}
+
+// ---------------------------------------------------------------- dispatch side
+template <bool MX>
+__device__ void fill_rows(const RingArgs& a, char* slot, const GTile& mbt, int q0, int nr) {
+  const int upr = a.d / 8;  // 16-byte units (8 bf16) per row
+  const int total = nr * upr;
+  for (int u = threadIdx.x; u < total; u += kThreads) {
+    const int row = u / upr, c = u % upr;
+    const int q = q0 + row;  // row within the minibatch
+    const int tok = a.row_src[mbt.r0 + q] / a.k;
+    const bf16_t* src = reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
+                        (size_t)(tok % a.T_src) * a.d;
+    const uint4 v = ld16(src + c * 8);
+    if constexpr (!MX) {
+      st16(reinterpret_cast<bf16_t*>(slot) + (size_t)q * a.d + c * 8, v);
+    } else {
+      // a 32-element MX block is 4 consecutive units (4 lanes); upr % 4 == 0
+      // and kThreads % 4 == 0, so a lane group is all in or all out of the loop
+      float f[8];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      {
+        const int sh = mx_shared_exp(amax);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(f[i], -sh)) << (8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hi |= e4m3_code(__builtin_amdgcn_ldexpf(f[4 + i], -sh)) << (8 * i);
+        uint8_t* codes = reinterpret_cast<uint8_t*>(slot) + (size_t)q * a.d;
+        *reinterpret_cast<uint2*>(codes + c * 8) = make_uint2(lo, hi);
+        if ((c & 3) == 0) {
+          uint8_t* scales = reinterpret_cast<uint8_t*>(slot) + (size_t)a.mb * a.d + (size_t)q * (a.d / 32);
+          scales[c >> 2] = (uint8_t)(sh + 127);
+        }
+      }
+    }
+  }
+}
+
+template <bool MX>
+__device__ void dispatch_role(const RingArgs& a, int M, const int* s_mbp, int* s_val) {
+  int32_t* x_ready = a.ctr + kCtr;
+  int32_t* g1_done = x_ready + a.M_max;
+  const int nfill = M * a.cpm;
+  for (;;) {
+    const int f = wg_ticket(a.ctr + 0, s_val);
+    if (f >= nfill) return;
+    const int m = f / a.cpm, c = f % a.cpm;
+    const GTile mbt = minibatch(a, s_mbp, m);
+    if (m >= a.nslot && !wg_wait(g1_done + (m - a.nslot), a.nmt * a.ntn1, a, s_val + 1)) return;
+    const int q0 = c * kFillRows;
+    const int nr = min(kFillRows, (mbt.r1 - mbt.r0) - q0);
+    if (nr > 0) fill_rows<MX>(a, a.ring + (size_t)(m % a.nslot) * a.slot_bytes, mbt, q0, nr);
+    wg_publish(x_ready + m);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM side
+template <class C, bool MX>
+__device__ void gemm_role(const RingArgs& a, int M, const int* s_mbp, int* s_val, char* smem) {
+  int32_t* x_ready = a.ctr + kCtr;
+  int32_t* g1_done = x_ready + a.M_max;
+  const int n1 = a.nmt * a.ntn1, n2 = a.nmt * a.ntn2;
+  const int total = (M + kLag) * (n1 + n2);
+  for (;;) {
+    __syncthreads();  // the previous unit is done with LDS and the broadcast slots
+    const int t = wg_ticket(a.ctr + 1, s_val);
+    if (t >= total) return;
+    const int u = t / (n1 + n2);
+    int o = t % (n1 + n2);
+    if (o < n1) {
+      const int m = u;
+      if (m >= M) continue;
+      const int mt = o / a.ntn1, nt = o % a.ntn1;
+      const GTile mbt = minibatch(a, s_mbp, m);
+      GTile g;
+      g.e = mbt.e;
+      g.r0 = mbt.r0 + mt * BM;
+      g.r1 = min(mbt.r1, g.r0 + BM);
+      if (g.r0 < g.r1) {
+        if (!wg_wait(x_ready + m, a.cpm, a, s_val + 1)) return;
+        const char* slot = a.ring + (size_t)(m % a.nslot) * a.slot_bytes;
+        if constexpr (!MX) {
+          ffn1_tile<C>(a.f1, smem, g, nt, [&](int row) -> const bf16_t* {
+            const int r = g.r0 + row;
+            return r < g.r1 ? reinterpret_cast<const bf16_t*>(slot) + (size_t)(r - mbt.r0) * a.d
+                            : nullptr;
+          });
+        } else {
+          ffn1_mx_tile(
+              a.f1m, smem, g, nt,
+              [&](int row) -> const bf16_t* {
+                const int r = g.r0 + row;
+                return r < g.r1 ? reinterpret_cast<const bf16_t*>(slot + (size_t)(r - mbt.r0) * a.d)
+                                : nullptr;
+              },
+              [&](int row) -> const uint8_t* {
+                const int r = g.r0 + row;
+                return r < g.r1 ? reinterpret_cast<const uint8_t*>(slot) + (size_t)a.mb * a.d +
+                                      (size_t)(r - mbt.r0) * (a.d / 32)
+                                : nullptr;
+              });
+        }
+      }
+      wg_publish(g1_done + m);
+    } else {
+      const int m = u - kLag;
+      if (m < 0) continue;
+      o -= n1;
+      const int mt = o / a.ntn2, nt = o % a.ntn2;
+      const GTile mbt = minibatch(a, s_mbp, m);
+      GTile g;
+      g.e = mbt.e;
+      g.r0 = mbt.r0 + mt * BM;
+      g.r1 = min(mbt.r1, g.r0 + BM);
+      if (g.r0 >= g.r1) continue;
+      if (!wg_wait(g1_done + m, n1, a, s_val + 1)) return;
+      if constexpr (!MX)
+        ffn2_tile<C>(a.f2, smem, g, nt);
+      else
+        ffn2_mx_tile(a.f2, smem, g, nt);
+    }
+  }
+}
+
+template <class C, bool MX>
+__global__ __launch_bounds__(kThreads) void ring_kernel(RingArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  __shared__ int s_mbp[257];
+  __shared__ int s_val[2];
+  const int M = uniform(group_prefix(a.offsets, a.E_local, a.R_cap, s_mbp, a.mb));
+  const int role = wg_ticket(a.ctr + 2, s_val);
+  __syncthreads();  // every lane has read the role before s_val is reused
+  if (role < a.comm_wgs)
+    dispatch_role<MX>(a, M, s_mbp, s_val);
+  else
+    gemm_role<C, MX>(a, M, s_mbp, s_val, smem);
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+}  // namespace
+
+int64_t ring_slot_bytes(int prec, int d, int mb) {
+  const int64_t b = prec == MOK_MXFP8 ? (int64_t)mb * d + (int64_t)mb * (d / 32) : (int64_t)mb * d * 2;
+  return (b + 255) & ~(int64_t)255;
+}
+
+int ring_max_minibatches(int R_cap, int E_local, int mb) {
+  return (R_cap + mb - 1) / mb + E_local;
+}
+
+size_t ring_counter_bytes(int R_cap, int E_local, int mb) {
+  return (size_t)(kCtr + 2 * ring_max_minibatches(R_cap, E_local, mb)) * sizeof(int32_t);
+}
+
+mok_status ring_check(int prec, int d, int I, int mb, int64_t ring_bytes, int comm_wgs,
+                      int gemm_wgs, int* comm_out, int* gemm_out) {
+  if (prec != MOK_BF16 && prec != MOK_MXFP8) return MOK_EINVAL;
+  if (mb < 1) return MOK_EINVAL;
+  if (prec == MOK_MXFP8 && (d % MxCfg::KB != 0 || I % MxCfg::KB != 0)) return MOK_ESHAPE;
+  if (ring_bytes / ring_slot_bytes(prec, d, mb) < 1) return MOK_EINVAL;  // one minibatch at least
+  const int cus = device_cus();
+  if (cus <= 0) return MOK_EDEVICE;
+  const int comm = comm_wgs > 0 ? comm_wgs : (cus >= 64 ? cus / 8 : 1);
+  const int gemm = gemm_wgs > 0 ? gemm_wgs : cus - comm;
+  if (comm < 1 || gemm < 1 || comm + gemm > cus) return MOK_EINVAL;  // all resident: one per CU
+  if (comm_out) *comm_out = comm;
+  if (gemm_out) *gemm_out = gemm;
+  return MOK_OK;
+}
+
+mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr) {
+  int comm = 0, gemm = 0;
+  const mok_status ok = ring_check(p.prec, p.d, p.I, p.mb, p.ring_bytes, p.comm_wgs, p.gemm_wgs,
+                                   &comm, &gemm);
+  if (ok != MOK_OK) return ok;
+  const int64_t slot = ring_slot_bytes(p.prec, p.d, p.mb);
+  const int64_t nslot = p.ring_bytes / slot;
+  if (p.R_cap == 0) return MOK_OK;
+  RingArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src = p.src;
+  a.row_src = p.row_src;
+  a.offsets = p.offsets;
+  a.d = p.d;
+  a.I = p.I;
+  a.E_local = p.E_local;
+  a.R_cap = p.R_cap;
+  a.T_src = p.T_src;
+  a.k = p.k;
+  a.mb = p.mb;
+  a.nslot = nslot > (1 << 30) ? (1 << 30) : (int)nslot;
+  a.cpm = (p.mb + kFillRows - 1) / kFillRows;
+  a.nmt = (p.mb + BM - 1) / BM;
+  a.M_max = ring_max_minibatches(p.R_cap, p.E_local, p.mb);
+  a.comm_wgs = comm;
+  a.ring = reinterpret_cast<char*>(p.ring);
+  a.slot_bytes = slot;
+  a.ctr = p.counters;
+  a.status = p.status;
+  const uint64_t us = p.wait_limit_us > 0 ? (uint64_t)p.wait_limit_us : 2000000ull;
+  a.wait_ticks = us * 100;  // s_memrealtime runs at 100 MHz
+  if (p.prec == MOK_BF16) {
+    a.ntn1 = (p.I + Default::BN / 2 - 1) / (Default::BN / 2);
+    a.ntn2 = (p.d + Default::BN - 1) / Default::BN;
+    F1Args& f1 = a.f1;
+    f1.row_src = p.row_src;
+    f1.wg = reinterpret_cast<const bf16_t*>(p.w->w_gate);
+    f1.wu = reinterpret_cast<const bf16_t*>(p.w->w_up);
+    f1.offsets = p.offsets;
+    f1.h = reinterpret_cast<bf16_t*>(p.h);
+    f1.ab = reinterpret_cast<bf16_t*>(p.ab);
+    f1.d = p.d;
+    f1.I = p.I;
+    f1.E_local = p.E_local;
+    f1.R_cap = p.R_cap;
+    f1.ntn = a.ntn1;
+    f1.T_src = p.T_src;
+    f1.k = p.k;
+  } else {
+    a.ntn1 = (p.I + MxCfg::BN / 2 - 1) / (MxCfg::BN / 2);
+    a.ntn2 = (p.d + MxCfg::BN - 1) / MxCfg::BN;
+    F1MxArgs& f1 = a.f1m;
+    f1.wg = reinterpret_cast<const uint8_t*>(p.w->w_gate);
+    f1.wu = reinterpret_cast<const uint8_t*>(p.w->w_up);
+    f1.sg = p.w->s_gate;
+    f1.su = p.w->s_up;
+    f1.offsets = p.offsets;
+    f1.hq = reinterpret_cast<uint8_t*>(p.h);
+    f1.hs = p.h_scale;
+    f1.d = p.d;
+    f1.I = p.I;
+    f1.E_local = p.E_local;
+    f1.R_cap = p.R_cap;
+    f1.ntn = a.ntn1;
+  }
+  F2Args& f2 = a.f2;
+  f2.h = reinterpret_cast<const bf16_t*>(p.h);
+  f2.wd = reinterpret_cast<const bf16_t*>(p.w->w_down);
+  f2.hs = p.h_scale;
+  f2.sd = p.w->s_down;
+  f2.offsets = p.offsets;
+  f2.row_src = p.row_src;
+  f2.push = 1;
+  f2.staging = p.staging;
+  f2.d = p.d;
+  f2.I = p.I;
+  f2.E_local = p.E_local;
+  f2.R_cap = p.R_cap;
+  f2.ntn = a.ntn2;
+  f2.T_src = p.T_src;
+  f2.k = p.k;
+  const int nctr = kCtr + 2 * a.M_max;
+  hipLaunchKernelGGL(ring_init_kernel, dim3((nctr + 255) / 256), dim3(256), 0, stream, p.counters, nctr);
+  trace_mark(tr, "ring_init", stream);
+  if (p.prec == MOK_BF16)
+    hipLaunchKernelGGL((ring_kernel<Default, false>), dim3(comm + gemm), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((ring_kernel<MxCfg, true>), dim3(comm + gemm), dim3(kThreads), 0, stream, a);
+  trace_mark(tr, "ring_fused_ffn", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+}  // namespace mok

@@ -103,6 +103,9 @@ typedef struct mok_config {
   int64_t ring_bytes;     /* fused path: bytes of the ring of token slots; 0 = staged path */
   int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = auto) */
   int32_t gemm_wgs;       /* fused path: grouped-GEMM workgroups (0 = auto) */
+  int32_t wait_limit_us;  /* fused path: bound of every device-side wait in microseconds;
+                             on expiry MOK_ETIMEOUT is latched and the kernel returns
+                             (0 = 2 s) */
   mok_trace* trace;       /* optional kernel timing, NULL = off (host memory) */
 } mok_config;
 

@@ -66,3 +66,29 @@ def test_null_pointers_rejected(L):
     assert L.mok_layout(ctypes.byref(cfg), None, 1, 1, 1, 1, 1, 1, None, None) == -1
     assert L.mok_mx_quantize(4, 48, 1, 1, 1, None) == -1       # K % 32 != 0
     assert L.mok_combine(ctypes.byref(cfg), None, 1, 1, None, 0, 3, None, None, None) == -1
+
+
+def _layer_fwd_rc(L, cfg):
+    """mok_layer_fwd with dummy (never dereferenced) non-null pointers."""
+    S = cfg.S
+    tab = (ctypes.c_void_p * S)(*([1] * S))
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+    return L.mok_layer_fwd(ctypes.byref(cfg), 0, S, ctypes.cast(tab, ctypes.c_void_p), 1, None, 1,
+                           ctypes.byref(w), ctypes.byref(st), ctypes.cast(tab, ctypes.c_void_p),
+                           ctypes.cast(tab, ctypes.c_void_p), 1, 1, None)
+
+
+def test_ring_workspace_and_rejections(L):
+    base = mok.mok_workspace_bytes(_cfg())
+    ring = 3 << 20
+    assert mok.mok_workspace_bytes(_cfg(ring_bytes=ring)) >= max(base, ring)  # fwd and bwd share
+    assert mok.mok_workspace_bytes(_cfg(ring_bytes=ring, minibatch_rows=0)) == 0
+    assert mok.mok_workspace_bytes(_cfg(ring_bytes=ring, comm_wgs=-1)) == 0
+    assert mok.mok_workspace_bytes(_cfg(wait_limit_us=-5)) == 0
+    # the ring path takes bf16 or MXFP8 (rejected before any launch)
+    assert _layer_fwd_rc(L, _cfg(prec="f32", ring_bytes=ring)) == -1
+    # a ring smaller than one minibatch of rows (256 rows x 256 x 2 bytes)
+    assert _layer_fwd_rc(L, _cfg(ring_bytes=256 * 256 * 2 - 1, minibatch_rows=256)) == -1
+    # MXFP8 expert GEMMs need d and I multiples of 128
+    assert _layer_fwd_rc(L, _cfg(prec="mxfp8", I=192, ring_bytes=ring)) == -2

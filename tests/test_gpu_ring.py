@@ -1,0 +1,127 @@
+"""The persistent ring kernel (mok_layer_fwd with ring_bytes > 0) against the
+one-launch-per-GEMM path and the oracle.
+
+The ring path must give bit-identical h, a | b, staging rows and outputs for
+every ring size (down to one slot, so slots are recycled), minibatch size and
+split of workgroups between the dispatch and GEMM sides.  A wait bound set
+from the host (1 microsecond) must end in MOK_ETIMEOUT with every workgroup
+returning, after which the layer runs normally again."""
+import numpy as np
+import pytest
+import torch
+
+from cases import make_host_case, sample_tokens
+from combine_router_top_expert_amd import synth
+from test_gpu_parity import DEV, _check_fwd, _layer, _log, _small
+
+pytestmark = pytest.mark.gpu
+
+MiB = 1 << 20
+
+
+def _slot_bytes(w, mb):
+    b = mb * w.d * 2 if w.prec != "mxfp8" else mb * w.d + mb * (w.d // 32)
+    return (b + 255) // 256 * 256
+
+
+BF16_SMALL = _small("C2", S=2, T_src=300, d=256, E=8, k=2, I=320, own=[0, 1],
+                    local_experts=list(range(8)))
+SHARE = _small("C3", S=3, T_src=65, d=128, E=16, k=4, I=192, own=[1],
+               local_experts=[1, 4, 7, 10, 13], zipf_s=0.0)
+MX_SMALL = _small("C4", S=2, T_src=300, d=256, E=8, k=2, I=256, own=[0, 1],
+                  local_experts=list(range(8)))
+
+# name -> (workload, minibatch rows, ring slots or bytes, comm_wgs, gemm_wgs, oracle check)
+RING_CASES = {
+    "bf16_mb64_2slots_split4x12": (BF16_SMALL, 64, 2, 4, 12, True),
+    "bf16_mb256_1slot_auto": (BF16_SMALL, 256, 1, 0, 0, True),
+    "bf16_mb512_3slots_split2x30": (BF16_SMALL, 512, 3, 2, 30, False),
+    "bf16_mb32_1slot_split1x1": (BF16_SMALL, 32, 1, 1, 1, False),
+    "share_mb64_2slots": (SHARE, 64, 2, 3, 9, True),
+    "mx_mb128_2slots": (MX_SMALL, 128, 2, 4, 28, True),
+    "mx_mb256_1slot_auto": (MX_SMALL, 256, 1, 0, 0, False),
+    "c2_full_256MiB": (synth.WORKLOADS["C2"], 256, 256 * MiB, 0, 0, False),
+    "c4_full_64MiB": (synth.WORKLOADS["C4"], 256, 64 * MiB, 0, 0, False),
+}
+
+
+def _ring_bytes(w, mb, ring):
+    return ring if ring >= MiB else ring * _slot_bytes(w, mb)
+
+
+def _same(a, b):
+    a = a.view(torch.uint8) if a.dtype != torch.uint8 else a
+    b = b.view(torch.uint8) if b.dtype != torch.uint8 else b
+    return torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", list(RING_CASES))
+def test_ring_bit_identical_to_staged(name):
+    w, mb, ring, comm, gemm, check = RING_CASES[name]
+    _log("ring", name)
+    c = make_host_case(w)
+    ref = _layer(c, with_bwd=False)
+    ref.forward()
+    rb = _ring_bytes(w, mb, ring)
+    L = _layer(c, with_bwd=False, ring_bytes=rb, minibatch_rows=mb, comm_wgs=comm,
+               gemm_wgs=gemm)
+    L.forward()
+    torch.cuda.synchronize()
+    ref.check_status()
+    L.check_status()
+    R = int(c.layout["R"])
+    _log(f"  R={R} slots={rb // _slot_bytes(w, mb)} minibatches>={-(-R // mb)}")
+    if w.prec == "mxfp8":
+        n = R * w.I
+        assert _same(L.h[:n], ref.h[:n])
+    else:
+        assert _same(L.h[:R], ref.h[:R])
+        assert _same(L.ab[:R], ref.ab[:R])
+    for s in range(w.S):
+        assert _same(L.staging[s], ref.staging[s]), s
+    for s in w.own:
+        assert _same(L.out[s], ref.out[s]), s
+    if check:
+        toks = sorted({(s, t) for s in w.own for t in range(w.T_src)})[::5]
+        _check_fwd(c, L, toks)
+
+
+def test_ring_repeated_calls_bit_identical():
+    """Counters are re-armed on every call: three calls in a row agree."""
+    w = BF16_SMALL
+    _log("ring repeat")
+    c = make_host_case(w)
+    L = _layer(c, with_bwd=False, ring_bytes=2 * _slot_bytes(w, 64), minibatch_rows=64)
+    outs = []
+    for _ in range(3):
+        L.forward()
+        torch.cuda.synchronize()
+        L.check_status()
+        outs.append([t.clone() for t in L.staging] + [L.out[0].clone(), L.out[1].clone()])
+    for a, b in zip(outs[0], outs[2]):
+        assert _same(a, b)
+
+
+def test_ring_wait_bound_latches_timeout():
+    """A 1 us bound on every wait: the kernel ends with MOK_ETIMEOUT (the
+    waits of a C2-sized forward cannot all be met that fast) and every
+    workgroup returns; a normal call afterwards is correct."""
+    w = synth.WORKLOADS["C2"]
+    _log("ring timeout")
+    c = make_host_case(w)
+    rb = 4 * _slot_bytes(w, 256)
+    L = _layer(c, with_bwd=False, ring_bytes=rb, minibatch_rows=256, wait_limit_us=1)
+    L.forward()
+    torch.cuda.synchronize()
+    assert int(L.status.item()) == -5  # MOK_ETIMEOUT
+    ok = _layer(c, with_bwd=False, ring_bytes=rb, minibatch_rows=256)
+    ok.forward()
+    torch.cuda.synchronize()
+    ok.check_status()
+    ref = _layer(c, with_bwd=False)
+    ref.forward()
+    torch.cuda.synchronize()
+    for s in w.own:
+        assert _same(ok.out[s], ref.out[s])
+    toks = sample_tokens(w, 12)
+    _check_fwd(c, ok, toks)

@@ -50,13 +50,16 @@ def kernel_work(name, w, R):
         "ffn2_down": 2.0 * R * I * d,
         "ffn1_gate_up_swiglu_mx": 2.0 * R * d * 2 * I,
         "ffn2_down_mx": 2.0 * R * I * d,
+        # persistent ring kernel: pull into ring slots + GEMM1/SwiGLU + GEMM2 + push
+        "ring_fused_ffn": 2.0 * R * d * 2 * I + 2.0 * R * I * d,
         "bwd_dh_swiglu": 2.0 * R * d * I,
         "bwd_dx_push": 2.0 * R * 2 * I * d,
         "bwd_wgrad_gate_up": 2.0 * R * 2 * I * d,
         "bwd_wgrad_down": 2.0 * R * d * I,
     }
     if name in gemm:
-        return ("mfma_fp8" if name.endswith("_mx") else "mfma"), gemm[name]
+        fp8 = name.endswith("_mx") or (name == "ring_fused_ffn" and w.prec == "mxfp8")
+        return ("mfma_fp8" if fp8 else "mfma"), gemm[name]
     moves = {
         # read token row, write slot row (MX: d E4M3 codes + d/32 scales)
         "gather": R * d * 2.0 + (R * d * (1 + 1 / 32) if w.prec == "mxfp8" else R * d * eb),
@@ -107,54 +110,8 @@ def cpu_baseline(w, host, n_tok):
                       f"float64 C"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="C2")
-    ap.add_argument("--cpu-tokens", type=int, default=20)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
-              "(--gpus must be 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    from combine_router_top_expert_amd import Trace, synth
-    from combine_router_top_expert_amd.layer import MoELayer, to_device
-
-    if not torch.cuda.is_available():
-        raise SystemExit("no GPU visible")
-    dev = "cuda:0"
-    w = synth.WORKLOADS[args.workload]
-    has_bwd = w.prec != "mxfp8"
-    t0 = time.time()
-    xs = [synth.gen_x(w, s) for s in range(w.S)]
-    wr = synth.gen_router(w)
-    bias = synth.load_bias(w)
-    wg = synth.gen_expert_weights(w, "gate")
-    wu = synth.gen_expert_weights(w, "up")
-    wd = synth.gen_expert_weights(w, "down")
-    dout = [synth.gen_dout(w, s) for s in range(w.S)] if has_bwd else None
-    other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
-    log(f"inputs generated in {time.time() - t0:.1f} s")
-    N = w.S * w.T_src * w.k
-    # row capacity: every item when all experts are local, else twice the
-    # balanced share (a layer latches MOK_ECAPACITY if routing exceeds it)
-    R_cap = N if w.E_local == w.E else min(N, 2 * N * w.E_local // w.E)
-    L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
-                 len(w.own), device=dev, with_bwd=has_bwd)
-    L.set_inputs([to_device(a, w.prec, dev) for a, _ in xs], to_device(wr[0], w.prec, dev),
-                 None if bias is None else torch.from_numpy(bias).to(dev),
-                 torch.from_numpy(w.expert_to_local()).to(dev),
-                 to_device(wg[0], w.prec, dev), to_device(wu[0], w.prec, dev),
-                 to_device(wd[0], w.prec, dev), other_topk=other)
-    d_out = [to_device(a, w.prec, dev) for a, _ in dout] if has_bwd else None
-
+def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
+    """Warm up, time args.steps steps of the layer, and build the JSON record."""
     def step():
         L.forward()
         if has_bwd:
@@ -185,7 +142,7 @@ def main():
         per_kernel.setdefault(name, []).append(ms)
     fwd_names = {"route", "layout_count", "layout_scan", "layout_place", "gather",
                  "ffn1_gate_up_swiglu", "ffn2_down", "ffn1_gate_up_swiglu_mx", "ffn2_down_mx",
-                 "combine"}
+                 "ring_init", "ring_fused_ffn", "combine"}
     fwd_ms = sum(sum(v) for n, v in per_kernel.items() if n in fwd_names) / args.steps
     bwd_ms = sum(sum(v) for n, v in per_kernel.items() if n not in fwd_names) / args.steps
     kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps}
@@ -233,19 +190,98 @@ def main():
                                f"E={w.E} ({w.E_local} local), top-{w.k}, SwiGLU I={w.I}, {w.prec}, "
                                f"{'Zipf %.1f skew' % w.zipf_s if w.zipf_s else 'balanced routing'}; "
                                f"step = {'forward + backward' if has_bwd else 'forward'}",
-                   "routed_rows": R, "path": "staged"},
+                   "routed_rows": R,
+                   "path": ("ring %d MiB, minibatch %d rows, comm/gemm workgroups %s/%s"
+                            % (args.ring_mib, mb, args.comm_wgs or "auto",
+                               args.gemm_wgs or "auto")) if args.ring_mib else "staged"},
         "fwd_tokens_per_s": T_tok / (fwd_ms * 1e-3),
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms if has_bwd else None,
         "roofline": roof,
         "kernels": kernels,
     }
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--cpu-tokens", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring-mib", type=int, default=0,
+                    help="forward through the persistent ring kernel with a ring of this many "
+                         "MiB (0 = one launch per step)")
+    ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
+    ap.add_argument("--comm-wgs", type=int, default=0, help="ring path: dispatch workgroups")
+    ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
+    ap.add_argument("--mb-sweep", default="",
+                    help="ring path: comma-separated minibatch sizes, one JSON line each")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_router_top_expert_amd import Trace, synth
+    from combine_router_top_expert_amd.layer import MoELayer, to_device
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.workload]
+    has_bwd = w.prec != "mxfp8"
+    t0 = time.time()
+    xs = [synth.gen_x(w, s) for s in range(w.S)]
+    wr = synth.gen_router(w)
+    bias = synth.load_bias(w)
+    wg = synth.gen_expert_weights(w, "gate")
+    wu = synth.gen_expert_weights(w, "up")
+    wd = synth.gen_expert_weights(w, "down")
+    dout = [synth.gen_dout(w, s) for s in range(w.S)] if has_bwd else None
+    other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    N = w.S * w.T_src * w.k
+    # row capacity: every item when all experts are local, else twice the
+    # balanced share (a layer latches MOK_ECAPACITY if routing exceeds it)
+    R_cap = N if w.E_local == w.E else min(N, 2 * N * w.E_local // w.E)
+    dev_in = dict(xs=[to_device(a, w.prec, dev) for a, _ in xs], wr=to_device(wr[0], w.prec, dev),
+                  bias=None if bias is None else torch.from_numpy(bias).to(dev),
+                  e2l=torch.from_numpy(w.expert_to_local()).to(dev),
+                  wg=to_device(wg[0], w.prec, dev), wu=to_device(wu[0], w.prec, dev),
+                  wd=to_device(wd[0], w.prec, dev))
+    d_out = [to_device(a, w.prec, dev) for a, _ in dout] if has_bwd else None
+
+    def make_layer(mb):
+        L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
+                     len(w.own), device=dev, with_bwd=has_bwd, ring_bytes=args.ring_mib << 20,
+                     minibatch_rows=mb, comm_wgs=args.comm_wgs, gemm_wgs=args.gemm_wgs)
+        L.set_inputs(dev_in["xs"], dev_in["wr"], dev_in["bias"], dev_in["e2l"], dev_in["wg"],
+                     dev_in["wu"], dev_in["wd"], other_topk=other)
+        return L
+
+    mbs = [int(v) for v in args.mb_sweep.split(",")] if args.mb_sweep else [args.mb]
+    results = []
+    for mb in mbs:
+        L = make_layer(mb)
+        results.append(measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace))
+        del L
+        torch.cuda.empty_cache()
+    result = results[-1]
     if not args.no_cpu_baseline:
         host = {"x_val": [b for _, b in xs], "dout_val": [b for _, b in dout] if has_bwd else None,
                 "wr_val": wr[1], "bias": bias, "wg_val": wg[1], "wu_val": wu[1], "wd_val": wd[1]}
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_tokens)
     else:
         result["cpu_baseline"] = None
+    for r in results[:-1]:
+        r["cpu_baseline"] = None
+        print(json.dumps(r), flush=True)
     print(json.dumps(result), flush=True)
 
 

@@ -32,7 +32,7 @@ bool valid_cfg(const mok_config* c) {
 
 struct Ws {
   size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
-      r_row_src, r_dest_row, r_scratch, bx, total;
+      r_row_src, r_dest_row, r_scratch, bx, wpart, total;
 };
 
 Ws ws_layout(const mok_config* c) {
@@ -82,6 +82,8 @@ Ws ws_layout(const mok_config* c) {
   b += align256(c->E <= 256 ? layout_ws_bytes(N, c->E) : 0);
   w.bx = b;
   b += align256(R * c->d * act_bytes(c->prec));
+  w.wpart = b;
+  b += align256(c->prec == MOK_BF16 ? wgrad_partial_bytes(c->R_cap, c->d, c->I) : 0);
   w.total = f > b ? f : b;
   return w;
 }
@@ -365,6 +367,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.r_dest_row = (int32_t*)(wsb + wl.r_dest_row);
   p.r_scratch = wsb + wl.r_scratch;
   p.x_perm = wsb + wl.bx;
+  p.wg_part = (float*)(wsb + wl.wpart);
   p.tr = cfg->trace;
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);

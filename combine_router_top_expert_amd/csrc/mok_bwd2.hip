@@ -5,7 +5,8 @@
 //         two weight matrices read as [2I][d] -> epilogue pushes dx rows to
 //         their reverse-dispatch staging rows
 //   wgrad (per expert, contraction over the expert's rows in ascending row
-//         order; rows past the expert read zeros):
+//         order, split into chunks of 4096 rows whose partial sums are
+//         added in chunk order; rows past a chunk read zeros):
 //         [dW_gate; dW_up][e] = dab^T X_e   (A = dab, B = gathered rows X)
 //         dW_down[e]          = dy^T h_e    (A = dy,  B = h)
 // The m/n-contiguous operands are read with the transposing LDS fragment
@@ -150,21 +151,89 @@ struct WgArgs {
   const bf16_t* B;     // [R_cap, ldb]
   float* out0;         // MODE 0: dW_gate [E_local, I, d]; MODE 1: dW_down [E_local, d, I]
   float* out1;         // MODE 0: dW_up
+  float* part;         // [extra chunks, M, N] partial sums of chunks 1, 2, ... of an expert
   const int32_t* offsets;
   int lda, ldb, M, N, I, E_local, R_cap, mtn, ntn;
 };
 
+// Split-K of the weight gradients.  An expert's rows are cut into chunks of
+// kWgChunk rows (contraction length of one tile), so that a heavily routed
+// expert spreads over as many tiles as its rows need instead of one long
+// tile per output block.  Chunk 0 writes dW; chunk c >= 1 writes a partial
+// block, and wgrad_reduce adds the partials to dW in chunk order (a fixed
+// order: the result is run-to-run identical).
+constexpr int kWgChunk = 4096;
+
+// Wave 0 scans the per-expert chunk counts: s_cp[e] = chunks of the experts
+// before e, s_xp[e] = their chunks beyond the first (partial slots); index
+// 256 holds the totals.
+__device__ __forceinline__ void wg_chunk_prefix(const int32_t* offsets, int E_local, int R_cap,
+                                                int* s_cp, int* s_xp) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int ch[4], run_c = 0, run_x = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      int c = 0;
+      if (e < E_local) {
+        const int lo = min(offsets[e], R_cap), hi = min(offsets[e + 1], R_cap);
+        c = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 0;
+      }
+      ch[q] = c;
+      run_c += c;
+      run_x += c > 1 ? c - 1 : 0;
+    }
+    int inc_c = run_c, inc_x = run_x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oc = __shfl_up(inc_c, off, 64), ox = __shfl_up(inc_x, off, 64);
+      if (lane >= off) {
+        inc_c += oc;
+        inc_x += ox;
+      }
+    }
+    int ec = inc_c - run_c, ex = inc_x - run_x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s_cp[lane * 4 + q] = ec;
+      s_xp[lane * 4 + q] = ex;
+      ec += ch[q];
+      ex += ch[q] > 1 ? ch[q] - 1 : 0;
+    }
+    if (lane == 63) {
+      s_cp[256] = inc_c;
+      s_xp[256] = inc_x;
+    }
+  }
+  __syncthreads();
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  __shared__ int s_cp[257], s_xp[257];
+  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp);
+  // Chunks are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+  // b % 8) and a chunk's tiles stay on one XCD: chunks of a heavily routed
+  // expert spread over all XCDs while the tiles that share a chunk's operand
+  // rows share an L2.  The grid holds a multiple of 8 chunk slots.
   const int per = a.mtn * a.ntn;
-  const int total = a.E_local * per;
-  const int t = xcd_tile(blockIdx.x, total);
-  const int e = t / per;
-  const int mt = (t % per) / a.ntn, nt = t % a.ntn;
-  const int off = min(a.offsets[e], a.R_cap);
+  const int TC = s_cp[a.E_local < 256 ? a.E_local : 256];
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int q = xcd + 8 * (slot / per);
+  if (q >= TC) return;
+  const int tile = slot % per;
+  const int mt = tile / a.ntn, nt = tile % a.ntn;
+  int e = 0, hi = a.E_local - 1;
+  while (e < hi) {
+    const int mid = (e + hi + 1) >> 1;
+    if (s_cp[mid] <= q) e = mid; else hi = mid - 1;
+  }
+  const int c = q - s_cp[e];
   const int end = min(a.offsets[e + 1], a.R_cap);
-  const int cnt = end > off ? end - off : 0;
+  const int off = min(a.offsets[e], a.R_cap) + c * kWgChunk;
+  const int cnt = min(kWgChunk, end - off);
   const int m0 = mt * BM, n0 = nt * C::BN;
   MNMajor<BM, C::BK> la;
   MNMajor<C::BN, C::BK> lb;
@@ -185,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
                          });
                        },
                        smem, acc);
+  float* part = c > 0 ? a.part + (size_t)(s_xp[e] + c - 1) * a.M * a.N : nullptr;
   __syncthreads();
   const WaveStage<C, float> st(smem);
   const int wave = threadIdx.x >> 6;
@@ -192,22 +262,62 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   for (int pass = 0; pass < WaveStage<C, float>::PASSES; ++pass) {
     st.put(acc, pass);
     wave_lds_fence();
-    st.for_chunks(pass, [&](int trow, int srow, int c) {
+    st.for_chunks(pass, [&](int trow, int srow, int cc) {
       const int m = m0 + (wave >> 1) * 128 + trow;
-      const int col = n0 + (wave & 1) * (C::BN / 2) + c * 4;
+      const int col = n0 + (wave & 1) * (C::BN / 2) + cc * 4;
       if (m >= a.M || col >= a.N) return;
       float* dst;
-      if (MODE == 0)
+      if (part)
+        dst = part + (size_t)m * a.N;
+      else if (MODE == 0)
         dst = m < a.I ? a.out0 + ((size_t)e * a.I + m) * a.N : a.out1 + ((size_t)e * a.I + (m - a.I)) * a.N;
       else
         dst = a.out0 + ((size_t)e * a.M + m) * a.N;
-      *reinterpret_cast<uint4*>(dst + col) = st.raw(srow, c);
+      *reinterpret_cast<uint4*>(dst + col) = st.raw(srow, cc);
     });
     wave_lds_fence();
   }
 }
 
+// dW[e] += partial chunks 1, 2, ... of expert e, in chunk order; grid
+// (blocks per expert, E_local), experts with one chunk return at once.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void wgrad_reduce(WgArgs a) {
+  __shared__ int s_cp[257], s_xp[257];
+  const int e = blockIdx.y;
+  const int lo = min(a.offsets[e], a.R_cap), hi = min(a.offsets[e + 1], a.R_cap);
+  const int ch = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 0;
+  if (ch <= 1) return;
+  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp);
+  const int xp = s_xp[e];
+  const int n4 = a.N / 4;
+  const size_t units = (size_t)a.M * n4;
+  for (size_t u = (size_t)blockIdx.x * kThreads + threadIdx.x; u < units;
+       u += (size_t)gridDim.x * kThreads) {
+    const int m = (int)(u / n4), c4 = (int)(u % n4);
+    float* dst;
+    if (MODE == 0)
+      dst = m < a.I ? a.out0 + ((size_t)e * a.I + m) * a.N : a.out1 + ((size_t)e * a.I + (m - a.I)) * a.N;
+    else
+      dst = a.out0 + ((size_t)e * a.M + m) * a.N;
+    float4 v = *reinterpret_cast<const float4*>(dst + c4 * 4);
+    for (int c = 1; c < ch; ++c) {
+      const float4 p = *reinterpret_cast<const float4*>(a.part + (size_t)(xp + c - 1) * a.M * a.N +
+                                                        (size_t)m * a.N + c4 * 4);
+      v.x += p.x;
+      v.y += p.y;
+      v.z += p.z;
+      v.w += p.w;
+    }
+    *reinterpret_cast<float4*>(dst + c4 * 4) = v;
+  }
+}
+
 }  // namespace
+
+size_t wgrad_partial_bytes(int R_cap, int d, int I) {
+  return (size_t)(R_cap / kWgChunk) * 2 * (size_t)I * d * sizeof(float);
+}
 
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream) {
   const int mt = (p.R_cap + BM - 1) / BM + p.E_local;
@@ -242,7 +352,11 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
     hipLaunchKernelGGL(dx_g2<Default>, dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
     trace_mark(p.tr, "bwd_dx_push", stream);
   }
+  // grid bound of the split-K tiles: every expert's chunks, at most
+  // R_cap / kWgChunk + E_local of them, rounded up to a multiple of 8
+  const int max_chunks = (p.R_cap / kWgChunk + p.E_local + 7) / 8 * 8;
   WgArgs w;
+  w.part = p.wg_part;
   w.A = reinterpret_cast<const bf16_t*>(p.dab);
   w.B = reinterpret_cast<const bf16_t*>(x_perm);
   w.out0 = p.dw_gate;
@@ -257,9 +371,11 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.R_cap = p.R_cap;
   w.mtn = (w.M + BM - 1) / BM;
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(p.E_local * w.mtn * w.ntn)), dim3(kThreads), 0,
-                     stream, w);
+  hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
+                     dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_gate_up", stream);
+  hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+  trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
   w.A = reinterpret_cast<const bf16_t*>(p.dy);
   w.B = reinterpret_cast<const bf16_t*>(p.h);
   w.out0 = p.dw_down;
@@ -270,9 +386,11 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.N = p.I;
   w.mtn = (w.M + BM - 1) / BM;
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  hipLaunchKernelGGL((wgrad_g2<Default, 1>), dim3((unsigned)(p.E_local * w.mtn * w.ntn)), dim3(kThreads), 0,
-                     stream, w);
+  hipLaunchKernelGGL((wgrad_g2<Default, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
+                     dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down", stream);
+  hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+  trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

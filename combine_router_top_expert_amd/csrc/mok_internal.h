@@ -108,9 +108,11 @@ struct BwdPlan {
   int32_t *r_ident, *r_counts, *r_offsets, *r_row_src, *r_dest_row;
   void* r_scratch;
   void* x_perm;     // [R_cap, d] token rows gathered again for the wgrad GEMM
+  float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
   mok_trace* tr;    // host-side trace, may be null
 };
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream);
+size_t wgrad_partial_bytes(int R_cap, int d, int I);
 
 }  // namespace mok

@@ -348,6 +348,9 @@ BWD_CASES = {
     "f32": _small("C1", S=1, T_src=90, d=64, E=4, k=2, I=192, own=[0], local_experts=[0, 1, 2, 3]),
     "bf16_share": _small("C3", S=3, T_src=65, d=128, E=16, k=4, I=192, own=[1],
                          local_experts=[1, 4, 7, 10, 13], zipf_s=0.0),
+    # about 6000 rows per expert: the weight gradients run split over 4096-row chunks
+    "bf16_split_k": _small("C2", S=2, T_src=6000, d=128, E=4, k=2, I=128, own=[0],
+                           local_experts=[0, 1, 2, 3]),
 }
 
 

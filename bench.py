@@ -52,6 +52,7 @@ def kernel_work(name, w, R):
         "ffn2_down_mx": 2.0 * R * I * d,
         # persistent ring kernel: pull into ring slots + GEMM1/SwiGLU + GEMM2 + push
         "ring_fused_ffn": 2.0 * R * d * 2 * I + 2.0 * R * I * d,
+        "bwd_dh": 2.0 * R * d * I,
         "bwd_dh_swiglu": 2.0 * R * d * I,
         "bwd_dx_push": 2.0 * R * 2 * I * d,
         "bwd_wgrad_gate_up": 2.0 * R * 2 * I * d,
@@ -66,6 +67,7 @@ def kernel_work(name, w, R):
         "bwd_regather_x": 2.0 * R * d * eb,
         "combine": (T * k * d + T * d) * eb,              # read k pushed rows, write out
         "bwd_reverse_combine_pull": 3.0 * R * d * eb,     # read dout + y rows, write dy
+        "bwd_swiglu": 5.0 * R * I * eb,                   # read dh, a, b; write da, db
         "bwd_dx_sum_router": (T * k * d + T * d) * eb,    # read k dx rows, write dX
     }
     if name in moves:

@@ -1,6 +1,7 @@
 // Backward expert GEMMs, bf16, on the pipelined 256 x 256 tile engine.
 //   dh  : dh = dy W_down[e]           A = dy (k = d contiguous), B = W_down
-//         read as [d][I] (n contiguous) -> epilogue SwiGLU derivative, dab
+//         read as [d][I] (n contiguous) -> bf16 dh, then the SwiGLU
+//         derivative pass turns it into dab
 //   dx  : dx = dab [W_gate; W_up]      A = dab (k = 2I contiguous), B = the
 //         two weight matrices read as [2I][d] -> epilogue pushes dx rows to
 //         their reverse-dispatch staging rows
@@ -54,40 +55,57 @@ __global__ __launch_bounds__(kThreads) void dh_g2(DhArgs a) {
                           lb.issue(kt, l, [&](int kk) -> const bf16_t* { return wd + (size_t)kk * a.I; });
                         },
                         smem, acc);
-  // dh staged as fp32; the row walk reads a | b and writes da | db with
-  // contiguous 8-byte pieces per lane
+  // dh (bf16) goes to the first half of its dab row; swiglu_bwd_kernel then
+  // turns it into da | db in place with the saved a | b, as a separate pass
+  // that runs at full memory bandwidth (as an epilogue, every workgroup would
+  // stall on its a | b loads at the same time while the matrix cores idle).
   __syncthreads();
-  const WaveStage<C, float> st(smem);
+  const WaveStage<C, bf16_t> st(smem);
+  st.put(acc, 0);
+  wave_lds_fence();
   const int wave = threadIdx.x >> 6;
+  st.for_chunks(0, [&](int trow, int srow, int c) {
+    const int r = g.r0 + (wave >> 1) * 128 + trow;
+    const int col = n0 + (wave & 1) * (C::BN / 2) + c * 8;
+    if (r >= g.r1 || col >= a.I) return;
+    *reinterpret_cast<uint4*>(a.dab + (size_t)r * 2 * a.I + col) = st.raw(srow, c);
+  });
+}
+
+// SwiGLU backward of every routed row, in place: dab[r] = da | db from
+// dh = dab[r][0, I) and the saved a | b:  s = sigmoid(a),
+// da = dh * b * s * (1 + a (1 - s)),  db = dh * a * s.  One 8-column piece
+// per thread; rows beyond R are skipped.
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const bf16_t* ab, bf16_t* dab,
+                                                              const int32_t* offsets, int E_local,
+                                                              int R_cap, int I) {
+  const int R = min(offsets[E_local], R_cap);
+  const int per_row = I / 8;
+  const size_t u = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const int r = (int)(u / per_row), c = (int)(u % per_row) * 8;
+  if (r >= R) return;
+  const bf16_t* abr = ab + (size_t)r * 2 * I;
+  bf16_t* dabr = dab + (size_t)r * 2 * I;
+  const uint4 hv = *reinterpret_cast<const uint4*>(dabr + c);
+  const uint4 av = *reinterpret_cast<const uint4*>(abr + c);
+  const uint4 bv = *reinterpret_cast<const uint4*>(abr + I + c);
+  const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, aw[4] = {av.x, av.y, av.z, av.w},
+                 bw[4] = {bv.x, bv.y, bv.z, bv.w};
+  float da[8], db[8];
 #pragma unroll
-  for (int pass = 0; pass < WaveStage<C, float>::PASSES; ++pass) {
-    st.put(acc, pass);
-    wave_lds_fence();
-    st.for_chunks(pass, [&](int trow, int srow, int c) {
-      const int r = g.r0 + (wave >> 1) * 128 + trow;
-      const int i = n0 + (wave & 1) * (C::BN / 2) + c * 4;
-      if (r >= g.r1 || i >= a.I) return;
-      float dh[4];
-      st.get(srow, c, dh);
-      const bf16_t* abr = a.ab + (size_t)r * 2 * a.I;
-      bf16_t* dabr = a.dab + (size_t)r * 2 * a.I;
-      const uint2 av4 = *reinterpret_cast<const uint2*>(abr + i);
-      const uint2 bv4 = *reinterpret_cast<const uint2*>(abr + a.I + i);
-      const uint32_t aw[2] = {av4.x, av4.y}, bw[2] = {bv4.x, bv4.y};
-      float da[4], db[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float av = __uint_as_float(e & 1 ? aw[e >> 1] & 0xFFFF0000u : aw[e >> 1] << 16);
-        const float bv = __uint_as_float(e & 1 ? bw[e >> 1] & 0xFFFF0000u : bw[e >> 1] << 16);
-        const float sg = 1.0f / (1.0f + __expf(-av));
-        da[e] = dh[e] * bv * sg * (1.0f + av * (1.0f - sg));
-        db[e] = dh[e] * av * sg;
-      }
-      *reinterpret_cast<uint2*>(dabr + i) = pack4_bf16(da[0], da[1], da[2], da[3]);
-      *reinterpret_cast<uint2*>(dabr + a.I + i) = pack4_bf16(db[0], db[1], db[2], db[3]);
-    });
-    wave_lds_fence();
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    const float dh = __uint_as_float(e & 1 ? hw[w] & 0xFFFF0000u : hw[w] << 16);
+    const float x = __uint_as_float(e & 1 ? aw[w] & 0xFFFF0000u : aw[w] << 16);
+    const float y = __uint_as_float(e & 1 ? bw[w] & 0xFFFF0000u : bw[w] << 16);
+    const float sg = 1.0f / (1.0f + __expf(-x));
+    da[e] = dh * y * sg * (1.0f + x * (1.0f - sg));
+    db[e] = dh * x * sg;
   }
+  const uint2 d0 = pack4_bf16(da[0], da[1], da[2], da[3]), d1 = pack4_bf16(da[4], da[5], da[6], da[7]);
+  const uint2 e0 = pack4_bf16(db[0], db[1], db[2], db[3]), e1 = pack4_bf16(db[4], db[5], db[6], db[7]);
+  *reinterpret_cast<uint4*>(dabr + c) = make_uint4(d0.x, d0.y, d1.x, d1.y);
+  *reinterpret_cast<uint4*>(dabr + I + c) = make_uint4(e0.x, e0.y, e1.x, e1.y);
 }
 
 struct DxArgs {
@@ -128,6 +146,8 @@ __global__ __launch_bounds__(kThreads) void dx_g2(DxArgs a) {
                           });
                         },
                         smem, acc);
+  __shared__ int s_rows[BM];
+  stage_rows(s_rows, a.row_src, g);
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
   st.put(acc, 0);
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void dx_g2(DxArgs a) {
     const int r = g.r0 + (wave >> 1) * 128 + trow;
     const int col = n0 + (wave & 1) * (C::BN / 2) + c * 8;
     if (r >= g.r1 || col >= a.d) return;
-    const int n = a.row_src[r];
+    const int n = s_rows[r - g.r0];
     const int tok = n / a.k, j = n % a.k;
     bf16_t* dst = reinterpret_cast<bf16_t*>(a.dx_stage.p[tok / a.T_src]) +
                   ((size_t)(tok % a.T_src) * a.k + j) * a.d;
@@ -334,7 +354,11 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
     d.R_cap = p.R_cap;
     d.ntn = (p.I + Default::BN - 1) / Default::BN;
     hipLaunchKernelGGL(dh_g2<Default>, dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
-    trace_mark(p.tr, "bwd_dh_swiglu", stream);
+    trace_mark(p.tr, "bwd_dh", stream);
+    const size_t pieces = (size_t)p.R_cap * (p.I / 8);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((pieces + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, d.ab, d.dab, p.offsets, p.E_local, p.R_cap, p.I);
+    trace_mark(p.tr, "bwd_swiglu", stream);
     DxArgs x;
     x.dab = reinterpret_cast<const bf16_t*>(p.dab);
     x.wg = reinterpret_cast<const bf16_t*>(p.wg);

@@ -136,6 +136,8 @@ __device__ __forceinline__ void ffn1_tile(const F1Args& a, char* smem, const GTi
 template <class C, class AccT>
 __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GTile& g, int nt,
                                            const F2Args& a) {
+  __shared__ int s_rows[BM];
+  if (a.push) stage_rows(s_rows, a.row_src, g);
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
   st.put(acc, 0);
@@ -147,7 +149,7 @@ __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GT
     if (r >= g.r1 || col >= a.d) return;
     bf16_t* dst;
     if (a.push) {
-      const int n = a.row_src[r];
+      const int n = s_rows[r - g.r0];
       const int tok = n / a.k, j = n % a.k;
       dst = reinterpret_cast<bf16_t*>(a.staging.p[tok / a.T_src]) +
             ((size_t)(tok % a.T_src) * a.k + j) * a.d;

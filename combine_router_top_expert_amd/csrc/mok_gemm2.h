@@ -188,7 +188,7 @@ struct Cfg {
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int SMEM = NS * STAGE;
   static constexpr int LOADS = STAGE / 1024 / 4;  // per wave per stage
-  static_assert(NS >= 2 && NS <= 6 && (NS - 2) * LOADS < 64, "vmcnt range");
+  static_assert(NS >= 2 && NS <= 8 && (NS - 2) * LOADS < 64, "vmcnt range");
 };
 
 // The default configuration of the expert GEMMs.
@@ -272,19 +272,15 @@ __device__ __forceinline__ void stage_mma(const char* As, const char* Bs, Acc<C>
 // (after = stages issued after the one about to be consumed, 0 .. MAXA).
 template <int N, int MAXA>
 __device__ __forceinline__ void wait_stages(int after) {
-  if constexpr (MAXA >= 4) {
-    if (after >= 4) { wait_vmcnt<4 * N>(); return; }
+  if constexpr (MAXA > 0) {
+    if (after >= MAXA) {
+      wait_vmcnt<MAXA * N>();
+      return;
+    }
+    wait_stages<N, MAXA - 1>(after);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (MAXA >= 3) {
-    if (after == 3) { wait_vmcnt<3 * N>(); return; }
-  }
-  if constexpr (MAXA >= 2) {
-    if (after == 2) { wait_vmcnt<2 * N>(); return; }
-  }
-  if constexpr (MAXA >= 1) {
-    if (after == 1) { wait_vmcnt<N>(); return; }
-  }
-  wait_vmcnt<0>();
 }
 
 // Main loop over KT stages of C::STAGE bytes in an NS-deep LDS ring.
@@ -308,19 +304,67 @@ __device__ __forceinline__ void pipeline(int KT, Issue issue, Compute compute, c
   }
 }
 
-// bf16 main loop: issueA(kt, lds) / issueB(kt, lds) issue this wave's direct
+// MFMAs of one k16 step for row blocks [I0, I1) of the wave tile.
+template <class C, bool A_MN, bool B_MN, int I0, int I1>
+__device__ __forceinline__ void mma_rows(const Frags<C, A_MN, B_MN>& f, Acc<C>& acc) {
+#pragma unroll
+  for (int i = I0; i < I1; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WNB; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
+}
+
+// bf16 main loop over KT stages of BK k in a two-stage LDS ring, pipelined
+// across stages.  issueA(kt, lds) / issueB(kt, lds) issue this wave's direct
 // loads of one stage (lds = LDS byte address of the operand's tile in the
-// stage).
+// stage).  The hand-over to stage kt+1 (wait for this wave's loads of kt+1
+// and its LDS reads of kt, then the workgroup barrier) comes before the last
+// k16 step of stage kt; the loads of stage kt+2 into the slot just freed and
+// the first fragment reads of stage kt+1 are then issued between the MFMAs of
+// that last step, so their latency is covered by matrix work instead of
+// standing in front of it.  The inline-assembly loads are scheduling
+// boundaries, which keeps that order in the instruction stream.
 template <class C, bool A_MN, bool B_MN, class IA, class IB>
 __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* smem, Acc<C>& acc) {
+  static_assert(C::NS == 2, "the cross-stage pipeline uses two LDS stages");
+  constexpr int S = C::BK / 16;
+  static_assert(S >= 2, "at least two k16 steps per stage");
+  typedef Frags<C, A_MN, B_MN> F;
   acc.zero();
-  pipeline<C>(
-      KT,
-      [&](int kt, unsigned st) {
-        issueA(kt, st);
-        issueB(kt, st + C::A_BYTES);
-      },
-      [&](const char* cur) { stage_mma<C, A_MN, B_MN>(cur, cur + C::A_BYTES, acc); }, smem);
+  if (KT <= 0) return;
+  const unsigned lds0 = lds_addr_of(smem);
+  issueA(0, lds0);
+  issueB(0, lds0 + C::A_BYTES);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  if (KT > 1) {
+    issueA(1, lds0 + C::STAGE);
+    issueB(1, lds0 + C::STAGE + C::A_BYTES);
+  }
+  F f[2];
+  f[0].load(smem, smem + C::A_BYTES, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt & 1) * C::STAGE;
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s) {
+      f[(s + 1) & 1].load(cur, cur + C::A_BYTES, s + 1);
+      mma_rows<C, A_MN, B_MN, 0, 4>(f[s & 1], acc);
+    }
+    // (the hand-over also runs after the last stage, where it is harmless:
+    // every MFMA stays outside branches, so the accumulators keep one
+    // register assignment through the loop)
+    const F& last = f[(S - 1) & 1];
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    const unsigned slot = lds0 + (kt & 1) * C::STAGE;
+    const bool more = kt + 2 < KT;
+    if (more) issueA(kt + 2, slot);
+    mma_rows<C, A_MN, B_MN, 0, 2>(last, acc);
+    if (more) issueB(kt + 2, slot + C::A_BYTES);
+    const char* nxt = smem + ((kt + 1) & 1) * C::STAGE;
+    f[S & 1].load(nxt, nxt + C::A_BYTES, 0);
+    mma_rows<C, A_MN, B_MN, 2, 4>(last, acc);
+  }
 }
 
 // ---------------------------------------------------------------- epilogue staging
@@ -341,6 +385,7 @@ struct WaveStage {
   static constexpr int ROWS = 32768 / PITCH < 128 ? 32768 / PITCH : 128;  // rows per pass
   static constexpr int PASSES = 128 / ROWS;
   static constexpr int SW = CPR < 32 ? CPR : 32;              // swizzle period
+  static_assert(C::SMEM >= 4 * 32768, "the four waves' staging regions reuse the operand ring");
   char* base;
   __device__ __forceinline__ explicit WaveStage(char* smem) : base(smem + (threadIdx.x >> 6) * 32768) {}
   __device__ __forceinline__ char* chunk_addr(int row, int c) const {
@@ -467,6 +512,16 @@ __device__ __forceinline__ GTile group_tile(const int32_t* offsets, int E_local,
   t.r0 = offsets[lo] + (mtile - s_prefix[lo]) * tile_rows;
   t.r1 = min(t.r0 + tile_rows, end);
   return t;
+}
+
+// Item numbers of a tile's rows, copied to LDS ahead of an epilogue that
+// pushes rows to their (source, token, slot) addresses: one global load per
+// row instead of one per 16-byte chunk (the workgroup's 256 threads cover the
+// 256 rows; a barrier must follow before they are read).
+__device__ __forceinline__ void stage_rows(int* s_rows, const int32_t* row_src, const GTile& g) {
+  static_assert(kThreads == BM, "one thread per tile row");
+  const int r = g.r0 + (int)threadIdx.x;
+  s_rows[threadIdx.x] = r < g.r1 ? row_src[r] : 0;
 }
 
 }  // namespace g2

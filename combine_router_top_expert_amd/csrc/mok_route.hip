@@ -7,9 +7,9 @@
 //   top-k   = k largest z, equal z -> lower expert id first, slot 0 largest;
 //   gate_j  = exp(z_j - z_0) / sum_i exp(z_i - z_0) over the chosen slots
 //             (= softmax over all experts renormalised over the chosen ones).
-// Every output (t, e) keeps its own sequential chain, so the logits -- and
-// hence the selection -- are reproducible bit for bit.  No matrix cores here:
-// the chain order is the contract.
+// Every output (t, e) keeps its own sequential chain (one lane, d ascending),
+// so the logits -- and hence the selection -- are reproducible bit for bit.
+// No matrix cores here: the chain order is the contract.
 #include "mok_internal.h"
 
 namespace mok {
@@ -17,7 +17,6 @@ namespace mok {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kTE = 4;      // experts per thread
 constexpr int kMaxK = 16;
 
 struct RouteArgs {
@@ -28,9 +27,10 @@ struct RouteArgs {
   int32_t* topk_idx;  // [T, k] for the launch's tokens, in order
   float* topk_gate;
   int T, d, E, k;
-  int EG, TG, TB;   // threads across experts, threads across tokens, tokens per block
+  int EL;           // expert lanes per wave (each lane: 4 experts)
+  int ESETS;        // sets of 4 * EL experts
+  int TB;           // tokens per block
   int dc;           // d-chunk staged through LDS
-  int xs_pitch, ws_pitch, zs_pitch;
 };
 
 template <typename T>
@@ -63,96 +63,140 @@ __device__ __forceinline__ void unpack<float>(uint4 u, float* out) {
   out[3] = __uint_as_float(u.w);
 }
 
-template <typename T, int TT>
+// A block routes TB tokens against all E experts.  A lane keeps 16 logit
+// chains: 4 consecutive experts x 4 consecutive tokens; per d step it reads
+// the 4 weights and the 4 token values as one 16-byte LDS read each (lanes of
+// the same tokens share the address) and issues 16 fmaf.  A wave unit is EL
+// expert lanes x (64 / EL) token lanes; the block's units (expert set, token
+// group) are its four waves.  Chunks of dc along d are staged
+// through two LDS buffers as fp32 -- [dc][TB] tokens, [dc][Epad + 4]
+// weights -- with the global loads of chunk c + 1 in flight (in registers)
+// while chunk c is computed.
+template <typename T, int DC, int PT>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
-  float* xs = smem;                              // [dc][xs_pitch]  (token fastest)
-  float* ws = xs + a.dc * a.xs_pitch;            // [dc][ws_pitch]  (expert fastest)
-  float* zs = smem;                              // [TB][zs_pitch] logits, after the d loop
+  constexpr int dc = DC;
+  const int TB = a.TB, EL = a.EL;
+  const int Epad = a.ESETS * 4 * EL;
+  const int wpitch = Epad + 4;
+  const int buf = dc * TB + dc * wpitch;         // floats per staging buffer
   constexpr int U = Unit<T>::n;
-  const int UPR = a.dc / U;                      // units per row chunk
-
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * a.TB;
-  const int eg = tid % a.EG;
-  const int tg = tid / a.EG;
-  const bool computes = tg < a.TG;
+  constexpr int UPR = dc / U;                    // 16-byte units per row chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int el = lane % EL, tl = lane / EL;
+  const int TPU = (64 / EL) * 4;                 // tokens per unit
+  const int units = a.ESETS * (TB / TPU);
+  const int t0 = blockIdx.x * TB;
   const T* w = reinterpret_cast<const T*>(a.w);
-  const int Epad = a.EG * kTE;
+  const int nx = TB * UPR, nw = Epad * UPR;      // staging units per chunk
 
-  float acc[TT][kTE];
+  // This thread's staging units (up to PT per operand): global source of
+  // chunk 0 (null = zeros) and LDS offset of the unit's first value.
+  const T* gx[PT];
+  const T* gw[PT];
+  int lx[PT], lw[PT];
 #pragma unroll
-  for (int i = 0; i < TT; ++i)
-#pragma unroll
-    for (int j = 0; j < kTE; ++j) acc[i][j] = 0.0f;
-
-  for (int c0 = 0; c0 < a.d; c0 += a.dc) {
-    // stage x[t0 .. t0+TB) x [c0, c0+dc) transposed
-    for (int u = tid; u < a.TB * UPR; u += kRouteThreads) {
-      int t = u / UPR, q = u % UPR;
-      float v[U];
+  for (int j = 0; j < PT; ++j) {
+    const int u = tid + j * kRouteThreads;
+    const int t = u / UPR, q = u % UPR;
+    gx[j] = nullptr;
+    lx[j] = -1;
+    if (u < nx) {
+      lx[j] = (q * U) * TB + t;
       if (t0 + t < a.T) {
         const int g = t0 + t;
-        const T* x = reinterpret_cast<const T*>(a.src.p[a.src_lo + g / a.T_src]) +
-                     (size_t)(g % a.T_src) * a.d;
-        unpack<T>(ld16(x + c0 + q * U), v);
-      } else {
-#pragma unroll
-        for (int i = 0; i < U; ++i) v[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < U; ++i) xs[(q * U + i) * a.xs_pitch + t] = v[i];
-    }
-    // stage w[0 .. Epad) x [c0, c0+dc) transposed
-    for (int u = tid; u < Epad * UPR; u += kRouteThreads) {
-      int e = u / UPR, q = u % UPR;
-      float v[U];
-      if (e < a.E) {
-        unpack<T>(ld16(w + (size_t)e * a.d + c0 + q * U), v);
-      } else {
-#pragma unroll
-        for (int i = 0; i < U; ++i) v[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < U; ++i) ws[(q * U + i) * a.ws_pitch + e] = v[i];
-    }
-    __syncthreads();
-    if (computes) {
-#pragma unroll 4
-      for (int i = 0; i < a.dc; ++i) {
-        float xv[TT], wv[kTE];
-#pragma unroll
-        for (int q = 0; q < TT; ++q) xv[q] = xs[i * a.xs_pitch + tg * TT + q];
-#pragma unroll
-        for (int q = 0; q < kTE; ++q) wv[q] = ws[i * a.ws_pitch + eg * kTE + q];
-#pragma unroll
-        for (int p = 0; p < TT; ++p)
-#pragma unroll
-          for (int q = 0; q < kTE; ++q) acc[p][q] = __builtin_fmaf(xv[p], wv[q], acc[p][q]);
+        gx[j] = reinterpret_cast<const T*>(a.src.p[a.src_lo + g / a.T_src]) +
+                (size_t)(g % a.T_src) * a.d + q * U;
       }
     }
-    __syncthreads();
+    gw[j] = nullptr;
+    lw[j] = -1;
+    if (u < nw) {
+      lw[j] = (q * U) * wpitch + t;  // t = expert here
+      if (t < a.E) gw[j] = w + (size_t)t * a.d + q * U;
+    }
   }
-
-  if (computes) {
+  uint4 rx[PT], rw[PT];
+  auto fetch = [&](int c0) {
 #pragma unroll
-    for (int p = 0; p < TT; ++p)
+    for (int j = 0; j < PT; ++j) {
+      rx[j] = gx[j] ? ld16(gx[j] + c0) : make_uint4(0, 0, 0, 0);
+      rw[j] = gw[j] ? ld16(gw[j] + c0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto deposit = [&](float* xs, float* ws) {
 #pragma unroll
-      for (int q = 0; q < kTE; ++q) {
-        int e = eg * kTE + q;
-        if (e < a.E) {
-          float z = acc[p][q];
-          if (a.bias) z = z + a.bias[e];
-          zs[(tg * TT + p) * a.zs_pitch + e] = z;
-        }
+    for (int j = 0; j < PT; ++j) {
+      float v[U];
+      if (lx[j] >= 0) {
+        unpack<T>(rx[j], v);
+#pragma unroll
+        for (int i = 0; i < U; ++i) xs[lx[j] + i * TB] = v[i];
       }
+      if (lw[j] >= 0) {
+        unpack<T>(rw[j], v);
+#pragma unroll
+        for (int i = 0; i < U; ++i) ws[lw[j] + i * wpitch] = v[i];
+      }
+    }
+  };
+
+  float acc[4][4];  // [token][expert]
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[p][q] = 0.0f;
+  const bool active = wave < units;
+  const int es = wave % a.ESETS, tg = wave / a.ESETS;
+
+  fetch(0);
+  for (int c0 = 0, b = 0; c0 < a.d; c0 += dc, b ^= 1) {
+    float* xs = smem + b * buf;
+    float* ws = xs + dc * TB;
+    // buffer b was last read by the chunk before the previous one, which
+    // every wave finished before the previous barrier
+    deposit(xs, ws);
+    __syncthreads();
+    if (c0 + dc < a.d) fetch(c0 + dc);
+    if (active) {
+      const float* wr = ws + es * 4 * EL + 4 * el;
+      const float* xr = xs + tg * TPU + 4 * tl;
+#pragma unroll
+      for (int i = 0; i < dc; ++i) {
+        const float4 wv = *reinterpret_cast<const float4*>(wr + i * wpitch);
+        const float4 xv = *reinterpret_cast<const float4*>(xr + i * TB);
+        const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fmaf(xa[p], wa[q], acc[p][q]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // logits [TB][Epad + 1] (aliasing the staging area), then top-k per token
+  const int zp = Epad + 1;
+  float* zs = smem;
+  if (active) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = es * 4 * EL + 4 * el + q;
+      const float b = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float z = acc[p][q];
+        if (a.bias) z = z + b;
+        zs[(tg * TPU + 4 * tl + p) * zp + e] = z;
+      }
+    }
   }
   __syncthreads();
 
   // selection: one wave per token
-  const int lane = tid & 63, wave = tid >> 6;
   const int MPL = (a.E + 63) / 64;   // entries per lane (<= 8)
-  for (int tl = wave; tl < a.TB; tl += kRouteThreads / 64) {
+  for (int tl = wave; tl < TB; tl += kRouteThreads / 64) {
     const int t = t0 + tl;
     if (t >= a.T) break;
     float zv[8];
@@ -160,7 +204,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       int e = lane + 64 * m;
-      zv[m] = (m < MPL && e < a.E) ? zs[tl * a.zs_pitch + e] : -__builtin_inff();
+      zv[m] = (m < MPL && e < a.E) ? zs[tl * zp + e] : -__builtin_inff();
     }
     float zsel[kMaxK];
     int esel[kMaxK];
@@ -206,24 +250,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
 }  // namespace
 
-// Block geometry for E experts: EG threads across experts (kTE each), TG across
-// tokens (TT each), TB tokens per block, dc-wide d chunks.  Returns TT.
-int route_geometry(int E, int T, int* EG, int* TG, int* TB, int* dc) {
-  *EG = (E + kTE - 1) / kTE;
-  int tg = kRouteThreads / *EG;
-  *dc = E > 256 ? 16 : 32;
-  // 4 tokens per thread, fewer when that leaves fewer than two workgroups per CU
-  int TT = 4;
-  while (TT > 1) {
-    int cap = 128 / TT;
-    int g = tg < cap ? tg : cap;
-    if ((T + g * TT - 1) / (g * TT) >= 512) break;
-    TT >>= 1;
-  }
-  int cap = 128 / TT;
-  *TG = tg < cap ? tg : cap;
-  *TB = *TG * TT;
-  return TT;
+// Block geometry: EL expert lanes per wave (4 experts each; a power of two up
+// to 64), ESETS sets of 4 EL experts, TB tokens per block (four wave units
+// when the expert sets allow), dc-wide d chunks (smaller when a block holds
+// many tokens or experts).  Returns the units per wave.
+int route_geometry(int E, int* EL, int* ESETS, int* TB, int* dc) {
+  int el = 1;
+  while (el < 64 && 4 * el < E) el <<= 1;
+  *EL = el;
+  *ESETS = (E + 4 * el - 1) / (4 * el);
+  const int tpu = (64 / el) * 4;
+  *TB = *ESETS >= 4 ? tpu : tpu * (4 / *ESETS);
+  int c = 32;
+  while (c > 8 && (size_t)c * (*TB + *ESETS * 4 * el + 4) > 12288) c >>= 1;
+  *dc = c;
+  const int units = *ESETS * (*TB / tpu);
+  return (units + 3) / 4;
+}
+
+size_t route_smem_bytes(int E) {
+  int EL, ES, TB, dc;
+  route_geometry(E, &EL, &ES, &TB, &dc);
+  const size_t Epad = (size_t)ES * 4 * EL;
+  const size_t stage = 2 * ((size_t)dc * TB + (size_t)dc * (Epad + 4));
+  const size_t logits = (size_t)TB * (Epad + 1);
+  return sizeof(float) * (stage > logits ? stage : logits);
 }
 
 mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, int T, int d,
@@ -242,35 +293,40 @@ mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, in
   a.d = d;
   a.E = E;
   a.k = k;
-  const int TT = route_geometry(E, T, &a.EG, &a.TG, &a.TB, &a.dc);
-  a.xs_pitch = a.TB + 4;
-  a.ws_pitch = a.EG * kTE + 4;
-  a.zs_pitch = a.EG * kTE + 1;
-  size_t smem = route_smem_bytes(E, T);
+  const int upw = route_geometry(E, &a.EL, &a.ESETS, &a.TB, &a.dc);
+  if (d % a.dc != 0 || upw != 1) return MOK_ESHAPE;
+  // staging units per thread (both operands) must fit the kernel's slots
+  const int U = prec == MOK_F32 ? 4 : 8;
+  const int per = (a.ESETS * 4 * a.EL * (a.dc / U) + kRouteThreads - 1) / kRouteThreads;
+  const int perx = (a.TB * (a.dc / U) + kRouteThreads - 1) / kRouteThreads;
+  const int need = per > perx ? per : perx;
+  const int pt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  if (need > 8) return MOK_ESHAPE;
+  const size_t smem = route_smem_bytes(E);
   dim3 grid((T + a.TB - 1) / a.TB);
   dim3 blk(kRouteThreads);
-#define MOK_ROUTE_LAUNCH(TY, TTV) \
-  hipLaunchKernelGGL((route_kernel<TY, TTV>), grid, blk, smem, stream, a)
-  if (prec == MOK_F32) {
-    if (TT == 4) MOK_ROUTE_LAUNCH(float, 4);
-    else if (TT == 2) MOK_ROUTE_LAUNCH(float, 2);
-    else MOK_ROUTE_LAUNCH(float, 1);
-  } else {
-    if (TT == 4) MOK_ROUTE_LAUNCH(bf16_t, 4);
-    else if (TT == 2) MOK_ROUTE_LAUNCH(bf16_t, 2);
-    else MOK_ROUTE_LAUNCH(bf16_t, 1);
-  }
+#define MOK_ROUTE_LAUNCH(TY, DCV, PTV) \
+  hipLaunchKernelGGL((route_kernel<TY, DCV, PTV>), grid, blk, smem, stream, a)
+#define MOK_ROUTE_PT(TY, DCV)                          \
+  do {                                                 \
+    if (pt == 1) MOK_ROUTE_LAUNCH(TY, DCV, 1);         \
+    else if (pt == 2) MOK_ROUTE_LAUNCH(TY, DCV, 2);    \
+    else if (pt == 4) MOK_ROUTE_LAUNCH(TY, DCV, 4);    \
+    else MOK_ROUTE_LAUNCH(TY, DCV, 8);                 \
+  } while (0)
+#define MOK_ROUTE_DC(TY)                               \
+  do {                                                 \
+    if (a.dc == 32) MOK_ROUTE_PT(TY, 32);              \
+    else if (a.dc == 16) MOK_ROUTE_PT(TY, 16);         \
+    else MOK_ROUTE_PT(TY, 8);                          \
+  } while (0)
+  if (prec == MOK_F32) MOK_ROUTE_DC(float);
+  else MOK_ROUTE_DC(bf16_t);
+#undef MOK_ROUTE_DC
+#undef MOK_ROUTE_PT
 #undef MOK_ROUTE_LAUNCH
   trace_mark(tr, "route", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
-}
-
-size_t route_smem_bytes(int E, int T) {
-  int EG, TG, TB, dc;
-  route_geometry(E, T, &EG, &TG, &TB, &dc);
-  size_t stage = (size_t)dc * (TB + 4) + (size_t)dc * (EG * kTE + 4);
-  size_t logits = (size_t)TB * (EG * kTE + 1);
-  return sizeof(float) * (stage > logits ? stage : logits);
 }
 
 }  // namespace mok

@@ -164,6 +164,8 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
                 "algorithmic_bytes_per_launch": work}
+    from combine_router_top_expert_amd.profiling import recorded_traffic
+    roof["traffic"] = recorded_traffic(dom, w.name, "ring" if args.ring_mib else "staged")
     # per-kernel roofline fractions, for the record
     for n, v in kernels.items():
         kd, wk = kernel_work(n, w, R)
@@ -221,6 +223,9 @@ def main():
     ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
     ap.add_argument("--mb-sweep", default="",
                     help="ring path: comma-separated minibatch sizes, one JSON line each")
+    ap.add_argument("--hbm-copy-gib", type=float, default=0.0,
+                    help="instead of the layer: time a plain device copy of this many GiB "
+                         "(the reference for HBM bandwidth and for scaling byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "
@@ -236,6 +241,22 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     dev = "cuda:0"
+    if args.hbm_copy_gib > 0:
+        n = int(args.hbm_copy_gib * (1 << 30)) // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"metric": "device copy bytes moved per second (read + write)",
+                          "value": 2.0 * n / dt / 1e9, "unit": "GB/s", "bytes_per_copy": n,
+                          "ms_per_copy": dt * 1e3, "steps": args.steps}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     has_bwd = w.prec != "mxfp8"
     t0 = time.time()

@@ -1,0 +1,157 @@
+"""Summaries of rocprofv3 output for the layer's kernels.
+
+``python -m combine_router_top_expert_amd.profiling OUT_DIR`` reads, from
+OUT_DIR (a gpurun output folder):
+  kt/kt_kernel_stats.csv                  rocprofv3 --kernel-trace --stats of bench.py
+  pf/pf_counter_collection.csv            rocprofv3 --pmc FETCH_SIZE of bench.py
+  pw/pw_counter_collection.csv            rocprofv3 --pmc WRITE_SIZE of bench.py
+  cf/cf_counter_collection.csv            rocprofv3 --pmc FETCH_SIZE of bench.py --hbm-copy-gib 1
+  cw/cw_counter_collection.csv            rocprofv3 --pmc WRITE_SIZE of bench.py --hbm-copy-gib 1
+and writes ``profiles/c2_fwd_bwd_kernel_trace.md``, ``profiles/c2_hbm_traffic.md``
+and ``profiles/hbm_traffic.json``.
+
+The byte counters are scaled by what they read for the plain 1 GiB device copy
+(``FETCH_SIZE`` and ``WRITE_SIZE`` are in KiB; the factor maps the copy's
+reading onto its known 1 GiB).  ``hbm_traffic.json`` records the traffic of one
+launch of each kernel (its last profiled launch) under the name ``bench.py``
+reports, together with a hash of the kernel sources: ``bench.py`` reports the
+traffic only while the sources still hash to that value.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# HIP kernel (as named in the profiler) -> the name bench.py's trace uses
+TRACE_NAME = {
+    "route_kernel": "route", "layout_count": "layout_count", "layout_scan": "layout_scan",
+    "layout_place": "layout_place", "gather_kernel": "gather", "gather_mx_kernel": "gather",
+    "ffn1_g2": "ffn1_gate_up_swiglu", "ffn2_g2": "ffn2_down", "ffn1_mx": "ffn1_gate_up_swiglu_mx",
+    "ffn2_mx": "ffn2_down_mx", "combine_kernel": "combine", "rc_pull_kernel": "bwd_reverse_combine_pull",
+    "dh_g2": "bwd_dh", "swiglu_bwd_kernel": "bwd_swiglu", "dx_g2": "bwd_dx_push",
+    "wgrad_g2<0>": "bwd_wgrad_gate_up", "wgrad_g2<1>": "bwd_wgrad_down",
+    "wgrad_reduce<0>": "bwd_wgrad_gate_up_reduce", "wgrad_reduce<1>": "bwd_wgrad_down_reduce",
+    "dx_final_kernel": "bwd_dx_sum_router", "dwr_part_kernel": "bwd_dw_router_part",
+    "dwr_reduce_kernel": "bwd_dw_router_reduce", "ring_kernel": "ring_fused_ffn",
+}
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources (csrc/*.hip, csrc/*.h, include/*.h)."""
+    h = hashlib.sha256()
+    files = []
+    for d, exts in ((CSRC, (".hip", ".h")), (os.path.join(ROOT, "include"), (".h",))):
+        files += sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(exts))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_key(name: str) -> str:
+    m = re.search(r"mok::\(anonymous namespace\)::(\w+)", name)
+    if not m:
+        m = re.search(r"^(?:void\s+)?([\w:]+)", name)
+        return m.group(1) if m else name
+    key = m.group(1)
+    if key in ("wgrad_g2", "wgrad_reduce"):
+        t = re.search(r"(\d)>\(", name)
+        key += "<%s>" % (t.group(1) if t else "?")
+    return key
+
+
+def counters(path: str):
+    """kernel key -> list of counter values (one per dispatch, in order)."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.setdefault(kernel_key(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def copy_factor(path: str, expect_kib: float) -> float:
+    vals = counters(path).get("__amd_rocclr_copyBuffer")
+    if not vals:
+        raise SystemExit(f"{path}: no copy kernel dispatches")
+    return expect_kib / (sum(vals) / len(vals))
+
+
+def main(out_dir: str, workload: str = "C2", path: str = "staged"):
+    fs = copy_factor(os.path.join(out_dir, "cf", "cf_counter_collection.csv"), 1 << 20)
+    ws = copy_factor(os.path.join(out_dir, "cw", "cw_counter_collection.csv"), 1 << 20)
+    fetch = counters(os.path.join(out_dir, "pf", "pf_counter_collection.csv"))
+    write = counters(os.path.join(out_dir, "pw", "pw_counter_collection.csv"))
+    traffic = {}
+    lines = ["# HBM traffic per launch, mid-size layer (forward + backward)", "",
+             "Byte counters from two rocprofv3 passes over one timed step of `bench.py`",
+             "(`FETCH_SIZE`, then `WRITE_SIZE`, in KiB per dispatch), each scaled by what the",
+             f"same counter reads for a plain 1 GiB device copy: FETCH_SIZE x {fs:.3f},",
+             f"WRITE_SIZE x {ws:.3f}.  Values are for the last profiled launch of each kernel.", "",
+             "Commands (from the repository root, output under OUT = gpurun_out):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pf -o pf -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pw -o pw -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/cf -o cf -- python3 bench.py --hbm-copy-gib 1 --steps 3 --warmup 1",
+             "    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/cw -o cw -- python3 bench.py --hbm-copy-gib 1 --steps 3 --warmup 1",
+             "    python3 -m combine_router_top_expert_amd.profiling OUT", "",
+             "| kernel | trace name | read MB | written MB | total MB |", "|---|---|---|---|---|"]
+    for k, fv in fetch.items():
+        name = TRACE_NAME.get(k)
+        if name is None:
+            continue
+        rb = fv[-1] * 1024 * fs
+        wb = write.get(k, [0.0])[-1] * 1024 * ws
+        traffic[name] = {"read_bytes": rb, "write_bytes": wb, "bytes": rb + wb}
+        lines.append(f"| {k} | {name} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "c2_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
+        json.dump({"source_sha256": source_hash(), "workload": workload, "path": path,
+                   "fetch_factor": fs, "write_factor": ws, "kernels": traffic}, f, indent=1)
+    stats = os.path.join(out_dir, "kt", "kt_kernel_stats.csv")
+    if os.path.exists(stats):
+        rows = list(csv.DictReader(open(stats)))
+        t = ["# Kernel trace summary, mid-size layer (forward + backward)", "",
+             "Command (from the repository root):", "",
+             "    rocprofv3 --kernel-trace --stats -f csv -d OUT/kt -o kt -- python3 bench.py --steps 3 --warmup 2 --no-cpu-baseline",
+             "", "Five steps (2 warm-up + 3 timed) of the mid-size layer: T=16384 tokens (8 x 2048),",
+             "d=2048, E=64 all local, top-6, SwiGLU I=1408, bf16.", "",
+             "| kernel | trace name | calls | average us | share % |", "|---|---|---|---|---|"]
+        for r in rows:
+            k = kernel_key(r["Name"])
+            t.append(f"| {k} | {TRACE_NAME.get(k, '')} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        with open(os.path.join(PROFILES, "c2_fwd_bwd_kernel_trace.md"), "w") as f:
+            f.write("\n".join(t) + "\n")
+    print("written under", PROFILES)
+
+
+def recorded_traffic(kernel: str, workload: str, path: str):
+    """HBM bytes of one launch of ``kernel`` as profiled, or None when the
+    record is missing, was taken on another workload or path, or the kernel
+    sources have changed since."""
+    f = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        rec = json.load(fh)
+    if rec.get("workload") != workload or rec.get("path") != path:
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    k = rec["kernels"].get(kernel)
+    return None if k is None else k["bytes"]
+
+
+if __name__ == "__main__":
+    main(*sys.argv[1:])

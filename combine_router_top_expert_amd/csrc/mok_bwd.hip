@@ -18,7 +18,9 @@
 //      with X_e the expert's token rows gathered again through row_src;
 //   5. per own token: dz_j = g_j (dg_j - sum_i g_i dg_i) over the chosen
 //      experts (router through the renormalised softmax; selection is
-//      piecewise constant), d_x = sum_j dx_stage_j + sum_j dz_j w_router[e_j];
+//      piecewise constant), d_x = sum_j dx_stage_j + sum_j dz_j w_router[e_j],
+//      over every slot but local rows dropped beyond R_cap (a remote slot's
+//      dg and dx_stage row are written by the GPU holding that expert);
 //   6. dW_router[e] = sum_t dz_{t,e} x_t: partial sums over fixed token
 //      chunks, then a fixed-order sum of the chunks.
 #include "mok_gemm.h"
@@ -239,11 +241,13 @@ __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
     float dg[16];
     float m = 0.0f;
     for (int j = 0; j < p.k; ++j) {
+      // present: a local row, or a remote slot whose gate gradient and dx row
+      // the GPU holding that expert wrote here; absent: dropped beyond R_cap
       const int row = p.dest_row[n0 + j];
-      const bool loc = row >= 0 && row < p.R_cap;
-      dg[j] = loc ? p.d_gate[n0 + j] : 0.0f;
+      const bool present = row < p.R_cap;
+      dg[j] = present ? p.d_gate[n0 + j] : 0.0f;
       m = __builtin_fmaf(p.topk_gate[n0 + j], dg[j], m);
-      s_loc[j] = loc;
+      s_loc[j] = present;
       s_e[j] = p.topk_idx[n0 + j];
     }
     for (int j = 0; j < p.k; ++j) {

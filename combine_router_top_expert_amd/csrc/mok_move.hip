@@ -149,8 +149,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int i = 0; i < U; ++i) acc[i] = 0.0f;
       for (int j = 0; j < a.k; ++j) {
+        // every slot but a local row dropped beyond R_cap: a remote slot
+        // (row -1) holds what the GPU with that expert pushed here
         const int row = a.dest_row[n0 + j];
-        if (row < 0 || row >= a.R_cap) continue;
+        if (row >= a.R_cap) continue;
         const float gj = a.gate[n0 + j];
         uint4 v = ld16(stg + (size_t)j * a.d + u * U);
         const T* e = reinterpret_cast<const T*>(&v);

@@ -94,6 +94,19 @@ class MoELayer:
         else:
             self.weights = make_weights(w_gate, w_up, w_down)
 
+    def set_peer_slots(self, s: int, y: torch.Tensor, d_gate: torch.Tensor,
+                       dx: Optional[torch.Tensor] = None):
+        """What the GPUs holding remote experts write back to own source s:
+        y [T_src*k, d] into its staging rows, d_gate [T_src*k] and dx
+        [T_src*k, d] into its reverse-dispatch rows.  The layer overwrites the
+        rows of local slots on every pass, so only remote slots keep them."""
+        per = self.T_src * self.k
+        self.staging[s].copy_(y)
+        if self.with_bwd and self.prec != "mxfp8":
+            self.d_gate[s * per:(s + 1) * per].copy_(d_gate)
+            if dx is not None:
+                self.dx_stage[s].copy_(dx)
+
     def _quantize_weights(self):
         """MX-quantise the expert weights once (off the timed path)."""
         q = []

@@ -184,9 +184,12 @@ mok_status mok_expert_ffn(const mok_config* cfg, const void* x_perm, const uint8
 /* Push combine + final weighted combine [K02 push combine; K03 final weighted
  * combine].  Push: staging[s][t*k+j] = y[dest_row[n]] for every routed item
  * (staging: host array of S device pointers, each [T_src*k, d] activation
- * dtype; rows of remote items are not written).  Final combine for the own
- * sources s in [own_lo, own_lo+own_n):  out[s][t] = sum over j ascending with
- * dest_row[n] >= 0 of topk_gate[n] * staging[s][t*k+j], fp32, rounded once.
+ * dtype; rows of remote items are not written: the GPU holding that expert
+ * pushes them).  Final combine for the own sources s in [own_lo,
+ * own_lo+own_n):  out[s][t] = sum over j ascending of topk_gate[n] *
+ * staging[s][t*k+j], fp32, rounded once, over every slot except local rows
+ * dropped beyond R_cap (dest_row[n] >= R_cap); a remote slot (dest_row[n] ==
+ * -1) is read as its pusher left it, so the caller fills or zeroes it.
  * out: host array of S device pointers ([T_src, d]); only own entries used.
  * y may be NULL to skip the push (staging already filled). */
 mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest_row,
@@ -214,13 +217,16 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
  * push reverse-dispatch].  Inputs: d_out (host array of S device pointers
  * [T_src, d], the upstream gradient; sources whose rows are routed here are
  * read), src_x, w_router, expert_to_local, the weights, the forward state and
- * `staging` as the forward pass left them.  Outputs:
+ * `staging` as the forward pass left them; for own items whose expert is
+ * remote, their d_gate entry and dx_stage row as the GPU holding that expert
+ * wrote them (read, never written here).  Outputs:
  *   d_gate [S*T_src*k] fp32: dL/dg for every local item (others untouched);
  *   dx_stage (host array of S device pointers [T_src*k, d], activation
  *     dtype): the pushed input gradient of every local row;
  *   d_x (host array of S pointers [T_src, d]): for own sources, the sum over
- *     local slots of dx_stage plus the router path sum_j dz_j w_router[e_j],
- *     dz_j = g_j (dg_j - sum_i g_i dg_i);
+ *     the slots of dx_stage plus the router path sum_j dz_j w_router[e_j],
+ *     dz_j = g_j (dg_j - sum_i g_i dg_i), over every slot except local rows
+ *     dropped beyond R_cap;
  *   dw_gate, dw_up [E_local, I, d], dw_down [E_local, d, I] fp32 (overwritten);
  *   dw_router [E, d] fp32 over the own tokens (overwritten), or NULL.
  * Only MOK_F32 and MOK_BF16 are supported (MOK_EINVAL otherwise). */

@@ -71,11 +71,12 @@ def _declare(L):
     L.mokref_layout.argtypes = [_i, _i, _i, _i, _p, _p, _i, _i, _p, _p, _p, _p]
     L.mokref_layout.restype = _i
     L.mokref_ffn_row.argtypes = [_i, _i, _int, _p, _p, _p, _p, _p, _p, _p, _p]
-    L.mokref_fwd_tokens.argtypes = [_i, _i, _i, _i, _i, _int, _p, _p, _p, _p, _p, _p, _p, _p, _p]
+    L.mokref_fwd_tokens.argtypes = [_i, _i, _i, _i, _i, _int, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                    _p]
     L.mokref_bwd_row.argtypes = [_i, _i, _p, _d, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
     L.mokref_router_bwd_token.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
     L.mokref_bwd_tokens.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
-                                    _p]
+                                    _p, _p, _p]
     L.mokref_expert_wgrad.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
     L.mokref_router_wgrad.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p]
 
@@ -203,8 +204,10 @@ def ffn_row(x, wg, wu, wd, prec):
     return a, b, h, y
 
 
-def fwd_tokens(tok_x, topk_idx, gate, e2l, wg, wu, wd, prec):
-    """Forward of a list of tokens -> (y [n, k, d], out [n, d]) float64."""
+def fwd_tokens(tok_x, topk_idx, gate, e2l, wg, wu, wd, prec, peer_y=None):
+    """Forward of a list of tokens -> (y [n, k, d], out [n, d]) float64.
+    peer_y [n, k, d]: rows pushed by the GPUs holding the remote experts
+    (read at remote slots only; None = zeros)."""
     tok_x = _c(tok_x, np.float32)
     topk_idx = _c(topk_idx, np.int32)
     gate = _c(gate, np.float64)
@@ -217,9 +220,11 @@ def fwd_tokens(tok_x, topk_idx, gate, e2l, wg, wu, wd, prec):
     I = wg.shape[1]
     y = np.empty((n, k, d))
     out = np.empty((n, d))
+    if peer_y is not None:
+        peer_y = _c(np.asarray(peer_y).reshape(n, k, d), np.float64)
     lib().mokref_fwd_tokens(n, d, e2l.shape[0], k, I, PREC.get(prec, prec), _ptr(tok_x),
                             _ptr(topk_idx), _ptr(gate), _ptr(e2l), _ptr(wg), _ptr(wu), _ptr(wd),
-                            _ptr(y), _ptr(out))
+                            _ptr(peer_y), _ptr(y), _ptr(out))
     return y, out
 
 
@@ -257,8 +262,11 @@ def router_bwd_token(idx, g, dg, wr):
     return dz, dxr
 
 
-def bwd_tokens(tok_x, tok_dout, topk_idx, gate, e2l, wr, wg, wu, wd):
-    """Backward of tokens routed here -> (d_gate [n,k], dz [n,k], dx [n,d])."""
+def bwd_tokens(tok_x, tok_dout, topk_idx, gate, e2l, wr, wg, wu, wd, peer_dg=None, peer_dx=None):
+    """Backward of a list of tokens -> (d_gate [n,k], dz [n,k], dx [n,d]).
+    peer_dg [n, k], peer_dx [n, k, d]: gate gradients and input-gradient rows
+    written back by the GPUs holding the remote experts (read at remote slots
+    only; None = zeros)."""
     tok_x = _c(tok_x, np.float32)
     tok_dout = _c(tok_dout, np.float32)
     topk_idx = _c(topk_idx, np.int32)
@@ -274,9 +282,13 @@ def bwd_tokens(tok_x, tok_dout, topk_idx, gate, e2l, wr, wg, wu, wd):
     d_gate = np.empty((n, k))
     dz = np.empty((n, k))
     dx = np.empty((n, d))
+    if peer_dg is not None:
+        peer_dg = _c(np.asarray(peer_dg).reshape(n, k), np.float64)
+    if peer_dx is not None:
+        peer_dx = _c(np.asarray(peer_dx).reshape(n, k, d), np.float64)
     lib().mokref_bwd_tokens(n, d, e2l.shape[0], k, I, _ptr(tok_x), _ptr(tok_dout), _ptr(topk_idx),
                             _ptr(gate), _ptr(e2l), _ptr(wr), _ptr(wg), _ptr(wu), _ptr(wd),
-                            _ptr(d_gate), _ptr(dz), _ptr(dx))
+                            _ptr(peer_dg), _ptr(peer_dx), _ptr(d_gate), _ptr(dz), _ptr(dx))
     return d_gate, dz, dx
 
 

@@ -330,16 +330,20 @@ void mokref_ffn_row(int64_t d, int64_t I, int prec, const float* x, const float*
  * tok_x: [n_tok, d] the tokens' rows; topk/gate: [n_tok, k] their routing;
  * e2l: [E] expert -> local index (-1 remote); weights of the local experts
  * (wg, wu: [E_local, I, d], wd: [E_local, d, I]).
+ * peer_y: [n_tok, k, d] or NULL (= zeros): for a slot whose expert is remote,
+ *    the row that the GPU holding that expert pushed into the token's source
+ *    (kucoin article, section 02, push combine: every expert's output lands in
+ *    the source's buffer, so the source's combine reads all k slots).
  * y: [n_tok, k, d] the expert output of each (token, slot) -- what the push
- *    combine delivers to the token's source, in the stored dtype; 0 when the
- *    slot's expert is remote (that row is not computed here);
- * out: [n_tok, d] the final weighted combine out = sum_j g_j y_j over the
- *    slots computed here (kucoin article, section 03 lists it as its own
- *    step), float64 sum rounded once to the output dtype. */
+ *    combine delivers to the token's source, in the stored dtype; the peer's
+ *    row when the slot's expert is remote;
+ * out: [n_tok, d] the final weighted combine out = sum_j g_j y_j over all k
+ *    slots (kucoin article, section 03 lists it as its own step), float64 sum
+ *    rounded once to the output dtype. */
 void mokref_fwd_tokens(int64_t n_tok, int64_t d, int64_t E, int64_t k, int64_t I, int prec,
                        const float* tok_x, const int32_t* topk, const double* gate,
                        const int32_t* e2l, const float* wg, const float* wu, const float* wd,
-                       double* y, double* out) {
+                       const double* peer_y, double* y, double* out) {
   for (int64_t t = 0; t < n_tok; ++t) {
     double* o = out + t * d;
     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
@@ -348,11 +352,11 @@ void mokref_fwd_tokens(int64_t n_tok, int64_t d, int64_t E, int64_t k, int64_t I
       int32_t e = topk[t * k + j];
       int32_t le = (e >= 0 && e < E) ? e2l[e] : -1;
       if (le < 0) {
-        for (int64_t c = 0; c < d; ++c) yj[c] = 0.0;
-        continue;
+        for (int64_t c = 0; c < d; ++c) yj[c] = peer_y ? peer_y[(t * k + j) * d + c] : 0.0;
+      } else {
+        mokref_ffn_row(d, I, prec, tok_x + t * d, wg + le * I * d, wu + le * I * d,
+                       wd + le * d * I, NULL, NULL, NULL, yj);
       }
-      mokref_ffn_row(d, I, prec, tok_x + t * d, wg + le * I * d, wu + le * I * d,
-                     wd + le * d * I, NULL, NULL, NULL, yj);
       for (int64_t c = 0; c < d; ++c) o[c] += gate[t * k + j] * yj[c];
     }
     store_round(prec == MOKREF_MXFP8 ? MOKREF_BF16 : prec, d, o);
@@ -426,16 +430,20 @@ void mokref_router_bwd_token(int64_t d, int64_t k, const int32_t* idx, const dou
   }
 }
 
-/* Backward of a list of tokens routed here (float64, no roundings).
+/* Backward of a list of tokens (float64, no roundings).
  * Per token: for each slot whose expert is local, the row backward above;
- * d_gate[t][j] (0 for remote slots); dx[t] = sum_j dx_row_j + the router path
- * (computed with the remote slots' gate gradients taken as 0, i.e. this GPU's
- * share of a sum over GPUs -- the router gradient is linear in d_gate).
- * dz: [n_tok, k] out. */
+ * for a slot whose expert is remote, the GPU holding that expert computes
+ * the same row backward and writes its gate gradient and pushes its input
+ * gradient back to the token's source (kucoin article, section 02: pull
+ * reverse-combine, push reverse-dispatch): those arrive as peer_dg [n_tok, k]
+ * and peer_dx [n_tok, k, d] (either may be NULL = zeros).
+ * d_gate[t][j] = the slot's gate gradient; dx[t] = sum_j dx_row_j + the
+ * router path through dz = g (dg - sum g dg).  dz: [n_tok, k] out. */
 void mokref_bwd_tokens(int64_t n_tok, int64_t d, int64_t E, int64_t k, int64_t I,
                        const float* tok_x, const float* tok_dout, const int32_t* topk,
                        const double* gate, const int32_t* e2l, const float* wr, const float* wg,
-                       const float* wu, const float* wd, double* d_gate, double* dz, double* dx) {
+                       const float* wu, const float* wd, const double* peer_dg,
+                       const double* peer_dx, double* d_gate, double* dz, double* dx) {
   double* dxr = (double*)malloc(sizeof(double) * (size_t)d);
   double* dxj = (double*)malloc(sizeof(double) * (size_t)d);
   for (int64_t t = 0; t < n_tok; ++t) {
@@ -444,7 +452,9 @@ void mokref_bwd_tokens(int64_t n_tok, int64_t d, int64_t E, int64_t k, int64_t I
     for (int64_t j = 0; j < k; ++j) {
       int32_t le = e2l[topk[t * k + j]];
       if (le < 0) {
-        d_gate[t * k + j] = 0.0;
+        d_gate[t * k + j] = peer_dg ? peer_dg[t * k + j] : 0.0;
+        if (peer_dx)
+          for (int64_t c = 0; c < d; ++c) o[c] += peer_dx[(t * k + j) * d + c];
         continue;
       }
       mokref_bwd_row(d, I, tok_x + t * d, gate[t * k + j], tok_dout + t * d, wg + le * I * d,

@@ -28,6 +28,9 @@ class HostCase:
     wd_val: np.ndarray
     e2l: np.ndarray
     other: Dict[int, tuple]        # non-own sources: (topk_idx, topk_gate)
+    # own sources of a share: what the GPUs holding the remote experts write
+    # back (synth.gen_peer_slots: y store, y values, d_gate, dx store, dx values)
+    peer: Dict[int, tuple] = dataclasses.field(default_factory=dict)
     # oracle results
     topk_all: np.ndarray = None    # [S, T_src, k]
     gate_all: np.ndarray = None    # [S, T_src, k] float64 (own: oracle gates)
@@ -51,6 +54,8 @@ def make_host_case(w: synth.Workload, route_own=True) -> HostCase:
     other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
     c = HostCase(w, [a for a, _ in xs], [b for _, b in xs], wr[0], wr[1], bias, wg[0], wg[1], wu[0],
                  wu[1], wd[0], wd[1], w.expert_to_local(), other)
+    if w.E_local < w.E:
+        c.peer = {s: synth.gen_peer_slots(w, s) for s in w.own}
     if route_own:
         oracle_routing(c)
     return c
@@ -81,13 +86,23 @@ def oracle_weights(c: HostCase):
     return tuple(out)
 
 
+def peer_rows(c: HostCase, toks, which: int):
+    """Peer-written values of the tokens' k slots (which: 1 = y rows, 2 =
+    d_gate, 4 = dx rows), or None when every expert is local."""
+    if not c.peer:
+        return None
+    k = c.w.k
+    return np.stack([c.peer[s][which][t * k:(t + 1) * k] for s, t in toks])
+
+
 def oracle_fwd_tokens(c: HostCase, toks):
     """toks: list of (s, t) -> (y [n, k, d], out [n, d]) from the oracle."""
     tok_x = np.stack([c.x_val[s][t] for s, t in toks])
     idx = np.stack([c.topk_all[s, t] for s, t in toks])
     g = np.stack([c.gate_all[s, t] for s, t in toks])
     wg, wu, wd = oracle_weights(c)
-    return oracle.fwd_tokens(tok_x, idx, g, c.e2l, wg, wu, wd, c.w.prec)
+    return oracle.fwd_tokens(tok_x, idx, g, c.e2l, wg, wu, wd, c.w.prec,
+                             peer_y=peer_rows(c, toks, 1))
 
 
 def rel_err(got, ref) -> float:

@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle
-from cases import make_host_case, oracle_fwd_tokens, oracle_weights, rel_err, sample_tokens
+from cases import (make_host_case, oracle_fwd_tokens, oracle_weights, peer_rows, rel_err,
+                   sample_tokens)
 from combine_router_top_expert_amd import (STATUS, make_config, make_weights, mok_combine,
                                            mok_dispatch, mok_expert_ffn, mok_layout,
                                            mok_mx_quantize, mok_route, mok_workspace_bytes, synth)
@@ -32,6 +33,9 @@ def _layer(c, R_cap=None, with_bwd=True, **kw):
     L.set_inputs(xs, to_device(c.wr_store, w.prec, DEV), bias, torch.from_numpy(c.e2l).to(DEV),
                  to_device(c.wg_store, w.prec, DEV), to_device(c.wu_store, w.prec, DEV),
                  to_device(c.wd_store, w.prec, DEV), other_topk=c.other)
+    for s, (ys, _, dg, dxs, _) in c.peer.items():
+        L.set_peer_slots(s, to_device(ys, w.prec, DEV), torch.from_numpy(dg).to(DEV),
+                         to_device(dxs, w.prec, DEV))
     return L
 
 
@@ -162,16 +166,18 @@ def test_dispatch_tagged_rows_and_identity_combine():
     toks = ref["row_src"] // w.k
     want = np.stack([xs_val[t // w.T_src][t % w.T_src] for t in toks])
     np.testing.assert_array_equal(got, want)
-    # identity experts: y = gathered rows; push + final combine for the own source
+    # identity experts here and at the peers: y = the token's row in every
+    # slot (the peers' pushes written up front); push + final combine for the
+    # own source sums all k slots
     staging = [torch.zeros(w.T_src * w.k, w.d, dtype=torch.bfloat16, device=DEV) for _ in range(w.S)]
+    staging[1].copy_(x[1].repeat_interleave(w.k, dim=0))
     out = [torch.zeros(w.T_src, w.d, dtype=torch.bfloat16, device=DEV) for _ in range(w.S)]
     mok_combine(cfg, xp, torch.from_numpy(ref["dest_row"]).to(DEV),
                 torch.from_numpy(gate.reshape(-1)).to(DEV), staging, 1, 1, out, st)
     torch.cuda.synchronize()
     o = out[1].float().cpu().numpy()
     xv = synth.bf16_bits_to_f32(xs_val[1]).astype(np.float64)
-    loc = (e2l[topk[1]] >= 0)
-    gsum = (gate[1].astype(np.float64) * loc).sum(1)
+    gsum = gate[1].astype(np.float64).sum(1)
     expect = xv * gsum[:, None]
     assert np.all(np.abs(o - expect) <= 2.0 ** -8 * np.abs(expect) + 1e-30)
 
@@ -320,6 +326,9 @@ def _check_fwd(c, L, toks):
             if c.e2l[c.topk_all[s, t, j]] >= 0:
                 ys.append(L.staging[s][t * w.k + j].float().cpu().numpy())
                 ysr.append(y_ref[i, j])
+            else:  # a remote slot keeps what its pusher wrote
+                got = L.staging[s][t * w.k + j].float().cpu().numpy()
+                np.testing.assert_array_equal(got, c.peer[s][1][t * w.k + j])
     e_out = rel_err(np.stack(outs), out_ref)
     e_y = rel_err(np.stack(ys), np.stack(ysr)) if ys else 0.0
     _log(f"  out rel err {e_out:.3e}  y rel err {e_y:.3e}")
@@ -375,11 +384,14 @@ def test_layer_bwd(name):
     idx = np.stack([c.topk_all[s, t] for s, t in toks])
     g = np.stack([c.gate_all[s, t] for s, t in toks])
     dg_ref, dz_ref, dx_ref = oracle.bwd_tokens(tok_x, tok_d, idx, g, c.e2l, c.wr_val, c.wg_val,
-                                               c.wu_val, c.wd_val)
+                                               c.wu_val, c.wd_val, peer_dg=peer_rows(c, toks, 2),
+                                               peer_dx=peer_rows(c, toks, 4))
     dg = L.d_gate.cpu().numpy().reshape(w.S, w.T_src, w.k)
     dg_got = np.stack([dg[s, t] for s, t in toks])
     local = c.e2l[idx] >= 0
     assert rel_err(dg_got[local], dg_ref[local]) <= tol
+    # remote slots: the peers' gate gradients are read, never overwritten
+    np.testing.assert_array_equal(dg_got[~local], dg_ref[~local].astype(np.float32))
     dx_got = np.stack([L.d_x[s][t].float().cpu().numpy() for s, t in toks])
     e_dx = rel_err(dx_got, dx_ref)
     # weight gradients per local expert (rows of all sources, in layout order)

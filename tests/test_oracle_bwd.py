@@ -131,3 +131,59 @@ def test_router_bwd_closed_form_properties():
         zp[j] += 1e-6; zm[j] -= 1e-6
         f = lambda zz: (np.exp(zz - zz.max()) / np.exp(zz - zz.max()).sum() * dg).sum()
         np.testing.assert_allclose(dz3[j], (f(zp) - f(zm)) / 2e-6, rtol=1e-6, atol=1e-10)
+
+
+def _split(p, mine):
+    """Experts split between this GPU (`mine`) and a peer holding the rest:
+    (e2l here, e2l at the peer, weights here, weights at the peer)."""
+    E = p["e2l"].shape[0]
+    theirs = [e for e in range(E) if e not in mine]
+    e2l_a = np.full(E, -1, np.int32)
+    e2l_b = np.full(E, -1, np.int32)
+    for i, e in enumerate(mine):
+        e2l_a[e] = i
+    for i, e in enumerate(theirs):
+        e2l_b[e] = i
+    pick = lambda es: tuple(p[n][[p["e2l"][e] for e in es]] for n in ("wg", "wu", "wd"))
+    return e2l_a, e2l_b, pick(mine), pick(theirs)
+
+
+@pytest.mark.parametrize("mine", [[0, 2], [1], [0, 1, 3]])
+def test_share_with_peer_slots_equals_all_local(mine):
+    """Expert parallelism over two GPUs: the source's combine and backward
+    sum over all k slots, the remote ones filled by the peer's push and its
+    reverse-combine (pull, then push back).  With the peer's values taken from
+    the same oracle run on the peer's experts, the share reproduces the
+    all-local result exactly (same values, same slot order)."""
+    p = _setup(21, T=7, d=16, E=4, k=3, I=12)
+    idx, g = oracle.route(p["x"], p["wr"], p["bias"], p["k"], "exact")
+    e2l_a, e2l_b, wa, wb = _split(p, mine)
+    y_all, out_all = oracle.fwd_tokens(p["x"], idx, g, p["e2l"], p["wg"], p["wu"], p["wd"], "exact")
+    y_b, _ = oracle.fwd_tokens(p["x"], idx, g, e2l_b, *wb, "exact")
+    y_a, out_a = oracle.fwd_tokens(p["x"], idx, g, e2l_a, *wa, "exact", peer_y=y_b)
+    np.testing.assert_array_equal(y_a, y_all)
+    np.testing.assert_array_equal(out_a, out_all)
+    # without the peer's rows the share misses exactly the remote slots' terms
+    _, out_0 = oracle.fwd_tokens(p["x"], idx, g, e2l_a, *wa, "exact")
+    remote = e2l_a[idx] < 0
+    miss = np.einsum("tj,tjd->td", g * remote, y_all)
+    np.testing.assert_allclose(out_all - out_0, miss, rtol=0, atol=1e-12)
+    assert np.abs(miss).max() > 0.01
+    # backward: the peer's gate gradients and dx rows of its slots
+    dg_all, dz_all, dx_all = oracle.bwd_tokens(p["x"], p["dout"], idx, g, p["e2l"], p["wr"],
+                                               p["wg"], p["wu"], p["wd"])
+    T, k, d = idx.shape[0], idx.shape[1], p["x"].shape[1]
+    peer_dg = np.zeros((T, k))
+    peer_dx = np.zeros((T, k, d))
+    for t in range(T):
+        for j in range(k):
+            lb = e2l_b[idx[t, j]]
+            if lb >= 0:
+                r = oracle.bwd_row(p["x"][t], g[t, j], p["dout"][t], wb[0][lb], wb[1][lb], wb[2][lb])
+                peer_dg[t, j], peer_dx[t, j] = r["dg"], r["dx"]
+    dg_a, dz_a, dx_a = oracle.bwd_tokens(p["x"], p["dout"], idx, g, e2l_a, p["wr"], *wa,
+                                         peer_dg=peer_dg, peer_dx=peer_dx)
+    np.testing.assert_array_equal(dg_a, dg_all)
+    np.testing.assert_array_equal(dz_a, dz_all)
+    np.testing.assert_array_equal(dx_a, dx_all)
+    assert remote.any() and (~remote).any()

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kGemmThreads) void dh_kernel(BwdPlan p, int ntn) {
         const float dh = acc.c[mi][nj][v];
         const float av = to_f32<T>(ab[(size_t)r * 2 * p.I + i]);
         const float bv = to_f32<T>(ab[(size_t)r * 2 * p.I + p.I + i]);
-        const float sg = 1.0f / (1.0f + __expf(-av));
+        const float sg = sigmoid_f(av);
         dab[(size_t)r * 2 * p.I + i] = from_f32<T>(dh * bv * sg * (1.0f + av * (1.0f - sg)));
         dab[(size_t)r * 2 * p.I + p.I + i] = from_f32<T>(dh * av * sg);
       }

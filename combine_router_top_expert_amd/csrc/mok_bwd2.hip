@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const bf16_t* ab, 
     const float dh = __uint_as_float(e & 1 ? hw[w] & 0xFFFF0000u : hw[w] << 16);
     const float x = __uint_as_float(e & 1 ? aw[w] & 0xFFFF0000u : aw[w] << 16);
     const float y = __uint_as_float(e & 1 ? bw[w] & 0xFFFF0000u : bw[w] << 16);
-    const float sg = 1.0f / (1.0f + __expf(-x));
+    const float sg = sigmoid_f(x);
     da[e] = dh * y * sg * (1.0f + x * (1.0f - sg));
     db[e] = dh * x * sg;
   }

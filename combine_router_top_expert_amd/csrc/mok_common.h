@@ -27,11 +27,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
+// fp32 -> bf16, round to nearest even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+// Two values -> one word (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const f32x2_hw_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw_t));
 }
 
 template <typename T>
@@ -67,7 +73,13 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+// sigmoid(a) = 1 / (1 + e^-a) with the hardware base-2 exponential and
+// reciprocal (each within 1 ulp): e^-a = 2^(-a log2 e).  a -> -inf gives
+// 1/inf = 0, a -> +inf gives 1.
+__device__ __forceinline__ float sigmoid_f(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
+__device__ __forceinline__ float silu_f(float a) { return a * sigmoid_f(a); }
 
 // Record one trace event after the kernel just launched (host side).
 inline void trace_mark(mok_trace* t, const char* name, hipStream_t s) {

@@ -224,8 +224,7 @@ __device__ __forceinline__ int out_col(int j, int g) {
 
 // Four fp32 -> four bf16 packed in 8 bytes.
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-  return make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
-                    (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+  return make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
 }
 
 // Fragments of one k16 step for a wave: 4 row blocks of A, WNB column blocks of B.

@@ -92,17 +92,22 @@ typedef struct mok_trace {
 typedef struct mok_config {
   int32_t S;              /* source token buffers (simulated source ranks), 1..MOK_MAX_SOURCES */
   int32_t T_src;          /* tokens per source buffer */
-  int32_t d;              /* hidden size (multiple of 8; of 32 for MXFP8) */
-  int32_t E;              /* experts in the layer */
-  int32_t k;              /* experts chosen per token, 1..min(E, 8) */
-  int32_t I;              /* SwiGLU intermediate size per expert (multiple of 8; of 32 for MXFP8) */
+  int32_t d;              /* hidden size: multiple of 64 (MOK_EINVAL otherwise); the MXFP8
+                             expert FFN and the MXFP8 ring need a multiple of 128 (MOK_ESHAPE) */
+  int32_t E;              /* experts in the layer, 1..512 */
+  int32_t k;              /* experts chosen per token, 1..min(E, 16) */
+  int32_t I;              /* SwiGLU intermediate size per expert: multiple of 64; of 128 for
+                             the MXFP8 expert FFN (MOK_ESHAPE) */
   int32_t E_local;        /* experts whose FFN runs on this GPU, 1..256 */
   int32_t prec;           /* mok_prec */
   int32_t R_cap;          /* row capacity of every routed-row buffer */
   int32_t minibatch_rows; /* fused path: at most this many rows of one expert per minibatch */
-  int64_t ring_bytes;     /* fused path: bytes of the ring of token slots; 0 = staged path */
-  int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = auto) */
-  int32_t gemm_wgs;       /* fused path: grouped-GEMM workgroups (0 = auto) */
+  int64_t ring_bytes;     /* fused path (persistent ring kernel, bf16 and MXFP8): bytes of the
+                             ring of token slots, at least one slot of minibatch_rows rows;
+                             0 = staged path (one launch per step) */
+  int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = CUs / 8) */
+  int32_t gemm_wgs;       /* fused path: grouped-GEMM workgroups (0 = the remaining CUs);
+                             comm_wgs + gemm_wgs must not exceed the CU count */
   int32_t wait_limit_us;  /* fused path: bound of every device-side wait in microseconds;
                              on expiry MOK_ETIMEOUT is latched and the kernel returns
                              (0 = 2 s) */

@@ -415,6 +415,73 @@ def test_layer_bwd(name):
     assert e_dx <= tol and e_w <= tol and e_r <= tol
 
 
+def _bwd_sampled(c, L, dout_store, toks):
+    """d_gate and d_x of sampled own tokens against the oracle."""
+    w = c.w
+    tok_x = np.stack([c.x_val[s][t] for s, t in toks])
+    tok_d = np.stack([dout_store[s][1][t] for s, t in toks])
+    idx = np.stack([c.topk_all[s, t] for s, t in toks])
+    g = np.stack([c.gate_all[s, t] for s, t in toks])
+    dg_ref, _, dx_ref = oracle.bwd_tokens(tok_x, tok_d, idx, g, c.e2l, c.wr_val, c.wg_val,
+                                          c.wu_val, c.wd_val, peer_dg=peer_rows(c, toks, 2),
+                                          peer_dx=peer_rows(c, toks, 4))
+    dg = L.d_gate.cpu().numpy().reshape(w.S, w.T_src, w.k)
+    dg_got = np.stack([dg[s, t] for s, t in toks])
+    local = c.e2l[idx] >= 0
+    e_dg = rel_err(dg_got[local], dg_ref[local])
+    np.testing.assert_array_equal(dg_got[~local], dg_ref[~local].astype(np.float32))
+    dx_got = np.stack([L.d_x[s][t].float().cpu().numpy() for s, t in toks])
+    e_dx = rel_err(dx_got, dx_ref)
+    _log(f"  sampled d_gate {e_dg:.3e} dx {e_dx:.3e}")
+    assert e_dg <= TOL[w.prec] and e_dx <= TOL[w.prec]
+
+
+# full-size backward workloads: (workload, check the weight gradients of the
+# least-routed local expert -- the oracle computes them row by row)
+BWD_FULL = {
+    "c5_full": (synth.WORKLOADS["C5"], True),
+    "c3_full": (synth.WORKLOADS["C3"], False),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_FULL))
+def test_layer_bwd_full_sampled(name):
+    """Full-size forward + backward in the launch configuration bench.py
+    times, checked on sampled tokens (forward: routing and layout bit-exact,
+    outputs and pushed rows; backward: d_gate and d_x; for the skewed
+    mid-size layer also one expert's weight gradients)."""
+    w, check_dw = BWD_FULL[name]
+    _log("layer_bwd_full", name)
+    c = make_host_case(w)
+    L = _layer(c)
+    dout_store = [synth.gen_dout(w, s) for s in range(w.S)]
+    d_out = [to_device(a, w.prec, DEV) for a, _ in dout_store]
+    L.forward()
+    L.backward(d_out)
+    torch.cuda.synchronize()
+    L.check_status()
+    toks = sample_tokens(w, 16)
+    _check_fwd(c, L, toks)
+    _bwd_sampled(c, L, dout_store, toks)
+    if not check_dw:
+        return
+    lay = c.layout
+    cnt = np.diff(lay["offsets"])
+    le = int(np.argmin(np.where(cnt > 0, cnt, np.iinfo(np.int64).max)))
+    rows = lay["row_src"][lay["offsets"][le]:lay["offsets"][le + 1]]
+    _log(f"  expert {le}: {len(rows)} rows")
+    tt = rows // w.k
+    jj = rows % w.k
+    rx = np.stack([c.x_val[t // w.T_src][t % w.T_src] for t in tt])
+    rg = np.array([c.gate_all[t // w.T_src, t % w.T_src, j] for t, j in zip(tt, jj)])
+    rd = np.stack([dout_store[t // w.T_src][1][t % w.T_src] for t in tt])
+    dwg, dwu, dwd = oracle.expert_wgrad(rx, rg, rd, c.wg_val[le], c.wu_val[le], c.wd_val[le])
+    e_w = max(rel_err(L.dw_gate[le].cpu().numpy(), dwg), rel_err(L.dw_up[le].cpu().numpy(), dwu),
+              rel_err(L.dw_down[le].cpu().numpy(), dwd))
+    _log(f"  dW rel err {e_w:.3e}")
+    assert e_w <= TOL[w.prec]
+
+
 def test_fwd_bwd_run_to_run_bit_identical():
     w = BWD_CASES["bf16_all_local"].replace(T_src=400)
     _log("determinism")

@@ -37,8 +37,8 @@ __global__ __launch_bounds__(kThreads) void dh_g2(DhArgs a) {
   const int total_m = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix);
   const int total = total_m * a.ntn;
   if ((int)blockIdx.x >= total) return;
-  const int t = xcd_tile(blockIdx.x, total);
-  const int mtile = t / a.ntn, nt = t % a.ntn;
+  int mtile, nt;
+  grouped_order(xcd_tile(blockIdx.x, total), total_m, a.ntn, &mtile, &nt);
   const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mtile);
   const int n0 = nt * C::BN;
   const bf16_t* wd = a.wd + (size_t)g.e * a.d * a.I + n0;
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(kThreads) void dx_g2(DxArgs a) {
   const int total_m = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix);
   const int total = total_m * a.ntn;
   if ((int)blockIdx.x >= total) return;
-  const int t = xcd_tile(blockIdx.x, total);
-  const int mtile = t / a.ntn, nt = t % a.ntn;
+  int mtile, nt;
+  grouped_order(xcd_tile(blockIdx.x, total), total_m, a.ntn, &mtile, &nt);
   const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mtile);
   const int n0 = nt * C::BN;
   const bf16_t* wg = a.wg + (size_t)g.e * a.I * a.d + n0;

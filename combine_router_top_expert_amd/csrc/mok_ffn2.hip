@@ -25,9 +25,9 @@ __device__ __forceinline__ bool launch_tile(const int32_t* offsets, int E_local,
   const int total_m = group_prefix(offsets, E_local, R_cap, s_prefix);
   const int total = total_m * ntn;
   if ((int)blockIdx.x >= total) return false;
-  const int t = xcd_tile(blockIdx.x, total);
-  *nt = t % ntn;
-  *g = group_tile(offsets, E_local, R_cap, s_prefix, t / ntn);
+  int mt;
+  grouped_order(xcd_tile(blockIdx.x, total), total_m, ntn, &mt, nt);
+  *g = group_tile(offsets, E_local, R_cap, s_prefix, mt);
   return true;
 }
 

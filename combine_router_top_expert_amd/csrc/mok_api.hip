@@ -81,7 +81,8 @@ Ws ws_layout(const mok_config* c) {
   w.r_scratch = b;
   b += align256(c->E <= 256 ? layout_ws_bytes(N, c->E) : 0);
   w.bx = b;
-  b += align256(R * c->d * act_bytes(c->prec));
+  b += align256(c->prec == MOK_BF16 ? (size_t)c->d * xt_ld(c->R_cap, c->E_local) * 2
+                                    : R * c->d * act_bytes(c->prec));
   w.wpart = b;
   b += align256(c->prec == MOK_BF16 ? wgrad_partial_bytes(c->R_cap, c->d, c->I) : 0);
   w.total = f > b ? f : b;

@@ -393,8 +393,7 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
     if (p.R_cap > 0) {
       hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
       trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
-      mok_status rc = launch_gather(MOK_BF16, p.src_x, p.T_src, p.d, p.k, p.E_local, p.R_cap,
-                                    p.row_src, p.offsets, p.x_perm, nullptr, stream, nullptr);
+      mok_status rc = launch_gather_t(p, p.x_perm, stream);
       if (rc != MOK_OK) return rc;
       trace_mark(p.tr, "bwd_regather_x", stream);
     }

@@ -172,6 +172,8 @@ struct WgArgs {
   float* out0;         // MODE 0: dW_gate [E_local, I, d]; MODE 1: dW_down [E_local, d, I]
   float* out1;         // MODE 0: dW_up
   float* part;         // [extra chunks, M, N] partial sums of chunks 1, 2, ... of an expert
+  const bf16_t* BT;    // MODE 0: the expert rows' tokens transposed, [N, ldt] (gather_t_kernel)
+  int64_t ldt;
   const int32_t* offsets;
   int lda, ldb, M, N, I, E_local, R_cap, mtn, ntn;
 };
@@ -185,55 +187,124 @@ struct WgArgs {
 constexpr int kWgChunk = 4096;
 
 // Wave 0 scans the per-expert chunk counts: s_cp[e] = chunks of the experts
-// before e, s_xp[e] = their chunks beyond the first (partial slots); index
-// 256 holds the totals.
+// before e, s_xp[e] = their chunks beyond the first (partial slots), s_tp[e]
+// = their 64-row tiles (the expert's first column in the transposed token
+// rows is 64 s_tp[e]); index 256 holds the totals.
 __device__ __forceinline__ void wg_chunk_prefix(const int32_t* offsets, int E_local, int R_cap,
-                                                int* s_cp, int* s_xp) {
+                                                int* s_cp, int* s_xp, int* s_tp) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int ch[4], run_c = 0, run_x = 0;
+    int ch[4], tl[4], run_c = 0, run_x = 0, run_t = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      int c = 0;
+      int c = 0, t = 0;
       if (e < E_local) {
         const int lo = min(offsets[e], R_cap), hi = min(offsets[e + 1], R_cap);
         c = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 0;
+        t = hi > lo ? (hi - lo + 63) / 64 : 0;
       }
       ch[q] = c;
+      tl[q] = t;
       run_c += c;
       run_x += c > 1 ? c - 1 : 0;
+      run_t += t;
     }
-    int inc_c = run_c, inc_x = run_x;
+    int inc_c = run_c, inc_x = run_x, inc_t = run_t;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(inc_c, off, 64), ox = __shfl_up(inc_x, off, 64);
+      const int oc = __shfl_up(inc_c, off, 64), ox = __shfl_up(inc_x, off, 64),
+                ot = __shfl_up(inc_t, off, 64);
       if (lane >= off) {
         inc_c += oc;
         inc_x += ox;
+        inc_t += ot;
       }
     }
-    int ec = inc_c - run_c, ex = inc_x - run_x;
+    int ec = inc_c - run_c, ex = inc_x - run_x, et = inc_t - run_t;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       s_cp[lane * 4 + q] = ec;
       s_xp[lane * 4 + q] = ex;
+      s_tp[lane * 4 + q] = et;
       ec += ch[q];
       ex += ch[q] > 1 ? ch[q] - 1 : 0;
+      et += tl[q];
     }
     if (lane == 63) {
       s_cp[256] = inc_c;
       s_xp[256] = inc_x;
+      s_tp[256] = inc_t;
     }
   }
   __syncthreads();
 }
 
+// Token rows of the local experts gathered again for the gate/up weight
+// gradients, transposed: xT[c][col] = x_token(r)[c] for routed row r of
+// expert e at column col = 64 P(e) + (r - offsets[e]), P(e) = 64-row tiles of
+// the experts before e; the columns up to the next multiple of 64 hold zeros.
+// The weight-gradient GEMM then reads this operand k-contiguous, in whole
+// 64-k stages, instead of through transposing LDS reads.  A workgroup covers
+// 4 consecutive 64-row tiles (256 columns of xT) x 64 columns of d: thread
+// (rg, cb) loads 16 bytes (8 columns of d) of each of its 8 rows, transposes
+// the 8 x 8 block in registers and stores 16 bytes (8 rows) into each of its
+// 8 columns of d.  A wave instruction reads 8 rows x 128 bytes; a workgroup
+// writes 512 contiguous bytes of each of its 64 rows of xT.  Workgroups
+// stride over the tile groups so the per-expert tile prefix is computed once
+// per workgroup.
+struct GatherTArgs {
+  SrcTable src;
+  const int32_t* row_src;
+  const int32_t* offsets;
+  bf16_t* xT;      // [d, ldt]
+  int64_t ldt;
+  int d, E_local, R_cap, T_src, k;
+};
+
+__global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
+  __shared__ int s_prefix[257];
+  const int total = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix, 64);
+  const int cb = threadIdx.x & 7, rg = (threadIdx.x >> 3) & 7, sub = threadIdx.x >> 6;
+  const int c0 = blockIdx.y * 64 + 8 * cb;
+  for (int grp = blockIdx.x; 4 * grp < total; grp += gridDim.x) {
+    const int mt = 4 * grp + sub;  // this wave's 64-row tile
+    if (mt >= total) continue;
+    const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mt, 64);
+    uint32_t v[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = g.r0 + 8 * rg + i;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (r < g.r1) {
+        const int tok = a.row_src[r] / a.k;
+        u = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
+                                            (size_t)(tok % a.T_src) * a.d + c0);
+      }
+      v[i][0] = u.x;
+      v[i][1] = u.y;
+      v[i][2] = u.z;
+      v[i][3] = u.w;
+    }
+    bf16_t* dst = a.xT + (size_t)c0 * a.ldt + 64 * mt + 8 * rg;
+#pragma unroll
+    for (int jc = 0; jc < 8; ++jc) {
+      const int w = jc >> 1;
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (jc & 1) ? (v[2 * q][w] >> 16) | (v[2 * q + 1][w] & 0xFFFF0000u)
+                        : (v[2 * q][w] & 0xFFFFu) | (v[2 * q + 1][w] << 16);
+      *reinterpret_cast<uint4*>(dst + (size_t)jc * a.ldt) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  __shared__ int s_cp[257], s_xp[257];
-  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp);
+  __shared__ int s_cp[257], s_xp[257], s_tp[257];
+  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp);
   // Chunks are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
   // b % 8) and a chunk's tiles stay on one XCD: chunks of a heavily routed
   // expert spread over all XCDs while the tiles that share a chunk's operand
@@ -256,24 +327,37 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   const int cnt = min(kWgChunk, end - off);
   const int m0 = mt * BM, n0 = nt * C::BN;
   MNMajor<BM, C::BK> la;
-  MNMajor<C::BN, C::BK> lb;
   la.ncols_left = a.M - m0;
-  lb.ncols_left = a.N - n0;
   const bf16_t* Ab = a.A + (size_t)off * a.lda + m0;
-  const bf16_t* Bb = a.B + (size_t)off * a.ldb + n0;
+  auto issue_a = [&](int kt, unsigned l) {
+    la.issue(kt, l, [&](int kk) -> const bf16_t* { return kk < cnt ? Ab + (size_t)kk * a.lda : nullptr; });
+  };
   Acc<C> acc;
-  mainloop<C, true, true>((cnt + C::BK - 1) / C::BK,
-                       [&](int kt, unsigned l) {
-                         la.issue(kt, l, [&](int kk) -> const bf16_t* {
-                           return kk < cnt ? Ab + (size_t)kk * a.lda : nullptr;
-                         });
-                       },
-                       [&](int kt, unsigned l) {
-                         lb.issue(kt, l, [&](int kk) -> const bf16_t* {
-                           return kk < cnt ? Bb + (size_t)kk * a.ldb : nullptr;
-                         });
-                       },
-                       smem, acc);
+  if constexpr (MODE == 0) {
+    // B = the chunk's token rows from the transposed copy: row n of the tile
+    // is column n0 + n of d, k-contiguous from the chunk's first column; the
+    // last stage runs into the expert's zero padding
+    static_assert(C::BK == 64, "the transposed rows are padded to 64");
+    KMajor<C::BN, C::BK> lb;
+    const bf16_t* Bt = a.BT + (size_t)64 * s_tp[e] + (size_t)c * kWgChunk;
+    lb.init([&](int nr) -> const bf16_t* {
+      const int n = n0 + nr;
+      return n < a.N ? Bt + (size_t)n * a.ldt : nullptr;
+    });
+    mainloop<C, true, false>((cnt + C::BK - 1) / C::BK, issue_a,
+                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+  } else {
+    MNMajor<C::BN, C::BK> lb;
+    lb.ncols_left = a.N - n0;
+    const bf16_t* Bb = a.B + (size_t)off * a.ldb + n0;
+    mainloop<C, true, true>((cnt + C::BK - 1) / C::BK, issue_a,
+                            [&](int kt, unsigned l) {
+                              lb.issue(kt, l, [&](int kk) -> const bf16_t* {
+                                return kk < cnt ? Bb + (size_t)kk * a.ldb : nullptr;
+                              });
+                            },
+                            smem, acc);
+  }
   float* part = c > 0 ? a.part + (size_t)(s_xp[e] + c - 1) * a.M * a.N : nullptr;
   __syncthreads();
   const WaveStage<C, float> st(smem);
@@ -303,12 +387,12 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
 // (blocks per expert, E_local), experts with one chunk return at once.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void wgrad_reduce(WgArgs a) {
-  __shared__ int s_cp[257], s_xp[257];
+  __shared__ int s_cp[257], s_xp[257], s_tp[257];
   const int e = blockIdx.y;
   const int lo = min(a.offsets[e], a.R_cap), hi = min(a.offsets[e + 1], a.R_cap);
   const int ch = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 0;
   if (ch <= 1) return;
-  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp);
+  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp);
   const int xp = s_xp[e];
   const int n4 = a.N / 4;
   const size_t units = (size_t)a.M * n4;
@@ -337,6 +421,27 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce(WgArgs a) {
 
 size_t wgrad_partial_bytes(int R_cap, int d, int I) {
   return (size_t)(R_cap / kWgChunk) * 2 * (size_t)I * d * sizeof(float);
+}
+
+mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream) {
+  if (p.R_cap == 0) return MOK_OK;
+  GatherTArgs g;
+  g.src = p.src_x;
+  g.row_src = p.row_src;
+  g.offsets = p.offsets;
+  g.xT = reinterpret_cast<bf16_t*>(xT);
+  g.ldt = xt_ld(p.R_cap, p.E_local);
+  g.d = p.d;
+  g.E_local = p.E_local;
+  g.R_cap = p.R_cap;
+  g.T_src = p.T_src;
+  g.k = p.k;
+  const int tiles = (p.R_cap + 63) / 64 + p.E_local;  // bound of the 64-row tiles
+  const int groups = (tiles + 3) / 4;
+  const int gx = groups < 256 ? groups : 256;
+  hipLaunchKernelGGL(gather_t_kernel, dim3((unsigned)gx, (unsigned)(p.d / 64)), dim3(kThreads), 0,
+                     stream, g);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream) {
@@ -382,7 +487,9 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   WgArgs w;
   w.part = p.wg_part;
   w.A = reinterpret_cast<const bf16_t*>(p.dab);
-  w.B = reinterpret_cast<const bf16_t*>(x_perm);
+  w.B = nullptr;
+  w.BT = reinterpret_cast<const bf16_t*>(x_perm);
+  w.ldt = xt_ld(p.R_cap, p.E_local);
   w.out0 = p.dw_gate;
   w.out1 = p.dw_up;
   w.offsets = p.offsets;

@@ -107,11 +107,17 @@ struct BwdPlan {
   // router layout of the own items over all E experts (workspace)
   int32_t *r_ident, *r_counts, *r_offsets, *r_row_src, *r_dest_row;
   void* r_scratch;
-  void* x_perm;     // [R_cap, d] token rows gathered again for the wgrad GEMM
+  void* x_perm;     // bf16: [d, xt_ld] token rows gathered again, transposed, for the wgrad GEMM
   float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
   mok_trace* tr;    // host-side trace, may be null
 };
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
+// Leading dimension of the transposed token rows of the gate/up weight
+// gradients ([d, xt_ld] bf16): every expert's rows padded to 64 columns.
+inline int64_t xt_ld(int R_cap, int E_local) {
+  return ((int64_t)R_cap + 63) / 64 * 64 + 64 * (int64_t)E_local;
+}
+mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream);
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream);
 size_t wgrad_partial_bytes(int R_cap, int d, int I);
 

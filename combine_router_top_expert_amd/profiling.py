@@ -42,6 +42,7 @@ TRACE_NAME = {
     "wgrad_reduce<0>": "bwd_wgrad_gate_up_reduce", "wgrad_reduce<1>": "bwd_wgrad_down_reduce",
     "dx_final_kernel": "bwd_dx_sum_router", "dwr_part_kernel": "bwd_dw_router_part",
     "dwr_reduce_kernel": "bwd_dw_router_reduce", "ring_kernel": "ring_fused_ffn",
+    "gather_t_kernel": "bwd_regather_x",
 }
 
 

@@ -24,7 +24,12 @@
 //                 rows (push combine); waits for g1_done[m] == GEMM1 tiles.
 // Each side takes its units from an atomic ticket counter in a fixed order:
 // fills by (m, c); GEMM work in steps u = 0, 1, ... each holding the GEMM1
-// tiles of minibatch u followed by the GEMM2 tiles of minibatch u - kLag.
+// tiles of minibatch u followed by the GEMM2 tiles of minibatch u - lag.  The
+// lag covers the steps that run at once (GEMM workgroups / tiles per step,
+// plus one), so that when a workgroup takes a GEMM2 tile the GEMM1 tiles it
+// needs were taken a full round of the GEMM side earlier and are normally
+// done: with a lag of 2 on the mid-size layer (224 GEMM workgroups, 19 tiles
+// per step) almost every GEMM2 tile waited most of a tile's time.
 // Every wait is on work with a smaller ticket (GEMM2 on GEMM1 of an earlier
 // step, a fill on GEMM1 of minibatch m - nslot < m, GEMM1 on the fills of its
 // own step), and tickets are taken in order by running workgroups, so the
@@ -55,7 +60,6 @@ namespace {
 using namespace g2;
 
 constexpr int kFillRows = 32;  // rows per fill unit
-constexpr int kLag = 2;        // GEMM2 of minibatch u runs in step u + kLag
 constexpr int kCtr = 4;        // fill ticket, GEMM ticket, role ticket, abort flag
 
 struct RingArgs {
@@ -65,6 +69,7 @@ struct RingArgs {
   int d, I, E_local, R_cap, T_src, k;
   int mb, nslot, cpm, nmt, ntn1, ntn2, M_max;
   int comm_wgs;
+  int lag;             // GEMM2 of minibatch u runs in step u + lag (>= 1)
   char* ring;
   int64_t slot_bytes;
   int32_t* ctr;        // [kCtr + 2 * M_max]: tickets, abort, x_ready[], g1_done[]
@@ -225,7 +230,7 @@ __device__ void gemm_role(const RingArgs& a, int M, const int* s_mbp, int* s_val
   int32_t* x_ready = a.ctr + kCtr;
   int32_t* g1_done = x_ready + a.M_max;
   const int n1 = a.nmt * a.ntn1, n2 = a.nmt * a.ntn2;
-  const int total = (M + kLag) * (n1 + n2);
+  const int total = (M + a.lag) * (n1 + n2);
   for (;;) {
     __syncthreads();  // the previous unit is done with LDS and the broadcast slots
     const int t = wg_ticket(a.ctr + 1, s_val);
@@ -268,7 +273,7 @@ __device__ void gemm_role(const RingArgs& a, int M, const int* s_mbp, int* s_val
       }
       wg_publish(g1_done + m);
     } else {
-      const int m = u - kLag;
+      const int m = u - a.lag;
       if (m < 0) continue;
       o -= n1;
       const int mt = o / a.ntn2, nt = o % a.ntn2;
@@ -420,6 +425,10 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
   f2.ntn = a.ntn2;
   f2.T_src = p.T_src;
   f2.k = p.k;
+  {
+    const int per_step = a.nmt * (a.ntn1 + a.ntn2);
+    a.lag = (gemm + per_step - 1) / per_step + 1;
+  }
   const int nctr = kCtr + 2 * a.M_max;
   hipLaunchKernelGGL(ring_init_kernel, dim3((nctr + 255) / 256), dim3(256), 0, stream, p.counters, nctr);
   trace_mark(tr, "ring_init", stream);

@@ -32,7 +32,7 @@ bool valid_cfg(const mok_config* c) {
 
 struct Ws {
   size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
-      r_row_src, r_dest_row, r_scratch, bx, wpart, total;
+      r_row_src, r_dest_row, r_scratch, bx, wpart, worder, total;
 };
 
 Ws ws_layout(const mok_config* c) {
@@ -85,6 +85,8 @@ Ws ws_layout(const mok_config* c) {
                                     : R * c->d * act_bytes(c->prec));
   w.wpart = b;
   b += align256(c->prec == MOK_BF16 ? wgrad_partial_bytes(c->R_cap, c->d, c->I) : 0);
+  w.worder = b;
+  b += align256((size_t)c->E_local * sizeof(int32_t));
   w.total = f > b ? f : b;
   return w;
 }
@@ -369,6 +371,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.r_scratch = wsb + wl.r_scratch;
   p.x_perm = wsb + wl.bx;
   p.wg_part = (float*)(wsb + wl.wpart);
+  p.wg_order = (int32_t*)(wsb + wl.worder);
   p.tr = cfg->trace;
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);

@@ -176,6 +176,8 @@ struct WgArgs {
   int64_t ldt;
   const int32_t* offsets;
   int lda, ldb, M, N, I, E_local, R_cap, mtn, ntn;
+  int spread;            // 1: whole experts, tiles spread over all XCDs, experts by `order`
+  const int32_t* order;  // [E_local] local experts by routed rows, descending (spread mode)
 };
 
 // Split-K of the weight gradients.  An expert's rows are cut into chunks of
@@ -185,6 +187,8 @@ struct WgArgs {
 // block, and wgrad_reduce adds the partials to dW in chunk order (a fixed
 // order: the result is run-to-run identical).
 constexpr int kWgChunk = 4096;
+// Tiles per expert from which the weight gradients run in spread mode.
+constexpr int kSpreadTiles = 128;
 
 // Wave 0 scans the per-expert chunk counts: s_cp[e] = chunks of the experts
 // before e, s_xp[e] = their chunks beyond the first (partial slots), s_tp[e]
@@ -201,7 +205,8 @@ __device__ __forceinline__ void wg_chunk_prefix(const int32_t* offsets, int E_lo
       int c = 0, t = 0;
       if (e < E_local) {
         const int lo = min(offsets[e], R_cap), hi = min(offsets[e + 1], R_cap);
-        c = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 0;
+        // an expert without rows keeps one empty chunk: its tiles write zeros
+        c = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 1;
         t = hi > lo ? (hi - lo + 63) / 64 : 0;
       }
       ch[q] = c;
@@ -310,21 +315,41 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   // expert spread over all XCDs while the tiles that share a chunk's operand
   // rows share an L2.  The grid holds a multiple of 8 chunk slots.
   const int per = a.mtn * a.ntn;
-  const int TC = s_cp[a.E_local < 256 ? a.E_local : 256];
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int q = xcd + 8 * (slot / per);
-  if (q >= TC) return;
-  const int tile = slot % per;
-  const int mt = tile / a.ntn, nt = tile % a.ntn;
-  int e = 0, hi = a.E_local - 1;
-  while (e < hi) {
-    const int mid = (e + hi + 1) >> 1;
-    if (s_cp[mid] <= q) e = mid; else hi = mid - 1;
+  int e, c, mt, nt;
+  if (a.spread) {
+    // Spread mode (an expert's tiles alone fill half the chip or more):
+    // whole experts, no split; expert order(j) owns workgroups [j per,
+    // (j+1) per), the most routed expert first so its long tiles start first;
+    // within an expert each XCD gets a contiguous range of tiles in grouped
+    // order, so tiles sharing operand panels share an L2.
+    const int j = blockIdx.x / per;
+    if (j >= a.E_local) return;
+    e = a.order[j];
+    c = 0;
+    grouped_order(xcd_tile(blockIdx.x % per, per), a.mtn, a.ntn, &mt, &nt);
+  } else {
+    // Chunks are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+    // b % 8) and a chunk's tiles stay on one XCD: chunks of a heavily routed
+    // expert spread over all XCDs while the tiles that share a chunk's
+    // operand rows share an L2.  The grid holds a multiple of 8 chunk slots.
+    const int TC = s_cp[a.E_local < 256 ? a.E_local : 256];
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int q = xcd + 8 * (slot / per);
+    if (q >= TC) return;
+    const int tile = slot % per;
+    mt = tile / a.ntn;
+    nt = tile % a.ntn;
+    e = 0;
+    int hi = a.E_local - 1;
+    while (e < hi) {
+      const int mid = (e + hi + 1) >> 1;
+      if (s_cp[mid] <= q) e = mid; else hi = mid - 1;
+    }
+    c = q - s_cp[e];
   }
-  const int c = q - s_cp[e];
   const int end = min(a.offsets[e + 1], a.R_cap);
   const int off = min(a.offsets[e], a.R_cap) + c * kWgChunk;
-  const int cnt = min(kWgChunk, end - off);
+  const int cnt = a.spread ? end - off : min(kWgChunk, end - off);
   const int m0 = mt * BM, n0 = nt * C::BN;
   MNMajor<BM, C::BK> la;
   la.ncols_left = a.M - m0;
@@ -423,6 +448,27 @@ size_t wgrad_partial_bytes(int R_cap, int d, int I) {
   return (size_t)(R_cap / kWgChunk) * 2 * (size_t)I * d * sizeof(float);
 }
 
+// Local experts by routed rows (clipped to R_cap), descending; equal counts
+// keep the lower id first.  One workgroup of 256 threads, thread e ranks
+// expert e against all others.
+__global__ __launch_bounds__(kThreads) void expert_order_kernel(const int32_t* offsets, int E_local,
+                                                                int R_cap, int32_t* order) {
+  __shared__ int s_cnt[kThreads];
+  const int e = threadIdx.x;
+  int c = -1;
+  if (e < E_local) c = min(offsets[e + 1], R_cap) - min(offsets[e], R_cap);
+  s_cnt[e] = c;
+  __syncthreads();
+  if (e < E_local) {
+    int rank = 0;
+    for (int f = 0; f < E_local; ++f) {
+      const int cf = s_cnt[f];
+      rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+    }
+    order[rank] = e;
+  }
+}
+
 mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream) {
   if (p.R_cap == 0) return MOK_OK;
   GatherTArgs g;
@@ -485,6 +531,7 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   // R_cap / kWgChunk + E_local of them, rounded up to a multiple of 8
   const int max_chunks = (p.R_cap / kWgChunk + p.E_local + 7) / 8 * 8;
   WgArgs w;
+  w.order = p.wg_order;
   w.part = p.wg_part;
   w.A = reinterpret_cast<const bf16_t*>(p.dab);
   w.B = nullptr;
@@ -502,11 +549,21 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.R_cap = p.R_cap;
   w.mtn = (w.M + BM - 1) / BM;
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
+  // Spread mode when one expert's tiles fill half the chip: no split-K.
+  const bool spread_gu = w.mtn * w.ntn >= kSpreadTiles, spread_d = (p.d + BM - 1) / BM *
+                             ((p.I + Default::BN - 1) / Default::BN) >= kSpreadTiles;
+  if (spread_gu || spread_d)
+    hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets, p.E_local,
+                       p.R_cap, p.wg_order);
+  w.spread = spread_gu;
+  hipLaunchKernelGGL((wgrad_g2<Default, 0>),
+                     dim3((unsigned)((spread_gu ? p.E_local : max_chunks) * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_gate_up", stream);
-  hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
-  trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
+  if (!spread_gu) {
+    hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+    trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
+  }
   w.A = reinterpret_cast<const bf16_t*>(p.dy);
   w.B = reinterpret_cast<const bf16_t*>(p.h);
   w.out0 = p.dw_down;
@@ -517,11 +574,15 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.N = p.I;
   w.mtn = (w.M + BM - 1) / BM;
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  hipLaunchKernelGGL((wgrad_g2<Default, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
+  w.spread = spread_d;
+  hipLaunchKernelGGL((wgrad_g2<Default, 1>),
+                     dim3((unsigned)((spread_d ? p.E_local : max_chunks) * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down", stream);
-  hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
-  trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
+  if (!spread_d) {
+    hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+    trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
+  }
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

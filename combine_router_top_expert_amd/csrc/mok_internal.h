@@ -109,6 +109,7 @@ struct BwdPlan {
   void* r_scratch;
   void* x_perm;     // bf16: [d, xt_ld] token rows gathered again, transposed, for the wgrad GEMM
   float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
+  int32_t* wg_order;  // [E_local] local experts by routed rows, descending
   mok_trace* tr;    // host-side trace, may be null
 };
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);

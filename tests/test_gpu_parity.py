@@ -360,6 +360,10 @@ BWD_CASES = {
     # about 6000 rows per expert: the weight gradients run split over 4096-row chunks
     "bf16_split_k": _small("C2", S=2, T_src=6000, d=128, E=4, k=2, I=128, own=[0],
                            local_experts=[0, 1, 2, 3]),
+    # 256 (gate/up) and 128 (down) weight-gradient tiles per expert: whole experts
+    # spread over all XCDs, most routed expert first
+    "bf16_spread": _small("C2", S=2, T_src=32, d=4096, E=4, k=2, I=2048, own=[0, 1],
+                          local_experts=[0, 1, 2]),
 }
 
 
@@ -371,6 +375,8 @@ def test_layer_bwd(name):
     L = _layer(c)
     dout_store = [synth.gen_dout(w, s) for s in range(w.S)]
     d_out = [to_device(a, w.prec, DEV) for a, _ in dout_store]
+    for t in (L.dw_gate, L.dw_up, L.dw_down, L.dw_router):
+        t.fill_(float("nan"))  # every element must be overwritten
     L.forward()
     L.backward(d_out)
     torch.cuda.synchronize()

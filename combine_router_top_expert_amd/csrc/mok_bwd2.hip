@@ -176,7 +176,6 @@ struct WgArgs {
   int64_t ldt;
   const int32_t* offsets;
   int lda, ldb, M, N, I, E_local, R_cap, mtn, ntn;
-  int spread;            // 1: whole experts, tiles spread over all XCDs, experts by `order`
   const int32_t* order;  // [E_local] local experts by routed rows, descending (spread mode)
 };
 
@@ -187,18 +186,18 @@ struct WgArgs {
 // block, and wgrad_reduce adds the partials to dW in chunk order (a fixed
 // order: the result is run-to-run identical).
 constexpr int kWgChunk = 4096;
-// Tiles per expert from which the weight gradients run in spread mode.
-constexpr int kSpreadTiles = 128;
+// Tiles per expert from which the weight gradients may run in spread mode.
+constexpr int kSpreadTiles = 32;
 
 // Wave 0 scans the per-expert chunk counts: s_cp[e] = chunks of the experts
 // before e, s_xp[e] = their chunks beyond the first (partial slots), s_tp[e]
 // = their 64-row tiles (the expert's first column in the transposed token
 // rows is 64 s_tp[e]); index 256 holds the totals.
 __device__ __forceinline__ void wg_chunk_prefix(const int32_t* offsets, int E_local, int R_cap,
-                                                int* s_cp, int* s_xp, int* s_tp) {
+                                                int* s_cp, int* s_xp, int* s_tp, int* s_rows) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int ch[4], tl[4], run_c = 0, run_x = 0, run_t = 0;
+    int ch[4], tl[4], run_c = 0, run_x = 0, run_t = 0, rmax = 0, rtot = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
@@ -208,6 +207,8 @@ __device__ __forceinline__ void wg_chunk_prefix(const int32_t* offsets, int E_lo
         // an expert without rows keeps one empty chunk: its tiles write zeros
         c = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 1;
         t = hi > lo ? (hi - lo + 63) / 64 : 0;
+        rmax = max(rmax, hi - lo);
+        rtot += hi - lo;
       }
       ch[q] = c;
       tl[q] = t;
@@ -241,8 +242,29 @@ __device__ __forceinline__ void wg_chunk_prefix(const int32_t* offsets, int E_lo
       s_xp[256] = inc_x;
       s_tp[256] = inc_t;
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      rmax = max(rmax, __shfl_xor(rmax, off, 64));
+      rtot += __shfl_xor(rtot, off, 64);
+    }
+    if (lane == 0) {
+      s_rows[0] = rmax;
+      s_rows[1] = rtot;
+    }
   }
   __syncthreads();
+}
+
+// Spread mode (whole experts, no split-K, tiles of every expert over all
+// XCDs, most routed expert first) when an expert's output tiles fill an
+// eighth of the chip and no expert's single tile -- the whole expert's rows
+// -- is longer than a CU's average share of the work (rows_max <= per * R /
+// 256, so the longest-first order keeps the CUs balanced); otherwise the
+// experts are cut into kWgChunk-row chunks whose partial sums are added in
+// chunk order.  Decided on the device, identically by every workgroup of
+// both kernels, from the routed counts.
+__device__ __forceinline__ bool wg_spread(int per, const int* s_rows) {
+  return per >= kSpreadTiles && (int64_t)s_rows[0] * 256 <= (int64_t)per * s_rows[1];
 }
 
 // Token rows of the local experts gathered again for the gate/up weight
@@ -308,20 +330,16 @@ __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
 template <class C, int MODE>
 __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  __shared__ int s_cp[257], s_xp[257], s_tp[257];
-  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp);
-  // Chunks are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
-  // b % 8) and a chunk's tiles stay on one XCD: chunks of a heavily routed
-  // expert spread over all XCDs while the tiles that share a chunk's operand
-  // rows share an L2.  The grid holds a multiple of 8 chunk slots.
+  __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2];
+  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp, s_rows);
   const int per = a.mtn * a.ntn;
+  const bool spread = wg_spread(per, s_rows);
   int e, c, mt, nt;
-  if (a.spread) {
-    // Spread mode (an expert's tiles alone fill half the chip or more):
-    // whole experts, no split; expert order(j) owns workgroups [j per,
-    // (j+1) per), the most routed expert first so its long tiles start first;
-    // within an expert each XCD gets a contiguous range of tiles in grouped
-    // order, so tiles sharing operand panels share an L2.
+  if (spread) {
+    // Spread mode: expert order(j) owns workgroups [j per, (j+1) per), the
+    // most routed expert first so its long tiles start first; within an
+    // expert each XCD gets a contiguous range of tiles in grouped order, so
+    // tiles sharing operand panels share an L2.
     const int j = blockIdx.x / per;
     if (j >= a.E_local) return;
     e = a.order[j];
@@ -349,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
   }
   const int end = min(a.offsets[e + 1], a.R_cap);
   const int off = min(a.offsets[e], a.R_cap) + c * kWgChunk;
-  const int cnt = a.spread ? end - off : min(kWgChunk, end - off);
+  const int cnt = spread ? end - off : min(kWgChunk, end - off);
   const int m0 = mt * BM, n0 = nt * C::BN;
   MNMajor<BM, C::BK> la;
   la.ncols_left = a.M - m0;
@@ -412,12 +430,13 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
 // (blocks per expert, E_local), experts with one chunk return at once.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void wgrad_reduce(WgArgs a) {
-  __shared__ int s_cp[257], s_xp[257], s_tp[257];
+  __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2];
   const int e = blockIdx.y;
   const int lo = min(a.offsets[e], a.R_cap), hi = min(a.offsets[e + 1], a.R_cap);
   const int ch = hi > lo ? (hi - lo + kWgChunk - 1) / kWgChunk : 0;
   if (ch <= 1) return;
-  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp);
+  wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp, s_rows);
+  if (wg_spread(a.mtn * a.ntn, s_rows)) return;  // no partial sums were written
   const int xp = s_xp[e];
   const int n4 = a.N / 4;
   const size_t units = (size_t)a.M * n4;
@@ -549,21 +568,15 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.R_cap = p.R_cap;
   w.mtn = (w.M + BM - 1) / BM;
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  // Spread mode when one expert's tiles fill half the chip: no split-K.
-  const bool spread_gu = w.mtn * w.ntn >= kSpreadTiles, spread_d = (p.d + BM - 1) / BM *
-                             ((p.I + Default::BN - 1) / Default::BN) >= kSpreadTiles;
-  if (spread_gu || spread_d)
-    hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets, p.E_local,
-                       p.R_cap, p.wg_order);
-  w.spread = spread_gu;
-  hipLaunchKernelGGL((wgrad_g2<Default, 0>),
-                     dim3((unsigned)((spread_gu ? p.E_local : max_chunks) * w.mtn * w.ntn)),
+  // The grid covers both schedules (max_chunks >= E_local); the kernels pick
+  // one from the routed counts (wg_spread) and surplus workgroups return.
+  hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets, p.E_local,
+                     p.R_cap, p.wg_order);
+  hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_gate_up", stream);
-  if (!spread_gu) {
-    hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
-    trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
-  }
+  hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+  trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
   w.A = reinterpret_cast<const bf16_t*>(p.dy);
   w.B = reinterpret_cast<const bf16_t*>(p.h);
   w.out0 = p.dw_down;
@@ -574,15 +587,11 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.N = p.I;
   w.mtn = (w.M + BM - 1) / BM;
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  w.spread = spread_d;
-  hipLaunchKernelGGL((wgrad_g2<Default, 1>),
-                     dim3((unsigned)((spread_d ? p.E_local : max_chunks) * w.mtn * w.ntn)),
+  hipLaunchKernelGGL((wgrad_g2<Default, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down", stream);
-  if (!spread_d) {
-    hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
-    trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
-  }
+  hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+  trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

@@ -67,36 +67,49 @@ __global__ __launch_bounds__(64) void layout_count(LayoutArgs a) {
     a.chunk_base[(int64_t)blockIdx.x * a.E_local + e] = hist[e];
 }
 
+// Exclusive scan of the per-chunk counts of every local expert (over chunks,
+// then over experts).  The 256 threads split each expert's column of chunk
+// counts into segments: tpe = 256 / E_local threads per expert, each summing
+// a contiguous run of chunks; the segment sums are scanned in LDS, and every
+// thread then writes the global starting rows of its chunks.
 __global__ __launch_bounds__(256) void layout_scan(LayoutArgs a) {
-  __shared__ int tot[256];
+  __shared__ int part[256];
   __shared__ int off[257];
   const int tid = threadIdx.x;
-  if (tid < a.E_local) {
-    int run = 0;
-    for (int c = 0; c < a.nchunk; ++c) {
-      int64_t i = (int64_t)c * a.E_local + tid;
-      int v = a.chunk_base[i];
-      a.chunk_base[i] = run;
-      run += v;
-    }
-    tot[tid] = run;
-  }
+  const int tpe = 256 / a.E_local;  // E_local <= 256
+  const int e = tid / tpe, sub = tid % tpe;
+  const bool act = e < a.E_local;
+  const int L = (a.nchunk + tpe - 1) / tpe;
+  const int c0 = sub * L, c1 = min(a.nchunk, c0 + L);
+  int sum = 0;
+  if (act)
+    for (int c = c0; c < c1; ++c) sum += a.chunk_base[(int64_t)c * a.E_local + e];
+  part[tid] = sum;
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int e = 0; e < a.E_local; ++e) {
-      off[e] = run;
-      run += tot[e];
+    for (int x = 0; x < a.E_local; ++x) {
+      off[x] = run;
+      for (int q = 0; q < tpe; ++q) run += part[x * tpe + q];
     }
     off[a.E_local] = run;
     if (run > a.R_cap) latch(a.status, MOK_ECAPACITY);
   }
   __syncthreads();
-  if (tid < a.E_local) {
-    a.counts[tid] = tot[tid];
-    for (int c = 0; c < a.nchunk; ++c) a.chunk_base[(int64_t)c * a.E_local + tid] += off[tid];
+  if (act) {
+    int run = off[e];
+    for (int q = 0; q < sub; ++q) run += part[e * tpe + q];
+    for (int c = c0; c < c1; ++c) {
+      const int64_t i = (int64_t)c * a.E_local + e;
+      const int v = a.chunk_base[i];
+      a.chunk_base[i] = run;
+      run += v;
+    }
+    if (sub == 0) {
+      a.counts[e] = off[e + 1] - off[e];
+      a.offsets[e] = off[e];
+    }
   }
-  if (tid < a.E_local) a.offsets[tid] = off[tid];
   if (tid == 0) a.offsets[a.E_local] = off[a.E_local];
 }
 

@@ -160,20 +160,46 @@ __device__ __forceinline__ GTile minibatch(const RingArgs& a, const int* s_mbp, 
 }
 
 // ---------------------------------------------------------------- dispatch side
+// Rows [q0, q0 + nr) of minibatch mbt into its slot.  The rows' source
+// addresses are looked up once into LDS; then every thread issues kBatch
+// independent 16-byte loads before their stores, so a fill costs about one
+// memory round trip per kBatch units instead of two dependent ones per unit.
+// nr is uniform over the workgroup (it holds a barrier).
+constexpr int kBatch = 8;
+
 template <bool MX>
 __device__ void fill_rows(const RingArgs& a, char* slot, const GTile& mbt, int q0, int nr) {
+  __shared__ const bf16_t* s_src[kFillRows];
+  if ((int)threadIdx.x < nr) {
+    const int tok = a.row_src[mbt.r0 + q0 + threadIdx.x] / a.k;
+    s_src[threadIdx.x] = reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
+                         (size_t)(tok % a.T_src) * a.d;
+  }
+  __syncthreads();
   const int upr = a.d / 8;  // 16-byte units (8 bf16) per row
   const int total = nr * upr;
+  if constexpr (!MX) {
+    for (int u0 = threadIdx.x; u0 < total; u0 += kThreads * kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int u = u0 + b * kThreads;
+        if (u < total) v[b] = ld16(s_src[u / upr] + (u % upr) * 8);
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int u = u0 + b * kThreads;
+        if (u < total)
+          st16(reinterpret_cast<bf16_t*>(slot) + (size_t)(q0 + u / upr) * a.d + (u % upr) * 8, v[b]);
+      }
+    }
+    return;
+  }
   for (int u = threadIdx.x; u < total; u += kThreads) {
     const int row = u / upr, c = u % upr;
     const int q = q0 + row;  // row within the minibatch
-    const int tok = a.row_src[mbt.r0 + q] / a.k;
-    const bf16_t* src = reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
-                        (size_t)(tok % a.T_src) * a.d;
-    const uint4 v = ld16(src + c * 8);
-    if constexpr (!MX) {
-      st16(reinterpret_cast<bf16_t*>(slot) + (size_t)q * a.d + c * 8, v);
-    } else {
+    const uint4 v = ld16(s_src[row] + c * 8);
+    {
       // a 32-element MX block is 4 consecutive units (4 lanes); upr % 4 == 0
       // and kThreads % 4 == 0, so a lane group is all in or all out of the loop
       float f[8];

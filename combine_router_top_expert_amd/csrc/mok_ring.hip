@@ -195,13 +195,24 @@ __device__ void fill_rows(const RingArgs& a, char* slot, const GTile& mbt, int q
     }
     return;
   }
-  for (int u = threadIdx.x; u < total; u += kThreads) {
+  for (int u0 = threadIdx.x; u0 < total; u0 += kThreads * kBatch) {
+    // a 32-element MX block is 4 consecutive units (4 lanes); upr % 4 == 0
+    // and kThreads % 4 == 0, so a lane group is all in or all out of a batch
+    // entry, and the lanes of a group take part in the same shuffles
+    uint4 vb[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int u = u0 + b * kThreads;
+      if (u < total) vb[b] = ld16(s_src[u / upr] + (u % upr) * 8);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+    const int u = u0 + b * kThreads;
+    if (u >= total) break;
     const int row = u / upr, c = u % upr;
     const int q = q0 + row;  // row within the minibatch
-    const uint4 v = ld16(s_src[row] + c * 8);
+    const uint4 v = vb[b];
     {
-      // a 32-element MX block is 4 consecutive units (4 lanes); upr % 4 == 0
-      // and kThreads % 4 == 0, so a lane group is all in or all out of the loop
       float f[8];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -228,6 +239,7 @@ __device__ void fill_rows(const RingArgs& a, char* slot, const GTile& mbt, int q
           scales[c >> 2] = (uint8_t)(sh + 127);
         }
       }
+    }
     }
   }
 }

@@ -31,7 +31,7 @@ struct DhArgs {
 };
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void dh_g2(DhArgs a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
   const int total_m = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix);
@@ -61,6 +61,7 @@ __global__ __launch_bounds__(kThreads) void dh_g2(DhArgs a) {
   // stall on its a | b loads at the same time while the matrix cores idle).
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
+  static_assert(WaveStage<C, bf16_t>::PASSES == 1, "one staging pass");
   st.put(acc, 0);
   wave_lds_fence();
   const int wave = threadIdx.x >> 6;
@@ -119,7 +120,7 @@ struct DxArgs {
 };
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void dx_g2(DxArgs a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
   const int total_m = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix);
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void dx_g2(DxArgs a) {
   stage_rows(s_rows, a.row_src, g);
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
+  static_assert(WaveStage<C, bf16_t>::PASSES == 1, "one staging pass");
   st.put(acc, 0);
   wave_lds_fence();
   const int wave = threadIdx.x >> 6;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
 }
 
 template <class C, int MODE>
-__global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2];
   wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp, s_rows);
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_g2(WgArgs a) {
     // B = the chunk's token rows from the transposed copy: row n of the tile
     // is column n0 + n of d, k-contiguous from the chunk's first column; the
     // last stage runs into the expert's zero padding
-    static_assert(C::BK == 64, "the transposed rows are padded to 64");
+    static_assert(64 % C::BK == 0, "the transposed rows are padded to 64");
     KMajor<C::BN, C::BK> lb;
     const bf16_t* Bt = a.BT + (size_t)64 * s_tp[e] + (size_t)c * kWgChunk;
     lb.init([&](int nr) -> const bf16_t* {
@@ -586,8 +588,8 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.M = p.d;
   w.N = p.I;
   w.mtn = (w.M + BM - 1) / BM;
-  w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  hipLaunchKernelGGL((wgrad_g2<Default, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
+  w.ntn = (w.N + Narrow::BN - 1) / Narrow::BN;
+  hipLaunchKernelGGL((wgrad_g2<Narrow, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down", stream);
   hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);

@@ -32,7 +32,7 @@ __device__ __forceinline__ bool launch_tile(const int32_t* offsets, int E_local,
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void ffn1_g2(F1Args a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void ffn1_g2(F1Args a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
   GTile g;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void ffn1_g2(F1Args a) {
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void ffn2_g2(F2Args a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void ffn2_g2(F2Args a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
   GTile g;

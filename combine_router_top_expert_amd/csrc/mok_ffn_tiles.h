@@ -140,6 +140,7 @@ __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GT
   if (a.push) stage_rows(s_rows, a.row_src, g);
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
+  static_assert(WaveStage<C, bf16_t>::PASSES == 1, "one staging pass");
   st.put(acc, 0);
   wave_lds_fence();
   const int wave = threadIdx.x >> 6;

@@ -178,10 +178,11 @@ struct MNMajor {
 
 // ---------------------------------------------------------------- tile config
 // BM = 256 rows x BN columns per workgroup (4 waves, 2 x 2, each 128 x BN/2),
-// BK-wide k stages, NS stages in the LDS ring.
-template <int BN_, int BK_, int NS_>
+// BK-wide k stages, NS stages in the LDS ring, OCC workgroups resident per CU
+// (the kernels ask the compiler for a register budget that allows OCC).
+template <int BN_, int BK_, int NS_, int OCC_ = 1>
 struct Cfg {
-  static constexpr int BN = BN_, BK = BK_, NS = NS_;
+  static constexpr int BN = BN_, BK = BK_, NS = NS_, OCC = OCC_;
   static constexpr int WNB = BN / 64;  // 32-column MFMA blocks per wave
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
@@ -189,12 +190,20 @@ struct Cfg {
   static constexpr int SMEM = NS * STAGE;
   static constexpr int LOADS = STAGE / 1024 / 4;  // per wave per stage
   static_assert(NS >= 2 && NS <= 8 && (NS - 1) * LOADS < 64, "vmcnt range");
+  static_assert(OCC * (SMEM + 4096) <= 160 * 1024, "LDS of OCC workgroups per CU");
 };
 
-// The default configuration of the expert GEMMs.  (A four-deep ring of 32-k
-// stages measured about 2 % slower on the layer's GEMMs: operand latency is
-// not what bounds them.)
+// The default configuration of the expert GEMMs: 256 x 256 tiles, two 64-k
+// stages, one workgroup per CU.  (A four-deep ring of 32-k stages measured
+// about 2 % slower on the layer's GEMMs: operand latency is not what bounds
+// them.)
 typedef Cfg<256, 64, 2> Default;
+// 256 x 128 tiles, three 32-k stages (72 KiB of LDS), two workgroups per CU:
+// while one workgroup stores its tile or waits at a stage barrier, the other
+// keeps the CU's matrix cores busy.  It pays only where both operands are
+// MN-major (the down-projection weight gradient); with a K-major operand the
+// extra operand traffic of the narrower tile costs more than it hides.
+typedef Cfg<128, 32, 3, 2> Narrow;
 
 template <class C>
 struct Acc {
@@ -392,7 +401,8 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
 
 // ---------------------------------------------------------------- epilogue staging
 // After the main loop every wave copies its 128 x BN/2 accumulator tile (as T =
-// float or bf16) into a private 32 KiB LDS region, then walks it row by row:
+// float or bf16) into a private LDS region (a quarter of the operand ring, at
+// most 32 KiB), then walks it row by row:
 // each lane takes one 16-byte chunk of a row, so the global stores (and the
 // loads of an epilogue's extra operands) of a wave instruction cover whole
 // rows instead of one 8-byte piece of 32 different rows.  Rows of a region
@@ -405,12 +415,14 @@ struct WaveStage {
   static constexpr int PITCH = WCOLS * (int)sizeof(T);       // bytes per row
   static constexpr int CPR = PITCH / 16;                      // chunks per row
   static constexpr int EPC = 16 / (int)sizeof(T);             // elements per chunk
-  static constexpr int ROWS = 32768 / PITCH < 128 ? 32768 / PITCH : 128;  // rows per pass
+  static constexpr int REGION = C::SMEM >= 4 * 32768 ? 32768 : C::SMEM >= 4 * 16384 ? 16384 : 8192;
+  static constexpr int ROWS = REGION / PITCH < 128 ? REGION / PITCH : 128;  // rows per pass
   static constexpr int PASSES = 128 / ROWS;
   static constexpr int SW = CPR < 32 ? CPR : 32;              // swizzle period
-  static_assert(C::SMEM >= 4 * 32768, "the four waves' staging regions reuse the operand ring");
+  static_assert(C::SMEM >= 4 * REGION, "the four waves' staging regions reuse the operand ring");
+  static_assert(ROWS >= 32 && 128 % ROWS == 0, "whole 32-row blocks per pass");
   char* base;
-  __device__ __forceinline__ explicit WaveStage(char* smem) : base(smem + (threadIdx.x >> 6) * 32768) {}
+  __device__ __forceinline__ explicit WaveStage(char* smem) : base(smem + (threadIdx.x >> 6) * REGION) {}
   __device__ __forceinline__ char* chunk_addr(int row, int c) const {
     return base + row * PITCH + ((c ^ (row % SW)) * 16);
   }

@@ -236,6 +236,9 @@ def main():
     ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
     ap.add_argument("--comm-wgs", type=int, default=0, help="ring path: dispatch workgroups")
     ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
+    ap.add_argument("--tune", action="store_true",
+                    help="ring path: choose minibatch rows and dispatch workgroups with "
+                         "mok_tune_fwd before the timed steps (untimed)")
     ap.add_argument("--mb-sweep", default="",
                     help="ring path: comma-separated minibatch sizes, one JSON line each")
     ap.add_argument("--hbm-copy-gib", type=float, default=0.0,
@@ -304,10 +307,21 @@ def main():
         return L
 
     mbs = [int(v) for v in args.mb_sweep.split(",")] if args.mb_sweep else [args.mb]
+    if args.tune and (not args.ring_mib or args.mb_sweep):
+        sys.exit("--tune needs --ring-mib and no --mb-sweep")
     results = []
     for mb in mbs:
         L = make_layer(mb)
+        tuned = None
+        if args.tune:
+            table = L.tune()
+            log("tuner (minibatch rows, dispatch workgroups) -> ms per forward:",
+                {f"{m}/{c}": (round(v, 3) if v is not None else None) for (m, c), v in table.items()})
+            mb, args.comm_wgs = L.cfg.minibatch_rows, L.cfg.comm_wgs
+            tuned = {f"{m}/{c}": v for (m, c), v in table.items()}
         results.append(measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace))
+        if tuned is not None:
+            results[-1]["config"]["tuner_ms_per_forward"] = tuned
         del L
         torch.cuda.empty_cache()
     result = results[-1]

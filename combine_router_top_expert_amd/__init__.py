@@ -27,7 +27,8 @@ STATUS = {
 
 # every symbol include/mok.h declares
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
-           "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_version")
+           "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
+           "mok_version")
 
 
 class MokError(RuntimeError):
@@ -169,6 +170,9 @@ def lib():
         L.mok_layer_bwd.argtypes = [cfgp, I32, I32, P, P, P, P, ctypes.POINTER(mok_expert_weights),
                                     ctypes.POINTER(mok_fwd_state), P, P, P, P, P, P, P, P, P, P, P]
         L.mok_mx_quantize.argtypes = [I64, I64, P, P, P, P]
+        L.mok_tune_fwd.argtypes = [cfgp, P, I32, P, I32, I32, ctypes.c_size_t, I32, I32, P, P, P, P,
+                                   ctypes.POINTER(mok_expert_weights),
+                                   ctypes.POINTER(mok_fwd_state), P, P, P, P, P, cfgp, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -284,6 +288,34 @@ def mok_layer_bwd(cfg, own_lo, own_n, d_out, src_x, w_router, expert_to_local,
         _ptr(expert_to_local), ctypes.byref(weights), ctypes.byref(state), _table(staging),
         _ptr(d_gate), _table(dx_stage), _table(d_x) if d_x is not None else None, _ptr(dw_gate),
         _ptr(dw_up), _ptr(dw_down), _ptr(dw_router), _ptr(ws), _ptr(dev_status), _stream(stream)))
+
+
+def mok_tune_fwd(cfg, mbs, comms, reps, ws_bytes, own_lo, own_n, src_x, w_router, bias,
+                 expert_to_local, weights: mok_expert_weights, state: mok_fwd_state, staging, out,
+                 ws, dev_status, stream=None):
+    """Returns (best mok_config, {(minibatch_rows, comm_wgs): mean ms or None if skipped})."""
+    mbs = list(mbs) if mbs is not None else [64, 128, 256, 512]
+    if comms is None:
+        import torch
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        comms = [max(cus * q // 16, 1) for q in (1, 2, 3, 4)]
+    comms = list(comms)
+    mb_arr = (ctypes.c_int32 * len(mbs))(*mbs)
+    cm_arr = (ctypes.c_int32 * len(comms))(*comms)
+    times = (ctypes.c_float * (len(mbs) * len(comms)))()
+    best = mok_config()
+    _check("mok_tune_fwd", lib().mok_tune_fwd(
+        ctypes.byref(cfg), ctypes.cast(mb_arr, ctypes.c_void_p), len(mbs),
+        ctypes.cast(cm_arr, ctypes.c_void_p), len(comms), reps, ws_bytes, own_lo, own_n,
+        _table(src_x), _ptr(w_router), _ptr(bias), _ptr(expert_to_local), ctypes.byref(weights),
+        ctypes.byref(state), _table(staging), _table(out) if out is not None else None, _ptr(ws),
+        _ptr(dev_status), _stream(stream), ctypes.byref(best), ctypes.cast(times, ctypes.c_void_p)))
+    table = {}
+    for i, mb in enumerate(mbs):
+        for j, c in enumerate(comms):
+            v = times[i * len(comms) + j]
+            table[(mb, c)] = float(v) if v >= 0 else None
+    return best, table
 
 
 def mok_mx_quantize(rows, K, src, codes, scales, stream=None):

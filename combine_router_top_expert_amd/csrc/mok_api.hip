@@ -8,6 +8,8 @@ using namespace mok;
 
 namespace {
 
+constexpr int kTuneMax = 64;  // candidates per tuned parameter
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t act_bytes(int prec) { return prec == MOK_F32 ? 4 : 2; }
@@ -375,6 +377,91 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.tr = cfg->trace;
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);
+}
+
+mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
+                        const int32_t* comms, int32_t n_comm, int32_t reps, size_t ws_bytes,
+                        int32_t own_lo, int32_t own_n, const void* const* src_x,
+                        const void* w_router, const float* bias, const int32_t* expert_to_local,
+                        const mok_expert_weights* w, const mok_fwd_state* st,
+                        void* const* staging, void* const* out, void* ws, int32_t* dev_status,
+                        void* stream, mok_config* best, float* times_ms) {
+  if (!valid_cfg(cfg) || !best || !dev_status || cfg->ring_bytes <= 0 || cfg->R_cap <= 0)
+    return MOK_EINVAL;
+  if (reps < 1 || reps > 1000) return MOK_EINVAL;
+  if ((mbs && (n_mb < 1 || n_mb > kTuneMax)) || (comms && (n_comm < 1 || n_comm > kTuneMax)))
+    return MOK_EINVAL;
+  const int cus = device_cus();
+  if (cus <= 0) return MOK_EDEVICE;
+  // default grid: the minibatch sizes of the 256-expert share's sweep and
+  // dispatch sides of 1/16 .. 1/4 of the CUs
+  const int32_t mb_def[4] = {64, 128, 256, 512};
+  const int32_t comm_def[4] = {cus / 16 > 0 ? cus / 16 : 1, cus / 8 > 0 ? cus / 8 : 1,
+                               3 * cus / 16 > 0 ? 3 * cus / 16 : 1, cus / 4 > 0 ? cus / 4 : 1};
+  if (!mbs) {
+    mbs = mb_def;
+    n_mb = 4;
+  }
+  if (!comms) {
+    comms = comm_def;
+    n_comm = 4;
+  }
+  hipStream_t sm = (hipStream_t)stream;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
+    if (ev[0]) hipEventDestroy(ev[0]);
+    return MOK_EDEVICE;
+  }
+  mok_status result = MOK_EINVAL;  // until one candidate ran
+  float best_ms = 0.0f;
+  for (int i = 0; i < n_mb; ++i)
+    for (int j = 0; j < n_comm; ++j) {
+      const int idx = i * n_comm + j;
+      if (times_ms) times_ms[idx] = -1.0f;
+      mok_config c = *cfg;
+      c.minibatch_rows = mbs[i];
+      c.comm_wgs = comms[j];
+      c.gemm_wgs = 0;
+      c.trace = nullptr;
+      // a candidate the ring cannot take (no slot of that minibatch, a
+      // split beyond the CUs) or whose counters outgrow ws is skipped
+      if (c.minibatch_rows < 1 || c.comm_wgs < 1 || mok_workspace_bytes(&c) > ws_bytes ||
+          ring_check(c.prec, c.d, c.I, c.minibatch_rows, c.ring_bytes, c.comm_wgs, c.gemm_wgs,
+                     nullptr, nullptr) != MOK_OK)
+        continue;
+      mok_status rc = MOK_OK;
+      for (int r = 0; r <= reps && rc == MOK_OK; ++r) {  // call 0 warms up
+        if (r == 1 && hipEventRecord(ev[0], sm) != hipSuccess) rc = MOK_EDEVICE;
+        if (rc == MOK_OK)
+          rc = mok_layer_fwd(&c, own_lo, own_n, src_x, w_router, bias, expert_to_local, w, st,
+                             staging, out, ws, dev_status, stream);
+      }
+      int32_t h_status = 0;
+      if (rc == MOK_OK && (hipEventRecord(ev[1], sm) != hipSuccess ||
+                           hipMemcpyAsync(&h_status, dev_status, sizeof(int32_t),
+                                          hipMemcpyDeviceToHost, sm) != hipSuccess ||
+                           hipStreamSynchronize(sm) != hipSuccess))
+        rc = MOK_EDEVICE;
+      if (rc == MOK_OK && h_status != 0) rc = (mok_status)h_status;
+      float ms = 0.0f;
+      if (rc == MOK_OK && hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) rc = MOK_EDEVICE;
+      if (rc != MOK_OK) {
+        result = rc;
+        goto done;
+      }
+      ms /= (float)reps;
+      if (times_ms) times_ms[idx] = ms;
+      if (result != MOK_OK || ms < best_ms) {
+        best_ms = ms;
+        *best = c;
+        best->trace = cfg->trace;
+        result = MOK_OK;
+      }
+    }
+done:
+  hipEventDestroy(ev[0]);
+  hipEventDestroy(ev[1]);
+  return result;
 }
 
 mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,

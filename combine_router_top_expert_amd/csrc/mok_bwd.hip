@@ -228,62 +228,82 @@ __global__ __launch_bounds__(kGemmThreads) void wgrad_kernel(BwdPlan p, int mtn,
 }
 
 // ------------------------------------------------------------------ 5. d_x
+// Two own tokens per workgroup.  Lanes 16q + j of wave 0 read slot j of
+// token q in parallel and each group forms its token's dz in the order
+// written out -- m = sum_j g_j dg_j by fma in slot order (the slot values
+// gathered with lane shuffles), dz_j = g_j (dg_j - m) -- for the whole
+// workgroup through LDS.
+constexpr int kDxTokPerBlock = 2;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
-  __shared__ float s_dz[16];
-  __shared__ int s_e[16];
-  __shared__ int s_loc[16];
-  const int64_t gt = blockIdx.x;  // own token index
-  const int s = p.own_lo + (int)(gt / p.T_src);
-  const int t = (int)(gt % p.T_src);
-  const int64_t n0 = ((int64_t)s * p.T_src + t) * p.k;
-  if (threadIdx.x == 0) {
-    float dg[16];
-    float m = 0.0f;
-    for (int j = 0; j < p.k; ++j) {
+  __shared__ float s_dz[kDxTokPerBlock][16];
+  __shared__ int s_e[kDxTokPerBlock][16];
+  __shared__ int s_loc[kDxTokPerBlock][16];
+  const int64_t n_tok = (int64_t)p.own_n * p.T_src;
+  const int64_t g0 = (int64_t)blockIdx.x * kDxTokPerBlock;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, q = lane >> 4, j = lane & 15;
+    const int64_t gt = g0 + q;
+    const bool valid = q < kDxTokPerBlock && gt < n_tok && j < p.k;
+    float g = 0.0f, dg = 0.0f;
+    int e = 0, loc = 0;
+    if (valid) {
+      const int s = p.own_lo + (int)(gt / p.T_src);
+      const int t = (int)(gt % p.T_src);
+      const int64_t n = ((int64_t)s * p.T_src + t) * p.k + j;
       // present: a local row, or a remote slot whose gate gradient and dx row
       // the GPU holding that expert wrote here; absent: dropped beyond R_cap
-      const int row = p.dest_row[n0 + j];
-      const bool present = row < p.R_cap;
-      dg[j] = present ? p.d_gate[n0 + j] : 0.0f;
-      m = __builtin_fmaf(p.topk_gate[n0 + j], dg[j], m);
-      s_loc[j] = present;
-      s_e[j] = p.topk_idx[n0 + j];
+      loc = p.dest_row[n] < p.R_cap;
+      dg = loc ? p.d_gate[n] : 0.0f;
+      g = p.topk_gate[n];
+      e = p.topk_idx[n];
     }
-    for (int j = 0; j < p.k; ++j) {
-      const float dz = p.topk_gate[n0 + j] * (dg[j] - m);
-      s_dz[j] = dz;
+    float m = 0.0f;
+    for (int i = 0; i < p.k; ++i)
+      m = __builtin_fmaf(__shfl(g, (lane & ~15) + i, 64), __shfl(dg, (lane & ~15) + i, 64), m);
+    if (valid) {
+      const float dz = g * (dg - m);
+      s_dz[q][j] = dz;
+      s_e[q][j] = e;
+      s_loc[q][j] = loc;
       p.dz[gt * p.k + j] = dz;
     }
   }
   __syncthreads();
-  const T* stg = reinterpret_cast<const T*>(p.dx_stage.p[s]) + (size_t)t * p.k * p.d;
-  const T* wr = reinterpret_cast<const T*>(p.w_router);
-  T* o = reinterpret_cast<T*>(p.d_x.p[s]) + (size_t)t * p.d;
   constexpr int U = 16 / sizeof(T);
-  for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
-    float acc[U];
+  const T* wr = reinterpret_cast<const T*>(p.w_router);
+  for (int q = 0; q < kDxTokPerBlock; ++q) {
+    const int64_t gt = g0 + q;
+    if (gt >= n_tok) return;
+    const int s = p.own_lo + (int)(gt / p.T_src);
+    const int t = (int)(gt % p.T_src);
+    const T* stg = reinterpret_cast<const T*>(p.dx_stage.p[s]) + (size_t)t * p.k * p.d;
+    T* o = reinterpret_cast<T*>(p.d_x.p[s]) + (size_t)t * p.d;
+    for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
+      float acc[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < p.k; ++j) {
-      if (!s_loc[j]) continue;
-      uint4 v = ld16(stg + (size_t)j * p.d + u * U);
-      const T* e = reinterpret_cast<const T*>(&v);
+      for (int i = 0; i < U; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < p.k; ++j) {
+        if (!s_loc[q][j]) continue;
+        uint4 v = ld16(stg + (size_t)j * p.d + u * U);
+        const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-      for (int i = 0; i < U; ++i) acc[i] += to_f32<T>(e[i]);
+        for (int i = 0; i < U; ++i) acc[i] += to_f32<T>(e[i]);
+      }
+      for (int j = 0; j < p.k; ++j) {
+        const float dz = s_dz[q][j];
+        uint4 v = ld16(wr + (size_t)s_e[q][j] * p.d + u * U);
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz, to_f32<T>(e[i]), acc[i]);
+      }
+      uint4 ov;
+      T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+      for (int i = 0; i < U; ++i) oe[i] = from_f32<T>(acc[i]);
+      st16(o + u * U, ov);
     }
-    for (int j = 0; j < p.k; ++j) {
-      const float dz = s_dz[j];
-      uint4 v = ld16(wr + (size_t)s_e[j] * p.d + u * U);
-      const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-      for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz, to_f32<T>(e[i]), acc[i]);
-    }
-    uint4 ov;
-    T* oe = reinterpret_cast<T*>(&ov);
-#pragma unroll
-    for (int i = 0; i < U; ++i) oe[i] = from_f32<T>(acc[i]);
-    st16(o + u * U, ov);
   }
 }
 
@@ -425,7 +445,8 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   }
   const int64_t n_own = (int64_t)p.own_n * p.T_src;
   if (n_own > 0) {
-    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)n_own), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)((n_own + kDxTokPerBlock - 1) / kDxTokPerBlock)),
+                       dim3(kThreads), 0, stream, p);
     trace_mark(p.tr, "bwd_dx_sum_router", stream);
   }
   if (p.dw_router) {

@@ -74,6 +74,8 @@ struct RingPlan {
   DstTable staging;
 };
 int64_t ring_slot_bytes(int prec, int d, int mb);
+// Compute units of the current device (0 if the runtime cannot tell).
+int device_cus();
 int ring_max_minibatches(int R_cap, int E_local, int mb);
 size_t ring_counter_bytes(int R_cap, int E_local, int mb);
 // Argument check of the ring path (also run by launch_ring_fwd); the auto

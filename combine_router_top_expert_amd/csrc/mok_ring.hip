@@ -344,14 +344,14 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(RingArgs a) {
     gemm_role<C, MX>(a, M, s_mbp, s_val, smem);
 }
 
+}  // namespace
+
 int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return n;
 }
-
-}  // namespace
 
 int64_t ring_slot_bytes(int prec, int d, int mb) {
   const int64_t b = prec == MOK_MXFP8 ? (int64_t)mb * d + (int64_t)mb * (d / 32) : (int64_t)mb * d * 2;

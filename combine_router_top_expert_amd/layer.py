@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import (MAX_SOURCES, make_config, make_state, make_weights, mok_layer_bwd, mok_layer_fwd,
-               mok_mx_quantize, mok_workspace_bytes, STATUS)
+               mok_mx_quantize, mok_tune_fwd, mok_workspace_bytes, STATUS)
 
 
 def _dt(prec: str):
@@ -125,6 +125,28 @@ class MoELayer:
         mok_layer_fwd(self.cfg, self.own_lo, self.own_n, self.xs, self.w_router, self.bias,
                       self.e2l, self.weights, self.state, self.staging, self.out, self.ws,
                       self.status, stream)
+
+    def tune(self, mbs=None, comms=None, reps=3, stream=None):
+        """Pick the fused path's minibatch size and dispatch/GEMM split with
+        mok_tune_fwd (off the timed path; synchronises).  The workspace grows
+        to fit every candidate first.  Returns {(minibatch_rows, comm_wgs):
+        ms per forward or None}; self.cfg holds the fastest pair after."""
+        mbs = list(mbs) if mbs is not None else [64, 128, 256, 512]
+        need = self.ws.numel()
+        for mb in mbs:
+            c = type(self.cfg).from_buffer_copy(self.cfg)
+            c.minibatch_rows = mb
+            need = max(need, mok_workspace_bytes(c))
+        if need > self.ws.numel():
+            self.ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        best, table = mok_tune_fwd(self.cfg, mbs, comms, reps, self.ws.numel(), self.own_lo,
+                                   self.own_n, self.xs, self.w_router, self.bias, self.e2l,
+                                   self.weights, self.state, self.staging, self.out, self.ws,
+                                   self.status, stream)
+        self.cfg.minibatch_rows = best.minibatch_rows
+        self.cfg.comm_wgs = best.comm_wgs
+        self.cfg.gemm_wgs = best.gemm_wgs
+        return table
 
     def backward(self, d_out: List[torch.Tensor], stream=None, router_grad=True):
         mok_layer_bwd(self.cfg, self.own_lo, self.own_n, d_out, self.xs, self.w_router, self.e2l,

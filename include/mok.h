@@ -26,7 +26,8 @@
  * Conventions for every entry point
  *   - Memory: the caller owns every buffer (device memory unless stated).
  *     The library allocates and frees nothing, keeps no global mutable state
- *     and never synchronises the host with the device.
+ *     and never synchronises the host with the device (except the tuner,
+ *     mok_tune_fwd, which runs off the timed path).
  *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and runs asynchronously.
  *   - Errors: invalid arguments are rejected before anything is enqueued with
@@ -242,6 +243,36 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          void* const* staging, float* d_gate, void* const* dx_stage,
                          void* const* d_x, float* dw_gate, float* dw_up, float* dw_down,
                          float* dw_router, void* ws, int32_t* dev_status, void* stream);
+
+/* Tuner of the fused path's minibatch size and workgroup split [K02: the
+ * split of SMs between the communication and compute sides is set directly,
+ * and the minibatch size trades a long wait for the first computation
+ * (too large) against too few GEMM tasks to keep the SMs busy (too small);
+ * K03: the right minibatch size and number of communication SMs change with
+ * the hidden size, top-k and expert size].  Off the
+ * timed path, and unlike every other entry point it synchronises the host
+ * with `stream`.  For each candidate (mbs[i], comms[j]) -- cfg with
+ * minibatch_rows = mbs[i], comm_wgs = comms[j], gemm_wgs = 0 (the remaining
+ * CUs) -- it runs mok_layer_fwd once to warm up and then `reps` times
+ * (1..1000) between two HIP events, with the arguments of mok_layer_fwd.
+ * mbs / comms: host arrays of 1..64 entries, or NULL for {64, 128, 256, 512}
+ * rows and {1/16, 1/8, 3/16, 1/4} of the CUs.  cfg->ring_bytes and
+ * cfg->R_cap must be > 0.  ws_bytes: size of ws; a candidate whose
+ * mok_workspace_bytes exceeds it, or that the ring cannot take (no slot of
+ * that many rows, a split beyond the CUs), is skipped.  Outputs:
+ * *best = cfg with the fastest candidate's two fields (host), times_ms
+ * [n_mb*n_comm] (host, row i*n_comm + j; NULL allowed) the mean milliseconds
+ * per call or -1 for a skipped candidate.  The forward outputs and state
+ * are those of one mok_layer_fwd call: they do not depend on the tunables.
+ * Returns MOK_EINVAL if no candidate could run; a status the device latched
+ * during a candidate (read back after it) is returned and tuning stops. */
+mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
+                        const int32_t* comms, int32_t n_comm, int32_t reps, size_t ws_bytes,
+                        int32_t own_lo, int32_t own_n, const void* const* src_x,
+                        const void* w_router, const float* bias, const int32_t* expert_to_local,
+                        const mok_expert_weights* w, const mok_fwd_state* st,
+                        void* const* staging, void* const* out, void* ws, int32_t* dev_status,
+                        void* stream, mok_config* best, float* times_ms);
 
 /* MX quantisation of rows of bf16 values (weight preparation off the timed
  * path, and the same codec as the fused activation paths):  src [rows, K]

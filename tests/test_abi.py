@@ -92,3 +92,27 @@ def test_ring_workspace_and_rejections(L):
     assert _layer_fwd_rc(L, _cfg(ring_bytes=256 * 256 * 2 - 1, minibatch_rows=256)) == -1
     # MXFP8 expert GEMMs need d and I multiples of 128
     assert _layer_fwd_rc(L, _cfg(prec="mxfp8", I=192, ring_bytes=ring)) == -2
+
+
+def _tune_rc(L, cfg, best=True, reps=1, n_mb=1):
+    """mok_tune_fwd with dummy (never dereferenced) non-null pointers."""
+    S = cfg.S
+    tab = (ctypes.c_void_p * S)(*([1] * S))
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+    mbs = (ctypes.c_int32 * 1)(64)
+    out = mok.mok_config()
+    return L.mok_tune_fwd(ctypes.byref(cfg), ctypes.cast(mbs, ctypes.c_void_p), n_mb, None, 0,
+                          reps, 1 << 30, 0, S, ctypes.cast(tab, ctypes.c_void_p), 1, None, 1,
+                          ctypes.byref(w), ctypes.byref(st), ctypes.cast(tab, ctypes.c_void_p),
+                          ctypes.cast(tab, ctypes.c_void_p), 1, 1, None,
+                          ctypes.byref(out) if best else None, None)
+
+
+def test_tuner_rejects_bad_arguments_on_the_host(L):
+    ring = _cfg(ring_bytes=1 << 20, minibatch_rows=64)
+    assert _tune_rc(L, _cfg()) == -1                   # staged path: nothing to tune
+    assert _tune_rc(L, ring, best=False) == -1         # no place for the result
+    assert _tune_rc(L, ring, reps=0) == -1             # no timed call
+    assert _tune_rc(L, ring, n_mb=65) == -1            # too many candidates
+    assert _tune_rc(L, _cfg(ring_bytes=1 << 20, minibatch_rows=64, R_cap=0)) == -1

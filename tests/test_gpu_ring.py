@@ -102,6 +102,37 @@ def test_ring_repeated_calls_bit_identical():
         assert _same(a, b)
 
 
+def test_ring_tuner_picks_a_candidate_and_keeps_results():
+    """mok_tune_fwd times every (minibatch rows, dispatch workgroups) pair the
+    ring can take, skips the others (a minibatch larger than the ring, a
+    split beyond the CUs), returns the fastest, and leaves the outputs of one
+    forward call: bit-identical to the staged path."""
+    w = BF16_SMALL
+    _log("ring tuner")
+    c = make_host_case(w)
+    ref = _layer(c, with_bwd=False)
+    ref.forward()
+    rb = 2 * _slot_bytes(w, 128)  # two 128-row slots: a 512-row minibatch does not fit
+    L = _layer(c, with_bwd=False, ring_bytes=rb, minibatch_rows=64)
+    table = L.tune(mbs=[64, 128, 512], comms=[4, 8, 100000], reps=2)
+    torch.cuda.synchronize()
+    L.check_status()
+    ran = {key: v for key, v in table.items() if v is not None}
+    assert set(ran) == {(64, 4), (64, 8), (128, 4), (128, 8)}, table
+    assert all(v > 0 for v in ran.values())
+    best = (L.cfg.minibatch_rows, L.cfg.comm_wgs)
+    assert ran[best] == min(ran.values())
+    for s in range(w.S):
+        assert _same(L.staging[s], ref.staging[s]), s
+    for s in w.own:
+        assert _same(L.out[s], ref.out[s]), s
+    L.forward()
+    torch.cuda.synchronize()
+    L.check_status()
+    for s in w.own:
+        assert _same(L.out[s], ref.out[s]), s
+
+
 def test_ring_wait_bound_latches_timeout():
     """A 1 us bound on every wait: the kernel ends with MOK_ETIMEOUT (the
     waits of a C2-sized forward cannot all be met that fast) and every

@@ -152,7 +152,9 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
                  "ffn1_gate_up_swiglu", "ffn2_down", "ffn1_gate_up_swiglu_mx", "ffn2_down_mx",
                  "ring_init", "ring_fused_ffn", "combine"}
     fwd_ms = sum(sum(v) for n, v in per_kernel.items() if n in fwd_names) / args.steps
-    bwd_ms = sum(sum(v) for n, v in per_kernel.items() if n not in fwd_names) / args.steps
+    # the backward's side work runs on a second stream beside its GEMMs, so
+    # its time is the step's wall time less the forward's kernels
+    bwd_ms = ms_per_step - fwd_ms
     kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps}
                for n, v in per_kernel.items()}
     # dominant kernel: largest time per step among kernels with a work model
@@ -210,6 +212,7 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
                                f"{'Zipf %.1f skew' % w.zipf_s if w.zipf_s else 'balanced routing'}; "
                                f"step = {'forward + backward' if has_bwd else 'forward'}",
                    "routed_rows": R,
+                   "backward_streams": 2 if (has_bwd and L.aux is not None) else 1,
                    "path": ("ring %d MiB, minibatch %d rows, comm/gemm workgroups %s/%s"
                             % (args.ring_mib, mb, args.comm_wgs or "auto",
                                args.gemm_wgs or "auto")) if args.ring_mib else "staged"},

@@ -43,13 +43,20 @@ class mok_config(ctypes.Structure):
                 ("E_local", ctypes.c_int32), ("prec", ctypes.c_int32), ("R_cap", ctypes.c_int32),
                 ("minibatch_rows", ctypes.c_int32), ("ring_bytes", ctypes.c_int64),
                 ("comm_wgs", ctypes.c_int32), ("gemm_wgs", ctypes.c_int32),
-                ("wait_limit_us", ctypes.c_int32), ("trace", ctypes.c_void_p)]
+                ("wait_limit_us", ctypes.c_int32), ("trace", ctypes.c_void_p),
+                ("aux", ctypes.c_void_p)]
 
 
 class mok_trace(ctypes.Structure):
     _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)),
                 ("names", ctypes.POINTER(ctypes.c_char_p)),
-                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("from_", ctypes.POINTER(ctypes.c_int32)),
+                ("last_stream", ctypes.c_void_p * 2), ("last_idx", ctypes.c_int32 * 2)]
+
+
+class mok_aux(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("events", ctypes.c_void_p * 3)]
 
 
 def _hip_runtime():
@@ -67,6 +74,8 @@ def _hip_runtime():
     hip = ctypes.CDLL(path or "libamdhip64.so.7")
     P = ctypes.c_void_p
     hip.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+    hip.hipEventCreateWithFlags.restype = ctypes.c_int
     hip.hipEventSynchronize.argtypes = [P]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
     hip.hipEventDestroy.argtypes = [P]
@@ -91,7 +100,8 @@ class Trace:
                 raise RuntimeError(f"hipEventCreate failed: {rc}")
             self.events[i] = ev
         self.names = (ctypes.c_char_p * capacity)()
-        self.t = mok_trace(self.events, self.names, capacity, 0)
+        self.from_ = (ctypes.c_int32 * capacity)()
+        self.t = mok_trace(self.events, self.names, capacity, 0, self.from_)
 
     def attach(self, cfg: "mok_config"):
         cfg.trace = ctypes.addressof(self.t)
@@ -102,10 +112,12 @@ class Trace:
 
     def reset(self):
         self.t.count = 0
+        self.t.last_stream[0] = self.t.last_stream[1] = None
+        self.t.last_idx[0] = self.t.last_idx[1] = 0
 
     def records(self):
-        """[(name, ms since the previous event)] for every recorded event after
-        the first of each call (the 'start' marks carry no duration)."""
+        """[(name, ms since the previous event on the same stream)] for every
+        recorded event but the 'start' marks of each call and stream."""
         if self.t.count == 0:
             return []
         rc = self.hip.hipEventSynchronize(self.events[self.t.count - 1])
@@ -114,10 +126,11 @@ class Trace:
         out = []
         for i in range(1, self.t.count):
             name = self.names[i].decode()
-            if name == "start":
+            if name == "start" or self.from_[i] < 0:
                 continue
             ms = ctypes.c_float()
-            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[i - 1], self.events[i])
+            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[self.from_[i]],
+                                              self.events[i])
             if rc != 0:
                 raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
             out.append((name, float(ms.value)))
@@ -127,6 +140,35 @@ class Trace:
         try:
             for i in range(self.capacity):
                 self.hip.hipEventDestroy(self.events[i])
+        except Exception:
+            pass
+
+
+class AuxStream:
+    """A second stream for the backward pass (a torch stream of default
+    priority) and the three events mok_aux asks for; attach() points a
+    mok_config at it."""
+
+    def __init__(self, device):
+        import torch
+        self.hip = _hip_runtime()
+        self.stream = torch.cuda.Stream(device=device)
+        evs = []
+        for _ in range(3):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), 2)  # hipEventDisableTiming
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+            evs.append(ev.value)
+        self.a = mok_aux(self.stream.cuda_stream, (ctypes.c_void_p * 3)(*evs))
+
+    def attach(self, cfg: "mok_config"):
+        cfg.aux = ctypes.addressof(self.a)
+
+    def __del__(self):
+        try:
+            for i in range(3):
+                self.hip.hipEventDestroy(self.a.events[i])
         except Exception:
             pass
 
@@ -214,7 +256,7 @@ def _check(fn: str, rc: int):
 def make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows=256, ring_bytes=0,
                 comm_wgs=0, gemm_wgs=0, wait_limit_us=0) -> mok_config:
     return mok_config(S, T_src, d, E, k, I, E_local, PREC.get(prec, prec), R_cap, minibatch_rows,
-                      ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, None)
+                      ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, None, None)
 
 
 def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> mok_expert_weights:

@@ -375,6 +375,13 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.wg_part = (float*)(wsb + wl.wpart);
   p.wg_order = (int32_t*)(wsb + wl.worder);
   p.tr = cfg->trace;
+  if (cfg->aux) {
+    const mok_aux* a = cfg->aux;
+    if (!a->stream || a->stream == stream || !a->events[0] || !a->events[1] || !a->events[2])
+      return MOK_EINVAL;
+    p.aux = (hipStream_t)a->stream;
+    for (int i = 0; i < 3; ++i) p.aux_ev[i] = (hipEvent_t)a->events[i];
+  }
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);
 }

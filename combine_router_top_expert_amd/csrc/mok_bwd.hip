@@ -407,8 +407,70 @@ __global__ __launch_bounds__(kThreads) void dwr_reduce_kernel(BwdPlan p) {
   p.dw_router[(size_t)e * p.d + c] = acc;
 }
 
+// bf16 backward over two streams.  The call's stream runs the chain that
+// feeds the next GEMM (reverse-combine pull, dh, SwiGLU backward, dx with the
+// reverse-dispatch push, the weight gradients); the second stream runs what
+// only a later step reads, beside it: the transposed re-gather of the token
+// rows (read by the gate/up weight gradient) and the router-gradient layout
+// (read by the router weight gradient) once the reverse-combine pull is
+// done, then -- once dx has been pushed -- the per-token dx sum and the
+// router weight gradient.
+// Every buffer is written on one stream and read after an event the reader
+// waits for; no kernel changes, so results are bit-identical to one stream.
+template <typename T>
+mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
+  hipStream_t aux = p.aux;
+  hipEvent_t fork = p.aux_ev[0], gx_ready = p.aux_ev[1], dx_pushed = p.aux_ev[2];
+  // the pull is HBM-bound like the side work: fork after it, so the side
+  // work meets the dh GEMM instead
+  if (p.R_cap > 0) {
+    hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
+  }
+  MOK_HIP_CHECK(hipEventRecord(fork, stream));
+  MOK_HIP_CHECK(hipStreamWaitEvent(aux, fork, 0));
+  trace_mark(p.tr, "start", aux);
+  const int64_t n_own = (int64_t)p.own_n * p.T_src;
+  const int N_own = (int)(n_own * p.k);
+  if (p.R_cap > 0) {
+    mok_status rc = launch_gather_t(p, p.x_perm, aux);
+    if (rc != MOK_OK) return rc;
+    trace_mark(p.tr, "bwd_regather_x", aux);
+  }
+  MOK_HIP_CHECK(hipEventRecord(gx_ready, aux));
+  if (p.dw_router) {
+    hipLaunchKernelGGL(iota_kernel, dim3((p.E + 255) / 256), dim3(256), 0, aux, p.r_ident, p.E);
+    mok_status rc = launch_layout(N_own, p.E, p.E, N_own, p.topk_idx + (int64_t)p.own_lo * p.T_src * p.k,
+                                  p.r_ident, p.r_counts, p.r_offsets, p.r_row_src, p.r_dest_row,
+                                  p.r_scratch, nullptr, aux, nullptr);
+    if (rc != MOK_OK) return rc;
+    trace_mark(p.tr, "bwd_router_layout", aux);
+  }
+  mok_status rc = launch_bwd_gemms_bf16(p, p.x_perm, stream, gx_ready, dx_pushed);
+  if (rc != MOK_OK) return rc;
+  MOK_HIP_CHECK(hipStreamWaitEvent(aux, dx_pushed, 0));
+  trace_mark(p.tr, "start", aux);  // the wait is not the dx sum's time
+  if (n_own > 0) {
+    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)((n_own + kDxTokPerBlock - 1) / kDxTokPerBlock)),
+                       dim3(kThreads), 0, aux, p);
+    trace_mark(p.tr, "bwd_dx_sum_router", aux);
+  }
+  if (p.dw_router) {
+    const int nchunk = N_own / kRChunk + p.E;
+    hipLaunchKernelGGL(dwr_part_kernel<T>, dim3(nchunk), dim3(kThreads), 0, aux, p, N_own);
+    trace_mark(p.tr, "bwd_dw_router_part", aux);
+    dim3 g((p.d + kThreads - 1) / kThreads, p.E);
+    hipLaunchKernelGGL(dwr_reduce_kernel, g, dim3(kThreads), 0, aux, p);
+    trace_mark(p.tr, "bwd_dw_router_reduce", aux);
+  }
+  MOK_HIP_CHECK(hipEventRecord(fork, aux));  // re-recorded as the join
+  MOK_HIP_CHECK(hipStreamWaitEvent(stream, fork, 0));
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
 template <typename T>
 mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
+  if (sizeof(T) == 2 && p.aux) return run_bwd_two_streams<T>(p, stream);
   if (sizeof(T) == 2) {
     if (p.R_cap > 0) {
       hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);

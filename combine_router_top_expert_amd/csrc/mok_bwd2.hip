@@ -511,7 +511,8 @@ mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
-mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream) {
+mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
+                                 hipEvent_t before_wgrad, hipEvent_t after_dx) {
   const int mt = (p.R_cap + BM - 1) / BM + p.E_local;
   if (p.R_cap > 0) {
     DhArgs d;
@@ -548,6 +549,7 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
     hipLaunchKernelGGL(dx_g2<Default>, dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
     trace_mark(p.tr, "bwd_dx_push", stream);
   }
+  if (after_dx) hipEventRecord(after_dx, stream);
   // grid bound of the split-K tiles: every expert's chunks, at most
   // R_cap / kWgChunk + E_local of them, rounded up to a multiple of 8
   const int max_chunks = (p.R_cap / kWgChunk + p.E_local + 7) / 8 * 8;
@@ -572,6 +574,7 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
   w.ntn = (w.N + Default::BN - 1) / Default::BN;
   // The grid covers both schedules (max_chunks >= E_local); the kernels pick
   // one from the routed counts (wg_spread) and surplus workgroups return.
+  if (before_wgrad) hipStreamWaitEvent(stream, before_wgrad, 0);
   hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets, p.E_local,
                      p.R_cap, p.wg_order);
   hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),

@@ -86,6 +86,14 @@ inline void trace_mark(mok_trace* t, const char* name, hipStream_t s) {
   if (!t || !t->events || t->count >= t->capacity) return;
   (void)hipEventRecord((hipEvent_t)t->events[t->count], s);
   if (t->names) t->names[t->count] = name;
+  // the previous event on the same stream (the last two streams are kept)
+  int slot = t->last_stream[0] == (void*)s ? 0 : t->last_stream[1] == (void*)s ? 1 : -1;
+  if (t->from) t->from[t->count] = slot >= 0 ? t->last_idx[slot] : -1;
+  if (slot < 0) {  // replace the older entry
+    slot = t->last_idx[0] <= t->last_idx[1] ? 0 : 1;
+    t->last_stream[slot] = (void*)s;
+  }
+  t->last_idx[slot] = t->count;
   t->count += 1;
 }
 

@@ -113,6 +113,8 @@ struct BwdPlan {
   float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
   int32_t* wg_order;  // [E_local] local experts by routed rows, descending
   mok_trace* tr;    // host-side trace, may be null
+  hipStream_t aux;      // second stream for the work beside the GEMMs, or null
+  hipEvent_t aux_ev[3]; // fork/join events of the second stream
 };
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
 // Leading dimension of the transposed token rows of the gate/up weight
@@ -121,7 +123,8 @@ inline int64_t xt_ld(int R_cap, int E_local) {
   return ((int64_t)R_cap + 63) / 64 * 64 + 64 * (int64_t)E_local;
 }
 mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream);
-mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream);
+mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
+                                 hipEvent_t before_wgrad = nullptr, hipEvent_t after_dx = nullptr);
 size_t wgrad_partial_bytes(int R_cap, int d, int I);
 
 }  // namespace mok

@@ -12,7 +12,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import (MAX_SOURCES, make_config, make_state, make_weights, mok_layer_bwd, mok_layer_fwd,
+from . import (MAX_SOURCES, AuxStream, make_config, make_state, make_weights, mok_layer_bwd, mok_layer_fwd,
                mok_mx_quantize, mok_tune_fwd, mok_workspace_bytes, STATUS)
 
 
@@ -30,7 +30,7 @@ def to_device(a: np.ndarray, prec: str, device) -> torch.Tensor:
 class MoELayer:
     def __init__(self, S, T_src, d, E, k, I, E_local, prec, R_cap, own_lo, own_n, device="cuda",
                  ring_bytes=0, minibatch_rows=256, comm_wgs=0, gemm_wgs=0, with_bwd=True,
-                 wait_limit_us=0):
+                 wait_limit_us=0, two_streams=True):
         assert S <= MAX_SOURCES
         self.S, self.T_src, self.d, self.E, self.k, self.I = S, T_src, d, E, k, I
         self.E_local, self.prec, self.R_cap = E_local, prec, R_cap
@@ -59,6 +59,11 @@ class MoELayer:
         self.ws = torch.zeros(max(mok_workspace_bytes(self.cfg), 256), dtype=torch.uint8,
                               device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        # the bf16 backward runs its side work on a second stream (mok_aux)
+        self.aux = None
+        if two_streams and with_bwd and prec == "bf16":
+            self.aux = AuxStream(dev)
+            self.aux.attach(self.cfg)
         self.state = make_state(self.topk_idx, self.topk_gate, self.counts, self.offsets,
                                 self.row_src, self.dest_row, self.h, self.ab)
         self.with_bwd = with_bwd

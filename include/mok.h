@@ -88,7 +88,28 @@ typedef struct mok_trace {
   const char** names;
   int32_t capacity;
   int32_t count;
+  int32_t* from;          /* optional [capacity]: from[i] = the index of the previous event
+                             recorded on the same stream (the start of kernel i), -1 for the
+                             first event of a stream; NULL = not kept.  With a second stream
+                             (mok_aux) durations are elapsed(events[from[i]], events[i]). */
+  void* last_stream[2];   /* bookkeeping of the library (zero-initialise): the last two */
+  int32_t last_idx[2];    /* streams seen and their latest event index */
 } mok_trace;
+
+/* Optional second stream of the backward pass (caller-owned).  With
+ * mok_config.aux non-NULL, the bf16 mok_layer_bwd runs the steps that do not
+ * feed the next GEMM -- the transposed re-gather of the token rows, the
+ * router-gradient layout, the per-token dx sum and the router weight
+ * gradient -- on `stream`, beside the dgrad/wgrad GEMMs on the call's
+ * stream, ordered by the three events; the call's stream then waits for the
+ * second one, so work enqueued after the call sees every output.  `stream`
+ * must differ from the call's stream and have the default priority;
+ * `events` are hipEvent_t handles (timing may be disabled), re-recorded by
+ * every call.  Results are bit-identical with and without it. */
+typedef struct mok_aux {
+  void* stream;
+  void* events[3];
+} mok_aux;
 
 typedef struct mok_config {
   int32_t S;              /* source token buffers (simulated source ranks), 1..MOK_MAX_SOURCES */
@@ -113,6 +134,7 @@ typedef struct mok_config {
                              on expiry MOK_ETIMEOUT is latched and the kernel returns
                              (0 = 2 s) */
   mok_trace* trace;       /* optional kernel timing, NULL = off (host memory) */
+  mok_aux* aux;           /* optional second stream of the backward pass, NULL = one stream */
 } mok_config;
 
 /* Expert weights of the E_local local experts (see Layout above).  For

@@ -116,3 +116,21 @@ def test_tuner_rejects_bad_arguments_on_the_host(L):
     assert _tune_rc(L, ring, reps=0) == -1             # no timed call
     assert _tune_rc(L, ring, n_mb=65) == -1            # too many candidates
     assert _tune_rc(L, _cfg(ring_bytes=1 << 20, minibatch_rows=64, R_cap=0)) == -1
+
+
+def test_backward_second_stream_checked_on_the_host(L):
+    """mok_aux must name its own stream and three events (MOK_EINVAL before any launch)."""
+    S = 2
+    tab = (ctypes.c_void_p * S)(*([1] * S))
+    tp = ctypes.cast(tab, ctypes.c_void_p)
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+    for aux in (mok.mok_aux(None, (ctypes.c_void_p * 3)(1, 1, 1)),      # no stream
+                mok.mok_aux(7, (ctypes.c_void_p * 3)(1, None, 1)),      # an event missing
+                mok.mok_aux(7, (ctypes.c_void_p * 3)(1, 1, 1))):        # the call's own stream
+        cfg = _cfg()
+        cfg.aux = ctypes.addressof(aux)
+        rc = L.mok_layer_bwd(ctypes.byref(cfg), 0, S, tp, tp, 1, 1, ctypes.byref(w),
+                             ctypes.byref(st), tp, 1, tp, tp, 1, 1, 1, None, 1, 1,
+                             7 if aux.stream == 7 and aux.events[1] else None)
+        assert rc == -1

@@ -507,6 +507,30 @@ def test_fwd_bwd_run_to_run_bit_identical():
                            b.view(torch.uint8) if b.dtype != torch.uint8 else b)
 
 
+@pytest.mark.parametrize("name", ["bf16_all_local", "bf16_share", "bf16_split_k"])
+def test_bwd_two_streams_bit_identical_to_one(name):
+    """The backward with its side work on a second stream (mok_aux) gives the
+    same bytes as the one-stream backward, twice in a row."""
+    w = BWD_CASES[name]
+    _log("two streams", name)
+    c = make_host_case(w)
+    d_out = [to_device(synth.gen_dout(w, s)[0], w.prec, DEV) for s in range(w.S)]
+    snaps = []
+    for two in (False, True, True):
+        L = _layer(c, two_streams=two)
+        assert (L.aux is not None) == two
+        L.forward()
+        L.backward(d_out)
+        torch.cuda.synchronize()
+        L.check_status()
+        snaps.append([t.clone() for t in [L.d_gate, L.dw_gate, L.dw_up, L.dw_down, L.dw_router] +
+                      [L.d_x[s] for s in w.own] + [L.dx_stage[s] for s in range(w.S)]])
+        del L
+    for snap in snaps[1:]:
+        for a, b in zip(snaps[0], snap):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 def test_mx_quantize_bit_exact():
     w = synth.WORKLOADS["C2"].replace(E=2, local_experts=[0, 1], I=256, d=512)
     _log("mx_quantize")

@@ -162,15 +162,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     if (active) {
       const float* wr = ws + es * 4 * EL + 4 * el;
       const float* xr = xs + tg * TPU + 4 * tl;
+      // the LDS reads of the next kG d steps are issued before the fmaf of
+      // the current kG: with one wave per SIMD nothing else hides their
+      // latency (the chains still advance one d step at a time, ascending)
+      constexpr int kG = 4;
+      static_assert(dc % kG == 0, "d chunk of whole groups");
+      float4 wv[2][kG], xv[2][kG];
 #pragma unroll
-      for (int i = 0; i < dc; ++i) {
-        const float4 wv = *reinterpret_cast<const float4*>(wr + i * wpitch);
-        const float4 xv = *reinterpret_cast<const float4*>(xr + i * TB);
-        const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, wa[4] = {wv.x, wv.y, wv.z, wv.w};
+      for (int g = 0; g < kG; ++g) {
+        wv[0][g] = *reinterpret_cast<const float4*>(wr + g * wpitch);
+        xv[0][g] = *reinterpret_cast<const float4*>(xr + g * TB);
+      }
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+      for (int i0 = 0; i0 < dc; i0 += kG) {
+        const int cur = (i0 / kG) & 1;
+        if (i0 + kG < dc) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fmaf(xa[p], wa[q], acc[p][q]);
+          for (int g = 0; g < kG; ++g) {
+            wv[cur ^ 1][g] = *reinterpret_cast<const float4*>(wr + (i0 + kG + g) * wpitch);
+            xv[cur ^ 1][g] = *reinterpret_cast<const float4*>(xr + (i0 + kG + g) * TB);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+          const float xa[4] = {xv[cur][g].x, xv[cur][g].y, xv[cur][g].z, xv[cur][g].w};
+          const float wa[4] = {wv[cur][g].x, wv[cur][g].y, wv[cur][g].z, wv[cur][g].w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fmaf(xa[p], wa[q], acc[p][q]);
+        }
       }
     }
   }

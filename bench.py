@@ -194,6 +194,31 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
             v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
             v["frac_alu_peak"] = v["tflops"] / PEAK_FP32_FMA_TFLOPS
 
+    graph = None
+    if args.graph:
+        # the whole step captured once and replayed: no host launch cost
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        L.check_status()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        L.check_status()
+        graph = {"ms_per_step": g_ms, "tokens_per_s": T_tok / (g_ms * 1e-3)}
+        del g
+
     result = {
         "metric": METRIC,
         "value": T_tok / (ms_per_step * 1e-3),
@@ -222,6 +247,8 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
         "roofline": roof,
         "kernels": kernels,
     }
+    if graph is not None:
+        result["graph"] = graph
     return result
 
 
@@ -239,6 +266,9 @@ def main():
     ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
     ap.add_argument("--comm-wgs", type=int, default=0, help="ring path: dispatch workgroups")
     ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step in a HIP graph and time its replays "
+                         "(reported under 'graph'; the headline stays the eager step)")
     ap.add_argument("--tune", action="store_true",
                     help="ring path: choose minibatch rows and dispatch workgroups with "
                          "mok_tune_fwd before the timed steps (untimed)")

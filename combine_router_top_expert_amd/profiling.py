@@ -14,8 +14,9 @@ The byte counters are scaled by what they read for the plain 1 GiB device copy
 (``FETCH_SIZE`` and ``WRITE_SIZE`` are in KiB; the factor maps the copy's
 reading onto its known 1 GiB).  ``hbm_traffic.json`` records the traffic of one
 launch of each kernel (its last profiled launch) under the name ``bench.py``
-reports, together with a hash of the kernel sources: ``bench.py`` reports the
-traffic only while the sources still hash to that value.
+reports, together with a hash of each kernel's sources (the .hip file that
+defines it, every header under csrc/ and include/): ``bench.py`` reports a
+kernel's traffic only while its sources still hash to that value.
 """
 from __future__ import annotations
 
@@ -52,6 +53,28 @@ def source_hash() -> str:
     files = []
     for d, exts in ((CSRC, (".hip", ".h")), (os.path.join(ROOT, "include"), (".h",))):
         files += sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(exts))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_source_hash(key: str):
+    """sha256 over the .hip file that defines kernel ``key`` (a name as
+    kernel_key returns it, template arguments dropped) and every header, or
+    None if no source defines it."""
+    base = key.split("<")[0]
+    pat = re.compile(r"__global__[^;{]*\b%s\s*\(" % re.escape(base))
+    hip = [f for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")
+           and pat.search(open(os.path.join(CSRC, f)).read())]
+    if len(hip) != 1:
+        return None
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, hip[0])]
+    files += sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h"))
+    inc = os.path.join(ROOT, "include")
+    files += sorted(os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h"))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -111,7 +134,8 @@ def main(out_dir: str, workload: str = "C2", path: str = "staged"):
             continue
         rb = fv[-1] * 1024 * fs
         wb = write.get(k, [0.0])[-1] * 1024 * ws
-        traffic[name] = {"read_bytes": rb, "write_bytes": wb, "bytes": rb + wb}
+        traffic[name] = {"read_bytes": rb, "write_bytes": wb, "bytes": rb + wb,
+                         "source_sha256": kernel_source_hash(k)}
         lines.append(f"| {k} | {name} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, "c2_hbm_traffic.md"), "w") as f:
@@ -148,10 +172,14 @@ def recorded_traffic(kernel: str, workload: str, path: str):
         rec = json.load(fh)
     if rec.get("workload") != workload or rec.get("path") != path:
         return None
-    if rec.get("source_sha256") != source_hash():
-        return None
     k = rec["kernels"].get(kernel)
-    return None if k is None else k["bytes"]
+    if k is None:
+        return None
+    keys = [key for key, n in TRACE_NAME.items() if n == kernel]
+    now = {kernel_source_hash(key) for key in keys} - {None}
+    if k.get("source_sha256") is None or k["source_sha256"] not in now:
+        return None
+    return k["bytes"]
 
 
 if __name__ == "__main__":

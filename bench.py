@@ -194,6 +194,32 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
             v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
             v["frac_alu_peak"] = v["tflops"] / PEAK_FP32_FMA_TFLOPS
 
+    # run-to-run identity at full size: every output of two consecutive
+    # untimed steps compared byte for byte on the device; the digest covers
+    # the combined outputs (and input gradients) of the own tokens
+    def outputs():
+        outs = [L.out[s] for s in w.own] + list(L.staging) + [L.h]
+        if has_bwd:
+            outs += [L.d_x[s] for s in w.own] + [L.d_gate, L.dw_gate, L.dw_up, L.dw_down,
+                                                 L.dw_router] + list(L.dx_stage)
+        return outs
+
+    step()
+    torch.cuda.synchronize()
+    L.check_status()
+    first = [t.clone() for t in outputs()]
+    step()
+    torch.cuda.synchronize()
+    L.check_status()
+    identical = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+                    for a, b in zip(first, outputs()))
+    import hashlib
+    h = hashlib.sha256()
+    for t in [L.out[s] for s in w.own] + ([L.d_x[s] for s in w.own] if has_bwd else []):
+        h.update(t.contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    del first
+    torch.cuda.empty_cache()
+
     graph = None
     if args.graph:
         # the whole step captured once and replayed: no host launch cost
@@ -249,6 +275,8 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     }
     if graph is not None:
         result["graph"] = graph
+    result["determinism"] = {"two_steps_identical": identical,
+                             "own_outputs_sha256": h.hexdigest()}
     return result
 
 

@@ -6,8 +6,8 @@
 
 namespace mok {
 
-int route_geometry(int E, int* EL, int* ESETS, int* TB, int* dc);
-size_t route_smem_bytes(int E);
+int route_geometry(int E, int T, int* EL, int* ESETS, int* TB, int* dc);
+size_t route_smem_bytes(int E, int T);
 // Routes T consecutive tokens starting at token 0 of source src_lo (sources
 // of T_src tokens each, contiguous in the table).
 mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, int T, int d,

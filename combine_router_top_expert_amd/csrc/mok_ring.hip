@@ -374,7 +374,11 @@ mok_status ring_check(int prec, int d, int I, int mb, int64_t ring_bytes, int co
   if (ring_bytes / ring_slot_bytes(prec, d, mb) < 1) return MOK_EINVAL;  // one minibatch at least
   const int cus = device_cus();
   if (cus <= 0) return MOK_EDEVICE;
-  const int comm = comm_wgs > 0 ? comm_wgs : (cus >= 64 ? cus / 8 : 1);
+  // default split: 1/8 of the CUs pull bf16 rows; MXFP8 dispatch also
+  // quantises every row and needs 1/4 (measured by mok_tune_fwd on the
+  // mid-size layer: 3.70 ms with 32 dispatch workgroups, 2.62 ms with 64)
+  const int comm = comm_wgs > 0 ? comm_wgs
+                                : (cus >= 64 ? (prec == MOK_MXFP8 ? cus / 4 : cus / 8) : 1);
   const int gemm = gemm_wgs > 0 ? gemm_wgs : cus - comm;
   if (comm < 1 || gemm < 1 || comm + gemm > cus) return MOK_EINVAL;  // all resident: one per CU
   if (comm_out) *comm_out = comm;

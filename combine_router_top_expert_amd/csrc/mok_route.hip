@@ -17,7 +17,7 @@ namespace mok {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kMaxK = 16;
+constexpr int kRouteMinBlocks = 256;  // one block per CU before blocks shrink
 
 struct RouteArgs {
   SrcTable src;     // token buffers: token g of the launch is src.p[src_lo + g / T_src][g % T_src]
@@ -61,6 +61,70 @@ __device__ __forceinline__ void unpack<float>(uint4 u, float* out) {
   out[1] = __uint_as_float(u.y);
   out[2] = __uint_as_float(u.z);
   out[3] = __uint_as_float(u.w);
+}
+
+// Top-k and gates of a block's tokens from the logits zs[TB][zp].  LP = 2^LPS
+// lanes per token (the power of two covering E, at most 64), 64 / LP tokens
+// per wave at a time; lane li of a token's group holds experts li, li + LP,
+// ...  The butterfly stays inside the group, so the reduction takes LPS
+// steps.  Lanes of a token past the block's end run the same steps on -inf
+// and write nothing.
+template <int LPS>
+__device__ __forceinline__ void select_topk(const RouteArgs& a, const float* zs, int zp, int t0,
+                                            int TB, int wave, int lane) {
+  constexpr int LP = 1 << LPS, TPI = 64 >> LPS;
+  const int MPL = (a.E + LP - 1) >> LPS;  // entries per lane (<= 8)
+  const int grp = lane >> LPS, li = lane & (LP - 1);
+  for (int tb0 = wave * TPI; tb0 < TB && t0 + tb0 < a.T; tb0 += (kRouteThreads / 64) * TPI) {
+    const int tl = tb0 + grp;
+    const int t = t0 + tl;
+    const bool live = tl < TB && t < a.T;
+    float zv[8];
+    uint32_t used = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      int e = li + LP * m;
+      zv[m] = (live && m < MPL && e < a.E) ? zs[tl * zp + e] : -__builtin_inff();
+    }
+    // round j picks slot j; lane li == j keeps that slot (k <= E <= LP, so
+    // every slot has a lane); the exponentials are summed in slot order
+    float z0 = 0.0f, sum = 0.0f, my_ex = 0.0f;
+    int my_e = 0;
+    for (int j = 0; j < a.k; ++j) {
+      float bz = -__builtin_inff();
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        int e = li + LP * m;
+        bool ok = m < MPL && e < a.E && !((used >> m) & 1u);
+        if (ok && (zv[m] > bz || (zv[m] == bz && e < be))) {
+          bz = zv[m];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int off = LP >> 1; off >= 1; off >>= 1) {
+        float oz = __shfl_xor(bz, off, 64);
+        int oe = __shfl_xor(be, off, 64);
+        if (oz > bz || (oz == bz && oe < be)) {
+          bz = oz;
+          be = oe;
+        }
+      }
+      if (live && (be & (LP - 1)) == li) used |= 1u << (be >> LPS);
+      if (j == 0) z0 = bz;
+      const float exj = expf(bz - z0);
+      sum += exj;
+      if (li == j) {
+        my_ex = exj;
+        my_e = be;
+      }
+    }
+    if (live && li < a.k) {
+      a.topk_idx[(size_t)t * a.k + li] = my_e;
+      a.topk_gate[(size_t)t * a.k + li] = my_ex / sum;
+    }
+  }
 }
 
 // A block routes TB tokens against all E experts.  A lane keeps 16 logit
@@ -215,57 +279,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // selection: one wave per token
-  const int MPL = (a.E + 63) / 64;   // entries per lane (<= 8)
-  for (int tl = wave; tl < TB; tl += kRouteThreads / 64) {
-    const int t = t0 + tl;
-    if (t >= a.T) break;
-    float zv[8];
-    uint32_t used = 0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      int e = lane + 64 * m;
-      zv[m] = (m < MPL && e < a.E) ? zs[tl * zp + e] : -__builtin_inff();
-    }
-    float zsel[kMaxK];
-    int esel[kMaxK];
-    for (int j = 0; j < a.k; ++j) {
-      float bz = -__builtin_inff();
-      int be = 0x7FFFFFFF;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        int e = lane + 64 * m;
-        bool ok = m < MPL && e < a.E && !((used >> m) & 1u);
-        if (ok && (zv[m] > bz || (zv[m] == bz && e < be))) {
-          bz = zv[m];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        float oz = __shfl_xor(bz, off, 64);
-        int oe = __shfl_xor(be, off, 64);
-        if (oz > bz || (oz == bz && oe < be)) {
-          bz = oz;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) used |= 1u << (be >> 6);
-      zsel[j < kMaxK ? j : 0] = bz;
-      esel[j < kMaxK ? j : 0] = be;
-    }
-    float sum = 0.0f;
-    float ex[kMaxK];
-    for (int j = 0; j < a.k; ++j) {
-      ex[j] = expf(zsel[j] - zsel[0]);
-      sum += ex[j];
-    }
-    for (int j = 0; j < a.k; ++j) {
-      if (lane == j) {
-        a.topk_idx[(size_t)t * a.k + j] = esel[j];
-        a.topk_gate[(size_t)t * a.k + j] = ex[j] / sum;
-      }
-    }
+  // selection: LP lanes per token (the power of two covering E, at most 64)
+  const int LPS = a.E >= 64 ? 6 : (a.E <= 1 ? 0 : 32 - __builtin_clz(a.E - 1));  // log2 LP
+  switch (LPS) {
+    case 6: select_topk<6>(a, zs, zp, t0, TB, wave, lane); break;
+    case 5: select_topk<5>(a, zs, zp, t0, TB, wave, lane); break;
+    case 4: select_topk<4>(a, zs, zp, t0, TB, wave, lane); break;
+    case 3: select_topk<3>(a, zs, zp, t0, TB, wave, lane); break;
+    case 2: select_topk<2>(a, zs, zp, t0, TB, wave, lane); break;
+    case 1: select_topk<1>(a, zs, zp, t0, TB, wave, lane); break;
+    default: select_topk<0>(a, zs, zp, t0, TB, wave, lane); break;
   }
 }
 
@@ -273,15 +296,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
 // Block geometry: EL expert lanes per wave (4 experts each; a power of two up
 // to 64), ESETS sets of 4 EL experts, TB tokens per block (four wave units
-// when the expert sets allow), dc-wide d chunks (smaller when a block holds
-// many tokens or experts).  Returns the units per wave.
-int route_geometry(int E, int* EL, int* ESETS, int* TB, int* dc) {
+// when the expert sets allow, fewer while the T tokens would leave CUs
+// without a block), dc-wide d chunks (smaller when a block holds many tokens
+// or experts).  Returns the units per wave.
+int route_geometry(int E, int T, int* EL, int* ESETS, int* TB, int* dc) {
   int el = 1;
   while (el < 64 && 4 * el < E) el <<= 1;
   *EL = el;
   *ESETS = (E + 4 * el - 1) / (4 * el);
   const int tpu = (64 / el) * 4;
   *TB = *ESETS >= 4 ? tpu : tpu * (4 / *ESETS);
+  while (*TB > tpu && (T + *TB - 1) / *TB < kRouteMinBlocks) *TB >>= 1;
   int c = 32;
   while (c > 8 && (size_t)c * (*TB + *ESETS * 4 * el + 4) > 12288) c >>= 1;
   *dc = c;
@@ -289,9 +314,9 @@ int route_geometry(int E, int* EL, int* ESETS, int* TB, int* dc) {
   return (units + 3) / 4;
 }
 
-size_t route_smem_bytes(int E) {
+size_t route_smem_bytes(int E, int T) {
   int EL, ES, TB, dc;
-  route_geometry(E, &EL, &ES, &TB, &dc);
+  route_geometry(E, T, &EL, &ES, &TB, &dc);
   const size_t Epad = (size_t)ES * 4 * EL;
   const size_t stage = 2 * ((size_t)dc * TB + (size_t)dc * (Epad + 4));
   const size_t logits = (size_t)TB * (Epad + 1);
@@ -314,7 +339,7 @@ mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, in
   a.d = d;
   a.E = E;
   a.k = k;
-  const int upw = route_geometry(E, &a.EL, &a.ESETS, &a.TB, &a.dc);
+  const int upw = route_geometry(E, T, &a.EL, &a.ESETS, &a.TB, &a.dc);
   if (d % a.dc != 0 || upw != 1) return MOK_ESHAPE;
   // staging units per thread (both operands) must fit the kernel's slots
   const int U = prec == MOK_F32 ? 4 : 8;
@@ -323,7 +348,7 @@ mok_status launch_route(int prec, const SrcTable& src, int src_lo, int T_src, in
   const int need = per > perx ? per : perx;
   const int pt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
   if (need > 8) return MOK_ESHAPE;
-  const size_t smem = route_smem_bytes(E);
+  const size_t smem = route_smem_bytes(E, T);
   dim3 grid((T + a.TB - 1) / a.TB);
   dim3 blk(kRouteThreads);
 #define MOK_ROUTE_LAUNCH(TY, DCV, PTV) \

@@ -127,7 +127,8 @@ typedef struct mok_config {
   int64_t ring_bytes;     /* fused path (persistent ring kernel, bf16 and MXFP8): bytes of the
                              ring of token slots, at least one slot of minibatch_rows rows;
                              0 = staged path (one launch per step) */
-  int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = CUs / 8) */
+  int32_t comm_wgs;       /* fused path: dispatch/combine workgroups (0 = CUs / 8 for bf16,
+                             CUs / 4 for MXFP8, whose dispatch also quantises) */
   int32_t gemm_wgs;       /* fused path: grouped-GEMM workgroups (0 = the remaining CUs);
                              comm_wgs + gemm_wgs must not exceed the CU count */
   int32_t wait_limit_us;  /* fused path: bound of every device-side wait in microseconds;

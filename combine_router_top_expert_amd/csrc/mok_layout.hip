@@ -147,12 +147,10 @@ __global__ __launch_bounds__(64) void layout_place(LayoutArgs a) {
     }
     __syncthreads();
     if (in) {
-      if (valid && row < a.R_cap) {
-        a.row_src[row] = (int32_t)n;
-        a.dest_row[n] = row;
-      } else {
-        a.dest_row[n] = -1;
-      }
+      // a local item past the capacity keeps its row number (>= R_cap): the
+      // consumers skip it, where -1 would read it as a remote slot
+      if (valid && row < a.R_cap) a.row_src[row] = (int32_t)n;
+      a.dest_row[n] = valid ? row : -1;
     }
   }
 }

@@ -158,7 +158,7 @@ typedef struct mok_fwd_state {
   int32_t* counts;     /* [E_local] routed rows per local expert */
   int32_t* offsets;    /* [E_local+1] exclusive scan of counts; offsets[E_local] = R */
   int32_t* row_src;    /* [R_cap] row -> item n */
-  int32_t* dest_row;   /* [S*T_src*k] item n -> row, -1 for remote experts */
+  int32_t* dest_row;   /* [S*T_src*k] item n -> row, -1 for remote experts (>= R_cap: dropped) */
   void* h;             /* [R_cap, I] SwiGLU output in the activation dtype (bf16 / f32) */
   void* ab;            /* [R_cap, 2I] pre-activation a | b in the activation dtype, or NULL */
 } mok_fwd_state;
@@ -181,9 +181,12 @@ mok_status mok_route(const mok_config* cfg, int32_t T, const void* x, const void
  * placement ordered by local expert].  Input: routing of all S sources
  * topk_idx_all [S*T_src*k] and expert_to_local [E] (local index, -1 remote).
  * Output: counts [E_local], offsets [E_local+1], row_src [R_cap] (row -> n),
- * dest_row [S*T_src*k] (n -> row or -1).  Rows of an expert are in ascending
- * n (a stable counting sort).  R > R_cap latches MOK_ECAPACITY (rows past
- * R_cap are not written); a bad expert id latches MOK_EROUTE.  ws: workspace. */
+ * dest_row [S*T_src*k] (n -> row, or -1 if the expert is remote).  Rows of an
+ * expert are in ascending n (a stable counting sort).  R > R_cap latches
+ * MOK_ECAPACITY: rows past R_cap are not written to row_src, their items keep
+ * their row number (>= R_cap) in dest_row, and every later step skips them
+ * (a dropped slot adds nothing to the output and has a zero gate gradient);
+ * a bad expert id latches MOK_EROUTE.  ws: workspace. */
 mok_status mok_layout(const mok_config* cfg, const int32_t* topk_idx_all,
                       const int32_t* expert_to_local, int32_t* counts, int32_t* offsets,
                       int32_t* row_src, int32_t* dest_row, void* ws, int32_t* dev_status,

@@ -133,6 +133,12 @@ def test_layout_errors_latched():
         assert STATUS[int(st.item())] == expect
         rs = row_src.cpu().numpy()
         assert rs.min() >= 0 and rs.max() < t.size   # nothing written out of range
+        if not bad:
+            # the rows below R_cap as without a capacity; a dropped item keeps its
+            # row number (>= R_cap) so that later steps skip it
+            ref = oracle.layout(t.reshape(1, w.T_src, w.k), e2l, w.E_local)
+            np.testing.assert_array_equal(rs, ref["row_src"][:R_cap])
+            np.testing.assert_array_equal(dest_row.cpu().numpy(), ref["dest_row"])
 
 
 def test_dispatch_tagged_rows_and_identity_combine():
@@ -419,6 +425,73 @@ def test_layer_bwd(name):
     e_r = rel_err(L.dw_router.cpu().numpy(), dwr_ref)
     _log(f"  dx {e_dx:.3e} dW {e_w:.3e} dWr {e_r:.3e}")
     assert e_dx <= tol and e_w <= tol and e_r <= tol
+
+
+def test_layer_rows_beyond_capacity_dropped():
+    """More routed rows than R_cap: the layer latches MOK_ECAPACITY, computes
+    the rows below R_cap, and the combine and the dx sum leave out the
+    dropped slots (a dropped slot adds nothing to the output and has a zero
+    gate gradient).  Expected values: the oracle's forward with the dropped
+    slots sent to a remote expert holding zeros, and the backward composed
+    of the oracle's per-row backward over the kept slots plus its router
+    backward with zero gate gradients at the dropped slots."""
+    w = BWD_CASES["bf16_all_local"]
+    _log("capacity")
+    c = make_host_case(w)
+    R = int(c.layout["R"])
+    R_cap = R - 37  # the last rows of the last expert(s) are dropped
+    L = _layer(c, R_cap=R_cap)
+    dout_store = [synth.gen_dout(w, s) for s in range(w.S)]
+    d_out = [to_device(a, w.prec, DEV) for a, _ in dout_store]
+    L.forward()
+    L.backward(d_out)
+    torch.cuda.synchronize()
+    assert STATUS[int(L.status.item())] == "MOK_ECAPACITY"
+    dest = c.layout["dest_row"].reshape(w.S, w.T_src, w.k)
+    toks = [(s, t) for s in w.own for t in range(w.T_src)]
+    dropped = np.stack([dest[s, t] >= R_cap for s, t in toks])
+    assert dropped.sum() == 37
+    tok_x = np.stack([c.x_val[s][t] for s, t in toks])
+    idx = np.stack([c.topk_all[s, t] for s, t in toks])
+    g = np.stack([c.gate_all[s, t] for s, t in toks])
+    # forward: dropped slots -> an extra expert id that is remote, pushed rows 0
+    e2l_x = np.concatenate([c.e2l, [-1]]).astype(np.int32)
+    idx_x = np.where(dropped, w.E, idx)
+    wg, wu, wd = oracle_weights(c)
+    _, out_ref = oracle.fwd_tokens(tok_x, idx_x, g, e2l_x, wg, wu, wd, w.prec,
+                                   peer_y=np.zeros((len(toks), w.k, w.d)))
+    out = np.stack([L.out[s][t].float().cpu().numpy() for s, t in toks])
+    e_out = rel_err(out, out_ref)
+    # backward: per-row backward of the kept slots, router backward with dg = 0
+    # at the dropped ones
+    dx_ref = np.zeros((len(toks), w.d))
+    for i, (s, t) in enumerate(toks):
+        dg = np.zeros(w.k)
+        for j in range(w.k):
+            if dropped[i, j]:
+                continue
+            le = c.e2l[idx[i, j]]
+            r = oracle.bwd_row(tok_x[i], g[i, j], dout_store[s][1][t], c.wg_val[le], c.wu_val[le],
+                               c.wd_val[le])
+            dg[j] = r["dg"]
+            dx_ref[i] += r["dx"]
+        _, dxr = oracle.router_bwd_token(idx[i], g[i], dg, c.wr_val)
+        dx_ref[i] += dxr
+    dx = np.stack([L.d_x[s][t].float().cpu().numpy() for s, t in toks])
+    e_dx = rel_err(dx, dx_ref)
+    # the weight gradients of the expert cut by the capacity cover its kept rows
+    lay = c.layout
+    le = int(np.searchsorted(lay["offsets"], R_cap - 1, side="right")) - 1
+    rows = lay["row_src"][lay["offsets"][le]:min(lay["offsets"][le + 1], R_cap)]
+    tt, jj = rows // w.k, rows % w.k
+    rx = np.stack([c.x_val[q // w.T_src][q % w.T_src] for q in tt])
+    rg = np.array([c.gate_all[q // w.T_src, q % w.T_src, j] for q, j in zip(tt, jj)])
+    rd = np.stack([dout_store[q // w.T_src][1][q % w.T_src] for q in tt])
+    dwg, dwu, dwd = oracle.expert_wgrad(rx, rg, rd, c.wg_val[le], c.wu_val[le], c.wd_val[le])
+    e_w = max(rel_err(L.dw_gate[le].cpu().numpy(), dwg), rel_err(L.dw_up[le].cpu().numpy(), dwu),
+              rel_err(L.dw_down[le].cpu().numpy(), dwd))
+    _log(f"  out {e_out:.3e} dx {e_dx:.3e} dW(last expert) {e_w:.3e}")
+    assert e_out <= TOL[w.prec] and e_dx <= TOL[w.prec] and e_w <= TOL[w.prec]
 
 
 def _bwd_sampled(c, L, dout_store, toks):

@@ -149,8 +149,10 @@ def main(out_dir: str, workload: str = "C2", path: str = "staged"):
         t = ["# Kernel trace summary, mid-size layer (forward + backward)", "",
              "Command (from the repository root):", "",
              "    rocprofv3 --kernel-trace --stats -f csv -d OUT/kt -o kt -- python3 bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-             "", "Five steps (2 warm-up + 3 timed) of the mid-size layer: T=16384 tokens (8 x 2048),",
-             "d=2048, E=64 all local, top-6, SwiGLU I=1408, bf16.", "",
+             "", "Seven steps of the mid-size layer (2 warm-up, 3 timed, 2 for the run-to-run identity",
+             "check, whose byte comparisons and host copies are the torch kernels below): T=16384",
+             "tokens (8 x 2048), d=2048, E=64 all local, top-6, SwiGLU I=1408, bf16; the backward's",
+             "side work runs on a second stream beside its GEMMs.", "",
              "| kernel | trace name | calls | average us | share % |", "|---|---|---|---|---|"]
         for r in rows:
             k = kernel_key(r["Name"])

@@ -443,6 +443,11 @@ def test_layer_rows_beyond_capacity_dropped():
     L = _layer(c, R_cap=R_cap)
     dout_store = [synth.gen_dout(w, s) for s in range(w.S)]
     d_out = [to_device(a, w.prec, DEV) for a, _ in dout_store]
+    # rows an earlier call could have left: a dropped slot must not be read
+    for s in range(w.S):
+        L.staging[s].fill_(float("nan"))
+        L.dx_stage[s].fill_(float("nan"))
+    L.d_gate.fill_(float("nan"))
     L.forward()
     L.backward(d_out)
     torch.cuda.synchronize()

@@ -163,6 +163,63 @@ def main(out_dir: str, workload: str = "C2", path: str = "staged"):
     print("written under", PROFILES)
 
 
+def last_counters(path: str):
+    """kernel key -> {counter: value of its last profiled dispatch}."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.setdefault(kernel_key(r["Kernel_Name"]), {})[r["Counter_Name"]] = \
+                float(r["Counter_Value"])
+    return out
+
+
+def mfma_main(out_dir: str):
+    """MFMA utilisation of the GEMMs from three rocprofv3 passes:
+    mfma/c2 (MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16), mfma/c2l
+    (SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE) and mfma/c4 (MfmaUtil,
+    SQ_INSTS_VALU_MFMA_MOPS_F8) -> profiles/mfma_util.md.  Executed flops are
+    the MOPS counter x 512; the algorithmic flops are those bench.py uses."""
+    sys.path.insert(0, ROOT)
+    from bench import kernel_work  # noqa: E402  (the work model of the bench line)
+    from combine_router_top_expert_amd import synth  # noqa: E402
+    c2 = last_counters(os.path.join(out_dir, "c2", "c2_counter_collection.csv"))
+    c2l = last_counters(os.path.join(out_dir, "c2l", "c2l_counter_collection.csv"))
+    c4 = last_counters(os.path.join(out_dir, "c4", "c4_counter_collection.csv"))
+    R = 98304
+    lines = ["# MFMA utilisation of the expert GEMMs (mid-size layer, bf16 and MXFP8)", "",
+             "rocprofv3 counters of one profiled step (forward + backward in bf16; forward in",
+             "MXFP8).  `MfmaUtil` is rocprofv3's derived metric: MFMA busy cycles summed over",
+             "the SIMDs / (active cycles x SIMDs).  Executed flops are the MFMA op counter x 512,",
+             "against the algorithmic flops of the launch (R = 98304 routed rows); the excess is",
+             "the work on padding (rows past an expert's last tile, columns past I).  LDS bank",
+             "conflicts are the share of LDS-active cycles spent in conflicts.", "",
+             "Commands (from the repository root, OUT = gpurun_out/mfma):", "",
+             "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d OUT/c2 -o c2 -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE -f csv -d OUT/c2l -o c2l -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_MOPS_F6F4 -f csv -d OUT/c4 -o c4 -- python3 bench.py --workload C4 --steps 1 --warmup 1 --no-cpu-baseline",
+             "    python3 -m combine_router_top_expert_amd.profiling --mfma OUT", "",
+             "| kernel | trace name | MfmaUtil % | executed TFLOP | algorithmic TFLOP | padding % | LDS bank-conflict % |",
+             "|---|---|---|---|---|---|---|"]
+    w2 = synth.WORKLOADS["C2"]
+    w4 = synth.WORKLOADS["C4"]
+    for table, mops, w in ((c2, "SQ_INSTS_VALU_MFMA_MOPS_BF16", w2), (c4, "SQ_INSTS_VALU_MFMA_MOPS_F8", w4)):
+        for k, v in table.items():
+            name = TRACE_NAME.get(k)
+            if name is None or v.get("MfmaUtil", 0.0) == 0.0:
+                continue
+            kind, work = kernel_work(name, w, R)
+            ex = v.get(mops, 0.0) * 512
+            lds = c2l.get(k, {}) if w is w2 else {}
+            act = lds.get("SQ_LDS_IDX_ACTIVE", 0.0)
+            conf = 100.0 * lds["SQ_LDS_BANK_CONFLICT"] / act if act else None
+            lines.append(f"| {k} | {name} | {v['MfmaUtil']:.1f} | {ex / 1e12:.3f} | "
+                         f"{(work or 0) / 1e12:.3f} | {100.0 * (ex / work - 1) if work else 0:.1f} | "
+                         + (f"{conf:.1f}" if conf is not None else "-") + " |")
+    with open(os.path.join(PROFILES, "mfma_util.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("written", os.path.join(PROFILES, "mfma_util.md"))
+
+
 def recorded_traffic(kernel: str, workload: str, path: str):
     """HBM bytes of one launch of ``kernel`` as profiled, or None when the
     record is missing, was taken on another workload or path, or the kernel
@@ -185,4 +242,7 @@ def recorded_traffic(kernel: str, workload: str, path: str):
 
 
 if __name__ == "__main__":
-    main(*sys.argv[1:])
+    if len(sys.argv) > 1 and sys.argv[1] == "--mfma":
+        mfma_main(sys.argv[2])
+    else:
+        main(*sys.argv[1:])

@@ -196,8 +196,8 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
   }
   if (own_n == 0) return MOK_OK;
   if (!fill_table(&o, (const void* const*)out, cfg->S) || !topk_gate) return MOK_EINVAL;
-  for (int s = own_lo; s < own_lo + own_n; ++s)
-    if (!o.p[s] || !stg.p[s]) return MOK_EINVAL;
+  for (int s = own_lo; s < own_lo + own_n; ++s)  // empty sources may pass NULL buffers
+    if (cfg->T_src > 0 && (!o.p[s] || !stg.p[s])) return MOK_EINVAL;
   return launch_combine(prec, dest_row, topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k, own_lo,
                         own_n, cfg->R_cap, st, cfg->trace);
 }
@@ -225,7 +225,7 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   const int64_t per_src = (int64_t)cfg->T_src * cfg->k;
   const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
   for (int s = own_lo; s < own_lo + own_n; ++s)
-    if (!src_x[s]) return MOK_EINVAL;
+    if (cfg->T_src > 0 && !src_x[s]) return MOK_EINVAL;
   {
     SrcTable src;
     fill_table(&src, src_x, cfg->S);
@@ -304,7 +304,7 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   DstTable o;
   fill_table(&o, (const void* const*)out, cfg->S);
   for (int s = own_lo; s < own_lo + own_n; ++s)
-    if (!o.p[s] || !stg.p[s]) return MOK_EINVAL;
+    if (cfg->T_src > 0 && (!o.p[s] || !stg.p[s])) return MOK_EINVAL;
   return launch_combine(rprec, st->dest_row, st->topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k,
                         own_lo, own_n, cfg->R_cap, sm, tr);
 }

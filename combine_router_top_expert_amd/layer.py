@@ -41,8 +41,8 @@ class MoELayer:
         dev = self.device
         act = _dt(prec)
         N = S * T_src * k
-        self.topk_idx = torch.zeros(N, dtype=torch.int32, device=dev)
-        self.topk_gate = torch.zeros(N, dtype=torch.float32, device=dev)
+        self.topk_idx = torch.zeros(max(N, 1), dtype=torch.int32, device=dev)
+        self.topk_gate = torch.zeros(max(N, 1), dtype=torch.float32, device=dev)
         self.counts = torch.zeros(E_local, dtype=torch.int32, device=dev)
         self.offsets = torch.zeros(E_local + 1, dtype=torch.int32, device=dev)
         self.row_src = torch.zeros(max(R_cap, 1), dtype=torch.int32, device=dev)
@@ -68,7 +68,7 @@ class MoELayer:
                                 self.row_src, self.dest_row, self.h, self.ab)
         self.with_bwd = with_bwd
         if with_bwd and prec != "mxfp8":
-            self.d_gate = torch.zeros(N, dtype=torch.float32, device=dev)
+            self.d_gate = torch.zeros(max(N, 1), dtype=torch.float32, device=dev)
             self.dx_stage = [torch.zeros(T_src * k, d, dtype=act, device=dev) for _ in range(S)]
             self.d_x = [torch.zeros(T_src, d, dtype=act, device=dev) if own_lo <= s < own_lo + own_n
                         else None for s in range(S)]

@@ -46,7 +46,8 @@
  *   - Source buffers: S simulated source ranks, each a separate device buffer
  *     of T_src tokens, passed as a host array of S device pointers (up to
  *     MOK_MAX_SOURCES).  Item n = (s * T_src + t) * k + j names slot j of
- *     token t of source s.
+ *     token t of source s.  With T_src = 0 (an empty batch) the per-source
+ *     device pointers may be NULL; the state arrays must still be non-NULL.
  */
 #ifndef MOK_H
 #define MOK_H

@@ -366,6 +366,10 @@ BWD_CASES = {
     # about 6000 rows per expert: the weight gradients run split over 4096-row chunks
     "bf16_split_k": _small("C2", S=2, T_src=6000, d=128, E=4, k=2, I=128, own=[0],
                            local_experts=[0, 1, 2, 3]),
+    # the largest top-k the ABI takes (16): 16 slots per token through the
+    # combine, the gate-gradient group of the dx sum and the router backward
+    "bf16_k16": _small("C2", S=1, T_src=96, d=128, E=32, k=16, I=128, own=[0],
+                       local_experts=list(range(32))),
     # 256 (gate/up) and 128 (down) weight-gradient tiles per expert: whole experts
     # spread over all XCDs, most routed expert first
     "bf16_spread": _small("C2", S=2, T_src=32, d=4096, E=4, k=2, I=2048, own=[0, 1],
@@ -425,6 +429,28 @@ def test_layer_bwd(name):
     e_r = rel_err(L.dw_router.cpu().numpy(), dwr_ref)
     _log(f"  dx {e_dx:.3e} dW {e_w:.3e} dWr {e_r:.3e}")
     assert e_dx <= tol and e_w <= tol and e_r <= tol
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_layer_empty_batch(two_streams):
+    """No tokens at all (T_src = 0, so no routed rows): forward and backward
+    run, latch no error, and every weight gradient -- of experts that
+    received no rows -- is exactly zero."""
+    w = _small("C2", S=2, T_src=0, d=128, E=8, k=2, I=128, own=[0, 1],
+               local_experts=list(range(8)))
+    _log("empty batch", two_streams)
+    c = make_host_case(w)
+    L = _layer(c, two_streams=two_streams)
+    for t in (L.dw_gate, L.dw_up, L.dw_down, L.dw_router):
+        t.fill_(float("nan"))
+    d_out = [to_device(synth.gen_dout(w, s)[0], w.prec, DEV) for s in range(w.S)]
+    L.forward()
+    L.backward(d_out)
+    torch.cuda.synchronize()
+    L.check_status()
+    assert int(L.offsets[-1].item()) == 0
+    for t in (L.dw_gate, L.dw_up, L.dw_down, L.dw_router):
+        assert float(t.abs().max()) == 0.0
 
 
 def test_layer_rows_beyond_capacity_dropped():

@@ -241,69 +241,74 @@ __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
   __shared__ int s_e[kDxTokPerBlock][16];
   __shared__ int s_loc[kDxTokPerBlock][16];
   const int64_t n_tok = (int64_t)p.own_n * p.T_src;
-  const int64_t g0 = (int64_t)blockIdx.x * kDxTokPerBlock;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x, q = lane >> 4, j = lane & 15;
-    const int64_t gt = g0 + q;
-    const bool valid = q < kDxTokPerBlock && gt < n_tok && j < p.k;
-    float g = 0.0f, dg = 0.0f;
-    int e = 0, loc = 0;
-    if (valid) {
+  // workgroups stride over the token pairs (the grid may be capped so that
+  // the sum runs thin beside a GEMM on another stream)
+  for (int64_t g0 = (int64_t)blockIdx.x * kDxTokPerBlock; g0 < n_tok;
+       g0 += (int64_t)gridDim.x * kDxTokPerBlock) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x, q = lane >> 4, j = lane & 15;
+      const int64_t gt = g0 + q;
+      const bool valid = q < kDxTokPerBlock && gt < n_tok && j < p.k;
+      float g = 0.0f, dg = 0.0f;
+      int e = 0, loc = 0;
+      if (valid) {
+        const int s = p.own_lo + (int)(gt / p.T_src);
+        const int t = (int)(gt % p.T_src);
+        const int64_t n = ((int64_t)s * p.T_src + t) * p.k + j;
+        // present: a local row, or a remote slot whose gate gradient and dx row
+        // the GPU holding that expert wrote here; absent: dropped beyond R_cap
+        loc = p.dest_row[n] < p.R_cap;
+        dg = loc ? p.d_gate[n] : 0.0f;
+        g = p.topk_gate[n];
+        e = p.topk_idx[n];
+      }
+      float m = 0.0f;
+      for (int i = 0; i < p.k; ++i)
+        m = __builtin_fmaf(__shfl(g, (lane & ~15) + i, 64), __shfl(dg, (lane & ~15) + i, 64), m);
+      if (valid) {
+        const float dz = g * (dg - m);
+        s_dz[q][j] = dz;
+        s_e[q][j] = e;
+        s_loc[q][j] = loc;
+        p.dz[gt * p.k + j] = dz;
+      }
+    }
+    __syncthreads();
+    constexpr int U = 16 / sizeof(T);
+    const T* wr = reinterpret_cast<const T*>(p.w_router);
+    for (int q = 0; q < kDxTokPerBlock; ++q) {
+      const int64_t gt = g0 + q;
+      if (gt >= n_tok) break;
       const int s = p.own_lo + (int)(gt / p.T_src);
       const int t = (int)(gt % p.T_src);
-      const int64_t n = ((int64_t)s * p.T_src + t) * p.k + j;
-      // present: a local row, or a remote slot whose gate gradient and dx row
-      // the GPU holding that expert wrote here; absent: dropped beyond R_cap
-      loc = p.dest_row[n] < p.R_cap;
-      dg = loc ? p.d_gate[n] : 0.0f;
-      g = p.topk_gate[n];
-      e = p.topk_idx[n];
-    }
-    float m = 0.0f;
-    for (int i = 0; i < p.k; ++i)
-      m = __builtin_fmaf(__shfl(g, (lane & ~15) + i, 64), __shfl(dg, (lane & ~15) + i, 64), m);
-    if (valid) {
-      const float dz = g * (dg - m);
-      s_dz[q][j] = dz;
-      s_e[q][j] = e;
-      s_loc[q][j] = loc;
-      p.dz[gt * p.k + j] = dz;
-    }
-  }
-  __syncthreads();
-  constexpr int U = 16 / sizeof(T);
-  const T* wr = reinterpret_cast<const T*>(p.w_router);
-  for (int q = 0; q < kDxTokPerBlock; ++q) {
-    const int64_t gt = g0 + q;
-    if (gt >= n_tok) return;
-    const int s = p.own_lo + (int)(gt / p.T_src);
-    const int t = (int)(gt % p.T_src);
-    const T* stg = reinterpret_cast<const T*>(p.dx_stage.p[s]) + (size_t)t * p.k * p.d;
-    T* o = reinterpret_cast<T*>(p.d_x.p[s]) + (size_t)t * p.d;
-    for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
-      float acc[U];
+      const T* stg = reinterpret_cast<const T*>(p.dx_stage.p[s]) + (size_t)t * p.k * p.d;
+      T* o = reinterpret_cast<T*>(p.d_x.p[s]) + (size_t)t * p.d;
+      for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
+        float acc[U];
 #pragma unroll
-      for (int i = 0; i < U; ++i) acc[i] = 0.0f;
-      for (int j = 0; j < p.k; ++j) {
-        if (!s_loc[q][j]) continue;
-        uint4 v = ld16(stg + (size_t)j * p.d + u * U);
-        const T* e = reinterpret_cast<const T*>(&v);
+        for (int i = 0; i < U; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < p.k; ++j) {
+          if (!s_loc[q][j]) continue;
+          uint4 v = ld16(stg + (size_t)j * p.d + u * U);
+          const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-        for (int i = 0; i < U; ++i) acc[i] += to_f32<T>(e[i]);
+          for (int i = 0; i < U; ++i) acc[i] += to_f32<T>(e[i]);
+        }
+        for (int j = 0; j < p.k; ++j) {
+          const float dz = s_dz[q][j];
+          uint4 v = ld16(wr + (size_t)s_e[q][j] * p.d + u * U);
+          const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+          for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz, to_f32<T>(e[i]), acc[i]);
+        }
+        uint4 ov;
+        T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+        for (int i = 0; i < U; ++i) oe[i] = from_f32<T>(acc[i]);
+        st16(o + u * U, ov);
       }
-      for (int j = 0; j < p.k; ++j) {
-        const float dz = s_dz[q][j];
-        uint4 v = ld16(wr + (size_t)s_e[q][j] * p.d + u * U);
-        const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-        for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(dz, to_f32<T>(e[i]), acc[i]);
-      }
-      uint4 ov;
-      T* oe = reinterpret_cast<T*>(&ov);
-#pragma unroll
-      for (int i = 0; i < U; ++i) oe[i] = from_f32<T>(acc[i]);
-      st16(o + u * U, ov);
     }
+    __syncthreads();  // the slot values of this pair are read before the next pair's
   }
 }
 
@@ -432,8 +437,11 @@ mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
   trace_mark(p.tr, "start", aux);
   const int64_t n_own = (int64_t)p.own_n * p.T_src;
   const int N_own = (int)(n_own * p.k);
+  const int cus = device_cus();
   if (p.R_cap > 0) {
-    mok_status rc = launch_gather_t(p, p.x_perm, aux);
+    // one workgroup per CU: the copy runs thin beside dh (mid-size layer: dh
+    // 870 -> 800 us, step 7.31 -> 7.27 ms; half that made it outlast dx)
+    mok_status rc = launch_gather_t(p, p.x_perm, aux, cus);
     if (rc != MOK_OK) return rc;
     trace_mark(p.tr, "bwd_regather_x", aux);
   }
@@ -451,8 +459,13 @@ mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
   MOK_HIP_CHECK(hipStreamWaitEvent(aux, dx_pushed, 0));
   trace_mark(p.tr, "start", aux);  // the wait is not the dx sum's time
   if (n_own > 0) {
-    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)((n_own + kDxTokPerBlock - 1) / kDxTokPerBlock)),
-                       dim3(kThreads), 0, aux, p);
+    // one workgroup per CU, striding over the tokens: the sum runs thin
+    // beside the gate/up weight gradient instead of in a burst (mid-size
+    // layer: that GEMM 1.54 -> 1.51 ms, step 7.17 -> 7.15 ms; 64 workgroups
+    // made the sum outlast the GEMM)
+    int64_t blocks = (n_own + kDxTokPerBlock - 1) / kDxTokPerBlock;
+    if (cus > 0 && blocks > cus) blocks = cus;
+    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, aux, p);
     trace_mark(p.tr, "bwd_dx_sum_router", aux);
   }
   if (p.dw_router) {

@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void expert_order_kernel(const int32_t* o
   }
 }
 
-mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream) {
+mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks) {
   if (p.R_cap == 0) return MOK_OK;
   GatherTArgs g;
   g.src = p.src_x;
@@ -505,7 +505,13 @@ mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream) {
   g.k = p.k;
   const int tiles = (p.R_cap + 63) / 64 + p.E_local;  // bound of the 64-row tiles
   const int groups = (tiles + 3) / 4;
-  const int gx = groups < 256 ? groups : 256;
+  int gx = groups < 256 ? groups : 256;
+  // a cap on the workgroups (the copy then runs thin beside a GEMM on
+  // another stream); workgroups stride over the tile groups either way
+  if (max_blocks > 0) {
+    const int cap = max_blocks / (p.d / 64) > 0 ? max_blocks / (p.d / 64) : 1;
+    if (gx > cap) gx = cap;
+  }
   hipLaunchKernelGGL(gather_t_kernel, dim3((unsigned)gx, (unsigned)(p.d / 64)), dim3(kThreads), 0,
                      stream, g);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;

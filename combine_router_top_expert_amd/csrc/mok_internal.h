@@ -122,7 +122,7 @@ mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
 inline int64_t xt_ld(int R_cap, int E_local) {
   return ((int64_t)R_cap + 63) / 64 * 64 + 64 * (int64_t)E_local;
 }
-mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream);
+mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks = 0);
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
                                  hipEvent_t before_wgrad = nullptr, hipEvent_t after_dx = nullptr);
 size_t wgrad_partial_bytes(int R_cap, int d, int I);

@@ -307,7 +307,7 @@ def main():
                          "(the reference for HBM bandwidth and for scaling byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 

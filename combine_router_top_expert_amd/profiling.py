@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the layer's kernels.
 
 ``python -m combine_router_top_expert_amd.profiling OUT_DIR`` reads, from
-OUT_DIR (a gpurun output folder):
+OUT_DIR (the folder the rocprofv3 runs below wrote to):
   kt/kt_kernel_stats.csv                  rocprofv3 --kernel-trace --stats of bench.py
   pf/pf_counter_collection.csv            rocprofv3 --pmc FETCH_SIZE of bench.py
   pw/pw_counter_collection.csv            rocprofv3 --pmc WRITE_SIZE of bench.py
@@ -121,7 +121,7 @@ def main(out_dir: str, workload: str = "C2", path: str = "staged"):
              "(`FETCH_SIZE`, then `WRITE_SIZE`, in KiB per dispatch), each scaled by what the",
              f"same counter reads for a plain 1 GiB device copy: FETCH_SIZE x {fs:.3f},",
              f"WRITE_SIZE x {ws:.3f}.  Values are for the last profiled launch of each kernel.", "",
-             "Commands (from the repository root, output under OUT = gpurun_out):", "",
+             "Commands (from the repository root; OUT = the output folder):", "",
              "    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pf -o pf -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
              "    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pw -o pw -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
              "    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/cf -o cf -- python3 bench.py --hbm-copy-gib 1 --steps 3 --warmup 1",
@@ -193,7 +193,7 @@ def mfma_main(out_dir: str):
              "against the algorithmic flops of the launch (R = 98304 routed rows); the excess is",
              "the work on padding (rows past an expert's last tile, columns past I).  LDS bank",
              "conflicts are the share of LDS-active cycles spent in conflicts.", "",
-             "Commands (from the repository root, OUT = gpurun_out/mfma):", "",
+             "Commands (from the repository root; OUT = the output folder):", "",
              "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d OUT/c2 -o c2 -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
              "    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE -f csv -d OUT/c2l -o c2l -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
              "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_MOPS_F6F4 -f csv -d OUT/c4 -o c4 -- python3 bench.py --workload C4 --steps 1 --warmup 1 --no-cpu-baseline",

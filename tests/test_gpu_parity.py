@@ -50,6 +50,8 @@ ROUTE_CASES = {
     "c2shape": _small("C2", S=1, T_src=1000, own=[0]),
     "c3shape": _small("C3", S=1, T_src=100, own=[0], local_experts=[0]),
     "e512k16": _small("C2", S=1, T_src=33, d=256, E=512, k=16, I=64, own=[0], local_experts=[0]),
+    # two experts per lane, a ragged token count across two sources
+    "e128": _small("C2", S=2, T_src=777, d=256, E=128, k=4, I=64, own=[0, 1], local_experts=[0]),
 }
 
 

@@ -1,0 +1,45 @@
+"""Host-side logic of the measurement tools (no GPU): every kernel the
+profiles name is defined in exactly one source file (its traffic record is
+hashed against that file), the traffic record is well-formed, and bench.py
+has a work model for every GEMM and streaming kernel the library traces."""
+import json
+import os
+import re
+
+from combine_router_top_expert_amd import profiling
+from combine_router_top_expert_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_every_profiled_kernel_has_one_source():
+    for key in profiling.TRACE_NAME:
+        h = profiling.kernel_source_hash(key)
+        assert h is not None and re.fullmatch(r"[0-9a-f]{64}", h), key
+
+
+def test_traffic_record_well_formed():
+    rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))
+    assert rec["workload"] == "C2" and rec["path"] == "staged"
+    assert rec["fetch_factor"] > 0 and rec["write_factor"] > 0
+    names = set(profiling.TRACE_NAME.values())
+    for name, k in rec["kernels"].items():
+        assert name in names, name
+        assert k["bytes"] == k["read_bytes"] + k["write_bytes"] >= 0
+        assert k["source_sha256"] is None or re.fullmatch(r"[0-9a-f]{64}", k["source_sha256"])
+
+
+def test_bench_work_model_covers_the_traced_kernels():
+    import bench
+    traced = set()
+    for f in os.listdir(os.path.join(ROOT, "combine_router_top_expert_amd", "csrc")):
+        src = open(os.path.join(ROOT, "combine_router_top_expert_amd", "csrc", f)).read()
+        traced |= set(re.findall(r'trace_mark\([^,]+,\s*"(\w+)"', src))
+    traced.discard("start")
+    w = synth.WORKLOADS["C2"]
+    modeled = {n for n in traced if bench.kernel_work(n, w, 98304)[0] is not None}
+    # the expert GEMMs and the HBM-bound copies must be priced against a roofline
+    for n in ("ffn1_gate_up_swiglu", "ffn2_down", "bwd_dh", "bwd_dx_push", "bwd_wgrad_gate_up",
+              "bwd_wgrad_down", "combine", "bwd_reverse_combine_pull", "bwd_swiglu",
+              "bwd_regather_x", "bwd_dx_sum_router", "route"):
+        assert n in traced and n in modeled, n

@@ -111,6 +111,15 @@ def copy_factor(path: str, expect_kib: float) -> float:
 
 
 def main(out_dir: str, workload: str = "C2", path: str = "staged"):
+    # the traffic record is written only from counter passes of this
+    # folder (run post-processing before any source changes: the record
+    # takes the kernels' current source hashes)
+    if os.path.exists(os.path.join(out_dir, "pf", "pf_counter_collection.csv")):
+        traffic_main(out_dir, workload, path)
+    trace_main(out_dir)
+
+
+def traffic_main(out_dir: str, workload: str, path: str):
     fs = copy_factor(os.path.join(out_dir, "cf", "cf_counter_collection.csv"), 1 << 20)
     ws = copy_factor(os.path.join(out_dir, "cw", "cw_counter_collection.csv"), 1 << 20)
     fetch = counters(os.path.join(out_dir, "pf", "pf_counter_collection.csv"))
@@ -143,6 +152,9 @@ def main(out_dir: str, workload: str = "C2", path: str = "staged"):
     with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
         json.dump({"source_sha256": source_hash(), "workload": workload, "path": path,
                    "fetch_factor": fs, "write_factor": ws, "kernels": traffic}, f, indent=1)
+
+
+def trace_main(out_dir: str):
     stats = os.path.join(out_dir, "kt", "kt_kernel_stats.csv")
     if os.path.exists(stats):
         rows = list(csv.DictReader(open(stats)))

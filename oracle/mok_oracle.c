@@ -185,9 +185,18 @@ void mokref_logits(int64_t T, int64_t d, int64_t E, const float* x, const float*
     }
 }
 
-/* Top-k selection.  Reading: order by logit descending, lower expert id first
- * on equal logits; slot j = 0 holds the largest.  Picks the best unselected
- * expert k times. */
+/* Does logit a (expert ea) rank before logit b (expert eb)?  Reading: larger
+ * logit first, lower expert id first on equal logits.  The pages say nothing
+ * of non-numbers; here a NaN logit ranks after every number (-inf included)
+ * and NaNs rank among themselves by expert id, so that every token still gets
+ * k distinct valid experts. */
+static int ranks_before(double a, int64_t ea, double b, int64_t eb) {
+  if (isnan(a) || isnan(b)) return isnan(b) && (!isnan(a) || ea < eb);
+  return a > b || (a == b && ea < eb);
+}
+
+/* Top-k selection: slot j = 0 holds the first expert in the order above.
+ * Picks the first unselected expert k times. */
 void mokref_topk(int64_t T, int64_t E, int64_t k, const double* z, int32_t* idx) {
   char* used = (char*)malloc((size_t)E);
   for (int64_t t = 0; t < T; ++t) {
@@ -196,7 +205,7 @@ void mokref_topk(int64_t T, int64_t E, int64_t k, const double* z, int32_t* idx)
       int64_t best = -1;
       for (int64_t e = 0; e < E; ++e) {
         if (used[e]) continue;
-        if (best < 0 || z[t * E + e] > z[t * E + best]) best = e; /* strict: lower id wins ties */
+        if (best < 0 || ranks_before(z[t * E + e], e, z[t * E + best], best)) best = e;
       }
       used[best] = 1;
       idx[t * k + j] = (int32_t)best;
@@ -205,26 +214,19 @@ void mokref_topk(int64_t T, int64_t E, int64_t k, const double* z, int32_t* idx)
   free(used);
 }
 
-/* Gates: softmax over all E experts (float64), renormalised over the k chosen
- * ones, so that the k gates of a token sum to 1. */
+/* Gates: softmax over all E experts renormalised over the k chosen ones.  The
+ * renormalisation cancels the unchosen experts' terms, so this is the softmax
+ * of the chosen logits, computed as such in float64:
+ * g_j = exp(z_j - z_0) / sum_i exp(z_i - z_0), with z_0 the slot-0 logit.  A
+ * NaN among the unchosen logits then leaves the gates alone. */
 void mokref_gates(int64_t T, int64_t E, int64_t k, const double* z, const int32_t* idx,
                   double* g) {
-  double* p = (double*)malloc(sizeof(double) * (size_t)E);
   for (int64_t t = 0; t < T; ++t) {
-    double zmax = z[t * E];
-    for (int64_t e = 1; e < E; ++e)
-      if (z[t * E + e] > zmax) zmax = z[t * E + e];
+    const double z0 = z[t * E + idx[t * k]];
     double tot = 0.0;
-    for (int64_t e = 0; e < E; ++e) {
-      p[e] = exp(z[t * E + e] - zmax);
-      tot += p[e];
-    }
-    for (int64_t e = 0; e < E; ++e) p[e] /= tot;
-    double sel = 0.0;
-    for (int64_t j = 0; j < k; ++j) sel += p[idx[t * k + j]];
-    for (int64_t j = 0; j < k; ++j) g[t * k + j] = p[idx[t * k + j]] / sel;
+    for (int64_t j = 0; j < k; ++j) tot += exp(z[t * E + idx[t * k + j]] - z0);
+    for (int64_t j = 0; j < k; ++j) g[t * k + j] = exp(z[t * E + idx[t * k + j]] - z0) / tot;
   }
-  free(p);
 }
 
 /* Route T tokens: logits, top-k, gates.  z may be NULL (scratch allocated). */

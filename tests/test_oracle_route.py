@@ -107,3 +107,42 @@ def test_route_composes_logits_topk_gates():
         order = np.argsort(-z[t], kind="stable")[:3]
         assert idx[t].tolist() == order.tolist()
         np.testing.assert_allclose(g[t], softmax(z[t][order]), rtol=1e-5)
+
+
+def _lexsort_topk(z, k):
+    """Independent ordering: numbers before NaNs, larger logit first, lower
+    id first among equals (numpy lexsort: the last key is the primary one)."""
+    E = z.shape[0]
+    nan = np.isnan(z)
+    negz = np.where(nan, 0.0, -z)
+    return np.lexsort((np.arange(E), negz, nan))[:k]
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (8, 8), (7, 3), (16, 5)])
+def test_topk_nan_ranks_after_every_number(E, k):
+    """Reading (the pages say nothing of non-numbers): a NaN logit ranks
+    after every number, -inf included; NaNs rank among themselves by id."""
+    rng = np.random.default_rng(40 + E + k)
+    z = rng.integers(-2, 3, size=(400, E)).astype(np.float64)
+    z[rng.random(z.shape) < 0.25] = np.nan
+    z[rng.random(z.shape) < 0.1] = -np.inf
+    z[:5] = np.nan                    # whole rows of NaN
+    idx = oracle.topk(z, k)
+    for t in range(z.shape[0]):
+        np.testing.assert_array_equal(idx[t], _lexsort_topk(z[t], k))
+    assert np.all(idx[:5] == np.arange(k))   # an all-NaN row takes the k lowest ids
+
+
+def test_gates_ignore_nan_among_unchosen_logits():
+    """Gates are the softmax of the chosen logits: a NaN logit of an unchosen
+    expert leaves them finite; an all-NaN row gives NaN gates."""
+    rng = np.random.default_rng(3)
+    z = rng.normal(size=(50, 8))
+    z[:, 5] = np.nan
+    idx = oracle.topk(z, 3)
+    assert not np.any(idx == 5)
+    g = oracle.gates(z, idx)
+    for t in range(50):
+        np.testing.assert_allclose(g[t], softmax(z[t, idx[t]]), rtol=1e-13, atol=0)
+    zn = np.full((2, 8), np.nan)
+    assert np.all(np.isnan(oracle.gates(zn, oracle.topk(zn, 2))))

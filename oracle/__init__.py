@@ -8,7 +8,10 @@ never do; the two implementations share no code.  ``build()`` compiles
 Every function here is a thin numpy wrapper over one C function of
 ``mok_oracle.c``; each C function cites the passage of the pages it follows.
 The composite helpers at the bottom (``route``, ``layout``, ``layer_fwd`` ...)
-only chain those calls in the layer's order.
+only chain those calls in the layer's order.  One function,
+``ffn_rows_exact``, is written with numpy instead: the exact expert FFN of
+many rows, with numpy's float64 matrix product as its contraction step, for
+checks at sizes where the row-by-row C loops are too slow.
 """
 from __future__ import annotations
 
@@ -79,6 +82,8 @@ def _declare(L):
                                     _p, _p, _p]
     L.mokref_expert_wgrad.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
     L.mokref_router_wgrad.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p]
+    L.mokref_expert_wgrad_cols.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p,
+                                           _p]
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -319,3 +324,54 @@ def router_wgrad(tok_x, topk_idx, dz, E):
     dwr = np.empty((E, d))
     lib().mokref_router_wgrad(n, d, E, k, _ptr(tok_x), _ptr(topk_idx), _ptr(dz), _ptr(dwr))
     return dwr
+
+
+def expert_wgrad_cols(rows_x, rows_g, rows_dout, wg, wu, wd, sel):
+    """Columns sel of one expert's weight gradients -> (dW_gate[sel] [n_sel, d],
+    dW_up[sel] [n_sel, d], dW_down[:, sel] [d, n_sel]) float64."""
+    rows_x = _c(rows_x, np.float32)
+    rows_g = _c(rows_g, np.float64)
+    rows_dout = _c(rows_dout, np.float32)
+    wg = _c(wg, np.float32)
+    wu = _c(wu, np.float32)
+    wd = _c(wd, np.float32)
+    sel = _c(sel, np.int32)
+    n, d = rows_x.shape
+    I = wg.shape[0]
+    q = sel.shape[0]
+    dwg = np.empty((q, d))
+    dwu = np.empty((q, d))
+    dwd = np.empty((d, q))
+    lib().mokref_expert_wgrad_cols(n, d, I, _ptr(rows_x), _ptr(rows_g), _ptr(rows_dout), _ptr(wg),
+                                   _ptr(wu), _ptr(wd), q, _ptr(sel), _ptr(dwg), _ptr(dwu),
+                                   _ptr(dwd))
+    return dwg, dwu, dwd
+
+
+def ffn_rows_exact(rows_x, wg, wu, wd):
+    """Exact expert FFN of many rows of one expert, float64 (no roundings):
+    a = x W_gate^T, b = x W_up^T, h = silu(a) * b, y = h W_down^T, with
+    silu(a) = a / (1 + exp(-a)).  The three contractions are numpy matrix
+    products; nothing else is blocked or reordered.  -> y [n, d]."""
+    x = np.asarray(rows_x, np.float64)
+    a = x @ np.asarray(wg, np.float64).T
+    b = x @ np.asarray(wu, np.float64).T
+    h = a / (1.0 + np.exp(-a)) * b
+    return h @ np.asarray(wd, np.float64).T
+
+
+def router_dz(topk_idx, gate, d_gate):
+    """dz [n, k] of many tokens from their gates and gate gradients (the
+    router backward of each token, without the input-gradient part)."""
+    topk_idx = _c(topk_idx, np.int32)
+    gate = _c(gate, np.float64)
+    d_gate = _c(d_gate, np.float64)
+    n, k = topk_idx.shape
+    dz = np.empty((n, k))
+    L = lib()
+    rowb = k * 8
+    for t in range(n):
+        L.mokref_router_bwd_token(0, k, topk_idx.ctypes.data + t * k * 4,
+                                  gate.ctypes.data + t * rowb, d_gate.ctypes.data + t * rowb,
+                                  None, dz.ctypes.data + t * rowb, None)
+    return dz

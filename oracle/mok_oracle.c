@@ -500,6 +500,47 @@ void mokref_expert_wgrad(int64_t n, int64_t d, int64_t I, const float* rows_x,
   free(dy); free(h); free(da); free(db);
 }
 
+/* Selected columns of one expert's weight gradients (float64), for checks at
+ * sizes where the whole gradient is too slow: the same sums as
+ * mokref_expert_wgrad, restricted to the intermediate indices sel[0..n_sel):
+ *   dwg_sel[q][c] = dW_gate[sel[q]][c], dwu_sel[q][c] = dW_up[sel[q]][c],
+ *   dwd_sel[c][q] = dW_down[c][sel[q]],
+ * rows in the order given.  Per row only a, b, h, dh, da, db at the selected
+ * indices are formed (dy = g dout as in the row backward). */
+void mokref_expert_wgrad_cols(int64_t n, int64_t d, int64_t I, const float* rows_x,
+                              const double* rows_g, const float* rows_dout, const float* wg,
+                              const float* wu, const float* wd, int64_t n_sel,
+                              const int32_t* sel, double* dwg_sel, double* dwu_sel,
+                              double* dwd_sel) {
+  double* dy = (double*)malloc(sizeof(double) * (size_t)d);
+  memset(dwg_sel, 0, sizeof(double) * (size_t)(n_sel * d));
+  memset(dwu_sel, 0, sizeof(double) * (size_t)(n_sel * d));
+  memset(dwd_sel, 0, sizeof(double) * (size_t)(n_sel * d));
+  for (int64_t r = 0; r < n; ++r) {
+    const float* x = rows_x + r * d;
+    for (int64_t c = 0; c < d; ++c) dy[c] = rows_g[r] * (double)rows_dout[r * d + c];
+    for (int64_t q = 0; q < n_sel; ++q) {
+      const int64_t i = sel[q];
+      double a = 0.0, b = 0.0, dh = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        a += (double)x[c] * (double)wg[i * d + c];
+        b += (double)x[c] * (double)wu[i * d + c];
+      }
+      for (int64_t c = 0; c < d; ++c) dh += dy[c] * (double)wd[c * I + i];
+      const double h = silu(a) * b;
+      const double sg = sigmoid(a);
+      const double da = dh * b * sg * (1.0 + a * (1.0 - sg));
+      const double db = dh * silu(a);
+      for (int64_t c = 0; c < d; ++c) {
+        dwg_sel[q * d + c] += da * (double)x[c];
+        dwu_sel[q * d + c] += db * (double)x[c];
+        dwd_sel[c * n_sel + q] += dy[c] * h;
+      }
+    }
+  }
+  free(dy);
+}
+
 /* Router weight gradient over the tokens routed here: dWr[e] = sum_t dz_t,e x_t
  * with dz from mokref_router_bwd_token (tokens in the order given).
  * dwr: [E, d] out (zeroed here). */

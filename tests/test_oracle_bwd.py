@@ -187,3 +187,54 @@ def test_share_with_peer_slots_equals_all_local(mine):
     np.testing.assert_array_equal(dz_a, dz_all)
     np.testing.assert_array_equal(dx_a, dx_all)
     assert remote.any() and (~remote).any()
+
+
+def test_expert_wgrad_cols_equal_the_whole_gradient_at_those_columns():
+    """The sampled-column weight gradients are the same sums as the whole
+    gradients (pinned by finite differences above), restricted to the
+    selected intermediate indices."""
+    rng = np.random.default_rng(21)
+    n, d, I = 37, 24, 20
+    x = rng.normal(size=(n, d)).astype(np.float32)
+    g = rng.random(n)
+    dout = rng.normal(size=(n, d)).astype(np.float32)
+    wg = (rng.normal(size=(I, d)) / 5).astype(np.float32)
+    wu = (rng.normal(size=(I, d)) / 5).astype(np.float32)
+    wd = (rng.normal(size=(d, I)) / 5).astype(np.float32)
+    dwg, dwu, dwd = oracle.expert_wgrad(x, g, dout, wg, wu, wd)
+    sel = np.array([0, 7, 19, 3], np.int32)
+    cg, cu, cd = oracle.expert_wgrad_cols(x, g, dout, wg, wu, wd, sel)
+    np.testing.assert_allclose(cg, dwg[sel], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cu, dwu[sel], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cd, dwd[:, sel], rtol=1e-12, atol=1e-14)
+
+
+def test_ffn_rows_exact_matches_the_row_oracle():
+    """The matrix-product form of the exact FFN gives the row-by-row C
+    oracle's exact y (float64, summation order aside)."""
+    rng = np.random.default_rng(22)
+    n, d, I = 19, 64, 96
+    x = rng.normal(size=(n, d)).astype(np.float32)
+    wg = (rng.normal(size=(I, d)) / 8).astype(np.float32)
+    wu = (rng.normal(size=(I, d)) / 8).astype(np.float32)
+    wd = (rng.normal(size=(d, I)) / 10).astype(np.float32)
+    y = oracle.ffn_rows_exact(x, wg, wu, wd)
+    for r in range(n):
+        _, _, _, yr = oracle.ffn_row(x[r], wg, wu, wd, "exact")
+        np.testing.assert_allclose(y[r], yr, rtol=1e-11, atol=1e-13)
+
+
+def test_router_dz_matches_the_token_backward():
+    rng = np.random.default_rng(23)
+    n, k, E, d = 30, 3, 9, 16
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(n)]).astype(np.int32)
+    g = rng.random((n, k))
+    g /= g.sum(1, keepdims=True)
+    dg = rng.normal(size=(n, k))
+    wr = rng.normal(size=(E, d)).astype(np.float32)
+    dz = oracle.router_dz(idx, g, dg)
+    for t in range(n):
+        ref, _ = oracle.router_bwd_token(idx[t], g[t], dg[t], wr)
+        np.testing.assert_array_equal(dz[t], ref)
+    # closed form: sum_j dz_j = sum_j g_j dg_j (1 - sum_i g_i) = 0 for gates summing to 1
+    assert np.all(np.abs(dz.sum(1)) < 1e-12)

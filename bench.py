@@ -1,23 +1,27 @@
 """Benchmark of the MoE layer hot path on one MI355X.
 
-One step = the whole layer, forward and backward, over one batch of synthetic
-input resident in HBM: route -> layout -> gather -> SwiGLU grouped GEMMs ->
-push + final weighted combine, then reverse-combine pull -> dgrad GEMMs with
-the SwiGLU derivative -> wgrad GEMMs -> reverse-dispatch push + router
-backward.  Workload (default): the mid-size layer, T = 16384 tokens in 8
-source buffers of 2048, d = 2048, E = 64 experts all local, top-6, SwiGLU
-I = 1408, bf16 with fp32 accumulation, balanced routing.
+One step = the whole layer over one batch of synthetic input resident in HBM:
+route -> layout -> gather -> SwiGLU grouped GEMMs -> push + final weighted
+combine, then (where the workload has a backward pass) reverse-combine pull
+-> dgrad GEMMs with the SwiGLU derivative -> wgrad GEMMs -> reverse-dispatch
+push + router backward.
 
-Other workloads (--workload): C3, one GPU's share of a 256-expert layer
-(own 4096 tokens, 8 local experts, Zipf 1.2 skew), forward + backward; C4,
-the mid-size layer in MXFP8, forward only (the MXFP8 layer has no backward
-pass); C5, the mid-size layer with Zipf 1.2 skew, forward + backward.
+Workloads (--workload; default: all four, one JSON line each, the headline
+last):
+  C2  the mid-size layer: T = 16384 tokens in 8 source buffers of 2048,
+      d = 2048, E = 64 experts all local, top-6, SwiGLU I = 1408, bf16 with
+      fp32 accumulation, balanced routing; forward + backward;
+  C4  the same layer in MXFP8, forward only (the MXFP8 layer has no backward);
+  C5  the mid-size layer with Zipf 1.2 skew, forward + backward;
+  C3  one GPU's share of a 256-expert layer (own 4096 tokens of 32 source
+      buffers, 8 local experts, d = 7168, I = 2048, top-8, Zipf 1.2 skew),
+      forward + backward -- the largest configuration that one GPU holds, and
+      the headline (printed last).
 
-Prints ONE JSON line on stdout: layer tokens/s (forward + backward), the
-forward-only rate, per-kernel average times (HIP events recorded by the
-library between its kernels on the layer's stream, during the timed steps),
-the roofline of the dominant kernel, and the CPU oracle's rate on a bounded
-sample of the same workload.
+Each JSON line: layer tokens/s, the forward-only rate, per-kernel average
+times (HIP events recorded by the library between its kernels on the
+layer's streams, during the timed steps), the roofline of the dominant
+kernel, and the CPU oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -44,9 +48,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(name, w, R):
-    """Algorithmic work of one launch: ('mfma', flops), ('alu', flops) or ('hbm', bytes)."""
+def kernel_work(name, w, R, T_pull=None):
+    """Algorithmic work of one launch: ('mfma', flops), ('alu', flops) or ('hbm', bytes).
+    R: routed rows computed here; T_pull: tokens with at least one of them
+    (the tokens whose upstream gradient the reverse-combine pull reads)."""
     d, I, k = w.d, w.I, w.k
+    if T_pull is None:
+        T_pull = R
     T = len(w.own) * w.T_src  # tokens combined / summed here (own sources)
     eb = 2 if w.prec != "f32" else 4
     gemm = {
@@ -70,7 +78,8 @@ def kernel_work(name, w, R):
         "gather": R * d * 2.0 + (R * d * (1 + 1 / 32) if w.prec == "mxfp8" else R * d * eb),
         "bwd_regather_x": 2.0 * R * d * eb,
         "combine": (T * k * d + T * d) * eb,              # read k pushed rows, write out
-        "bwd_reverse_combine_pull": 3.0 * R * d * eb,     # read dout + y rows, write dy
+        # read each pulled token's dout once and every row's pushed y, write dy
+        "bwd_reverse_combine_pull": (T_pull + 2.0 * R) * d * eb,
         "bwd_swiglu": 5.0 * R * I * eb,                   # read dh, a, b; write da, db
         "bwd_dx_sum_router": (T * k * d + T * d) * eb,    # read k dx rows, write dX
     }
@@ -130,6 +139,7 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     torch.cuda.synchronize()
     L.check_status()
     R = int(L.offsets[-1].item())
+    T_pull = int(torch.unique(L.row_src[:R].long() // w.k).numel()) if R > 0 else 0
 
     trace = Trace(capacity=64 * (args.steps + 1))
     trace.attach(L.cfg)
@@ -158,9 +168,9 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps}
                for n, v in per_kernel.items()}
     # dominant kernel: largest time per step among kernels with a work model
-    modeled = [n for n in per_kernel if kernel_work(n, w, R)[0] is not None]
+    modeled = [n for n in per_kernel if kernel_work(n, w, R, T_pull)[0] is not None]
     dom = max(modeled, key=lambda n: sum(per_kernel[n]))
-    kind, work = kernel_work(dom, w, R)
+    kind, work = kernel_work(dom, w, R, T_pull)
     avg_s = float(np.mean(per_kernel[dom])) * 1e-3
     if kind == "alu":
         achieved = work / avg_s / 1e12
@@ -182,7 +192,7 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     roof["traffic"] = recorded_traffic(dom, w.name, "ring" if args.ring_mib else "staged")
     # per-kernel roofline fractions, for the record
     for n, v in kernels.items():
-        kd, wk = kernel_work(n, w, R)
+        kd, wk = kernel_work(n, w, R, T_pull)
         if kd in ("mfma", "mfma_fp8"):
             v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
             v["frac_mfma_peak"] = v["tflops"] / (PEAK_FP8_TFLOPS if kd == "mfma_fp8"
@@ -263,6 +273,7 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
                                f"{'Zipf %.1f skew' % w.zipf_s if w.zipf_s else 'balanced routing'}; "
                                f"step = {'forward + backward' if has_bwd else 'forward'}",
                    "routed_rows": R,
+                   "pulled_tokens": T_pull,
                    "backward_streams": 2 if (has_bwd and L.aux is not None) else 1,
                    "path": ("ring %d MiB, minibatch %d rows, comm/gemm workgroups %s/%s"
                             % (args.ring_mib, mb, args.comm_wgs or "auto",
@@ -280,63 +291,36 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     return result
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="C2")
-    ap.add_argument("--cpu-tokens", type=int, default=20)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ring-mib", type=int, default=0,
-                    help="forward through the persistent ring kernel with a ring of this many "
-                         "MiB (0 = one launch per step)")
-    ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
-    ap.add_argument("--comm-wgs", type=int, default=0, help="ring path: dispatch workgroups")
-    ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
-    ap.add_argument("--graph", action="store_true",
-                    help="also capture one step in a HIP graph and time its replays "
-                         "(reported under 'graph'; the headline stays the eager step)")
-    ap.add_argument("--tune", action="store_true",
-                    help="ring path: choose minibatch rows and dispatch workgroups with "
-                         "mok_tune_fwd before the timed steps (untimed)")
-    ap.add_argument("--mb-sweep", default="",
-                    help="ring path: comma-separated minibatch sizes, one JSON line each")
-    ap.add_argument("--hbm-copy-gib", type=float, default=0.0,
-                    help="instead of the layer: time a plain device copy of this many GiB "
-                         "(the reference for HBM bandwidth and for scaling byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one MI355X: the library has no multi-GPU path "
-              "(--gpus must be 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    from combine_router_top_expert_amd import Trace, synth
-    from combine_router_top_expert_amd.layer import MoELayer, to_device
-
-    if not torch.cuda.is_available():
-        raise SystemExit("no GPU visible")
-    dev = "cuda:0"
-    if args.hbm_copy_gib > 0:
-        n = int(args.hbm_copy_gib * (1 << 30)) // 16 * 16
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
+def hbm_stream_lines(args, torch):
+    """The HBM streaming probe (16-byte loads and stores over a grid-stride
+    loop, the access of the layer's data-movement kernels): read-only,
+    write-only and copy rates, one JSON line each."""
+    from combine_router_top_expert_amd import mok_hbm_stream
+    n = int(args.hbm_stream_gib * (1 << 30)) // 256 * 256
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for mode, name, moved in ((0, "read", n), (1, "write", n), (2, "copy", 2 * n)):
         for _ in range(args.warmup):
-            dst.copy_(src)
+            mok_hbm_stream(mode, dst, src, n)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            dst.copy_(src)
+            mok_hbm_stream(mode, dst, src, n)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
-        print(json.dumps({"metric": "device copy bytes moved per second (read + write)",
-                          "value": 2.0 * n / dt / 1e9, "unit": "GB/s", "bytes_per_copy": n,
-                          "ms_per_copy": dt * 1e3, "steps": args.steps}), flush=True)
-        return
-    w = synth.WORKLOADS[args.workload]
+        print(json.dumps({"metric": f"HBM streaming probe, {name} (bytes moved per second)",
+                          "value": moved / dt / 1e9, "unit": "GB/s", "bytes_per_call": moved,
+                          "ms_per_call": dt * 1e3, "frac_hbm_peak": moved / dt / 1e9 / PEAK_HBM_GBS,
+                          "steps": args.steps}), flush=True)
+
+
+def run_workload(args, name, np, torch):
+    """Inputs, layer, timed steps and the CPU baseline of one workload -> records."""
+    from combine_router_top_expert_amd import Trace, synth
+    from combine_router_top_expert_amd.layer import MoELayer, to_device
+
+    dev = "cuda:0"
+    w = synth.WORKLOADS[name]
     has_bwd = w.prec != "mxfp8"
     t0 = time.time()
     xs = [synth.gen_x(w, s) for s in range(w.S)]
@@ -347,7 +331,7 @@ def main():
     wd = synth.gen_expert_weights(w, "down")
     dout = [synth.gen_dout(w, s) for s in range(w.S)] if has_bwd else None
     other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
-    log(f"inputs generated in {time.time() - t0:.1f} s")
+    log(f"{name}: inputs generated in {time.time() - t0:.1f} s")
     N = w.S * w.T_src * w.k
     # row capacity: every item when all experts are local, else twice the
     # balanced share (a layer latches MOK_ECAPACITY if routing exceeds it)
@@ -368,34 +352,87 @@ def main():
         return L
 
     mbs = [int(v) for v in args.mb_sweep.split(",")] if args.mb_sweep else [args.mb]
-    if args.tune and (not args.ring_mib or args.mb_sweep):
-        sys.exit("--tune needs --ring-mib and no --mb-sweep")
     results = []
     for mb in mbs:
         L = make_layer(mb)
         tuned = None
+        comm = args.comm_wgs
         if args.tune:
             table = L.tune()
             log("tuner (minibatch rows, dispatch workgroups) -> ms per forward:",
                 {f"{m}/{c}": (round(v, 3) if v is not None else None) for (m, c), v in table.items()})
-            mb, args.comm_wgs = L.cfg.minibatch_rows, L.cfg.comm_wgs
+            mb, comm = L.cfg.minibatch_rows, L.cfg.comm_wgs
             tuned = {f"{m}/{c}": v for (m, c), v in table.items()}
-        results.append(measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace))
+        a = argparse.Namespace(**{**vars(args), "comm_wgs": comm})
+        results.append(measure(a, w, L, d_out, has_bwd, mb, np, torch, Trace))
         if tuned is not None:
             results[-1]["config"]["tuner_ms_per_forward"] = tuned
         del L
         torch.cuda.empty_cache()
-    result = results[-1]
+    for r in results:
+        r["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         host = {"x_val": [b for _, b in xs], "dout_val": [b for _, b in dout] if has_bwd else None,
                 "wr_val": wr[1], "bias": bias, "wg_val": wg[1], "wu_val": wu[1], "wd_val": wd[1]}
-        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_tokens)
-    else:
-        result["cpu_baseline"] = None
-    for r in results[:-1]:
-        r["cpu_baseline"] = None
-        print(json.dumps(r), flush=True)
-    print(json.dumps(result), flush=True)
+        base = cpu_baseline(w, host, args.cpu_tokens)
+        for r in results:
+            r["cpu_baseline"] = base
+    del dev_in, d_out
+    torch.cuda.empty_cache()
+    return results
+
+
+# the default run: every configuration one GPU holds, the largest (the
+# headline) last
+DEFAULT_ORDER = ["C2", "C4", "C5", "C3"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="all",
+                    help="C1..C5, or 'all' (C2, C4, C5, then C3, one JSON line each)")
+    ap.add_argument("--cpu-tokens", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring-mib", type=int, default=0,
+                    help="forward through the persistent ring kernel with a ring of this many "
+                         "MiB (0 = one launch per step)")
+    ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
+    ap.add_argument("--comm-wgs", type=int, default=0, help="ring path: dispatch workgroups")
+    ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step in a HIP graph and time its replays "
+                         "(reported under 'graph'; the headline stays the eager step)")
+    ap.add_argument("--tune", action="store_true",
+                    help="ring path: choose minibatch rows and dispatch workgroups with "
+                         "mok_tune_fwd before the timed steps (untimed)")
+    ap.add_argument("--mb-sweep", default="",
+                    help="ring path: comma-separated minibatch sizes, one JSON line each")
+    ap.add_argument("--hbm-stream-gib", type=float, default=0.0,
+                    help="instead of the layer: the HBM streaming probe (read, write, copy) "
+                         "over this many GiB")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    if args.hbm_stream_gib > 0:
+        hbm_stream_lines(args, torch)
+        return
+    if args.tune and (not args.ring_mib or args.mb_sweep):
+        sys.exit("--tune needs --ring-mib and no --mb-sweep")
+    names = DEFAULT_ORDER if args.workload == "all" else [args.workload]
+    for name in names:
+        for r in run_workload(args, name, np, torch):
+            print(json.dumps(r), flush=True)
 
 
 if __name__ == "__main__":

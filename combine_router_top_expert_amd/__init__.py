@@ -28,7 +28,7 @@ STATUS = {
 # every symbol include/mok.h declares
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
-           "mok_version")
+           "mok_ring_layout", "mok_hbm_stream", "mok_version")
 
 
 class MokError(RuntimeError):
@@ -215,6 +215,9 @@ def lib():
         L.mok_tune_fwd.argtypes = [cfgp, P, I32, P, I32, I32, ctypes.c_size_t, I32, I32, P, P, P, P,
                                    ctypes.POINTER(mok_expert_weights),
                                    ctypes.POINTER(mok_fwd_state), P, P, P, P, P, cfgp, P]
+        L.mok_ring_layout.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t),
+                                      ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(I32)]
+        L.mok_hbm_stream.argtypes = [I32, P, P, I64, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -363,3 +366,17 @@ def mok_tune_fwd(cfg, mbs, comms, reps, ws_bytes, own_lo, own_n, src_x, w_router
 def mok_mx_quantize(rows, K, src, codes, scales, stream=None):
     _check("mok_mx_quantize", lib().mok_mx_quantize(rows, K, _ptr(src), _ptr(codes), _ptr(scales),
                                                     _stream(stream)))
+
+
+def mok_ring_layout(cfg):
+    """-> (offset, slot_bytes, nslot) of the fused path's ring inside the workspace."""
+    off, sb, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+    _check("mok_ring_layout", lib().mok_ring_layout(ctypes.byref(cfg), ctypes.byref(off),
+                                                    ctypes.byref(sb), ctypes.byref(n)))
+    return int(off.value), int(sb.value), int(n.value)
+
+
+def mok_hbm_stream(mode, dst, src, nbytes, stream=None):
+    """HBM streaming probe: mode 0 read src, 1 write dst, 2 copy src -> dst."""
+    _check("mok_hbm_stream", lib().mok_hbm_stream(mode, _ptr(dst), _ptr(src), nbytes,
+                                                  _stream(stream)))

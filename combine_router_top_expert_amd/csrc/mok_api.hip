@@ -105,6 +105,26 @@ bool own_range_ok(const mok_config* c, int own_lo, int own_n) {
   return own_lo >= 0 && own_n >= 0 && own_lo + own_n <= c->S;
 }
 
+// Per-source pointer arrays.  Which sources have items routed to a local
+// expert is known on the device only, so a call that pulls from or pushes
+// to the sources needs all S entries (when there are tokens at all); the
+// final combine and the per-token sums touch the own sources only.
+bool all_sources_set(const void* const* p, int S, int T_src) {
+  if (!p) return false;
+  if (T_src == 0) return true;
+  for (int s = 0; s < S; ++s)
+    if (!p[s]) return false;
+  return true;
+}
+
+bool own_sources_set(const void* const* p, int own_lo, int own_n, int T_src) {
+  if (own_n == 0 || T_src == 0) return true;
+  if (!p) return false;
+  for (int s = own_lo; s < own_lo + own_n; ++s)
+    if (!p[s]) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,6 +170,7 @@ mok_status mok_dispatch(const mok_config* cfg, const void* const* src_x, const i
   if (!valid_cfg(cfg)) return MOK_EINVAL;
   if (cfg->R_cap == 0) return MOK_OK;
   SrcTable src;
+  if (!all_sources_set(src_x, cfg->S, cfg->T_src)) return MOK_EINVAL;
   if (!fill_table(&src, src_x, cfg->S) || !row_src || !offsets || !x_perm) return MOK_EINVAL;
   if (cfg->prec == MOK_MXFP8 && !x_scale) return MOK_EINVAL;
   trace_mark(cfg->trace, "start", (hipStream_t)stream);
@@ -187,6 +208,13 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
   if (N == 0) return MOK_OK;
   DstTable stg, o;
   if (!fill_table(&stg, (const void* const*)staging, cfg->S) || !dest_row) return MOK_EINVAL;
+  // the push reaches every source with a local row; the combine the own ones
+  if (y && !all_sources_set((const void* const*)staging, cfg->S, cfg->T_src)) return MOK_EINVAL;
+  if (own_n > 0) {
+    if (!topk_gate || !own_sources_set((const void* const*)staging, own_lo, own_n, cfg->T_src) ||
+        !own_sources_set((const void* const*)out, own_lo, own_n, cfg->T_src))
+      return MOK_EINVAL;
+  }
   const int prec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
   hipStream_t st = (hipStream_t)stream;
   if (y) {
@@ -195,9 +223,7 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
     if (rc != MOK_OK) return rc;
   }
   if (own_n == 0) return MOK_OK;
-  if (!fill_table(&o, (const void* const*)out, cfg->S) || !topk_gate) return MOK_EINVAL;
-  for (int s = own_lo; s < own_lo + own_n; ++s)  // empty sources may pass NULL buffers
-    if (cfg->T_src > 0 && (!o.p[s] || !stg.p[s])) return MOK_EINVAL;
+  fill_table(&o, (const void* const*)out, cfg->S);
   return launch_combine(prec, dest_row, topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k, own_lo,
                         own_n, cfg->R_cap, st, cfg->trace);
 }
@@ -212,7 +238,15 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   if (!st->topk_idx || !st->topk_gate || !st->counts || !st->offsets || !st->dest_row)
     return MOK_EINVAL;
   if (cfg->R_cap > 0 && (!st->row_src || !st->h)) return MOK_EINVAL;
-  if (own_n > 0 && !out) return MOK_EINVAL;
+  // the pull reads and the push writes any source with a local row; the
+  // router and the final combine touch the own sources
+  if (cfg->R_cap > 0 && (!all_sources_set(src_x, cfg->S, cfg->T_src) ||
+                         !all_sources_set((const void* const*)staging, cfg->S, cfg->T_src)))
+    return MOK_EINVAL;
+  if (!own_sources_set(src_x, own_lo, own_n, cfg->T_src) ||
+      !own_sources_set((const void* const*)staging, own_lo, own_n, cfg->T_src) ||
+      !own_sources_set((const void* const*)out, own_lo, own_n, cfg->T_src))
+    return MOK_EINVAL;
   if (cfg->ring_bytes > 0 && cfg->R_cap > 0) {  // ring path: bf16 / MXFP8
     if (!dev_status) return MOK_EINVAL;
     const mok_status rc = ring_check(cfg->prec, cfg->d, cfg->I, cfg->minibatch_rows,
@@ -224,8 +258,6 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   trace_mark(tr, "start", sm);
   const int64_t per_src = (int64_t)cfg->T_src * cfg->k;
   const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
-  for (int s = own_lo; s < own_lo + own_n; ++s)
-    if (cfg->T_src > 0 && !src_x[s]) return MOK_EINVAL;
   {
     SrcTable src;
     fill_table(&src, src_x, cfg->S);
@@ -303,8 +335,6 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   if (own_n == 0) return MOK_OK;
   DstTable o;
   fill_table(&o, (const void* const*)out, cfg->S);
-  for (int s = own_lo; s < own_lo + own_n; ++s)
-    if (cfg->T_src > 0 && (!o.p[s] || !stg.p[s])) return MOK_EINVAL;
   return launch_combine(rprec, st->dest_row, st->topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k,
                         own_lo, own_n, cfg->R_cap, sm, tr);
 }
@@ -316,14 +346,25 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          void* const* staging, float* d_gate, void* const* dx_stage,
                          void* const* d_x, float* dw_gate, float* dw_up, float* dw_down,
                          float* dw_router, void* ws, int32_t* dev_status, void* stream) {
-  (void)dev_status;
   (void)expert_to_local;
   if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
   if (cfg->prec == MOK_MXFP8) return MOK_EINVAL;
   if (!d_out || !src_x || !w_router || !w || !st || !staging || !d_gate || !dx_stage || !ws)
     return MOK_EINVAL;
   if (!dw_gate || !dw_up || !dw_down || !st->ab || !st->h) return MOK_EINVAL;
-  if (own_n > 0 && !d_x) return MOK_EINVAL;
+  if (!st->topk_idx || !st->topk_gate || !st->offsets || !st->dest_row) return MOK_EINVAL;
+  if (cfg->R_cap > 0 && !st->row_src) return MOK_EINVAL;
+  // the pulls and pushes reach every source with a local row; the per-token
+  // sums and the router gradient the own ones
+  if (cfg->R_cap > 0 &&
+      (!all_sources_set(d_out, cfg->S, cfg->T_src) || !all_sources_set(src_x, cfg->S, cfg->T_src) ||
+       !all_sources_set((const void* const*)staging, cfg->S, cfg->T_src) ||
+       !all_sources_set((const void* const*)dx_stage, cfg->S, cfg->T_src)))
+    return MOK_EINVAL;
+  if (!own_sources_set(src_x, own_lo, own_n, cfg->T_src) ||
+      !own_sources_set((const void* const*)dx_stage, own_lo, own_n, cfg->T_src) ||
+      !own_sources_set((const void* const*)d_x, own_lo, own_n, cfg->T_src))
+    return MOK_EINVAL;
   if (dw_router && cfg->E > 256) return MOK_EINVAL;  // router layout holds at most 256 experts
   BwdPlan p;
   memset(&p, 0, sizeof(p));
@@ -374,6 +415,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.x_perm = wsb + wl.bx;
   p.wg_part = (float*)(wsb + wl.wpart);
   p.wg_order = (int32_t*)(wsb + wl.worder);
+  p.status = dev_status;
   p.tr = cfg->trace;
   if (cfg->aux) {
     const mok_aux* a = cfg->aux;
@@ -469,6 +511,29 @@ done:
   hipEventDestroy(ev[0]);
   hipEventDestroy(ev[1]);
   return result;
+}
+
+mok_status mok_ring_layout(const mok_config* cfg, size_t* offset, size_t* slot_bytes,
+                           int32_t* nslot) {
+  if (!valid_cfg(cfg) || cfg->ring_bytes <= 0 || !offset || !slot_bytes || !nslot)
+    return MOK_EINVAL;
+  if (cfg->prec != MOK_BF16 && cfg->prec != MOK_MXFP8) return MOK_EINVAL;
+  const int64_t sb = ring_slot_bytes(cfg->prec, cfg->d, cfg->minibatch_rows);
+  const int64_t n = cfg->ring_bytes / sb;
+  if (n < 1) return MOK_EINVAL;
+  *offset = ws_layout(cfg).ring;
+  *slot_bytes = (size_t)sb;
+  *nslot = n > (1 << 30) ? (1 << 30) : (int32_t)n;
+  return MOK_OK;
+}
+
+mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t bytes,
+                          void* stream) {
+  if (mode < 0 || mode > 2 || bytes < 0 || bytes % 16 != 0) return MOK_EINVAL;
+  if (bytes == 0) return MOK_OK;
+  if (!dst || (mode != 1 && !src)) return MOK_EINVAL;
+  if (((uintptr_t)dst | (uintptr_t)src) % 16 != 0) return MOK_EINVAL;
+  return launch_stream(mode, dst, src, bytes, (hipStream_t)stream);
 }
 
 mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,

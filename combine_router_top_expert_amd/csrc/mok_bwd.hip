@@ -267,10 +267,14 @@ __global__ __launch_bounds__(kThreads) void dx_final_kernel(BwdPlan p) {
         m = __builtin_fmaf(__shfl(g, (lane & ~15) + i, 64), __shfl(dg, (lane & ~15) + i, 64), m);
       if (valid) {
         const float dz = g * (dg - m);
-        s_dz[q][j] = dz;
-        s_e[q][j] = e;
+        // an id outside [0, E) has no router row: latched, and its router
+        // term left out (the router only writes valid ids)
+        const bool ok_e = e >= 0 && e < p.E;
+        if (!ok_e) latch(p.status, MOK_EROUTE);
+        s_dz[q][j] = ok_e ? dz : 0.0f;
+        s_e[q][j] = ok_e ? e : 0;
         s_loc[q][j] = loc;
-        p.dz[gt * p.k + j] = dz;
+        p.dz[gt * p.k + j] = ok_e ? dz : 0.0f;
       }
     }
     __syncthreads();
@@ -489,8 +493,8 @@ mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
 
 template <typename T>
 mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
-  if (sizeof(T) == 2 && p.aux) return run_bwd_two_streams<T>(p, stream);
-  if (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2) {
+    if (p.aux) return run_bwd_two_streams<T>(p, stream);
     if (p.R_cap > 0) {
       hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
       trace_mark(p.tr, "bwd_reverse_combine_pull", stream);

@@ -12,6 +12,8 @@
 //          (push combine fused into the GEMM epilogue).
 // Tiles are 128 x 128, a flat grid over (m-tile of the grouped rows, n-tile);
 // workgroups past the routed rows exit at once (row counts stay on device).
+// This engine runs the fp32 layer only; bf16 goes to the pipelined engine
+// (mok_ffn2.hip), the one the layer path uses.
 #include "mok_gemm.h"
 #include "mok_internal.h"
 
@@ -140,9 +142,11 @@ mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void
                       const DstTable* staging, int T_src, int k, hipStream_t stream,
                       mok_trace* tr) {
   if (R_cap == 0) return MOK_OK;
+  // bf16 runs on the pipelined engine of the layer path; this engine is fp32 only
   if (prec == MOK_BF16)
     return launch_ffn_bf16(d, I, E_local, R_cap, x, nullptr, T_src, k, offsets, row_src, wg, wu,
                            wd, h, ab, y, staging, stream, tr);
+  if (prec != MOK_F32) return MOK_EINVAL;
   const int mt = grouped_mtiles_bound(R_cap, E_local);
   Ffn1Args a1;
   a1.x = x;
@@ -173,15 +177,9 @@ mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void
   a2.T_src = T_src;
   a2.k = k;
   dim3 g2((unsigned)(mt * a2.ntn));
-  if (prec == MOK_F32)
-    hipLaunchKernelGGL(ffn1_kernel<float>, g1, dim3(kGemmThreads), 0, stream, a1);
-  else
-    hipLaunchKernelGGL(ffn1_kernel<bf16_t>, g1, dim3(kGemmThreads), 0, stream, a1);
+  hipLaunchKernelGGL(ffn1_kernel<float>, g1, dim3(kGemmThreads), 0, stream, a1);
   trace_mark(tr, "ffn1_gate_up_swiglu", stream);
-  if (prec == MOK_F32)
-    hipLaunchKernelGGL(ffn2_kernel<float>, g2, dim3(kGemmThreads), 0, stream, a2);
-  else
-    hipLaunchKernelGGL(ffn2_kernel<bf16_t>, g2, dim3(kGemmThreads), 0, stream, a2);
+  hipLaunchKernelGGL(ffn2_kernel<float>, g2, dim3(kGemmThreads), 0, stream, a2);
   trace_mark(tr, "ffn2_down", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }

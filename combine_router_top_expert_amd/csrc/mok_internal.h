@@ -84,6 +84,9 @@ mok_status ring_check(int prec, int d, int I, int mb, int64_t ring_bytes, int co
                       int gemm_wgs, int* comm_out, int* gemm_out);
 mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr = nullptr);
 
+// HBM streaming probe (mok_stream.hip): mode 0 read, 1 write, 2 copy.
+mok_status launch_stream(int mode, void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
 struct BwdPlan {
   int prec;
   int S, T_src, d, E, k, I, E_local, R_cap;
@@ -112,6 +115,7 @@ struct BwdPlan {
   void* x_perm;     // bf16: [d, xt_ld] token rows gathered again, transposed, for the wgrad GEMM
   float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
   int32_t* wg_order;  // [E_local] local experts by routed rows, descending
+  int32_t* status;  // device status word (may be null)
   mok_trace* tr;    // host-side trace, may be null
   hipStream_t aux;      // second stream for the work beside the GEMMs, or null
   hipEvent_t aux_ev[3]; // fork/join events of the second stream

@@ -63,6 +63,16 @@ __device__ __forceinline__ void unpack<float>(uint4 u, float* out) {
   out[3] = __uint_as_float(u.w);
 }
 
+// Selection order of two (logit, expert) entries: the larger logit first,
+// the lower expert id first on equal logits.  A NaN logit ranks after every
+// number, -inf included, and NaNs rank among themselves by id, so a token
+// whose logits are NaN still gets k distinct valid experts.
+__device__ __forceinline__ bool ranks_before(float a, int ea, float b, int eb) {
+  const bool na = __builtin_isnan(a), nb = __builtin_isnan(b);
+  if (na || nb) return nb && (!na || ea < eb);
+  return a > b || (a == b && ea < eb);
+}
+
 // Top-k and gates of a block's tokens from the logits zs[TB][zp].  LP = 2^LPS
 // lanes per token (the power of two covering E, at most 64), 64 / LP tokens
 // per wave at a time; lane li of a token's group holds experts li, li + LP,
@@ -91,13 +101,14 @@ __device__ __forceinline__ void select_topk(const RouteArgs& a, const float* zs,
     float z0 = 0.0f, sum = 0.0f, my_ex = 0.0f;
     int my_e = 0;
     for (int j = 0; j < a.k; ++j) {
-      float bz = -__builtin_inff();
+      // no candidate yet: a NaN with the largest id, which every entry beats
+      float bz = __builtin_nanf("");
       int be = 0x7FFFFFFF;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         int e = li + LP * m;
         bool ok = m < MPL && e < a.E && !((used >> m) & 1u);
-        if (ok && (zv[m] > bz || (zv[m] == bz && e < be))) {
+        if (ok && ranks_before(zv[m], e, bz, be)) {
           bz = zv[m];
           be = e;
         }
@@ -106,7 +117,7 @@ __device__ __forceinline__ void select_topk(const RouteArgs& a, const float* zs,
       for (int off = LP >> 1; off >= 1; off >>= 1) {
         float oz = __shfl_xor(bz, off, 64);
         int oe = __shfl_xor(be, off, 64);
-        if (oz > bz || (oz == bz && oe < be)) {
+        if (ranks_before(oz, oe, bz, be)) {
           bz = oz;
           be = oe;
         }

@@ -46,8 +46,15 @@
  *   - Source buffers: S simulated source ranks, each a separate device buffer
  *     of T_src tokens, passed as a host array of S device pointers (up to
  *     MOK_MAX_SOURCES).  Item n = (s * T_src + t) * k + j names slot j of
- *     token t of source s.  With T_src = 0 (an empty batch) the per-source
- *     device pointers may be NULL; the state arrays must still be non-NULL.
+ *     token t of source s.  Which sources have items routed to a local
+ *     expert is known on the device only, so a call that pulls rows from the
+ *     sources or pushes rows to them (mok_dispatch, the push of mok_combine,
+ *     mok_layer_fwd, mok_layer_bwd) needs all S entries of those arrays
+ *     non-NULL whenever T_src > 0 and R_cap > 0; arrays read or written for
+ *     the own sources only (out, d_x) need their own entries only.  Any NULL
+ *     entry a call needs is MOK_EINVAL before anything is enqueued.  With
+ *     T_src = 0 (an empty batch) the per-source device pointers may be NULL;
+ *     the state arrays must still be non-NULL.
  */
 #ifndef MOK_H
 #define MOK_H
@@ -300,6 +307,26 @@ mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
                         const mok_expert_weights* w, const mok_fwd_state* st,
                         void* const* staging, void* const* out, void* ws, int32_t* dev_status,
                         void* stream, mok_config* best, float* times_ms);
+
+/* Where the fused path keeps its ring inside the workspace, for inspection
+ * [K02 ring token buffer]: the ring of cfg (ring_bytes > 0, bf16 or MXFP8)
+ * starts *offset bytes into ws and holds *nslot slots of *slot_bytes bytes.
+ * After mok_layer_fwd, minibatch m (the m-th run of at most minibatch_rows
+ * consecutive rows of one local expert, experts in order) is in slot
+ * m % nslot unless a later minibatch reused the slot.  A slot holds its
+ * rows in order: bf16 rows of d values, or for MOK_MXFP8 minibatch_rows * d
+ * E4M3 codes followed by minibatch_rows * d/32 E8M0 scales.  Host only;
+ * MOK_EINVAL if cfg has no ring or the ring holds no slot. */
+mok_status mok_ring_layout(const mok_config* cfg, size_t* offset, size_t* slot_bytes,
+                           int32_t* nslot);
+
+/* HBM streaming probe: the bandwidth ceiling the layer's data-movement
+ * kernels are measured against.  Moves `bytes` (a multiple of 16) with
+ * 16-byte vector loads and stores, the access of those kernels.  mode 0:
+ * read src (dst must hold 256 * 16 * CUs * 4 bytes; nothing is written there
+ * for any real data); 1: write dst; 2: copy src to dst.  Pointers 16-byte
+ * aligned, device memory.  MOK_EINVAL on a bad mode, size or pointer. */
+mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t bytes, void* stream);
 
 /* MX quantisation of rows of bf16 values (weight preparation off the timed
  * path, and the same codec as the fused activation paths):  src [rows, K]

@@ -134,3 +134,87 @@ def test_backward_second_stream_checked_on_the_host(L):
                              ctypes.byref(st), tp, 1, tp, tp, 1, 1, 1, None, 1, 1,
                              7 if aux.stream == 7 and aux.events[1] else None)
         assert rc == -1
+
+
+def _tab(S, null_at=None):
+    tab = (ctypes.c_void_p * S)(*([1] * S))
+    if null_at is not None:
+        tab[null_at] = None
+    return ctypes.cast(tab, ctypes.c_void_p), tab
+
+
+@pytest.mark.parametrize("which", ["src_x", "staging", "out_own"])
+def test_layer_fwd_rejects_null_source_pointers(L, which):
+    """The pull and the push may reach any source (which ones is known on the
+    device only), so every src_x[s] and staging[s] must be set; out[s] only
+    for the own sources.  MOK_EINVAL comes back before anything is enqueued."""
+    S = 3
+    cfg = _cfg(S=S)
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+    full, _k1 = _tab(S)
+    bad, _k2 = _tab(S, 2 if which != "out_own" else 0)
+    src = bad if which == "src_x" else full
+    stg = bad if which == "staging" else full
+    out = bad if which == "out_own" else full
+    # own source 0 only: sources 1 and 2 are other ranks'
+    rc = L.mok_layer_fwd(ctypes.byref(cfg), 0, 1, src, 1, None, 1, ctypes.byref(w),
+                         ctypes.byref(st), stg, out, 1, 1, None)
+    assert rc == -1
+
+
+def test_layer_fwd_out_of_non_own_source_may_be_null(L):
+    """out[s] of a source this GPU does not combine is never touched: a NULL
+    there passes validation (the call then fails only at launch on a host
+    without a GPU, with MOK_EDEVICE, never with MOK_EINVAL)."""
+    S = 3
+    cfg = _cfg(S=S, R_cap=0)
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+    full, _k1 = _tab(S)
+    out, _k2 = _tab(S, 2)
+    rc = L.mok_layer_fwd(ctypes.byref(cfg), 0, 1, full, 1, None, 1, ctypes.byref(w),
+                         ctypes.byref(st), full, out, 1, 1, None)
+    assert rc != -1
+
+
+def test_combine_and_dispatch_reject_null_source_pointers(L):
+    S = 3
+    cfg = _cfg(S=S)
+    full, _k1 = _tab(S)
+    bad, _k2 = _tab(S, 1)
+    # push (y given) into a NULL staging buffer of a non-own source
+    assert L.mok_combine(ctypes.byref(cfg), 1, 1, 1, bad, 0, 1, full, 1, None) == -1
+    # gather from a NULL source buffer
+    assert L.mok_dispatch(ctypes.byref(cfg), bad, 1, 1, 1, None, 1, None) == -1
+
+
+@pytest.mark.parametrize("which", ["d_out", "src_x", "staging", "dx_stage"])
+def test_layer_bwd_rejects_null_source_pointers(L, which):
+    S = 3
+    cfg = _cfg(S=S)
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+    full, _k1 = _tab(S)
+    bad, _k2 = _tab(S, 2)
+    args = {k: (bad if k == which else full) for k in ("d_out", "src_x", "staging", "dx_stage")}
+    rc = L.mok_layer_bwd(ctypes.byref(cfg), 0, 1, args["d_out"], args["src_x"], 1, 1,
+                         ctypes.byref(w), ctypes.byref(st), args["staging"], 1, args["dx_stage"],
+                         full, 1, 1, 1, None, 1, 1, None)
+    assert rc == -1
+
+
+def test_ring_layout_host_logic(L):
+    """Where the ring sits in the workspace: past the forward's other pieces,
+    slots of minibatch_rows rows (256-byte aligned), as many as fit."""
+    cfg = _cfg(ring_bytes=10 * 64 * 256 * 2 + 100, minibatch_rows=64)
+    off, sb, n = mok.mok_ring_layout(cfg)
+    assert sb == 64 * 256 * 2 and n == 10
+    assert off % 256 == 0 and off + n * sb <= mok.mok_workspace_bytes(cfg)
+    cm = _cfg(prec="mxfp8", ring_bytes=1 << 20, minibatch_rows=128)
+    off, sb, n = mok.mok_ring_layout(cm)
+    assert sb == (128 * 256 + 128 * 8 + 255) // 256 * 256 and n == (1 << 20) // sb
+    with pytest.raises(mok.MokError):
+        mok.mok_ring_layout(_cfg())                         # no ring
+    with pytest.raises(mok.MokError):
+        mok.mok_ring_layout(_cfg(prec="f32", ring_bytes=1 << 20))

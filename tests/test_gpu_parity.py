@@ -77,6 +77,98 @@ def test_route_bit_exact(name):
     np.testing.assert_allclose(g.cpu().numpy(), ref_g, atol=2e-6, rtol=0)
 
 
+def _special_route_inputs(kind):
+    """Router inputs that exercise the selection rule: exact ties (small
+    integer values, duplicated router rows, equal biases), k = E, and NaN /
+    infinite logits.  -> (T, d, E, k, x values, router values, bias)."""
+    rng = np.random.default_rng({"ties": 11, "k_eq_E": 12, "nan": 13}[kind])
+    if kind == "k_eq_E":
+        T, d, E, k = 300, 256, 16, 16
+        x = rng.normal(size=(T, d))
+        wr = rng.normal(size=(E, d)) / 16
+        bias = None
+    else:
+        T, d, E, k = 333, 128, 24, 4
+        # sums of small multiples of 1/4 are exact in fp32: many equal logits
+        x = rng.integers(-2, 3, size=(T, d)).astype(np.float64)
+        wr = rng.integers(-1, 2, size=(E, d)) * 0.25
+        wr[5] = wr[2]
+        wr[9] = wr[2]
+        wr[E - 1] = wr[0]
+        bias = np.zeros(E, np.float32)
+        bias[[3, 4, 11]] = 0.5
+        bias[[7, 8]] = -0.25
+    if kind == "nan":
+        x[0, :] = np.nan           # every logit of token 0 is NaN
+        x[1, 17] = np.nan
+        x[2, 3] = np.inf           # +-inf logits, NaN where a weight is 0
+        x[3, :] = np.inf
+        wr[6, 40] = np.nan         # expert 6 has a NaN logit for every token
+    xs = synth.f64_to_bf16_bits(x)
+    ws = synth.f64_to_bf16_bits(wr)
+    return T, d, E, k, xs, ws, bias
+
+
+@pytest.mark.parametrize("kind", ["ties", "k_eq_E", "nan"])
+def test_route_selection_rule_bit_exact(kind):
+    """Equal logits go to the lower expert id; k = E selects every expert in
+    logit order; a NaN logit ranks after every number (-inf included), so a
+    token with NaN logits still gets k distinct valid experts."""
+    T, d, E, k, xs, ws, bias = _special_route_inputs(kind)
+    _log("route rule", kind, T, d, E, k)
+    xv = synth.bf16_bits_to_f32(xs)
+    wv = synth.bf16_bits_to_f32(ws)
+    ref_idx, ref_g = oracle.route(xv, wv, bias, k, "bf16")
+    if kind == "ties":   # the inputs really produce ties that decide a slot
+        z = oracle.logits(xv, wv, bias, "bf16")
+        kth = np.sort(z, axis=1)[:, ::-1][:, k - 1:k + 1]
+        assert np.sum(kth[:, 0] == kth[:, 1]) > 20
+    cfg = make_config(1, T, d, E, k, 64, 1, "bf16", 1)
+    x = to_device(xs, "bf16", DEV)
+    wrd = to_device(ws, "bf16", DEV)
+    b = None if bias is None else torch.from_numpy(bias).to(DEV)
+    idx = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+    g = torch.zeros((T, k), dtype=torch.float32, device=DEV)
+    mok_route(cfg, T, x, wrd, b, idx, g)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    np.testing.assert_array_equal(gi, ref_idx)
+    assert gi.min() >= 0 and gi.max() < E
+    assert all(len(set(r)) == k for r in gi.tolist())
+    np.testing.assert_allclose(g.cpu().numpy(), ref_g, atol=2e-6, rtol=0)  # NaN == NaN here
+
+
+def test_layer_with_nan_token_keeps_valid_experts():
+    """A token row holding NaN routes to valid experts (the k lowest ids), so
+    the forward and the backward -- whose router term reads the router row
+    of each chosen expert -- stay in bounds and latch nothing; the other
+    tokens' outputs and input gradients are finite."""
+    w = _small("C2", S=2, T_src=100, d=128, E=8, k=2, I=128, own=[0, 1],
+               local_experts=list(range(8)))
+    _log("nan token")
+    c = make_host_case(w, route_own=False)
+    v = synth.bf16_bits_to_f32(c.x_store[0]).astype(np.float64)
+    v[7, :] = np.nan
+    c.x_store[0] = synth.f64_to_bf16_bits(v)
+    c.x_val[0] = synth.bf16_bits_to_f32(c.x_store[0])
+    from cases import oracle_routing
+    oracle_routing(c)
+    L = _layer(c)
+    d_out = [to_device(synth.gen_dout(w, s)[0], w.prec, DEV) for s in range(w.S)]
+    L.forward()
+    L.backward(d_out)
+    torch.cuda.synchronize()
+    L.check_status()
+    gi = L.topk_idx.cpu().numpy().reshape(w.S, w.T_src, w.k)
+    np.testing.assert_array_equal(gi, c.topk_all)
+    np.testing.assert_array_equal(gi[0, 7], np.arange(w.k))
+    out0 = L.out[0].float().cpu().numpy()
+    dx0 = L.d_x[0].float().cpu().numpy()
+    assert np.all(np.isnan(out0[7]))
+    keep = np.arange(w.T_src) != 7
+    assert np.all(np.isfinite(out0[keep])) and np.all(np.isfinite(dx0[keep]))
+
+
 LAYOUT_CASES = {
     "c2": (synth.WORKLOADS["C2"], None),
     "c3": (synth.WORKLOADS["C3"], None),
@@ -548,12 +640,68 @@ def _bwd_sampled(c, L, dout_store, toks):
     assert e_dg <= TOL[w.prec] and e_dx <= TOL[w.prec]
 
 
-# full-size backward workloads: (workload, check the weight gradients of the
-# least-routed local expert -- the oracle computes them row by row)
+# full-size backward workloads: (workload, check the whole weight gradients of
+# the least-routed local expert and the router weight gradient)
 BWD_FULL = {
     "c5_full": (synth.WORKLOADS["C5"], True),
     "c3_full": (synth.WORKLOADS["C3"], False),
 }
+
+
+def _expert_rows(c, dout_store, le):
+    """Token rows, gates and upstream gradients of local expert le's rows."""
+    w = c.w
+    lay = c.layout
+    rows = lay["row_src"][lay["offsets"][le]:lay["offsets"][le + 1]]
+    tt, jj = rows // w.k, rows % w.k
+    rx = np.stack([c.x_val[t // w.T_src][t % w.T_src] for t in tt])
+    rg = np.array([c.gate_all[t // w.T_src, t % w.T_src, j] for t, j in zip(tt, jj)])
+    rd = np.stack([dout_store[t // w.T_src][1][t % w.T_src] for t in tt])
+    return rx, rg, rd
+
+
+def _check_wgrad_columns(c, L, dout_store, le, n_sel=6):
+    """Sampled intermediate columns of local expert le's three weight
+    gradients against the oracle (every d column of each)."""
+    w = c.w
+    rng = np.random.default_rng(le)
+    sel = np.unique(np.concatenate([[0, w.I - 1, 255, 256],
+                                    rng.integers(0, w.I, n_sel)])).astype(np.int32)
+    sel = sel[sel < w.I]
+    rx, rg, rd = _expert_rows(c, dout_store, le)
+    cg, cu, cd = oracle.expert_wgrad_cols(rx, rg, rd, c.wg_val[le], c.wu_val[le], c.wd_val[le], sel)
+    st = torch.from_numpy(sel.astype(np.int64)).to(DEV)
+    e = max(rel_err(L.dw_gate[le][st].cpu().numpy(), cg), rel_err(L.dw_up[le][st].cpu().numpy(), cu),
+            rel_err(L.dw_down[le][:, st].cpu().numpy(), cd))
+    _log(f"  expert {le} ({len(rx)} rows) dW columns {sel.tolist()}: rel err {e:.3e}")
+    assert e <= TOL[w.prec]
+
+
+def _check_router_wgrad_full(c, L, dout_store):
+    """The whole router weight gradient over every own token: the oracle's
+    gate gradients of every routed row come from its exact FFN of all rows
+    (numpy matrix products), then dz and dW_router from the oracle."""
+    w = c.w
+    assert w.E_local == w.E and w.own == list(range(w.S))
+    lay = c.layout
+    dg = np.zeros(w.S * w.T_src * w.k)
+    for le in range(w.E_local):
+        rows = lay["row_src"][lay["offsets"][le]:lay["offsets"][le + 1]]
+        if len(rows) == 0:
+            continue
+        tt = rows // w.k
+        rx = np.stack([c.x_val[t // w.T_src][t % w.T_src] for t in tt])
+        rd = np.stack([dout_store[t // w.T_src][1][t % w.T_src] for t in tt]).astype(np.float64)
+        y = oracle.ffn_rows_exact(rx, c.wg_val[le], c.wu_val[le], c.wd_val[le])
+        dg[rows] = np.einsum("rc,rc->r", rd, y)
+    n_tok = w.S * w.T_src
+    idx = c.topk_all.reshape(n_tok, w.k)
+    dz = oracle.router_dz(idx, c.gate_all.reshape(n_tok, w.k), dg.reshape(n_tok, w.k))
+    tok_x = np.concatenate([c.x_val[s] for s in range(w.S)])
+    ref = oracle.router_wgrad(tok_x, idx, dz, w.E)
+    e = rel_err(L.dw_router.cpu().numpy(), ref)
+    _log(f"  dW_router (all {n_tok} tokens) rel err {e:.3e}")
+    assert e <= TOL[w.prec]
 
 
 @pytest.mark.parametrize("name", list(BWD_FULL))
@@ -575,23 +723,23 @@ def test_layer_bwd_full_sampled(name):
     toks = sample_tokens(w, 16)
     _check_fwd(c, L, toks)
     _bwd_sampled(c, L, dout_store, toks)
-    if not check_dw:
-        return
     lay = c.layout
     cnt = np.diff(lay["offsets"])
+    # the most-routed expert's weight gradients, on sampled columns (the
+    # chunked split-K schedule or the spread schedule, whichever the device
+    # picks for these counts, at their longest contraction)
+    _check_wgrad_columns(c, L, dout_store, int(np.argmax(cnt)))
+    if not check_dw:
+        return
     le = int(np.argmin(np.where(cnt > 0, cnt, np.iinfo(np.int64).max)))
-    rows = lay["row_src"][lay["offsets"][le]:lay["offsets"][le + 1]]
-    _log(f"  expert {le}: {len(rows)} rows")
-    tt = rows // w.k
-    jj = rows % w.k
-    rx = np.stack([c.x_val[t // w.T_src][t % w.T_src] for t in tt])
-    rg = np.array([c.gate_all[t // w.T_src, t % w.T_src, j] for t, j in zip(tt, jj)])
-    rd = np.stack([dout_store[t // w.T_src][1][t % w.T_src] for t in tt])
+    rx, rg, rd = _expert_rows(c, dout_store, le)
+    _log(f"  expert {le}: {len(rx)} rows")
     dwg, dwu, dwd = oracle.expert_wgrad(rx, rg, rd, c.wg_val[le], c.wu_val[le], c.wd_val[le])
     e_w = max(rel_err(L.dw_gate[le].cpu().numpy(), dwg), rel_err(L.dw_up[le].cpu().numpy(), dwu),
               rel_err(L.dw_down[le].cpu().numpy(), dwd))
     _log(f"  dW rel err {e_w:.3e}")
     assert e_w <= TOL[w.prec]
+    _check_router_wgrad_full(c, L, dout_store)
 
 
 def test_fwd_bwd_run_to_run_bit_identical():
@@ -649,3 +797,48 @@ def test_mx_quantize_bit_exact():
     rc, rs = oracle.mx_quantize(val.reshape(rows, K).astype(np.float64))
     np.testing.assert_array_equal(codes.cpu().numpy().reshape(rows, K), rc)
     np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, K // 32), rs)
+
+
+def _mx_rows_ref(c, rows):
+    """The oracle's MX codes and scales of the token rows behind routed rows."""
+    w = c.w
+    toks = c.layout["row_src"][rows] // w.k
+    v = np.stack([c.x_val[t // w.T_src][t % w.T_src] for t in toks]).astype(np.float64)
+    return oracle.mx_quantize(v)
+
+
+@pytest.mark.parametrize("name", ["mx_share", "c4_full"])
+def test_dispatch_mx_bytes_bit_exact(name):
+    """The MXFP8 pull dispatch quantises each gathered row: its E4M3 codes and
+    E8M0 scales equal the oracle's MX quantisation of the token rows, byte
+    for byte (every row of the small share; at full size the first and last
+    rows of every expert plus 3000 sampled rows)."""
+    w = FWD_CASES[name]
+    _log("dispatch mx bytes", name)
+    c = make_host_case(w)
+    lay = c.layout
+    R = int(lay["R"])
+    cfg = make_config(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, "mxfp8", R)
+    xq = torch.zeros(R * w.d, dtype=torch.uint8, device=DEV)
+    xs = torch.zeros(R * w.d // 32, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mok_dispatch(cfg, [to_device(a, "bf16", DEV) for a in c.x_store],
+                 torch.from_numpy(lay["row_src"]).to(DEV), torch.from_numpy(lay["offsets"]).to(DEV),
+                 xq, xs, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    if name.endswith("_full"):
+        rng = np.random.default_rng(9)
+        offs = lay["offsets"]
+        rows = set(rng.integers(0, R, 3000).tolist())
+        for e in range(w.E_local):
+            if offs[e + 1] > offs[e]:
+                rows |= {int(offs[e]), int(offs[e + 1]) - 1}
+        rows = np.array(sorted(rows))
+    else:
+        rows = np.arange(R)
+    rc, rs = _mx_rows_ref(c, rows)
+    got_c = xq.view(R, w.d)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    got_s = xs.view(R, w.d // 32)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    np.testing.assert_array_equal(got_c, rc)
+    np.testing.assert_array_equal(got_s, rs)

@@ -22,13 +22,13 @@ MAX_SOURCES = 64
 
 STATUS = {
     0: "MOK_OK", -1: "MOK_EINVAL", -2: "MOK_ESHAPE", -3: "MOK_EDEVICE", -4: "MOK_ECAPACITY",
-    -5: "MOK_ETIMEOUT", -6: "MOK_EROUTE",
+    -5: "MOK_ETIMEOUT", -6: "MOK_EROUTE", -7: "MOK_ESCRATCH",
 }
 
 # every symbol include/mok.h declares
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
-           "mok_ring_layout", "mok_hbm_stream", "mok_version")
+           "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_version")
 
 
 class MokError(RuntimeError):
@@ -218,6 +218,9 @@ def lib():
         L.mok_ring_layout.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(I32)]
         L.mok_hbm_stream.argtypes = [I32, P, P, I64, P]
+        L.mok_layer_fwd_noalloc.argtypes = [cfgp, I32, I32, P, P, P, P,
+                                            ctypes.POINTER(mok_expert_weights),
+                                            ctypes.POINTER(mok_fwd_state), P, P, P, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -380,3 +383,12 @@ def mok_hbm_stream(mode, dst, src, nbytes, stream=None):
     """HBM streaming probe: mode 0 read src, 1 write dst, 2 copy src -> dst."""
     _check("mok_hbm_stream", lib().mok_hbm_stream(mode, _ptr(dst), _ptr(src), nbytes,
                                                   _stream(stream)))
+
+
+def mok_layer_fwd_noalloc(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_local,
+                          weights: mok_expert_weights, state: mok_fwd_state, staging, out,
+                          dev_status, stream=None):
+    _check("mok_layer_fwd_noalloc", lib().mok_layer_fwd_noalloc(
+        ctypes.byref(cfg), own_lo, own_n, _table(src_x), _ptr(w_router), _ptr(bias),
+        _ptr(expert_to_local), ctypes.byref(weights), ctypes.byref(state), _table(staging),
+        _table(out) if out is not None else None, _ptr(dev_status), _stream(stream)))

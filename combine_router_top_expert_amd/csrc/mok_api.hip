@@ -2,6 +2,8 @@
 // workspace carving and launch sequencing.  No allocation, no host sync.
 #include <string.h>
 
+#include <mutex>
+
 #include "mok_internal.h"
 
 using namespace mok;
@@ -228,13 +230,22 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
                         own_n, cfg->R_cap, st, cfg->trace);
 }
 
-mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
-                         const void* const* src_x, const void* w_router, const float* bias,
-                         const int32_t* expert_to_local, const mok_expert_weights* w,
-                         const mok_fwd_state* st, void* const* staging, void* const* out,
-                         void* ws, int32_t* dev_status, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass.  layout_ws: the layout kernels' scratch (the start of ws,
+// or the no-allocation entry point's static array); ws may then be null on
+// the paths that use no other workspace (bf16, no ring).
+mok_status layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                     const void* const* src_x, const void* w_router, const float* bias,
+                     const int32_t* expert_to_local, const mok_expert_weights* w,
+                     const mok_fwd_state* st, void* const* staging, void* const* out, void* ws,
+                     void* layout_ws, int32_t* dev_status, void* stream) {
   if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
-  if (!src_x || !w_router || !expert_to_local || !w || !st || !staging || !ws) return MOK_EINVAL;
+  if (!src_x || !w_router || !expert_to_local || !w || !st || !staging || !layout_ws)
+    return MOK_EINVAL;
+  if (!ws && (cfg->prec != MOK_BF16 || cfg->ring_bytes > 0)) return MOK_EINVAL;
   if (!st->topk_idx || !st->topk_gate || !st->counts || !st->offsets || !st->dest_row)
     return MOK_EINVAL;
   if (cfg->R_cap > 0 && (!st->row_src || !st->h)) return MOK_EINVAL;
@@ -268,8 +279,8 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   }
   mok_status rc = launch_layout((int64_t)cfg->S * cfg->T_src * cfg->k, cfg->E, cfg->E_local,
                                 cfg->R_cap, st->topk_idx, expert_to_local, st->counts,
-                                st->offsets, st->row_src, st->dest_row,
-                                (char*)ws + ws_layout(cfg).layout, dev_status, sm, tr);
+                                st->offsets, st->row_src, st->dest_row, layout_ws, dev_status, sm,
+                                tr);
   if (rc != MOK_OK) return rc;
   const Ws wl = ws_layout(cfg);
   char* wsb = (char*)ws;
@@ -337,6 +348,61 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   fill_table(&o, (const void* const*)out, cfg->S);
   return launch_combine(rprec, st->dest_row, st->topk_gate, stg, o, cfg->T_src, cfg->d, cfg->k,
                         own_lo, own_n, cfg->R_cap, sm, tr);
+}
+
+// Scratch of the no-allocation forward entry point: the layout kernels'
+// per-chunk expert counts.  One copy per GPU, held until the process ends;
+// host code uses only the per-device address from hipGetSymbolAddress.
+constexpr size_t kStaticScratchBytes = MOK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until looked up
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.  Null if the runtime cannot give it.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                         const void* const* src_x, const void* w_router, const float* bias,
+                         const int32_t* expert_to_local, const mok_expert_weights* w,
+                         const mok_fwd_state* st, void* const* staging, void* const* out,
+                         void* ws, int32_t* dev_status, void* stream) {
+  if (!valid_cfg(cfg) || !ws) return MOK_EINVAL;
+  return layer_fwd(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_local, w, st, staging,
+                   out, ws, (char*)ws + ws_layout(cfg).layout, dev_status, stream);
+}
+
+mok_status mok_layer_fwd_noalloc(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                                 const void* const* src_x, const void* w_router,
+                                 const float* bias, const int32_t* expert_to_local,
+                                 const mok_expert_weights* w, const mok_fwd_state* st,
+                                 void* const* staging, void* const* out, int32_t* dev_status,
+                                 void* stream) {
+  if (!valid_cfg(cfg)) return MOK_EINVAL;
+  // the bf16 layer without the ring: the layout's counts are its only scratch
+  if (cfg->prec != MOK_BF16 || cfg->ring_bytes != 0) return MOK_EINVAL;
+  const int64_t N = (int64_t)cfg->S * cfg->T_src * cfg->k;
+  if (layout_ws_bytes(N, cfg->E_local) > kStaticScratchBytes) return MOK_ESCRATCH;
+  void* scr = static_scratch();
+  if (!scr) return MOK_EDEVICE;
+  return layer_fwd(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_local, w, st, staging,
+                   out, nullptr, scr, dev_status, stream);
 }
 
 mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,

@@ -76,7 +76,8 @@ typedef enum {
   MOK_EDEVICE = -3,    /* HIP runtime error at launch */
   MOK_ECAPACITY = -4,  /* device-latched: routed rows exceed R_cap */
   MOK_ETIMEOUT = -5,   /* device-latched: a bounded wait in the fused kernel ran out */
-  MOK_EROUTE = -6      /* device-latched: an expert id outside [0, E) in routing input */
+  MOK_EROUTE = -6,     /* device-latched: an expert id outside [0, E) in routing input */
+  MOK_ESCRATCH = -7    /* mok_layer_fwd_noalloc: cfg needs more than its static scratch */
 } mok_status;
 
 typedef enum {
@@ -252,6 +253,29 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          const int32_t* expert_to_local, const mok_expert_weights* w,
                          const mok_fwd_state* st, void* const* staging, void* const* out,
                          void* ws, int32_t* dev_status, void* stream);
+
+/* mok_layer_fwd without a workspace argument, for callers that cannot
+ * allocate device memory at all: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results as mok_layer_fwd with ring_bytes == 0 and prec == MOK_BF16 (the
+ * path whose only scratch is the layout's per-chunk expert counts); any other
+ * precision or a ring is MOK_EINVAL.  The scratch is a static device array
+ * of MOK_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; it fits ceil(S*T_src*k / 1024) * E_local * 4 bytes, so a
+ * cfg needing more returns MOK_ESCRATCH before anything is enqueued.  The
+ * call itself allocates nothing (its first call on a device looks up that
+ * device's copy of the array once).  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, or two threads)
+ * race and give undefined results; calls in stream order do not.  The array
+ * keeps the last call's contents; every value a call reads from it is
+ * written by the same call first. */
+#define MOK_NOALLOC_SCRATCH_BYTES (4u << 20)
+mok_status mok_layer_fwd_noalloc(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                                 const void* const* src_x, const void* w_router,
+                                 const float* bias, const int32_t* expert_to_local,
+                                 const mok_expert_weights* w, const mok_fwd_state* st,
+                                 void* const* staging, void* const* out, int32_t* dev_status,
+                                 void* stream);
 
 /* Backward pass [K01 two more rounds in reverse; K02 pull reverse-combine and
  * push reverse-dispatch].  Inputs: d_out (host array of S device pointers

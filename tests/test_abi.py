@@ -218,3 +218,22 @@ def test_ring_layout_host_logic(L):
         mok.mok_ring_layout(_cfg())                         # no ring
     with pytest.raises(mok.MokError):
         mok.mok_ring_layout(_cfg(prec="f32", ring_bytes=1 << 20))
+
+
+def test_noalloc_forward_rejections_on_the_host(L):
+    """mok_layer_fwd_noalloc runs the bf16 staged layer only, and refuses a
+    configuration whose layout counts outgrow its static scratch
+    (MOK_ESCRATCH) -- both before any device call."""
+    S = 2
+    full, _k = _tab(S)
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+
+    def rc(cfg):
+        return L.mok_layer_fwd_noalloc(ctypes.byref(cfg), 0, 1, full, 1, None, 1, ctypes.byref(w),
+                                       ctypes.byref(st), full, full, 1, None)
+    assert rc(_cfg(prec="f32")) == -1
+    assert rc(_cfg(prec="mxfp8")) == -1
+    assert rc(_cfg(ring_bytes=1 << 24)) == -1
+    # ceil(64 * 8192 * 16 / 1024) chunks x 256 local experts x 4 bytes = 32 MiB > 4 MiB
+    assert rc(_cfg(S=64, T_src=8192, k=16, E=256, E_local=256)) == -7

@@ -134,8 +134,16 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
         if has_bwd:
             L.backward(d_out)
 
-    for _ in range(args.warmup):
+    # warm-up: args.warmup steps, continued until 0.5 s have passed, so that
+    # the clocks have left the idle state the host-side input generation left
+    # them in (untimed)
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t_w < 0.5:
         step()
+        if i % 4 == 3:
+            torch.cuda.synchronize()
+        i += 1
     torch.cuda.synchronize()
     L.check_status()
     R = int(L.offsets[-1].item())
@@ -300,8 +308,15 @@ def hbm_stream_lines(args, torch):
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     for mode, name, moved in ((0, "read", n), (1, "write", n), (2, "copy", 2 * n)):
-        for _ in range(args.warmup):
+        # warm-up: at least args.warmup calls and 0.5 s of streaming, so that
+        # the clocks have left their idle state
+        t_w = time.perf_counter()
+        i = 0
+        while i < args.warmup or time.perf_counter() - t_w < 0.5:
             mok_hbm_stream(mode, dst, src, n)
+            if i % 8 == 7:
+                torch.cuda.synchronize()
+            i += 1
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -351,6 +366,13 @@ def run_workload(args, name, np, torch):
                      dev_in["wu"], dev_in["wd"], other_topk=other)
         return L
 
+    # the share of the 256-expert layer runs its forward through the 256 MiB
+    # ring of token slots its configuration names, with the minibatch size and
+    # dispatch split the tuner picks (untimed); the others run staged
+    if args.path == "auto" and name == "C3" and not args.ring_mib and not args.mb_sweep:
+        args = argparse.Namespace(**{**vars(args), "ring_mib": 256, "tune": True})
+    elif args.path == "staged":
+        args = argparse.Namespace(**{**vars(args), "ring_mib": 0, "tune": False})
     mbs = [int(v) for v in args.mb_sweep.split(",")] if args.mb_sweep else [args.mb]
     results = []
     for mb in mbs:
@@ -374,13 +396,16 @@ def run_workload(args, name, np, torch):
     if not args.no_cpu_baseline:
         host = {"x_val": [b for _, b in xs], "dout_val": [b for _, b in dout] if has_bwd else None,
                 "wr_val": wr[1], "bias": bias, "wg_val": wg[1], "wu_val": wu[1], "wd_val": wd[1]}
-        base = cpu_baseline(w, host, args.cpu_tokens)
+        base = cpu_baseline(w, host, args.cpu_tokens or CPU_TOKENS.get(name, 20))
         for r in results:
             r["cpu_baseline"] = base
     del dev_in, d_out
     torch.cuda.empty_cache()
     return results
 
+
+# the CPU oracle's sample per workload: about 10 s of single-threaded work
+CPU_TOKENS = {"C1": 512, "C2": 36, "C3": 160, "C4": 600, "C5": 36}
 
 # the default run: every configuration one GPU holds, the largest (the
 # headline) last
@@ -394,7 +419,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     help="C1..C5, or 'all' (C2, C4, C5, then C3, one JSON line each)")
-    ap.add_argument("--cpu-tokens", type=int, default=20)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the CPU oracle's sample (0: per workload, about 10 s of "
+                         "single-threaded work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring-mib", type=int, default=0,
                     help="forward through the persistent ring kernel with a ring of this many "
@@ -410,6 +437,10 @@ def main():
                          "mok_tune_fwd before the timed steps (untimed)")
     ap.add_argument("--mb-sweep", default="",
                     help="ring path: comma-separated minibatch sizes, one JSON line each")
+    ap.add_argument("--path", choices=["auto", "staged"], default="auto",
+                    help="auto: the 256-expert share (C3) through its 256 MiB ring with the "
+                         "tuned minibatch and split, the others staged; staged: all staged "
+                         "(--ring-mib sets the ring for every workload)")
     ap.add_argument("--hbm-stream-gib", type=float, default=0.0,
                     help="instead of the layer: the HBM streaming probe (read, write, copy) "
                          "over this many GiB")

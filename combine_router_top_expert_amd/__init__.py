@@ -342,7 +342,7 @@ def mok_tune_fwd(cfg, mbs, comms, reps, ws_bytes, own_lo, own_n, src_x, w_router
                  expert_to_local, weights: mok_expert_weights, state: mok_fwd_state, staging, out,
                  ws, dev_status, stream=None):
     """Returns (best mok_config, {(minibatch_rows, comm_wgs): mean ms or None if skipped})."""
-    mbs = list(mbs) if mbs is not None else [64, 128, 256, 512]
+    mbs = list(mbs) if mbs is not None else [64, 128, 256, 512, 1024, 2048, 4096]
     if comms is None:
         import torch
         cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count

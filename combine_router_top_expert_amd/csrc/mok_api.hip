@@ -508,14 +508,17 @@ mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
     return MOK_EINVAL;
   const int cus = device_cus();
   if (cus <= 0) return MOK_EDEVICE;
-  // default grid: the minibatch sizes of the 256-expert share's sweep and
-  // dispatch sides of 1/16 .. 1/4 of the CUs
-  const int32_t mb_def[4] = {64, 128, 256, 512};
+  // default grid: the minibatch sizes of the 256-expert share's sweep, up to
+  // the sizes where two full waves of GEMM1 tiles fit in one minibatch on 256
+  // CUs (2 x 240 tiles of 256 rows x 256 columns over 2I = 4096 columns: about
+  // 7.7k rows), and dispatch sides of 1/16 .. 1/4 of the CUs; sizes the ring
+  // cannot hold are skipped
+  const int32_t mb_def[7] = {64, 128, 256, 512, 1024, 2048, 4096};
   const int32_t comm_def[4] = {cus / 16 > 0 ? cus / 16 : 1, cus / 8 > 0 ? cus / 8 : 1,
                                3 * cus / 16 > 0 ? 3 * cus / 16 : 1, cus / 4 > 0 ? cus / 4 : 1};
   if (!mbs) {
     mbs = mb_def;
-    n_mb = 4;
+    n_mb = 7;
   }
   if (!comms) {
     comms = comm_def;

@@ -33,45 +33,125 @@ namespace {
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------ 1. pull
-template <typename T>
+// Token-major: a workgroup takes kPullTok consecutive tokens (s, t) of the
+// item order; its lanes read the tokens' k row indices at once and list the
+// tokens that have a row computed here.  For each listed token it reads the
+// upstream gradient row once into registers (lane l keeps units l, l + 256,
+// ... of the row) and serves every slot whose row is here: the dot product
+// with the pushed y row gives d_gate, and g * dout is the slot's dy row.
+// Per slot, the dot product is summed per lane in unit order, then over the
+// wave's lanes by a butterfly and over the waves in order.  UMAX = units of
+// the row a lane keeps (0: re-read per slot).
+constexpr int kPullTok = 16;
+
+template <typename T, int UMAX>
 __global__ __launch_bounds__(kThreads) void rc_pull_kernel(BwdPlan p) {
-  __shared__ float red[kThreads / 64];
-  int R = p.offsets[p.E_local];
-  if (R > p.R_cap) R = p.R_cap;
-  const int r = blockIdx.x;
-  if (r >= R) return;
-  const int n = p.row_src[r];
-  const int tok = n / p.k, j = n % p.k;
-  const int s = tok / p.T_src, t = tok % p.T_src;
-  const float g = p.topk_gate[n];
-  const T* dout = reinterpret_cast<const T*>(p.d_out.p[s]) + (size_t)t * p.d;
-  const T* y = reinterpret_cast<const T*>(p.staging.p[s]) + ((size_t)t * p.k + j) * p.d;
-  T* dy = reinterpret_cast<T*>(p.dy) + (size_t)r * p.d;
+  __shared__ float red[kThreads / 64][16];
+  __shared__ uint32_t s_loc[kPullTok];
+  __shared__ int s_list[kPullTok];
+  __shared__ int s_nlist;
   constexpr int U = 16 / sizeof(T);
-  float part = 0.0f;
-  for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
-    uint4 dv = ld16(dout + u * U), yv = ld16(y + u * U);
-    const T* de = reinterpret_cast<const T*>(&dv);
-    const T* ye = reinterpret_cast<const T*>(&yv);
-    uint4 ov;
-    T* oe = reinterpret_cast<T*>(&ov);
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const float dvf = to_f32<T>(de[i]);
-      part = __builtin_fmaf(dvf, to_f32<T>(ye[i]), part);
-      oe[i] = from_f32<T>(g * dvf);
-    }
-    st16(dy + u * U, ov);
+  const int units = p.d / U;
+  const int64_t n_tok = (int64_t)p.S * p.T_src;
+  const int64_t tok0 = (int64_t)blockIdx.x * kPullTok;
+  if (threadIdx.x < kPullTok) s_loc[threadIdx.x] = 0;
+  __syncthreads();
+  // slots with a row here (a dropped row, >= R_cap, is skipped)
+  for (int i = threadIdx.x; i < kPullTok * p.k; i += kThreads) {
+    const int64_t tok = tok0 + i / p.k;
+    if (tok >= n_tok) break;
+    const int r = p.dest_row[tok * p.k + i % p.k];
+    if (r >= 0 && r < p.R_cap) atomicOr(&s_loc[i / p.k], 1u << (i % p.k));
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float tot = 0.0f;
-    for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
-    p.d_gate[n] = tot;
+    int n = 0;
+    for (int q = 0; q < kPullTok; ++q)
+      if (s_loc[q]) s_list[n++] = q;
+    s_nlist = n;
   }
+  __syncthreads();
+  const int nlist = s_nlist;
+  for (int li = 0; li < nlist; ++li) {
+    const int q = s_list[li];
+    const uint32_t loc = s_loc[q];
+    const int64_t tok = tok0 + q;
+    const int64_t n0 = tok * p.k;
+    const int s = (int)(tok / p.T_src), t = (int)(tok % p.T_src);
+    const T* dout = reinterpret_cast<const T*>(p.d_out.p[s]) + (size_t)t * p.d;
+    const T* ybase = reinterpret_cast<const T*>(p.staging.p[s]) + (size_t)t * p.k * p.d;
+    uint4 dv[UMAX > 0 ? UMAX : 1];
+    if constexpr (UMAX > 0) {
+#pragma unroll
+      for (int i = 0; i < UMAX; ++i) {
+        const int u = threadIdx.x + i * kThreads;
+        if (u < units) dv[i] = ld16(dout + u * U);
+      }
+    }
+    for (int j = 0; j < p.k; ++j) {
+      if (!((loc >> j) & 1u)) continue;
+      const int r = p.dest_row[n0 + j];
+      const float g = p.topk_gate[n0 + j];
+      const T* y = ybase + (size_t)j * p.d;
+      T* dy = reinterpret_cast<T*>(p.dy) + (size_t)r * p.d;
+      float part = 0.0f;
+      auto unit = [&](int u, const uint4& dvu) {
+        const uint4 yv = ld16(y + u * U);
+        const T* de = reinterpret_cast<const T*>(&dvu);
+        const T* ye = reinterpret_cast<const T*>(&yv);
+        uint4 ov;
+        T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+          const float dvf = to_f32<T>(de[i]);
+          part = __builtin_fmaf(dvf, to_f32<T>(ye[i]), part);
+          oe[i] = from_f32<T>(g * dvf);
+        }
+        st16(dy + u * U, ov);
+      };
+      if constexpr (UMAX > 0) {
+#pragma unroll
+        for (int i = 0; i < UMAX; ++i) {
+          const int u = threadIdx.x + i * kThreads;
+          if (u < units) unit(u, dv[i]);
+        }
+      } else {
+        for (int u = threadIdx.x; u < units; u += kThreads) unit(u, ld16(dout + u * U));
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][j] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < 16 && threadIdx.x < p.k && ((loc >> threadIdx.x) & 1u)) {
+      float tot = 0.0f;
+      for (int w = 0; w < kThreads / 64; ++w) tot += red[w][threadIdx.x];
+      p.d_gate[n0 + threadIdx.x] = tot;
+    }
+    __syncthreads();  // red is read before the next token's slots write it
+  }
+}
+
+template <typename T>
+mok_status launch_rc_pull(const BwdPlan& p, hipStream_t stream) {
+  const int64_t n_tok = (int64_t)p.S * p.T_src;
+  if (n_tok == 0 || p.R_cap == 0) return MOK_OK;
+  const int64_t blocks = (n_tok + kPullTok - 1) / kPullTok;
+  const int units = p.d / (16 / (int)sizeof(T));
+  const int per_lane = (units + kThreads - 1) / kThreads;
+  dim3 g((unsigned)blocks), b(kThreads);
+  if (per_lane <= 1)
+    hipLaunchKernelGGL((rc_pull_kernel<T, 1>), g, b, 0, stream, p);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL((rc_pull_kernel<T, 2>), g, b, 0, stream, p);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL((rc_pull_kernel<T, 4>), g, b, 0, stream, p);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL((rc_pull_kernel<T, 8>), g, b, 0, stream, p);
+  else
+    hipLaunchKernelGGL((rc_pull_kernel<T, 0>), g, b, 0, stream, p);
+  trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
 // ------------------------------------------------------------------ 2. dh + SwiGLU'
@@ -435,9 +515,9 @@ mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
   hipEvent_t fork = p.aux_ev[0], gx_ready = p.aux_ev[1], dx_pushed = p.aux_ev[2];
   // the pull is HBM-bound like the side work: fork after it, so the side
   // work meets the dh GEMM instead
-  if (p.R_cap > 0) {
-    hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
-    trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
+  {
+    mok_status rc = launch_rc_pull<T>(p, stream);
+    if (rc != MOK_OK) return rc;
   }
   MOK_HIP_CHECK(hipEventRecord(fork, stream));
   MOK_HIP_CHECK(hipStreamWaitEvent(aux, fork, 0));
@@ -496,9 +576,9 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
     if (p.aux) return run_bwd_two_streams<T>(p, stream);
     if (p.R_cap > 0) {
-      hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
-      trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
-      mok_status rc = launch_gather_t(p, p.x_perm, stream);
+      mok_status rc = launch_rc_pull<T>(p, stream);
+      if (rc != MOK_OK) return rc;
+      rc = launch_gather_t(p, p.x_perm, stream);
       if (rc != MOK_OK) return rc;
       trace_mark(p.tr, "bwd_regather_x", stream);
     }
@@ -507,8 +587,8 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   } else {
   if (p.R_cap > 0) {
     const int mt = grouped_mtiles_bound(p.R_cap, p.E_local);
-    hipLaunchKernelGGL(rc_pull_kernel<T>, dim3(p.R_cap), dim3(kThreads), 0, stream, p);
-    trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
+    mok_status rc = launch_rc_pull<T>(p, stream);
+    if (rc != MOK_OK) return rc;
     int ntn = (p.I + kBN - 1) / kBN;
     hipLaunchKernelGGL(dh_kernel<T>, dim3(mt * ntn), dim3(kGemmThreads), 0, stream, p, ntn);
     trace_mark(p.tr, "bwd_dh_swiglu", stream);

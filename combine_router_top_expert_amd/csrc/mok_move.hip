@@ -44,49 +44,65 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
 }
 
 // MX gather: a 32-element block is 4 consecutive 16-byte units (4 lanes).
+// The block's rows (kGatherRows) are loaded together before any is
+// quantised, so that many 16-byte loads per lane are in flight at once.
+constexpr int kGatherRows = 4;
+
+__device__ __forceinline__ void mx_encode_unit(const uint4& q, bool have, uint8_t* dst,
+                                               uint8_t* dsc, int u) {
+  float v[8];
+  float amax = 0.0f;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (!have) amax = 0.0f;
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  if (have) {
+    const int sh = mx_shared_exp(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[i], -sh)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + i], -sh)) << (8 * i);
+    *reinterpret_cast<uint2*>(dst + u * 8) = make_uint2(lo, hi);
+    if ((u & 3) == 0) dsc[u >> 2] = (uint8_t)(sh + 127);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void gather_mx_kernel(GatherArgs a) {
   int R = a.offsets[a.E_local];
   if (R > a.R_cap) R = a.R_cap;
   const int units = a.d / 8;
-  const int r0 = blockIdx.x * a.rows_per_block;
-  for (int rr = 0; rr < a.rows_per_block; ++rr) {
-    const int r = r0 + rr;
-    if (r >= R) return;
-    const int n = a.row_src[r];
+  const int r0 = blockIdx.x * kGatherRows;
+  if (r0 >= R) return;
+  const int nr = min(kGatherRows, R - r0);
+  const bf16_t* src[kGatherRows];
+#pragma unroll
+  for (int rr = 0; rr < kGatherRows; ++rr) {
+    const int n = a.row_src[r0 + min(rr, nr - 1)];
     const int tok = n / a.k;
     const int s = tok / a.T_src, t = tok % a.T_src;
-    const bf16_t* src = reinterpret_cast<const bf16_t*>(a.src.p[s]) + (size_t)t * a.d;
-    uint8_t* dst = reinterpret_cast<uint8_t*>(a.dst) + (size_t)r * a.d;
-    uint8_t* dsc = a.dst_scale + (size_t)r * (a.d / 32);
-    for (int u0 = 0; u0 < units; u0 += kThreads) {
-      const int u = u0 + threadIdx.x;
-      const bool have = u < units;  // units % 4 == 0: a 4-lane group is all in or all out
-      float v[8];
-      float amax = 0.0f;
-      if (have) {
-        uint4 q = ld16(src + u * 8);
-        uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    src[rr] = reinterpret_cast<const bf16_t*>(a.src.p[s]) + (size_t)t * a.d;
+  }
+  for (int u0 = 0; u0 < units; u0 += kThreads) {
+    const int u = u0 + threadIdx.x;
+    const bool have = u < units;  // units % 4 == 0: a 4-lane group is all in or all out
+    uint4 q[kGatherRows];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(w[i] << 16);
-          v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
+    for (int rr = 0; rr < kGatherRows; ++rr)
+      q[rr] = (have && rr < nr) ? ld16(src[rr] + u * 8) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      }
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-      if (have) {
-        const int sh = mx_shared_exp(amax);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[i], -sh)) << (8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + i], -sh)) << (8 * i);
-        *reinterpret_cast<uint2*>(dst + u * 8) = make_uint2(lo, hi);
-        if ((u & 3) == 0) dsc[u >> 2] = (uint8_t)(sh + 127);
-      }
+    for (int rr = 0; rr < kGatherRows; ++rr) {
+      if (rr >= nr) break;  // uniform over the block
+      const int r = r0 + rr;
+      mx_encode_unit(q[rr], have, reinterpret_cast<uint8_t*>(a.dst) + (size_t)r * a.d,
+                     a.dst_scale + (size_t)r * (a.d / 32), u);
     }
   }
 }
@@ -132,7 +148,13 @@ struct CombineArgs {
   int tok_per_block;
 };
 
-template <typename T>
+// A token's k slot units are loaded together before any is summed (K known
+// at compile time for the common top-k values, so the k 16-byte loads per
+// lane go out back to back); a slot that is not summed -- a local row
+// dropped beyond R_cap -- is loaded from its staging row (which exists) and
+// left out of the sum, which keeps the sum's order and rounding.  K = 0:
+// any k, one slot at a time.
+template <typename T, int K>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int U = 16 / sizeof(T);
   const int units = a.d / U;
@@ -144,20 +166,33 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int64_t n0 = ((int64_t)s * a.T_src + t) * a.k;
     const T* stg = reinterpret_cast<const T*>(a.staging.p[s]) + (size_t)t * a.k * a.d;
     T* o = reinterpret_cast<T*>(a.out.p[s]) + (size_t)t * a.d;
+    // every slot but a local row dropped beyond R_cap: a remote slot (row
+    // -1) holds what the GPU with that expert pushed here
     for (int u = threadIdx.x; u < units; u += kThreads) {
       float acc[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) acc[i] = 0.0f;
-      for (int j = 0; j < a.k; ++j) {
-        // every slot but a local row dropped beyond R_cap: a remote slot
-        // (row -1) holds what the GPU with that expert pushed here
-        const int row = a.dest_row[n0 + j];
-        if (row >= a.R_cap) continue;
-        const float gj = a.gate[n0 + j];
-        uint4 v = ld16(stg + (size_t)j * a.d + u * U);
-        const T* e = reinterpret_cast<const T*>(&v);
+      if constexpr (K > 0) {
+        uint4 v[K];
 #pragma unroll
-        for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(gj, to_f32<T>(e[i]), acc[i]);
+        for (int j = 0; j < K; ++j) v[j] = ld16(stg + (size_t)j * a.d + u * U);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          if (a.dest_row[n0 + j] >= a.R_cap) continue;
+          const float gj = a.gate[n0 + j];
+          const T* e = reinterpret_cast<const T*>(&v[j]);
+#pragma unroll
+          for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(gj, to_f32<T>(e[i]), acc[i]);
+        }
+      } else {
+        for (int j = 0; j < a.k; ++j) {
+          if (a.dest_row[n0 + j] >= a.R_cap) continue;
+          const float gj = a.gate[n0 + j];
+          const uint4 v = ld16(stg + (size_t)j * a.d + u * U);
+          const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+          for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(gj, to_f32<T>(e[i]), acc[i]);
+        }
       }
       uint4 outv;
       T* ov = reinterpret_cast<T*>(&outv);
@@ -228,7 +263,7 @@ mok_status launch_gather(int prec, const SrcTable& src, int T_src, int d, int k,
   a.k = k;
   a.E_local = E_local;
   a.R_cap = R_cap;
-  a.rows_per_block = 4;
+  a.rows_per_block = prec == MOK_MXFP8 ? kGatherRows : 4;
   dim3 grid((R_cap + a.rows_per_block - 1) / a.rows_per_block);
   if (prec == MOK_F32)
     hipLaunchKernelGGL(gather_kernel<float>, grid, dim3(kThreads), 0, stream, a);
@@ -281,10 +316,17 @@ mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
   a.tok_per_block = 2;
   if (a.n_tok == 0) return MOK_OK;
   dim3 grid((unsigned)((a.n_tok + a.tok_per_block - 1) / a.tok_per_block));
-  if (prec == MOK_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, a);
+  if (prec == MOK_F32) {
+    hipLaunchKernelGGL((combine_kernel<float, 0>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    switch (k) {
+      case 2: hipLaunchKernelGGL((combine_kernel<bf16_t, 2>), grid, dim3(kThreads), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((combine_kernel<bf16_t, 4>), grid, dim3(kThreads), 0, stream, a); break;
+      case 6: hipLaunchKernelGGL((combine_kernel<bf16_t, 6>), grid, dim3(kThreads), 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((combine_kernel<bf16_t, 8>), grid, dim3(kThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((combine_kernel<bf16_t, 0>), grid, dim3(kThreads), 0, stream, a);
+    }
+  }
   trace_mark(tr, "combine", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }

@@ -136,7 +136,7 @@ class MoELayer:
         mok_tune_fwd (off the timed path; synchronises).  The workspace grows
         to fit every candidate first.  Returns {(minibatch_rows, comm_wgs):
         ms per forward or None}; self.cfg holds the fastest pair after."""
-        mbs = list(mbs) if mbs is not None else [64, 128, 256, 512]
+        mbs = list(mbs) if mbs is not None else [64, 128, 256, 512, 1024, 2048, 4096]
         need = self.ws.numel()
         for mb in mbs:
             c = type(self.cfg).from_buffer_copy(self.cfg)

@@ -313,8 +313,8 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
  * minibatch_rows = mbs[i], comm_wgs = comms[j], gemm_wgs = 0 (the remaining
  * CUs) -- it runs mok_layer_fwd once to warm up and then `reps` times
  * (1..1000) between two HIP events, with the arguments of mok_layer_fwd.
- * mbs / comms: host arrays of 1..64 entries, or NULL for {64, 128, 256, 512}
- * rows and {1/16, 1/8, 3/16, 1/4} of the CUs.  cfg->ring_bytes and
+ * mbs / comms: host arrays of 1..64 entries, or NULL for {64, 128, 256, 512,
+ * 1024, 2048, 4096} rows and {1/16, 1/8, 3/16, 1/4} of the CUs.  cfg->ring_bytes and
  * cfg->R_cap must be > 0.  ws_bytes: size of ws; a candidate whose
  * mok_workspace_bytes exceeds it, or that the ring cannot take (no slot of
  * that many rows, a split beyond the CUs), is skipped.  Outputs:
@@ -347,9 +347,10 @@ mok_status mok_ring_layout(const mok_config* cfg, size_t* offset, size_t* slot_b
 /* HBM streaming probe: the bandwidth ceiling the layer's data-movement
  * kernels are measured against.  Moves `bytes` (a multiple of 16) with
  * 16-byte vector loads and stores, the access of those kernels.  mode 0:
- * read src (dst must hold 256 * 16 * CUs * 4 bytes; nothing is written there
- * for any real data); 1: write dst; 2: copy src to dst.  Pointers 16-byte
- * aligned, device memory.  MOK_EINVAL on a bad mode, size or pointer. */
+ * read src (dst must hold `bytes` too; a word is written there only in the
+ * unlikely case that a lane's folded words equal a fixed pattern); 1: write
+ * dst; 2: copy src to dst.  Pointers 16-byte aligned, device memory.
+ * MOK_EINVAL on a bad mode, size or pointer. */
 mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t bytes, void* stream);
 
 /* MX quantisation of rows of bf16 values (weight preparation off the timed

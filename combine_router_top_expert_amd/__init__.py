@@ -28,7 +28,8 @@ STATUS = {
 # every symbol include/mok.h declares
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
-           "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_version")
+           "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_layer_fwd_macro",
+           "mok_version")
 
 
 class MokError(RuntimeError):
@@ -185,6 +186,14 @@ class mok_fwd_state(ctypes.Structure):
                 ("h", ctypes.c_void_p), ("ab", ctypes.c_void_p)]
 
 
+class mok_layer_call(ctypes.Structure):
+    _fields_ = [("own_lo", ctypes.c_int32), ("own_n", ctypes.c_int32),
+                ("src_x", ctypes.c_void_p), ("st", ctypes.POINTER(mok_fwd_state)),
+                ("staging", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+MAX_CALLS = 8
+
 _lib = None
 
 
@@ -221,6 +230,8 @@ def lib():
         L.mok_layer_fwd_noalloc.argtypes = [cfgp, I32, I32, P, P, P, P,
                                             ctypes.POINTER(mok_expert_weights),
                                             ctypes.POINTER(mok_fwd_state), P, P, P, P]
+        L.mok_layer_fwd_macro.argtypes = [cfgp, I32, ctypes.POINTER(mok_layer_call), P, P, P,
+                                          ctypes.POINTER(mok_expert_weights), P, P, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -392,3 +403,21 @@ def mok_layer_fwd_noalloc(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_l
         ctypes.byref(cfg), own_lo, own_n, _table(src_x), _ptr(w_router), _ptr(bias),
         _ptr(expert_to_local), ctypes.byref(weights), ctypes.byref(state), _table(staging),
         _table(out) if out is not None else None, _ptr(dev_status), _stream(stream)))
+
+
+def mok_layer_fwd_macro(cfg, calls, w_router, bias, expert_to_local, weights: mok_expert_weights,
+                        ws, dev_status, stream=None):
+    """calls: list of dicts with own_lo, own_n, src_x, state (mok_fwd_state),
+    staging, out -- one per layer call (macrobatch)."""
+    keep = []
+    arr = (mok_layer_call * len(calls))()
+    for i, c in enumerate(calls):
+        src, stg = _table(c["src_x"]), _table(c["staging"])
+        out = _table(c["out"]) if c["out"] is not None else None
+        keep += [src, stg, out, c["state"]]
+        arr[i] = mok_layer_call(c["own_lo"], c["own_n"], ctypes.cast(src, ctypes.c_void_p),
+                                ctypes.pointer(c["state"]), ctypes.cast(stg, ctypes.c_void_p),
+                                ctypes.cast(out, ctypes.c_void_p) if out is not None else None)
+    _check("mok_layer_fwd_macro", lib().mok_layer_fwd_macro(
+        ctypes.byref(cfg), len(calls), arr, _ptr(w_router), _ptr(bias), _ptr(expert_to_local),
+        ctypes.byref(weights), _ptr(ws), _ptr(dev_status), _stream(stream)))

@@ -53,14 +53,15 @@ Ws ws_layout(const mok_config* c) {
   f += align256(c->prec == MOK_MXFP8 ? R * c->d : R * c->d * act_bytes(c->prec));
   w.xscale = f;
   f += align256(c->prec == MOK_MXFP8 ? R * (c->d / 32) : 0);
-  w.hscale = f;
-  f += align256(c->prec == MOK_MXFP8 ? R * (c->I / 32) : 0);
+  w.hscale = f;  // MXFP8: scales of h, one region per call of the ring path
+  f += align256(c->prec == MOK_MXFP8 ? R * (c->I / 32) * (c->ring_bytes > 0 ? kRingMaxCalls : 1)
+                                     : 0);
   w.ring = f;
   w.ring_ctr = f;
   if (c->ring_bytes > 0) {
     f += align256((size_t)c->ring_bytes);
     w.ring_ctr = f;
-    f += align256(ring_counter_bytes(c->R_cap, c->E_local, c->minibatch_rows));
+    f += align256(ring_meta_bytes(c->R_cap, c->E_local, c->minibatch_rows));
   }
   // backward pieces (same region)
   size_t b = base;
@@ -234,18 +235,12 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
 
 namespace {
 
-// The forward pass.  layout_ws: the layout kernels' scratch (the start of ws,
-// or the no-allocation entry point's static array); ws may then be null on
-// the paths that use no other workspace (bf16, no ring).
-mok_status layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
-                     const void* const* src_x, const void* w_router, const float* bias,
-                     const int32_t* expert_to_local, const mok_expert_weights* w,
-                     const mok_fwd_state* st, void* const* staging, void* const* out, void* ws,
-                     void* layout_ws, int32_t* dev_status, void* stream) {
-  if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
-  if (!src_x || !w_router || !expert_to_local || !w || !st || !staging || !layout_ws)
-    return MOK_EINVAL;
-  if (!ws && (cfg->prec != MOK_BF16 || cfg->ring_bytes > 0)) return MOK_EINVAL;
+// Arguments of one forward call (the state, per-source tables and outputs).
+mok_status check_call(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                      const void* const* src_x, const mok_fwd_state* st, void* const* staging,
+                      void* const* out) {
+  if (!own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
+  if (!src_x || !st || !staging) return MOK_EINVAL;
   if (!st->topk_idx || !st->topk_gate || !st->counts || !st->offsets || !st->dest_row)
     return MOK_EINVAL;
   if (cfg->R_cap > 0 && (!st->row_src || !st->h)) return MOK_EINVAL;
@@ -258,65 +253,126 @@ mok_status layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
       !own_sources_set((const void* const*)staging, own_lo, own_n, cfg->T_src) ||
       !own_sources_set((const void* const*)out, own_lo, own_n, cfg->T_src))
     return MOK_EINVAL;
-  if (cfg->ring_bytes > 0 && cfg->R_cap > 0) {  // ring path: bf16 / MXFP8
+  return MOK_OK;
+}
+
+// Router of the own sources, then the layout of all sources' items.
+mok_status route_and_layout(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                            const void* const* src_x, const void* w_router, const float* bias,
+                            const int32_t* expert_to_local, const mok_fwd_state* st,
+                            void* layout_ws, int32_t* dev_status, hipStream_t sm, mok_trace* tr) {
+  const int64_t per_src = (int64_t)cfg->T_src * cfg->k;
+  const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
+  SrcTable src;
+  fill_table(&src, src_x, cfg->S);
+  mok_status rc = launch_route(rprec, src, own_lo, cfg->T_src, own_n * cfg->T_src, cfg->d, cfg->E,
+                               cfg->k, w_router, bias, st->topk_idx + own_lo * per_src,
+                               st->topk_gate + own_lo * per_src, sm, tr);
+  if (rc != MOK_OK) return rc;
+  return launch_layout((int64_t)cfg->S * cfg->T_src * cfg->k, cfg->E, cfg->E_local, cfg->R_cap,
+                       st->topk_idx, expert_to_local, st->counts, st->offsets, st->row_src,
+                       st->dest_row, layout_ws, dev_status, sm, tr);
+}
+
+// One call's descriptor for the ring kernel.
+RingCall ring_call(const mok_config* cfg, int32_t own_lo, int32_t own_n, const void* const* src_x,
+                   const mok_fwd_state* st, void* const* staging, void* const* out,
+                   uint8_t* h_scale) {
+  RingCall c;
+  memset(&c, 0, sizeof(c));
+  fill_table(&c.src, src_x, cfg->S);
+  fill_table(&c.staging, (const void* const*)staging, cfg->S);
+  if (out) fill_table(&c.out, (const void* const*)out, cfg->S);
+  c.row_src = st->row_src;
+  c.offsets = st->offsets;
+  c.dest_row = st->dest_row;
+  c.gate = st->topk_gate;
+  c.h = st->h;
+  c.h_scale = h_scale;
+  c.ab = cfg->prec == MOK_BF16 ? st->ab : nullptr;
+  c.own_lo = own_lo;
+  c.own_n = own_n;
+  return c;
+}
+
+// The ring launch of n_calls calls (descriptors on the host).
+mok_status run_ring(const mok_config* cfg, int n_calls, const RingCall* calls,
+                    const mok_expert_weights* w, char* wsb, int32_t* dev_status, hipStream_t sm,
+                    mok_trace* tr) {
+  const Ws wl = ws_layout(cfg);
+  RingPlan p;
+  memset(&p, 0, sizeof(p));
+  p.prec = cfg->prec;
+  p.n_calls = n_calls;
+  p.calls = calls;
+  p.d = cfg->d;
+  p.I = cfg->I;
+  p.E_local = cfg->E_local;
+  p.R_cap = cfg->R_cap;
+  p.T_src = cfg->T_src;
+  p.k = cfg->k;
+  p.mb = cfg->minibatch_rows;
+  p.ring_bytes = cfg->ring_bytes;
+  p.comm_wgs = cfg->comm_wgs;
+  p.gemm_wgs = cfg->gemm_wgs;
+  p.wait_limit_us = cfg->wait_limit_us;
+  p.ring = wsb + wl.ring;
+  p.meta = wsb + wl.ring_ctr;
+  p.status = dev_status;
+  p.w = w;
+  return launch_ring_fwd(p, sm, tr);
+}
+
+// The final weighted combine of a ring launch's last call (the earlier
+// calls' combines run inside the ring kernel).
+mok_status last_combine(const mok_config* cfg, const RingCall& c, hipStream_t sm, mok_trace* tr) {
+  if (c.own_n == 0) return MOK_OK;
+  return launch_combine(cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16, c.dest_row, c.gate, c.staging,
+                        c.out, cfg->T_src, cfg->d, cfg->k, c.own_lo, c.own_n, cfg->R_cap, sm, tr);
+}
+
+// The forward pass.  layout_ws: the layout kernels' scratch (the start of ws,
+// or the no-allocation entry point's static array); ws may then be null on
+// the paths that use no other workspace (bf16, no ring).
+mok_status layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
+                     const void* const* src_x, const void* w_router, const float* bias,
+                     const int32_t* expert_to_local, const mok_expert_weights* w,
+                     const mok_fwd_state* st, void* const* staging, void* const* out, void* ws,
+                     void* layout_ws, int32_t* dev_status, void* stream) {
+  if (!valid_cfg(cfg)) return MOK_EINVAL;
+  if (!w_router || !expert_to_local || !w || !layout_ws) return MOK_EINVAL;
+  if (!ws && (cfg->prec != MOK_BF16 || cfg->ring_bytes > 0)) return MOK_EINVAL;
+  mok_status rc = check_call(cfg, own_lo, own_n, src_x, st, staging, out);
+  if (rc != MOK_OK) return rc;
+  const bool ring = cfg->ring_bytes > 0 && cfg->R_cap > 0;
+  if (ring) {  // ring path: bf16 / MXFP8
     if (!dev_status) return MOK_EINVAL;
-    const mok_status rc = ring_check(cfg->prec, cfg->d, cfg->I, cfg->minibatch_rows,
-                                     cfg->ring_bytes, cfg->comm_wgs, cfg->gemm_wgs, nullptr, nullptr);
+    rc = ring_check(cfg->prec, cfg->d, cfg->I, cfg->minibatch_rows, cfg->ring_bytes, cfg->comm_wgs,
+                    cfg->gemm_wgs, nullptr, nullptr);
     if (rc != MOK_OK) return rc;
   }
   hipStream_t sm = (hipStream_t)stream;
   mok_trace* tr = cfg->trace;
   trace_mark(tr, "start", sm);
-  const int64_t per_src = (int64_t)cfg->T_src * cfg->k;
   const int rprec = cfg->prec == MOK_F32 ? MOK_F32 : MOK_BF16;
-  {
-    SrcTable src;
-    fill_table(&src, src_x, cfg->S);
-    mok_status rc = launch_route(rprec, src, own_lo, cfg->T_src, own_n * cfg->T_src, cfg->d,
-                                 cfg->E, cfg->k, w_router, bias, st->topk_idx + own_lo * per_src,
-                                 st->topk_gate + own_lo * per_src, sm, tr);
-    if (rc != MOK_OK) return rc;
-  }
-  mok_status rc = launch_layout((int64_t)cfg->S * cfg->T_src * cfg->k, cfg->E, cfg->E_local,
-                                cfg->R_cap, st->topk_idx, expert_to_local, st->counts,
-                                st->offsets, st->row_src, st->dest_row, layout_ws, dev_status, sm,
-                                tr);
+  rc = route_and_layout(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_local, st, layout_ws,
+                        dev_status, sm, tr);
   if (rc != MOK_OK) return rc;
   const Ws wl = ws_layout(cfg);
   char* wsb = (char*)ws;
+  if (ring) {
+    // one persistent launch: dispatch workgroups fill ring slots, GEMM
+    // workgroups run GEMM1 + SwiGLU and GEMM2 and push to staging, and the
+    // dispatch side runs the final weighted combine once the pushes are in
+    const RingCall c = ring_call(cfg, own_lo, own_n, src_x, st, staging, out,
+                                 (uint8_t*)(wsb + wl.hscale));
+    rc = run_ring(cfg, 1, &c, w, wsb, dev_status, sm, tr);
+    if (rc != MOK_OK) return rc;
+    return last_combine(cfg, c, sm, tr);
+  }
   DstTable stg;
   fill_table(&stg, (const void* const*)staging, cfg->S);
-  if (cfg->R_cap > 0 && cfg->ring_bytes > 0) {
-    // one persistent launch: dispatch workgroups fill ring slots, GEMM
-    // workgroups run GEMM1 + SwiGLU and GEMM2 and push to staging
-    RingPlan p;
-    memset(&p, 0, sizeof(p));
-    p.prec = cfg->prec;
-    fill_table(&p.src, src_x, cfg->S);
-    p.row_src = st->row_src;
-    p.offsets = st->offsets;
-    p.d = cfg->d;
-    p.I = cfg->I;
-    p.E_local = cfg->E_local;
-    p.R_cap = cfg->R_cap;
-    p.T_src = cfg->T_src;
-    p.k = cfg->k;
-    p.mb = cfg->minibatch_rows;
-    p.ring_bytes = cfg->ring_bytes;
-    p.comm_wgs = cfg->comm_wgs;
-    p.gemm_wgs = cfg->gemm_wgs;
-    p.wait_limit_us = cfg->wait_limit_us;
-    p.ring = wsb + wl.ring;
-    p.counters = (int32_t*)(wsb + wl.ring_ctr);
-    p.status = dev_status;
-    p.w = w;
-    p.h = st->h;
-    p.h_scale = (uint8_t*)(wsb + wl.hscale);
-    p.ab = cfg->prec == MOK_BF16 ? st->ab : nullptr;
-    p.staging = stg;
-    rc = launch_ring_fwd(p, sm, tr);
-    if (rc != MOK_OK) return rc;
-  } else if (cfg->R_cap > 0) {
+  if (cfg->R_cap > 0) {
     SrcTable src;
     fill_table(&src, src_x, cfg->S);
     if (cfg->prec == MOK_MXFP8) {
@@ -386,6 +442,62 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   if (!valid_cfg(cfg) || !ws) return MOK_EINVAL;
   return layer_fwd(cfg, own_lo, own_n, src_x, w_router, bias, expert_to_local, w, st, staging,
                    out, ws, (char*)ws + ws_layout(cfg).layout, dev_status, stream);
+}
+
+mok_status mok_layer_fwd_macro(const mok_config* cfg, int32_t n_calls,
+                               const mok_layer_call* calls, const void* w_router,
+                               const float* bias, const int32_t* expert_to_local,
+                               const mok_expert_weights* w, void* ws, int32_t* dev_status,
+                               void* stream) {
+  if (!valid_cfg(cfg) || !calls || n_calls < 1 || n_calls > MOK_MAX_CALLS) return MOK_EINVAL;
+  if (cfg->ring_bytes <= 0 || (cfg->prec != MOK_BF16 && cfg->prec != MOK_MXFP8)) return MOK_EINVAL;
+  if (!w_router || !expert_to_local || !w || !ws || !dev_status) return MOK_EINVAL;
+  for (int c = 0; c < n_calls; ++c) {
+    const mok_status rc = check_call(cfg, calls[c].own_lo, calls[c].own_n, calls[c].src_x,
+                                     calls[c].st, calls[c].staging, calls[c].out);
+    if (rc != MOK_OK) return rc;
+  }
+  if (cfg->R_cap > 0) {
+    const mok_status rc = ring_check(cfg->prec, cfg->d, cfg->I, cfg->minibatch_rows,
+                                     cfg->ring_bytes, cfg->comm_wgs, cfg->gemm_wgs, nullptr,
+                                     nullptr);
+    if (rc != MOK_OK) return rc;
+  }
+  hipStream_t sm = (hipStream_t)stream;
+  mok_trace* tr = cfg->trace;
+  trace_mark(tr, "start", sm);
+  const Ws wl = ws_layout(cfg);
+  char* wsb = (char*)ws;
+  // every call's routing and layout first (the layout scratch is reused in
+  // stream order), then one ring launch for all of them
+  for (int c = 0; c < n_calls; ++c) {
+    const mok_status rc = route_and_layout(cfg, calls[c].own_lo, calls[c].own_n, calls[c].src_x,
+                                           w_router, bias, expert_to_local, calls[c].st,
+                                           wsb + wl.layout, dev_status, sm, tr);
+    if (rc != MOK_OK) return rc;
+  }
+  if (cfg->R_cap == 0) {  // no rows: only the combines of remote slots
+    for (int c = 0; c < n_calls; ++c) {
+      if (calls[c].own_n == 0) continue;
+      DstTable stg, o;
+      fill_table(&stg, (const void* const*)calls[c].staging, cfg->S);
+      fill_table(&o, (const void* const*)calls[c].out, cfg->S);
+      const mok_status rc =
+          launch_combine(MOK_BF16, calls[c].st->dest_row, calls[c].st->topk_gate, stg, o,
+                         cfg->T_src, cfg->d, cfg->k, calls[c].own_lo, calls[c].own_n, cfg->R_cap,
+                         sm, tr);
+      if (rc != MOK_OK) return rc;
+    }
+    return MOK_OK;
+  }
+  RingCall rc_calls[MOK_MAX_CALLS];
+  for (int c = 0; c < n_calls; ++c)
+    rc_calls[c] = ring_call(cfg, calls[c].own_lo, calls[c].own_n, calls[c].src_x, calls[c].st,
+                            calls[c].staging, calls[c].out,
+                            (uint8_t*)(wsb + wl.hscale) + (size_t)c * cfg->R_cap * (cfg->I / 32));
+  const mok_status rc = run_ring(cfg, n_calls, rc_calls, w, wsb, dev_status, sm, tr);
+  if (rc != MOK_OK) return rc;
+  return last_combine(cfg, rc_calls[n_calls - 1], sm, tr);
 }
 
 mok_status mok_layer_fwd_noalloc(const mok_config* cfg, int32_t own_lo, int32_t own_n,

@@ -32,7 +32,7 @@ __device__ __forceinline__ bool launch_tile(const int32_t* offsets, int E_local,
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads, C::OCC) void ffn1_g2(F1Args a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void ffn1_g2(F1Args a, SrcTable src) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
   GTile g;
@@ -43,18 +43,18 @@ __global__ __launch_bounds__(kThreads, C::OCC) void ffn1_g2(F1Args a) {
     if (r >= g.r1) return nullptr;
     if (a.x) return a.x + (size_t)r * a.d;
     const int tok = a.row_src[r] / a.k;
-    return reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) + (size_t)(tok % a.T_src) * a.d;
+    return reinterpret_cast<const bf16_t*>(src.p[tok / a.T_src]) + (size_t)(tok % a.T_src) * a.d;
   });
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads, C::OCC) void ffn2_g2(F2Args a) {
+__global__ __launch_bounds__(kThreads, C::OCC) void ffn2_g2(F2Args a, DstTable staging) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
   GTile g;
   int nt;
   if (!launch_tile(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, &g, &nt)) return;
-  ffn2_tile<C>(a, smem, g, nt);
+  ffn2_tile<C>(a, staging, smem, g, nt);
 }
 
 __global__ __launch_bounds__(kThreads) void ffn1_mx(F1MxArgs a) {
@@ -76,13 +76,13 @@ __global__ __launch_bounds__(kThreads) void ffn1_mx(F1MxArgs a) {
       });
 }
 
-__global__ __launch_bounds__(kThreads) void ffn2_mx(F2Args a) {
+__global__ __launch_bounds__(kThreads) void ffn2_mx(F2Args a, DstTable staging) {
   __shared__ __attribute__((aligned(16))) char smem[MxCfg::SMEM];
   __shared__ int s_prefix[257];
   GTile g;
   int nt;
   if (!launch_tile(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, &g, &nt)) return;
-  ffn2_mx_tile(a, smem, g, nt);
+  ffn2_mx_tile(a, staging, smem, g, nt);
 }
 
 }  // namespace
@@ -95,8 +95,11 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
   if (R_cap == 0) return MOK_OK;
   const int mt = (R_cap + BM - 1) / BM + E_local;
   F1Args a1;
+  memset(&a1, 0, sizeof(a1));
+  SrcTable stab;
+  memset(&stab, 0, sizeof(stab));
+  if (src) stab = *src;
   a1.x = reinterpret_cast<const bf16_t*>(x);
-  if (src) a1.src = *src;
   a1.row_src = row_src;
   a1.wg = reinterpret_cast<const bf16_t*>(wg);
   a1.wu = reinterpret_cast<const bf16_t*>(wu);
@@ -110,7 +113,8 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
   a1.ntn = (I + Default::BN / 2 - 1) / (Default::BN / 2);
   a1.T_src = T_src;
   a1.k = k;
-  hipLaunchKernelGGL(ffn1_g2<Default>, dim3((unsigned)(mt * a1.ntn)), dim3(kThreads), 0, stream, a1);
+  hipLaunchKernelGGL(ffn1_g2<Default>, dim3((unsigned)(mt * a1.ntn)), dim3(kThreads), 0, stream, a1,
+                     stab);
   trace_mark(tr, "ffn1_gate_up_swiglu", stream);
   F2Args a2;
   memset(&a2, 0, sizeof(a2));
@@ -120,7 +124,9 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
   a2.row_src = row_src;
   a2.y = reinterpret_cast<bf16_t*>(y);
   a2.push = staging != nullptr;
-  if (staging) a2.staging = *staging;
+  DstTable gtab;
+  memset(&gtab, 0, sizeof(gtab));
+  if (staging) gtab = *staging;
   a2.d = d;
   a2.I = I;
   a2.E_local = E_local;
@@ -128,7 +134,8 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
   a2.ntn = (d + Default::BN - 1) / Default::BN;
   a2.T_src = T_src;
   a2.k = k;
-  hipLaunchKernelGGL(ffn2_g2<Default>, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2);
+  hipLaunchKernelGGL(ffn2_g2<Default>, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2,
+                     gtab);
   trace_mark(tr, "ffn2_down", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
@@ -169,7 +176,9 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
   a2.row_src = row_src;
   a2.y = reinterpret_cast<bf16_t*>(y);
   a2.push = staging != nullptr;
-  if (staging) a2.staging = *staging;
+  DstTable gtab;
+  memset(&gtab, 0, sizeof(gtab));
+  if (staging) gtab = *staging;
   a2.d = d;
   a2.I = I;
   a2.E_local = E_local;
@@ -177,7 +186,7 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
   a2.ntn = (d + MxCfg::BN - 1) / MxCfg::BN;
   a2.T_src = T_src;
   a2.k = k;
-  hipLaunchKernelGGL(ffn2_mx, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2);
+  hipLaunchKernelGGL(ffn2_mx, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2, gtab);
   trace_mark(tr, "ffn2_down_mx", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }

@@ -21,9 +21,12 @@
 namespace mok {
 namespace g2 {
 
+// Argument blocks of the tiles: pointers and sizes only.  The per-source
+// pointer tables (source buffers, staging buffers) travel separately: in the
+// kernel arguments of the one-launch-per-GEMM kernels, in device memory for
+// the ring kernel's calls.
 struct F1Args {
-  const bf16_t* x;     // [R_cap, d] gathered rows, or null when gathering from src
-  SrcTable src;        // source buffers (used when x == null)
+  const bf16_t* x;     // [R_cap, d] gathered rows, or null when gathering from the sources
   const int32_t* row_src;
   const bf16_t* wg;    // [E_local, I, d]
   const bf16_t* wu;
@@ -41,8 +44,7 @@ struct F2Args {
   const int32_t* offsets;
   const int32_t* row_src;
   bf16_t* y;           // [R_cap, d] when not pushing
-  DstTable staging;
-  int push;
+  int push;            // 1: push each row to its staging row (table given to the tile)
   int d, I, E_local, R_cap, ntn, T_src, k;
 };
 
@@ -135,7 +137,7 @@ __device__ __forceinline__ void ffn1_tile(const F1Args& a, char* smem, const GTi
 // the staging row of each routed row (or stored at its expert-order row).
 template <class C, class AccT>
 __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GTile& g, int nt,
-                                           const F2Args& a) {
+                                           const F2Args& a, const DstTable& staging) {
   __shared__ int s_rows[BM];
   if (a.push) stage_rows(s_rows, a.row_src, g);
   __syncthreads();
@@ -152,7 +154,7 @@ __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GT
     if (a.push) {
       const int n = s_rows[r - g.r0];
       const int tok = n / a.k, j = n % a.k;
-      dst = reinterpret_cast<bf16_t*>(a.staging.p[tok / a.T_src]) +
+      dst = reinterpret_cast<bf16_t*>(staging.p[tok / a.T_src]) +
             ((size_t)(tok % a.T_src) * a.k + j) * a.d;
     } else {
       dst = a.y + (size_t)r * a.d;
@@ -163,7 +165,8 @@ __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GT
 
 // GEMM2 tile: y rows [g.r0, g.r1) x columns of N-tile nt, from h.
 template <class C>
-__device__ __forceinline__ void ffn2_tile(const F2Args& a, char* smem, const GTile& g, int nt) {
+__device__ __forceinline__ void ffn2_tile(const F2Args& a, const DstTable& staging, char* smem,
+                                          const GTile& g, int nt) {
   const bf16_t* wd = a.wd + (size_t)g.e * a.d * a.I;
   KMajor<BM, C::BK> la;
   KMajor<C::BN, C::BK> lb;
@@ -178,7 +181,7 @@ __device__ __forceinline__ void ffn2_tile(const F2Args& a, char* smem, const GTi
   Acc<C> acc;
   mainloop<C, false, false>(a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
-  ffn2_store<C>(acc, smem, g, nt, a);
+  ffn2_store<C>(acc, smem, g, nt, a, staging);
 }
 
 // ---------------------------------------------------------------- MXFP8
@@ -259,7 +262,8 @@ __device__ __forceinline__ void ffn1_mx_tile(const F1MxArgs& a, char* smem, cons
 }
 
 // GEMM2 tile on E4M3 codes of h and W_down.
-__device__ __forceinline__ void ffn2_mx_tile(const F2Args& a, char* smem, const GTile& g, int nt) {
+__device__ __forceinline__ void ffn2_mx_tile(const F2Args& a, const DstTable& staging, char* smem,
+                                             const GTile& g, int nt) {
   typedef MxCfg C;
   const uint8_t* hq = reinterpret_cast<const uint8_t*>(a.h);
   const uint8_t* wd = reinterpret_cast<const uint8_t*>(a.wd) + (size_t)g.e * a.d * a.I;
@@ -287,7 +291,7 @@ __device__ __forceinline__ void ffn2_mx_tile(const F2Args& a, char* smem, const 
   });
   Acc<C> acc;
   mx_mainloop(a.I / C::KB, la, lb, sa, sb, smem, acc);
-  ffn2_store<C>(acc, smem, g, nt, a);
+  ffn2_store<C>(acc, smem, g, nt, a, staging);
 }
 
 }  // namespace g2

@@ -54,30 +54,41 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
                            hipStream_t stream, mok_trace* tr = nullptr);
 
 // Persistent ring kernel of the forward pass (gather + GEMM1 + SwiGLU +
-// GEMM2 + push in one launch; see mok_ring.hip).
-struct RingPlan {
-  int prec;
-  SrcTable src;
+// GEMM2 + push + final weighted combine in one launch, for one or several
+// layer calls in a row; see mok_ring.hip).
+constexpr int kRingMaxCalls = MOK_MAX_CALLS;
+struct RingCall {       // one layer call (macrobatch) through the ring
+  SrcTable src;         // S source buffers [T_src, d]
+  DstTable staging;     // S staging buffers [T_src*k, d]
+  DstTable out;         // S outputs [T_src, d] (own entries)
   const int32_t* row_src;
   const int32_t* offsets;
+  const int32_t* dest_row;
+  const float* gate;
+  void* h;              // [R_cap, I] (MX: codes)
+  uint8_t* h_scale;     // MX: [R_cap, I/32]
+  void* ab;             // [R_cap, 2I] or null (bf16)
+  int own_lo, own_n;
+};
+struct RingPlan {
+  int prec;
+  int n_calls;
+  const RingCall* calls;  // host array [n_calls]
   int d, I, E_local, R_cap, T_src, k;
   int mb;                 // minibatch rows
   int64_t ring_bytes;
   int comm_wgs, gemm_wgs, wait_limit_us;
   void* ring;             // ring_bytes of workspace
-  int32_t* counters;      // ring_counter_bytes() of workspace
+  void* meta;             // ring_meta_bytes() of workspace: counters and call descriptors
   int32_t* status;
   const mok_expert_weights* w;
-  void* h;                // [R_cap, I] (MX: codes)
-  uint8_t* h_scale;       // MX: [R_cap, I/32]
-  void* ab;               // [R_cap, 2I] or null (bf16)
-  DstTable staging;
 };
 int64_t ring_slot_bytes(int prec, int d, int mb);
 // Compute units of the current device (0 if the runtime cannot tell).
 int device_cus();
 int ring_max_minibatches(int R_cap, int E_local, int mb);
-size_t ring_counter_bytes(int R_cap, int E_local, int mb);
+// Counters and call descriptors of the ring kernel, for up to kRingMaxCalls calls.
+size_t ring_meta_bytes(int R_cap, int E_local, int mb);
 // Argument check of the ring path (also run by launch_ring_fwd); the auto
 // split of workgroups is returned through comm_out / gemm_out.
 mok_status ring_check(int prec, int d, int I, int mb, int64_t ring_bytes, int comm_wgs,

@@ -4,6 +4,7 @@
 // All of them stream rows with 16-byte vector loads and stores; consecutive
 // lanes touch consecutive 16-byte units of one row, so every wave moves whole
 // 1 KiB spans of HBM.  They are bound by HBM bandwidth.
+#include "mok_combine.h"
 #include "mok_internal.h"
 #include "mok_mx.h"
 
@@ -166,13 +167,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int64_t n0 = ((int64_t)s * a.T_src + t) * a.k;
     const T* stg = reinterpret_cast<const T*>(a.staging.p[s]) + (size_t)t * a.k * a.d;
     T* o = reinterpret_cast<T*>(a.out.p[s]) + (size_t)t * a.d;
-    // every slot but a local row dropped beyond R_cap: a remote slot (row
-    // -1) holds what the GPU with that expert pushed here
-    for (int u = threadIdx.x; u < units; u += kThreads) {
-      float acc[U];
+    if constexpr (K == 0) {
+      combine_token<T>(a.dest_row, a.gate, n0, a.k, a.R_cap, stg, o, a.d, threadIdx.x, kThreads);
+    } else {
+      // the same sums as combine_token, with the K slot loads issued first
+      for (int u = threadIdx.x; u < units; u += kThreads) {
+        float acc[U];
 #pragma unroll
-      for (int i = 0; i < U; ++i) acc[i] = 0.0f;
-      if constexpr (K > 0) {
+        for (int i = 0; i < U; ++i) acc[i] = 0.0f;
         uint4 v[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) v[j] = ld16(stg + (size_t)j * a.d + u * U);
@@ -184,21 +186,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
           for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(gj, to_f32<T>(e[i]), acc[i]);
         }
-      } else {
-        for (int j = 0; j < a.k; ++j) {
-          if (a.dest_row[n0 + j] >= a.R_cap) continue;
-          const float gj = a.gate[n0 + j];
-          const uint4 v = ld16(stg + (size_t)j * a.d + u * U);
-          const T* e = reinterpret_cast<const T*>(&v);
+        uint4 outv;
+        T* ov = reinterpret_cast<T*>(&outv);
 #pragma unroll
-          for (int i = 0; i < U; ++i) acc[i] = __builtin_fmaf(gj, to_f32<T>(e[i]), acc[i]);
-        }
+        for (int i = 0; i < U; ++i) ov[i] = from_f32<T>(acc[i]);
+        st16(o + u * U, outv);
       }
-      uint4 outv;
-      T* ov = reinterpret_cast<T*>(&outv);
-#pragma unroll
-      for (int i = 0; i < U; ++i) ov[i] = from_f32<T>(acc[i]);
-      st16(o + u * U, outv);
     }
   }
 }

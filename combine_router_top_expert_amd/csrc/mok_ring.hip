@@ -2,40 +2,54 @@
 // section 02: the GPU's SMs are split into a side that dispatches, combines
 // and keeps state and a side that runs the expert FFN; the two hand work over
 // through local counters, a fixed-size ring token buffer whose space is reused
-// once the experts are done with it, and a minibatch size).
+// once the experts are done with it, and a minibatch size; the combine of the
+// previous macrobatch runs while the next one is dispatched).
 //
 // One launch of comm_wgs + gemm_wgs workgroups, all resident at once (one per
-// CU).  The first comm_wgs workgroups to start take the dispatch role, the
-// rest the grouped-GEMM role.
+// CU).  The first comm_wgs workgroups to start take the dispatch/combine role,
+// the rest the grouped-GEMM role.  The launch serves n_calls layer calls
+// (macrobatches) in a row; each call has its own sources, routing, layout,
+// staging rows and outputs, and all share the weights and the ring.
 //
-// Work units.  Every local expert's rows [offsets[e], offsets[e+1]) are cut
-// into minibatches of at most MB rows, numbered m = 0 .. M-1 in expert order.
-// Minibatch m lives in ring slot m % nslot (MB token rows; MXFP8: their E4M3
-// codes and E8M0 scales).
-//   fill (m, c)   dispatch side: pull rows [32c, 32c+32) of minibatch m from
+// Work units.  Every local expert's rows [offsets[e], offsets[e+1]) of a call
+// are cut into minibatches of at most MB rows, numbered in expert order, and
+// the calls' minibatches are numbered on: minibatch G (over all calls) lives
+// in ring slot G % nslot (MB token rows; MXFP8: their E4M3 codes and E8M0
+// scales).
+//   fill (G, c)   dispatch side: pull rows [32c, 32c+32) of minibatch G from
 //                 their source buffers into the slot (quantising for MXFP8);
 //                 waits until GEMM1 is done with the slot's previous
-//                 minibatch m - nslot; then x_ready[m] += 1.
-//   G1 (m, tile)  GEMM side: one 256 x BN tile of GEMM1 + SwiGLU over the
-//                 slot; waits for x_ready[m] == fill chunks of m; writes h
-//                 (and a | b) at the rows' global positions; then
-//                 g1_done[m] += 1.
-//   G2 (m, tile)  GEMM side: one tile of GEMM2 over h, pushed to the staging
-//                 rows (push combine); waits for g1_done[m] == GEMM1 tiles.
-// Each side takes its units from an atomic ticket counter in a fixed order:
-// fills by (m, c); GEMM work in steps u = 0, 1, ... each holding the GEMM1
-// tiles of minibatch u followed by the GEMM2 tiles of minibatch u - lag.  The
-// lag covers the steps that run at once (GEMM workgroups / tiles per step,
-// plus one), so that when a workgroup takes a GEMM2 tile the GEMM1 tiles it
-// needs were taken a full round of the GEMM side earlier and are normally
-// done: with a lag of 2 on the mid-size layer (224 GEMM workgroups, 19 tiles
-// per step) almost every GEMM2 tile waited most of a tile's time.
-// Every wait is on work with a smaller ticket (GEMM2 on GEMM1 of an earlier
-// step, a fill on GEMM1 of minibatch m - nslot < m, GEMM1 on the fills of its
-// own step), and tickets are taken in order by running workgroups, so the
-// smallest unfinished unit can always proceed.  Every wait is also bounded in
-// time: on expiry the kernel latches MOK_ETIMEOUT, raises an abort flag that
-// every other wait checks, and all workgroups return.
+//                 minibatch G - nslot; then x_ready[G] += 1.
+//   G1 (G, tile)  GEMM side: one 256 x BN tile of GEMM1 + SwiGLU over the
+//                 slot; waits for x_ready[G] == fill chunks of G; writes h
+//                 (and a | b) at the rows' positions; then g1_done[G] += 1.
+//   G2 (G, tile)  GEMM side: one tile of GEMM2 over h, pushed to the staging
+//                 rows (push combine); waits for g1_done[G] == GEMM1 tiles;
+//                 then g2_done[call] += 1.
+//   combine (call, q)  dispatch/combine side: the final weighted combine of
+//                 own tokens [32q, 32q+32) of the call; waits for g2_done of
+//                 the call == all its GEMM2 tiles.  Every call but the last:
+//                 the last call's combine has nothing left to overlap and runs
+//                 as the stand-alone combine launch after this kernel.
+// Tickets, in a fixed order per side.  Dispatch/combine: the fills of call 0,
+// the fills of call 1, the combine of call 0, the fills of call 2, the
+// combine of call 1, ..., the combine of the last call -- so the combine of
+// one call overlaps the pull of the next.  GEMM: per call, steps u = 0, 1,
+// ... each holding the GEMM1 tiles of minibatch u followed by the GEMM2 tiles
+// of minibatch u - lag, until the call's last GEMM2 tiles; then the next
+// call.  The lag covers the steps that run at once (GEMM workgroups / tiles
+// per step, plus one), so that a GEMM2 tile's GEMM1 tiles were taken a full
+// round of the GEMM side earlier and are normally done.
+// Every wait of a unit is on units with smaller tickets on its own side or on
+// the other side's units that precede, in that side's order, every unit the
+// waiter's side still needs: a fill waits on GEMM1 of an earlier minibatch,
+// GEMM1 on the fills of its own minibatch, GEMM2 on GEMM1 of its minibatch,
+// and the combine of call i -- ticketed after every fill of call i + 1 --
+// on GEMM2 of call i, whose tickets precede every GEMM ticket of call i + 1.
+// Tickets are taken in order by running workgroups, so the smallest
+// unfinished unit can always proceed.  Every wait is also bounded in time: on
+// expiry the kernel latches MOK_ETIMEOUT, raises an abort flag that every
+// other wait checks, and all workgroups return.
 //
 // Ordering: a producer's lanes wait for their stores, the workgroup meets at
 // a barrier, and one lane increments the counter with release semantics at
@@ -44,11 +58,13 @@
 // workgroup's barrier, and only then issues its loads.
 //
 // The arithmetic of each tile is the same device code as the one-launch-per-
-// GEMM path (mok_ffn_tiles.h), and every output element is produced by exactly
-// one tile, so the two paths give bit-identical results for any ring size and
-// minibatch size.
+// GEMM path (mok_ffn_tiles.h), the combine is the stand-alone combine's
+// (mok_combine.h), and every output element is produced by exactly one unit,
+// so the two paths give bit-identical results for any ring size, minibatch
+// size, split and number of calls.
 #include <string.h>
 
+#include "mok_combine.h"
 #include "mok_ffn_tiles.h"
 #include "mok_internal.h"
 #include "mok_mx.h"
@@ -60,24 +76,33 @@ namespace {
 using namespace g2;
 
 constexpr int kFillRows = 32;  // rows per fill unit
+constexpr int kCombTok = 32;   // own tokens per combine unit
 constexpr int kCtr = 4;        // fill ticket, GEMM ticket, role ticket, abort flag
 
 struct RingArgs {
-  SrcTable src;
-  const int32_t* row_src;
-  const int32_t* offsets;
+  const RingCall* calls;   // [n_calls] in device memory
+  int n_calls;
   int d, I, E_local, R_cap, T_src, k;
-  int mb, nslot, cpm, nmt, ntn1, ntn2, M_max;
+  int mb, nslot, cpm, nmt, ntn1, ntn2, M_max;  // M_max: minibatches of one call, at most
   int comm_wgs;
   int lag;             // GEMM2 of minibatch u runs in step u + lag (>= 1)
   char* ring;
   int64_t slot_bytes;
-  int32_t* ctr;        // [kCtr + 2 * M_max]: tickets, abort, x_ready[], g1_done[]
+  int32_t* ctr;        // [kCtr + 2 * n_calls * M_max + 2 * n_calls]: tickets, abort,
+                       // x_ready[], g1_done[] (by minibatch over all calls), g2_done[call],
+                       // combine unit tickets[call]
   int32_t* status;
   uint64_t wait_ticks;  // bound of one wait in s_memrealtime ticks (100 MHz)
-  F1Args f1;
+  F1Args f1;            // weights and sizes; the per-call pointers are set per unit
   F1MxArgs f1m;
   F2Args f2;
+};
+
+// Minibatch layout of every call, built by each workgroup at its start.
+struct CallsLds {
+  int mbp[kRingMaxCalls][257];  // per call: prefix of minibatches over the experts
+  int M[kRingMaxCalls];         // minibatches of the call
+  int base[kRingMaxCalls + 1];  // first minibatch of the call over all calls
 };
 
 __global__ void ring_init_kernel(int32_t* ctr, int n) {
@@ -150,9 +175,9 @@ __device__ int wg_ticket(int32_t* p, int* s_val) {
   return uniform(*s_val);
 }
 
-// Minibatch m -> (expert, rows [r0, r1)).
-__device__ __forceinline__ GTile minibatch(const RingArgs& a, const int* s_mbp, int m) {
-  GTile t = group_tile(a.offsets, a.E_local, a.R_cap, s_mbp, m, a.mb);
+// Minibatch m of call c -> (expert, rows [r0, r1)).
+__device__ __forceinline__ GTile minibatch(const RingArgs& a, const CallsLds& L, int c, int m) {
+  GTile t = group_tile(a.calls[c].offsets, a.E_local, a.R_cap, L.mbp[c], m, a.mb);
   t.e = uniform(t.e);
   t.r0 = uniform(t.r0);
   t.r1 = uniform(t.r1);
@@ -168,11 +193,12 @@ __device__ __forceinline__ GTile minibatch(const RingArgs& a, const int* s_mbp, 
 constexpr int kBatch = 8;
 
 template <bool MX>
-__device__ void fill_rows(const RingArgs& a, char* slot, const GTile& mbt, int q0, int nr) {
+__device__ void fill_rows(const RingArgs& a, const RingCall& call, char* slot, const GTile& mbt,
+                          int q0, int nr) {
   __shared__ const bf16_t* s_src[kFillRows];
   if ((int)threadIdx.x < nr) {
-    const int tok = a.row_src[mbt.r0 + q0 + threadIdx.x] / a.k;
-    s_src[threadIdx.x] = reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
+    const int tok = call.row_src[mbt.r0 + q0 + threadIdx.x] / a.k;
+    s_src[threadIdx.x] = reinterpret_cast<const bf16_t*>(call.src.p[tok / a.T_src]) +
                          (size_t)(tok % a.T_src) * a.d;
   }
   __syncthreads();
@@ -244,58 +270,163 @@ __device__ void fill_rows(const RingArgs& a, char* slot, const GTile& mbt, int q
   }
 }
 
+// Combine units of a call: own tokens in groups of kCombTok.  The last call's
+// combine has no later pull to overlap and runs as its own launch after this
+// kernel, where many workgroups per CU hide its memory latency; the earlier
+// calls' combines run here.
+__device__ __forceinline__ int combine_units(const RingArgs& a, int c) {
+  if (c >= a.n_calls - 1) return 0;
+  return (int)(((int64_t)a.calls[c].own_n * a.T_src + kCombTok - 1) / kCombTok);
+}
+
+// Dispatch/combine ticket f -> (kind, call, index): the fills of call 0, then
+// for c = 1 .. n_calls - 1 the fills of call c followed by the combine of
+// call c - 1, and last the combine of the last call.  kind 0 = fill, 1 =
+// combine, -1 = no more work.
+__device__ int comm_unit(const RingArgs& a, const CallsLds& L, int f, int* call, int* idx) {
+  for (int i = 0; i <= a.n_calls; ++i) {
+    if (i < a.n_calls) {  // fills of call i
+      const int nf = L.M[i] * a.cpm;
+      if (f < nf) {
+        *call = i;
+        *idx = f;
+        return 0;
+      }
+      f -= nf;
+    }
+    if (i >= 1) {  // combine of call i - 1
+      const int nc = combine_units(a, i - 1);
+      if (f < nc) {
+        *call = i - 1;
+        *idx = f;
+        return 1;
+      }
+      f -= nc;
+    }
+  }
+  return -1;
+}
+
+// Combine units of call c, taken from the call's combine ticket until none
+// is left: the final weighted combine of own tokens [32q, 32q + 32), once
+// every GEMM2 tile of the call has pushed its rows.  False if a wait failed.
+__device__ bool drain_combine(const RingArgs& a, const CallsLds& L, int c, int* s_val) {
+  int32_t* g2_done = a.ctr + kCtr + 2 * a.n_calls * a.M_max;
+  int32_t* ctick = g2_done + a.n_calls;
+  const RingCall& call = a.calls[c];
+  const int nu = combine_units(a, c);
+  bool waited = false;
+  for (;;) {
+    const int q = wg_ticket(ctick + c, s_val);
+    if (q >= nu) return true;
+    if (!waited) {
+      if (!wg_wait(g2_done + c, L.M[c] * a.nmt * a.ntn2, a, s_val + 1)) return false;
+      waited = true;
+    }
+    const int64_t n_tok = (int64_t)call.own_n * a.T_src;
+    const int64_t g0 = (int64_t)q * kCombTok;
+    for (int i = 0; i < kCombTok && g0 + i < n_tok; ++i) {
+      const int64_t g = g0 + i;
+      const int s = call.own_lo + (int)(g / a.T_src);
+      const int t = (int)(g % a.T_src);
+      const int64_t n0 = ((int64_t)s * a.T_src + t) * a.k;
+      const bf16_t* stg =
+          reinterpret_cast<const bf16_t*>(call.staging.p[s]) + (size_t)t * a.k * a.d;
+      bf16_t* o = reinterpret_cast<bf16_t*>(call.out.p[s]) + (size_t)t * a.d;
+      combine_token<bf16_t>(call.dest_row, call.gate, n0, a.k, a.R_cap, stg, o, a.d, threadIdx.x,
+                            kThreads);
+    }
+  }
+}
+
 template <bool MX>
-__device__ void dispatch_role(const RingArgs& a, int M, const int* s_mbp, int* s_val) {
+__device__ void dispatch_role(const RingArgs& a, const CallsLds& L, int* s_val) {
   int32_t* x_ready = a.ctr + kCtr;
-  int32_t* g1_done = x_ready + a.M_max;
-  const int nfill = M * a.cpm;
+  int32_t* g1_done = x_ready + a.n_calls * a.M_max;
   for (;;) {
     const int f = wg_ticket(a.ctr + 0, s_val);
-    if (f >= nfill) return;
-    const int m = f / a.cpm, c = f % a.cpm;
-    const GTile mbt = minibatch(a, s_mbp, m);
-    if (m >= a.nslot && !wg_wait(g1_done + (m - a.nslot), a.nmt * a.ntn1, a, s_val + 1)) return;
-    const int q0 = c * kFillRows;
-    const int nr = min(kFillRows, (mbt.r1 - mbt.r0) - q0);
-    if (nr > 0) fill_rows<MX>(a, a.ring + (size_t)(m % a.nslot) * a.slot_bytes, mbt, q0, nr);
-    wg_publish(x_ready + m);
+    int c = 0, idx = 0;
+    const int kind = uniform(comm_unit(a, L, f, &c, &idx));
+    c = uniform(c);
+    idx = uniform(idx);
+    if (kind < 0) break;
+    const RingCall& call = a.calls[c];
+    if (kind == 0) {
+      const int m = idx / a.cpm, ch = idx % a.cpm;
+      const int G = L.base[c] + m;
+      const GTile mbt = minibatch(a, L, c, m);
+      if (G >= a.nslot && !wg_wait(g1_done + (G - a.nslot), a.nmt * a.ntn1, a, s_val + 1)) return;
+      const int q0 = ch * kFillRows;
+      const int nr = min(kFillRows, (mbt.r1 - mbt.r0) - q0);
+      if (nr > 0)
+        fill_rows<MX>(a, call, a.ring + (size_t)(G % a.nslot) * a.slot_bytes, mbt, q0, nr);
+      wg_publish(x_ready + G);
+    } else if (!drain_combine(a, L, c, s_val)) {
+      // a combine ticket: help with the call's combine units until none is left
+      return;
+    }
   }
 }
 
 // ---------------------------------------------------------------- GEMM side
 template <class C, bool MX>
-__device__ void gemm_role(const RingArgs& a, int M, const int* s_mbp, int* s_val, char* smem) {
+__device__ void gemm_role(const RingArgs& a, const CallsLds& L, int* s_val, char* smem) {
   int32_t* x_ready = a.ctr + kCtr;
-  int32_t* g1_done = x_ready + a.M_max;
+  int32_t* g1_done = x_ready + a.n_calls * a.M_max;
+  int32_t* g2_done = g1_done + a.n_calls * a.M_max;
   const int n1 = a.nmt * a.ntn1, n2 = a.nmt * a.ntn2;
-  const int total = (M + a.lag) * (n1 + n2);
   for (;;) {
     __syncthreads();  // the previous unit is done with LDS and the broadcast slots
-    const int t = wg_ticket(a.ctr + 1, s_val);
-    if (t >= total) return;
+    int t = wg_ticket(a.ctr + 1, s_val);
+    int c = 0;
+    for (; c < a.n_calls; ++c) {  // the call of ticket t (its steps: M + lag)
+      const int nt_call = (L.M[c] + a.lag) * (n1 + n2);
+      if (t < nt_call) break;
+      t -= nt_call;
+    }
+    c = uniform(c);
+    t = uniform(t);
+    if (c >= a.n_calls) {
+      // no GEMM work left (every GEMM tile is taken): help with the combines
+      for (int cc = 0; cc < a.n_calls; ++cc)
+        if (!drain_combine(a, L, cc, s_val)) return;
+      return;
+    }
+    const RingCall& call = a.calls[c];
+    const int M = L.M[c];
     const int u = t / (n1 + n2);
     int o = t % (n1 + n2);
     if (o < n1) {
       const int m = u;
       if (m >= M) continue;
+      const int G = L.base[c] + m;
       const int mt = o / a.ntn1, nt = o % a.ntn1;
-      const GTile mbt = minibatch(a, s_mbp, m);
+      const GTile mbt = minibatch(a, L, c, m);
       GTile g;
       g.e = mbt.e;
       g.r0 = mbt.r0 + mt * BM;
       g.r1 = min(mbt.r1, g.r0 + BM);
       if (g.r0 < g.r1) {
-        if (!wg_wait(x_ready + m, a.cpm, a, s_val + 1)) return;
-        const char* slot = a.ring + (size_t)(m % a.nslot) * a.slot_bytes;
+        if (!wg_wait(x_ready + G, a.cpm, a, s_val + 1)) return;
+        const char* slot = a.ring + (size_t)(G % a.nslot) * a.slot_bytes;
         if constexpr (!MX) {
-          ffn1_tile<C>(a.f1, smem, g, nt, [&](int row) -> const bf16_t* {
+          F1Args f1 = a.f1;
+          f1.row_src = call.row_src;
+          f1.offsets = call.offsets;
+          f1.h = reinterpret_cast<bf16_t*>(call.h);
+          f1.ab = reinterpret_cast<bf16_t*>(call.ab);
+          ffn1_tile<C>(f1, smem, g, nt, [&](int row) -> const bf16_t* {
             const int r = g.r0 + row;
             return r < g.r1 ? reinterpret_cast<const bf16_t*>(slot) + (size_t)(r - mbt.r0) * a.d
                             : nullptr;
           });
         } else {
+          F1MxArgs f1 = a.f1m;
+          f1.offsets = call.offsets;
+          f1.hq = reinterpret_cast<uint8_t*>(call.h);
+          f1.hs = call.h_scale;
           ffn1_mx_tile(
-              a.f1m, smem, g, nt,
+              f1, smem, g, nt,
               [&](int row) -> const bf16_t* {
                 const int r = g.r0 + row;
                 return r < g.r1 ? reinterpret_cast<const bf16_t*>(slot + (size_t)(r - mbt.r0) * a.d)
@@ -309,23 +440,32 @@ __device__ void gemm_role(const RingArgs& a, int M, const int* s_mbp, int* s_val
               });
         }
       }
-      wg_publish(g1_done + m);
+      wg_publish(g1_done + G);
     } else {
       const int m = u - a.lag;
       if (m < 0) continue;
+      const int G = L.base[c] + m;
       o -= n1;
       const int mt = o / a.ntn2, nt = o % a.ntn2;
-      const GTile mbt = minibatch(a, s_mbp, m);
+      const GTile mbt = minibatch(a, L, c, m);
       GTile g;
       g.e = mbt.e;
       g.r0 = mbt.r0 + mt * BM;
       g.r1 = min(mbt.r1, g.r0 + BM);
-      if (g.r0 >= g.r1) continue;
-      if (!wg_wait(g1_done + m, n1, a, s_val + 1)) return;
-      if constexpr (!MX)
-        ffn2_tile<C>(a.f2, smem, g, nt);
-      else
-        ffn2_mx_tile(a.f2, smem, g, nt);
+      if (g.r0 < g.r1) {
+        if (!wg_wait(g1_done + G, n1, a, s_val + 1)) return;
+        F2Args f2 = a.f2;
+        f2.h = reinterpret_cast<const bf16_t*>(call.h);
+        f2.hs = call.h_scale;
+        f2.offsets = call.offsets;
+        f2.row_src = call.row_src;
+        if constexpr (!MX)
+          ffn2_tile<C>(f2, call.staging, smem, g, nt);
+        else
+          ffn2_mx_tile(f2, call.staging, smem, g, nt);
+      }
+      // every GEMM2 ticket of the call counts (the combine waits for all)
+      wg_publish(g2_done + c);
     }
   }
 }
@@ -333,15 +473,34 @@ __device__ void gemm_role(const RingArgs& a, int M, const int* s_mbp, int* s_val
 template <class C, bool MX>
 __global__ __launch_bounds__(kThreads) void ring_kernel(RingArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  __shared__ int s_mbp[257];
+  __shared__ CallsLds L;
   __shared__ int s_val[2];
-  const int M = uniform(group_prefix(a.offsets, a.E_local, a.R_cap, s_mbp, a.mb));
+  int base = 0;
+  for (int c = 0; c < a.n_calls; ++c) {
+    const int M = uniform(group_prefix(a.calls[c].offsets, a.E_local, a.R_cap, L.mbp[c], a.mb));
+    if (threadIdx.x == 0) {
+      L.M[c] = M;
+      L.base[c] = base;
+    }
+    base += M;
+  }
+  if (threadIdx.x == 0) L.base[a.n_calls] = base;
+  __syncthreads();
   const int role = wg_ticket(a.ctr + 2, s_val);
   __syncthreads();  // every lane has read the role before s_val is reused
   if (role < a.comm_wgs)
-    dispatch_role<MX>(a, M, s_mbp, s_val);
+    dispatch_role<MX>(a, L, s_val);
   else
-    gemm_role<C, MX>(a, M, s_mbp, s_val, smem);
+    gemm_role<C, MX>(a, L, s_val, smem);
+}
+
+// Copies one call's descriptor into device memory (tables travel as kernel
+// arguments, which are too large for the ring kernel to carry for every call).
+__global__ void ring_call_kernel(RingCall c, RingCall* dst) {
+  static_assert(sizeof(RingCall) % 8 == 0, "descriptor copied in 8-byte words");
+  const uint64_t* from = reinterpret_cast<const uint64_t*>(&c);
+  uint64_t* to = reinterpret_cast<uint64_t*>(dst);
+  for (int i = threadIdx.x; i < (int)(sizeof(RingCall) / 8); i += blockDim.x) to[i] = from[i];
 }
 
 }  // namespace
@@ -362,8 +521,16 @@ int ring_max_minibatches(int R_cap, int E_local, int mb) {
   return (R_cap + mb - 1) / mb + E_local;
 }
 
-size_t ring_counter_bytes(int R_cap, int E_local, int mb) {
-  return (size_t)(kCtr + 2 * ring_max_minibatches(R_cap, E_local, mb)) * sizeof(int32_t);
+// Counters (tickets, abort flag, x_ready and g1_done per minibatch of every
+// call, g2_done per call), then the call descriptors.
+static size_t ring_counter_ints(int R_cap, int E_local, int mb) {
+  return (size_t)kCtr + 2 * (size_t)kRingMaxCalls * ring_max_minibatches(R_cap, E_local, mb) +
+         2 * kRingMaxCalls;
+}
+
+size_t ring_meta_bytes(int R_cap, int E_local, int mb) {
+  const size_t ctr = (ring_counter_ints(R_cap, E_local, mb) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return ctr + kRingMaxCalls * sizeof(RingCall);
 }
 
 mok_status ring_check(int prec, int d, int I, int mb, int64_t ring_bytes, int comm_wgs,
@@ -391,14 +558,13 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
   const mok_status ok = ring_check(p.prec, p.d, p.I, p.mb, p.ring_bytes, p.comm_wgs, p.gemm_wgs,
                                    &comm, &gemm);
   if (ok != MOK_OK) return ok;
+  if (p.n_calls < 1 || p.n_calls > kRingMaxCalls) return MOK_EINVAL;
   const int64_t slot = ring_slot_bytes(p.prec, p.d, p.mb);
   const int64_t nslot = p.ring_bytes / slot;
   if (p.R_cap == 0) return MOK_OK;
   RingArgs a;
   memset(&a, 0, sizeof(a));
-  a.src = p.src;
-  a.row_src = p.row_src;
-  a.offsets = p.offsets;
+  a.n_calls = p.n_calls;
   a.d = p.d;
   a.I = p.I;
   a.E_local = p.E_local;
@@ -413,7 +579,12 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
   a.comm_wgs = comm;
   a.ring = reinterpret_cast<char*>(p.ring);
   a.slot_bytes = slot;
-  a.ctr = p.counters;
+  char* meta = reinterpret_cast<char*>(p.meta);
+  a.ctr = reinterpret_cast<int32_t*>(meta);
+  const size_t ctr_bytes =
+      (ring_counter_ints(p.R_cap, p.E_local, p.mb) * sizeof(int32_t) + 255) & ~(size_t)255;
+  RingCall* calls = reinterpret_cast<RingCall*>(meta + ctr_bytes);
+  a.calls = calls;
   a.status = p.status;
   const uint64_t us = p.wait_limit_us > 0 ? (uint64_t)p.wait_limit_us : 2000000ull;
   a.wait_ticks = us * 100;  // s_memrealtime runs at 100 MHz
@@ -421,12 +592,8 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
     a.ntn1 = (p.I + Default::BN / 2 - 1) / (Default::BN / 2);
     a.ntn2 = (p.d + Default::BN - 1) / Default::BN;
     F1Args& f1 = a.f1;
-    f1.row_src = p.row_src;
     f1.wg = reinterpret_cast<const bf16_t*>(p.w->w_gate);
     f1.wu = reinterpret_cast<const bf16_t*>(p.w->w_up);
-    f1.offsets = p.offsets;
-    f1.h = reinterpret_cast<bf16_t*>(p.h);
-    f1.ab = reinterpret_cast<bf16_t*>(p.ab);
     f1.d = p.d;
     f1.I = p.I;
     f1.E_local = p.E_local;
@@ -442,9 +609,6 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
     f1.wu = reinterpret_cast<const uint8_t*>(p.w->w_up);
     f1.sg = p.w->s_gate;
     f1.su = p.w->s_up;
-    f1.offsets = p.offsets;
-    f1.hq = reinterpret_cast<uint8_t*>(p.h);
-    f1.hs = p.h_scale;
     f1.d = p.d;
     f1.I = p.I;
     f1.E_local = p.E_local;
@@ -452,14 +616,9 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
     f1.ntn = a.ntn1;
   }
   F2Args& f2 = a.f2;
-  f2.h = reinterpret_cast<const bf16_t*>(p.h);
   f2.wd = reinterpret_cast<const bf16_t*>(p.w->w_down);
-  f2.hs = p.h_scale;
   f2.sd = p.w->s_down;
-  f2.offsets = p.offsets;
-  f2.row_src = p.row_src;
   f2.push = 1;
-  f2.staging = p.staging;
   f2.d = p.d;
   f2.I = p.I;
   f2.E_local = p.E_local;
@@ -471,8 +630,10 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
     const int per_step = a.nmt * (a.ntn1 + a.ntn2);
     a.lag = (gemm + per_step - 1) / per_step + 1;
   }
-  const int nctr = kCtr + 2 * a.M_max;
-  hipLaunchKernelGGL(ring_init_kernel, dim3((nctr + 255) / 256), dim3(256), 0, stream, p.counters, nctr);
+  for (int c = 0; c < p.n_calls; ++c)
+    hipLaunchKernelGGL(ring_call_kernel, dim3(1), dim3(64), 0, stream, p.calls[c], calls + c);
+  const int nctr = kCtr + 2 * p.n_calls * a.M_max + 2 * p.n_calls;
+  hipLaunchKernelGGL(ring_init_kernel, dim3((nctr + 255) / 256), dim3(256), 0, stream, a.ctr, nctr);
   trace_mark(tr, "ring_init", stream);
   if (p.prec == MOK_BF16)
     hipLaunchKernelGGL((ring_kernel<Default, false>), dim3(comm + gemm), dim3(kThreads), 0, stream, a);

@@ -68,6 +68,7 @@ extern "C" {
 
 #define MOK_MAX_SOURCES 64
 #define MOK_MX_BLOCK 32
+#define MOK_MAX_CALLS 8     /* layer calls (macrobatches) of one mok_layer_fwd_macro */
 
 typedef enum {
   MOK_OK = 0,
@@ -245,7 +246,8 @@ mok_status mok_combine(const mok_config* cfg, const void* y, const int32_t* dest
  * the steps run as separate kernels; with ring_bytes > 0 the gather, the FFN
  * and the push run in one persistent kernel whose workgroups are split into
  * dispatch/combine and grouped-GEMM roles handing minibatches over through a
- * fixed ring of expert-contiguous slots and device-scope counters [K02].
+ * fixed ring of expert-contiguous slots and device-scope counters [K02]; the
+ * final weighted combine follows as its own launch.
  * Results are bit-identical between the two paths, across ring sizes and
  * minibatch sizes. */
 mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
@@ -253,6 +255,37 @@ mok_status mok_layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          const int32_t* expert_to_local, const mok_expert_weights* w,
                          const mok_fwd_state* st, void* const* staging, void* const* out,
                          void* ws, int32_t* dev_status, void* stream);
+
+/* One layer call of mok_layer_fwd_macro: the arguments of mok_layer_fwd that
+ * differ between calls (all host memory; the tables are host arrays of S
+ * device pointers as for mok_layer_fwd). */
+typedef struct mok_layer_call {
+  int32_t own_lo, own_n;         /* own sources of the call */
+  const void* const* src_x;      /* S source buffers [T_src, d] */
+  const mok_fwd_state* st;       /* the call's forward state */
+  void* const* staging;          /* S staging buffers [T_src*k, d] */
+  void* const* out;              /* S outputs [T_src, d] (own entries) */
+} mok_layer_call;
+
+/* Macrobatch pipelining [K02: the combine of the previous macrobatch runs
+ * concurrently with the dispatch of the next]: the forward pass of n_calls
+ * layer calls (1..MOK_MAX_CALLS; consecutive layer calls or microbatches
+ * with the same configuration and weights, each with its own sources,
+ * state, staging rows and outputs) through one ring.  The routing and
+ * layout of every call run first; then one persistent launch pulls,
+ * computes and pushes the minibatches of call 0, 1, ... in order, and its
+ * dispatch/combine workgroups run the final weighted combine of call i
+ * while they pull the rows of call i + 1 (the last call's combine, with
+ * nothing left to overlap, is a launch of its own after that kernel).  Needs cfg->ring_bytes > 0 and
+ * prec MOK_BF16 or MOK_MXFP8 (MOK_EINVAL otherwise); the ring's counters
+ * and per-call descriptors are part of mok_workspace_bytes(cfg).  Results
+ * (state, staging rows, outputs) are bit-identical to n_calls separate
+ * mok_layer_fwd calls.  Calls must not share outputs or state. */
+mok_status mok_layer_fwd_macro(const mok_config* cfg, int32_t n_calls,
+                               const mok_layer_call* calls, const void* w_router,
+                               const float* bias, const int32_t* expert_to_local,
+                               const mok_expert_weights* w, void* ws, int32_t* dev_status,
+                               void* stream);
 
 /* mok_layer_fwd without a workspace argument, for callers that cannot
  * allocate device memory at all: code under HIP graph capture, tight serving

@@ -237,3 +237,26 @@ def test_noalloc_forward_rejections_on_the_host(L):
     assert rc(_cfg(ring_bytes=1 << 24)) == -1
     # ceil(64 * 8192 * 16 / 1024) chunks x 256 local experts x 4 bytes = 32 MiB > 4 MiB
     assert rc(_cfg(S=64, T_src=8192, k=16, E=256, E_local=256)) == -7
+
+
+def test_macro_forward_rejections_on_the_host(L):
+    """mok_layer_fwd_macro needs the ring, bf16 or MXFP8, 1..MOK_MAX_CALLS
+    calls and every call's pointers (MOK_EINVAL before anything runs)."""
+    S = 2
+    full, _k1 = _tab(S)
+    bad, _k2 = _tab(S, 1)
+    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
+    st = mok.mok_fwd_state(*([1] * 8))
+
+    def rc(cfg, n=2, src=full):
+        arr = (mok.mok_layer_call * max(n, 1))()
+        for i in range(max(n, 1)):
+            arr[i] = mok.mok_layer_call(0, 1, src, ctypes.pointer(st), full, full)
+        return L.mok_layer_fwd_macro(ctypes.byref(cfg), n, arr, 1, None, 1, ctypes.byref(w), 1, 1,
+                                     None)
+    ring = dict(ring_bytes=1 << 24, minibatch_rows=64)
+    assert rc(_cfg()) == -1                        # no ring
+    assert rc(_cfg(prec="f32", **ring)) == -1      # fp32 has no ring path
+    assert rc(_cfg(**ring), n=0) == -1
+    assert rc(_cfg(**ring), n=9) == -1             # more than MOK_MAX_CALLS
+    assert rc(_cfg(**ring), src=bad) == -1         # a call's NULL source pointer

@@ -223,3 +223,82 @@ def test_ring_mx_fill_bytes_bit_exact(name):
     qi = torch.from_numpy(q_of_row[rows]).to(DEV)
     np.testing.assert_array_equal(codes[si, qi].cpu().numpy(), rc)
     np.testing.assert_array_equal(scales[si, qi].cpu().numpy(), rs)
+
+
+def _second_call(c):
+    """Host inputs of a second layer call with the first one's weights and
+    router: new token rows (and new routing of the other sources), from the
+    generator with other seeds."""
+    from cases import oracle_routing
+    w = c.w
+    d = make_host_case(w.replace(index=w.index + 40), route_own=False)
+    d.w = w
+    d.wr_store, d.wr_val, d.bias = c.wr_store, c.wr_val, c.bias
+    d.wg_store, d.wg_val, d.wu_store, d.wu_val = c.wg_store, c.wg_val, c.wu_store, c.wu_val
+    d.wd_store, d.wd_val = c.wd_store, c.wd_val
+    oracle_routing(d)
+    return d
+
+
+def _state_bytes(L, R):
+    outs = [L.topk_idx, L.topk_gate, L.counts, L.offsets, L.row_src[:R], L.dest_row]
+    if L.prec == "mxfp8":
+        outs.append(L.h[:R * L.I])
+    else:
+        outs += [L.h[:R], L.ab[:R]]
+    return outs + list(L.staging) + [L.out[s] for s in range(L.S) if L.out[s] is not None]
+
+
+# name -> (workload, calls, minibatch rows, ring slots or bytes, comm_wgs, gemm_wgs)
+MACRO_CASES = {
+    "bf16_2calls_2slots_split4x12": (BF16_SMALL, 2, 64, 2, 4, 12),
+    "bf16_3calls_256MiB_auto": (BF16_SMALL, 3, 256, 256 * MiB, 0, 0),
+    "share_2calls_3slots": (SHARE, 2, 64, 3, 3, 9),
+    "mx_2calls_2slots": (MX_SMALL, 2, 128, 2, 4, 28),
+    "c2_full_2calls_256MiB": (synth.WORKLOADS["C2"], 2, 256, 256 * MiB, 0, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(MACRO_CASES))
+def test_macro_calls_bit_identical_to_separate_calls(name):
+    """mok_layer_fwd_macro over several layer calls (one ring launch, the
+    combine of call i beside the pull of call i + 1) leaves every call's
+    state, staging rows and outputs byte-identical to separate staged
+    mok_layer_fwd calls, and oracle-correct on sampled tokens."""
+    from combine_router_top_expert_amd import mok_layer_fwd_macro
+    w, n_calls, mb, ring, comm, gemm = MACRO_CASES[name]
+    _log("macro", name)
+    cases = [_host_case(w)]
+    while len(cases) < n_calls:
+        cases.append(_second_call(cases[-1]))
+    R_cap = max(int(c.layout["R"]) for c in cases)
+    refs, want = [], []
+    for c in cases:
+        ref = _layer(c, R_cap=R_cap, with_bwd=False)
+        ref.forward()
+        torch.cuda.synchronize()
+        ref.check_status()
+        want.append([t.clone() for t in _state_bytes(ref, int(c.layout["R"]))])
+        del ref
+    rb = _ring_bytes(w, mb, ring)
+    Ls = [_layer(c, R_cap=R_cap, with_bwd=False, ring_bytes=rb, minibatch_rows=mb, comm_wgs=comm,
+                 gemm_wgs=gemm) for c in cases]
+    for L in Ls:  # outputs and layout must be written by the call
+        for s in range(L.own_lo, L.own_lo + L.own_n):
+            L.out[s].fill_(float("nan"))
+        L.row_src.fill_(-7)
+    L0 = Ls[0]
+    calls = [dict(own_lo=L.own_lo, own_n=L.own_n, src_x=L.xs, state=L.state, staging=L.staging,
+                  out=L.out) for L in Ls]
+    mok_layer_fwd_macro(L0.cfg, calls, L0.w_router, L0.bias, L0.e2l, L0.weights, L0.ws, L0.status)
+    torch.cuda.synchronize()
+    L0.check_status()
+    for i, (c, L) in enumerate(zip(cases, Ls)):
+        got = _state_bytes(L, int(c.layout["R"]))
+        for j, (a, b) in enumerate(zip(want[i], got)):
+            assert _same(a, b), (i, j)
+        if w.T_src * len(w.own) <= 2000:
+            toks = sorted({(s, t) for s in w.own for t in range(w.T_src)})[::7]
+        else:
+            toks = sample_tokens(w, 8, seed=i)
+        _check_fwd(c, L, toks)

@@ -404,6 +404,81 @@ def run_workload(args, name, np, torch):
     return results
 
 
+def run_macro(args, name, np, torch):
+    """Macrobatch pipelining: args.macro layer calls of the workload's
+    forward through one ring launch (mok_layer_fwd_macro) against the same
+    calls one mok_layer_fwd (ring) after the other.  The calls take the same
+    inputs, each with its own state, staging rows and outputs."""
+    from combine_router_top_expert_amd import mok_layer_fwd_macro, synth
+    from combine_router_top_expert_amd.layer import MoELayer, to_device
+
+    dev = "cuda:0"
+    w = synth.WORKLOADS[name]
+    xs = [synth.gen_x(w, s) for s in range(w.S)]
+    wr = synth.gen_router(w)
+    bias = synth.load_bias(w)
+    wts = [synth.gen_expert_weights(w, p_) for p_ in ("gate", "up", "down")]
+    other = {s: synth.gen_other_routing(w, s) for s in range(w.S) if s not in w.own}
+    N = w.S * w.T_src * w.k
+    R_cap = N if w.E_local == w.E else min(N, 2 * N * w.E_local // w.E)
+    xs_d = [to_device(a, w.prec, dev) for a, _ in xs]
+    wr_d = to_device(wr[0], w.prec, dev)
+    bias_d = None if bias is None else torch.from_numpy(bias).to(dev)
+    e2l = torch.from_numpy(w.expert_to_local()).to(dev)
+    wts_d = [to_device(a[0], w.prec, dev) for a in wts]
+    ring = (args.ring_mib or 256) << 20
+    Ls = []
+    for _ in range(args.macro):
+        L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
+                     len(w.own), device=dev, with_bwd=False, ring_bytes=ring,
+                     minibatch_rows=args.mb, comm_wgs=args.comm_wgs, gemm_wgs=args.gemm_wgs)
+        L.set_inputs(xs_d, wr_d, bias_d, e2l, *wts_d, other_topk=other)
+        Ls.append(L)
+    L0 = Ls[0]
+    calls = [dict(own_lo=L.own_lo, own_n=L.own_n, src_x=L.xs, state=L.state, staging=L.staging,
+                  out=L.out) for L in Ls]
+
+    def macro():
+        mok_layer_fwd_macro(L0.cfg, calls, L0.w_router, L0.bias, L0.e2l, L0.weights, L0.ws,
+                            L0.status)
+
+    def separate():
+        for L in Ls:
+            L.forward()
+
+    res = {}
+    for label, fn in (("separate", separate), ("macro", macro)):
+        t_w = time.perf_counter()
+        i = 0
+        while i < args.warmup or time.perf_counter() - t_w < 0.5:
+            fn()
+            torch.cuda.synchronize()
+            i += 1
+        for L in Ls:
+            L.check_status()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        res[label] = (time.perf_counter() - t0) * 1e3 / args.steps
+    for L in Ls:
+        L.check_status()
+    T_tok = len(w.own) * w.T_src * args.macro
+    print(json.dumps({
+        "metric": "MoE layer forward tokens/sec, macrobatch pipelining on 1 MI355X",
+        "value": T_tok / (res["macro"] * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["macro"],
+        "higher_is_better": True, "dtype": "bf16" if w.prec == "bf16" else w.prec,
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {args.macro} layer calls of {len(w.own) * w.T_src} own "
+                               f"tokens (the same inputs), forward",
+                   "path": f"ring {ring >> 20} MiB, minibatch {args.mb} rows, comm/gemm "
+                           f"workgroups {args.comm_wgs or 'auto'}/{args.gemm_wgs or 'auto'}"},
+        "separate_calls_ms": res["separate"],
+        "separate_tokens_per_s": T_tok / (res["separate"] * 1e-3),
+        "speedup": res["separate"] / res["macro"]}), flush=True)
+
+
 # the CPU oracle's sample per workload: about 10 s of single-threaded work
 CPU_TOKENS = {"C1": 512, "C2": 36, "C3": 160, "C4": 600, "C5": 36}
 
@@ -441,6 +516,9 @@ def main():
                     help="auto: the 256-expert share (C3) through its 256 MiB ring with the "
                          "tuned minibatch and split, the others staged; staged: all staged "
                          "(--ring-mib sets the ring for every workload)")
+    ap.add_argument("--macro", type=int, default=0,
+                    help="instead of the step: this many forward calls through one ring launch "
+                         "(mok_layer_fwd_macro) against the same calls one after the other")
     ap.add_argument("--hbm-stream-gib", type=float, default=0.0,
                     help="instead of the layer: the HBM streaming probe (read, write, copy) "
                          "over this many GiB")
@@ -461,6 +539,10 @@ def main():
     if args.tune and (not args.ring_mib or args.mb_sweep):
         sys.exit("--tune needs --ring-mib and no --mb-sweep")
     names = DEFAULT_ORDER if args.workload == "all" else [args.workload]
+    if args.macro > 0:
+        for name in names:
+            run_macro(args, name, np, torch)
+        return
     for name in names:
         for r in run_workload(args, name, np, torch):
             print(json.dumps(r), flush=True)

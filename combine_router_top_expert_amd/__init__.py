@@ -45,7 +45,7 @@ class mok_config(ctypes.Structure):
                 ("minibatch_rows", ctypes.c_int32), ("ring_bytes", ctypes.c_int64),
                 ("comm_wgs", ctypes.c_int32), ("gemm_wgs", ctypes.c_int32),
                 ("wait_limit_us", ctypes.c_int32), ("trace", ctypes.c_void_p),
-                ("aux", ctypes.c_void_p)]
+                ("aux", ctypes.c_void_p), ("bwd_ring_bytes", ctypes.c_int64)]
 
 
 class mok_trace(ctypes.Structure):
@@ -271,9 +271,9 @@ def _check(fn: str, rc: int):
 
 
 def make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows=256, ring_bytes=0,
-                comm_wgs=0, gemm_wgs=0, wait_limit_us=0) -> mok_config:
+                comm_wgs=0, gemm_wgs=0, wait_limit_us=0, bwd_ring_bytes=0) -> mok_config:
     return mok_config(S, T_src, d, E, k, I, E_local, PREC.get(prec, prec), R_cap, minibatch_rows,
-                      ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, None, None)
+                      ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, None, None, bwd_ring_bytes)
 
 
 def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> mok_expert_weights:

@@ -31,13 +31,20 @@ bool valid_cfg(const mok_config* c) {
   if (c->ring_bytes < 0) return false;
   if (c->ring_bytes > 0 && c->minibatch_rows < 1) return false;
   if (c->comm_wgs < 0 || c->gemm_wgs < 0 || c->wait_limit_us < 0) return false;
+  if (c->bwd_ring_bytes < 0) return false;
+  if (c->bwd_ring_bytes > 0 && c->minibatch_rows < 1) return false;
   return true;
 }
 
 struct Ws {
   size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
-      r_row_src, r_dest_row, r_scratch, bx, wpart, worder, total;
+      r_row_src, r_dest_row, r_scratch, bx, wpart, wpart_down, worder, bwin, bring, total;
 };
+
+// The bf16 backward runs through the ring (window by window) when cfg has one.
+bool bwd_through_ring(const mok_config* c) {
+  return c->bwd_ring_bytes > 0 && c->prec == MOK_BF16 && c->R_cap > 0;
+}
 
 Ws ws_layout(const mok_config* c) {
   Ws w;
@@ -63,12 +70,14 @@ Ws ws_layout(const mok_config* c) {
     w.ring_ctr = f;
     f += align256(ring_meta_bytes(c->R_cap, c->E_local, c->minibatch_rows));
   }
-  // backward pieces (same region)
+  // backward pieces (same region); through the ring, dy, dab and the
+  // transposed token rows are a window's, in the ring region at the end
+  const bool bring = bwd_through_ring(c);
   size_t b = base;
   w.dy = b;
-  b += align256(R * c->d * act_bytes(c->prec));
+  if (!bring) b += align256(R * c->d * act_bytes(c->prec));
   w.dab = b;
-  b += align256(R * 2 * c->I * act_bytes(c->prec));
+  if (!bring) b += align256(R * 2 * c->I * act_bytes(c->prec));
   w.dz = b;
   b += align256((size_t)N * sizeof(float));
   w.dwr = b;
@@ -86,12 +95,21 @@ Ws ws_layout(const mok_config* c) {
   w.r_scratch = b;
   b += align256(c->E <= 256 ? layout_ws_bytes(N, c->E) : 0);
   w.bx = b;
-  b += align256(c->prec == MOK_BF16 ? (size_t)c->d * xt_ld(c->R_cap, c->E_local) * 2
-                                    : R * c->d * act_bytes(c->prec));
+  if (!bring)
+    b += align256(c->prec == MOK_BF16 ? (size_t)c->d * xt_ld(c->R_cap, c->E_local) * 2
+                                      : R * c->d * act_bytes(c->prec));
   w.wpart = b;
   b += align256(c->prec == MOK_BF16 ? wgrad_partial_bytes(c->R_cap, c->d, c->I) : 0);
+  // through the ring both weight gradients keep their partials until the
+  // last window: the down projection's get a region of their own (half size)
+  w.wpart_down = b;
+  if (bring) b += align256(wgrad_partial_bytes(c->R_cap, c->d, c->I) / 2);
   w.worder = b;
   b += align256((size_t)c->E_local * sizeof(int32_t));
+  w.bwin = b;
+  b += align256((size_t)(4 + c->E_local) * sizeof(int32_t));
+  w.bring = b;
+  if (bring) b += align256((size_t)c->bwd_ring_bytes);
   w.total = f > b ? f : b;
   return w;
 }
@@ -594,6 +612,26 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.wg_part = (float*)(wsb + wl.wpart);
   p.wg_order = (int32_t*)(wsb + wl.worder);
   p.status = dev_status;
+  if (bwd_through_ring(cfg)) {
+    // windows of whole minibatches through the ring: dy, dab and the
+    // transposed token rows of a window in its slots (rows r - lo)
+    int slots = 0, rows = 0, nwin = 0;
+    int64_t cols = 0;
+    if (!bwd_ring_geometry(cfg->bwd_ring_bytes, cfg->d, cfg->I, cfg->E_local, cfg->minibatch_rows,
+                           cfg->R_cap, &slots, &rows, &cols, &nwin))
+      return MOK_EINVAL;
+    char* ring = wsb + wl.bring;
+    p.dy = ring;
+    p.dab = ring + align256((size_t)rows * cfg->d * 2);
+    p.x_perm = (char*)p.dab + align256((size_t)rows * 2 * cfg->I * 2);
+    p.win = (int32_t*)(wsb + wl.bwin);
+    p.wd_part = (float*)(wsb + wl.wpart_down);
+    p.win_rows = rows;
+    p.win_cols = cols;
+    p.win_mb = cfg->minibatch_rows;
+    p.win_slots = slots;
+    p.n_win = nwin;
+  }
   p.tr = cfg->trace;
   if (cfg->aux) {
     const mok_aux* a = cfg->aux;

@@ -56,12 +56,15 @@ __global__ __launch_bounds__(kThreads) void rc_pull_kernel(BwdPlan p) {
   const int64_t tok0 = (int64_t)blockIdx.x * kPullTok;
   if (threadIdx.x < kPullTok) s_loc[threadIdx.x] = 0;
   __syncthreads();
-  // slots with a row here (a dropped row, >= R_cap, is skipped)
+  // slots with a row here (a dropped row, >= R_cap, is skipped); through the
+  // ring, rows of the current window [lo, hi) only, their dy at r - lo
+  const int lo = p.win ? p.win[0] : 0;
+  const int hi = p.win ? p.win[1] : p.R_cap;
   for (int i = threadIdx.x; i < kPullTok * p.k; i += kThreads) {
     const int64_t tok = tok0 + i / p.k;
     if (tok >= n_tok) break;
     const int r = p.dest_row[tok * p.k + i % p.k];
-    if (r >= 0 && r < p.R_cap) atomicOr(&s_loc[i / p.k], 1u << (i % p.k));
+    if (r >= lo && r < hi) atomicOr(&s_loc[i / p.k], 1u << (i % p.k));
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void rc_pull_kernel(BwdPlan p) {
       const int r = p.dest_row[n0 + j];
       const float g = p.topk_gate[n0 + j];
       const T* y = ybase + (size_t)j * p.d;
-      T* dy = reinterpret_cast<T*>(p.dy) + (size_t)r * p.d;
+      T* dy = reinterpret_cast<T*>(p.dy) + (size_t)(r - lo) * p.d;
       float part = 0.0f;
       auto unit = [&](int u, const uint4& dvu) {
         const uint4 yv = ld16(y + u * U);
@@ -571,9 +574,67 @@ mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
+// The per-token part of the backward on one stream, once every dx row is
+// pushed: the dx sum with the router path, then the router weight gradient.
+template <typename T>
+mok_status run_bwd_tail(const BwdPlan& p, hipStream_t stream) {
+  const int64_t n_own = (int64_t)p.own_n * p.T_src;
+  if (n_own > 0) {
+    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)((n_own + kDxTokPerBlock - 1) / kDxTokPerBlock)),
+                       dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_dx_sum_router", stream);
+  }
+  if (p.dw_router) {
+    const int N_own = (int)(n_own * p.k);
+    hipLaunchKernelGGL(iota_kernel, dim3((p.E + 255) / 256), dim3(256), 0, stream, p.r_ident, p.E);
+    mok_status rc = launch_layout(N_own, p.E, p.E, N_own, p.topk_idx + (int64_t)p.own_lo * p.T_src * p.k,
+                                  p.r_ident, p.r_counts, p.r_offsets, p.r_row_src, p.r_dest_row,
+                                  p.r_scratch, nullptr, stream, nullptr);
+    if (rc != MOK_OK) return rc;
+    trace_mark(p.tr, "bwd_router_layout", stream);
+    const int nchunk = N_own / kRChunk + p.E;
+    hipLaunchKernelGGL(dwr_part_kernel<T>, dim3(nchunk), dim3(kThreads), 0, stream, p, N_own);
+    trace_mark(p.tr, "bwd_dw_router_part", stream);
+    dim3 g((p.d + kThreads - 1) / kThreads, p.E);
+    hipLaunchKernelGGL(dwr_reduce_kernel, g, dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_dw_router_reduce", stream);
+  }
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+// bf16 backward through the ring: window by window (dy, da | db and the
+// transposed token rows of a window in the ring's slots, reused by the next
+// window), the weight gradients carried over from window to window; then the
+// split-K reduction and the per-token and router parts, as in one launch.
+template <typename T>
+mok_status run_bwd_ring(const BwdPlan& p, hipStream_t stream) {
+  mok_status rc = MOK_OK;
+  if (p.R_cap > 0) {
+    for (int w = 0; w < p.n_win; ++w) {
+      rc = launch_bwd_window(p, w, stream);
+      if (rc != MOK_OK) return rc;
+      rc = launch_rc_pull<T>(p, stream);
+      if (rc != MOK_OK) return rc;
+      rc = launch_gather_t(p, p.x_perm, stream);
+      if (rc != MOK_OK) return rc;
+      trace_mark(p.tr, "bwd_regather_x", stream);
+      rc = launch_bwd_dgrad(p, stream);
+      if (rc != MOK_OK) return rc;
+      // (the first window also orders the experts for the spread schedule,
+      // from the routed counts of all windows)
+      rc = launch_bwd_wgrad(p, p.x_perm, stream, w == 0, false);
+      if (rc != MOK_OK) return rc;
+    }
+    rc = launch_bwd_reduce(p, stream);
+    if (rc != MOK_OK) return rc;
+  }
+  return run_bwd_tail<T>(p, stream);
+}
+
 template <typename T>
 mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
+    if (p.win) return run_bwd_ring<T>(p, stream);
     if (p.aux) return run_bwd_two_streams<T>(p, stream);
     if (p.R_cap > 0) {
       mok_status rc = launch_rc_pull<T>(p, stream);
@@ -608,28 +669,7 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
     trace_mark(p.tr, "bwd_wgrad_down", stream);
   }
   }
-  const int64_t n_own = (int64_t)p.own_n * p.T_src;
-  if (n_own > 0) {
-    hipLaunchKernelGGL(dx_final_kernel<T>, dim3((unsigned)((n_own + kDxTokPerBlock - 1) / kDxTokPerBlock)),
-                       dim3(kThreads), 0, stream, p);
-    trace_mark(p.tr, "bwd_dx_sum_router", stream);
-  }
-  if (p.dw_router) {
-    const int N_own = (int)(n_own * p.k);
-    hipLaunchKernelGGL(iota_kernel, dim3((p.E + 255) / 256), dim3(256), 0, stream, p.r_ident, p.E);
-    mok_status rc = launch_layout(N_own, p.E, p.E, N_own, p.topk_idx + (int64_t)p.own_lo * p.T_src * p.k,
-                                  p.r_ident, p.r_counts, p.r_offsets, p.r_row_src, p.r_dest_row,
-                                  p.r_scratch, nullptr, stream, nullptr);
-    if (rc != MOK_OK) return rc;
-    trace_mark(p.tr, "bwd_router_layout", stream);
-    const int nchunk = N_own / kRChunk + p.E;
-    hipLaunchKernelGGL(dwr_part_kernel<T>, dim3(nchunk), dim3(kThreads), 0, stream, p, N_own);
-    trace_mark(p.tr, "bwd_dw_router_part", stream);
-    dim3 g((p.d + kThreads - 1) / kThreads, p.E);
-    hipLaunchKernelGGL(dwr_reduce_kernel, g, dim3(kThreads), 0, stream, p);
-    trace_mark(p.tr, "bwd_dw_router_reduce", stream);
-  }
-  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+  return run_bwd_tail<T>(p, stream);
 }
 
 }  // namespace

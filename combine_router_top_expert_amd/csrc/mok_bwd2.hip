@@ -12,6 +12,22 @@
 //         dW_down[e]          = dy^T h_e    (A = dy,  B = h)
 // The m/n-contiguous operands are read with the transposing LDS fragment
 // loads of the engine; no operand is transposed in memory.
+//
+// Ring windows.  Through the ring, the backward runs in windows of whole
+// minibatches (consecutive rows [lo, hi) of the expert order, cut at
+// minibatch boundaries): dy, dab and the transposed token rows of the
+// window's rows live in the ring at rows r - lo.  `win` (device memory)
+// holds lo, hi, the window's index and the expert pieces clipped to the
+// window, woff[e] = clamp(offsets[e], lo, hi); the GEMMs tile the pieces.
+// A weight-gradient tile sums its chunk's rows inside the window and, when
+// the chunk began in an earlier window, continues from the partial sum that
+// window stored (fp32, reloaded exactly into the accumulators): the MFMAs
+// then run on the same operands in the same order as in one launch, because
+// window cuts fall on minibatch boundaries (multiples of 64 rows from the
+// expert's first row), so the results are bit-identical to the one-launch
+// backward.  win == null: one launch over all rows.
+#include <string.h>
+
 #include "mok_gemm2.h"
 #include "mok_internal.h"
 
@@ -22,13 +38,16 @@ namespace {
 using namespace g2;
 
 struct DhArgs {
-  const bf16_t* dy;    // [R_cap, d]
+  const bf16_t* dy;    // [R_cap, d] (ring window: [rows, d] at r - lo)
   const bf16_t* wd;    // [E_local, d, I]
   const bf16_t* ab;    // [R_cap, 2I]
-  bf16_t* dab;         // [R_cap, 2I]
-  const int32_t* offsets;
+  bf16_t* dab;         // [R_cap, 2I] (ring window: at r - lo)
+  const int32_t* offsets;  // expert rows (ring window: the pieces woff)
+  const int32_t* win;      // ring window descriptor or null
   int d, I, E_local, R_cap, ntn;
 };
+
+__device__ __forceinline__ int win_lo(const int32_t* win) { return win ? win[0] : 0; }
 
 template <class C>
 __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
@@ -40,12 +59,13 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
   int mtile, nt;
   grouped_order(xcd_tile(blockIdx.x, total), total_m, a.ntn, &mtile, &nt);
   const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mtile);
+  const int lo = win_lo(a.win);
   const int n0 = nt * C::BN;
   const bf16_t* wd = a.wd + (size_t)g.e * a.d * a.I + n0;
   KMajor<BM, C::BK> la;
   la.init([&](int row) -> const bf16_t* {
     const int r = g.r0 + row;
-    return r < g.r1 ? a.dy + (size_t)r * a.d : nullptr;
+    return r < g.r1 ? a.dy + (size_t)(r - lo) * a.d : nullptr;
   });
   MNMajor<C::BN, C::BK> lb;
   lb.ncols_left = a.I - n0;
@@ -69,7 +89,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
     const int r = g.r0 + (wave >> 1) * 128 + trow;
     const int col = n0 + (wave & 1) * (C::BN / 2) + c * 8;
     if (r >= g.r1 || col >= a.I) return;
-    *reinterpret_cast<uint4*>(a.dab + (size_t)r * 2 * a.I + col) = st.raw(srow, c);
+    *reinterpret_cast<uint4*>(a.dab + (size_t)(r - lo) * 2 * a.I + col) = st.raw(srow, c);
   });
 }
 
@@ -79,14 +99,17 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
 // per thread; rows beyond R are skipped.
 __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const bf16_t* ab, bf16_t* dab,
                                                               const int32_t* offsets, int E_local,
-                                                              int R_cap, int I) {
-  const int R = min(offsets[E_local], R_cap);
+                                                              int R_cap, int I,
+                                                              const int32_t* win) {
+  // rows [lo, hi): all routed rows, or a ring window's (dab at r - lo)
+  const int lo = win_lo(win);
+  const int hi = win ? win[1] : min(offsets[E_local], R_cap);
   const int per_row = I / 8;
   const size_t u = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const int r = (int)(u / per_row), c = (int)(u % per_row) * 8;
-  if (r >= R) return;
+  const int r = lo + (int)(u / per_row), c = (int)(u % per_row) * 8;
+  if (r >= hi) return;
   const bf16_t* abr = ab + (size_t)r * 2 * I;
-  bf16_t* dabr = dab + (size_t)r * 2 * I;
+  bf16_t* dabr = dab + (size_t)(r - lo) * 2 * I;
   const uint4 hv = *reinterpret_cast<const uint4*>(dabr + c);
   const uint4 av = *reinterpret_cast<const uint4*>(abr + c);
   const uint4 bv = *reinterpret_cast<const uint4*>(abr + I + c);
@@ -110,7 +133,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const bf16_t* ab, 
 }
 
 struct DxArgs {
-  const bf16_t* dab;   // [R_cap, 2I]
+  const bf16_t* dab;   // [R_cap, 2I] (ring window: at r - lo)
+  const int32_t* win;  // ring window descriptor or null (offsets: the pieces woff)
   const bf16_t* wg;    // [E_local, I, d]
   const bf16_t* wu;
   const int32_t* offsets;
@@ -129,13 +153,14 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
   int mtile, nt;
   grouped_order(xcd_tile(blockIdx.x, total), total_m, a.ntn, &mtile, &nt);
   const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mtile);
+  const int lo = win_lo(a.win);
   const int n0 = nt * C::BN;
   const bf16_t* wg = a.wg + (size_t)g.e * a.I * a.d + n0;
   const bf16_t* wu = a.wu + (size_t)g.e * a.I * a.d + n0;
   KMajor<BM, C::BK> la;
   la.init([&](int row) -> const bf16_t* {
     const int r = g.r0 + row;
-    return r < g.r1 ? a.dab + (size_t)r * 2 * a.I : nullptr;
+    return r < g.r1 ? a.dab + (size_t)(r - lo) * 2 * a.I : nullptr;
   });
   MNMajor<C::BN, C::BK> lb;
   lb.ncols_left = a.d - n0;
@@ -179,6 +204,7 @@ struct WgArgs {
   const int32_t* offsets;
   int lda, ldb, M, N, I, E_local, R_cap, mtn, ntn;
   const int32_t* order;  // [E_local] local experts by routed rows, descending (spread mode)
+  const int32_t* win;    // ring window descriptor or null; A (ring) rows at r - lo
 };
 
 // Split-K of the weight gradients.  An expert's rows are cut into chunks of
@@ -332,8 +358,11 @@ __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
 template <class C, int MODE>
 __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2];
+  __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2], s_tpw[257];
   wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp, s_rows);
+  // ring window: 64-row tiles of the window's pieces before each expert (the
+  // expert's first column in the window's transposed rows is 64 s_tpw[e])
+  if (MODE == 0 && a.win) group_prefix(a.win + 3, a.E_local, a.R_cap, s_tpw, 64);
   const int per = a.mtn * a.ntn;
   const bool spread = wg_spread(per, s_rows);
   int e, c, mt, nt;
@@ -367,30 +396,70 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
     }
     c = q - s_cp[e];
   }
-  const int end = min(a.offsets[e + 1], a.R_cap);
-  const int off = min(a.offsets[e], a.R_cap) + c * kWgChunk;
-  const int cnt = spread ? end - off : min(kWgChunk, end - off);
+  const int e_lo = min(a.offsets[e], a.R_cap), e_hi = min(a.offsets[e + 1], a.R_cap);
+  const int cs = e_lo + c * kWgChunk;                       // the chunk's rows [cs, ce)
+  const int ce = spread ? e_hi : min(cs + kWgChunk, e_hi);
+  int off = cs, cnt = ce - cs, lo = 0, xcol = 0;
+  bool keep = false;
+  if (a.win) {
+    // the chunk's rows inside the window; an expert without rows writes its
+    // zero gradient in the first window
+    lo = a.win[0];
+    const int ws = a.win[3 + e], we = a.win[3 + e + 1];
+    const int ks = max(cs, ws), ke = min(ce, we);
+    if (ke <= ks && !(e_hi == e_lo && a.win[2] == 0)) return;
+    off = ke > ks ? ks : cs;
+    cnt = ke > ks ? ke - ks : 0;
+    keep = off > cs;  // the chunk began in an earlier window
+    xcol = off - ws;  // column of the row in the window's transposed rows
+  }
   const int m0 = mt * BM, n0 = nt * C::BN;
+  float* part = c > 0 ? a.part + (size_t)(s_xp[e] + c - 1) * a.M * a.N : nullptr;
+  auto out_row_ptr = [&](int m) -> float* {
+    if (part) return part + (size_t)m * a.N;
+    if (MODE == 0)
+      return m < a.I ? a.out0 + ((size_t)e * a.I + m) * a.N
+                     : a.out1 + ((size_t)e * a.I + (m - a.I)) * a.N;
+    return a.out0 + ((size_t)e * a.M + m) * a.N;
+  };
+  Acc<C> acc;
+  if (keep) {
+    // the partial sum of the chunk's earlier rows, as the last window left it
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WNB; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int m = m0 + out_row(i), col = n0 + out_col<C>(j, g4);
+          float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (m < a.M && col < a.N) v = *reinterpret_cast<const float4*>(out_row_ptr(m) + col);
+          acc.c[i][j][4 * g4] = v.x;
+          acc.c[i][j][4 * g4 + 1] = v.y;
+          acc.c[i][j][4 * g4 + 2] = v.z;
+          acc.c[i][j][4 * g4 + 3] = v.w;
+        }
+  }
   MNMajor<BM, C::BK> la;
   la.ncols_left = a.M - m0;
-  const bf16_t* Ab = a.A + (size_t)off * a.lda + m0;
+  const bf16_t* Ab = a.A + (size_t)(off - lo) * a.lda + m0;
   auto issue_a = [&](int kt, unsigned l) {
     la.issue(kt, l, [&](int kk) -> const bf16_t* { return kk < cnt ? Ab + (size_t)kk * a.lda : nullptr; });
   };
-  Acc<C> acc;
   if constexpr (MODE == 0) {
     // B = the chunk's token rows from the transposed copy: row n of the tile
     // is column n0 + n of d, k-contiguous from the chunk's first column; the
     // last stage runs into the expert's zero padding
     static_assert(64 % C::BK == 0, "the transposed rows are padded to 64");
     KMajor<C::BN, C::BK> lb;
-    const bf16_t* Bt = a.BT + (size_t)64 * s_tp[e] + (size_t)c * kWgChunk;
+    const bf16_t* Bt = a.win ? a.BT + (size_t)64 * s_tpw[e] + xcol
+                             : a.BT + (size_t)64 * s_tp[e] + (size_t)c * kWgChunk;
     lb.init([&](int nr) -> const bf16_t* {
       const int n = n0 + nr;
       return n < a.N ? Bt + (size_t)n * a.ldt : nullptr;
     });
     mainloop<C, true, false>((cnt + C::BK - 1) / C::BK, issue_a,
-                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc, keep);
   } else {
     MNMajor<C::BN, C::BK> lb;
     lb.ncols_left = a.N - n0;
@@ -401,9 +470,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
                                 return kk < cnt ? Bb + (size_t)kk * a.ldb : nullptr;
                               });
                             },
-                            smem, acc);
+                            smem, acc, keep);
   }
-  float* part = c > 0 ? a.part + (size_t)(s_xp[e] + c - 1) * a.M * a.N : nullptr;
   __syncthreads();
   const WaveStage<C, float> st(smem);
   const int wave = threadIdx.x >> 6;
@@ -415,14 +483,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
       const int m = m0 + (wave >> 1) * 128 + trow;
       const int col = n0 + (wave & 1) * (C::BN / 2) + cc * 4;
       if (m >= a.M || col >= a.N) return;
-      float* dst;
-      if (part)
-        dst = part + (size_t)m * a.N;
-      else if (MODE == 0)
-        dst = m < a.I ? a.out0 + ((size_t)e * a.I + m) * a.N : a.out1 + ((size_t)e * a.I + (m - a.I)) * a.N;
-      else
-        dst = a.out0 + ((size_t)e * a.M + m) * a.N;
-      *reinterpret_cast<uint4*>(dst + col) = st.raw(srow, cc);
+      *reinterpret_cast<uint4*>(out_row_ptr(m) + col) = st.raw(srow, cc);
     });
     wave_lds_fence();
   }
@@ -490,20 +551,41 @@ __global__ __launch_bounds__(kThreads) void expert_order_kernel(const int32_t* o
   }
 }
 
+// Rows of a launch: all routed rows, or one ring window's (at most win_rows).
+static int launch_rows(const BwdPlan& p) { return p.win ? p.win_rows : p.R_cap; }
+
+bool bwd_ring_geometry(int64_t ring_bytes, int d, int I, int E_local, int mb, int R_cap,
+                       int* slots, int* rows, int64_t* cols, int* n_win) {
+  if (mb < 64 || mb % 64 != 0) return false;  // windows cut at multiples of 64 rows
+  const int64_t slot = (int64_t)mb * (2 * (int64_t)d + 2 * (int64_t)I) * 2;
+  const int64_t fixed = (64 * (int64_t)E_local + 64) * d * 2 + 3 * 256;
+  if (ring_bytes < fixed + slot) return false;
+  int64_t ns = (ring_bytes - fixed) / slot;
+  const int64_t m_max = ((int64_t)R_cap + mb - 1) / mb + E_local;  // minibatches, at most
+  if (ns > m_max) ns = m_max;
+  if (ns < 1) ns = 1;
+  *slots = (int)ns;
+  *rows = (int)(ns * mb);
+  *cols = ((int64_t)*rows + 64 * (int64_t)E_local + 63) / 64 * 64;
+  *n_win = (int)((m_max + ns - 1) / ns);
+  return true;
+}
+
 mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks) {
   if (p.R_cap == 0) return MOK_OK;
   GatherTArgs g;
   g.src = p.src_x;
   g.row_src = p.row_src;
-  g.offsets = p.offsets;
+  // a ring window's pieces: columns 64 P(e) + (r - woff[e]) of the window's rows
+  g.offsets = p.win ? p.win + 3 : p.offsets;
   g.xT = reinterpret_cast<bf16_t*>(xT);
-  g.ldt = xt_ld(p.R_cap, p.E_local);
+  g.ldt = p.win ? p.win_cols : xt_ld(p.R_cap, p.E_local);
   g.d = p.d;
   g.E_local = p.E_local;
   g.R_cap = p.R_cap;
   g.T_src = p.T_src;
   g.k = p.k;
-  const int tiles = (p.R_cap + 63) / 64 + p.E_local;  // bound of the 64-row tiles
+  const int tiles = (launch_rows(p) + 63) / 64 + p.E_local;  // bound of the 64-row tiles
   const int groups = (tiles + 3) / 4;
   int gx = groups < 256 ? groups : 256;
   // a cap on the workgroups (the copy then runs thin beside a GEMM on
@@ -517,92 +599,169 @@ mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int m
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
-mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
-                                 hipEvent_t before_wgrad, hipEvent_t after_dx) {
-  const int mt = (p.R_cap + BM - 1) / BM + p.E_local;
-  if (p.R_cap > 0) {
-    DhArgs d;
-    d.dy = reinterpret_cast<const bf16_t*>(p.dy);
-    d.wd = reinterpret_cast<const bf16_t*>(p.wd);
-    d.ab = reinterpret_cast<const bf16_t*>(p.ab);
-    d.dab = reinterpret_cast<bf16_t*>(p.dab);
-    d.offsets = p.offsets;
-    d.d = p.d;
-    d.I = p.I;
-    d.E_local = p.E_local;
-    d.R_cap = p.R_cap;
-    d.ntn = (p.I + Default::BN - 1) / Default::BN;
-    hipLaunchKernelGGL(dh_g2<Default>, dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
-    trace_mark(p.tr, "bwd_dh", stream);
-    const size_t pieces = (size_t)p.R_cap * (p.I / 8);
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((pieces + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, d.ab, d.dab, p.offsets, p.E_local, p.R_cap, p.I);
-    trace_mark(p.tr, "bwd_swiglu", stream);
-    DxArgs x;
-    x.dab = reinterpret_cast<const bf16_t*>(p.dab);
-    x.wg = reinterpret_cast<const bf16_t*>(p.wg);
-    x.wu = reinterpret_cast<const bf16_t*>(p.wu);
-    x.offsets = p.offsets;
-    x.row_src = p.row_src;
-    x.dx_stage = p.dx_stage;
-    x.d = p.d;
-    x.I = p.I;
-    x.E_local = p.E_local;
-    x.R_cap = p.R_cap;
-    x.ntn = (p.d + Default::BN - 1) / Default::BN;
-    x.T_src = p.T_src;
-    x.k = p.k;
-    hipLaunchKernelGGL(dx_g2<Default>, dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
-    trace_mark(p.tr, "bwd_dx_push", stream);
-  }
-  if (after_dx) hipEventRecord(after_dx, stream);
-  // grid bound of the split-K tiles: every expert's chunks, at most
-  // R_cap / kWgChunk + E_local of them, rounded up to a multiple of 8
-  const int max_chunks = (p.R_cap / kWgChunk + p.E_local + 7) / 8 * 8;
+mok_status launch_bwd_dgrad(const BwdPlan& p, hipStream_t stream) {
+  if (p.R_cap == 0) return MOK_OK;
+  const int rows = launch_rows(p);
+  const int mt = (rows + BM - 1) / BM + p.E_local;
+  const int32_t* offs = p.win ? p.win + 3 : p.offsets;
+  DhArgs d;
+  d.dy = reinterpret_cast<const bf16_t*>(p.dy);
+  d.wd = reinterpret_cast<const bf16_t*>(p.wd);
+  d.ab = reinterpret_cast<const bf16_t*>(p.ab);
+  d.dab = reinterpret_cast<bf16_t*>(p.dab);
+  d.offsets = offs;
+  d.win = p.win;
+  d.d = p.d;
+  d.I = p.I;
+  d.E_local = p.E_local;
+  d.R_cap = p.R_cap;
+  d.ntn = (p.I + Default::BN - 1) / Default::BN;
+  hipLaunchKernelGGL(dh_g2<Default>, dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
+  trace_mark(p.tr, "bwd_dh", stream);
+  const size_t pieces = (size_t)rows * (p.I / 8);
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((pieces + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, d.ab, d.dab, p.offsets, p.E_local, p.R_cap, p.I,
+                     p.win);
+  trace_mark(p.tr, "bwd_swiglu", stream);
+  DxArgs x;
+  x.dab = reinterpret_cast<const bf16_t*>(p.dab);
+  x.win = p.win;
+  x.wg = reinterpret_cast<const bf16_t*>(p.wg);
+  x.wu = reinterpret_cast<const bf16_t*>(p.wu);
+  x.offsets = offs;
+  x.row_src = p.row_src;
+  x.dx_stage = p.dx_stage;
+  x.d = p.d;
+  x.I = p.I;
+  x.E_local = p.E_local;
+  x.R_cap = p.R_cap;
+  x.ntn = (p.d + Default::BN - 1) / Default::BN;
+  x.T_src = p.T_src;
+  x.k = p.k;
+  hipLaunchKernelGGL(dx_g2<Default>, dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
+  trace_mark(p.tr, "bwd_dx_push", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+static WgArgs wgrad_args(const BwdPlan& p, const void* x_perm, int mode) {
   WgArgs w;
+  memset(&w, 0, sizeof(w));
   w.order = p.wg_order;
   w.part = p.wg_part;
-  w.A = reinterpret_cast<const bf16_t*>(p.dab);
-  w.B = nullptr;
-  w.BT = reinterpret_cast<const bf16_t*>(x_perm);
-  w.ldt = xt_ld(p.R_cap, p.E_local);
-  w.out0 = p.dw_gate;
-  w.out1 = p.dw_up;
   w.offsets = p.offsets;
-  w.lda = 2 * p.I;
-  w.ldb = p.d;
-  w.M = 2 * p.I;
-  w.N = p.d;
+  w.win = p.win;
   w.I = p.I;
   w.E_local = p.E_local;
   w.R_cap = p.R_cap;
-  w.mtn = (w.M + BM - 1) / BM;
-  w.ntn = (w.N + Default::BN - 1) / Default::BN;
-  // The grid covers both schedules (max_chunks >= E_local); the kernels pick
-  // one from the routed counts (wg_spread) and surplus workgroups return.
-  if (before_wgrad) hipStreamWaitEvent(stream, before_wgrad, 0);
-  hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets, p.E_local,
-                     p.R_cap, p.wg_order);
+  if (mode == 0) {
+    w.A = reinterpret_cast<const bf16_t*>(p.dab);
+    w.BT = reinterpret_cast<const bf16_t*>(x_perm);
+    w.ldt = p.win ? p.win_cols : xt_ld(p.R_cap, p.E_local);
+    w.out0 = p.dw_gate;
+    w.out1 = p.dw_up;
+    w.lda = 2 * p.I;
+    w.ldb = p.d;
+    w.M = 2 * p.I;
+    w.N = p.d;
+    w.mtn = (w.M + BM - 1) / BM;
+    w.ntn = (w.N + Default::BN - 1) / Default::BN;
+  } else {
+    w.part = p.wd_part ? p.wd_part : p.wg_part;
+    w.A = reinterpret_cast<const bf16_t*>(p.dy);
+    w.B = reinterpret_cast<const bf16_t*>(p.h);
+    w.out0 = p.dw_down;
+    w.lda = p.d;
+    w.ldb = p.I;
+    w.M = p.d;
+    w.N = p.I;
+    w.mtn = (w.M + BM - 1) / BM;
+    w.ntn = (w.N + Narrow::BN - 1) / Narrow::BN;
+  }
+  return w;
+}
+
+mok_status launch_bwd_wgrad(const BwdPlan& p, const void* x_perm, hipStream_t stream,
+                            bool order, bool reduce) {
+  // grid bound of the split-K tiles: every expert's chunks, at most
+  // R_cap / kWgChunk + E_local of them, rounded up to a multiple of 8.  The
+  // grid covers both schedules (max_chunks >= E_local); the kernels pick one
+  // from the routed counts (wg_spread) and surplus workgroups return.
+  const int max_chunks = (p.R_cap / kWgChunk + p.E_local + 7) / 8 * 8;
+  if (order)
+    hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets,
+                       p.E_local, p.R_cap, p.wg_order);
+  WgArgs w = wgrad_args(p, x_perm, 0);
   hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_gate_up", stream);
-  hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
-  trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
-  w.A = reinterpret_cast<const bf16_t*>(p.dy);
-  w.B = reinterpret_cast<const bf16_t*>(p.h);
-  w.out0 = p.dw_down;
-  w.out1 = nullptr;
-  w.lda = p.d;
-  w.ldb = p.I;
-  w.M = p.d;
-  w.N = p.I;
-  w.mtn = (w.M + BM - 1) / BM;
-  w.ntn = (w.N + Narrow::BN - 1) / Narrow::BN;
+  if (reduce) {
+    hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream,
+                       w);
+    trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
+  }
+  w = wgrad_args(p, x_perm, 1);
   hipLaunchKernelGGL((wgrad_g2<Narrow, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
                      dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down", stream);
+  if (reduce) {
+    hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream,
+                       w);
+    trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
+  }
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_bwd_reduce(const BwdPlan& p, hipStream_t stream) {
+  WgArgs w = wgrad_args(p, nullptr, 0);
+  w.win = nullptr;
+  hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
+  trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
+  w = wgrad_args(p, nullptr, 1);
+  w.win = nullptr;
   hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down_reduce", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
+                                 hipEvent_t before_wgrad, hipEvent_t after_dx) {
+  mok_status rc = launch_bwd_dgrad(p, stream);
+  if (rc != MOK_OK) return rc;
+  if (after_dx) hipEventRecord(after_dx, stream);
+  if (before_wgrad) hipStreamWaitEvent(stream, before_wgrad, 0);
+  return launch_bwd_wgrad(p, x_perm, stream, true, true);
+}
+
+// The window descriptor of ring window w: minibatches [w nslot, (w+1) nslot)
+// of mb rows of one expert each, in expert order -> rows [lo, hi) and the
+// expert pieces clipped to them.  A window past the last minibatch is empty
+// (lo = hi = R).
+__global__ __launch_bounds__(kThreads) void bwd_window_kernel(const int32_t* offsets, int E_local,
+                                                              int R_cap, int mb, int nslot, int w,
+                                                              int32_t* win) {
+  __shared__ int s_mbp[257];
+  const int M = group_prefix(offsets, E_local, R_cap, s_mbp, mb);
+  const int R = min(offsets[E_local], R_cap);
+  const int64_t first = (int64_t)w * nslot;
+  int lo = R, hi = R;
+  if (first < M) {
+    const int last = (int)min<int64_t>(M, first + nslot) - 1;
+    lo = group_tile(offsets, E_local, R_cap, s_mbp, (int)first, mb).r0;
+    hi = group_tile(offsets, E_local, R_cap, s_mbp, last, mb).r1;
+  }
+  if (threadIdx.x == 0) {
+    win[0] = lo;
+    win[1] = hi;
+    win[2] = w;
+  }
+  for (int e = threadIdx.x; e <= E_local; e += kThreads)
+    win[3 + e] = min(max(min(offsets[e], R_cap), lo), hi);
+}
+
+mok_status launch_bwd_window(const BwdPlan& p, int w, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_window_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets, p.E_local,
+                     p.R_cap, p.win_mb, p.win_slots, w, p.win);
+  trace_mark(p.tr, "bwd_ring_window", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

@@ -357,12 +357,15 @@ __device__ __forceinline__ void wait_stages_lgkm0(int after) {
 // are scheduling boundaries, which keeps that order in the instruction
 // stream.  The accumulation order (k16 steps ascending) does not depend on
 // NS or BK.
+// keep_acc: continue from the accumulators' values (a partial sum carried
+// over exactly from an earlier launch) instead of starting from zero.
 template <class C, bool A_MN, bool B_MN, class IA, class IB>
-__device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* smem, Acc<C>& acc) {
+__device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* smem, Acc<C>& acc,
+                                         bool keep_acc = false) {
   constexpr int S = C::BK / 16, NS = C::NS;
   static_assert(S >= 2, "at least two k16 steps per stage");
   typedef Frags<C, A_MN, B_MN> F;
-  acc.zero();
+  if (!keep_acc) acc.zero();
   if (KT <= 0) return;
   const unsigned lds0 = lds_addr_of(smem);
 #pragma unroll

@@ -125,8 +125,17 @@ struct BwdPlan {
   void* r_scratch;
   void* x_perm;     // bf16: [d, xt_ld] token rows gathered again, transposed, for the wgrad GEMM
   float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
+  float* wd_part;   // the down projection's partials ([R_cap / 4096, d, I]): wg_part in one
+                    // launch (reduced before it is reused); a region of its own through the
+                    // ring, where both sets are reduced after the last window
   int32_t* wg_order;  // [E_local] local experts by routed rows, descending
   int32_t* status;  // device status word (may be null)
+  // ring windows (win != null): the backward runs window by window, dy, dab
+  // and the transposed token rows of a window in the ring (rows r - lo)
+  int32_t* win;       // [3 + E_local + 1]: lo, hi, window index, clipped offsets
+  int win_rows;       // rows of a window, at most (slots x minibatch rows)
+  int64_t win_cols;   // leading dimension of the window's transposed token rows
+  int win_mb, win_slots, n_win;
   mok_trace* tr;    // host-side trace, may be null
   hipStream_t aux;      // second stream for the work beside the GEMMs, or null
   hipEvent_t aux_ev[3]; // fork/join events of the second stream
@@ -140,6 +149,17 @@ inline int64_t xt_ld(int R_cap, int E_local) {
 mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks = 0);
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
                                  hipEvent_t before_wgrad = nullptr, hipEvent_t after_dx = nullptr);
+// Pieces of the bf16 backward GEMMs (one launch, or one ring window each).
+mok_status launch_bwd_dgrad(const BwdPlan& p, hipStream_t stream);
+mok_status launch_bwd_wgrad(const BwdPlan& p, const void* x_perm, hipStream_t stream, bool order,
+                            bool reduce);
+mok_status launch_bwd_reduce(const BwdPlan& p, hipStream_t stream);
+mok_status launch_bwd_window(const BwdPlan& p, int w, hipStream_t stream);
+// Geometry of the backward's ring windows for cfg (bf16, ring_bytes > 0):
+// slots of minibatch_rows rows, each holding dy and da | db rows and the
+// transposed token rows; false if the ring holds no slot.
+bool bwd_ring_geometry(int64_t ring_bytes, int d, int I, int E_local, int mb, int R_cap,
+                       int* slots, int* rows, int64_t* cols, int* n_win);
 size_t wgrad_partial_bytes(int R_cap, int d, int I);
 
 }  // namespace mok

@@ -30,14 +30,14 @@ def to_device(a: np.ndarray, prec: str, device) -> torch.Tensor:
 class MoELayer:
     def __init__(self, S, T_src, d, E, k, I, E_local, prec, R_cap, own_lo, own_n, device="cuda",
                  ring_bytes=0, minibatch_rows=256, comm_wgs=0, gemm_wgs=0, with_bwd=True,
-                 wait_limit_us=0, two_streams=True):
+                 wait_limit_us=0, two_streams=True, bwd_ring_bytes=0):
         assert S <= MAX_SOURCES
         self.S, self.T_src, self.d, self.E, self.k, self.I = S, T_src, d, E, k, I
         self.E_local, self.prec, self.R_cap = E_local, prec, R_cap
         self.own_lo, self.own_n = own_lo, own_n
         self.device = torch.device(device)
         self.cfg = make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows,
-                               ring_bytes, comm_wgs, gemm_wgs, wait_limit_us)
+                               ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, bwd_ring_bytes)
         dev = self.device
         act = _dt(prec)
         N = S * T_src * k
@@ -61,7 +61,7 @@ class MoELayer:
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         # the bf16 backward runs its side work on a second stream (mok_aux)
         self.aux = None
-        if two_streams and with_bwd and prec == "bf16":
+        if two_streams and with_bwd and prec == "bf16" and not bwd_ring_bytes:
             self.aux = AuxStream(dev)
             self.aux.attach(self.cfg)
         self.state = make_state(self.topk_idx, self.topk_gate, self.counts, self.offsets,

@@ -146,6 +146,13 @@ typedef struct mok_config {
                              (0 = 2 s) */
   mok_trace* trace;       /* optional kernel timing, NULL = off (host memory) */
   mok_aux* aux;           /* optional second stream of the backward pass, NULL = one stream */
+  int64_t bwd_ring_bytes; /* bf16 backward through a ring of this many bytes: the routed rows
+                             run in windows of whole minibatches (minibatch_rows, a multiple
+                             of 64) whose dy, da | db and transposed token rows occupy the
+                             ring's slots, reused window after window, instead of buffers of
+                             R_cap rows; 0 = one launch per step over all rows.  The results
+                             are bit-identical either way.  The ring must hold one slot
+                             (MOK_EINVAL otherwise); aux is not used on this path */
 } mok_config;
 
 /* Expert weights of the E_local local experts (see Layout above).  For

@@ -12,7 +12,8 @@ import torch
 
 from cases import make_host_case, sample_tokens
 from combine_router_top_expert_amd import synth
-from test_gpu_parity import DEV, _check_fwd, _layer, _log, _small
+from combine_router_top_expert_amd.layer import to_device
+from test_gpu_parity import BWD_CASES, DEV, _check_fwd, _layer, _log, _small
 
 pytestmark = pytest.mark.gpu
 
@@ -302,3 +303,78 @@ def test_macro_calls_bit_identical_to_separate_calls(name):
         else:
             toks = sample_tokens(w, 8, seed=i)
         _check_fwd(c, L, toks)
+
+
+def _bwd_ring_bytes(w, mb, slots):
+    """Bytes of a backward ring of `slots` minibatch slots (dy, da | db and the
+    transposed token rows of mb rows each, plus the column padding)."""
+    slot = mb * (2 * w.d + 2 * w.I) * 2
+    fixed = (64 * w.E_local + 64) * w.d * 2 + 3 * 256
+    return fixed + slots * slot
+
+
+def _bwd_bytes(L, w):
+    outs = [L.d_gate, L.dw_gate, L.dw_up, L.dw_down, L.dw_router] + list(L.dx_stage)
+    return outs + [L.d_x[s] for s in w.own]
+
+
+# name -> (workload, minibatch rows, ring slots or bytes, oracle check)
+BWD_RING_CASES = {
+    # 64-row minibatches in 3 slots: many windows, experts cut across windows
+    "all_local_mb64_3slots": (BWD_CASES["bf16_all_local"], 64, 3, "all"),
+    # ~6000 rows per expert on the split-K schedule: 4096-row chunks cut by windows
+    "split_k_mb256_2slots": (BWD_CASES["bf16_split_k"], 256, 2, None),
+    # the spread schedule (whole experts, d = 4096, I = 2048) cut by windows
+    "spread_mb64_5slots": (BWD_CASES["bf16_spread"], 64, 5, None),
+    # a share with peer-written slots
+    "share_mb64_2slots": (BWD_CASES["bf16_share"], 64, 2, "all"),
+    # the skewed mid-size layer's backward through its 256 MiB ring
+    "c5_full_256MiB": (synth.WORKLOADS["C5"], 256, 256 * MiB, "sampled"),
+    # the 256-expert share's backward through a 256 MiB ring
+    "c3_full_256MiB": (synth.WORKLOADS["C3"], 512, 256 * MiB, "sampled"),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_RING_CASES))
+def test_ring_backward_bit_identical_to_staged(name):
+    """The backward through the ring -- windows of whole minibatches whose dy,
+    da | db and transposed token rows occupy the ring's slots, weight
+    gradients carried over exactly from window to window -- gives the same
+    bytes as the one-launch backward (d_gate, pushed dx rows, d_x, every
+    weight gradient, the router gradient), and matches the oracle."""
+    from test_gpu_parity import _bwd_sampled, _check_wgrad_columns, peer_rows, TOL
+    import oracle
+    from cases import rel_err
+    w, mb, ring, check = BWD_RING_CASES[name]
+    _log("ring backward", name)
+    c = _host_case(w)
+    dout_store = [synth.gen_dout(w, s) for s in range(w.S)]
+    d_out = [to_device(a, w.prec, DEV) for a, _ in dout_store]
+    ref = _layer(c)
+    ref.forward()
+    ref.backward(d_out)
+    torch.cuda.synchronize()
+    ref.check_status()
+    want = [t.clone() for t in _bwd_bytes(ref, w)]
+    del ref
+    rb = ring if ring >= MiB else _bwd_ring_bytes(w, mb, ring)
+    L = _layer(c, minibatch_rows=mb, bwd_ring_bytes=rb)
+    for t in (L.dw_gate, L.dw_up, L.dw_down, L.dw_router):
+        t.fill_(float("nan"))
+    L.forward()
+    L.backward(d_out)
+    torch.cuda.synchronize()
+    L.check_status()
+    R = int(c.layout["R"])
+    slot = mb * (2 * w.d + 2 * w.I) * 2
+    slots = (rb - ((64 * w.E_local + 64) * w.d * 2 + 768)) // slot
+    _log(f"  R={R} window rows={slots * mb} windows>={-(-R // (slots * mb))}")
+    for j, (a, b) in enumerate(zip(want, _bwd_bytes(L, w))):
+        assert _same(a, b), j
+    if check == "all":
+        toks = [(s, t) for s in w.own for t in range(w.T_src)]
+        _bwd_sampled(c, L, dout_store, toks)
+    elif check == "sampled":
+        _bwd_sampled(c, L, dout_store, sample_tokens(w, 12))
+        cnt = np.diff(c.layout["offsets"])
+        _check_wgrad_columns(c, L, dout_store, int(np.argmax(cnt)))

@@ -82,6 +82,8 @@ def _declare(L):
                                     _p, _p, _p]
     L.mokref_expert_wgrad.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
     L.mokref_router_wgrad.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p]
+    L.mokref_expert_bwd_mx.argtypes = [_i, _i, _i, _int, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                       _p, _p, _p]
     L.mokref_expert_wgrad_cols.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p,
                                            _p]
 
@@ -375,3 +377,28 @@ def router_dz(topk_idx, gate, d_gate):
                                   gate.ctypes.data + t * rowb, d_gate.ctypes.data + t * rowb,
                                   None, dz.ctypes.data + t * rowb, None)
     return dz
+
+
+def expert_bwd_mx(rows_x, rows_g, rows_dout, rows_a, rows_b, rows_h, wg, wu, wd, quant=True):
+    """MXFP8 backward of one expert's rows -> (dx [n,d], dW_gate [I,d], dW_up [I,d],
+    dW_down [d,I]) float64; quant=False: the exact backward."""
+    rows_x = _c(rows_x, np.float32)
+    rows_g = _c(rows_g, np.float64)
+    rows_dout = _c(rows_dout, np.float32)
+    rows_a = _c(rows_a, np.float64)
+    rows_b = _c(rows_b, np.float64)
+    rows_h = _c(rows_h, np.float64)
+    wg = _c(wg, np.float32)
+    wu = _c(wu, np.float32)
+    wd = _c(wd, np.float32)
+    n, d = rows_x.shape
+    I = wg.shape[0]
+    dx = np.empty((n, d))
+    dwg = np.empty((I, d))
+    dwu = np.empty((I, d))
+    dwd = np.empty((d, I))
+    lib().mokref_expert_bwd_mx(n, d, I, 1 if quant else 0, _ptr(rows_x), _ptr(rows_g),
+                               _ptr(rows_dout), _ptr(rows_a), _ptr(rows_b), _ptr(rows_h),
+                               _ptr(wg), _ptr(wu), _ptr(wd), _ptr(dx), _ptr(dwg), _ptr(dwu),
+                               _ptr(dwd))
+    return dx, dwg, dwu, dwd

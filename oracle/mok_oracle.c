@@ -541,6 +541,114 @@ void mokref_expert_wgrad_cols(int64_t n, int64_t d, int64_t I, const float* rows
   free(dy);
 }
 
+/* MX round trip of a vector of n values quantised in blocks of 32 along it,
+ * the last block padded with zeros (the layout pads every expert's rows to
+ * whole blocks). */
+static void mx_roundtrip_padded(int64_t n, double* v) {
+  const int64_t np = (n + MX_BLOCK - 1) / MX_BLOCK * MX_BLOCK;
+  double* t = (double*)calloc((size_t)(np > 0 ? np : 1), sizeof(double));
+  memcpy(t, v, sizeof(double) * (size_t)n);
+  if (np > 0) mx_roundtrip(np, t);
+  memcpy(v, t, sizeof(double) * (size_t)n);
+  free(t);
+}
+
+/* MXFP8 backward of one local expert's routed rows (kucoin article, section
+ * 03: the layer's backward in MXFP8).  The pages fix only that the backward
+ * runs in MXFP8; the reading taken: every GEMM quantises both operands to
+ * E4M3 with one E8M0 scale per 32 elements along its contraction axis, from
+ * the values the layer stores (bf16), and accumulates exactly; results are
+ * stored in bf16 (rows) or kept exact (weight gradients):
+ *   dy   = bf16(g dout)
+ *   dh   = bf16(MX_d(dy) . MX_d(W_down^T))          contraction over d
+ *   da, db from dh and the saved a, b (bf16) -> bf16
+ *   dx   = bf16(MX_2I([da|db]) . MX_2I([W_gate; W_up]^T))   over 2I
+ *   dW_gate|up = MX_rows([da|db]^T) . MX_rows(X^T)  over the expert's rows
+ *   dW_down    = MX_rows(dy^T) . MX_rows(h^T)       over the expert's rows
+ * where MX_rows quantises each column in blocks of 32 consecutive rows of
+ * the expert, zero padded, and h is the forward's h as its GEMM2 used it.
+ * quant = 0 turns every MX quantisation and bf16 rounding off: the exact
+ * backward of mokref_bwd_row / mokref_expert_wgrad.
+ * rows_a, rows_b, rows_h [n, I]; wg, wu [I, d], wd [d, I] (the bf16 weights,
+ * not their forward MX values).  Outputs: dx [n, d] (the rows' input
+ * gradients), dwg, dwu [I, d], dwd [d, I]. */
+void mokref_expert_bwd_mx(int64_t n, int64_t d, int64_t I, int quant, const float* rows_x,
+                          const double* rows_g, const float* rows_dout, const double* rows_a,
+                          const double* rows_b, const double* rows_h, const float* wg,
+                          const float* wu, const float* wd, double* dx, double* dwg,
+                          double* dwu, double* dwd) {
+  const int64_t I2 = 2 * I;
+  double* wdt = (double*)malloc(sizeof(double) * (size_t)(I * d));   /* [I][d] */
+  double* wgut = (double*)malloc(sizeof(double) * (size_t)(d * I2)); /* [d][2I] */
+  for (int64_t i = 0; i < I; ++i)
+    for (int64_t c = 0; c < d; ++c) wdt[i * d + c] = (double)wd[c * I + i];
+  for (int64_t c = 0; c < d; ++c)
+    for (int64_t i = 0; i < I2; ++i)
+      wgut[c * I2 + i] = i < I ? (double)wg[i * d + c] : (double)wu[(i - I) * d + c];
+  if (quant) {
+    for (int64_t i = 0; i < I; ++i) mx_roundtrip(d, wdt + i * d);
+    for (int64_t c = 0; c < d; ++c) mx_roundtrip(I2, wgut + c * I2);
+  }
+  double* dy = (double*)malloc(sizeof(double) * (size_t)(n * d > 0 ? n * d : 1));
+  double* dab = (double*)malloc(sizeof(double) * (size_t)(n * I2 > 0 ? n * I2 : 1));
+  double* q = (double*)malloc(sizeof(double) * (size_t)(d > I2 ? d : I2));
+  for (int64_t r = 0; r < n; ++r) {
+    double* dyr = dy + r * d;
+    for (int64_t c = 0; c < d; ++c) dyr[c] = rows_g[r] * (double)rows_dout[r * d + c];
+    if (quant) store_round(MOKREF_BF16, d, dyr);
+    memcpy(q, dyr, sizeof(double) * (size_t)d);
+    if (quant) mx_roundtrip(d, q);
+    double* dabr = dab + r * I2;
+    for (int64_t i = 0; i < I; ++i) {
+      double dh = 0.0;
+      for (int64_t c = 0; c < d; ++c) dh += q[c] * wdt[i * d + c];
+      double a = rows_a[r * I + i], b = rows_b[r * I + i];
+      if (quant) {
+        dh = mokref_round_bf16(dh);
+        a = mokref_round_bf16(a);
+        b = mokref_round_bf16(b);
+      }
+      const double sg = sigmoid(a);
+      dabr[i] = dh * b * sg * (1.0 + a * (1.0 - sg));
+      dabr[I + i] = dh * silu(a);
+    }
+    if (quant) store_round(MOKREF_BF16, I2, dabr);
+    memcpy(q, dabr, sizeof(double) * (size_t)I2);
+    if (quant) mx_roundtrip(I2, q);
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < I2; ++i) acc += q[i] * wgut[c * I2 + i];
+      dx[r * d + c] = quant ? mokref_round_bf16(acc) : acc;
+    }
+  }
+  /* weight gradients: columns quantised along the rows */
+  double* ca = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double* cb = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int64_t i = 0; i < I2; ++i) {
+    for (int64_t r = 0; r < n; ++r) ca[r] = dab[r * I2 + i];
+    if (quant) mx_roundtrip_padded(n, ca);
+    for (int64_t c = 0; c < d; ++c) {
+      for (int64_t r = 0; r < n; ++r) cb[r] = (double)rows_x[r * d + c];
+      if (quant) mx_roundtrip_padded(n, cb);
+      double acc = 0.0;
+      for (int64_t r = 0; r < n; ++r) acc += ca[r] * cb[r];
+      if (i < I) dwg[i * d + c] = acc; else dwu[(i - I) * d + c] = acc;
+    }
+  }
+  for (int64_t c = 0; c < d; ++c) {
+    for (int64_t r = 0; r < n; ++r) ca[r] = dy[r * d + c];
+    if (quant) mx_roundtrip_padded(n, ca);
+    for (int64_t i = 0; i < I; ++i) {
+      for (int64_t r = 0; r < n; ++r) cb[r] = rows_h[r * I + i];
+      if (quant) mx_roundtrip_padded(n, cb);
+      double acc = 0.0;
+      for (int64_t r = 0; r < n; ++r) acc += ca[r] * cb[r];
+      dwd[c * I + i] = acc;
+    }
+  }
+  free(wdt); free(wgut); free(dy); free(dab); free(q); free(ca); free(cb);
+}
+
 /* Router weight gradient over the tokens routed here: dWr[e] = sum_t dz_t,e x_t
  * with dz from mokref_router_bwd_token (tokens in the order given).
  * dwr: [E, d] out (zeroed here). */

@@ -238,3 +238,64 @@ def test_router_dz_matches_the_token_backward():
         np.testing.assert_array_equal(dz[t], ref)
     # closed form: sum_j dz_j = sum_j g_j dg_j (1 - sum_i g_i) = 0 for gates summing to 1
     assert np.all(np.abs(dz.sum(1)) < 1e-12)
+
+
+def _mx_bwd_case(seed, n=45, d=64, I=64):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.normal(size=(n, d)))
+    g = rng.random(n)
+    dout = _bf16(rng.normal(size=(n, d)))
+    wg = _bf16(rng.normal(size=(I, d)) / np.sqrt(d))
+    wu = _bf16(rng.normal(size=(I, d)) / np.sqrt(d))
+    wd = _bf16(rng.normal(size=(d, I)) / np.sqrt(I))
+    a = np.zeros((n, I))
+    b = np.zeros((n, I))
+    h = np.zeros((n, I))
+    for r in range(n):
+        a[r], b[r], h[r], _ = oracle.ffn_row(x[r], wg, wu, wd, "exact")
+    return x, g, dout, a, b, h, wg, wu, wd
+
+
+def test_mx_backward_without_quantisation_is_the_exact_backward():
+    """With every MX quantisation and bf16 rounding off, the MXFP8 backward is
+    the exact backward (pinned above by finite differences): the same rows'
+    input gradients and the same weight gradients."""
+    x, g, dout, a, b, h, wg, wu, wd = _mx_bwd_case(31)
+    dx, dwg, dwu, dwd = oracle.expert_bwd_mx(x, g, dout, a, b, h, wg, wu, wd, quant=False)
+    for r in range(x.shape[0]):
+        ref = oracle.bwd_row(x[r], g[r], dout[r], wg, wu, wd)
+        np.testing.assert_allclose(dx[r], ref["dx"], rtol=1e-10, atol=1e-12)
+    rg, ru, rd = oracle.expert_wgrad(x, g, dout, wg, wu, wd)
+    np.testing.assert_allclose(dwg, rg, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dwu, ru, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dwd, rd, rtol=1e-10, atol=1e-12)
+
+
+def test_mx_backward_error_is_that_of_e4m3():
+    """With quantisation on, the result stays within the error of E4M3
+    operands (3 mantissa bits: each quantised factor carries at most 2^-4
+    relative error) of the exact backward, and is not the exact backward."""
+    x, g, dout, a, b, h, wg, wu, wd = _mx_bwd_case(32)
+    qx, qg, qu, qd = oracle.expert_bwd_mx(x, g, dout, a, b, h, wg, wu, wd, quant=True)
+    ex, eg, eu, ed = oracle.expert_bwd_mx(x, g, dout, a, b, h, wg, wu, wd, quant=False)
+    for got, ref in ((qx, ex), (qg, eg), (qu, eu), (qd, ed)):
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        assert 1e-4 < err < 0.1, err
+
+
+def test_mx_weight_gradient_quantises_along_the_rows():
+    """One routed row: every column of the weight-gradient operands is a
+    block holding that row's value and 31 zero paddings, so dW_down[c][i] is
+    the product of the single-value MX round trips of dy[c] = bf16(g dout[c])
+    and h[i] -- not of their row-wise (along d, along I) blocks."""
+    x, g, dout, a, b, h, wg, wu, wd = _mx_bwd_case(33, n=1)
+
+    def q1(v):
+        blk = np.zeros((1, 32))
+        blk[0, 0] = v
+        c, s = oracle.mx_quantize(blk)
+        return oracle.mx_dequantize(c, s)[0, 0]
+    _, _, _, dwd = oracle.expert_bwd_mx(x, g, dout, a, b, h, wg, wu, wd, quant=True)
+    dy = np.array([oracle.round_bf16(g[0] * float(v)) for v in dout[0]])
+    want = np.array([[q1(dy[c]) * q1(h[0, i]) for i in range(h.shape[1])] for c in range(dy.size)])
+    np.testing.assert_array_equal(dwd, want)

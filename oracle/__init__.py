@@ -8,10 +8,12 @@ never do; the two implementations share no code.  ``build()`` compiles
 Every function here is a thin numpy wrapper over one C function of
 ``mok_oracle.c``; each C function cites the passage of the pages it follows.
 The composite helpers at the bottom (``route``, ``layout``, ``layer_fwd`` ...)
-only chain those calls in the layer's order.  One function,
-``ffn_rows_exact``, is written with numpy instead: the exact expert FFN of
-many rows, with numpy's float64 matrix product as its contraction step, for
-checks at sizes where the row-by-row C loops are too slow.
+only chain those calls in the layer's order.  Two functions are written
+with numpy instead: ``ffn_rows_exact``, the exact expert FFN of many rows,
+with numpy's float64 matrix product as its contraction step, for checks at
+sizes where the row-by-row C loops are too slow; and ``gate_grads``, the
+gate gradients of rows whose expert outputs are given (one float64 dot
+product per row).
 """
 from __future__ import annotations
 
@@ -377,6 +379,16 @@ def router_dz(topk_idx, gate, d_gate):
                                   gate.ctypes.data + t * rowb, d_gate.ctypes.data + t * rowb,
                                   None, dz.ctypes.data + t * rowb, None)
     return dz
+
+
+def gate_grads(dout_rows, y_rows):
+    """Gate gradients of routed rows from the expert outputs the forward
+    produced: the final weighted combine sums g_j y_j into the token's output
+    (kucoin article, section 03: the final weighted combine), so
+    dL/dg_j = dout . y_j, a float64 dot product per row.  -> [n]."""
+    d = np.asarray(dout_rows, np.float64)
+    y = np.asarray(y_rows, np.float64)
+    return (d * y).sum(axis=1)
 
 
 def expert_bwd_mx(rows_x, rows_g, rows_dout, rows_a, rows_b, rows_h, wg, wu, wd, quant=True):

@@ -553,6 +553,17 @@ static void mx_roundtrip_padded(int64_t n, double* v) {
   free(t);
 }
 
+/* Columns of a row-major [n, cols] matrix as [cols][n] copies, each
+ * MX-quantised along the rows (zero padded to whole blocks) when quant. */
+static double* column_copies(int64_t n, int64_t cols, const double* m, int quant) {
+  double* o = (double*)malloc(sizeof(double) * (size_t)(n * cols > 0 ? n * cols : 1));
+  for (int64_t c = 0; c < cols; ++c) {
+    for (int64_t r = 0; r < n; ++r) o[c * n + r] = m[r * cols + c];
+    if (quant) mx_roundtrip_padded(n, o + c * n);
+  }
+  return o;
+}
+
 /* MXFP8 backward of one local expert's routed rows (kucoin article, section
  * 03: the layer's backward in MXFP8).  The pages fix only that the backward
  * runs in MXFP8; the reading taken: every GEMM quantises both operands to
@@ -621,32 +632,30 @@ void mokref_expert_bwd_mx(int64_t n, int64_t d, int64_t I, int quant, const floa
       dx[r * d + c] = quant ? mokref_round_bf16(acc) : acc;
     }
   }
-  /* weight gradients: columns quantised along the rows */
-  double* ca = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-  double* cb = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-  for (int64_t i = 0; i < I2; ++i) {
-    for (int64_t r = 0; r < n; ++r) ca[r] = dab[r * I2 + i];
-    if (quant) mx_roundtrip_padded(n, ca);
+  /* weight gradients: every column of [da|db], X, dy and h quantised along
+   * the rows once ([column][row] copies), then one dot product per element */
+  double* cab = column_copies(n, I2, dab, quant);
+  double* cx = (double*)malloc(sizeof(double) * (size_t)(n * d > 0 ? n * d : 1));
+  for (int64_t c = 0; c < d; ++c) {
+    for (int64_t r = 0; r < n; ++r) cx[c * n + r] = (double)rows_x[r * d + c];
+    if (quant) mx_roundtrip_padded(n, cx + c * n);
+  }
+  double* cdy = column_copies(n, d, dy, quant);
+  double* ch = column_copies(n, I, rows_h, quant);
+  for (int64_t i = 0; i < I2; ++i)
     for (int64_t c = 0; c < d; ++c) {
-      for (int64_t r = 0; r < n; ++r) cb[r] = (double)rows_x[r * d + c];
-      if (quant) mx_roundtrip_padded(n, cb);
       double acc = 0.0;
-      for (int64_t r = 0; r < n; ++r) acc += ca[r] * cb[r];
+      for (int64_t r = 0; r < n; ++r) acc += cab[i * n + r] * cx[c * n + r];
       if (i < I) dwg[i * d + c] = acc; else dwu[(i - I) * d + c] = acc;
     }
-  }
-  for (int64_t c = 0; c < d; ++c) {
-    for (int64_t r = 0; r < n; ++r) ca[r] = dy[r * d + c];
-    if (quant) mx_roundtrip_padded(n, ca);
+  for (int64_t c = 0; c < d; ++c)
     for (int64_t i = 0; i < I; ++i) {
-      for (int64_t r = 0; r < n; ++r) cb[r] = rows_h[r * I + i];
-      if (quant) mx_roundtrip_padded(n, cb);
       double acc = 0.0;
-      for (int64_t r = 0; r < n; ++r) acc += ca[r] * cb[r];
+      for (int64_t r = 0; r < n; ++r) acc += cdy[c * n + r] * ch[i * n + r];
       dwd[c * I + i] = acc;
     }
-  }
-  free(wdt); free(wgut); free(dy); free(dab); free(q); free(ca); free(cb);
+  free(cab); free(cx); free(cdy); free(ch);
+  free(wdt); free(wgut); free(dy); free(dab); free(q);
 }
 
 /* Router weight gradient over the tokens routed here: dWr[e] = sum_t dz_t,e x_t

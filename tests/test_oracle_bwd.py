@@ -299,3 +299,19 @@ def test_mx_weight_gradient_quantises_along_the_rows():
     dy = np.array([oracle.round_bf16(g[0] * float(v)) for v in dout[0]])
     want = np.array([[q1(dy[c]) * q1(h[0, i]) for i in range(h.shape[1])] for c in range(dy.size)])
     np.testing.assert_array_equal(dwd, want)
+
+
+def test_gate_grads_match_the_rows_backward():
+    """gate_grads on the exact forward's y equals the gate gradient the
+    row backward derives (dout . y of the same row)."""
+    rng = np.random.default_rng(41)
+    d, I = 16, 24
+    x = rng.standard_normal((3, d)).astype(np.float32)
+    dout = rng.standard_normal((3, d)).astype(np.float32)
+    wg, wu = (rng.standard_normal((I, d)) * 0.2).astype(np.float32), (rng.standard_normal((I, d)) * 0.2).astype(np.float32)
+    wd = (rng.standard_normal((d, I)) * 0.2).astype(np.float32)
+    y = np.stack([oracle.ffn_row(x[r], wg, wu, wd, "exact")[3] for r in range(3)])
+    got = oracle.gate_grads(dout, y)
+    for r in range(3):
+        assert got[r] == pytest.approx(oracle.bwd_row(x[r], 0.5, dout[r], wg, wu, wd)["dg"],
+                                       rel=1e-12, abs=1e-12)

@@ -149,7 +149,8 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     R = int(L.offsets[-1].item())
     T_pull = int(torch.unique(L.row_src[:R].long() // w.k).numel()) if R > 0 else 0
 
-    trace = Trace(capacity=64 * (args.steps + 1))
+    # (through the backward ring, every window adds its kernels' events)
+    trace = Trace(capacity=512 * (args.steps + 1))
     trace.attach(L.cfg)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -173,13 +174,17 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     # the backward's side work runs on a second stream beside its GEMMs, so
     # its time is the step's wall time less the forward's kernels
     bwd_ms = ms_per_step - fwd_ms
-    kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps}
+    kernels = {n: {"avg_ms": float(np.mean(v)), "launches_per_step": len(v) // args.steps,
+                   "ms_per_step": float(np.sum(v)) / args.steps}
                for n, v in per_kernel.items()}
     # dominant kernel: largest time per step among kernels with a work model
     modeled = [n for n in per_kernel if kernel_work(n, w, R, T_pull)[0] is not None]
     dom = max(modeled, key=lambda n: sum(per_kernel[n]))
     kind, work = kernel_work(dom, w, R, T_pull)
-    avg_s = float(np.mean(per_kernel[dom])) * 1e-3
+    # the work of a step over the kernel's time in the step: per launch for a
+    # kernel launched once per step (through the backward ring, several
+    # windows each launch the kernel over their rows)
+    avg_s = float(np.sum(per_kernel[dom])) / args.steps * 1e-3
     if kind == "alu":
         achieved = work / avg_s / 1e12
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_FMA_TFLOPS, "unit": "TFLOP/s",
@@ -201,15 +206,16 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     # per-kernel roofline fractions, for the record
     for n, v in kernels.items():
         kd, wk = kernel_work(n, w, R, T_pull)
+        t_s = v["ms_per_step"] * 1e-3
         if kd in ("mfma", "mfma_fp8"):
-            v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
+            v["tflops"] = wk / t_s / 1e12
             v["frac_mfma_peak"] = v["tflops"] / (PEAK_FP8_TFLOPS if kd == "mfma_fp8"
                                                  else PEAK_BF16_TFLOPS)
         elif kd == "hbm":
-            v["gbs"] = wk / (v["avg_ms"] * 1e-3) / 1e9
+            v["gbs"] = wk / t_s / 1e9
             v["frac_hbm_peak"] = v["gbs"] / PEAK_HBM_GBS
         elif kd == "alu":
-            v["tflops"] = wk / (v["avg_ms"] * 1e-3) / 1e12
+            v["tflops"] = wk / t_s / 1e12
             v["frac_alu_peak"] = v["tflops"] / PEAK_FP32_FMA_TFLOPS
 
     # run-to-run identity at full size: every output of two consecutive
@@ -285,7 +291,10 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
                    "backward_streams": 2 if (has_bwd and L.aux is not None) else 1,
                    "path": ("ring %d MiB, minibatch %d rows, comm/gemm workgroups %s/%s"
                             % (args.ring_mib, mb, args.comm_wgs or "auto",
-                               args.gemm_wgs or "auto")) if args.ring_mib else "staged"},
+                               args.gemm_wgs or "auto")) if args.ring_mib else "staged",
+                   "backward_path": (("ring %d MiB in windows of whole %d-row minibatches"
+                                      % (args.bwd_ring_mib, mb)) if args.bwd_ring_mib
+                                     else "one launch per step") if has_bwd else None},
         "fwd_tokens_per_s": T_tok / (fwd_ms * 1e-3),
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms if has_bwd else None,
@@ -361,7 +370,8 @@ def run_workload(args, name, np, torch):
     def make_layer(mb):
         L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
                      len(w.own), device=dev, with_bwd=has_bwd, ring_bytes=args.ring_mib << 20,
-                     minibatch_rows=mb, comm_wgs=args.comm_wgs, gemm_wgs=args.gemm_wgs)
+                     minibatch_rows=mb, comm_wgs=args.comm_wgs, gemm_wgs=args.gemm_wgs,
+                     bwd_ring_bytes=(args.bwd_ring_mib << 20) if has_bwd else 0)
         L.set_inputs(dev_in["xs"], dev_in["wr"], dev_in["bias"], dev_in["e2l"], dev_in["wg"],
                      dev_in["wu"], dev_in["wd"], other_topk=other)
         return L
@@ -389,6 +399,25 @@ def run_workload(args, name, np, torch):
         results.append(measure(a, w, L, d_out, has_bwd, mb, np, torch, Trace))
         if tuned is not None:
             results[-1]["config"]["tuner_ms_per_forward"] = tuned
+        del L
+        torch.cuda.empty_cache()
+    # the skewed mid-size layer's configuration names a 256 MiB ring for its
+    # backward: the same step with the backward through that ring (windows of
+    # whole minibatches) is measured beside the one-launch backward
+    if (args.path == "auto" and name == "C5" and not args.bwd_ring_mib and not args.mb_sweep
+            and not args.ring_mib):
+        a = argparse.Namespace(**{**vars(args), "bwd_ring_mib": 256})
+        L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
+                     len(w.own), device=dev, with_bwd=True, minibatch_rows=args.mb,
+                     bwd_ring_bytes=256 << 20)
+        L.set_inputs(dev_in["xs"], dev_in["wr"], dev_in["bias"], dev_in["e2l"], dev_in["wg"],
+                     dev_in["wu"], dev_in["wd"], other_topk=other)
+        rr = measure(a, w, L, d_out, True, args.mb, np, torch, Trace)
+        results[-1]["ring_backward"] = {
+            "ms_per_step": rr["ms_per_step"], "tokens_per_s": rr["value"],
+            "bwd_ms": rr["bwd_ms"], "backward_path": rr["config"]["backward_path"],
+            "determinism": rr["determinism"],
+            "kernels": {n: v for n, v in rr["kernels"].items() if n.startswith("bwd")}}
         del L
         torch.cuda.empty_cache()
     for r in results:
@@ -502,6 +531,9 @@ def main():
                     help="forward through the persistent ring kernel with a ring of this many "
                          "MiB (0 = one launch per step)")
     ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
+    ap.add_argument("--bwd-ring-mib", type=int, default=0,
+                    help="backward through a ring of this many MiB (windows of whole "
+                         "minibatches; 0 = one launch per step over all rows)")
     ap.add_argument("--comm-wgs", type=int, default=0, help="ring path: dispatch workgroups")
     ap.add_argument("--gemm-wgs", type=int, default=0, help="ring path: GEMM workgroups")
     ap.add_argument("--graph", action="store_true",

@@ -29,7 +29,7 @@ STATUS = {
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
            "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_layer_fwd_macro",
-           "mok_version")
+           "mok_mx_prepare_bwd", "mok_version")
 
 
 class MokError(RuntimeError):
@@ -176,14 +176,16 @@ class AuxStream:
 
 class mok_expert_weights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("wt_down", ctypes.c_void_p), ("st_down", ctypes.c_void_p),
+                ("wt_gu", ctypes.c_void_p), ("st_gu", ctypes.c_void_p)]
 
 
 class mok_fwd_state(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p),
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("row_src", ctypes.c_void_p), ("dest_row", ctypes.c_void_p),
-                ("h", ctypes.c_void_p), ("ab", ctypes.c_void_p)]
+                ("h", ctypes.c_void_p), ("ab", ctypes.c_void_p), ("h_scale", ctypes.c_void_p)]
 
 
 class mok_layer_call(ctypes.Structure):
@@ -232,6 +234,7 @@ def lib():
                                             ctypes.POINTER(mok_fwd_state), P, P, P, P]
         L.mok_layer_fwd_macro.argtypes = [cfgp, I32, ctypes.POINTER(mok_layer_call), P, P, P,
                                           ctypes.POINTER(mok_expert_weights), P, P, P]
+        L.mok_mx_prepare_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -276,14 +279,17 @@ def make_config(S, T_src, d, E, k, I, E_local, prec, R_cap, minibatch_rows=256, 
                       ring_bytes, comm_wgs, gemm_wgs, wait_limit_us, None, None, bwd_ring_bytes)
 
 
-def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None) -> mok_expert_weights:
+def make_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, wt_down=None,
+                 st_down=None, wt_gu=None, st_gu=None) -> mok_expert_weights:
     return mok_expert_weights(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
-                              _ptr(s_down))
+                              _ptr(s_down), _ptr(wt_down), _ptr(st_down), _ptr(wt_gu),
+                              _ptr(st_gu))
 
 
-def make_state(topk_idx, topk_gate, counts, offsets, row_src, dest_row, h, ab) -> mok_fwd_state:
+def make_state(topk_idx, topk_gate, counts, offsets, row_src, dest_row, h, ab,
+               h_scale=None) -> mok_fwd_state:
     return mok_fwd_state(_ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(offsets),
-                         _ptr(row_src), _ptr(dest_row), _ptr(h), _ptr(ab))
+                         _ptr(row_src), _ptr(dest_row), _ptr(h), _ptr(ab), _ptr(h_scale))
 
 
 # ------------------------------------------------------------------ entry points
@@ -380,6 +386,12 @@ def mok_tune_fwd(cfg, mbs, comms, reps, ws_bytes, own_lo, own_n, src_x, w_router
 def mok_mx_quantize(rows, K, src, codes, scales, stream=None):
     _check("mok_mx_quantize", lib().mok_mx_quantize(rows, K, _ptr(src), _ptr(codes), _ptr(scales),
                                                     _stream(stream)))
+
+
+def mok_mx_prepare_bwd(cfg, w_gate, w_up, w_down, wt_down, st_down, wt_gu, st_gu, stream=None):
+    _check("mok_mx_prepare_bwd", lib().mok_mx_prepare_bwd(
+        ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wt_down), _ptr(st_down),
+        _ptr(wt_gu), _ptr(st_gu), _stream(stream)))
 
 
 def mok_ring_layout(cfg):

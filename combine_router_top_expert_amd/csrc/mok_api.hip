@@ -38,7 +38,9 @@ bool valid_cfg(const mok_config* c) {
 
 struct Ws {
   size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
-      r_row_src, r_dest_row, r_scratch, bx, wpart, wpart_down, worder, bwin, bring, total;
+      r_row_src, r_dest_row, r_scratch, bx, wpart, wpart_down, worder, bwin, bring, mx_dyq,
+      mx_dys, mx_dabq, mx_dabs, mx_hdeq, mx_dabT, mx_dabTs, mx_xT, mx_xTs, mx_dyT, mx_dyTs, mx_hT,
+      mx_hTs, total;
 };
 
 // The bf16 backward runs through the ring (window by window) when cfg has one.
@@ -95,7 +97,7 @@ Ws ws_layout(const mok_config* c) {
   w.r_scratch = b;
   b += align256(c->E <= 256 ? layout_ws_bytes(N, c->E) : 0);
   w.bx = b;
-  if (!bring)
+  if (!bring && c->prec != MOK_MXFP8)
     b += align256(c->prec == MOK_BF16 ? (size_t)c->d * xt_ld(c->R_cap, c->E_local) * 2
                                       : R * c->d * act_bytes(c->prec));
   w.wpart = b;
@@ -110,6 +112,22 @@ Ws ws_layout(const mok_config* c) {
   b += align256((size_t)(4 + c->E_local) * sizeof(int32_t));
   w.bring = b;
   if (bring) b += align256((size_t)c->bwd_ring_bytes);
+  // MXFP8 backward: the quantised rows of dy and da | db, h dequantised, and
+  // the weight gradients' operands transposed (every expert's rows padded to
+  // 128 columns), each E4M3 codes + E8M0 scales per 32
+  const bool mx = c->prec == MOK_MXFP8;
+  const size_t cols = mx ? (size_t)bwd_mx_cols(c->R_cap, c->E_local) : 0;
+  const size_t d = (size_t)c->d, I2 = 2 * (size_t)c->I;
+  size_t* const regions[13] = {&w.mx_dyq, &w.mx_dys, &w.mx_dabq, &w.mx_dabs, &w.mx_hdeq,
+                               &w.mx_dabT, &w.mx_dabTs, &w.mx_xT, &w.mx_xTs, &w.mx_dyT,
+                               &w.mx_dyTs, &w.mx_hT, &w.mx_hTs};
+  const size_t bytes[13] = {R * d, R * d / 32, R * I2, R * I2 / 32, R * I2,
+                            I2 * cols, I2 * cols / 32, d * cols, d * cols / 32, d * cols,
+                            d * cols / 32, I2 / 2 * cols, I2 / 2 * cols / 32};
+  for (int i = 0; i < 13; ++i) {
+    *regions[i] = b;
+    if (mx) b += align256(bytes[i]);
+  }
   w.total = f > b ? f : b;
   return w;
 }
@@ -293,6 +311,13 @@ mok_status route_and_layout(const mok_config* cfg, int32_t own_lo, int32_t own_n
 }
 
 // One call's descriptor for the ring kernel.
+// Where the forward writes h's MX scales: the caller's buffer when the state
+// has one (kept for the backward), else call c's region of the workspace.
+uint8_t* h_scale_of(const mok_config* cfg, const mok_fwd_state* st, char* wsb, int c) {
+  if (st->h_scale) return st->h_scale;
+  return (uint8_t*)(wsb + ws_layout(cfg).hscale) + (size_t)c * cfg->R_cap * (cfg->I / 32);
+}
+
 RingCall ring_call(const mok_config* cfg, int32_t own_lo, int32_t own_n, const void* const* src_x,
                    const mok_fwd_state* st, void* const* staging, void* const* out,
                    uint8_t* h_scale) {
@@ -307,7 +332,7 @@ RingCall ring_call(const mok_config* cfg, int32_t own_lo, int32_t own_n, const v
   c.gate = st->topk_gate;
   c.h = st->h;
   c.h_scale = h_scale;
-  c.ab = cfg->prec == MOK_BF16 ? st->ab : nullptr;
+  c.ab = st->ab;  // a | b for the backward pass (bf16 and MXFP8), or null
   c.own_lo = own_lo;
   c.own_n = own_n;
   return c;
@@ -383,7 +408,7 @@ mok_status layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
     // workgroups run GEMM1 + SwiGLU and GEMM2 and push to staging, and the
     // dispatch side runs the final weighted combine once the pushes are in
     const RingCall c = ring_call(cfg, own_lo, own_n, src_x, st, staging, out,
-                                 (uint8_t*)(wsb + wl.hscale));
+                                 h_scale_of(cfg, st, wsb, 0));
     rc = run_ring(cfg, 1, &c, w, wsb, dev_status, sm, tr);
     if (rc != MOK_OK) return rc;
     return last_combine(cfg, c, sm, tr);
@@ -400,7 +425,7 @@ mok_status layer_fwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
       if (rc != MOK_OK) return rc;
       rc = launch_ffn_mx(cfg->d, cfg->I, cfg->E_local, cfg->R_cap, (const uint8_t*)(wsb + wl.xperm),
                          (const uint8_t*)(wsb + wl.xscale), st->offsets, st->row_src, w,
-                         (uint8_t*)st->h, (uint8_t*)(wsb + wl.hscale), st->ab, nullptr, &stg,
+                         (uint8_t*)st->h, h_scale_of(cfg, st, wsb, 0), st->ab, nullptr, &stg,
                          cfg->T_src, cfg->k, sm, tr);
     } else if (cfg->prec == MOK_BF16) {
       // the pull dispatch runs inside GEMM1: its A rows are read from the sources
@@ -512,7 +537,7 @@ mok_status mok_layer_fwd_macro(const mok_config* cfg, int32_t n_calls,
   for (int c = 0; c < n_calls; ++c)
     rc_calls[c] = ring_call(cfg, calls[c].own_lo, calls[c].own_n, calls[c].src_x, calls[c].st,
                             calls[c].staging, calls[c].out,
-                            (uint8_t*)(wsb + wl.hscale) + (size_t)c * cfg->R_cap * (cfg->I / 32));
+                            h_scale_of(cfg, calls[c].st, wsb, c));
   const mok_status rc = run_ring(cfg, n_calls, rc_calls, w, wsb, dev_status, sm, tr);
   if (rc != MOK_OK) return rc;
   return last_combine(cfg, rc_calls[n_calls - 1], sm, tr);
@@ -544,9 +569,13 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          float* dw_router, void* ws, int32_t* dev_status, void* stream) {
   (void)expert_to_local;
   if (!valid_cfg(cfg) || !own_range_ok(cfg, own_lo, own_n)) return MOK_EINVAL;
-  if (cfg->prec == MOK_MXFP8) return MOK_EINVAL;
   if (!d_out || !src_x || !w_router || !w || !st || !staging || !d_gate || !dx_stage || !ws)
     return MOK_EINVAL;
+  const bool mx = cfg->prec == MOK_MXFP8;
+  if (mx) {
+    if (!w->wt_down || !w->st_down || !w->wt_gu || !w->st_gu || !st->h_scale) return MOK_EINVAL;
+    if (cfg->d % 128 != 0) return MOK_ESHAPE;  // dh contracts over d in 128-wide stages
+  }
   if (!dw_gate || !dw_up || !dw_down || !st->ab || !st->h) return MOK_EINVAL;
   if (!st->topk_idx || !st->topk_gate || !st->offsets || !st->dest_row) return MOK_EINVAL;
   if (cfg->R_cap > 0 && !st->row_src) return MOK_EINVAL;
@@ -632,8 +661,29 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
     p.win_slots = slots;
     p.n_win = nwin;
   }
+  if (mx) {
+    p.mx_hs = st->h_scale;
+    p.mx_wt_down = w->wt_down;
+    p.mx_st_down = w->st_down;
+    p.mx_wt_gu = w->wt_gu;
+    p.mx_st_gu = w->st_gu;
+    p.mx_dyq = (uint8_t*)(wsb + wl.mx_dyq);
+    p.mx_dys = (uint8_t*)(wsb + wl.mx_dys);
+    p.mx_dabq = (uint8_t*)(wsb + wl.mx_dabq);
+    p.mx_dabs = (uint8_t*)(wsb + wl.mx_dabs);
+    p.mx_hdeq = wsb + wl.mx_hdeq;
+    p.mx_cols = bwd_mx_cols(cfg->R_cap, cfg->E_local);
+    p.mx_dabT = (uint8_t*)(wsb + wl.mx_dabT);
+    p.mx_dabTs = (uint8_t*)(wsb + wl.mx_dabTs);
+    p.mx_xT = (uint8_t*)(wsb + wl.mx_xT);
+    p.mx_xTs = (uint8_t*)(wsb + wl.mx_xTs);
+    p.mx_dyT = (uint8_t*)(wsb + wl.mx_dyT);
+    p.mx_dyTs = (uint8_t*)(wsb + wl.mx_dyTs);
+    p.mx_hT = (uint8_t*)(wsb + wl.mx_hT);
+    p.mx_hTs = (uint8_t*)(wsb + wl.mx_hTs);
+  }
   p.tr = cfg->trace;
-  if (cfg->aux) {
+  if (cfg->aux && !mx) {
     const mok_aux* a = cfg->aux;
     if (!a->stream || a->stream == stream || !a->events[0] || !a->events[1] || !a->events[2])
       return MOK_EINVAL;
@@ -642,6 +692,16 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   }
   trace_mark(p.tr, "start", (hipStream_t)stream);
   return launch_bwd(p, (hipStream_t)stream);
+}
+
+mok_status mok_mx_prepare_bwd(const mok_config* cfg, const void* w_gate, const void* w_up,
+                              const void* w_down, uint8_t* wt_down, uint8_t* st_down,
+                              uint8_t* wt_gu, uint8_t* st_gu, void* stream) {
+  if (!valid_cfg(cfg)) return MOK_EINVAL;
+  if (!w_gate || !w_up || !w_down || !wt_down || !st_down || !wt_gu || !st_gu) return MOK_EINVAL;
+  if (cfg->d % 128 != 0) return MOK_ESHAPE;
+  return launch_mx_prepare_bwd(cfg->E_local, cfg->d, cfg->I, w_gate, w_up, w_down, wt_down,
+                               st_down, wt_gu, st_gu, (hipStream_t)stream);
 }
 
 mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,

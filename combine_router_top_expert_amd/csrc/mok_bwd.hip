@@ -135,8 +135,62 @@ __global__ __launch_bounds__(kThreads) void rc_pull_kernel(BwdPlan p) {
   }
 }
 
+// Through the ring: the rows of the current window [lo, hi), row-major (a
+// workgroup per row: the window's rows are few, and a scan of every token
+// per window would cost more than re-reading a token's upstream gradient
+// for each of its rows).  Same sums in the same order as above.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rc_pull_rows_kernel(BwdPlan p) {
+  __shared__ float red[kThreads / 64];
+  constexpr int U = 16 / sizeof(T);
+  const int lo = p.win[0], hi = p.win[1];
+  for (int r = lo + blockIdx.x; r < hi; r += gridDim.x) {
+    const int n = p.row_src[r];
+    const int tok = n / p.k, j = n % p.k;
+    const int s = tok / p.T_src, t = tok % p.T_src;
+    const float g = p.topk_gate[n];
+    const T* dout = reinterpret_cast<const T*>(p.d_out.p[s]) + (size_t)t * p.d;
+    const T* y = reinterpret_cast<const T*>(p.staging.p[s]) + ((size_t)t * p.k + j) * p.d;
+    T* dy = reinterpret_cast<T*>(p.dy) + (size_t)(r - lo) * p.d;
+    float part = 0.0f;
+    for (int u = threadIdx.x; u < p.d / U; u += kThreads) {
+      const uint4 dv = ld16(dout + u * U), yv = ld16(y + u * U);
+      const T* de = reinterpret_cast<const T*>(&dv);
+      const T* ye = reinterpret_cast<const T*>(&yv);
+      uint4 ov;
+      T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const float dvf = to_f32<T>(de[i]);
+        part = __builtin_fmaf(dvf, to_f32<T>(ye[i]), part);
+        oe[i] = from_f32<T>(g * dvf);
+      }
+      st16(dy + u * U, ov);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float tot = 0.0f;
+      for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
+      p.d_gate[n] = tot;
+    }
+    __syncthreads();  // red is read before the next row writes it
+  }
+}
+
 template <typename T>
 mok_status launch_rc_pull(const BwdPlan& p, hipStream_t stream) {
+  if (p.win) {
+    if (p.R_cap == 0) return MOK_OK;
+    const int cus = device_cus();
+    int blocks = (cus > 0 ? cus : 256) * 8;
+    if (blocks > p.win_rows) blocks = p.win_rows;
+    hipLaunchKernelGGL(rc_pull_rows_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    trace_mark(p.tr, "bwd_reverse_combine_pull", stream);
+    return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+  }
   const int64_t n_tok = (int64_t)p.S * p.T_src;
   if (n_tok == 0 || p.R_cap == 0) return MOK_OK;
   const int64_t blocks = (n_tok + kPullTok - 1) / kPullTok;
@@ -672,9 +726,22 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
   return run_bwd_tail<T>(p, stream);
 }
 
+// MXFP8 backward: the bf16 reverse-combine pull, the four expert GEMMs on
+// the scaled matrix cores, then the per-token part as for bf16.
+mok_status run_bwd_mx(const BwdPlan& p, hipStream_t stream) {
+  if (p.R_cap > 0) {
+    const mok_status rc = launch_rc_pull<bf16_t>(p, stream);
+    if (rc != MOK_OK) return rc;
+  }
+  const mok_status rc = launch_bwd_mx_gemms(p, stream);
+  if (rc != MOK_OK) return rc;
+  return run_bwd_tail<bf16_t>(p, stream);
+}
+
 }  // namespace
 
 mok_status launch_bwd(const BwdPlan& p, hipStream_t stream) {
+  if (p.prec == MOK_MXFP8) return run_bwd_mx(p, stream);
   return p.prec == MOK_F32 ? run_bwd<float>(p, stream) : run_bwd<bf16_t>(p, stream);
 }
 

@@ -599,6 +599,16 @@ mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int m
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
+mok_status launch_swiglu_bwd(const BwdPlan& p, hipStream_t stream) {
+  const size_t pieces = (size_t)launch_rows(p) * (p.I / 8);
+  if (pieces == 0) return MOK_OK;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((pieces + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, reinterpret_cast<const bf16_t*>(p.ab),
+                     reinterpret_cast<bf16_t*>(p.dab), p.offsets, p.E_local, p.R_cap, p.I, p.win);
+  trace_mark(p.tr, "bwd_swiglu", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
 mok_status launch_bwd_dgrad(const BwdPlan& p, hipStream_t stream) {
   if (p.R_cap == 0) return MOK_OK;
   const int rows = launch_rows(p);
@@ -618,11 +628,8 @@ mok_status launch_bwd_dgrad(const BwdPlan& p, hipStream_t stream) {
   d.ntn = (p.I + Default::BN - 1) / Default::BN;
   hipLaunchKernelGGL(dh_g2<Default>, dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
   trace_mark(p.tr, "bwd_dh", stream);
-  const size_t pieces = (size_t)rows * (p.I / 8);
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((pieces + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, d.ab, d.dab, p.offsets, p.E_local, p.R_cap, p.I,
-                     p.win);
-  trace_mark(p.tr, "bwd_swiglu", stream);
+  const mok_status rc = launch_swiglu_bwd(p, stream);
+  if (rc != MOK_OK) return rc;
   DxArgs x;
   x.dab = reinterpret_cast<const bf16_t*>(p.dab);
   x.win = p.win;

@@ -145,7 +145,6 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
                          const mok_expert_weights* w, uint8_t* hq, uint8_t* hs, void* ab, void* y,
                          const DstTable* staging, int T_src, int k, hipStream_t stream,
                          mok_trace* tr) {
-  (void)ab;  // the MXFP8 layer keeps no pre-activations (it has no backward pass)
   if (R_cap == 0) return MOK_OK;
   if (d % MxCfg::KB != 0 || I % MxCfg::KB != 0) return MOK_EINVAL;
   const int mt = (R_cap + BM - 1) / BM + E_local;
@@ -159,6 +158,7 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
   a1.offsets = offsets;
   a1.hq = hq;
   a1.hs = hs;
+  a1.ab = reinterpret_cast<bf16_t*>(ab);
   a1.d = d;
   a1.I = I;
   a1.E_local = E_local;
@@ -188,6 +188,40 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
   a2.k = k;
   hipLaunchKernelGGL(ffn2_mx, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2, gtab);
   trace_mark(tr, "ffn2_down_mx", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_mx_rows_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
+                               const uint8_t* bs, int K, int N, int E_local, int R_cap,
+                               const int32_t* offsets, const int32_t* row_src, void* y, int ldy,
+                               const DstTable* push, int T_src, int k, hipStream_t stream,
+                               mok_trace* tr, const char* name) {
+  if (R_cap == 0) return MOK_OK;
+  if (K % MxCfg::KB != 0) return MOK_EINVAL;
+  const int mt = (R_cap + BM - 1) / BM + E_local;
+  F2Args a;
+  memset(&a, 0, sizeof(a));
+  a.h = reinterpret_cast<const bf16_t*>(aq);
+  a.hs = as;
+  a.wd = reinterpret_cast<const bf16_t*>(bq);
+  a.sd = bs;
+  a.offsets = offsets;
+  a.row_src = row_src;
+  a.y = reinterpret_cast<bf16_t*>(y);
+  a.ldy = ldy;
+  a.push = push != nullptr;
+  DstTable tab;
+  memset(&tab, 0, sizeof(tab));
+  if (push) tab = *push;
+  a.d = N;  // output columns (the tile's N)
+  a.I = K;  // contraction
+  a.E_local = E_local;
+  a.R_cap = R_cap;
+  a.ntn = (N + MxCfg::BN - 1) / MxCfg::BN;
+  a.T_src = T_src;
+  a.k = k;
+  hipLaunchKernelGGL(ffn2_mx, dim3((unsigned)(mt * a.ntn)), dim3(kThreads), 0, stream, a, tab);
+  trace_mark(tr, name, stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

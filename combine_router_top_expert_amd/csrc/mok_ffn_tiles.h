@@ -43,7 +43,8 @@ struct F2Args {
   const uint8_t* sd;   // MX: [E_local, d, I/32] scales of W_down
   const int32_t* offsets;
   const int32_t* row_src;
-  bf16_t* y;           // [R_cap, d] when not pushing
+  bf16_t* y;           // [R_cap, d] when not pushing (row stride ldy, 0 = d)
+  int ldy;
   int push;            // 1: push each row to its staging row (table given to the tile)
   int d, I, E_local, R_cap, ntn, T_src, k;
 };
@@ -58,6 +59,7 @@ struct F1MxArgs {
   const int32_t* offsets;
   uint8_t* hq;         // [R_cap, I] codes of h
   uint8_t* hs;         // [R_cap, I/32] scales of h
+  bf16_t* ab;          // [R_cap, 2I] a | b kept for the backward pass, or null
   int d, I, E_local, R_cap, ntn;
 };
 
@@ -157,7 +159,7 @@ __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GT
       dst = reinterpret_cast<bf16_t*>(staging.p[tok / a.T_src]) +
             ((size_t)(tok % a.T_src) * a.k + j) * a.d;
     } else {
-      dst = a.y + (size_t)r * a.d;
+      dst = a.y + (size_t)r * (a.ldy ? a.ldy : a.d);
     }
     *reinterpret_cast<uint4*>(dst + col) = st.raw(srow, c);
   });
@@ -243,6 +245,11 @@ __device__ __forceinline__ void ffn1_mx_tile(const F1MxArgs& a, char* smem, cons
         st.get(srow, cg + 8, bv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) hv[e] = silu_f(av[e]) * bv[e];
+        if (a.ab) {  // a | b for the backward pass, bf16 from the fp32 accumulators
+          bf16_t* abr = a.ab + (size_t)r * 2 * a.I;
+          *reinterpret_cast<uint2*>(abr + i) = pack4_bf16(av[0], av[1], av[2], av[3]);
+          *reinterpret_cast<uint2*>(abr + a.I + i) = pack4_bf16(bv[0], bv[1], bv[2], bv[3]);
+        }
       }
       float amax = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));

@@ -45,6 +45,16 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
                          const DstTable* staging, int T_src, int k, hipStream_t stream,
                          mok_trace* tr = nullptr);
 
+// MX GEMM over grouped rows on the scaled matrix cores: out[r][n] = sum over
+// k < K of A[r][k] B_e[n][k] for the rows r of each local expert e, A and B
+// E4M3 codes (K-major, B [E_local, N, K]) with E8M0 scales per 32 along k;
+// bf16 out stored at y + r ldy, or pushed to the staging rows of the items.
+mok_status launch_mx_rows_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
+                               const uint8_t* bs, int K, int N, int E_local, int R_cap,
+                               const int32_t* offsets, const int32_t* row_src, void* y, int ldy,
+                               const DstTable* push, int T_src, int k, hipStream_t stream,
+                               mok_trace* tr, const char* name);
+
 // bf16 forward GEMMs on the pipelined engine; x == null gathers the A rows
 // from the source table through row_src.
 mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
@@ -67,7 +77,7 @@ struct RingCall {       // one layer call (macrobatch) through the ring
   const float* gate;
   void* h;              // [R_cap, I] (MX: codes)
   uint8_t* h_scale;     // MX: [R_cap, I/32]
-  void* ab;             // [R_cap, 2I] or null (bf16)
+  void* ab;             // [R_cap, 2I] bf16 a | b (bf16 and MXFP8 layers), or null
   int own_lo, own_n;
 };
 struct RingPlan {
@@ -136,6 +146,15 @@ struct BwdPlan {
   int win_rows;       // rows of a window, at most (slots x minibatch rows)
   int64_t win_cols;   // leading dimension of the window's transposed token rows
   int win_mb, win_slots, n_win;
+  // MXFP8 backward (prec == MOK_MXFP8): E4M3 codes + E8M0 scales per 32
+  const uint8_t* mx_hs;                     // [R_cap, I/32] the forward's h scales
+  const uint8_t *mx_wt_down, *mx_st_down;   // [E_local, I, d], [.., d/32]
+  const uint8_t *mx_wt_gu, *mx_st_gu;       // [E_local, d, 2I], [.., 2I/32]
+  uint8_t *mx_dyq, *mx_dys;                 // dy rows along d
+  uint8_t *mx_dabq, *mx_dabs;               // [da|db] rows along 2I
+  void* mx_hdeq;                            // [R_cap, I] bf16: h as GEMM2 read it
+  int64_t mx_cols;                          // columns of the transposed operands
+  uint8_t *mx_dabT, *mx_dabTs, *mx_xT, *mx_xTs, *mx_dyT, *mx_dyTs, *mx_hT, *mx_hTs;
   mok_trace* tr;    // host-side trace, may be null
   hipStream_t aux;      // second stream for the work beside the GEMMs, or null
   hipEvent_t aux_ev[3]; // fork/join events of the second stream
@@ -155,6 +174,15 @@ mok_status launch_bwd_wgrad(const BwdPlan& p, const void* x_perm, hipStream_t st
                             bool reduce);
 mok_status launch_bwd_reduce(const BwdPlan& p, hipStream_t stream);
 mok_status launch_bwd_window(const BwdPlan& p, int w, hipStream_t stream);
+mok_status launch_swiglu_bwd(const BwdPlan& p, hipStream_t stream);
+// MXFP8 backward GEMMs (dh, SwiGLU backward, dx push, weight gradients) and
+// their transposed operands; columns of those operands: every local expert's
+// rows padded to 128.
+mok_status launch_bwd_mx_gemms(const BwdPlan& p, hipStream_t stream);
+int64_t bwd_mx_cols(int R_cap, int E_local);
+mok_status launch_mx_prepare_bwd(int E_local, int d, int I, const void* w_gate, const void* w_up,
+                                 const void* w_down, uint8_t* wt_down, uint8_t* st_down,
+                                 uint8_t* wt_gu, uint8_t* st_gu, hipStream_t stream);
 // Geometry of the backward's ring windows for cfg (bf16, ring_bytes > 0):
 // slots of minibatch_rows rows, each holding dy and da | db rows and the
 // transposed token rows; false if the ring holds no slot.

@@ -425,6 +425,7 @@ __device__ void gemm_role(const RingArgs& a, const CallsLds& L, int* s_val, char
           f1.offsets = call.offsets;
           f1.hq = reinterpret_cast<uint8_t*>(call.h);
           f1.hs = call.h_scale;
+          f1.ab = reinterpret_cast<bf16_t*>(call.ab);
           ffn1_mx_tile(
               f1, smem, g, nt,
               [&](int row) -> const bf16_t* {

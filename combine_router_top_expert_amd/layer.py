@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import (MAX_SOURCES, AuxStream, make_config, make_state, make_weights, mok_layer_bwd, mok_layer_fwd,
-               mok_mx_quantize, mok_tune_fwd, mok_workspace_bytes, STATUS)
+               mok_mx_prepare_bwd, mok_mx_quantize, mok_tune_fwd, mok_workspace_bytes, STATUS)
 
 
 def _dt(prec: str):
@@ -64,10 +64,13 @@ class MoELayer:
         if two_streams and with_bwd and prec == "bf16" and not bwd_ring_bytes:
             self.aux = AuxStream(dev)
             self.aux.attach(self.cfg)
+        # MXFP8: h holds E4M3 codes; its scales are kept for the backward
+        self.h_scale = (torch.zeros(max(R_cap, 1) * I // 32, dtype=torch.uint8, device=dev)
+                        if prec == "mxfp8" and with_bwd else None)
         self.state = make_state(self.topk_idx, self.topk_gate, self.counts, self.offsets,
-                                self.row_src, self.dest_row, self.h, self.ab)
+                                self.row_src, self.dest_row, self.h, self.ab, self.h_scale)
         self.with_bwd = with_bwd
-        if with_bwd and prec != "mxfp8":
+        if with_bwd:
             self.d_gate = torch.zeros(max(N, 1), dtype=torch.float32, device=dev)
             self.dx_stage = [torch.zeros(T_src * k, d, dtype=act, device=dev) for _ in range(S)]
             self.d_x = [torch.zeros(T_src, d, dtype=act, device=dev) if own_lo <= s < own_lo + own_n
@@ -107,7 +110,7 @@ class MoELayer:
         rows of local slots on every pass, so only remote slots keep them."""
         per = self.T_src * self.k
         self.staging[s].copy_(y)
-        if self.with_bwd and self.prec != "mxfp8":
+        if self.with_bwd:
             self.d_gate[s * per:(s + 1) * per].copy_(d_gate)
             if dx is not None:
                 self.dx_stage[s].copy_(dx)
@@ -123,7 +126,17 @@ class MoELayer:
             mok_mx_quantize(rows, K, w, codes, scales)
             q.append((codes, scales))
         self.wq = q
-        self.weights = make_weights(q[0][0], q[1][0], q[2][0], q[0][1], q[1][1], q[2][1])
+        t = [None] * 4
+        if self.with_bwd:
+            # the backward's transposed operands: W_down^T and [W_gate; W_up]^T
+            E, d, I = self.E_local, self.d, self.I
+            t = [torch.empty(E * I * d, dtype=torch.uint8, device=self.device),
+                 torch.empty(E * I * d // 32, dtype=torch.uint8, device=self.device),
+                 torch.empty(E * d * 2 * I, dtype=torch.uint8, device=self.device),
+                 torch.empty(E * d * 2 * I // 32, dtype=torch.uint8, device=self.device)]
+            mok_mx_prepare_bwd(self.cfg, self.w_gate, self.w_up, self.w_down, *t)
+        self.wt = t
+        self.weights = make_weights(q[0][0], q[1][0], q[2][0], q[0][1], q[1][1], q[2][1], *t)
 
     # ---------------------------------------------------------------- passes
     def forward(self, stream=None):

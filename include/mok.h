@@ -158,7 +158,12 @@ typedef struct mok_config {
 /* Expert weights of the E_local local experts (see Layout above).  For
  * MOK_MXFP8 the three matrices hold E4M3 codes (uint8, same shapes) and
  * s_gate, s_up, s_down their E8M0 scales ([E_local, I, d/32] and
- * [E_local, d, I/32]); otherwise the s_* pointers are NULL. */
+ * [E_local, d, I/32]); otherwise the s_* pointers are NULL.
+ * The MXFP8 backward (mok_layer_bwd) contracts the weights along their other
+ * axis and reads them transposed, from mok_mx_prepare_bwd: wt_down
+ * [E_local, I, d] codes (W_down^T, blocks of 32 along d) with st_down
+ * [E_local, I, d/32]; wt_gu [E_local, d, 2I] codes ([W_gate; W_up]^T,
+ * blocks of 32 along 2I) with st_gu [E_local, d, 2I/32].  NULL otherwise. */
 typedef struct mok_expert_weights {
   const void* w_gate;
   const void* w_up;
@@ -166,6 +171,10 @@ typedef struct mok_expert_weights {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
+  const uint8_t* wt_down;
+  const uint8_t* st_down;
+  const uint8_t* wt_gu;
+  const uint8_t* st_gu;
 } mok_expert_weights;
 
 /* State the forward pass leaves for the backward pass (all caller-owned). */
@@ -177,7 +186,11 @@ typedef struct mok_fwd_state {
   int32_t* row_src;    /* [R_cap] row -> item n */
   int32_t* dest_row;   /* [S*T_src*k] item n -> row, -1 for remote experts (>= R_cap: dropped) */
   void* h;             /* [R_cap, I] SwiGLU output in the activation dtype (bf16 / f32) */
-  void* ab;            /* [R_cap, 2I] pre-activation a | b in the activation dtype, or NULL */
+  void* ab;            /* [R_cap, 2I] pre-activation a | b in the activation dtype (bf16 for
+                          MOK_MXFP8), or NULL */
+  uint8_t* h_scale;    /* MOK_MXFP8: [R_cap, I/32] E8M0 scales of h (h holds its E4M3
+                          codes), kept for the backward; NULL = the forward keeps them in
+                          its workspace only.  Unused otherwise. */
 } mok_fwd_state;
 
 /* Bytes of device workspace the calls below need for `cfg` (256-byte aligned
@@ -333,7 +346,16 @@ mok_status mok_layer_fwd_noalloc(const mok_config* cfg, int32_t own_lo, int32_t 
  *     dropped beyond R_cap;
  *   dw_gate, dw_up [E_local, I, d], dw_down [E_local, d, I] fp32 (overwritten);
  *   dw_router [E, d] fp32 over the own tokens (overwritten), or NULL.
- * Only MOK_F32 and MOK_BF16 are supported (MOK_EINVAL otherwise). */
+ * MOK_MXFP8 [K02 MXFP8 in the GEMM data paths; K03 the backward in MXFP8]:
+ * the four expert GEMMs run on the scaled matrix cores, each operand E4M3
+ * with one E8M0 scale per 32 along its contraction axis, quantised from the
+ * stored bf16 values: dy and [da|db] along the row, the weight gradients'
+ * operands along the expert's rows (blocks of 32 from the expert's first
+ * row, zero padded), h as the forward's GEMM2 read it.  It needs st->ab,
+ * st->h_scale and the prepared wt_* / st_* weights (MOK_EINVAL otherwise),
+ * and d % 128 == 0, I % 64 == 0 (MOK_ESHAPE); bwd_ring_bytes and aux are not
+ * used.  The rows, the router path and the outputs are bf16 as for MOK_BF16.
+ * MOK_F32, MOK_BF16 and MOK_MXFP8 are supported. */
 mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          const void* const* d_out, const void* const* src_x,
                          const void* w_router, const int32_t* expert_to_local,
@@ -341,6 +363,19 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          void* const* staging, float* d_gate, void* const* dx_stage,
                          void* const* d_x, float* dw_gate, float* dw_up, float* dw_down,
                          float* dw_router, void* ws, int32_t* dev_status, void* stream);
+
+/* Transposed MX weights of the MXFP8 backward [K02 MXFP8 in the GEMM data
+ * paths]: from the bf16 weights w_gate, w_up [E_local, I, d] and w_down
+ * [E_local, d, I] (cfg->E_local, d, I; d % 128 == 0 and I % 64 == 0, else
+ * MOK_ESHAPE), writes wt_down [E_local, I, d] = the E4M3 codes of W_down^T
+ * with st_down [E_local, I, d/32], and wt_gu [E_local, d, 2I] = those of
+ * [W_gate; W_up]^T with st_gu [E_local, d, 2I/32] (OCP MX v1.0 blocks of 32
+ * along the last axis; shared exponent floor(log2 amax) - 8, nearest E4M3
+ * with ties to even, saturating).  Caller-owned outputs; run once per weight
+ * update, off the step. */
+mok_status mok_mx_prepare_bwd(const mok_config* cfg, const void* w_gate, const void* w_up,
+                              const void* w_down, uint8_t* wt_down, uint8_t* st_down,
+                              uint8_t* wt_gu, uint8_t* st_gu, void* stream);
 
 /* Tuner of the fused path's minibatch size and workgroup split [K02: the
  * split of SMs between the communication and compute sides is set directly,

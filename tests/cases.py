@@ -74,12 +74,15 @@ def oracle_routing(c: HostCase):
     c.layout = oracle.layout(topk, c.e2l, w.E_local)
 
 
-def oracle_weights(c: HostCase):
-    """Expert weights as the layer uses them (MX round trip for MXFP8)."""
+def oracle_weights(c: HostCase, le=None):
+    """Expert weights as the layer uses them (MX round trip for MXFP8); le:
+    only local expert le's ([I, d], [I, d], [d, I])."""
+    vals = (c.wg_val, c.wu_val, c.wd_val) if le is None else (c.wg_val[le], c.wu_val[le],
+                                                             c.wd_val[le])
     if c.w.prec != "mxfp8":
-        return c.wg_val, c.wu_val, c.wd_val
+        return vals
     out = []
-    for v in (c.wg_val, c.wu_val, c.wd_val):
+    for v in vals:
         K = v.shape[-1]
         codes, scales = oracle.mx_quantize(v.reshape(-1, K).astype(np.float64))
         out.append(oracle.mx_dequantize(codes, scales).astype(np.float32).reshape(v.shape))

@@ -72,8 +72,8 @@ def _layer_fwd_rc(L, cfg):
     """mok_layer_fwd with dummy (never dereferenced) non-null pointers."""
     S = cfg.S
     tab = (ctypes.c_void_p * S)(*([1] * S))
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
     return L.mok_layer_fwd(ctypes.byref(cfg), 0, S, ctypes.cast(tab, ctypes.c_void_p), 1, None, 1,
                            ctypes.byref(w), ctypes.byref(st), ctypes.cast(tab, ctypes.c_void_p),
                            ctypes.cast(tab, ctypes.c_void_p), 1, 1, None)
@@ -98,8 +98,8 @@ def _tune_rc(L, cfg, best=True, reps=1, n_mb=1):
     """mok_tune_fwd with dummy (never dereferenced) non-null pointers."""
     S = cfg.S
     tab = (ctypes.c_void_p * S)(*([1] * S))
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
     mbs = (ctypes.c_int32 * 1)(64)
     out = mok.mok_config()
     return L.mok_tune_fwd(ctypes.byref(cfg), ctypes.cast(mbs, ctypes.c_void_p), n_mb, None, 0,
@@ -123,8 +123,8 @@ def test_backward_second_stream_checked_on_the_host(L):
     S = 2
     tab = (ctypes.c_void_p * S)(*([1] * S))
     tp = ctypes.cast(tab, ctypes.c_void_p)
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
     for aux in (mok.mok_aux(None, (ctypes.c_void_p * 3)(1, 1, 1)),      # no stream
                 mok.mok_aux(7, (ctypes.c_void_p * 3)(1, None, 1)),      # an event missing
                 mok.mok_aux(7, (ctypes.c_void_p * 3)(1, 1, 1))):        # the call's own stream
@@ -150,8 +150,8 @@ def test_layer_fwd_rejects_null_source_pointers(L, which):
     for the own sources.  MOK_EINVAL comes back before anything is enqueued."""
     S = 3
     cfg = _cfg(S=S)
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
     full, _k1 = _tab(S)
     bad, _k2 = _tab(S, 2 if which != "out_own" else 0)
     src = bad if which == "src_x" else full
@@ -169,8 +169,8 @@ def test_layer_fwd_out_of_non_own_source_may_be_null(L):
     without a GPU, with MOK_EDEVICE, never with MOK_EINVAL)."""
     S = 3
     cfg = _cfg(S=S, R_cap=0)
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
     full, _k1 = _tab(S)
     out, _k2 = _tab(S, 2)
     rc = L.mok_layer_fwd(ctypes.byref(cfg), 0, 1, full, 1, None, 1, ctypes.byref(w),
@@ -193,8 +193,8 @@ def test_combine_and_dispatch_reject_null_source_pointers(L):
 def test_layer_bwd_rejects_null_source_pointers(L, which):
     S = 3
     cfg = _cfg(S=S)
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
     full, _k1 = _tab(S)
     bad, _k2 = _tab(S, 2)
     args = {k: (bad if k == which else full) for k in ("d_out", "src_x", "staging", "dx_stage")}
@@ -226,8 +226,8 @@ def test_noalloc_forward_rejections_on_the_host(L):
     (MOK_ESCRATCH) -- both before any device call."""
     S = 2
     full, _k = _tab(S)
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
 
     def rc(cfg):
         return L.mok_layer_fwd_noalloc(ctypes.byref(cfg), 0, 1, full, 1, None, 1, ctypes.byref(w),
@@ -245,8 +245,8 @@ def test_macro_forward_rejections_on_the_host(L):
     S = 2
     full, _k1 = _tab(S)
     bad, _k2 = _tab(S, 1)
-    w = mok.mok_expert_weights(1, 1, 1, 1, 1, 1)
-    st = mok.mok_fwd_state(*([1] * 8))
+    w = mok.mok_expert_weights(*([1] * 10))
+    st = mok.mok_fwd_state(*([1] * 9))
 
     def rc(cfg, n=2, src=full):
         arr = (mok.mok_layer_call * max(n, 1))()
@@ -260,3 +260,26 @@ def test_macro_forward_rejections_on_the_host(L):
     assert rc(_cfg(**ring), n=0) == -1
     assert rc(_cfg(**ring), n=9) == -1             # more than MOK_MAX_CALLS
     assert rc(_cfg(**ring), src=bad) == -1         # a call's NULL source pointer
+
+
+def test_mxfp8_backward_rejections_on_the_host(L):
+    """The MXFP8 backward needs the transposed MX weights and h's scales, and
+    d % 128 == 0; the weight preparation checks its pointers and shapes."""
+    S = 2
+    full, _k = _tab(S)
+
+    def bwd(cfg, w, st):
+        return L.mok_layer_bwd(ctypes.byref(cfg), 0, S, full, full, 1, 1, ctypes.byref(w),
+                               ctypes.byref(st), full, 1, full, full, 1, 1, 1, None, 1, 1, None)
+
+    cfg = _cfg(S=S, prec="mxfp8")
+    st = mok.mok_fwd_state(*([1] * 9))
+    for i in range(6, 10):  # wt_down, st_down, wt_gu, st_gu
+        p = [1] * 10
+        p[i] = None
+        assert bwd(cfg, mok.mok_expert_weights(*p), st) == -1
+    st0 = mok.mok_fwd_state(*([1] * 8), None)  # no h scales kept
+    assert bwd(cfg, mok.mok_expert_weights(*([1] * 10)), st0) == -1
+    assert bwd(_cfg(S=S, prec="mxfp8", d=192), mok.mok_expert_weights(*([1] * 10)), st) == -2
+    assert L.mok_mx_prepare_bwd(ctypes.byref(cfg), 1, 1, 1, 1, 1, 1, None, None) == -1
+    assert L.mok_mx_prepare_bwd(ctypes.byref(_cfg(d=192)), 1, 1, 1, 1, 1, 1, 1, None) == -2

@@ -69,6 +69,10 @@ def kernel_work(name, w, R, T_pull=None):
         "bwd_dx_push": 2.0 * R * 2 * I * d,
         "bwd_wgrad_gate_up": 2.0 * R * 2 * I * d,
         "bwd_wgrad_down": 2.0 * R * d * I,
+        "bwd_dh_mx": 2.0 * R * d * I,
+        "bwd_dx_push_mx": 2.0 * R * 2 * I * d,
+        "bwd_wgrad_gate_up_mx": 2.0 * R * 2 * I * d,
+        "bwd_wgrad_down_mx": 2.0 * R * d * I,
     }
     if name in gemm:
         fp8 = name.endswith("_mx") or (name == "ring_fused_ffn" and w.prec == "mxfp8")
@@ -82,6 +86,12 @@ def kernel_work(name, w, R, T_pull=None):
         "bwd_reverse_combine_pull": (T_pull + 2.0 * R) * d * eb,
         "bwd_swiglu": 5.0 * R * I * eb,                   # read dh, a, b; write da, db
         "bwd_dx_sum_router": (T * k * d + T * d) * eb,    # read k dx rows, write dX
+        # MX quantisation: read bf16, write E4M3 codes + one scale byte per 32
+        "bwd_quantise_dy_mx": R * d * (2 + 33 / 32),
+        "bwd_quantise_dab_mx": R * 2 * I * (2 + 33 / 32),
+        # h's codes to bf16, then [da|db], the token rows, dy and h transposed
+        # and quantised along the rows
+        "bwd_transpose_quantise_mx": R * (I + 2 * I + d + d + I) * (2 + 33 / 32),
     }
     if name in moves:
         return "hbm", moves[name]
@@ -419,6 +429,21 @@ def run_workload(args, name, np, torch):
             "determinism": rr["determinism"],
             "kernels": {n: v for n, v in rr["kernels"].items() if n.startswith("bwd")}}
         del L
+        torch.cuda.empty_cache()
+    # the MXFP8 layer: its backward in MXFP8, measured beside the forward line
+    if args.path == "auto" and name == "C4" and not args.mb_sweep and not args.ring_mib:
+        dmx = [to_device(synth.gen_dout(w, s)[0], w.prec, dev) for s in range(w.S)]
+        L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
+                     len(w.own), device=dev, with_bwd=True, minibatch_rows=args.mb)
+        L.set_inputs(dev_in["xs"], dev_in["wr"], dev_in["bias"], dev_in["e2l"], dev_in["wg"],
+                     dev_in["wu"], dev_in["wd"], other_topk=other)
+        rr = measure(args, w, L, dmx, True, args.mb, np, torch, Trace)
+        results[-1]["mxfp8_backward"] = {
+            "ms_per_step": rr["ms_per_step"], "tokens_per_s": rr["value"],
+            "bwd_ms": rr["bwd_ms"], "roofline": rr["roofline"],
+            "determinism": rr["determinism"],
+            "kernels": {n: v for n, v in rr["kernels"].items() if n.startswith("bwd")}}
+        del L, dmx
         torch.cuda.empty_cache()
     for r in results:
         r["cpu_baseline"] = None

@@ -332,6 +332,7 @@ mok_status launch_bwd_mx_gemms(const BwdPlan& p, hipStream_t stream) {
   // dh = dy W_down: dy quantised along d, into the first half of each dab row
   mok_status rc = launch_mx_quantize(p.R_cap, d, p.dy, p.mx_dyq, p.mx_dys, stream);
   if (rc != MOK_OK) return rc;
+  trace_mark(p.tr, "bwd_quantise_dy_mx", stream);
   rc = launch_mx_rows_gemm(p.mx_dyq, p.mx_dys, p.mx_wt_down, p.mx_st_down, d, I, p.E_local,
                            p.R_cap, p.offsets, p.row_src, p.dab, 2 * I, nullptr, p.T_src, p.k,
                            stream, p.tr, "bwd_dh_mx");
@@ -341,6 +342,7 @@ mok_status launch_bwd_mx_gemms(const BwdPlan& p, hipStream_t stream) {
   // dx = [da|db] [W_gate; W_up]: quantised along 2I, pushed to the dx rows
   rc = launch_mx_quantize(p.R_cap, 2 * I, p.dab, p.mx_dabq, p.mx_dabs, stream);
   if (rc != MOK_OK) return rc;
+  trace_mark(p.tr, "bwd_quantise_dab_mx", stream);
   rc = launch_mx_rows_gemm(p.mx_dabq, p.mx_dabs, p.mx_wt_gu, p.mx_st_gu, 2 * I, d, p.E_local,
                            p.R_cap, p.offsets, p.row_src, nullptr, 0, &p.dx_stage, p.T_src, p.k,
                            stream, p.tr, "bwd_dx_push_mx");

@@ -318,6 +318,26 @@ def measure(args, w, L, d_out, has_bwd, mb, np, torch, Trace):
     return result
 
 
+def hbm_copy_line(args, torch):
+    """A plain device-to-device copy of args.hbm_copy_gib GiB (the runtime's
+    copy kernel), args.steps times: the reference of known size that scales
+    the profiler's byte counters."""
+    n = int(args.hbm_copy_gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(max(args.warmup, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"metric": "device copy (bytes read + written per second)",
+                      "value": 8 * n / dt / 1e9, "unit": "GB/s", "bytes_per_copy": 4 * n,
+                      "steps": args.steps}), flush=True)
+
+
 def hbm_stream_lines(args, torch):
     """The HBM streaming probe (16-byte loads and stores over a grid-stride
     loop, the access of the layer's data-movement kernels): read-only,
@@ -576,6 +596,9 @@ def main():
     ap.add_argument("--macro", type=int, default=0,
                     help="instead of the step: this many forward calls through one ring launch "
                          "(mok_layer_fwd_macro) against the same calls one after the other")
+    ap.add_argument("--hbm-copy-gib", type=float, default=0.0,
+                    help="only a plain device copy of this many GiB (profiler byte-counter "
+                         "reference)")
     ap.add_argument("--hbm-stream-gib", type=float, default=0.0,
                     help="instead of the layer: the HBM streaming probe (read, write, copy) "
                          "over this many GiB")
@@ -592,6 +615,9 @@ def main():
         raise SystemExit("no GPU visible")
     if args.hbm_stream_gib > 0:
         hbm_stream_lines(args, torch)
+        return
+    if args.hbm_copy_gib > 0:
+        hbm_copy_line(args, torch)
         return
     if args.tune and (not args.ring_mib or args.mb_sweep):
         sys.exit("--tune needs --ring-mib and no --mb-sweep")

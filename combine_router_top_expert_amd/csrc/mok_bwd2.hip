@@ -355,14 +355,17 @@ __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
   }
 }
 
-template <class C, int MODE>
+// WIN: launched for one window of the backward through the ring (a.win set);
+// a one-launch kernel (WIN false) has none of the window code, so its
+// accumulators have one definition and stay in registers.
+template <class C, int MODE, bool WIN>
 __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2], s_tpw[257];
   wg_chunk_prefix(a.offsets, a.E_local, a.R_cap, s_cp, s_xp, s_tp, s_rows);
   // ring window: 64-row tiles of the window's pieces before each expert (the
   // expert's first column in the window's transposed rows is 64 s_tpw[e])
-  if (MODE == 0 && a.win) group_prefix(a.win + 3, a.E_local, a.R_cap, s_tpw, 64);
+  if (MODE == 0 && WIN) group_prefix(a.win + 3, a.E_local, a.R_cap, s_tpw, 64);
   const int per = a.mtn * a.ntn;
   const bool spread = wg_spread(per, s_rows);
   int e, c, mt, nt;
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   const int ce = spread ? e_hi : min(cs + kWgChunk, e_hi);
   int off = cs, cnt = ce - cs, lo = 0, xcol = 0;
   bool keep = false;
-  if (a.win) {
+  if constexpr (WIN) {
     // the chunk's rows inside the window; an expert without rows writes its
     // zero gradient in the first window
     lo = a.win[0];
@@ -423,23 +426,37 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
     return a.out0 + ((size_t)e * a.M + m) * a.N;
   };
   Acc<C> acc;
-  if (keep) {
-    // the partial sum of the chunk's earlier rows, as the last window left it
+  // through the ring: the partial sum of the chunk's earlier rows as the
+  // last window left it, else zeros -- one unconditional definition of every
+  // accumulator, right before the main loop continues from it (earlier, the
+  // accumulators would be live across the loaders' set-up and spill)
+  // (branch-free: every lane loads, from the zero page where there is nothing
+  // to carry, so the loads stay in one block)
+  auto preload = [&]() {
+    if constexpr (WIN) {
+      const float* rowp[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + out_row(i);
+        rowp[i] = keep && m < a.M ? out_row_ptr(m) : nullptr;
+      }
 #pragma unroll
-      for (int j = 0; j < C::WNB; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int m = m0 + out_row(i), col = n0 + out_col<C>(j, g4);
-          float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-          if (m < a.M && col < a.N) v = *reinterpret_cast<const float4*>(out_row_ptr(m) + col);
-          acc.c[i][j][4 * g4] = v.x;
-          acc.c[i][j][4 * g4 + 1] = v.y;
-          acc.c[i][j][4 * g4 + 2] = v.z;
-          acc.c[i][j][4 * g4 + 3] = v.w;
-        }
-  }
+        for (int j = 0; j < C::WNB; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int col = n0 + out_col<C>(j, g4);
+            const float* src = rowp[i] && col < a.N ? rowp[i] + col
+                                                    : reinterpret_cast<const float*>(g_zero);
+            const float4 v = *reinterpret_cast<const float4*>(src);
+            acc.c[i][j][4 * g4] = v.x;
+            acc.c[i][j][4 * g4 + 1] = v.y;
+            acc.c[i][j][4 * g4 + 2] = v.z;
+            acc.c[i][j][4 * g4 + 3] = v.w;
+          }
+    }
+  };
   MNMajor<BM, C::BK> la;
   la.ncols_left = a.M - m0;
   const bf16_t* Ab = a.A + (size_t)(off - lo) * a.lda + m0;
@@ -452,25 +469,27 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
     // last stage runs into the expert's zero padding
     static_assert(64 % C::BK == 0, "the transposed rows are padded to 64");
     KMajor<C::BN, C::BK> lb;
-    const bf16_t* Bt = a.win ? a.BT + (size_t)64 * s_tpw[e] + xcol
-                             : a.BT + (size_t)64 * s_tp[e] + (size_t)c * kWgChunk;
+    const bf16_t* Bt = WIN ? a.BT + (size_t)64 * s_tpw[e] + xcol
+                           : a.BT + (size_t)64 * s_tp[e] + (size_t)c * kWgChunk;
     lb.init([&](int nr) -> const bf16_t* {
       const int n = n0 + nr;
       return n < a.N ? Bt + (size_t)n * a.ldt : nullptr;
     });
+    preload();
     mainloop<C, true, false>((cnt + C::BK - 1) / C::BK, issue_a,
-                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc, keep);
+                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc, WIN);
   } else {
     MNMajor<C::BN, C::BK> lb;
     lb.ncols_left = a.N - n0;
     const bf16_t* Bb = a.B + (size_t)off * a.ldb + n0;
+    preload();
     mainloop<C, true, true>((cnt + C::BK - 1) / C::BK, issue_a,
                             [&](int kt, unsigned l) {
                               lb.issue(kt, l, [&](int kk) -> const bf16_t* {
                                 return kk < cnt ? Bb + (size_t)kk * a.ldb : nullptr;
                               });
                             },
-                            smem, acc, keep);
+                            smem, acc, WIN);
   }
   __syncthreads();
   const WaveStage<C, float> st(smem);
@@ -698,8 +717,11 @@ mok_status launch_bwd_wgrad(const BwdPlan& p, const void* x_perm, hipStream_t st
     hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(kThreads), 0, stream, p.offsets,
                        p.E_local, p.R_cap, p.wg_order);
   WgArgs w = wgrad_args(p, x_perm, 0);
-  hipLaunchKernelGGL((wgrad_g2<Default, 0>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
-                     dim3(kThreads), 0, stream, w);
+  const dim3 grid0((unsigned)(max_chunks * w.mtn * w.ntn));
+  if (p.win)
+    hipLaunchKernelGGL((wgrad_g2<Default, 0, true>), grid0, dim3(kThreads), 0, stream, w);
+  else
+    hipLaunchKernelGGL((wgrad_g2<Default, 0, false>), grid0, dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_gate_up", stream);
   if (reduce) {
     hipLaunchKernelGGL((wgrad_reduce<0>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream,
@@ -707,8 +729,11 @@ mok_status launch_bwd_wgrad(const BwdPlan& p, const void* x_perm, hipStream_t st
     trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
   }
   w = wgrad_args(p, x_perm, 1);
-  hipLaunchKernelGGL((wgrad_g2<Narrow, 1>), dim3((unsigned)(max_chunks * w.mtn * w.ntn)),
-                     dim3(kThreads), 0, stream, w);
+  const dim3 grid1((unsigned)(max_chunks * w.mtn * w.ntn));
+  if (p.win)
+    hipLaunchKernelGGL((wgrad_g2<Narrow, 1, true>), grid1, dim3(kThreads), 0, stream, w);
+  else
+    hipLaunchKernelGGL((wgrad_g2<Narrow, 1, false>), grid1, dim3(kThreads), 0, stream, w);
   trace_mark(p.tr, "bwd_wgrad_down", stream);
   if (reduce) {
     hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream,

@@ -1,14 +1,17 @@
 """Summaries of rocprofv3 output for the layer's kernels.
 
-``python -m combine_router_top_expert_amd.profiling OUT_DIR`` reads, from
-OUT_DIR (the folder the rocprofv3 runs below wrote to):
+``python -m combine_router_top_expert_amd.profiling OUT_DIR WORKLOAD PATH [BENCH ARGS...]``
+reads, from OUT_DIR (the folder the rocprofv3 runs below wrote to; BENCH ARGS
+are the bench.py arguments they were run with, e.g. ``--workload C3
+--ring-mib 256 --mb 1024 --comm-wgs 16``):
   kt/kt_kernel_stats.csv                  rocprofv3 --kernel-trace --stats of bench.py
   pf/pf_counter_collection.csv            rocprofv3 --pmc FETCH_SIZE of bench.py
   pw/pw_counter_collection.csv            rocprofv3 --pmc WRITE_SIZE of bench.py
   cf/cf_counter_collection.csv            rocprofv3 --pmc FETCH_SIZE of bench.py --hbm-copy-gib 1
   cw/cw_counter_collection.csv            rocprofv3 --pmc WRITE_SIZE of bench.py --hbm-copy-gib 1
-and writes ``profiles/c2_fwd_bwd_kernel_trace.md``, ``profiles/c2_hbm_traffic.md``
-and ``profiles/hbm_traffic.json``.
+and writes ``profiles/<workload>_<path>_kernel_trace.md``,
+``profiles/<workload>_<path>_hbm_traffic.md`` and that workload and path's
+record in ``profiles/hbm_traffic.json``.
 
 The byte counters are scaled by what they read for the plain 1 GiB device copy
 (``FETCH_SIZE`` and ``WRITE_SIZE`` are in KiB; the factor maps the copy's
@@ -43,7 +46,10 @@ TRACE_NAME = {
     "wgrad_reduce<0>": "bwd_wgrad_gate_up_reduce", "wgrad_reduce<1>": "bwd_wgrad_down_reduce",
     "dx_final_kernel": "bwd_dx_sum_router", "dwr_part_kernel": "bwd_dw_router_part",
     "dwr_reduce_kernel": "bwd_dw_router_reduce", "ring_kernel": "ring_fused_ffn",
-    "gather_t_kernel": "bwd_regather_x",
+    "gather_t_kernel": "bwd_regather_x", "rc_pull_rows_kernel": "bwd_reverse_combine_pull",
+    "tq_rows_kernel<0>": "bwd_transpose_quantise_mx", "tq_rows_kernel<1>": "bwd_transpose_quantise_mx",
+    "mx_dequant_kernel": "bwd_transpose_quantise_mx", "wgrad_mx_kernel<0>": "bwd_wgrad_gate_up_mx",
+    "wgrad_mx_kernel<1>": "bwd_wgrad_down_mx", "mx_quantize_kernel": "mx_quantize",
 }
 
 
@@ -88,7 +94,7 @@ def kernel_key(name: str) -> str:
         m = re.search(r"^(?:void\s+)?([\w:]+)", name)
         return m.group(1) if m else name
     key = m.group(1)
-    if key in ("wgrad_g2", "wgrad_reduce"):
+    if key in ("wgrad_g2", "wgrad_reduce", "wgrad_mx_kernel", "tq_rows_kernel"):
         t = re.search(r"(\d)>\(", name)
         key += "<%s>" % (t.group(1) if t else "?")
     return key
@@ -110,32 +116,52 @@ def copy_factor(path: str, expect_kib: float) -> float:
     return expect_kib / (sum(vals) / len(vals))
 
 
-def main(out_dir: str, workload: str = "C2", path: str = "staged"):
+WHAT = {
+    "C2": ("mid-size layer (forward + backward)",
+           "T=16384 tokens (8 x 2048), d=2048, E=64 all local, top-6, SwiGLU I=1408, bf16"),
+    "C3": ("one GPU's share of the 256-expert layer (forward through the ring + backward)",
+           "T=131072 tokens (32 x 4096), d=7168, E=256 with 8 local, top-8, SwiGLU I=2048, "
+           "bf16, Zipf 1.2 skew"),
+    "C4": ("mid-size layer in MXFP8 (forward; backward in MXFP8 beside it)",
+           "T=16384 tokens (8 x 2048), d=2048, E=64 all local, top-6, SwiGLU I=1408, MXFP8"),
+    "C5": ("mid-size layer with skewed routing (forward + backward)",
+           "T=16384 tokens (8 x 2048), d=2048, E=64 all local, top-6, SwiGLU I=1408, bf16, "
+           "Zipf 1.2 skew"),
+}
+
+
+def main(out_dir: str, workload: str = "C2", path: str = "staged", *bench_args: str):
     # the traffic record is written only from counter passes of this
     # folder (run post-processing before any source changes: the record
     # takes the kernels' current source hashes)
+    args = " ".join(bench_args) if bench_args else f"--workload {workload}"
     if os.path.exists(os.path.join(out_dir, "pf", "pf_counter_collection.csv")):
-        traffic_main(out_dir, workload, path)
-    trace_main(out_dir)
+        traffic_main(out_dir, workload, path, args)
+    trace_main(out_dir, workload, path, args)
 
 
-def traffic_main(out_dir: str, workload: str, path: str):
+def _stem(workload: str, path: str) -> str:
+    return f"{workload.lower()}_{path}"
+
+
+def traffic_main(out_dir: str, workload: str, path: str, args: str):
     fs = copy_factor(os.path.join(out_dir, "cf", "cf_counter_collection.csv"), 1 << 20)
     ws = copy_factor(os.path.join(out_dir, "cw", "cw_counter_collection.csv"), 1 << 20)
     fetch = counters(os.path.join(out_dir, "pf", "pf_counter_collection.csv"))
     write = counters(os.path.join(out_dir, "pw", "pw_counter_collection.csv"))
     traffic = {}
-    lines = ["# HBM traffic per launch, mid-size layer (forward + backward)", "",
+    title, shape = WHAT.get(workload, (workload, ""))
+    lines = [f"# HBM traffic per launch, {title}", "", shape + ".", "",
              "Byte counters from two rocprofv3 passes over one timed step of `bench.py`",
              "(`FETCH_SIZE`, then `WRITE_SIZE`, in KiB per dispatch), each scaled by what the",
              f"same counter reads for a plain 1 GiB device copy: FETCH_SIZE x {fs:.3f},",
              f"WRITE_SIZE x {ws:.3f}.  Values are for the last profiled launch of each kernel.", "",
              "Commands (from the repository root; OUT = the output folder):", "",
-             "    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pf -o pf -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
-             "    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pw -o pw -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             f"    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pf -o pf -- python3 bench.py {args} --steps 1 --warmup 1 --no-cpu-baseline",
+             f"    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pw -o pw -- python3 bench.py {args} --steps 1 --warmup 1 --no-cpu-baseline",
              "    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/cf -o cf -- python3 bench.py --hbm-copy-gib 1 --steps 3 --warmup 1",
              "    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/cw -o cw -- python3 bench.py --hbm-copy-gib 1 --steps 3 --warmup 1",
-             "    python3 -m combine_router_top_expert_amd.profiling OUT", "",
+             f"    python3 -m combine_router_top_expert_amd.profiling OUT {workload} {path} {args}", "",
              "| kernel | trace name | read MB | written MB | total MB |", "|---|---|---|---|---|"]
     for k, fv in fetch.items():
         name = TRACE_NAME.get(k)
@@ -147,30 +173,38 @@ def traffic_main(out_dir: str, workload: str, path: str):
                          "source_sha256": kernel_source_hash(k)}
         lines.append(f"| {k} | {name} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, "c2_hbm_traffic.md"), "w") as f:
+    with open(os.path.join(PROFILES, _stem(workload, path) + "_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
-        json.dump({"source_sha256": source_hash(), "workload": workload, "path": path,
-                   "fetch_factor": fs, "write_factor": ws, "kernels": traffic}, f, indent=1)
+    jf = os.path.join(PROFILES, "hbm_traffic.json")
+    rec = {}
+    if os.path.exists(jf):
+        with open(jf) as fh:
+            rec = json.load(fh)
+        if "records" not in rec:
+            rec = {}
+    rec.setdefault("records", {})[f"{workload}/{path}"] = {
+        "source_sha256": source_hash(), "bench_args": args, "fetch_factor": fs,
+        "write_factor": ws, "kernels": traffic}
+    with open(jf, "w") as f:
+        json.dump(rec, f, indent=1)
 
 
-def trace_main(out_dir: str):
+def trace_main(out_dir: str, workload: str, path: str, args: str):
     stats = os.path.join(out_dir, "kt", "kt_kernel_stats.csv")
     if os.path.exists(stats):
         rows = list(csv.DictReader(open(stats)))
-        t = ["# Kernel trace summary, mid-size layer (forward + backward)", "",
+        title, shape = WHAT.get(workload, (workload, ""))
+        t = [f"# Kernel trace summary, {title}", "",
              "Command (from the repository root):", "",
-             "    rocprofv3 --kernel-trace --stats -f csv -d OUT/kt -o kt -- python3 bench.py --steps 3 --warmup 2 --no-cpu-baseline",
-             "", "Seven steps of the mid-size layer (2 warm-up, 3 timed, 2 for the run-to-run identity",
-             "check, whose byte comparisons and host copies are the torch kernels below): T=16384",
-             "tokens (8 x 2048), d=2048, E=64 all local, top-6, SwiGLU I=1408, bf16; the backward's",
-             "side work runs on a second stream beside its GEMMs.", "",
+             f"    rocprofv3 --kernel-trace --stats -f csv -d OUT/kt -o kt -- python3 bench.py {args} --steps 3 --warmup 2 --no-cpu-baseline",
+             "", "Seven or more steps (2 warm-up, 3 timed, 2 for the run-to-run identity check, whose",
+             "byte comparisons and host copies are the torch kernels below) of: " + shape + ".", "",
              "| kernel | trace name | calls | average us | share % |", "|---|---|---|---|---|"]
         for r in rows:
             k = kernel_key(r["Name"])
             t.append(f"| {k} | {TRACE_NAME.get(k, '')} | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-        with open(os.path.join(PROFILES, "c2_fwd_bwd_kernel_trace.md"), "w") as f:
+        with open(os.path.join(PROFILES, _stem(workload, path) + "_kernel_trace.md"), "w") as f:
             f.write("\n".join(t) + "\n")
     print("written under", PROFILES)
 
@@ -240,8 +274,8 @@ def recorded_traffic(kernel: str, workload: str, path: str):
     if not os.path.exists(f):
         return None
     with open(f) as fh:
-        rec = json.load(fh)
-    if rec.get("workload") != workload or rec.get("path") != path:
+        rec = json.load(fh).get("records", {}).get(f"{workload}/{path}")
+    if rec is None:
         return None
     k = rec["kernels"].get(kernel)
     if k is None:

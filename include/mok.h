@@ -419,9 +419,10 @@ mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
 mok_status mok_ring_layout(const mok_config* cfg, size_t* offset, size_t* slot_bytes,
                            int32_t* nslot);
 
-/* HBM streaming probe: the bandwidth ceiling the layer's data-movement
- * kernels are measured against.  Moves `bytes` (a multiple of 16) with
- * 16-byte vector loads and stores, the access of those kernels.  mode 0:
+/* HBM streaming probe: a reference rate for the layer's data-movement
+ * kernels.  Moves `bytes` (a multiple of 16) with 16-byte vector loads and
+ * stores, the access of those kernels, from a persistent grid of a few
+ * workgroups per CU that walks 32 KiB chunks with a grid stride.  mode 0:
  * read src (dst must hold `bytes` too; a word is written there only in the
  * unlikely case that a lane's folded words equal a fixed pattern); 1: write
  * dst; 2: copy src to dst.  Pointers 16-byte aligned, device memory.

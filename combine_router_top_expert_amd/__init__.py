@@ -14,7 +14,9 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmok.so")
+# MOK_LIB: another build of the library to load instead (the host-sanitizer
+# build that the CPU tests run the argument checks through)
+LIB_PATH = os.environ.get("MOK_LIB") or os.path.join(HERE, "libmok.so")
 
 MOK_F32, MOK_BF16, MOK_MXFP8 = 0, 1, 2
 PREC = {"f32": MOK_F32, "bf16": MOK_BF16, "mxfp8": MOK_MXFP8}

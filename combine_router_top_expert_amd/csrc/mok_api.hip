@@ -737,7 +737,7 @@ mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
   hipStream_t sm = (hipStream_t)stream;
   hipEvent_t ev[2] = {nullptr, nullptr};
   if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
-    if (ev[0]) hipEventDestroy(ev[0]);
+    if (ev[0]) (void)hipEventDestroy(ev[0]);
     return MOK_EDEVICE;
   }
   mok_status result = MOK_EINVAL;  // until one candidate ran
@@ -787,8 +787,9 @@ mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,
       }
     }
 done:
-  hipEventDestroy(ev[0]);
-  hipEventDestroy(ev[1]);
+  // (a failed destroy leaves nothing the caller could act on; the result stands)
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
   return result;
 }
 

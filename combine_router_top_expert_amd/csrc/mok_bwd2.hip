@@ -759,8 +759,8 @@ mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream
                                  hipEvent_t before_wgrad, hipEvent_t after_dx) {
   mok_status rc = launch_bwd_dgrad(p, stream);
   if (rc != MOK_OK) return rc;
-  if (after_dx) hipEventRecord(after_dx, stream);
-  if (before_wgrad) hipStreamWaitEvent(stream, before_wgrad, 0);
+  if (after_dx) MOK_HIP_CHECK(hipEventRecord(after_dx, stream));
+  if (before_wgrad) MOK_HIP_CHECK(hipStreamWaitEvent(stream, before_wgrad, 0));
   return launch_bwd_wgrad(p, x_perm, stream, true, true);
 }
 

@@ -34,19 +34,30 @@ PREC = {"f32": F32, "bf16": BF16, "mxfp8": MXFP8, "exact": EXACT}
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle (single-threaded C; fmaf must be the hardware fused op)."""
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-mfma", "-ffp-contract=off", "-fPIC", "-shared",
-           "-o", tmp, SRC, "-lm"]
+def build(out: str = LIB, sanitize: bool = False) -> str:
+    """Compile the oracle (single-threaded C; fmaf must be the hardware fused op).
+    sanitize: an AddressSanitizer + UndefinedBehaviorSanitizer build (every
+    report fatal) for the host-side memory and UB check; it is loaded only
+    through MOK_ORACLE_LIB, with libasan preloaded into the process."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-mfma", "-ffp-contract=off", "-fPIC", "-shared"]
+    if sanitize:
+        cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=all"]
+    cmd += ["-o", tmp, SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def lib():
     global _lib
     if _lib is None:
+        alt = os.environ.get("MOK_ORACLE_LIB")
+        if alt:
+            _lib = ctypes.CDLL(alt)
+            _declare(_lib)
+            return _lib
         if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
             build()
         _lib = ctypes.CDLL(LIB)

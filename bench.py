@@ -86,12 +86,13 @@ def kernel_work(name, w, R, T_pull=None):
         "bwd_reverse_combine_pull": (T_pull + 2.0 * R) * d * eb,
         "bwd_swiglu": 5.0 * R * I * eb,                   # read dh, a, b; write da, db
         "bwd_dx_sum_router": (T * k * d + T * d) * eb,    # read k dx rows, write dX
-        # MX quantisation: read bf16, write E4M3 codes + one scale byte per 32
-        "bwd_quantise_dy_mx": R * d * (2 + 33 / 32),
-        "bwd_quantise_dab_mx": R * 2 * I * (2 + 33 / 32),
-        # h's codes to bf16, then [da|db], the token rows, dy and h transposed
-        # and quantised along the rows
-        "bwd_transpose_quantise_mx": R * (I + 2 * I + d + d + I) * (2 + 33 / 32),
+        # MX packs (E4M3 codes + one scale byte per 32 = 33/32 bytes a value):
+        # dy read once, quantised along d and along the rows
+        "bwd_pack_dy_mx": R * d * (2 + 2 * 33 / 32),
+        # dh, a, b read; da | db quantised along 2I and along the rows
+        "bwd_swiglu_pack_mx": R * I * (3 * 2 + 2 * 2 * 33 / 32),
+        # h's codes read and re-quantised along the rows; token rows likewise
+        "bwd_pack_h_x_mx": R * I * 2 * 33 / 32 + R * d * (2 + 33 / 32),
     }
     if name in moves:
         return "hbm", moves[name]

@@ -39,7 +39,7 @@ bool valid_cfg(const mok_config* c) {
 struct Ws {
   size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
       r_row_src, r_dest_row, r_scratch, bx, wpart, wpart_down, worder, bwin, bring, mx_dyq,
-      mx_dys, mx_dabq, mx_dabs, mx_hdeq, mx_dabT, mx_dabTs, mx_xT, mx_xTs, mx_dyT, mx_dyTs, mx_hT,
+      mx_dys, mx_dabq, mx_dabs, mx_dabT, mx_dabTs, mx_xT, mx_xTs, mx_dyT, mx_dyTs, mx_hT,
       mx_hTs, total;
 };
 
@@ -112,19 +112,19 @@ Ws ws_layout(const mok_config* c) {
   b += align256((size_t)(4 + c->E_local) * sizeof(int32_t));
   w.bring = b;
   if (bring) b += align256((size_t)c->bwd_ring_bytes);
-  // MXFP8 backward: the quantised rows of dy and da | db, h dequantised, and
-  // the weight gradients' operands transposed (every expert's rows padded to
-  // 128 columns), each E4M3 codes + E8M0 scales per 32
+  // MXFP8 backward: the quantised rows of dy and da | db and the weight
+  // gradients' operands transposed (every expert's rows padded to 128
+  // columns), each E4M3 codes + E8M0 scales per 32
   const bool mx = c->prec == MOK_MXFP8;
   const size_t cols = mx ? (size_t)bwd_mx_cols(c->R_cap, c->E_local) : 0;
   const size_t d = (size_t)c->d, I2 = 2 * (size_t)c->I;
-  size_t* const regions[13] = {&w.mx_dyq, &w.mx_dys, &w.mx_dabq, &w.mx_dabs, &w.mx_hdeq,
+  size_t* const regions[12] = {&w.mx_dyq, &w.mx_dys, &w.mx_dabq, &w.mx_dabs,
                                &w.mx_dabT, &w.mx_dabTs, &w.mx_xT, &w.mx_xTs, &w.mx_dyT,
                                &w.mx_dyTs, &w.mx_hT, &w.mx_hTs};
-  const size_t bytes[13] = {R * d, R * d / 32, R * I2, R * I2 / 32, R * I2,
+  const size_t bytes[12] = {R * d, R * d / 32, R * I2, R * I2 / 32,
                             I2 * cols, I2 * cols / 32, d * cols, d * cols / 32, d * cols,
                             d * cols / 32, I2 / 2 * cols, I2 / 2 * cols / 32};
-  for (int i = 0; i < 13; ++i) {
+  for (int i = 0; i < 12; ++i) {
     *regions[i] = b;
     if (mx) b += align256(bytes[i]);
   }
@@ -671,7 +671,6 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
     p.mx_dys = (uint8_t*)(wsb + wl.mx_dys);
     p.mx_dabq = (uint8_t*)(wsb + wl.mx_dabq);
     p.mx_dabs = (uint8_t*)(wsb + wl.mx_dabs);
-    p.mx_hdeq = wsb + wl.mx_hdeq;
     p.mx_cols = bwd_mx_cols(cfg->R_cap, cfg->E_local);
     p.mx_dabT = (uint8_t*)(wsb + wl.mx_dabT);
     p.mx_dabTs = (uint8_t*)(wsb + wl.mx_dabTs);

@@ -7,11 +7,15 @@
 //   dW_gate|up = [da|db]^T X, dW_down = dy^T h: both operands transposed,
 //                           each column quantised along the expert's rows in
 //                           blocks of 32 (the expert's rows padded to 128)
-// The transposed weights are prepared once (mok_mx_prepare_bwd); the
-// transposed activations are written by one kernel that stages a block of
-// 128 rows x 64 channels through LDS and quantises each channel's 32-row
-// blocks.  The weight gradients contract over a whole expert per output
-// tile (a fixed order; the results are run-to-run identical).
+// The transposed weights are prepared once (mok_mx_prepare_bwd).  The
+// activations are packed by one kernel per operand that stages 128 rows (one
+// MX stage of an expert's rows) x 64 channels through LDS and writes both
+// quantisations from that one copy: along the row (32 channels a block, for
+// dh and dx) and along the rows (32 rows a block, transposed, for the weight
+// gradients).  The SwiGLU backward runs inside the [da|db] pack, and h's
+// codes are decoded inside its pack, so no bf16 [da|db] or h is written.
+// The weight gradients contract over a whole expert per output tile (a fixed
+// order; the results are run-to-run identical).
 #include <string.h>
 
 #include "mok_gemm_mx.h"
@@ -67,41 +71,240 @@ __device__ __forceinline__ void tq_block(RowPtr rowp, uint8_t* codes, uint8_t* s
   scales[(size_t)ch * (ldc / 32) + (col0 / 32) + blk] = (uint8_t)(sh + 127);
 }
 
-// Activations: the rows of every local expert, 128-row tiles of the grouped
-// layout (tile t of the layout is column block t of the output); rows past
-// an expert's end are zeros.  KIND 0: bf16 rows src + r * ld; KIND 1: the
-// token rows of the items, from the source buffers through row_src.
-struct TqArgs {
-  const bf16_t* src;
-  int64_t ld;
-  SrcTable tok;
+// ---------------------------------------------------------------- packs
+// One tile of 128 rows x 64 channels in LDS, bf16.  Row r's elements sit at
+// r * kPitch + (r / 32) * 8 + c: the 32-row blocks are shifted against each
+// other by 16 bytes, so the lanes of a column read (4 blocks of one channel)
+// fall in different banks, and 16-byte row chunks stay aligned.
+constexpr int kPitch = kTqCh + 8;
+constexpr int kTileElems = kTqRows * kPitch + 32;
+__device__ __forceinline__ int tix(int r, int c) { return r * kPitch + (r >> 5) * 8 + c; }
+
+// Both quantisations read the LDS tile twice (the block's largest
+// magnitude, then the codes) rather than hold 32 values in registers: the
+// packs are HBM-bound, and the registers saved let twice the workgroups
+// overlap their loads with each other's quantisation.
+
+// 8 bf16 of a 16-byte LDS chunk as floats.
+__device__ __forceinline__ void unpack8(uint4 u, float* v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+
+// Quantise tile rows [0, nrows) along the row: row r's two 32-channel blocks
+// -> codes[(r0 + r) ldq + ch0 + ..], scales[(r0 + r) ldq / 32 + ch0 / 32 + ..].
+__device__ __forceinline__ void pack_rows(const bf16_t* t, int nrows, uint8_t* codes,
+                                          uint8_t* scales, int64_t ldq, int64_t r0, int ch0) {
+  const int r = threadIdx.x >> 1, blk = threadIdx.x & 1;
+  if (r >= nrows) return;
+  const bf16_t* row = t + tix(r, blk * 32);
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(row + q * 8), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  const int sh = mx_shared_exp(amax);
+  uint32_t wq[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(row + q * 8), v);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        word |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 * h + e], -sh)) << (8 * e);
+      wq[2 * q + h] = word;
+    }
+  }
+  uint8_t* out = codes + (r0 + r) * ldq + ch0 + blk * 32;
+  *reinterpret_cast<uint4*>(out) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+  *reinterpret_cast<uint4*>(out + 16) = make_uint4(wq[4], wq[5], wq[6], wq[7]);
+  scales[(r0 + r) * (ldq / 32) + ch0 / 32 + blk] = (uint8_t)(sh + 127);
+}
+
+// Quantise the tile's channels along its 128 rows (rows past the expert's
+// end are zeros): codes[(ch0 + ch) ldc + col0 + ..] and the scales of its four
+// 32-row blocks.  Four consecutive lanes write one channel's 128 codes.
+__device__ __forceinline__ void pack_cols(const bf16_t* t, uint8_t* codes, uint8_t* scales,
+                                          int64_t ldc, int64_t col0, int ch0) {
+  const int ch = threadIdx.x >> 2, blk = threadIdx.x & 3;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(t[tix(blk * 32 + i, ch)])));
+  const int sh = mx_shared_exp(amax);
+  uint32_t wq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      word |= e4m3_code(__builtin_amdgcn_ldexpf(bf16_to_f32(t[tix(blk * 32 + 4 * q + e, ch)]), -sh))
+              << (8 * e);
+    wq[q] = word;
+  }
+  uint8_t* out = codes + (int64_t)(ch0 + ch) * ldc + col0 + blk * 32;
+  *reinterpret_cast<uint4*>(out) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+  *reinterpret_cast<uint4*>(out + 16) = make_uint4(wq[4], wq[5], wq[6], wq[7]);
+  scales[(int64_t)(ch0 + ch) * (ldc / 32) + col0 / 32 + blk] = (uint8_t)(sh + 127);
+}
+
+// What a pack reads and writes.  KIND 0: dy rows (bf16 [R_cap, ld]) -> both
+// quantisations.  KIND 1: the SwiGLU backward of the tile's 64 columns of I
+// from dh (bf16 [R_cap, ld]) and the saved a | b: da -> channels ch0, db ->
+// channels I + ch0, both quantisations of each.  KIND 2: h's E4M3 codes and
+// scales decoded (exact in bf16) -> the transposed quantisation only.
+// KIND 3: the token rows of the items, from the sources through row_src ->
+// the transposed quantisation only.
+struct PackArgs {
+  const bf16_t* src;       // KIND 0: dy; 1: dh
+  int64_t ld;              // leading dimension of src (elements)
+  const bf16_t* ab;        // KIND 1: [R_cap, 2I]
+  const uint8_t* hq;       // KIND 2: [R_cap, I] codes
+  const uint8_t* hs;       // KIND 2: [R_cap, I / 32] scales
+  SrcTable tok;            // KIND 3
   const int32_t* row_src;
   const int32_t* offsets;
-  uint8_t* codes;      // [channels, ldc]
-  uint8_t* scales;     // [channels, ldc / 32]
+  uint8_t *rq, *rs;        // along the row: codes [R_cap, ldq], scales
+  int64_t ldq;
+  uint8_t *cq, *cs;        // transposed: codes [channels, ldc], scales
   int64_t ldc;
-  int E_local, R_cap, T_src, k;
+  int E_local, R_cap, T_src, k, I;
+};
+
+__device__ __forceinline__ void swiglu_bwd8(const uint4 hv, const uint4 av, const uint4 bv,
+                                            uint4* da_out, uint4* db_out) {
+  const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, aw[4] = {av.x, av.y, av.z, av.w},
+                 bw[4] = {bv.x, bv.y, bv.z, bv.w};
+  float da[8], db[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    const float dh = __uint_as_float(e & 1 ? hw[w] & 0xFFFF0000u : hw[w] << 16);
+    const float x = __uint_as_float(e & 1 ? aw[w] & 0xFFFF0000u : aw[w] << 16);
+    const float y = __uint_as_float(e & 1 ? bw[w] & 0xFFFF0000u : bw[w] << 16);
+    const float sg = sigmoid_f(x);
+    da[e] = dh * y * sg * (1.0f + x * (1.0f - sg));
+    db[e] = dh * x * sg;
+  }
+  const uint2 d0 = pack4_bf16(da[0], da[1], da[2], da[3]), d1 = pack4_bf16(da[4], da[5], da[6], da[7]);
+  const uint2 e0 = pack4_bf16(db[0], db[1], db[2], db[3]), e1 = pack4_bf16(db[4], db[5], db[6], db[7]);
+  *da_out = make_uint4(d0.x, d0.y, d1.x, d1.y);
+  *db_out = make_uint4(e0.x, e0.y, e1.x, e1.y);
+}
+
+// One E4M3 code times 2^sh, as bf16 (exact: 4 significant bits).
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c, int sh) {
+  const uint32_t mag = c & 0x7Fu, ex = mag >> 3, man = mag & 7u;
+  float v = ex ? __builtin_amdgcn_ldexpf((float)(8u + man), (int)ex - 10)
+               : __builtin_amdgcn_ldexpf((float)man, -9);
+  v = __builtin_amdgcn_ldexpf(v, sh);
+  return f32_to_bf16((c & 0x80u) ? -v : v);
+}
+
+// A tile's raw loads, one 16-byte chunk per thread and pass (KIND 1: dh, a,
+// b; KIND 2: 8 codes and their scale).  Issued for the next tile before the
+// current one is quantised, so the loads are in flight during that work.
+struct PackRaw {
+  uint4 v[4][3];
+  int sh[4];
 };
 
 template <int KIND>
-__global__ __launch_bounds__(kThreads) void tq_rows_kernel(TqArgs a) {
+__device__ __forceinline__ void pack_fetch(const PackArgs& a, const GTile& g, int ch0,
+                                           PackRaw& raw) {
+  const int nrows = g.r1 - g.r0, cc = threadIdx.x % 8;
+#pragma unroll
+  for (int pass = 0; pass < kTqRows / 32; ++pass) {
+    const int row = pass * 32 + threadIdx.x / 8;
+    const int r = g.r0 + row;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    raw.v[pass][0] = raw.v[pass][1] = raw.v[pass][2] = z;
+    raw.sh[pass] = 0;
+    if (row >= nrows) continue;
+    if (KIND == 0) {
+      raw.v[pass][0] = ld16(a.src + (size_t)r * a.ld + ch0 + cc * 8);
+    } else if (KIND == 1) {
+      const bf16_t* abr = a.ab + (size_t)r * 2 * a.I + ch0 + cc * 8;
+      raw.v[pass][0] = ld16(a.src + (size_t)r * a.ld + ch0 + cc * 8);
+      raw.v[pass][1] = ld16(abr);
+      raw.v[pass][2] = ld16(abr + a.I);
+    } else if (KIND == 2) {
+      const uint2 c8 = *reinterpret_cast<const uint2*>(a.hq + (size_t)r * a.I + ch0 + cc * 8);
+      raw.v[pass][0] = make_uint4(c8.x, c8.y, 0, 0);
+      raw.sh[pass] = (int)a.hs[(size_t)r * (a.I / 32) + (ch0 + cc * 8) / 32] - 127;
+    } else {
+      const int tok = a.row_src[r] / a.k;
+      raw.v[pass][0] = ld16(reinterpret_cast<const bf16_t*>(a.tok.p[tok / a.T_src]) +
+                            (size_t)(tok % a.T_src) * a.ld + ch0 + cc * 8);
+    }
+  }
+}
+
+// The raw loads -> the LDS tile(s) (KIND 1: the SwiGLU backward here; rows
+// past the expert's end hold zeros either way).
+template <int KIND>
+__device__ __forceinline__ void pack_stash(const PackRaw& raw, const GTile& g, bf16_t* t0,
+                                           bf16_t* t1) {
+  const int nrows = g.r1 - g.r0, cc = threadIdx.x % 8;
+#pragma unroll
+  for (int pass = 0; pass < kTqRows / 32; ++pass) {
+    const int row = pass * 32 + threadIdx.x / 8;
+    uint4 v0 = raw.v[pass][0], v1 = make_uint4(0, 0, 0, 0);
+    if (KIND == 1 && row < nrows) swiglu_bwd8(raw.v[pass][0], raw.v[pass][1], raw.v[pass][2], &v0, &v1);
+    if (KIND == 2) {
+      const uint32_t cw[2] = {v0.x, v0.y};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = e4m3_to_bf16_bits((cw[q >> 1] >> (16 * (q & 1))) & 0xFFu, raw.sh[pass]);
+        const uint32_t hi = e4m3_to_bf16_bits((cw[q >> 1] >> (16 * (q & 1) + 8)) & 0xFFu, raw.sh[pass]);
+        o[q] = lo | (hi << 16);
+      }
+      v0 = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    *reinterpret_cast<uint4*>(t0 + tix(row, cc * 8)) = v0;
+    if (KIND == 1) *reinterpret_cast<uint4*>(t1 + tix(row, cc * 8)) = v1;
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void mx_pack_kernel(PackArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[KIND == 1 ? 2 : 1][kTileElems];
   __shared__ int s_prefix[257];
   const int total = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix, kTqRows);
   const int ch0 = blockIdx.y * kTqCh;
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
-    const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, t, kTqRows);
-    tq_block(
-        [&](int row) -> const bf16_t* {
-          const int r = g.r0 + row;
-          if (r >= g.r1) return nullptr;
-          if (KIND == 0) return a.src + (size_t)r * a.ld + ch0;
-          const int tok = a.row_src[r] / a.k;
-          return reinterpret_cast<const bf16_t*>(a.tok.p[tok / a.T_src]) +
-                 (size_t)(tok % a.T_src) * a.ld + ch0;
-        },
-        a.codes + (size_t)ch0 * a.ldc, a.scales + (size_t)ch0 * (a.ldc / 32), a.ldc,
-        (int64_t)t * kTqRows);
-    __syncthreads();  // the tile is read before the next block's loads overwrite it
+  int t = blockIdx.x;
+  if (t >= total) return;
+  GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, t, kTqRows);
+  PackRaw raw;
+  pack_fetch<KIND>(a, g, ch0, raw);
+  for (; t < total; t += gridDim.x) {
+    const GTile cur = g;
+    pack_stash<KIND>(raw, cur, tile[0], tile[KIND == 1 ? 1 : 0]);
+    __syncthreads();
+    const int tn = t + gridDim.x;
+    if (tn < total) {
+      g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, tn, kTqRows);
+      pack_fetch<KIND>(a, g, ch0, raw);
+    }
+    const int nrows = cur.r1 - cur.r0;
+    const int64_t col0 = (int64_t)t * kTqRows;
+#pragma unroll
+    for (int h = 0; h < (KIND == 1 ? 2 : 1); ++h) {
+      const int ch = ch0 + h * a.I;  // KIND 1: da at ch0, db at I + ch0
+      if (KIND <= 1) pack_rows(tile[h], nrows, a.rq, a.rs, a.ldq, cur.r0, ch);
+      pack_cols(tile[h], a.cq, a.cs, a.ldc, col0, ch);
+    }
+    __syncthreads();  // the tile is read before the next one is stored over it
   }
 }
 
@@ -129,22 +332,6 @@ __global__ __launch_bounds__(kThreads) void tq_weights_kernel(TqWArgs a) {
       },
       a.codes + (size_t)e * a.N * K + (size_t)ch0 * K,
       a.scales + (size_t)e * a.N * (K / 32) + (size_t)ch0 * (K / 32), K, k0);
-}
-
-// h as GEMM2 used it: E4M3 codes and their scales -> bf16 (exact: three
-// mantissa bits and an E8M0 exponent fit bf16).
-__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* codes,
-                                                              const uint8_t* scales, bf16_t* out,
-                                                              int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
-  const uint32_t c = codes[i];
-  const int sh = (int)scales[i / 32] - 127;
-  const uint32_t mag = c & 0x7Fu, ex = mag >> 3, man = mag & 7u;
-  float v = ex ? __builtin_amdgcn_ldexpf((float)(8u + man), (int)ex - 10)
-               : __builtin_amdgcn_ldexpf((float)man, -9);
-  v = __builtin_amdgcn_ldexpf(v, sh);
-  out[i] = f32_to_bf16((c & 0x80u) ? -v : v);
 }
 
 // Weight gradient of one local expert's output tile, contraction over its
@@ -258,30 +445,31 @@ mok_status launch_mx_prepare_bwd(int E_local, int d, int I, const void* w_gate, 
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
-static mok_status launch_tq(const BwdPlan& p, int kind, const void* src, int64_t ld, int channels,
-                            uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  TqArgs a;
+template <int KIND>
+static mok_status launch_pack(const BwdPlan& p, const PackArgs& a, int channels,
+                              hipStream_t stream) {
+  // about four tiles per workgroup, so each one's loads overlap the
+  // quantisation of the one before
+  const int tiles = (int)(p.mx_cols / kTqRows);
+  const int gx = tiles / 4 > 0 ? tiles / 4 : 1;
+  hipLaunchKernelGGL(mx_pack_kernel<KIND>, dim3((unsigned)gx, (unsigned)(channels / kTqCh)),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+static PackArgs pack_args(const BwdPlan& p) {
+  PackArgs a;
   memset(&a, 0, sizeof(a));
-  a.src = reinterpret_cast<const bf16_t*>(src);
-  a.ld = ld;
   a.tok = p.src_x;
   a.row_src = p.row_src;
   a.offsets = p.offsets;
-  a.codes = codes;
-  a.scales = scales;
   a.ldc = p.mx_cols;
   a.E_local = p.E_local;
   a.R_cap = p.R_cap;
   a.T_src = p.T_src;
   a.k = p.k;
-  const int tiles = (int)(p.mx_cols / kTqRows);
-  const int gx = tiles < 512 ? tiles : 512;
-  dim3 g((unsigned)gx, (unsigned)(channels / kTqCh));
-  if (kind == 0)
-    hipLaunchKernelGGL(tq_rows_kernel<0>, g, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(tq_rows_kernel<1>, g, dim3(kThreads), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+  a.I = p.I;
+  return a;
 }
 
 // [dW_gate; dW_up] = MX([da|db]^T) MX(X^T) and dW_down = MX(dy^T) MX(h^T),
@@ -329,34 +517,53 @@ mok_status launch_bwd_mx_gemms(const BwdPlan& p, hipStream_t stream) {
   // (no rows: every expert's tile contracts over nothing and stores zeros)
   if (p.R_cap == 0) return launch_bwd_mx_wgrad(p, stream);
   const int d = p.d, I = p.I;
-  // dh = dy W_down: dy quantised along d, into the first half of each dab row
-  mok_status rc = launch_mx_quantize(p.R_cap, d, p.dy, p.mx_dyq, p.mx_dys, stream);
+  // dy: along d for dh, along the rows for dW_down
+  PackArgs a = pack_args(p);
+  a.src = reinterpret_cast<const bf16_t*>(p.dy);
+  a.ld = d;
+  a.rq = p.mx_dyq;
+  a.rs = p.mx_dys;
+  a.ldq = d;
+  a.cq = p.mx_dyT;
+  a.cs = p.mx_dyTs;
+  mok_status rc = launch_pack<0>(p, a, d, stream);
   if (rc != MOK_OK) return rc;
-  trace_mark(p.tr, "bwd_quantise_dy_mx", stream);
+  trace_mark(p.tr, "bwd_pack_dy_mx", stream);
+  // dh = dy W_down -> bf16 [R_cap, I] (the first R_cap I elements of dab)
   rc = launch_mx_rows_gemm(p.mx_dyq, p.mx_dys, p.mx_wt_down, p.mx_st_down, d, I, p.E_local,
-                           p.R_cap, p.offsets, p.row_src, p.dab, 2 * I, nullptr, p.T_src, p.k,
+                           p.R_cap, p.offsets, p.row_src, p.dab, I, nullptr, p.T_src, p.k,
                            stream, p.tr, "bwd_dh_mx");
   if (rc != MOK_OK) return rc;
-  rc = launch_swiglu_bwd(p, stream);
-  if (rc != MOK_OK) return rc;
-  // dx = [da|db] [W_gate; W_up]: quantised along 2I, pushed to the dx rows
-  rc = launch_mx_quantize(p.R_cap, 2 * I, p.dab, p.mx_dabq, p.mx_dabs, stream);
-  if (rc != MOK_OK) return rc;
-  trace_mark(p.tr, "bwd_quantise_dab_mx", stream);
+  // the SwiGLU backward -> [da|db] along 2I for dx, along the rows for dW
+  a = pack_args(p);
+  a.src = reinterpret_cast<const bf16_t*>(p.dab);
+  a.ld = I;
+  a.ab = reinterpret_cast<const bf16_t*>(p.ab);
+  a.rq = p.mx_dabq;
+  a.rs = p.mx_dabs;
+  a.ldq = 2 * I;
+  a.cq = p.mx_dabT;
+  a.cs = p.mx_dabTs;
+  if ((rc = launch_pack<1>(p, a, I, stream)) != MOK_OK) return rc;
+  trace_mark(p.tr, "bwd_swiglu_pack_mx", stream);
+  // dx = [da|db] [W_gate; W_up], pushed to the dx rows
   rc = launch_mx_rows_gemm(p.mx_dabq, p.mx_dabs, p.mx_wt_gu, p.mx_st_gu, 2 * I, d, p.E_local,
                            p.R_cap, p.offsets, p.row_src, nullptr, 0, &p.dx_stage, p.T_src, p.k,
                            stream, p.tr, "bwd_dx_push_mx");
   if (rc != MOK_OK) return rc;
-  // the weight gradients' operands, transposed and quantised along the rows
-  const int64_t nh = (int64_t)p.R_cap * I;
-  hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)((nh + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, reinterpret_cast<const uint8_t*>(p.h), p.mx_hs,
-                     reinterpret_cast<bf16_t*>(p.mx_hdeq), nh);
-  if ((rc = launch_tq(p, 0, p.dab, 2 * I, 2 * I, p.mx_dabT, p.mx_dabTs, stream)) != MOK_OK) return rc;
-  if ((rc = launch_tq(p, 1, nullptr, d, d, p.mx_xT, p.mx_xTs, stream)) != MOK_OK) return rc;
-  if ((rc = launch_tq(p, 0, p.dy, d, d, p.mx_dyT, p.mx_dyTs, stream)) != MOK_OK) return rc;
-  if ((rc = launch_tq(p, 0, p.mx_hdeq, I, I, p.mx_hT, p.mx_hTs, stream)) != MOK_OK) return rc;
-  trace_mark(p.tr, "bwd_transpose_quantise_mx", stream);
+  // h (as GEMM2 read it) and the token rows, along the rows
+  a = pack_args(p);
+  a.hq = reinterpret_cast<const uint8_t*>(p.h);
+  a.hs = p.mx_hs;
+  a.cq = p.mx_hT;
+  a.cs = p.mx_hTs;
+  if ((rc = launch_pack<2>(p, a, I, stream)) != MOK_OK) return rc;
+  a = pack_args(p);
+  a.ld = d;
+  a.cq = p.mx_xT;
+  a.cs = p.mx_xTs;
+  if ((rc = launch_pack<3>(p, a, d, stream)) != MOK_OK) return rc;
+  trace_mark(p.tr, "bwd_pack_h_x_mx", stream);
   return launch_bwd_mx_wgrad(p, stream);
 }
 

@@ -152,7 +152,6 @@ struct BwdPlan {
   const uint8_t *mx_wt_gu, *mx_st_gu;       // [E_local, d, 2I], [.., 2I/32]
   uint8_t *mx_dyq, *mx_dys;                 // dy rows along d
   uint8_t *mx_dabq, *mx_dabs;               // [da|db] rows along 2I
-  void* mx_hdeq;                            // [R_cap, I] bf16: h as GEMM2 read it
   int64_t mx_cols;                          // columns of the transposed operands
   uint8_t *mx_dabT, *mx_dabTs, *mx_xT, *mx_xTs, *mx_dyT, *mx_dyTs, *mx_hT, *mx_hTs;
   mok_trace* tr;    // host-side trace, may be null

@@ -47,8 +47,9 @@ TRACE_NAME = {
     "dx_final_kernel": "bwd_dx_sum_router", "dwr_part_kernel": "bwd_dw_router_part",
     "dwr_reduce_kernel": "bwd_dw_router_reduce", "ring_kernel": "ring_fused_ffn",
     "gather_t_kernel": "bwd_regather_x", "rc_pull_rows_kernel": "bwd_reverse_combine_pull",
-    "tq_rows_kernel<0>": "bwd_transpose_quantise_mx", "tq_rows_kernel<1>": "bwd_transpose_quantise_mx",
-    "mx_dequant_kernel": "bwd_transpose_quantise_mx", "wgrad_mx_kernel<0>": "bwd_wgrad_gate_up_mx",
+    "mx_pack_kernel<0>": "bwd_pack_dy_mx", "mx_pack_kernel<1>": "bwd_swiglu_pack_mx",
+    "mx_pack_kernel<2>": "bwd_pack_h_x_mx", "mx_pack_kernel<3>": "bwd_pack_h_x_mx",
+    "wgrad_mx_kernel<0>": "bwd_wgrad_gate_up_mx",
     "wgrad_mx_kernel<1>": "bwd_wgrad_down_mx", "mx_quantize_kernel": "mx_quantize",
 }
 
@@ -94,7 +95,7 @@ def kernel_key(name: str) -> str:
         m = re.search(r"^(?:void\s+)?([\w:]+)", name)
         return m.group(1) if m else name
     key = m.group(1)
-    if key in ("wgrad_g2", "wgrad_reduce", "wgrad_mx_kernel", "tq_rows_kernel"):
+    if key in ("wgrad_g2", "wgrad_reduce", "wgrad_mx_kernel", "mx_pack_kernel"):
         t = re.search(r"(\d)>\(", name)
         key += "<%s>" % (t.group(1) if t else "?")
     return key

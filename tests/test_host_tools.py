@@ -47,6 +47,6 @@ def test_bench_work_model_covers_the_traced_kernels():
     for n in ("ffn1_gate_up_swiglu", "ffn2_down", "bwd_dh", "bwd_dx_push", "bwd_wgrad_gate_up",
               "bwd_wgrad_down", "combine", "bwd_reverse_combine_pull", "bwd_swiglu",
               "bwd_regather_x", "bwd_dx_sum_router", "route", "bwd_dh_mx", "bwd_dx_push_mx",
-              "bwd_wgrad_gate_up_mx", "bwd_wgrad_down_mx", "bwd_quantise_dy_mx",
-              "bwd_quantise_dab_mx", "bwd_transpose_quantise_mx"):
+              "bwd_wgrad_gate_up_mx", "bwd_wgrad_down_mx", "bwd_pack_dy_mx",
+              "bwd_swiglu_pack_mx", "bwd_pack_h_x_mx"):
         assert n in traced and n in modeled, n

@@ -402,7 +402,8 @@ def run_workload(args, name, np, torch):
         L = MoELayer(w.S, w.T_src, w.d, w.E, w.k, w.I, w.E_local, w.prec, R_cap, w.own[0],
                      len(w.own), device=dev, with_bwd=has_bwd, ring_bytes=args.ring_mib << 20,
                      minibatch_rows=mb, comm_wgs=args.comm_wgs, gemm_wgs=args.gemm_wgs,
-                     bwd_ring_bytes=(args.bwd_ring_mib << 20) if has_bwd else 0)
+                     bwd_ring_bytes=(args.bwd_ring_mib << 20) if has_bwd else 0,
+                     two_streams=args.bwd_streams == 2)
         L.set_inputs(dev_in["xs"], dev_in["wr"], dev_in["bias"], dev_in["e2l"], dev_in["wg"],
                      dev_in["wu"], dev_in["wd"], other_topk=other)
         return L
@@ -577,6 +578,8 @@ def main():
                     help="forward through the persistent ring kernel with a ring of this many "
                          "MiB (0 = one launch per step)")
     ap.add_argument("--mb", type=int, default=256, help="ring path: rows per minibatch")
+    ap.add_argument("--bwd-streams", type=int, choices=[1, 2], default=2,
+                    help="bf16 backward: side work on a second stream (2) or all on one (1)")
     ap.add_argument("--bwd-ring-mib", type=int, default=0,
                     help="backward through a ring of this many MiB (windows of whole "
                          "minibatches; 0 = one launch per step over all rows)")

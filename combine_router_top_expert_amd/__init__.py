@@ -31,7 +31,7 @@ STATUS = {
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
            "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_layer_fwd_macro",
-           "mok_mx_prepare_bwd", "mok_version")
+           "mok_prepare_bwd", "mok_version")
 
 
 class MokError(RuntimeError):
@@ -236,7 +236,7 @@ def lib():
                                             ctypes.POINTER(mok_fwd_state), P, P, P, P]
         L.mok_layer_fwd_macro.argtypes = [cfgp, I32, ctypes.POINTER(mok_layer_call), P, P, P,
                                           ctypes.POINTER(mok_expert_weights), P, P, P]
-        L.mok_mx_prepare_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P]
+        L.mok_prepare_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -390,8 +390,8 @@ def mok_mx_quantize(rows, K, src, codes, scales, stream=None):
                                                     _stream(stream)))
 
 
-def mok_mx_prepare_bwd(cfg, w_gate, w_up, w_down, wt_down, st_down, wt_gu, st_gu, stream=None):
-    _check("mok_mx_prepare_bwd", lib().mok_mx_prepare_bwd(
+def mok_prepare_bwd(cfg, w_gate, w_up, w_down, wt_down, st_down, wt_gu, st_gu, stream=None):
+    _check("mok_prepare_bwd", lib().mok_prepare_bwd(
         ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wt_down), _ptr(st_down),
         _ptr(wt_gu), _ptr(st_gu), _stream(stream)))
 

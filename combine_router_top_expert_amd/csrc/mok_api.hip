@@ -613,6 +613,12 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.wg = w->w_gate;
   p.wu = w->w_up;
   p.wd = w->w_down;
+  // transposed weights: required by MXFP8, optional for bf16 (both or none)
+  if (cfg->prec == MOK_BF16 && (!w->wt_down) != (!w->wt_gu)) return MOK_EINVAL;
+  if (cfg->prec != MOK_F32) {
+    p.wt_down = w->wt_down;
+    p.wt_gu = w->wt_gu;
+  }
   p.topk_idx = st->topk_idx;
   p.topk_gate = st->topk_gate;
   p.offsets = st->offsets;
@@ -663,9 +669,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   }
   if (mx) {
     p.mx_hs = st->h_scale;
-    p.mx_wt_down = w->wt_down;
     p.mx_st_down = w->st_down;
-    p.mx_wt_gu = w->wt_gu;
     p.mx_st_gu = w->st_gu;
     p.mx_dyq = (uint8_t*)(wsb + wl.mx_dyq);
     p.mx_dys = (uint8_t*)(wsb + wl.mx_dys);
@@ -693,14 +697,21 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   return launch_bwd(p, (hipStream_t)stream);
 }
 
-mok_status mok_mx_prepare_bwd(const mok_config* cfg, const void* w_gate, const void* w_up,
-                              const void* w_down, uint8_t* wt_down, uint8_t* st_down,
-                              uint8_t* wt_gu, uint8_t* st_gu, void* stream) {
+mok_status mok_prepare_bwd(const mok_config* cfg, const void* w_gate, const void* w_up,
+                           const void* w_down, void* wt_down, uint8_t* st_down, void* wt_gu,
+                           uint8_t* st_gu, void* stream) {
   if (!valid_cfg(cfg)) return MOK_EINVAL;
-  if (!w_gate || !w_up || !w_down || !wt_down || !st_down || !wt_gu || !st_gu) return MOK_EINVAL;
-  if (cfg->d % 128 != 0) return MOK_ESHAPE;
-  return launch_mx_prepare_bwd(cfg->E_local, cfg->d, cfg->I, w_gate, w_up, w_down, wt_down,
-                               st_down, wt_gu, st_gu, (hipStream_t)stream);
+  if (!w_gate || !w_up || !w_down || !wt_down || !wt_gu) return MOK_EINVAL;
+  if (cfg->prec == MOK_MXFP8) {
+    if (!st_down || !st_gu) return MOK_EINVAL;
+    if (cfg->d % 128 != 0) return MOK_ESHAPE;
+    return launch_mx_prepare_bwd(cfg->E_local, cfg->d, cfg->I, w_gate, w_up, w_down,
+                                 (uint8_t*)wt_down, st_down, (uint8_t*)wt_gu, st_gu,
+                                 (hipStream_t)stream);
+  }
+  if (cfg->prec != MOK_BF16) return MOK_EINVAL;
+  return launch_prepare_bwd_bf16(cfg->E_local, cfg->d, cfg->I, w_gate, w_up, w_down, wt_down,
+                                 wt_gu, (hipStream_t)stream);
 }
 
 mok_status mok_tune_fwd(const mok_config* cfg, const int32_t* mbs, int32_t n_mb,

@@ -1,10 +1,15 @@
 // Backward expert GEMMs, bf16, on the pipelined 256 x 256 tile engine.
 //   dh  : dh = dy W_down[e]           A = dy (k = d contiguous), B = W_down
-//         read as [d][I] (n contiguous) -> bf16 dh, then the SwiGLU
+//         read as [d][I] (n contiguous), or W_down^T [I][d] (k contiguous)
+//         when the caller prepared it -> bf16 dh, then the SwiGLU
 //         derivative pass turns it into dab
 //   dx  : dx = dab [W_gate; W_up]      A = dab (k = 2I contiguous), B = the
-//         two weight matrices read as [2I][d] -> epilogue pushes dx rows to
-//         their reverse-dispatch staging rows
+//         two weight matrices read as [2I][d], or [W_gate; W_up]^T [d][2I]
+//         when prepared -> epilogue pushes dx rows to their reverse-dispatch
+//         staging rows
+// The transposed weights give the MFMAs the same fragments (lane l: column
+// n0 + l % 32, k = 16 s + 8 (l / 32) + 0..7 either way), so dh and dx are
+// bit-identical with and without them; they spare the transposing LDS reads.
 //   wgrad (per expert, contraction over the expert's rows in ascending row
 //         order, split into chunks of 4096 rows whose partial sums are
 //         added in chunk order; rows past a chunk read zeros):
@@ -40,6 +45,7 @@ using namespace g2;
 struct DhArgs {
   const bf16_t* dy;    // [R_cap, d] (ring window: [rows, d] at r - lo)
   const bf16_t* wd;    // [E_local, d, I]
+  const bf16_t* wt;    // [E_local, I, d] = W_down^T, or null
   const bf16_t* ab;    // [R_cap, 2I]
   bf16_t* dab;         // [R_cap, 2I] (ring window: at r - lo)
   const int32_t* offsets;  // expert rows (ring window: the pieces woff)
@@ -49,7 +55,7 @@ struct DhArgs {
 
 __device__ __forceinline__ int win_lo(const int32_t* win) { return win ? win[0] : 0; }
 
-template <class C>
+template <class C, bool BT>
 __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
@@ -67,14 +73,25 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
     const int r = g.r0 + row;
     return r < g.r1 ? a.dy + (size_t)(r - lo) * a.d : nullptr;
   });
-  MNMajor<C::BN, C::BK> lb;
-  lb.ncols_left = a.I - n0;
   Acc<C> acc;
-  mainloop<C, false, true>(a.d / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                        [&](int kt, unsigned l) {
-                          lb.issue(kt, l, [&](int kk) -> const bf16_t* { return wd + (size_t)kk * a.I; });
-                        },
-                        smem, acc);
+  if constexpr (BT) {
+    const bf16_t* wt = a.wt + (size_t)g.e * a.I * a.d;
+    KMajor<C::BN, C::BK> lb;
+    lb.init([&](int nr) -> const bf16_t* {
+      const int n = n0 + nr;
+      return n < a.I ? wt + (size_t)n * a.d : nullptr;
+    });
+    mainloop<C, false, false>(a.d / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
+                              [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+  } else {
+    MNMajor<C::BN, C::BK> lb;
+    lb.ncols_left = a.I - n0;
+    mainloop<C, false, true>(a.d / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
+                             [&](int kt, unsigned l) {
+                               lb.issue(kt, l, [&](int kk) -> const bf16_t* { return wd + (size_t)kk * a.I; });
+                             },
+                             smem, acc);
+  }
   // dh (bf16) goes to the first half of its dab row; swiglu_bwd_kernel then
   // turns it into da | db in place with the saved a | b, as a separate pass
   // that runs at full memory bandwidth (as an epilogue, every workgroup would
@@ -137,13 +154,14 @@ struct DxArgs {
   const int32_t* win;  // ring window descriptor or null (offsets: the pieces woff)
   const bf16_t* wg;    // [E_local, I, d]
   const bf16_t* wu;
+  const bf16_t* wt;    // [E_local, d, 2I] = [W_gate; W_up]^T, or null
   const int32_t* offsets;
   const int32_t* row_src;
   DstTable dx_stage;
   int d, I, E_local, R_cap, ntn, T_src, k;
 };
 
-template <class C>
+template <class C, bool BT>
 __global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
@@ -162,16 +180,27 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
     const int r = g.r0 + row;
     return r < g.r1 ? a.dab + (size_t)(r - lo) * 2 * a.I : nullptr;
   });
-  MNMajor<C::BN, C::BK> lb;
-  lb.ncols_left = a.d - n0;
   Acc<C> acc;
-  mainloop<C, false, true>(2 * a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                        [&](int kt, unsigned l) {
-                          lb.issue(kt, l, [&](int kk) -> const bf16_t* {
-                            return kk < a.I ? wg + (size_t)kk * a.d : wu + (size_t)(kk - a.I) * a.d;
-                          });
-                        },
-                        smem, acc);
+  if constexpr (BT) {
+    const bf16_t* wt = a.wt + (size_t)g.e * a.d * 2 * a.I;
+    KMajor<C::BN, C::BK> lb;
+    lb.init([&](int nr) -> const bf16_t* {
+      const int n = n0 + nr;
+      return n < a.d ? wt + (size_t)n * 2 * a.I : nullptr;
+    });
+    mainloop<C, false, false>(2 * a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
+                              [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+  } else {
+    MNMajor<C::BN, C::BK> lb;
+    lb.ncols_left = a.d - n0;
+    mainloop<C, false, true>(2 * a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
+                             [&](int kt, unsigned l) {
+                               lb.issue(kt, l, [&](int kk) -> const bf16_t* {
+                                 return kk < a.I ? wg + (size_t)kk * a.d : wu + (size_t)(kk - a.I) * a.d;
+                               });
+                             },
+                             smem, acc);
+  }
   __shared__ int s_rows[BM];
   stage_rows(s_rows, a.row_src, g);
   __syncthreads();
@@ -618,6 +647,44 @@ mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int m
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
+// W^T of the expert weights, bf16, for dh and dx: out[e][n][k] for k < K0
+// from src0[e][k][n], for K0 <= k < K0 + K1 from src1[e][k - K0][n].  A
+// workgroup moves 128 k x 64 n through LDS; K0 + K1 and N are multiples of
+// 128 and 64 (d % 128 == 0, I % 64 == 0).
+__global__ __launch_bounds__(kThreads) void transpose_weights_kernel(const bf16_t* src0,
+                                                                    const bf16_t* src1,
+                                                                    int64_t estride, int K0,
+                                                                    int K1, int N, bf16_t* out) {
+  __shared__ bf16_t tile[128][64 + 8];
+  const int e = blockIdx.z, n0 = blockIdx.y * 64, K = K0 + K1;
+  const int k0 = blockIdx.x * 128;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int row = pass * 32 + threadIdx.x / 8, c = threadIdx.x % 8;
+    const int k = k0 + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k < K) {
+      const bf16_t* src = k < K0 ? src0 + (size_t)e * estride + (size_t)k * N
+                                 : src1 + (size_t)e * estride + (size_t)(k - K0) * N;
+      v = ld16(src + n0 + c * 8);
+    }
+    *reinterpret_cast<uint4*>(&tile[row][c * 8]) = v;
+  }
+  __syncthreads();
+  // 64 rows n x 16 chunks of 8 k; lanes take consecutive n (conflict-free LDS)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = threadIdx.x + kThreads * j, n = q % 64, kc = q / 64;
+    if (k0 + kc * 8 >= K) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      w[h] = (uint32_t)tile[kc * 8 + 2 * h][n] | ((uint32_t)tile[kc * 8 + 2 * h + 1][n] << 16);
+    *reinterpret_cast<uint4*>(out + ((size_t)e * N + n0 + n) * K + k0 + kc * 8) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 mok_status launch_swiglu_bwd(const BwdPlan& p, hipStream_t stream) {
   const size_t pieces = (size_t)launch_rows(p) * (p.I / 8);
   if (pieces == 0) return MOK_OK;
@@ -625,6 +692,24 @@ mok_status launch_swiglu_bwd(const BwdPlan& p, hipStream_t stream) {
                      dim3(kThreads), 0, stream, reinterpret_cast<const bf16_t*>(p.ab),
                      reinterpret_cast<bf16_t*>(p.dab), p.offsets, p.E_local, p.R_cap, p.I, p.win);
   trace_mark(p.tr, "bwd_swiglu", stream);
+  return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
+}
+
+mok_status launch_prepare_bwd_bf16(int E_local, int d, int I, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* wt_down, void* wt_gu,
+                                   hipStream_t stream) {
+  // W_down^T [E_local, I, d] from W_down [E_local, d, I]
+  hipLaunchKernelGGL(transpose_weights_kernel, dim3((unsigned)((d + 127) / 128), (unsigned)(I / 64),
+                                                    (unsigned)E_local),
+                     dim3(kThreads), 0, stream, reinterpret_cast<const bf16_t*>(w_down),
+                     (const bf16_t*)nullptr, (int64_t)d * I, d, 0, I,
+                     reinterpret_cast<bf16_t*>(wt_down));
+  // [W_gate; W_up]^T [E_local, d, 2I] from W_gate, W_up [E_local, I, d]
+  hipLaunchKernelGGL(transpose_weights_kernel, dim3((unsigned)((2 * I + 127) / 128),
+                                                    (unsigned)(d / 64), (unsigned)E_local),
+                     dim3(kThreads), 0, stream, reinterpret_cast<const bf16_t*>(w_gate),
+                     reinterpret_cast<const bf16_t*>(w_up), (int64_t)I * d, I, I, d,
+                     reinterpret_cast<bf16_t*>(wt_gu));
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 
@@ -645,7 +730,11 @@ mok_status launch_bwd_dgrad(const BwdPlan& p, hipStream_t stream) {
   d.E_local = p.E_local;
   d.R_cap = p.R_cap;
   d.ntn = (p.I + Default::BN - 1) / Default::BN;
-  hipLaunchKernelGGL(dh_g2<Default>, dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
+  d.wt = reinterpret_cast<const bf16_t*>(p.wt_down);
+  if (d.wt)
+    hipLaunchKernelGGL((dh_g2<Default, true>), dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
+  else
+    hipLaunchKernelGGL((dh_g2<Default, false>), dim3((unsigned)(mt * d.ntn)), dim3(kThreads), 0, stream, d);
   trace_mark(p.tr, "bwd_dh", stream);
   const mok_status rc = launch_swiglu_bwd(p, stream);
   if (rc != MOK_OK) return rc;
@@ -664,7 +753,11 @@ mok_status launch_bwd_dgrad(const BwdPlan& p, hipStream_t stream) {
   x.ntn = (p.d + Default::BN - 1) / Default::BN;
   x.T_src = p.T_src;
   x.k = p.k;
-  hipLaunchKernelGGL(dx_g2<Default>, dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
+  x.wt = reinterpret_cast<const bf16_t*>(p.wt_gu);
+  if (x.wt)
+    hipLaunchKernelGGL((dx_g2<Default, true>), dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
+  else
+    hipLaunchKernelGGL((dx_g2<Default, false>), dim3((unsigned)(mt * x.ntn)), dim3(kThreads), 0, stream, x);
   trace_mark(p.tr, "bwd_dx_push", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }

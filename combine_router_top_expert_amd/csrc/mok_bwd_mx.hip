@@ -7,7 +7,7 @@
 //   dW_gate|up = [da|db]^T X, dW_down = dy^T h: both operands transposed,
 //                           each column quantised along the expert's rows in
 //                           blocks of 32 (the expert's rows padded to 128)
-// The transposed weights are prepared once (mok_mx_prepare_bwd).  The
+// The transposed weights are prepared once (mok_prepare_bwd).  The
 // activations are packed by one kernel per operand that stages 128 rows (one
 // MX stage of an expert's rows) x 64 channels through LDS and writes both
 // quantisations from that one copy: along the row (32 channels a block, for
@@ -530,7 +530,7 @@ mok_status launch_bwd_mx_gemms(const BwdPlan& p, hipStream_t stream) {
   if (rc != MOK_OK) return rc;
   trace_mark(p.tr, "bwd_pack_dy_mx", stream);
   // dh = dy W_down -> bf16 [R_cap, I] (the first R_cap I elements of dab)
-  rc = launch_mx_rows_gemm(p.mx_dyq, p.mx_dys, p.mx_wt_down, p.mx_st_down, d, I, p.E_local,
+  rc = launch_mx_rows_gemm(p.mx_dyq, p.mx_dys, reinterpret_cast<const uint8_t*>(p.wt_down), p.mx_st_down, d, I, p.E_local,
                            p.R_cap, p.offsets, p.row_src, p.dab, I, nullptr, p.T_src, p.k,
                            stream, p.tr, "bwd_dh_mx");
   if (rc != MOK_OK) return rc;
@@ -547,7 +547,7 @@ mok_status launch_bwd_mx_gemms(const BwdPlan& p, hipStream_t stream) {
   if ((rc = launch_pack<1>(p, a, I, stream)) != MOK_OK) return rc;
   trace_mark(p.tr, "bwd_swiglu_pack_mx", stream);
   // dx = [da|db] [W_gate; W_up], pushed to the dx rows
-  rc = launch_mx_rows_gemm(p.mx_dabq, p.mx_dabs, p.mx_wt_gu, p.mx_st_gu, 2 * I, d, p.E_local,
+  rc = launch_mx_rows_gemm(p.mx_dabq, p.mx_dabs, reinterpret_cast<const uint8_t*>(p.wt_gu), p.mx_st_gu, 2 * I, d, p.E_local,
                            p.R_cap, p.offsets, p.row_src, nullptr, 0, &p.dx_stage, p.T_src, p.k,
                            stream, p.tr, "bwd_dx_push_mx");
   if (rc != MOK_OK) return rc;

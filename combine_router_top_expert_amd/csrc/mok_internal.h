@@ -148,8 +148,11 @@ struct BwdPlan {
   int win_mb, win_slots, n_win;
   // MXFP8 backward (prec == MOK_MXFP8): E4M3 codes + E8M0 scales per 32
   const uint8_t* mx_hs;                     // [R_cap, I/32] the forward's h scales
-  const uint8_t *mx_wt_down, *mx_st_down;   // [E_local, I, d], [.., d/32]
-  const uint8_t *mx_wt_gu, *mx_st_gu;       // [E_local, d, 2I], [.., 2I/32]
+  // the weights transposed (mok_prepare_bwd): W_down^T [E_local, I, d] and
+  // [W_gate; W_up]^T [E_local, d, 2I]; bf16 (optional, null = read W
+  // n-contiguous) or MXFP8 codes with the scales below
+  const void *wt_down, *wt_gu;
+  const uint8_t *mx_st_down, *mx_st_gu;     // MXFP8: [.., d/32], [.., 2I/32]
   uint8_t *mx_dyq, *mx_dys;                 // dy rows along d
   uint8_t *mx_dabq, *mx_dabs;               // [da|db] rows along 2I
   int64_t mx_cols;                          // columns of the transposed operands
@@ -182,6 +185,9 @@ int64_t bwd_mx_cols(int R_cap, int E_local);
 mok_status launch_mx_prepare_bwd(int E_local, int d, int I, const void* w_gate, const void* w_up,
                                  const void* w_down, uint8_t* wt_down, uint8_t* st_down,
                                  uint8_t* wt_gu, uint8_t* st_gu, hipStream_t stream);
+mok_status launch_prepare_bwd_bf16(int E_local, int d, int I, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* wt_down, void* wt_gu,
+                                   hipStream_t stream);
 // Geometry of the backward's ring windows for cfg (bf16, ring_bytes > 0):
 // slots of minibatch_rows rows, each holding dy and da | db rows and the
 // transposed token rows; false if the ring holds no slot.

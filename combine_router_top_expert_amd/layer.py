@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import (MAX_SOURCES, AuxStream, make_config, make_state, make_weights, mok_layer_bwd, mok_layer_fwd,
-               mok_mx_prepare_bwd, mok_mx_quantize, mok_tune_fwd, mok_workspace_bytes, STATUS)
+               mok_prepare_bwd, mok_mx_quantize, mok_tune_fwd, mok_workspace_bytes, STATUS)
 
 
 def _dt(prec: str):
@@ -30,7 +30,7 @@ def to_device(a: np.ndarray, prec: str, device) -> torch.Tensor:
 class MoELayer:
     def __init__(self, S, T_src, d, E, k, I, E_local, prec, R_cap, own_lo, own_n, device="cuda",
                  ring_bytes=0, minibatch_rows=256, comm_wgs=0, gemm_wgs=0, with_bwd=True,
-                 wait_limit_us=0, two_streams=True, bwd_ring_bytes=0):
+                 wait_limit_us=0, two_streams=True, bwd_ring_bytes=0, transposed_weights=True):
         assert S <= MAX_SOURCES
         self.S, self.T_src, self.d, self.E, self.k, self.I = S, T_src, d, E, k, I
         self.E_local, self.prec, self.R_cap = E_local, prec, R_cap
@@ -70,6 +70,9 @@ class MoELayer:
         self.state = make_state(self.topk_idx, self.topk_gate, self.counts, self.offsets,
                                 self.row_src, self.dest_row, self.h, self.ab, self.h_scale)
         self.with_bwd = with_bwd
+        # bf16 backward: the weights also transposed (mok_prepare_bwd), so dh
+        # and dx read them k-contiguous (bit-identical either way)
+        self.transposed_weights = transposed_weights
         if with_bwd:
             self.d_gate = torch.zeros(max(N, 1), dtype=torch.float32, device=dev)
             self.dx_stage = [torch.zeros(T_src * k, d, dtype=act, device=dev) for _ in range(S)]
@@ -99,6 +102,13 @@ class MoELayer:
             self.topk_gate[s * per:(s + 1) * per] = torch.from_numpy(g.reshape(-1)).to(self.device)
         if self.prec == "mxfp8":
             self._quantize_weights()
+        elif self.prec == "bf16" and self.with_bwd and self.transposed_weights:
+            E, d, I = self.E_local, self.d, self.I
+            self.wt = [torch.empty(E * I * d, dtype=torch.bfloat16, device=self.device),
+                       torch.empty(E * d * 2 * I, dtype=torch.bfloat16, device=self.device)]
+            mok_prepare_bwd(self.cfg, w_gate, w_up, w_down, self.wt[0], None, self.wt[1], None)
+            self.weights = make_weights(w_gate, w_up, w_down, wt_down=self.wt[0],
+                                        wt_gu=self.wt[1])
         else:
             self.weights = make_weights(w_gate, w_up, w_down)
 
@@ -134,7 +144,7 @@ class MoELayer:
                  torch.empty(E * I * d // 32, dtype=torch.uint8, device=self.device),
                  torch.empty(E * d * 2 * I, dtype=torch.uint8, device=self.device),
                  torch.empty(E * d * 2 * I // 32, dtype=torch.uint8, device=self.device)]
-            mok_mx_prepare_bwd(self.cfg, self.w_gate, self.w_up, self.w_down, *t)
+            mok_prepare_bwd(self.cfg, self.w_gate, self.w_up, self.w_down, *t)
         self.wt = t
         self.weights = make_weights(q[0][0], q[1][0], q[2][0], q[0][1], q[1][1], q[2][1], *t)
 

@@ -159,11 +159,14 @@ typedef struct mok_config {
  * MOK_MXFP8 the three matrices hold E4M3 codes (uint8, same shapes) and
  * s_gate, s_up, s_down their E8M0 scales ([E_local, I, d/32] and
  * [E_local, d, I/32]); otherwise the s_* pointers are NULL.
- * The MXFP8 backward (mok_layer_bwd) contracts the weights along their other
- * axis and reads them transposed, from mok_mx_prepare_bwd: wt_down
- * [E_local, I, d] codes (W_down^T, blocks of 32 along d) with st_down
- * [E_local, I, d/32]; wt_gu [E_local, d, 2I] codes ([W_gate; W_up]^T,
- * blocks of 32 along 2I) with st_gu [E_local, d, 2I/32].  NULL otherwise. */
+ * The backward (mok_layer_bwd) contracts W_down over d and W_gate, W_up over
+ * I, and can read them transposed, from mok_prepare_bwd: wt_down
+ * [E_local, I, d] = W_down^T and wt_gu [E_local, d, 2I] = [W_gate; W_up]^T.
+ * MOK_MXFP8: E4M3 codes, blocks of 32 along the last axis, with st_down
+ * [E_local, I, d/32] and st_gu [E_local, d, 2I/32]; required by the MXFP8
+ * backward.  MOK_BF16: bf16 values (st_* unused), optional (both or
+ * neither): with them the dh and dx GEMMs read their weights k-contiguous,
+ * with bit-identical results.  NULL otherwise. */
 typedef struct mok_expert_weights {
   const void* w_gate;
   const void* w_up;
@@ -171,9 +174,9 @@ typedef struct mok_expert_weights {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
-  const uint8_t* wt_down;
+  const void* wt_down;
   const uint8_t* st_down;
-  const uint8_t* wt_gu;
+  const void* wt_gu;
   const uint8_t* st_gu;
 } mok_expert_weights;
 
@@ -364,18 +367,19 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
                          void* const* d_x, float* dw_gate, float* dw_up, float* dw_down,
                          float* dw_router, void* ws, int32_t* dev_status, void* stream);
 
-/* Transposed MX weights of the MXFP8 backward [K02 MXFP8 in the GEMM data
- * paths]: from the bf16 weights w_gate, w_up [E_local, I, d] and w_down
- * [E_local, d, I] (cfg->E_local, d, I; d % 128 == 0 and I % 64 == 0, else
- * MOK_ESHAPE), writes wt_down [E_local, I, d] = the E4M3 codes of W_down^T
- * with st_down [E_local, I, d/32], and wt_gu [E_local, d, 2I] = those of
- * [W_gate; W_up]^T with st_gu [E_local, d, 2I/32] (OCP MX v1.0 blocks of 32
- * along the last axis; shared exponent floor(log2 amax) - 8, nearest E4M3
- * with ties to even, saturating).  Caller-owned outputs; run once per weight
- * update, off the step. */
-mok_status mok_mx_prepare_bwd(const mok_config* cfg, const void* w_gate, const void* w_up,
-                              const void* w_down, uint8_t* wt_down, uint8_t* st_down,
-                              uint8_t* wt_gu, uint8_t* st_gu, void* stream);
+/* Transposed weights of the backward [K01 the backward of the expert FFN;
+ * K02 MXFP8 in the GEMM data paths]: from the bf16 weights w_gate, w_up
+ * [E_local, I, d] and w_down [E_local, d, I] (cfg->E_local, d, I), writes
+ * wt_down [E_local, I, d] = W_down^T and wt_gu [E_local, d, 2I] =
+ * [W_gate; W_up]^T.  cfg->prec MOK_BF16: bf16 copies (st_down, st_gu
+ * unused).  MOK_MXFP8 (d % 128 == 0, else MOK_ESHAPE): their E4M3 codes with
+ * st_down [E_local, I, d/32] and st_gu [E_local, d, 2I/32] (OCP MX v1.0
+ * blocks of 32 along the last axis; shared exponent floor(log2 amax) - 8,
+ * nearest E4M3 with ties to even, saturating).  MOK_F32: MOK_EINVAL.
+ * Caller-owned outputs; run once per weight update, off the step. */
+mok_status mok_prepare_bwd(const mok_config* cfg, const void* w_gate, const void* w_up,
+                           const void* w_down, void* wt_down, uint8_t* st_down, void* wt_gu,
+                           uint8_t* st_gu, void* stream);
 
 /* Tuner of the fused path's minibatch size and workgroup split [K02: the
  * split of SMs between the communication and compute sides is set directly,

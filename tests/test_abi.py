@@ -281,5 +281,10 @@ def test_mxfp8_backward_rejections_on_the_host(L):
     st0 = mok.mok_fwd_state(*([1] * 8), None)  # no h scales kept
     assert bwd(cfg, mok.mok_expert_weights(*([1] * 10)), st0) == -1
     assert bwd(_cfg(S=S, prec="mxfp8", d=192), mok.mok_expert_weights(*([1] * 10)), st) == -2
-    assert L.mok_mx_prepare_bwd(ctypes.byref(cfg), 1, 1, 1, 1, 1, 1, None, None) == -1
-    assert L.mok_mx_prepare_bwd(ctypes.byref(_cfg(d=192)), 1, 1, 1, 1, 1, 1, 1, None) == -2
+    assert L.mok_prepare_bwd(ctypes.byref(cfg), 1, 1, 1, 1, 1, 1, None, None) == -1
+    assert L.mok_prepare_bwd(ctypes.byref(_cfg(prec="mxfp8", d=192)), 1, 1, 1, 1, 1, 1, 1,
+                             None) == -2
+    assert L.mok_prepare_bwd(ctypes.byref(_cfg(prec="f32")), 1, 1, 1, 1, None, 1, None,
+                             None) == -1
+    # bf16: the scales are unused, the transposes both required
+    assert L.mok_prepare_bwd(ctypes.byref(_cfg()), 1, 1, 1, None, None, 1, None, None) == -1

@@ -785,6 +785,29 @@ def test_bwd_two_streams_bit_identical_to_one(name):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+@pytest.mark.parametrize("name", ["bf16_all_local", "bf16_share", "bf16_spread"])
+def test_bwd_transposed_weights_bit_identical(name):
+    """dh and dx reading the prepared W^T (k-contiguous, mok_prepare_bwd) give
+    the same bytes as reading W itself through the transposing LDS loads."""
+    w = BWD_CASES[name]
+    _log("transposed weights", name)
+    c = make_host_case(w)
+    d_out = [to_device(synth.gen_dout(w, s)[0], w.prec, DEV) for s in range(w.S)]
+    snaps = []
+    for tw in (False, True):
+        L = _layer(c, transposed_weights=tw)
+        assert (L.weights.wt_down is not None) == tw
+        L.forward()
+        L.backward(d_out)
+        torch.cuda.synchronize()
+        L.check_status()
+        snaps.append([t.clone() for t in [L.d_gate, L.dw_gate, L.dw_up, L.dw_down, L.dw_router] +
+                      [L.d_x[s] for s in w.own] + [L.dx_stage[s] for s in range(w.S)]])
+        del L
+    for a, b in zip(*snaps):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 def test_mx_quantize_bit_exact():
     w = synth.WORKLOADS["C2"].replace(E=2, local_experts=[0, 1], I=256, d=512)
     _log("mx_quantize")

@@ -81,6 +81,8 @@ def kernel_work(name, w, R, T_pull=None):
         # read token row, write slot row (MX: d E4M3 codes + d/32 scales)
         "gather": R * d * 2.0 + (R * d * (1 + 1 / 32) if w.prec == "mxfp8" else R * d * eb),
         "bwd_regather_x": 2.0 * R * d * eb,
+        # the token rows and h, each read and written transposed per expert
+        "bwd_transpose_x_h": 2.0 * R * (d + I) * eb,
         "combine": (T * k * d + T * d) * eb,              # read k pushed rows, write out
         # read each pulled token's dout once and every row's pushed y, write dy
         "bwd_reverse_combine_pull": (T_pull + 2.0 * R) * d * eb,

@@ -38,7 +38,7 @@ bool valid_cfg(const mok_config* c) {
 
 struct Ws {
   size_t layout, xperm, xscale, hscale, ring, ring_ctr, dy, dab, dz, dwr, r_ident, r_counts, r_offsets,
-      r_row_src, r_dest_row, r_scratch, bx, wpart, wpart_down, worder, bwin, bring, mx_dyq,
+      r_row_src, r_dest_row, r_scratch, bx, bh, wpart, wpart_down, worder, bwin, bring, mx_dyq,
       mx_dys, mx_dabq, mx_dabs, mx_dabT, mx_dabTs, mx_xT, mx_xTs, mx_dyT, mx_dyTs, mx_hT,
       mx_hTs, total;
 };
@@ -100,6 +100,10 @@ Ws ws_layout(const mok_config* c) {
   if (!bring && c->prec != MOK_MXFP8)
     b += align256(c->prec == MOK_BF16 ? (size_t)c->d * xt_ld(c->R_cap, c->E_local) * 2
                                       : R * c->d * act_bytes(c->prec));
+  // h transposed like the token rows, for the down projection's weight
+  // gradient (one-launch bf16 backward)
+  w.bh = b;
+  if (!bring && c->prec == MOK_BF16) b += align256((size_t)c->I * xt_ld(c->R_cap, c->E_local) * 2);
   w.wpart = b;
   b += align256(c->prec == MOK_BF16 ? wgrad_partial_bytes(c->R_cap, c->d, c->I) : 0);
   // through the ring both weight gradients keep their partials until the
@@ -644,6 +648,7 @@ mok_status mok_layer_bwd(const mok_config* cfg, int32_t own_lo, int32_t own_n,
   p.r_dest_row = (int32_t*)(wsb + wl.r_dest_row);
   p.r_scratch = wsb + wl.r_scratch;
   p.x_perm = wsb + wl.bx;
+  p.hT = cfg->prec == MOK_BF16 && !bwd_through_ring(cfg) ? wsb + wl.bh : nullptr;
   p.wg_part = (float*)(wsb + wl.wpart);
   p.wg_order = (int32_t*)(wsb + wl.worder);
   p.status = dev_status;

@@ -587,7 +587,9 @@ mok_status run_bwd_two_streams(const BwdPlan& p, hipStream_t stream) {
     // 870 -> 800 us, step 7.31 -> 7.27 ms; half that made it outlast dx)
     mok_status rc = launch_gather_t(p, p.x_perm, aux, cus);
     if (rc != MOK_OK) return rc;
-    trace_mark(p.tr, "bwd_regather_x", aux);
+    if (p.hT) rc = launch_gather_t(p, p.hT, aux, cus, p.h, p.I);
+    if (rc != MOK_OK) return rc;
+    trace_mark(p.tr, p.hT ? "bwd_transpose_x_h" : "bwd_regather_x", aux);
   }
   MOK_HIP_CHECK(hipEventRecord(gx_ready, aux));
   if (p.dw_router) {
@@ -695,7 +697,9 @@ mok_status run_bwd(const BwdPlan& p, hipStream_t stream) {
       if (rc != MOK_OK) return rc;
       rc = launch_gather_t(p, p.x_perm, stream);
       if (rc != MOK_OK) return rc;
-      trace_mark(p.tr, "bwd_regather_x", stream);
+      if (p.hT) rc = launch_gather_t(p, p.hT, stream, 0, p.h, p.I);
+      if (rc != MOK_OK) return rc;
+      trace_mark(p.tr, p.hT ? "bwd_transpose_x_h" : "bwd_regather_x", stream);
     }
     mok_status rc = launch_bwd_gemms_bf16(p, p.x_perm, stream);
     if (rc != MOK_OK) return rc;

@@ -339,6 +339,7 @@ __device__ __forceinline__ bool wg_spread(int per, const int* s_rows) {
 // per workgroup.
 struct GatherTArgs {
   SrcTable src;
+  const bf16_t* rows;  // a row-major [R_cap, d] matrix to transpose instead of the token rows
   const int32_t* row_src;
   const int32_t* offsets;
   bf16_t* xT;      // [d, ldt]
@@ -361,9 +362,13 @@ __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
       const int r = g.r0 + 8 * rg + i;
       uint4 u = make_uint4(0, 0, 0, 0);
       if (r < g.r1) {
-        const int tok = a.row_src[r] / a.k;
-        u = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
-                                            (size_t)(tok % a.T_src) * a.d + c0);
+        if (a.rows) {
+          u = *reinterpret_cast<const uint4*>(a.rows + (size_t)r * a.d + c0);
+        } else {
+          const int tok = a.row_src[r] / a.k;
+          u = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
+                                              (size_t)(tok % a.T_src) * a.d + c0);
+        }
       }
       v[i][0] = u.x;
       v[i][1] = u.y;
@@ -387,7 +392,9 @@ __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
 // WIN: launched for one window of the backward through the ring (a.win set);
 // a one-launch kernel (WIN false) has none of the window code, so its
 // accumulators have one definition and stay in registers.
-template <class C, int MODE, bool WIN>
+// HT (MODE 1, one launch): B = h transposed per expert like the token rows
+// (a.BT, [I, ldt]), k-contiguous, instead of h read n-contiguous.
+template <class C, int MODE, bool WIN, bool HT = false>
 __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_cp[257], s_xp[257], s_tp[257], s_rows[2], s_tpw[257];
@@ -492,10 +499,11 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   auto issue_a = [&](int kt, unsigned l) {
     la.issue(kt, l, [&](int kk) -> const bf16_t* { return kk < cnt ? Ab + (size_t)kk * a.lda : nullptr; });
   };
-  if constexpr (MODE == 0) {
-    // B = the chunk's token rows from the transposed copy: row n of the tile
-    // is column n0 + n of d, k-contiguous from the chunk's first column; the
-    // last stage runs into the expert's zero padding
+  if constexpr (MODE == 0 || HT) {
+    // B = the chunk's token rows (MODE 0) or h rows (MODE 1) from the
+    // transposed copy: row n of the tile is column n0 + n of d (of I),
+    // k-contiguous from the chunk's first column; the last stage runs into
+    // the expert's zero padding
     static_assert(64 % C::BK == 0, "the transposed rows are padded to 64");
     KMajor<C::BN, C::BK> lb;
     const bf16_t* Bt = WIN ? a.BT + (size_t)64 * s_tpw[e] + xcol
@@ -619,16 +627,18 @@ bool bwd_ring_geometry(int64_t ring_bytes, int d, int I, int E_local, int mb, in
   return true;
 }
 
-mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks) {
+mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks,
+                           const void* rows, int width) {
   if (p.R_cap == 0) return MOK_OK;
   GatherTArgs g;
   g.src = p.src_x;
+  g.rows = reinterpret_cast<const bf16_t*>(rows);
   g.row_src = p.row_src;
   // a ring window's pieces: columns 64 P(e) + (r - woff[e]) of the window's rows
   g.offsets = p.win ? p.win + 3 : p.offsets;
   g.xT = reinterpret_cast<bf16_t*>(xT);
   g.ldt = p.win ? p.win_cols : xt_ld(p.R_cap, p.E_local);
-  g.d = p.d;
+  g.d = rows ? width : p.d;
   g.E_local = p.E_local;
   g.R_cap = p.R_cap;
   g.T_src = p.T_src;
@@ -639,10 +649,10 @@ mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int m
   // a cap on the workgroups (the copy then runs thin beside a GEMM on
   // another stream); workgroups stride over the tile groups either way
   if (max_blocks > 0) {
-    const int cap = max_blocks / (p.d / 64) > 0 ? max_blocks / (p.d / 64) : 1;
+    const int cap = max_blocks / (g.d / 64) > 0 ? max_blocks / (g.d / 64) : 1;
     if (gx > cap) gx = cap;
   }
-  hipLaunchKernelGGL(gather_t_kernel, dim3((unsigned)gx, (unsigned)(p.d / 64)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(gather_t_kernel, dim3((unsigned)gx, (unsigned)(g.d / 64)), dim3(kThreads), 0,
                      stream, g);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
@@ -822,11 +832,21 @@ mok_status launch_bwd_wgrad(const BwdPlan& p, const void* x_perm, hipStream_t st
     trace_mark(p.tr, "bwd_wgrad_gate_up_reduce", stream);
   }
   w = wgrad_args(p, x_perm, 1);
-  const dim3 grid1((unsigned)(max_chunks * w.mtn * w.ntn));
-  if (p.win)
-    hipLaunchKernelGGL((wgrad_g2<Narrow, 1, true>), grid1, dim3(kThreads), 0, stream, w);
-  else
-    hipLaunchKernelGGL((wgrad_g2<Narrow, 1, false>), grid1, dim3(kThreads), 0, stream, w);
+  if (!p.win && p.hT) {
+    // h transposed per expert (k-contiguous B): the 256 x 256 tile
+    w.B = nullptr;
+    w.BT = reinterpret_cast<const bf16_t*>(p.hT);
+    w.ldt = xt_ld(p.R_cap, p.E_local);
+    w.ntn = (w.N + Default::BN - 1) / Default::BN;
+    hipLaunchKernelGGL((wgrad_g2<Default, 1, false, true>),
+                       dim3((unsigned)(max_chunks * w.mtn * w.ntn)), dim3(kThreads), 0, stream, w);
+  } else {
+    const dim3 grid1((unsigned)(max_chunks * w.mtn * w.ntn));
+    if (p.win)
+      hipLaunchKernelGGL((wgrad_g2<Narrow, 1, true>), grid1, dim3(kThreads), 0, stream, w);
+    else
+      hipLaunchKernelGGL((wgrad_g2<Narrow, 1, false>), grid1, dim3(kThreads), 0, stream, w);
+  }
   trace_mark(p.tr, "bwd_wgrad_down", stream);
   if (reduce) {
     hipLaunchKernelGGL((wgrad_reduce<1>), dim3(512, (unsigned)p.E_local), dim3(kThreads), 0, stream,

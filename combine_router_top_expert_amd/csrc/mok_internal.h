@@ -134,6 +134,7 @@ struct BwdPlan {
   int32_t *r_ident, *r_counts, *r_offsets, *r_row_src, *r_dest_row;
   void* r_scratch;
   void* x_perm;     // bf16: [d, xt_ld] token rows gathered again, transposed, for the wgrad GEMM
+  void* hT;         // bf16: [I, xt_ld] h transposed the same way (one-launch backward), or null
   float* wg_part;   // [R_cap / 4096, 2I, d] split-K partials of the weight gradients
   float* wd_part;   // the down projection's partials ([R_cap / 4096, d, I]): wg_part in one
                     // launch (reduced before it is reused); a region of its own through the
@@ -167,7 +168,11 @@ mok_status launch_bwd(const BwdPlan& p, hipStream_t stream);
 inline int64_t xt_ld(int R_cap, int E_local) {
   return ((int64_t)R_cap + 63) / 64 * 64 + 64 * (int64_t)E_local;
 }
-mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks = 0);
+// The token rows (rows == null) or a row-major [R_cap, width] matrix (h),
+// transposed per expert into [width, xt_ld] with every expert's rows padded
+// to 64 columns.
+mok_status launch_gather_t(const BwdPlan& p, void* xT, hipStream_t stream, int max_blocks = 0,
+                           const void* rows = nullptr, int width = 0);
 mok_status launch_bwd_gemms_bf16(const BwdPlan& p, const void* x_perm, hipStream_t stream,
                                  hipEvent_t before_wgrad = nullptr, hipEvent_t after_dx = nullptr);
 // Pieces of the bf16 backward GEMMs (one launch, or one ring window each).

@@ -37,7 +37,8 @@ def test_bench_work_model_covers_the_traced_kernels():
     traced = set()
     for f in os.listdir(os.path.join(ROOT, "combine_router_top_expert_amd", "csrc")):
         src = open(os.path.join(ROOT, "combine_router_top_expert_amd", "csrc", f)).read()
-        traced |= set(re.findall(r'trace_mark\([^,]+,\s*"(\w+)"', src))
+        for call in re.findall(r'trace_mark\(([^;]*)\);', src):
+            traced |= set(re.findall(r'"(\w+)"', call))
         # (the MX row GEMM launcher takes its trace name as its last argument)
         traced |= set(re.findall(r'launch_mx_rows_gemm\([^;]*?"(\w+)"\);', src))
     traced.discard("start")
@@ -46,7 +47,7 @@ def test_bench_work_model_covers_the_traced_kernels():
     # the expert GEMMs and the HBM-bound copies must be priced against a roofline
     for n in ("ffn1_gate_up_swiglu", "ffn2_down", "bwd_dh", "bwd_dx_push", "bwd_wgrad_gate_up",
               "bwd_wgrad_down", "combine", "bwd_reverse_combine_pull", "bwd_swiglu",
-              "bwd_regather_x", "bwd_dx_sum_router", "route", "bwd_dh_mx", "bwd_dx_push_mx",
+              "bwd_regather_x", "bwd_transpose_x_h", "bwd_dx_sum_router", "route", "bwd_dh_mx", "bwd_dx_push_mx",
               "bwd_wgrad_gate_up_mx", "bwd_wgrad_down_mx", "bwd_pack_dy_mx",
               "bwd_swiglu_pack_mx", "bwd_pack_h_x_mx"):
         assert n in traced and n in modeled, n

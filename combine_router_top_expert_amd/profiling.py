@@ -46,7 +46,7 @@ TRACE_NAME = {
     "wgrad_reduce<0>": "bwd_wgrad_gate_up_reduce", "wgrad_reduce<1>": "bwd_wgrad_down_reduce",
     "dx_final_kernel": "bwd_dx_sum_router", "dwr_part_kernel": "bwd_dw_router_part",
     "dwr_reduce_kernel": "bwd_dw_router_reduce", "ring_kernel": "ring_fused_ffn",
-    "gather_t_kernel": "bwd_regather_x", "rc_pull_rows_kernel": "bwd_reverse_combine_pull",
+    "gather_t_kernel": "bwd_transpose_x_h", "rc_pull_rows_kernel": "bwd_reverse_combine_pull",
     "mx_pack_kernel<0>": "bwd_pack_dy_mx", "mx_pack_kernel<1>": "bwd_swiglu_pack_mx",
     "mx_pack_kernel<2>": "bwd_pack_h_x_mx", "mx_pack_kernel<3>": "bwd_pack_h_x_mx",
     "wgrad_mx_kernel<0>": "bwd_wgrad_gate_up_mx",
@@ -96,7 +96,9 @@ def kernel_key(name: str) -> str:
         return m.group(1) if m else name
     key = m.group(1)
     if key in ("wgrad_g2", "wgrad_reduce", "wgrad_mx_kernel", "mx_pack_kernel"):
-        t = re.search(r"(\d)>\(", name)
+        # the MODE / KIND argument: the first integer argument after the
+        # optional tile configuration
+        t = re.search(r"%s<(?:[\w:]*Cfg<[^>]*>,\s*)?(\d)" % key, name)
         key += "<%s>" % (t.group(1) if t else "?")
     return key
 

@@ -324,6 +324,29 @@ __device__ __forceinline__ void mma_rows(const Frags<C, A_MN, B_MN>& f, Acc<C>& 
       acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
 }
 
+// Instruction order of one k16 step: NMFMA MFMAs, with the NREAD LDS reads of
+// the next step spread one (or a few) behind each of the first MFMAs, so the
+// reads' latency runs under matrix work.  Left alone, the scheduler sinks each
+// read to just before its first use, and every k16 step waits on LDS latency
+// with the matrix cores idle.  (Scheduling hints only: they reorder
+// instructions, never the MFMAs of one accumulator, so results do not change.)
+template <int NMFMA, int NREAD, int I = 0>
+__device__ __forceinline__ void interleave_reads() {
+  if constexpr (I < NMFMA) {
+    constexpr int r = NREAD / NMFMA + (I < NREAD % NMFMA ? 1 : 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
+    interleave_reads<NMFMA, NREAD, I + 1>();
+  }
+}
+
+// LDS reads of one k16 step's fragments (one per K-major fragment, two per
+// MN-major one).
+template <class C, bool A_MN, bool B_MN>
+constexpr int frag_reads() {
+  return (A_MN ? 8 : 4) + (B_MN ? 2 : 1) * C::WNB;
+}
+
 // s_waitcnt: vmcnt <= N and lgkmcnt == 0 (expcnt at its maximum).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
@@ -384,11 +407,14 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
     for (int s = 0; s + 1 < S; ++s) {
       f[(s + 1) & 1].load(cur, cur + C::A_BYTES, s + 1);
       mma_rows<C, A_MN, B_MN, 0, 4>(f[s & 1], acc);
+      interleave_reads<4 * C::WNB, frag_reads<C, A_MN, B_MN>()>();
     }
     // (the hand-over also runs after the last stage, where it is harmless:
     // every MFMA stays outside branches, so the accumulators keep one
     // register assignment through the loop)
     const F& last = f[(S - 1) & 1];
+    // the MFMAs above stay above the wait (they cover the last reads' latency)
+    __builtin_amdgcn_sched_barrier(0);
     wait_stages_lgkm0<C::LOADS, NS - 2>(min(KT - 1, kt + NS - 1) - (kt + 1));
     __builtin_amdgcn_s_barrier();
     const unsigned slot = lds0 + (kt % NS) * C::STAGE;
@@ -399,6 +425,7 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
     const char* nxt = smem + ((kt + 1) % NS) * C::STAGE;
     f[S & 1].load(nxt, nxt + C::A_BYTES, 0);
     mma_rows<C, A_MN, B_MN, 2, 4>(last, acc);
+    interleave_reads<2 * C::WNB, frag_reads<C, A_MN, B_MN>()>();
   }
 }
 

@@ -6,8 +6,8 @@
 // previous macrobatch runs while the next one is dispatched).
 //
 // One launch of comm_wgs + gemm_wgs workgroups, all resident at once (one per
-// CU).  The first comm_wgs workgroups to start take the dispatch/combine role,
-// the rest the grouped-GEMM role.  The launch serves n_calls layer calls
+// CU).  comm_wgs of them, spread evenly over the XCDs, take the
+// dispatch/combine role, the rest the grouped-GEMM role.  The launch serves n_calls layer calls
 // (macrobatches) in a row; each call has its own sources, routing, layout,
 // staging rows and outputs, and all share the weights and the ring.
 //
@@ -31,23 +31,29 @@
 //                 the call == all its GEMM2 tiles.  Every call but the last:
 //                 the last call's combine has nothing left to overlap and runs
 //                 as the stand-alone combine launch after this kernel.
-// Tickets, in a fixed order per side.  Dispatch/combine: the fills of call 0,
-// the fills of call 1, the combine of call 0, the fills of call 2, the
-// combine of call 1, ..., the combine of the last call -- so the combine of
-// one call overlaps the pull of the next.  GEMM: per call, steps u = 0, 1,
-// ... each holding the GEMM1 tiles of minibatch u followed by the GEMM2 tiles
-// of minibatch u - lag, until the call's last GEMM2 tiles; then the next
-// call.  The lag covers the steps that run at once (GEMM workgroups / tiles
-// per step, plus one), so that a GEMM2 tile's GEMM1 tiles were taken a full
-// round of the GEMM side earlier and are normally done.
-// Every wait of a unit is on units with smaller tickets on its own side or on
+// Tickets, in a fixed order per queue.  Dispatch/combine (one queue): the
+// fills of call 0, the fills of call 1, the combine of call 0, the fills of
+// call 2, the combine of call 1, ..., the combine of the last call -- so the
+// combine of one call overlaps the pull of the next.  GEMM: per call, steps
+// u = 0, 1, ... each holding the GEMM1 tiles of minibatch u followed by the
+// GEMM2 tiles of minibatch u - lag, until the call's last GEMM2 tiles; then
+// the next call.  The lag covers the steps that run at once (GEMM workgroups
+// / tiles per step, plus one), so that a GEMM2 tile's GEMM1 tiles were taken
+// a full round of the GEMM side earlier and are normally done.  Every step's
+// tiles are split into one share per XCD, each its own ticket queue served by
+// that XCD's GEMM workgroups only: a share spans a few n-tiles and all
+// m-tiles of the minibatch, so a panel of tokens or weights is fetched into
+// few L2s instead of into every one.
+// Every wait of a unit is on units of an earlier step (of any queue) or on
 // the other side's units that precede, in that side's order, every unit the
 // waiter's side still needs: a fill waits on GEMM1 of an earlier minibatch,
 // GEMM1 on the fills of its own minibatch, GEMM2 on GEMM1 of its minibatch,
 // and the combine of call i -- ticketed after every fill of call i + 1 --
 // on GEMM2 of call i, whose tickets precede every GEMM ticket of call i + 1.
-// Tickets are taken in order by running workgroups, so the smallest
-// unfinished unit can always proceed.  Every wait is also bounded in time: on
+// Each queue's tickets are taken in order by its own running workgroups
+// (every queue with tiles has at least one), so the unfinished unit of the
+// earliest step can always proceed: the units ahead of it in its queue are
+// of earlier steps, hence done, or of its own step, whose waits are met.  Every wait is also bounded in time: on
 // expiry the kernel latches MOK_ETIMEOUT, raises an abort flag that every
 // other wait checks, and all workgroups return.
 //
@@ -77,7 +83,12 @@ using namespace g2;
 
 constexpr int kFillRows = 32;  // rows per fill unit
 constexpr int kCombTok = 32;   // own tokens per combine unit
-constexpr int kCtr = 4;        // fill ticket, GEMM ticket, role ticket, abort flag
+// GEMM tile queues: one per XCD (workgroup b runs on XCD b % 8, the order in
+// which the dispatcher hands workgroups to the XCDs)
+constexpr int kQueues = 8;
+// counters: the fill ticket, the abort flag, then one GEMM ticket per queue
+constexpr int kFillTicket = 0, kAbort = 1, kGemmTicket = 2;
+constexpr int kCtr = kGemmTicket + kQueues;
 
 struct RingArgs {
   const RingCall* calls;   // [n_calls] in device memory
@@ -85,6 +96,7 @@ struct RingArgs {
   int d, I, E_local, R_cap, T_src, k;
   int mb, nslot, cpm, nmt, ntn1, ntn2, M_max;  // M_max: minibatches of one call, at most
   int comm_wgs;
+  int nq;              // GEMM queues: kQueues, or 1 when an XCD class has no GEMM workgroup
   int lag;             // GEMM2 of minibatch u runs in step u + lag (>= 1)
   char* ring;
   int64_t slot_bytes;
@@ -132,11 +144,11 @@ __device__ bool ring_wait(int32_t* p, int target, const RingArgs& a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       return true;
     }
-    if (uniform(__hip_atomic_load(a.ctr + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+    if (uniform(__hip_atomic_load(a.ctr + kAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
       return false;
     if (__builtin_amdgcn_s_memrealtime() - t0 > a.wait_ticks) {
       latch(a.status, MOK_ETIMEOUT);
-      __hip_atomic_store(a.ctr + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctr + kAbort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -344,7 +356,7 @@ __device__ void dispatch_role(const RingArgs& a, const CallsLds& L, int* s_val) 
   int32_t* x_ready = a.ctr + kCtr;
   int32_t* g1_done = x_ready + a.n_calls * a.M_max;
   for (;;) {
-    const int f = wg_ticket(a.ctr + 0, s_val);
+    const int f = wg_ticket(a.ctr + kFillTicket, s_val);
     int c = 0, idx = 0;
     const int kind = uniform(comm_unit(a, L, f, &c, &idx));
     c = uniform(c);
@@ -369,18 +381,32 @@ __device__ void dispatch_role(const RingArgs& a, const CallsLds& L, int* s_val) 
 }
 
 // ---------------------------------------------------------------- GEMM side
+// Queue q's share of a step: the tiles [q n / nq, (q + 1) n / nq) of each
+// GEMM in the step's order, n-tile outer and m-tile inner, so that the share
+// spans few n-tiles (weight panels) and every m-tile of the minibatch (its
+// token panels), and the tiles that read one panel run in one L2.
+__device__ __forceinline__ void queue_share(int n, int q, int nq, int* off, int* cnt) {
+  const int lo = (int)((int64_t)q * n / nq), hi = (int)((int64_t)(q + 1) * n / nq);
+  *off = lo;
+  *cnt = hi - lo;
+}
+
 template <class C, bool MX>
-__device__ void gemm_role(const RingArgs& a, const CallsLds& L, int* s_val, char* smem) {
+__device__ void gemm_role(const RingArgs& a, const CallsLds& L, int* s_val, char* smem, int q) {
   int32_t* x_ready = a.ctr + kCtr;
   int32_t* g1_done = x_ready + a.n_calls * a.M_max;
   int32_t* g2_done = g1_done + a.n_calls * a.M_max;
-  const int n1 = a.nmt * a.ntn1, n2 = a.nmt * a.ntn2;
+  const int n1 = a.nmt * a.ntn1;
+  int o1, s1, o2, s2;
+  queue_share(n1, q, a.nq, &o1, &s1);
+  queue_share(a.nmt * a.ntn2, q, a.nq, &o2, &s2);
+  const int per = s1 + s2;  // this queue's tiles per step
   for (;;) {
     __syncthreads();  // the previous unit is done with LDS and the broadcast slots
-    int t = wg_ticket(a.ctr + 1, s_val);
+    int t = wg_ticket(a.ctr + kGemmTicket + q, s_val);
     int c = 0;
     for (; c < a.n_calls; ++c) {  // the call of ticket t (its steps: M + lag)
-      const int nt_call = (L.M[c] + a.lag) * (n1 + n2);
+      const int nt_call = (L.M[c] + a.lag) * per;
       if (t < nt_call) break;
       t -= nt_call;
     }
@@ -394,13 +420,14 @@ __device__ void gemm_role(const RingArgs& a, const CallsLds& L, int* s_val, char
     }
     const RingCall& call = a.calls[c];
     const int M = L.M[c];
-    const int u = t / (n1 + n2);
-    int o = t % (n1 + n2);
-    if (o < n1) {
+    const int u = t / per;
+    const int o = t % per;
+    if (o < s1) {
       const int m = u;
       if (m >= M) continue;
       const int G = L.base[c] + m;
-      const int mt = o / a.ntn1, nt = o % a.ntn1;
+      const int i = o1 + o;
+      const int mt = i % a.nmt, nt = i / a.nmt;
       const GTile mbt = minibatch(a, L, c, m);
       GTile g;
       g.e = mbt.e;
@@ -446,8 +473,8 @@ __device__ void gemm_role(const RingArgs& a, const CallsLds& L, int* s_val, char
       const int m = u - a.lag;
       if (m < 0) continue;
       const int G = L.base[c] + m;
-      o -= n1;
-      const int mt = o / a.ntn2, nt = o % a.ntn2;
+      const int i = o2 + (o - s1);
+      const int mt = i % a.nmt, nt = i / a.nmt;
       const GTile mbt = minibatch(a, L, c, m);
       GTile g;
       g.e = mbt.e;
@@ -487,12 +514,16 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(RingArgs a) {
   }
   if (threadIdx.x == 0) L.base[a.n_calls] = base;
   __syncthreads();
-  const int role = wg_ticket(a.ctr + 2, s_val);
-  __syncthreads();  // every lane has read the role before s_val is reused
-  if (role < a.comm_wgs)
+  // roles by workgroup index: of the workgroups of XCD x (b % 8 == x, in the
+  // order j = b / 8) the first comm_wgs / 8 (one more for x < comm_wgs % 8)
+  // dispatch, so both sides spread evenly over the XCDs; the others serve
+  // the XCD's GEMM queue
+  const int b = (int)blockIdx.x, x = b % kQueues, j = b / kQueues;
+  const int cx = a.comm_wgs / kQueues + (x < a.comm_wgs % kQueues ? 1 : 0);
+  if (j < cx)
     dispatch_role<MX>(a, L, s_val);
   else
-    gemm_role<C, MX>(a, L, s_val, smem);
+    gemm_role<C, MX>(a, L, s_val, smem, a.nq == kQueues ? x : 0);
 }
 
 // Copies one call's descriptor into device memory (tables travel as kernel
@@ -511,6 +542,20 @@ int device_cus() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return n;
+}
+
+// GEMM queues of a split: one per XCD class (workgroups b with b % 8 == x)
+// when every class keeps at least one GEMM workgroup after its dispatch
+// share, else a single queue.  Every queue with tiles needs a workgroup for
+// the ring to make progress.
+static int ring_gemm_queues(int comm, int gemm) {
+  const int grid = comm + gemm;
+  for (int x = 0; x < kQueues; ++x) {
+    const int nx = grid / kQueues + (x < grid % kQueues ? 1 : 0);
+    const int cx = comm / kQueues + (x < comm % kQueues ? 1 : 0);
+    if (nx - cx < 1) return 1;
+  }
+  return kQueues;
 }
 
 int64_t ring_slot_bytes(int prec, int d, int mb) {
@@ -631,6 +676,7 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr)
     const int per_step = a.nmt * (a.ntn1 + a.ntn2);
     a.lag = (gemm + per_step - 1) / per_step + 1;
   }
+  a.nq = ring_gemm_queues(comm, gemm);
   for (int c = 0; c < p.n_calls; ++c)
     hipLaunchKernelGGL(ring_call_kernel, dim3(1), dim3(64), 0, stream, p.calls[c], calls + c);
   const int nctr = kCtr + 2 * p.n_calls * a.M_max + 2 * p.n_calls;

@@ -201,8 +201,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
                              },
                              smem, acc);
   }
-  __shared__ int s_rows[BM];
-  stage_rows(s_rows, a.row_src, g);
+  __shared__ bf16_t* s_dst[BM];
+  stage_dst_rows(s_dst, a.row_src, g, a.dx_stage, a.k, a.T_src, a.d);
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
   static_assert(WaveStage<C, bf16_t>::PASSES == 1, "one staging pass");
@@ -213,11 +213,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
     const int r = g.r0 + (wave >> 1) * 128 + trow;
     const int col = n0 + (wave & 1) * (C::BN / 2) + c * 8;
     if (r >= g.r1 || col >= a.d) return;
-    const int n = s_rows[r - g.r0];
-    const int tok = n / a.k, j = n % a.k;
-    bf16_t* dst = reinterpret_cast<bf16_t*>(a.dx_stage.p[tok / a.T_src]) +
-                  ((size_t)(tok % a.T_src) * a.k + j) * a.d;
-    *reinterpret_cast<uint4*>(dst + col) = st.raw(srow, c);
+    *reinterpret_cast<uint4*>(s_dst[r - g.r0] + col) = st.raw(srow, c);
   });
 }
 

@@ -31,19 +31,38 @@ __device__ __forceinline__ bool launch_tile(const int32_t* offsets, int E_local,
   return true;
 }
 
+// Persistent grouped-M launch: workgroup b runs tiles b, b + gridDim.x, ...
+// of the (expert rows, N-tile) grid in XCD-aware grouped order (gridDim.x a
+// multiple of 8, so every tile of a workgroup stays on its XCD's range); the
+// per-expert tile prefix is built once per workgroup.  fn(g, nt) runs one
+// tile; a barrier separates one tile's epilogue from the next tile's loads
+// into the same LDS.
+template <class Fn>
+__device__ __forceinline__ void persistent_tiles(const int32_t* offsets, int E_local, int R_cap,
+                                                 int ntn, int* s_prefix, Fn fn) {
+  const int total_m = group_prefix(offsets, E_local, R_cap, s_prefix);
+  const int total = total_m * ntn;
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    int mt, nt;
+    grouped_order(xcd_tile(t, total), total_m, ntn, &mt, &nt);
+    const GTile g = group_tile(offsets, E_local, R_cap, s_prefix, mt);
+    __syncthreads();
+    fn(g, nt);
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(kThreads, C::OCC) void ffn1_g2(F1Args a, SrcTable src) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
-  GTile g;
-  int nt;
-  if (!launch_tile(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, &g, &nt)) return;
-  ffn1_tile<C>(a, smem, g, nt, [&](int row) -> const bf16_t* {
-    const int r = g.r0 + row;
-    if (r >= g.r1) return nullptr;
-    if (a.x) return a.x + (size_t)r * a.d;
-    const int tok = a.row_src[r] / a.k;
-    return reinterpret_cast<const bf16_t*>(src.p[tok / a.T_src]) + (size_t)(tok % a.T_src) * a.d;
+  persistent_tiles(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, [&](const GTile& g, int nt) {
+    ffn1_tile<C>(a, smem, g, nt, [&](int row) -> const bf16_t* {
+      const int r = g.r0 + row;
+      if (r >= g.r1) return nullptr;
+      if (a.x) return a.x + (size_t)r * a.d;
+      const int tok = a.row_src[r] / a.k;
+      return reinterpret_cast<const bf16_t*>(src.p[tok / a.T_src]) + (size_t)(tok % a.T_src) * a.d;
+    });
   });
 }
 
@@ -51,10 +70,18 @@ template <class C>
 __global__ __launch_bounds__(kThreads, C::OCC) void ffn2_g2(F2Args a, DstTable staging) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_prefix[257];
-  GTile g;
-  int nt;
-  if (!launch_tile(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, &g, &nt)) return;
-  ffn2_tile<C>(a, staging, smem, g, nt);
+  persistent_tiles(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix,
+                   [&](const GTile& g, int nt) { ffn2_tile<C>(a, staging, smem, g, nt); });
+}
+
+// Workgroups of a persistent launch over at most `tiles` tiles: one per CU
+// (OCC per CU), a multiple of 8.
+static unsigned persistent_grid(int tiles, int occ) {
+  const int cus = device_cus();
+  int n = cus > 0 ? cus * occ : 256;
+  n -= n % 8;
+  if (n < 8) n = 8;
+  return (unsigned)(tiles < n ? ((tiles + 7) / 8) * 8 : n);
 }
 
 __global__ __launch_bounds__(kThreads) void ffn1_mx(F1MxArgs a) {
@@ -113,8 +140,8 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
   a1.ntn = (I + Default::BN / 2 - 1) / (Default::BN / 2);
   a1.T_src = T_src;
   a1.k = k;
-  hipLaunchKernelGGL(ffn1_g2<Default>, dim3((unsigned)(mt * a1.ntn)), dim3(kThreads), 0, stream, a1,
-                     stab);
+  hipLaunchKernelGGL(ffn1_g2<Default>, dim3(persistent_grid(mt * a1.ntn, Default::OCC)), dim3(kThreads),
+                     0, stream, a1, stab);
   trace_mark(tr, "ffn1_gate_up_swiglu", stream);
   F2Args a2;
   memset(&a2, 0, sizeof(a2));
@@ -134,7 +161,8 @@ mok_status launch_ffn_bf16(int d, int I, int E_local, int R_cap, const void* x,
   a2.ntn = (d + Default::BN - 1) / Default::BN;
   a2.T_src = T_src;
   a2.k = k;
-  hipLaunchKernelGGL(ffn2_g2<Default>, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2,
+  hipLaunchKernelGGL(ffn2_g2<Default>, dim3(persistent_grid(mt * a2.ntn, Default::OCC)), dim3(kThreads),
+                     0, stream, a2,
                      gtab);
   trace_mark(tr, "ffn2_down", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;

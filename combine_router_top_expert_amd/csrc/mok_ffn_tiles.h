@@ -140,8 +140,8 @@ __device__ __forceinline__ void ffn1_tile(const F1Args& a, char* smem, const GTi
 template <class C, class AccT>
 __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GTile& g, int nt,
                                            const F2Args& a, const DstTable& staging) {
-  __shared__ int s_rows[BM];
-  if (a.push) stage_rows(s_rows, a.row_src, g);
+  __shared__ bf16_t* s_dst[BM];
+  if (a.push) stage_dst_rows(s_dst, a.row_src, g, staging, a.k, a.T_src, a.d);
   __syncthreads();
   const WaveStage<C, bf16_t> st(smem);
   static_assert(WaveStage<C, bf16_t>::PASSES == 1, "one staging pass");
@@ -154,10 +154,7 @@ __device__ __forceinline__ void ffn2_store(const AccT& acc, char* smem, const GT
     if (r >= g.r1 || col >= a.d) return;
     bf16_t* dst;
     if (a.push) {
-      const int n = s_rows[r - g.r0];
-      const int tok = n / a.k, j = n % a.k;
-      dst = reinterpret_cast<bf16_t*>(staging.p[tok / a.T_src]) +
-            ((size_t)(tok % a.T_src) * a.k + j) * a.d;
+      dst = s_dst[r - g.r0];
     } else {
       dst = a.y + (size_t)r * (a.ldy ? a.ldy : a.d);
     }

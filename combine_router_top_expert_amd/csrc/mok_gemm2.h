@@ -594,14 +594,22 @@ __device__ __forceinline__ GTile group_tile(const int32_t* offsets, int E_local,
   return t;
 }
 
-// Item numbers of a tile's rows, copied to LDS ahead of an epilogue that
-// pushes rows to their (source, token, slot) addresses: one global load per
-// row instead of one per 16-byte chunk (the workgroup's 256 threads cover the
-// 256 rows; a barrier must follow before they are read).
-__device__ __forceinline__ void stage_rows(int* s_rows, const int32_t* row_src, const GTile& g) {
+// Destination row of every tile row for an epilogue that pushes rows into
+// per-source buffers: routed row r holds item n = row_src[r] (token n / k,
+// slot n % k), whose row is row (tok % T_src) * k + slot of source
+// tok / T_src's buffer.  One row per thread, so the stores of the row chunks
+// need no integer divisions (a barrier must follow before they are read).
+__device__ __forceinline__ void stage_dst_rows(bf16_t** s_dst, const int32_t* row_src, const GTile& g,
+                                               const DstTable& tab, int k, int T_src, int d) {
   static_assert(kThreads == BM, "one thread per tile row");
   const int r = g.r0 + (int)threadIdx.x;
-  s_rows[threadIdx.x] = r < g.r1 ? row_src[r] : 0;
+  bf16_t* p = nullptr;
+  if (r < g.r1) {
+    const int n = row_src[r];
+    const int tok = n / k, j = n % k;
+    p = reinterpret_cast<bf16_t*>(tab.p[tok / T_src]) + ((size_t)(tok % T_src) * k + j) * d;
+  }
+  s_dst[threadIdx.x] = p;
 }
 
 }  // namespace g2

@@ -345,27 +345,37 @@ struct GatherTArgs {
 
 __global__ __launch_bounds__(kThreads) void gather_t_kernel(GatherTArgs a) {
   __shared__ int s_prefix[257];
+  __shared__ const bf16_t* s_src[4][64];  // each wave's 64 tile rows (null past the expert)
   const int total = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix, 64);
   const int cb = threadIdx.x & 7, rg = (threadIdx.x >> 3) & 7, sub = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int c0 = blockIdx.y * 64 + 8 * cb;
   for (int grp = blockIdx.x; 4 * grp < total; grp += gridDim.x) {
     const int mt = 4 * grp + sub;  // this wave's 64-row tile
     if (mt >= total) continue;
     const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mt, 64);
+    {
+      // lane l looks up row l of the tile once (the 8 lanes that read a row
+      // share it), so no lane divides per load
+      const int r = g.r0 + lane;
+      const bf16_t* p = nullptr;
+      if (r < g.r1) {
+        if (a.rows) {
+          p = a.rows + (size_t)r * a.d;
+        } else {
+          const int tok = a.row_src[r] / a.k;
+          p = reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) + (size_t)(tok % a.T_src) * a.d;
+        }
+      }
+      s_src[sub][lane] = p;
+      wave_lds_fence();
+    }
     uint32_t v[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = g.r0 + 8 * rg + i;
+      const bf16_t* p = s_src[sub][8 * rg + i];
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < g.r1) {
-        if (a.rows) {
-          u = *reinterpret_cast<const uint4*>(a.rows + (size_t)r * a.d + c0);
-        } else {
-          const int tok = a.row_src[r] / a.k;
-          u = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.src.p[tok / a.T_src]) +
-                                              (size_t)(tok % a.T_src) * a.d + c0);
-        }
-      }
+      if (p) u = *reinterpret_cast<const uint4*>(p + c0);
       v[i][0] = u.x;
       v[i][1] = u.y;
       v[i][2] = u.z;

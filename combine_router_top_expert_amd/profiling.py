@@ -243,8 +243,8 @@ def mfma_main(out_dir: str):
              "the work on padding (rows past an expert's last tile, columns past I).  LDS bank",
              "conflicts are the share of LDS-active cycles spent in conflicts.", "",
              "Commands (from the repository root; OUT = the output folder):", "",
-             "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d OUT/c2 -o c2 -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
-             "    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE -f csv -d OUT/c2l -o c2l -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d OUT/c2 -o c2 -- python3 bench.py --workload C2 --steps 1 --warmup 1 --no-cpu-baseline",
+             "    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE -f csv -d OUT/c2l -o c2l -- python3 bench.py --workload C2 --steps 1 --warmup 1 --no-cpu-baseline",
              "    rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_MOPS_F6F4 -f csv -d OUT/c4 -o c4 -- python3 bench.py --workload C4 --path staged --steps 1 --warmup 1 --no-cpu-baseline",
              "    python3 -m combine_router_top_expert_amd.profiling --mfma OUT", "",
              "| kernel | trace name | MfmaUtil % | executed TFLOP | algorithmic TFLOP | padding % | LDS bank-conflict % |",

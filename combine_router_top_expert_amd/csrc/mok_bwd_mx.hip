@@ -60,10 +60,7 @@ __device__ __forceinline__ void tq_block(RowPtr rowp, uint8_t* codes, uint8_t* s
   uint32_t w[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) word |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 * q + e], -sh)) << (8 * e);
-    w[q] = word;
+    w[q] = e4m3_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], sh);
   }
   uint8_t* out = codes + (size_t)ch * ldc + col0 + blk * 32;
   *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -118,11 +115,7 @@ __device__ __forceinline__ void pack_rows(const bf16_t* t, int nrows, uint8_t* c
     unpack8(*reinterpret_cast<const uint4*>(row + q * 8), v);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        word |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 * h + e], -sh)) << (8 * e);
-      wq[2 * q + h] = word;
+      wq[2 * q + h] = e4m3_pack4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3], sh);
     }
   }
   uint8_t* out = codes + (r0 + r) * ldq + ch0 + blk * 32;
@@ -144,12 +137,9 @@ __device__ __forceinline__ void pack_cols(const bf16_t* t, uint8_t* codes, uint8
   uint32_t wq[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      word |= e4m3_code(__builtin_amdgcn_ldexpf(bf16_to_f32(t[tix(blk * 32 + 4 * q + e, ch)]), -sh))
-              << (8 * e);
-    wq[q] = word;
+    wq[q] = e4m3_pack4(bf16_to_f32(t[tix(blk * 32 + 4 * q, ch)]), bf16_to_f32(t[tix(blk * 32 + 4 * q + 1, ch)]),
+                       bf16_to_f32(t[tix(blk * 32 + 4 * q + 2, ch)]), bf16_to_f32(t[tix(blk * 32 + 4 * q + 3, ch)]),
+                       sh);
   }
   uint8_t* out = codes + (int64_t)(ch0 + ch) * ldc + col0 + blk * 32;
   *reinterpret_cast<uint4*>(out) = make_uint4(wq[0], wq[1], wq[2], wq[3]);

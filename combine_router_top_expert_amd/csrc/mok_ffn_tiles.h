@@ -254,10 +254,7 @@ __device__ __forceinline__ void ffn1_mx_tile(const F1MxArgs& a, char* smem, cons
       amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
       if (ok) {
         const int sh = mx_shared_exp(amax);
-        uint32_t code = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) code |= e4m3_code(__builtin_amdgcn_ldexpf(hv[e], -sh)) << (8 * e);
-        *reinterpret_cast<uint32_t*>(a.hq + (size_t)r * a.I + i) = code;
+        *reinterpret_cast<uint32_t*>(a.hq + (size_t)r * a.I + i) = e4m3_pack4(hv[0], hv[1], hv[2], hv[3], sh);
         if (within == 0) a.hs[(size_t)r * (a.I / 32) + i / 32] = (uint8_t)(sh + 127);
       }
     }

@@ -69,11 +69,8 @@ __device__ __forceinline__ void mx_encode_unit(const uint4& q, bool have, uint8_
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   if (have) {
     const int sh = mx_shared_exp(amax);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[i], -sh)) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + i], -sh)) << (8 * i);
+    const uint32_t lo = e4m3_pack4(v[0], v[1], v[2], v[3], sh);
+    const uint32_t hi = e4m3_pack4(v[4], v[5], v[6], v[7], sh);
     *reinterpret_cast<uint2*>(dst + u * 8) = make_uint2(lo, hi);
     if ((u & 3) == 0) dsc[u >> 2] = (uint8_t)(sh + 127);
   }
@@ -230,11 +227,8 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     if (have) {
       const int sh = mx_shared_exp(amax);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[i], -sh)) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + i], -sh)) << (8 * i);
+      const uint32_t lo = e4m3_pack4(v[0], v[1], v[2], v[3], sh);
+      const uint32_t hi = e4m3_pack4(v[4], v[5], v[6], v[7], sh);
       *reinterpret_cast<uint2*>(a.codes + u * 8) = make_uint2(lo, hi);
       if ((u & 3) == 0) a.scales[u >> 2] = (uint8_t)(sh + 127);
     }

@@ -24,20 +24,23 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Nearest E4M3 (OCP "fn") code of v, ties to even, saturating at +-448.
-// Normal range: round the fp32 bits to 3 mantissa bits and rebias the
-// exponent (127 -> 7); below 2^-6 the code is the integer v * 2^9.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  uint32_t b = __float_as_uint(v);
-  uint32_t s = (b >> 24) & 0x80u;
-  float a = __uint_as_float(b & 0x7FFFFFFFu);
-  if (a >= 448.0f) return s | 0x7Eu;
-  uint32_t ab = b & 0x7FFFFFFFu;
-  if (ab < 0x3C800000u) {  // a < 2^-6
-    return s | (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20;
-  return s | (r - 960u);
+// Nearest E4M3 (OCP "fn") code of v, ties to even, saturating at +-448: the
+// value clamped to +-448, then gfx950's fp8 conversion (which rounds to
+// nearest even and keeps E4M3 subnormals).  Over every finite fp32 value
+// below 1024 in magnitude (and so every scaled block value, which stays
+// below 512) this gives the codes of the bit-level rule -- the fp32 bits
+// rounded to 3 mantissa bits and rebiased (127 -> 7), and v * 2^9 rounded
+// below 2^-6 -- with no exception; above 448 both saturate.
+__device__ __forceinline__ float e4m3_clamp(float v) {
+  return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+}
+// Codes of v[0..3] * 2^-sh in bytes 0..3 (two packed conversions).
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3, int sh) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(__builtin_amdgcn_ldexpf(v0, -sh)),
+                                          e4m3_clamp(__builtin_amdgcn_ldexpf(v1, -sh)), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(__builtin_amdgcn_ldexpf(v2, -sh)),
+                                      e4m3_clamp(__builtin_amdgcn_ldexpf(v3, -sh)), w, true);
+  return (uint32_t)w;
 }
 
 }  // namespace mok

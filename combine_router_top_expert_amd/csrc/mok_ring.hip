@@ -265,11 +265,8 @@ __device__ void fill_rows(const RingArgs& a, const RingCall& call, char* slot, c
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
       {
         const int sh = mx_shared_exp(amax);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= e4m3_code(__builtin_amdgcn_ldexpf(f[i], -sh)) << (8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= e4m3_code(__builtin_amdgcn_ldexpf(f[4 + i], -sh)) << (8 * i);
+        const uint32_t lo = e4m3_pack4(f[0], f[1], f[2], f[3], sh);
+        const uint32_t hi = e4m3_pack4(f[4], f[5], f[6], f[7], sh);
         uint8_t* codes = reinterpret_cast<uint8_t*>(slot) + (size_t)q * a.d;
         *reinterpret_cast<uint2*>(codes + c * 8) = make_uint2(lo, hi);
         if ((c & 3) == 0) {

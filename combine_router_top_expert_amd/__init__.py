@@ -31,7 +31,7 @@ STATUS = {
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
            "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_layer_fwd_macro",
-           "mok_prepare_bwd", "mok_version")
+           "mok_prepare_bwd", "mok_mx_quantize_f32", "mok_version")
 
 
 class MokError(RuntimeError):
@@ -237,6 +237,7 @@ def lib():
         L.mok_layer_fwd_macro.argtypes = [cfgp, I32, ctypes.POINTER(mok_layer_call), P, P, P,
                                           ctypes.POINTER(mok_expert_weights), P, P, P]
         L.mok_prepare_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P]
+        L.mok_mx_quantize_f32.argtypes = [I64, I64, P, P, P, P]
         L.mok_version.argtypes = []
         L.mok_version.restype = ctypes.c_char_p
         for name in EXPORTS[1:-1]:
@@ -388,6 +389,11 @@ def mok_tune_fwd(cfg, mbs, comms, reps, ws_bytes, own_lo, own_n, src_x, w_router
 def mok_mx_quantize(rows, K, src, codes, scales, stream=None):
     _check("mok_mx_quantize", lib().mok_mx_quantize(rows, K, _ptr(src), _ptr(codes), _ptr(scales),
                                                     _stream(stream)))
+
+
+def mok_mx_quantize_f32(rows, K, src, codes, scales, stream=None):
+    _check("mok_mx_quantize_f32", lib().mok_mx_quantize_f32(rows, K, _ptr(src), _ptr(codes),
+                                                            _ptr(scales), _stream(stream)))
 
 
 def mok_prepare_bwd(cfg, w_gate, w_up, w_down, wt_down, st_down, wt_gu, st_gu, stream=None):

@@ -839,4 +839,12 @@ mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* co
   return launch_mx_quantize(rows, K, src, codes, scales, (hipStream_t)stream);
 }
 
+mok_status mok_mx_quantize_f32(int64_t rows, int64_t K, const float* src, uint8_t* codes,
+                               uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_EINVAL;
+  if (rows == 0) return MOK_OK;
+  if (!src || !codes || !scales) return MOK_EINVAL;
+  return launch_mx_quantize(rows, K, src, codes, scales, (hipStream_t)stream, true);
+}
+
 }  // extern "C"

@@ -31,7 +31,7 @@ mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
                           int own_lo, int own_n, int R_cap, hipStream_t stream,
                           mok_trace* tr = nullptr);
 mok_status launch_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
-                              uint8_t* scales, hipStream_t stream);
+                              uint8_t* scales, hipStream_t stream, bool f32 = false);
 
 int grouped_mtiles_bound(int R_cap, int E_local);
 mok_status launch_ffn(int prec, int d, int I, int E_local, int R_cap, const void* x,

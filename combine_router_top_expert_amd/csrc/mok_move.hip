@@ -198,12 +198,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 // ---------------------------------------------------------------- MX rows
 struct MxArgs {
-  const bf16_t* src;
+  const void* src;  // bf16 or fp32 values
   uint8_t* codes;
   uint8_t* scales;
   int64_t rows, K;
 };
 
+// The 8 values of 16-byte unit u of the source as floats.
+template <typename T>
+__device__ __forceinline__ void mx_unit(const void* src, int64_t u, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 q = ld16(reinterpret_cast<const bf16_t*>(src) + u * 8);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(src) + u * 8;
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <typename T>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
   // one 16-byte unit (8 values) per thread; 4 threads per 32-value block
   const int64_t units = a.rows * (a.K / 8);
@@ -213,13 +233,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
     float v[8];
     float amax = 0.0f;
     if (have) {
-      uint4 q = ld16(a.src + u * 8);
-      uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
+      mx_unit<T>(a.src, u, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     }
@@ -326,9 +340,9 @@ mok_status launch_combine(int prec, const int32_t* dest_row, const float* gate,
 }
 
 mok_status launch_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
-                              uint8_t* scales, hipStream_t stream) {
+                              uint8_t* scales, hipStream_t stream, bool f32) {
   MxArgs a;
-  a.src = reinterpret_cast<const bf16_t*>(src);
+  a.src = src;
   a.codes = codes;
   a.scales = scales;
   a.rows = rows;
@@ -337,7 +351,10 @@ mok_status launch_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t*
   if (units == 0) return MOK_OK;
   int64_t blocks = (units + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(mx_quantize_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (f32)
+    hipLaunchKernelGGL(mx_quantize_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mx_quantize_kernel<bf16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }
 

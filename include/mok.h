@@ -442,6 +442,12 @@ mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t byte
 mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
                            uint8_t* scales, void* stream);
 
+/* The same MX quantisation of rows of fp32 values (the codec the GEMM1
+ * epilogue applies to h, which it forms in fp32): src [rows, K] fp32, 16-byte
+ * aligned (K % 32 == 0); outputs and errors as mok_mx_quantize. */
+mok_status mok_mx_quantize_f32(int64_t rows, int64_t K, const float* src, uint8_t* codes,
+                               uint8_t* scales, void* stream);
+
 /* Library version string (static storage). */
 const char* mok_version(void);
 

@@ -31,6 +31,20 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_every_export_declares_its_arguments(L):
+    """Each binding gives ctypes the argument types of its C declaration, as
+    many as the header lists: without them ctypes passes Python ints as
+    32-bit C ints, and a 64-bit parameter then reads whatever the upper half
+    of its register holds."""
+    src = open(os.path.join(ROOT, "include", "mok.h")).read()
+    for n in _declared():
+        params = re.search(n + r"\(([^)]*)\);", src, re.S).group(1).strip()
+        count = 0 if params in ("", "void") else params.count(",") + 1
+        argtypes = getattr(L, n).argtypes
+        assert argtypes is not None, n
+        assert len(argtypes) == count, n
+
+
 def test_version(L):
     assert mok.mok_version().startswith("mok ")
 

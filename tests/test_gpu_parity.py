@@ -12,7 +12,8 @@ from cases import (make_host_case, oracle_fwd_tokens, oracle_weights, peer_rows,
                    sample_tokens)
 from combine_router_top_expert_amd import (STATUS, make_config, make_weights, mok_combine,
                                            mok_dispatch, mok_expert_ffn, mok_layout,
-                                           mok_mx_quantize, mok_route, mok_workspace_bytes, synth)
+                                           mok_mx_quantize, mok_mx_quantize_f32, mok_route,
+                                           mok_workspace_bytes, synth)
 from combine_router_top_expert_amd.layer import MoELayer, to_device
 
 pytestmark = pytest.mark.gpu
@@ -818,6 +819,71 @@ def test_mx_quantize_bit_exact():
     mok_mx_quantize(rows, K, to_device(store, "bf16", DEV), codes, scales)
     torch.cuda.synchronize()
     rc, rs = oracle.mx_quantize(val.reshape(rows, K).astype(np.float64))
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(rows, K), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, K // 32), rs)
+
+
+def test_mx_quantize_every_bf16_value():
+    """The E4M3 conversion (gfx950's packed fp8 conversion of the clamped
+    value) against the oracle's bit-level rule on every finite bf16 value
+    below 2 in magnitude, each in 32-blocks whose leader (the block maximum)
+    is 1, 1.5, 1.75, 1.875 or 1.9921875: the scaled values then reach every
+    E4M3 normal and subnormal, exact ties, and the saturation above 448."""
+    _log("mx_quantize every bf16 value")
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    f = f[np.isfinite(f) & (np.abs(f) < 2.0)]
+    blocks = []
+    for lead in (1.0, 1.5, 1.75, 1.875, 1.9921875):
+        v = f[np.abs(f) <= lead]
+        n = -(-len(v) // 31) * 31
+        v = np.concatenate([v, np.zeros(n - len(v), np.float32)]).reshape(-1, 31)
+        blocks.append(np.concatenate([np.full((len(v), 1), lead, np.float32), v], axis=1))
+    blk = np.concatenate(blocks)                        # [blocks, 32]
+    K = 512
+    nb = -(-len(blk) // (K // 32)) * (K // 32)
+    blk = np.concatenate([blk, np.zeros((nb - len(blk), 32), np.float32)])
+    val = blk.reshape(-1, K)
+    rows = val.shape[0]
+    codes = torch.zeros(rows * K, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(rows * K // 32, dtype=torch.uint8, device=DEV)
+    src = torch.from_numpy(val).to(torch.bfloat16).to(DEV)  # exact: every value is a bf16
+    mok_mx_quantize(rows, K, src, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(val.astype(np.float64))
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(rows, K), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, K // 32), rs)
+
+
+def test_mx_quantize_f32_rounding_cases():
+    """The E4M3 conversion of fp32 values (the GEMM1 epilogue's path for h)
+    against the oracle's bit-level rule: every fp32 exponent below 2^10 with
+    every top-7 mantissa pattern and the low mantissa bits that decide the
+    rounding (0, 1, just below, at and above the half-way point of the
+    dropped bits, all ones), both signs, in blocks of 31 under leaders that
+    put their scaled values across the whole E4M3 range (subnormals, ties,
+    saturation above 448)."""
+    _log("mx_quantize_f32 rounding cases")
+    hi = np.arange(0x4480, dtype=np.uint32) << 16            # sign 0, exponent <= 136, top 7 mantissa bits
+    low = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    pat = (hi[:, None] | low[None, :]).reshape(-1)
+    f = np.concatenate([pat, pat | 0x80000000]).view(np.float32)
+    blocks = []
+    for lead in (1.0, 1.75, 1.9921875, 512.0, 1000.0):
+        v = f[np.abs(f) <= lead]
+        n = -(-len(v) // 31) * 31
+        v = np.concatenate([v, np.zeros(n - len(v), np.float32)]).reshape(-1, 31)
+        blocks.append(np.concatenate([np.full((len(v), 1), lead, np.float32), v], axis=1))
+    blk = np.concatenate(blocks)
+    K = 512
+    nb = -(-len(blk) // (K // 32)) * (K // 32)
+    val = np.concatenate([blk, np.zeros((nb - len(blk), 32), np.float32)]).reshape(-1, K)
+    rows = val.shape[0]
+    codes = torch.zeros(rows * K, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(rows * K // 32, dtype=torch.uint8, device=DEV)
+    mok_mx_quantize_f32(rows, K, torch.from_numpy(val).to(DEV), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(val.astype(np.float64))
     np.testing.assert_array_equal(codes.cpu().numpy().reshape(rows, K), rc)
     np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, K // 32), rs)
 

@@ -78,11 +78,13 @@ def kernel_work(name, w, R, T_pull=None):
         fp8 = name.endswith("_mx") or (name == "ring_fused_ffn" and w.prec == "mxfp8")
         return ("mfma_fp8" if fp8 else "mfma"), gemm[name]
     moves = {
-        # read token row, write slot row (MX: d E4M3 codes + d/32 scales)
-        "gather": R * d * 2.0 + (R * d * (1 + 1 / 32) if w.prec == "mxfp8" else R * d * eb),
-        "bwd_regather_x": 2.0 * R * d * eb,
-        # the token rows and h, each read and written transposed per expert
-        "bwd_transpose_x_h": 2.0 * R * (d + I) * eb,
+        # read each pulled token's row once (its other routed rows hit the
+        # caches), write every slot row (MX: d E4M3 codes + d/32 scales)
+        "gather": T_pull * d * 2.0 + (R * d * (1 + 1 / 32) if w.prec == "mxfp8" else R * d * eb),
+        "bwd_regather_x": (T_pull + R) * d * eb,
+        # the token rows (each pulled token read once) and h, written
+        # transposed per expert
+        "bwd_transpose_x_h": ((T_pull + R) * d + 2.0 * R * I) * eb,
         "combine": (T * k * d + T * d) * eb,              # read k pushed rows, write out
         # read each pulled token's dout once and every row's pushed y, write dy
         "bwd_reverse_combine_pull": (T_pull + 2.0 * R) * d * eb,

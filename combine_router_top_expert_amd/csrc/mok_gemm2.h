@@ -325,15 +325,19 @@ __device__ __forceinline__ void mma_rows(const Frags<C, A_MN, B_MN>& f, Acc<C>& 
 }
 
 // Instruction order of one k16 step: NMFMA MFMAs, with the NREAD LDS reads of
-// the next step spread one (or a few) behind each of the first MFMAs, so the
-// reads' latency runs under matrix work.  Left alone, the scheduler sinks each
-// read to just before its first use, and every k16 step waits on LDS latency
-// with the matrix cores idle.  (Scheduling hints only: they reorder
-// instructions, never the MFMAs of one accumulator, so results do not change.)
+// the next step two behind each of the first MFMAs, so the reads' latency
+// runs under matrix work.  Left alone, the scheduler sinks each read to just
+// before its first use, and every k16 step waits on LDS latency with the
+// matrix cores idle.  (Two reads per MFMA measured 1 % faster than one, all
+// of them ahead of the first MFMA 1 % slower.  Scheduling hints only: they
+// reorder instructions, never the MFMAs of one accumulator, so results do
+// not change.)
 template <int NMFMA, int NREAD, int I = 0>
 __device__ __forceinline__ void interleave_reads() {
+  // reads per MFMA: two, or as many as the step needs to place them all
+  constexpr int P = (NREAD + NMFMA - 1) / NMFMA > 2 ? (NREAD + NMFMA - 1) / NMFMA : 2;
   if constexpr (I < NMFMA) {
-    constexpr int r = NREAD / NMFMA + (I < NREAD % NMFMA ? 1 : 0);
+    constexpr int r = NREAD - P * I >= P ? P : (NREAD - P * I > 0 ? NREAD - P * I : 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
     interleave_reads<NMFMA, NREAD, I + 1>();

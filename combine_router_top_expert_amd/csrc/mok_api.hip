@@ -836,6 +836,8 @@ mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* co
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_EINVAL;
   if (rows == 0) return MOK_OK;
   if (!src || !codes || !scales) return MOK_EINVAL;
+  // 16-byte loads of the values, 8-byte stores of the codes
+  if ((uintptr_t)src % 16 != 0 || (uintptr_t)codes % 8 != 0) return MOK_EINVAL;
   return launch_mx_quantize(rows, K, src, codes, scales, (hipStream_t)stream);
 }
 
@@ -844,6 +846,7 @@ mok_status mok_mx_quantize_f32(int64_t rows, int64_t K, const float* src, uint8_
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_EINVAL;
   if (rows == 0) return MOK_OK;
   if (!src || !codes || !scales) return MOK_EINVAL;
+  if ((uintptr_t)src % 16 != 0 || (uintptr_t)codes % 8 != 0) return MOK_EINVAL;
   return launch_mx_quantize(rows, K, src, codes, scales, (hipStream_t)stream, true);
 }
 

@@ -435,7 +435,8 @@ mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t byte
 
 /* MX quantisation of rows of bf16 values (weight preparation off the timed
  * path, and the same codec as the fused activation paths):  src [rows, K]
- * bf16 (K % 32 == 0) -> codes [rows, K] E4M3, scales [rows, K/32] E8M0.
+ * bf16 (K % 32 == 0), 16-byte aligned -> codes [rows, K] E4M3 (8-byte
+ * aligned), scales [rows, K/32] E8M0; MOK_EINVAL otherwise.
  * Per block of 32: shared = clamp(floor(log2 max|v|) - 8, -127, 127) (-127 for
  * an all-zero block), scale byte = shared + 127, code = E4M3 of v / 2^shared,
  * nearest, ties to even, saturating at +-448 (OCP Microscaling v1.0). */
@@ -444,7 +445,8 @@ mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* co
 
 /* The same MX quantisation of rows of fp32 values (the codec the GEMM1
  * epilogue applies to h, which it forms in fp32): src [rows, K] fp32, 16-byte
- * aligned (K % 32 == 0); outputs and errors as mok_mx_quantize. */
+ * aligned (K % 32 == 0); outputs, alignment and errors as mok_mx_quantize.
+ * Inputs are finite (a NaN gets an unspecified code). */
 mok_status mok_mx_quantize_f32(int64_t rows, int64_t K, const float* src, uint8_t* codes,
                                uint8_t* scales, void* stream);
 

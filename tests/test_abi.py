@@ -79,6 +79,11 @@ def test_null_pointers_rejected(L):
     assert L.mok_route(ctypes.byref(cfg), 10, None, 1, None, 1, 1, None) == -1
     assert L.mok_layout(ctypes.byref(cfg), None, 1, 1, 1, 1, 1, 1, None, None) == -1
     assert L.mok_mx_quantize(4, 48, 1, 1, 1, None) == -1       # K % 32 != 0
+    # misaligned values (16-byte loads) or codes (8-byte stores), never dereferenced
+    for f in (L.mok_mx_quantize, L.mok_mx_quantize_f32):
+        assert f(4, 64, 0x1008, 0x2000, 0x3000, None) == -1
+        assert f(4, 64, 0x1000, 0x2004, 0x3000, None) == -1
+        assert f(0, 64, 0x1008, 0x2004, 0x3000, None) == 0  # nothing to do
     assert L.mok_combine(ctypes.byref(cfg), None, 1, 1, None, 0, 3, None, None, None) == -1
 
 

@@ -81,14 +81,14 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dh_g2(DhArgs a) {
       const int n = n0 + nr;
       return n < a.I ? wt + (size_t)n * a.d : nullptr;
     });
-    mainloop<C, false, false>(a.d / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                              [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+    mainloop<C, false, false>(a.d / C::BK, [&](int kt, unsigned l, auto pt) { la.issue(kt, l, pt); },
+                              [&](int kt, unsigned l, auto pt) { lb.issue(kt, l, pt); }, smem, acc);
   } else {
     MNMajor<C::BN, C::BK> lb;
     lb.ncols_left = a.I - n0;
-    mainloop<C, false, true>(a.d / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                             [&](int kt, unsigned l) {
-                               lb.issue(kt, l, [&](int kk) -> const bf16_t* { return wd + (size_t)kk * a.I; });
+    mainloop<C, false, true>(a.d / C::BK, [&](int kt, unsigned l, auto pt) { la.issue(kt, l, pt); },
+                             [&](int kt, unsigned l, auto pt) {
+                               lb.issue(kt, l, [&](int kk) -> const bf16_t* { return wd + (size_t)kk * a.I; }, pt);
                              },
                              smem, acc);
   }
@@ -188,16 +188,16 @@ __global__ __launch_bounds__(kThreads, C::OCC) void dx_g2(DxArgs a) {
       const int n = n0 + nr;
       return n < a.d ? wt + (size_t)n * 2 * a.I : nullptr;
     });
-    mainloop<C, false, false>(2 * a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                              [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+    mainloop<C, false, false>(2 * a.I / C::BK, [&](int kt, unsigned l, auto pt) { la.issue(kt, l, pt); },
+                              [&](int kt, unsigned l, auto pt) { lb.issue(kt, l, pt); }, smem, acc);
   } else {
     MNMajor<C::BN, C::BK> lb;
     lb.ncols_left = a.d - n0;
-    mainloop<C, false, true>(2 * a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                             [&](int kt, unsigned l) {
+    mainloop<C, false, true>(2 * a.I / C::BK, [&](int kt, unsigned l, auto pt) { la.issue(kt, l, pt); },
+                             [&](int kt, unsigned l, auto pt) {
                                lb.issue(kt, l, [&](int kk) -> const bf16_t* {
                                  return kk < a.I ? wg + (size_t)kk * a.d : wu + (size_t)(kk - a.I) * a.d;
-                               });
+                               }, pt);
                              },
                              smem, acc);
   }
@@ -502,8 +502,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
   MNMajor<BM, C::BK> la;
   la.ncols_left = a.M - m0;
   const bf16_t* Ab = a.A + (size_t)(off - lo) * a.lda + m0;
-  auto issue_a = [&](int kt, unsigned l) {
-    la.issue(kt, l, [&](int kk) -> const bf16_t* { return kk < cnt ? Ab + (size_t)kk * a.lda : nullptr; });
+  auto issue_a = [&](int kt, unsigned l, auto pt) {
+    la.issue(kt, l, [&](int kk) -> const bf16_t* { return kk < cnt ? Ab + (size_t)kk * a.lda : nullptr; }, pt);
   };
   if constexpr (MODE == 0 || HT) {
     // B = the chunk's token rows (MODE 0) or h rows (MODE 1) from the
@@ -520,17 +520,17 @@ __global__ __launch_bounds__(kThreads, C::OCC) void wgrad_g2(WgArgs a) {
     });
     preload();
     mainloop<C, true, false>((cnt + C::BK - 1) / C::BK, issue_a,
-                             [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc, WIN);
+                             [&](int kt, unsigned l, auto pt) { lb.issue(kt, l, pt); }, smem, acc, WIN);
   } else {
     MNMajor<C::BN, C::BK> lb;
     lb.ncols_left = a.N - n0;
     const bf16_t* Bb = a.B + (size_t)off * a.ldb + n0;
     preload();
     mainloop<C, true, true>((cnt + C::BK - 1) / C::BK, issue_a,
-                            [&](int kt, unsigned l) {
+                            [&](int kt, unsigned l, auto pt) {
                               lb.issue(kt, l, [&](int kk) -> const bf16_t* {
                                 return kk < cnt ? Bb + (size_t)kk * a.ldb : nullptr;
-                              });
+                              }, pt);
                             },
                             smem, acc, WIN);
   }

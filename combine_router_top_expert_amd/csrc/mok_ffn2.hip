@@ -18,19 +18,6 @@ namespace {
 
 using namespace g2;
 
-// Tile of a grouped-M launch: workgroup -> (expert rows, N-tile); false if the
-// workgroup has no tile (the grid is an upper bound).
-__device__ __forceinline__ bool launch_tile(const int32_t* offsets, int E_local, int R_cap,
-                                            int ntn, int* s_prefix, GTile* g, int* nt) {
-  const int total_m = group_prefix(offsets, E_local, R_cap, s_prefix);
-  const int total = total_m * ntn;
-  if ((int)blockIdx.x >= total) return false;
-  int mt;
-  grouped_order(xcd_tile(blockIdx.x, total), total_m, ntn, &mt, nt);
-  *g = group_tile(offsets, E_local, R_cap, s_prefix, mt);
-  return true;
-}
-
 // Persistent grouped-M launch: workgroup b runs tiles b, b + gridDim.x, ...
 // of the (expert rows, N-tile) grid in XCD-aware grouped order (gridDim.x a
 // multiple of 8, so every tile of a workgroup stays on its XCD's range); the
@@ -84,12 +71,17 @@ static unsigned persistent_grid(int tiles, int occ) {
   return (unsigned)(tiles < n ? ((tiles + 7) / 8) * 8 : n);
 }
 
+// One tile per workgroup: GEMM1's epilogue keeps many addresses live, and a
+// tile loop around it spills (measured slower than one tile per workgroup).
 __global__ __launch_bounds__(kThreads) void ffn1_mx(F1MxArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[MxCfg::SMEM];
   __shared__ int s_prefix[257];
-  GTile g;
-  int nt;
-  if (!launch_tile(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, &g, &nt)) return;
+  const int total_m = group_prefix(a.offsets, a.E_local, a.R_cap, s_prefix);
+  const int total = total_m * a.ntn;
+  if ((int)blockIdx.x >= total) return;
+  int mt, nt;
+  grouped_order(xcd_tile(blockIdx.x, total), total_m, a.ntn, &mt, &nt);
+  const GTile g = group_tile(a.offsets, a.E_local, a.R_cap, s_prefix, mt);
   const int KS = a.d / 32;
   ffn1_mx_tile(
       a, smem, g, nt,
@@ -106,10 +98,8 @@ __global__ __launch_bounds__(kThreads) void ffn1_mx(F1MxArgs a) {
 __global__ __launch_bounds__(kThreads) void ffn2_mx(F2Args a, DstTable staging) {
   __shared__ __attribute__((aligned(16))) char smem[MxCfg::SMEM];
   __shared__ int s_prefix[257];
-  GTile g;
-  int nt;
-  if (!launch_tile(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix, &g, &nt)) return;
-  ffn2_mx_tile(a, staging, smem, g, nt);
+  persistent_tiles(a.offsets, a.E_local, a.R_cap, a.ntn, s_prefix,
+                   [&](const GTile& g, int nt) { ffn2_mx_tile(a, staging, smem, g, nt); });
 }
 
 }  // namespace
@@ -214,7 +204,7 @@ mok_status launch_ffn_mx(int d, int I, int E_local, int R_cap, const uint8_t* xq
   a2.ntn = (d + MxCfg::BN - 1) / MxCfg::BN;
   a2.T_src = T_src;
   a2.k = k;
-  hipLaunchKernelGGL(ffn2_mx, dim3((unsigned)(mt * a2.ntn)), dim3(kThreads), 0, stream, a2, gtab);
+  hipLaunchKernelGGL(ffn2_mx, dim3(persistent_grid(mt * a2.ntn, 1)), dim3(kThreads), 0, stream, a2, gtab);
   trace_mark(tr, "ffn2_down_mx", stream);
   return hipGetLastError() == hipSuccess ? MOK_OK : MOK_EDEVICE;
 }

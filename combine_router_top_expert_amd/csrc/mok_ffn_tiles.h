@@ -90,8 +90,8 @@ __device__ __forceinline__ void ffn1_tile(const F1Args& a, char* smem, const GTi
     return (up ? wu : wg) + (size_t)i * a.d;
   });
   Acc<C> acc;
-  mainloop<C, false, false>(a.d / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                            [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+  mainloop<C, false, false>(a.d / C::BK, [&](int kt, unsigned l, auto pt) { la.issue(kt, l, pt); },
+                            [&](int kt, unsigned l, auto pt) { lb.issue(kt, l, pt); }, smem, acc);
   // Wave column wn holds B-tile columns [wn*BN/2, (wn+1)*BN/2): 32-wide blocks
   // alternating gate, up, so i = nt*BN/2 + wn*BN/4 + 32*(block/2) + (col % 32).
   // Staged as fp32 so that h is formed from the unrounded a and b.
@@ -178,8 +178,8 @@ __device__ __forceinline__ void ffn2_tile(const F2Args& a, const DstTable& stagi
     return c < a.d ? wd + (size_t)c * a.I : nullptr;
   });
   Acc<C> acc;
-  mainloop<C, false, false>(a.I / C::BK, [&](int kt, unsigned l) { la.issue(kt, l); },
-                            [&](int kt, unsigned l) { lb.issue(kt, l); }, smem, acc);
+  mainloop<C, false, false>(a.I / C::BK, [&](int kt, unsigned l, auto pt) { la.issue(kt, l, pt); },
+                            [&](int kt, unsigned l, auto pt) { lb.issue(kt, l, pt); }, smem, acc);
   ffn2_store<C>(acc, smem, g, nt, a, staging);
 }
 

@@ -23,6 +23,7 @@
 // tails contribute nothing and no address leaves its buffer.
 #pragma once
 
+#include <type_traits>
 #include "mok_common.h"
 
 namespace mok {
@@ -33,6 +34,13 @@ constexpr int BM = 256;
 
 // Zeros read by lanes whose rows, k-rows or columns fall outside a problem.
 static __device__ const uint4 g_zero[64] = {};
+
+// Part P of NP of a wave's direct loads of one stage: the main loop spreads a
+// stage's loads over the MFMAs of its hand-over instead of issuing them in
+// one burst, which would stall the wave on the memory pipeline with its
+// matrix work queued behind them.
+template <int P, int NP>
+struct Part {};
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -104,10 +112,17 @@ struct KMajor {
       }
     }
   }
-  __device__ __forceinline__ void issue(int kt, unsigned lds_op) const {
+  __device__ __forceinline__ void issue(int kt, unsigned lds_op) const { issue_range<0, NI>(kt, lds_op); }
+  template <int P, int NP>
+  __device__ __forceinline__ void issue(int kt, unsigned lds_op, Part<P, NP>) const {
+    issue_range<P * NI / NP, (P + 1) * NI / NP>(kt, lds_op);
+  }
+  // loads [J0, J1) of this wave's NI loads of stage kt
+  template <int J0, int J1>
+  __device__ __forceinline__ void issue_range(int kt, unsigned lds_op) const {
     const unsigned w = wave_id();
 #pragma unroll
-    for (int j = 0; j < NI; ++j) load_lds16(p[j] + (size_t)kt * adv[j], lds_op + (w * NI + j) * 1024);
+    for (int j = J0; j < J1; ++j) load_lds16(p[j] + (size_t)kt * adv[j], lds_op + (w * NI + j) * 1024);
   }
   // fragment of rows [r0, r0+32), k16 step s: lane l reads row r0 + l%32
   __device__ __forceinline__ static bf16x8_t frag(const char* lds_op, int r0, int s) {
@@ -137,10 +152,14 @@ struct MNMajor {
   int ncols_left;
   template <class KPtr>
   __device__ __forceinline__ void issue(int kt, unsigned lds_op, KPtr kptr) const {
+    issue(kt, lds_op, kptr, Part<0, 1>());
+  }
+  template <class KPtr, int P, int NP>
+  __device__ __forceinline__ void issue(int kt, unsigned lds_op, KPtr kptr, Part<P, NP>) const {
     const int lane = threadIdx.x & 63;
     const unsigned w = wave_id();
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = P * NI / NP; j < (P + 1) * NI / NP; ++j) {
       const int I = w * NI + j;
       const int krow = KPI * I + lane / CPK;
       const int c = (lane % CPK) ^ (4 * (krow & 3));
@@ -332,15 +351,15 @@ __device__ __forceinline__ void mma_rows(const Frags<C, A_MN, B_MN>& f, Acc<C>& 
 // of them ahead of the first MFMA 1 % slower.  Scheduling hints only: they
 // reorder instructions, never the MFMAs of one accumulator, so results do
 // not change.)
-template <int NMFMA, int NREAD, int I = 0>
+template <int NMFMA, int NREAD, int I = 0, int PMIN = 2>
 __device__ __forceinline__ void interleave_reads() {
-  // reads per MFMA: two, or as many as the step needs to place them all
-  constexpr int P = (NREAD + NMFMA - 1) / NMFMA > 2 ? (NREAD + NMFMA - 1) / NMFMA : 2;
+  // reads per MFMA: PMIN, or as many as the step needs to place them all
+  constexpr int P = (NREAD + NMFMA - 1) / NMFMA > PMIN ? (NREAD + NMFMA - 1) / NMFMA : PMIN;
   if constexpr (I < NMFMA) {
     constexpr int r = NREAD - P * I >= P ? P : (NREAD - P * I > 0 ? NREAD - P * I : 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
-    interleave_reads<NMFMA, NREAD, I + 1>();
+    interleave_reads<NMFMA, NREAD, I + 1, PMIN>();
   }
 }
 
@@ -371,6 +390,16 @@ __device__ __forceinline__ void wait_stages_lgkm0(int after) {
   }
 }
 
+// Issue part P of NP of a stage's loads through a loader callback that takes
+// a Part; a callback without one issues the whole stage in part 0.
+template <int P, int NP, class F>
+__device__ __forceinline__ void issue_part(F& f, int kt, unsigned lds) {
+  if constexpr (std::is_invocable_v<F&, int, unsigned, Part<P, NP>>)
+    f(kt, lds, Part<P, NP>());
+  else if constexpr (P == 0)
+    f(kt, lds);
+}
+
 // bf16 main loop over KT stages of BK k in an NS-deep LDS ring, pipelined
 // across stages.  issueA(kt, lds) / issueB(kt, lds) issue this wave's direct
 // loads of one stage (lds = LDS byte address of the operand's tile in the
@@ -398,8 +427,8 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < KT) {
-      issueA(s, lds0 + s * C::STAGE);
-      issueB(s, lds0 + s * C::STAGE + C::A_BYTES);
+      issue_part<0, 1>(issueA, s, lds0 + s * C::STAGE);
+      issue_part<0, 1>(issueB, s, lds0 + s * C::STAGE + C::A_BYTES);
     }
   wait_stages_lgkm0<C::LOADS, NS - 1>(min(KT, NS) - 1);  // stage 0 landed
   __builtin_amdgcn_s_barrier();
@@ -423,13 +452,17 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
     __builtin_amdgcn_s_barrier();
     const unsigned slot = lds0 + (kt % NS) * C::STAGE;
     const bool more = kt + NS < KT;
-    if (more) issueA(kt + NS, slot);
-    mma_rows<C, A_MN, B_MN, 0, 2>(last, acc);
-    if (more) issueB(kt + NS, slot + C::A_BYTES);
+    if (more) issue_part<0, 2>(issueA, kt + NS, slot);
+    mma_rows<C, A_MN, B_MN, 0, 1>(last, acc);
+    if (more) issue_part<1, 2>(issueA, kt + NS, slot);
+    mma_rows<C, A_MN, B_MN, 1, 2>(last, acc);
+    if (more) issue_part<0, 2>(issueB, kt + NS, slot + C::A_BYTES);
     const char* nxt = smem + ((kt + 1) % NS) * C::STAGE;
     f[S & 1].load(nxt, nxt + C::A_BYTES, 0);
-    mma_rows<C, A_MN, B_MN, 2, 4>(last, acc);
-    interleave_reads<2 * C::WNB, frag_reads<C, A_MN, B_MN>()>();
+    mma_rows<C, A_MN, B_MN, 2, 3>(last, acc);
+    interleave_reads<C::WNB, frag_reads<C, A_MN, B_MN>()>();
+    if (more) issue_part<1, 2>(issueB, kt + NS, slot + C::A_BYTES);
+    mma_rows<C, A_MN, B_MN, 3, 4>(last, acc);
   }
 }
 

@@ -432,6 +432,58 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
     }
   wait_stages_lgkm0<C::LOADS, NS - 1>(min(KT, NS) - 1);  // stage 0 landed
   __builtin_amdgcn_s_barrier();
+  if constexpr (S == 4 && !A_MN) {
+    // Four k16 steps per stage: the hand-over comes before step 2, so that
+    // the stage's loads spread over the 32 MFMAs of steps 2 and 3 (a wave's
+    // 16 direct loads take the CU's memory pipeline about as long as 32
+    // MFMAs); steps 2 and 3 are both read during step 1.  (With a
+    // transposing A operand, twice a step's reads in one step cost more than
+    // the spread gains: the weight gradients keep the later hand-over.)
+    constexpr int R = frag_reads<C, A_MN, B_MN>();
+    F fa, fb, fc;
+    fa.load(smem, smem + C::A_BYTES, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const char* cur = smem + (kt % NS) * C::STAGE;
+      fb.load(cur, cur + C::A_BYTES, 1);
+      mma_rows<C, A_MN, B_MN, 0, 4>(fa, acc);
+      interleave_reads<4 * C::WNB, R>();
+      fc.load(cur, cur + C::A_BYTES, 2);
+      fa.load(cur, cur + C::A_BYTES, 3);
+      mma_rows<C, A_MN, B_MN, 0, 4>(fb, acc);
+      interleave_reads<4 * C::WNB, 2 * R>();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_stages_lgkm0<C::LOADS, NS - 2>(min(KT - 1, kt + NS - 1) - (kt + 1));
+      __builtin_amdgcn_s_barrier();
+      const unsigned slot = lds0 + (kt % NS) * C::STAGE;
+      const bool more = kt + NS < KT;
+      // step 2 (fc) and step 3 (fa), a quarter of the operand loads before
+      // each row block; the next stage's step 0 is read into fb during step 3
+      if (more) issue_part<0, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 0, 1>(fc, acc);
+      if (more) issue_part<1, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 1, 2>(fc, acc);
+      if (more) issue_part<2, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 2, 3>(fc, acc);
+      if (more) issue_part<3, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 3, 4>(fc, acc);
+      if (more) issue_part<0, 4>(issueB, kt + NS, slot + C::A_BYTES);
+      const char* nxt = smem + ((kt + 1) % NS) * C::STAGE;
+      fb.load(nxt, nxt + C::A_BYTES, 0);
+      mma_rows<C, A_MN, B_MN, 0, 1>(fa, acc);
+      interleave_reads<C::WNB, R, 0, (R + C::WNB - 1) / C::WNB>();
+      if (more) issue_part<1, 4>(issueB, kt + NS, slot + C::A_BYTES);
+      mma_rows<C, A_MN, B_MN, 1, 2>(fa, acc);
+      if (more) issue_part<2, 4>(issueB, kt + NS, slot + C::A_BYTES);
+      mma_rows<C, A_MN, B_MN, 2, 3>(fa, acc);
+      if (more) issue_part<3, 4>(issueB, kt + NS, slot + C::A_BYTES);
+      mma_rows<C, A_MN, B_MN, 3, 4>(fa, acc);
+      // the next stage's step 0 is in fb: rotate the roles
+      F t = fa;
+      fa = fb;
+      fb = t;
+    }
+    return;
+  }
   F f[2];
   f[0].load(smem, smem + C::A_BYTES, 0);
   for (int kt = 0; kt < KT; ++kt) {

@@ -373,6 +373,35 @@ def hbm_stream_lines(args, torch):
                           "steps": args.steps}), flush=True)
 
 
+def mfma_probe_lines(args, torch):
+    """The matrix-core rate probe (MFMAs on register operands, one wave per
+    SIMD, no memory traffic) for bf16 and E4M3, on hashed and on constant
+    operands: one JSON line each, with the fraction of the published peak."""
+    from combine_router_top_expert_amd import mok_mfma_probe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda:0")
+    iters = 4000
+    for kind, name, flops, peak in ((0, "bf16 32x32x16", 32768.0, PEAK_BF16_TFLOPS),
+                                    (1, "E4M3 scaled 32x32x64", 131072.0, PEAK_FP8_TFLOPS)):
+        for constant, data in ((0, "hashed"), (1, "ones")):
+            for _ in range(max(args.warmup, 1)):
+                mok_mfma_probe(kind, constant, iters, cus, out)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                mok_mfma_probe(kind, constant, iters, cus, out)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / args.steps
+            tf = cus * 4 * iters * 16 * flops / dt / 1e12
+            exact = None
+            if constant:
+                exact = bool(torch.all(out == 256.0 * (16 if kind == 0 else 64) * iters).item())
+            print(json.dumps({"metric": f"matrix-core rate probe, {name}, {data} operands",
+                              "value": tf, "unit": "TFLOP/s", "frac_peak": tf / peak,
+                              "ms_per_call": dt * 1e3, "workgroups": cus, "steps": args.steps,
+                              "sums_exact": exact}), flush=True)
+
+
 def run_workload(args, name, np, torch):
     """Inputs, layer, timed steps and the CPU baseline of one workload -> records."""
     from combine_router_top_expert_amd import Trace, synth
@@ -607,6 +636,9 @@ def main():
     ap.add_argument("--hbm-copy-gib", type=float, default=0.0,
                     help="only a plain device copy of this many GiB (profiler byte-counter "
                          "reference)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="instead of the layer: the matrix-core rate probe (bf16 and E4M3, "
+                         "hashed and constant operands)")
     ap.add_argument("--hbm-stream-gib", type=float, default=0.0,
                     help="instead of the layer: the HBM streaming probe (read, write, copy) "
                          "over this many GiB")
@@ -621,6 +653,9 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
+    if args.mfma_probe:
+        mfma_probe_lines(args, torch)
+        return
     if args.hbm_stream_gib > 0:
         hbm_stream_lines(args, torch)
         return

@@ -31,7 +31,7 @@ STATUS = {
 EXPORTS = ("mok_workspace_bytes", "mok_route", "mok_layout", "mok_dispatch", "mok_expert_ffn",
            "mok_combine", "mok_layer_fwd", "mok_layer_bwd", "mok_mx_quantize", "mok_tune_fwd",
            "mok_ring_layout", "mok_hbm_stream", "mok_layer_fwd_noalloc", "mok_layer_fwd_macro",
-           "mok_prepare_bwd", "mok_mx_quantize_f32", "mok_version")
+           "mok_prepare_bwd", "mok_mx_quantize_f32", "mok_mfma_probe", "mok_version")
 
 
 class MokError(RuntimeError):
@@ -231,6 +231,7 @@ def lib():
         L.mok_ring_layout.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(I32)]
         L.mok_hbm_stream.argtypes = [I32, P, P, I64, P]
+        L.mok_mfma_probe.argtypes = [I32, I32, I64, I32, P, P]
         L.mok_layer_fwd_noalloc.argtypes = [cfgp, I32, I32, P, P, P, P,
                                             ctypes.POINTER(mok_expert_weights),
                                             ctypes.POINTER(mok_fwd_state), P, P, P, P]
@@ -413,6 +414,12 @@ def mok_ring_layout(cfg):
 def mok_hbm_stream(mode, dst, src, nbytes, stream=None):
     """HBM streaming probe: mode 0 read src, 1 write dst, 2 copy src -> dst."""
     _check("mok_hbm_stream", lib().mok_hbm_stream(mode, _ptr(dst), _ptr(src), nbytes,
+                                                  _stream(stream)))
+
+
+def mok_mfma_probe(kind, constant, iters, workgroups, out, stream=None):
+    """Matrix-core rate probe: kind 0 bf16, 1 E4M3; constant 0 hashed data, 1 ones."""
+    _check("mok_mfma_probe", lib().mok_mfma_probe(kind, constant, iters, workgroups, _ptr(out),
                                                   _stream(stream)))
 
 

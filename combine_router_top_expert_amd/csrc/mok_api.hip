@@ -831,6 +831,14 @@ mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t byte
   return launch_stream(mode, dst, src, bytes, (hipStream_t)stream);
 }
 
+mok_status mok_mfma_probe(int32_t kind, int32_t constant, int64_t iters, int32_t workgroups,
+                          float* out, void* stream) {
+  if ((kind != 0 && kind != 1) || (constant != 0 && constant != 1) || iters <= 0 ||
+      workgroups <= 0 || !out)
+    return MOK_EINVAL;
+  return launch_mfma_probe(kind, constant, iters, workgroups, out, (hipStream_t)stream);
+}
+
 mok_status mok_mx_quantize(int64_t rows, int64_t K, const void* src, uint8_t* codes,
                            uint8_t* scales, void* stream) {
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_EINVAL;

@@ -107,6 +107,8 @@ mok_status launch_ring_fwd(const RingPlan& p, hipStream_t stream, mok_trace* tr 
 
 // HBM streaming probe (mok_stream.hip): mode 0 read, 1 write, 2 copy.
 mok_status launch_stream(int mode, void* dst, const void* src, int64_t bytes, hipStream_t stream);
+mok_status launch_mfma_probe(int kind, int constant, int64_t iters, int workgroups, float* out,
+                             hipStream_t stream);
 
 struct BwdPlan {
   int prec;

@@ -433,6 +433,20 @@ mok_status mok_ring_layout(const mok_config* cfg, size_t* offset, size_t* slot_b
  * MOK_EINVAL on a bad mode, size or pointer. */
 mok_status mok_hbm_stream(int32_t mode, void* dst, const void* src, int64_t bytes, void* stream);
 
+/* Matrix-core rate probe: a reference rate for the expert GEMMs.  Launches
+ * `workgroups` workgroups of 256 threads (one per CU gives one wave per
+ * SIMD); every wave runs `iters` rounds of 16 MFMAs on operands held in
+ * registers, with no memory traffic, so the rate reflects what the matrix
+ * cores sustain under the chip's power limit.  kind 0: bf16
+ * (32x32x16, 32768 flops each); kind 1: E4M3 with unit E8M0 scales
+ * (32x32x64, 131072 flops each).  constant 0: hashed operand values
+ * (random-looking data, the layer's case); 1: every operand 1.0, which makes
+ * out exact.  out: device memory, workgroups * 256 floats, one sum of its
+ * accumulators per thread.  MOK_EINVAL on a bad kind, flag, count or null
+ * out. */
+mok_status mok_mfma_probe(int32_t kind, int32_t constant, int64_t iters, int32_t workgroups,
+                          float* out, void* stream);
+
 /* MX quantisation of rows of bf16 values (weight preparation off the timed
  * path, and the same codec as the fused activation paths):  src [rows, K]
  * bf16 (K % 32 == 0), 16-byte aligned -> codes [rows, K] E4M3 (8-byte

@@ -85,6 +85,12 @@ def test_null_pointers_rejected(L):
         assert f(4, 64, 0x1000, 0x2004, 0x3000, None) == -1
         assert f(0, 64, 0x1008, 0x2004, 0x3000, None) == 0  # nothing to do
     assert L.mok_combine(ctypes.byref(cfg), None, 1, 1, None, 0, 3, None, None, None) == -1
+    # the matrix-core probe: kind, data flag, counts and output checked on the host
+    assert L.mok_mfma_probe(2, 0, 10, 1, 0x1000, None) == -1
+    assert L.mok_mfma_probe(0, 2, 10, 1, 0x1000, None) == -1
+    assert L.mok_mfma_probe(1, 0, 0, 1, 0x1000, None) == -1
+    assert L.mok_mfma_probe(1, 0, 10, 0, 0x1000, None) == -1
+    assert L.mok_mfma_probe(0, 1, 10, 1, None, None) == -1
 
 
 def _layer_fwd_rc(L, cfg):

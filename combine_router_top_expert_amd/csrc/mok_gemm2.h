@@ -484,6 +484,76 @@ __device__ __forceinline__ void mainloop(int KT, IA issueA, IB issueB, char* sme
     }
     return;
   }
+  if constexpr (S == 4 && A_MN) {
+    // Four k16 steps, a transposing A operand: the hand-over stays before the
+    // last step (reading two steps in one costs these GEMMs more than it
+    // gains), and the freed slot's loads are split: A during the last step
+    // of stage kt, B during step 0 of stage kt + 1, which still leaves the B
+    // loads three steps to land before the next hand-over.  Loads go out in
+    // stage order, so the vmcnt arithmetic of whole stages holds.  The
+    // steady-state stages run in a loop of their own whose body has no
+    // branch (a branch around the loads lets the compiler sink MFMAs below
+    // the hand-over).
+    constexpr int R = frag_reads<C, A_MN, B_MN>();
+    F f[2];
+    f[0].load(smem, smem + C::A_BYTES, 0);
+    auto stage = [&](int kt, auto steady, bool pmore, bool more) {
+      constexpr bool ST = decltype(steady)::value;
+      const char* cur = smem + (kt % NS) * C::STAGE;
+      const unsigned pslot = lds0 + ((kt + NS - 1) % NS) * C::STAGE + C::A_BYTES;
+      // step 0, with the B loads of stage kt - 1 + NS
+      f[1].load(cur, cur + C::A_BYTES, 1);
+      // (scheduling barriers keep each quarter of the loads in its place)
+      if (ST || pmore) issue_part<0, 4>(issueB, kt - 1 + NS, pslot);
+      mma_rows<C, A_MN, B_MN, 0, 1>(f[0], acc);
+      interleave_reads<C::WNB, R, 0, (R + C::WNB - 1) / C::WNB>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (ST || pmore) issue_part<1, 4>(issueB, kt - 1 + NS, pslot);
+      mma_rows<C, A_MN, B_MN, 1, 2>(f[0], acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ST || pmore) issue_part<2, 4>(issueB, kt - 1 + NS, pslot);
+      mma_rows<C, A_MN, B_MN, 2, 3>(f[0], acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ST || pmore) issue_part<3, 4>(issueB, kt - 1 + NS, pslot);
+      mma_rows<C, A_MN, B_MN, 3, 4>(f[0], acc);
+      __builtin_amdgcn_sched_barrier(0);
+      // steps 1 .. S-2
+#pragma unroll
+      for (int st = 1; st + 1 < S; ++st) {
+        f[(st + 1) & 1].load(cur, cur + C::A_BYTES, st + 1);
+        mma_rows<C, A_MN, B_MN, 0, 4>(f[st & 1], acc);
+        interleave_reads<4 * C::WNB, R>();
+      }
+      const F& last = f[(S - 1) & 1];
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ST)
+        wait_vmcnt_lgkm0<(NS - 2) * C::LOADS>();
+      else
+        wait_stages_lgkm0<C::LOADS, NS - 2>(min(KT - 1, kt + NS - 1) - (kt + 1));
+      __builtin_amdgcn_s_barrier();
+      // the last step, with the A loads of stage kt + NS
+      const unsigned slot = lds0 + (kt % NS) * C::STAGE;
+      if (ST || more) issue_part<0, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 0, 1>(last, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ST || more) issue_part<1, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 1, 2>(last, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ST || more) issue_part<2, 4>(issueA, kt + NS, slot);
+      const char* nxt = smem + ((kt + 1) % NS) * C::STAGE;
+      f[S & 1].load(nxt, nxt + C::A_BYTES, 0);
+      mma_rows<C, A_MN, B_MN, 2, 3>(last, acc);
+      interleave_reads<C::WNB, R, 0, (R + C::WNB - 1) / C::WNB>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (ST || more) issue_part<3, 4>(issueA, kt + NS, slot);
+      mma_rows<C, A_MN, B_MN, 3, 4>(last, acc);
+    };
+    int kt = 0;
+    if (KT > 0) stage(kt++, std::false_type(), false, NS < KT);
+    for (; kt + NS < KT; ++kt) stage(kt, std::true_type(), true, true);
+    for (; kt < KT; ++kt) stage(kt, std::false_type(), kt - 1 + NS < KT, false);
+    return;
+  }
   F f[2];
   f[0].load(smem, smem + C::A_BYTES, 0);
   for (int kt = 0; kt < KT; ++kt) {

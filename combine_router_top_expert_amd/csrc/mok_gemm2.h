@@ -401,18 +401,20 @@ __device__ __forceinline__ void issue_part(F& f, int kt, unsigned lds) {
 }
 
 // bf16 main loop over KT stages of BK k in an NS-deep LDS ring, pipelined
-// across stages.  issueA(kt, lds) / issueB(kt, lds) issue this wave's direct
-// loads of one stage (lds = LDS byte address of the operand's tile in the
-// stage).  All NS slots are filled up front.  The hand-over to stage kt+1
-// (wait for this wave's loads of kt+1 -- the loads of up to NS-2 later stages
-// stay in flight -- and for its LDS reads of kt, then the workgroup barrier)
-// comes before the last k16 step of stage kt; the loads of stage kt+NS into
-// the slot just freed and the first fragment reads of stage kt+1 are then
-// issued between the MFMAs of that last step, so their latency is covered by
-// matrix work instead of standing in front of it.  The inline-assembly loads
-// are scheduling boundaries, which keeps that order in the instruction
-// stream.  The accumulation order (k16 steps ascending) does not depend on
-// NS or BK.
+// across stages.  issueA(kt, lds[, Part]) / issueB(kt, lds[, Part]) issue
+// this wave's direct loads of one stage, or part P of NP of them (lds = LDS
+// byte address of the operand's tile in the stage).  All NS slots are filled
+// up front.  The hand-over to stage kt+1 (wait for this wave's loads of
+// kt+1 -- the loads of up to NS-2 later stages stay in flight -- and for its
+// LDS reads of kt, then the workgroup barrier) comes once the rest of stage
+// kt's fragments are in registers: before step 2 of four with a K-major A
+// operand, before the last step otherwise.  The loads of stage kt+NS into
+// the slot just freed go out in parts between the remaining MFMAs (for a
+// transposing A operand, B's part in step 0 of the next stage), and the
+// first fragment reads of stage kt+1 between the last ones, so neither the
+// loads' issue nor the reads' latency stands in front of matrix work.  The
+// accumulation order (k16 steps ascending) does not depend on NS, BK or the
+// hand-over.
 // keep_acc: continue from the accumulators' values (a partial sum carried
 // over exactly from an earlier launch) instead of starting from zero.
 template <class C, bool A_MN, bool B_MN, class IA, class IB>

@@ -455,7 +455,7 @@ def run_workload(args, name, np, torch):
         tuned = None
         comm = args.comm_wgs
         if args.tune:
-            table = L.tune()
+            table = L.tune(reps=10)
             log("tuner (minibatch rows, dispatch workgroups) -> ms per forward:",
                 {f"{m}/{c}": (round(v, 3) if v is not None else None) for (m, c), v in table.items()})
             mb, comm = L.cfg.minibatch_rows, L.cfg.comm_wgs

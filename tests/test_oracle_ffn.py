@@ -120,6 +120,24 @@ def test_bf16_rounding_is_nearest_even():
     assert all(oracle.round_bf16(float(a)) == b for a, b in zip(v, ref))
 
 
+def test_bf16_rounding_of_subnormals_matches_torch():
+    """The subnormal branch (|v| < 2^-126, fixed quantum 2^-133) against
+    torch's fp32 -> bf16 conversion (round to nearest even on the bit
+    pattern): every fp32 subnormal whose low 16 bits are 0, 1, half-way or
+    all ones, both signs, and values that round up into the normal range."""
+    import torch
+    hi = np.arange(0, 1 << 7, dtype=np.uint32) << 16
+    low = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    bits = (hi[:, None] | low[None, :]).reshape(-1)
+    bits = bits[bits > 0]
+    bits = np.concatenate([bits, bits | 0x80000000, np.array([0x007FFFFF, 0x007F8000], np.uint32)])
+    v = bits.view(np.float32)
+    ref = torch.from_numpy(v.copy()).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = np.array([oracle.round_bf16(float(a)) for a in v])
+    np.testing.assert_array_equal(got, ref)
+    assert oracle.round_bf16(float(np.float32(2.0 ** -126) - np.float32(2.0 ** -149))) == 2.0 ** -126
+
+
 def test_mxfp8_row_quantisation_points():
     rng = np.random.default_rng(6)
     d, I = 64, 96

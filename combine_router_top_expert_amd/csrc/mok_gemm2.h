@@ -275,64 +275,6 @@ struct Frags {
   }
 };
 
-// One LDS stage of MFMAs, the LDS reads of k16 step s+1 in flight while the
-// MFMAs of step s run (two fragment register sets).
-template <class C, bool A_MN, bool B_MN>
-__device__ __forceinline__ void stage_mma(const char* As, const char* Bs, Acc<C>& acc) {
-  constexpr int S = C::BK / 16;
-  constexpr int NMFMA = 4 * C::WNB;                         // per k16 step
-  constexpr int NREAD = (A_MN ? 8 : 4) + (B_MN ? 2 : 1) * C::WNB;  // LDS reads per step
-  Frags<C, A_MN, B_MN> f[2];
-  f[0].load(As, Bs, 0);
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    if (s + 1 < S) f[(s + 1) & 1].load(As, Bs, s + 1);
-    const Frags<C, A_MN, B_MN>& cur = f[s & 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < C::WNB; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc.c[i][j], 0, 0, 0);
-  }
-  __builtin_amdgcn_iglp_opt(0);
-}
-
-// Wait until at most `after` stages of N loads each are still in flight
-// (after = stages issued after the one about to be consumed, 0 .. MAXA).
-template <int N, int MAXA>
-__device__ __forceinline__ void wait_stages(int after) {
-  if constexpr (MAXA > 0) {
-    if (after >= MAXA) {
-      wait_vmcnt<MAXA * N>();
-      return;
-    }
-    wait_stages<N, MAXA - 1>(after);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-// Main loop over KT stages of C::STAGE bytes in an NS-deep LDS ring.
-// issue(kt, lds) issues this wave's C::LOADS direct loads of stage kt into the
-// stage at LDS byte address lds; compute(stage) consumes a landed stage.
-template <class C, class Issue, class Compute>
-__device__ __forceinline__ void pipeline(int KT, Issue issue, Compute compute, char* smem) {
-  if (KT <= 0) return;
-  const unsigned lds0 = lds_addr_of(smem);
-#pragma unroll
-  for (int s = 0; s < C::NS - 1; ++s)
-    if (s < KT) issue(s, lds0 + s * C::STAGE);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_stages<C::LOADS, C::NS - 2>(min(KT - 1, kt + C::NS - 2) - kt);
-    // every wave's loads of stage kt have landed, and every wave is done with
-    // the stage the next issue overwrites
-    __builtin_amdgcn_s_barrier();
-    const int nk = kt + C::NS - 1;
-    if (nk < KT) issue(nk, lds0 + (nk % C::NS) * C::STAGE);
-    compute(smem + (kt % C::NS) * C::STAGE);
-  }
-}
-
 // MFMAs of one k16 step for row blocks [I0, I1) of the wave tile.
 template <class C, bool A_MN, bool B_MN, int I0, int I1>
 __device__ __forceinline__ void mma_rows(const Frags<C, A_MN, B_MN>& f, Acc<C>& acc) {
